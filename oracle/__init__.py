@@ -1,0 +1,26 @@
+"""fp64 CPU oracle for local cluster attention over off-grid tokens.
+
+TEST INFRASTRUCTURE ONLY.  This package is imported by ``tests/``, by
+``__graft_entry__.smoke()`` and by the ``cpu_baseline`` leg of ``bench.py``;
+the product path (``gathered_local_attention_amd``) never imports, calls or
+links it, and it imports nothing from the product path.
+
+See :mod:`oracle.cluster_attention` for the functions and the passages of
+the pages each one follows.
+"""
+
+from .cluster_attention import (  # noqa: F401
+    quantize,
+    morton_code,
+    balanced_clusters,
+    centroid_sums,
+    nearest_clusters,
+    nearest_clusters_fullsort,
+    key_lists,
+    build_neighbors,
+    count_matrix,
+    attn_fwd_dense,
+    attn_fwd_gathered,
+    attn_bwd_dense,
+    attn_bwd_gathered,
+)
