@@ -1,0 +1,243 @@
+"""Throughput of one local-cluster-attention step on one MI355X.
+
+A step is one pass of the whole hot path over one batch: neighbour-list
+build, forward (O + LSE) and backward (dQ, dK, dV), on the stage-1
+pre-training shape (32 images x 2048 visible tokens of a 64x64 Perlin-masked
+patch grid, 4 heads x 32 dims, bf16, clusters of 8, 48 key slots).
+
+Inputs are resident in HBM before the timed region.  Steps rotate over
+several copies of the batch whose combined footprint exceeds the 256 MB
+last-level cache, so no step reads data a recent step left in cache (the
+"warm" figure, every step on one copy, is reported beside it).
+
+Prints one JSON line.  Usage:
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config stage1]
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, vendor figure
+BF16_MFMA_PEAK_TFLOPS = 2500.0  # dense
+
+
+def algorithmic(cfg):
+    """Compulsory bytes and matmul flops of each entry point (every tensor
+    touched once; gathered re-reads, workspace and atomics not counted)."""
+    T, H, D, nk = cfg.tokens, cfg.H, cfg.D, cfg.nk
+    es = 4 if cfg.dtype == "f32" else 2
+    C = T // cfg.cs
+    t = T * H * D * es                  # one [B, N, H, D] tensor
+    lse = T * H * 4
+    idx = T * 4 + C * nk * 4            # q_idx + key_idx
+    return {
+        "build": {"bytes": T * 8 + T * 4 + C * cfg.k * 4 + C * nk * 4, "flops": 0},
+        "fwd": {"bytes": 3 * t + t + lse + idx, "flops": T * H * 4 * nk * D},
+        "bwd": {"bytes": 5 * t + lse + 3 * t + idx, "flops": T * H * 10 * nk * D},
+    }
+
+
+def copy_bandwidth(torch, nbytes=1 << 30, reps=10):
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    src.fill_(1)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    del src, dst
+    return 2 * nbytes / (ms * 1e-3) / 1e9
+
+
+def cpu_baseline(cfg, case, images: int):
+    """The fp64 oracle (gathered form, forward + backward) on `images` images
+    of the same workload, single-threaded; neighbour build excluded."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    import oracle as O
+
+    sub = slice(0, images)
+    perm, _, key_idx = O.build_neighbors(case["coords"][sub], cfg.G)
+    q_idx = perm.reshape(images, cfg.C, cfg.cs)
+    args = [case[n][sub] for n in ("q", "k", "v", "do")]
+    scale = 1.0 / math.sqrt(cfg.D)
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        O.attn_fwd_gathered(*args[:3], q_idx, key_idx, scale)
+        O.attn_bwd_gathered(*args, q_idx, key_idx, scale)
+        dt = time.perf_counter() - t0
+    return {
+        "value": images * cfg.N / dt,
+        "unit": "tokens/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": f"{images} of {cfg.B} images ({images * cfg.N} tokens), fp64 gathered "
+                  f"forward+backward, {dt:.1f} s",
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", default="stage1")
+    ap.add_argument("--copies", type=int, default=4, help="rotating input copies")
+    ap.add_argument("--cpu-images", type=int, default=32)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(images shard across GPUs with no communication; see the design notes).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import gathered_local_attention_amd as ca
+    from gen import make_case
+
+    ca._lib.load()
+    case = make_case(args.config)
+    cfg = case["cfg"]
+    scale = 1.0 / math.sqrt(cfg.D)
+    dev = "cuda"
+
+    # rotating copies of the batch, all resident in HBM
+    sets = []
+    for r in range(args.copies):
+        s = {"coords": torch.from_numpy(case["coords"]).to(dev)}
+        for n in ("q", "k", "v", "do"):
+            s[n] = case[n].to(dev)
+        s["perm"] = torch.empty((cfg.B, cfg.N), dtype=torch.int32, device=dev)
+        sets.append(s)
+    bws = torch.empty(ca.build_workspace_bytes(cfg.B, cfg.N, cfg.cs, cfg.k) or 1,
+                      dtype=torch.uint8, device=dev)
+    gws = torch.empty(ca.bwd_workspace_bytes(case["q"].dtype, cfg.B, cfg.N, cfg.H, cfg.D,
+                                             cfg.cs, cfg.nk), dtype=torch.uint8, device=dev)
+
+    def step(s, ev=None):
+        if ev is not None:
+            ev[0].record()
+        perm, nbr, key = ca.build_neighbors(s["coords"], cfg.G, cfg.cs, cfg.k, workspace=bws)
+        if ev is not None:
+            ev[1].record()
+        o, lse = ca.fwd(s["q"], s["k"], s["v"], perm, key, scale)
+        if ev is not None:
+            ev[2].record()
+        dq, dk, dv = ca.bwd(s["q"], s["k"], s["v"], o, s["do"], lse, perm, key, scale,
+                            workspace=gws)
+        if ev is not None:
+            ev[3].record()
+        return dq
+
+    for i in range(args.warmup):
+        step(sets[i % len(sets)])
+    torch.cuda.synchronize()
+
+    # timed region: exactly `steps` steps
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(sets[i % len(sets)])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / args.steps
+
+    # per-entry-point durations (HIP events on the launch stream), same rotation
+    n_ev = min(args.steps, 100)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(n_ev)]
+    torch.cuda.synchronize()
+    for i in range(n_ev):
+        step(sets[i % len(sets)], evs[i])
+    torch.cuda.synchronize()
+    dur = {"build": 0.0, "fwd": 0.0, "bwd": 0.0}
+    for e in evs:
+        dur["build"] += e[0].elapsed_time(e[1])
+        dur["fwd"] += e[1].elapsed_time(e[2])
+        dur["bwd"] += e[2].elapsed_time(e[3])
+    dur = {k: v / n_ev * 1e3 for k, v in dur.items()}   # microseconds
+
+    # warm-cache variant: every step on the same copy
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(sets[0])
+    torch.cuda.synchronize()
+    warm_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+
+    alg = algorithmic(cfg)
+    dom = max(("build", "fwd", "bwd"), key=lambda k: dur[k])
+    achieved = alg[dom]["bytes"] / (dur[dom] * 1e-6) / 1e9
+    fb_us = dur["fwd"] + dur["bwd"]
+    fb_bytes = alg["fwd"]["bytes"] + alg["bwd"]["bytes"]
+    fb_flops = alg["fwd"]["flops"] + alg["bwd"]["flops"]
+    copy_gbps = copy_bandwidth(torch)
+
+    line = {
+        "metric": "cluster-attention fwd+bwd tokens/sec and % of HBM roofline (stage-1 shape)",
+        "value": cfg.tokens / (ms_per_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": {"f32": "f32", "bf16": "bf16", "f16": "f16"}[cfg.dtype],
+        "data": "synthetic",
+        "config": {
+            "workload": f"{cfg.name}: B={cfg.B} images x N={cfg.N} tokens, H={cfg.H}x{cfg.D}, "
+                        f"clusters of {cfg.cs}, {cfg.nk} key slots, {cfg.dtype}; step = "
+                        "neighbour build + forward + backward",
+            "B": cfg.B, "N": cfg.N, "H": cfg.H, "D": cfg.D, "cs": cfg.cs, "nk": cfg.nk,
+            "geometry": cfg.geometry, "seed": cfg.seed, "rotating_copies": args.copies,
+        },
+        "roofline": {
+            "bound": "hbm",
+            "kernel": f"cluster_attn_{dom}" if dom != "build" else "cluster_attn_build_neighbors",
+            "achieved": achieved,
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBPS,
+            "traffic": None,
+            "algorithmic_bytes": alg[dom]["bytes"],
+            "avg_us": dur[dom],
+        },
+        "fwd_bwd": {
+            "us": fb_us,
+            "tokens_per_s": cfg.tokens / (fb_us * 1e-6),
+            "effective_GBps": fb_bytes / (fb_us * 1e-6) / 1e9,
+            "hbm_frac": fb_bytes / (fb_us * 1e-6) / 1e9 / HBM_PEAK_GBPS,
+            "effective_TFLOPs": fb_flops / (fb_us * 1e-6) / 1e12,
+            "mfma_bf16_frac": fb_flops / (fb_us * 1e-6) / 1e12 / BF16_MFMA_PEAK_TFLOPS,
+        },
+        "entry_us": dur,
+        "warm_ms_per_step": warm_ms,
+        "copy_GBps": copy_gbps,
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(cfg, case, min(args.cpu_images, cfg.B))
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,174 @@
+"""Local cluster attention over off-grid tokens on MI355X (gfx950).
+
+Thin Python binding over the C ABI of ``libclusterattn.so`` (declared in
+``include/cluster_attn.h``).  Every step of the computation runs in the HIP
+kernels; this module only checks tensor properties, allocates outputs with
+torch and passes raw device pointers plus the current HIP stream.  There is
+no CPU fallback: if the library is missing, the calls raise.
+
+Functions
+---------
+build_neighbors(coords, grid_side, cs=8, k=6) -> (perm, nbr, key_idx)
+fwd(q, k, v, q_idx, key_idx, scale=None) -> (o, lse)
+bwd(q, k, v, o, do, lse, q_idx, key_idx, scale=None) -> (dq, dk, dv)
+cluster_attention(q, k, v, q_idx, key_idx, scale=None) -> o   (autograd)
+"""
+
+from __future__ import annotations
+
+import math
+
+import torch
+
+from . import _lib
+
+__all__ = [
+    "build_neighbors",
+    "fwd",
+    "bwd",
+    "cluster_attention",
+    "bwd_workspace_bytes",
+    "build_workspace_bytes",
+    "ClusterAttnError",
+    "CA_OK",
+]
+
+CA_OK = 0
+_DT = {torch.float32: 0, torch.bfloat16: 1, torch.float16: 2}
+
+
+class ClusterAttnError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        lib = _lib.load()
+        msg = lib.cluster_attn_status_string(status).decode()
+        detail = lib.cluster_attn_last_error().decode()
+        super().__init__(f"{where}: {msg}" + (f" ({detail})" if detail else ""))
+        self.status = status
+
+
+def _check(status: int, where: str):
+    if status != CA_OK:
+        raise ClusterAttnError(status, where)
+
+
+def _dev(t: torch.Tensor, name: str, dtype=None) -> int:
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    return t.data_ptr()
+
+
+def _stream(t: torch.Tensor) -> int:
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def build_workspace_bytes(B: int, N: int, cs: int = 8, k: int = 6) -> int:
+    return int(_lib.load().cluster_attn_build_neighbors_workspace(B, N, cs, k))
+
+
+def bwd_workspace_bytes(dtype: torch.dtype, B: int, N: int, H: int, D: int = 32, cs: int = 8,
+                        nk: int = 48) -> int:
+    return int(_lib.load().cluster_attn_bwd_workspace(_DT[dtype], B, N, H, D, cs, nk))
+
+
+def build_neighbors(coords: torch.Tensor, grid_side: int, cs: int = 8, k: int = 6,
+                    workspace: torch.Tensor | None = None):
+    """Morton-order balanced clusters and nearest-cluster key lists.
+
+    coords: [B, N, 2] float32 device tensor (x = column, y = row).
+    Returns perm [B, N] (== q_idx [B, C, cs] as a view), nbr [B, C, k] and
+    key_idx [B, C, cs*k], all int32."""
+    lib = _lib.load()
+    B, N, two = coords.shape
+    if two != 2:
+        raise ValueError("coords must be [B, N, 2]")
+    _dev(coords, "coords", torch.float32)
+    C = N // cs if cs else 0
+    perm = torch.empty((B, N), dtype=torch.int32, device=coords.device)
+    nbr = torch.empty((B, C, k), dtype=torch.int32, device=coords.device)
+    key_idx = torch.empty((B, C, cs * k), dtype=torch.int32, device=coords.device)
+    need = lib.cluster_attn_build_neighbors_workspace(B, N, cs, k)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=coords.device)
+    _check(lib.cluster_attn_build_neighbors(
+        coords.data_ptr(), B, N, int(grid_side), cs, k, perm.data_ptr(), nbr.data_ptr(),
+        key_idx.data_ptr(), workspace.data_ptr(), workspace.numel(), _stream(coords)),
+        "cluster_attn_build_neighbors")
+    return perm, nbr, key_idx
+
+
+def _shapes(q, q_idx, key_idx):
+    if q.dim() != 4:
+        raise ValueError("q/k/v must be [B, N, H, D]")
+    B, N, H, D = q.shape
+    if q_idx.dim() == 2:
+        q_idx = q_idx.view(B, -1, 8)
+    cs = q_idx.shape[-1]
+    nk = key_idx.shape[-1]
+    return B, N, H, D, cs, nk, q_idx
+
+
+def fwd(q, k, v, q_idx, key_idx, scale: float | None = None):
+    """Forward: returns O [B, N, H, D] (dtype of q) and LSE [B, N, H] f32."""
+    lib = _lib.load()
+    B, N, H, D, cs, nk, q_idx = _shapes(q, q_idx, key_idx)
+    if q.dtype not in _DT:
+        raise TypeError(f"unsupported dtype {q.dtype}")
+    for t, n in ((k, "k"), (v, "v")):
+        if t.shape != q.shape or t.dtype != q.dtype:
+            raise ValueError(f"{n} must match q in shape and dtype")
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, N, H), dtype=torch.float32, device=q.device)
+    _check(lib.cluster_attn_fwd(
+        _DT[q.dtype], B, N, H, D, cs, nk, scale, _dev(q, "q"), _dev(k, "k"), _dev(v, "v"),
+        _dev(q_idx, "q_idx", torch.int32), _dev(key_idx, "key_idx", torch.int32),
+        o.data_ptr(), lse.data_ptr(), _stream(q)), "cluster_attn_fwd")
+    return o, lse
+
+
+def bwd(q, k, v, o, do, lse, q_idx, key_idx, scale: float | None = None,
+        workspace: torch.Tensor | None = None):
+    """Backward: returns dQ, dK, dV (dtype of q)."""
+    lib = _lib.load()
+    B, N, H, D, cs, nk, q_idx = _shapes(q, q_idx, key_idx)
+    if q.dtype not in _DT:
+        raise TypeError(f"unsupported dtype {q.dtype}")
+    for t, n in ((k, "k"), (v, "v"), (o, "o"), (do, "do")):
+        if t.shape != q.shape or t.dtype != q.dtype:
+            raise ValueError(f"{n} must match q in shape and dtype")
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    dt = _DT[q.dtype]
+    need = lib.cluster_attn_bwd_workspace(dt, B, N, H, D, cs, nk)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+    _check(lib.cluster_attn_bwd(
+        dt, B, N, H, D, cs, nk, scale, _dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(o, "o"),
+        _dev(do, "do"), _dev(lse, "lse", torch.float32), _dev(q_idx, "q_idx", torch.int32),
+        _dev(key_idx, "key_idx", torch.int32), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+        workspace.data_ptr(), workspace.numel(), _stream(q)), "cluster_attn_bwd")
+    return dq, dk, dv
+
+
+class _ClusterAttention(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, q, k, v, q_idx, key_idx, scale):
+        o, lse = fwd(q, k, v, q_idx, key_idx, scale)
+        ctx.save_for_backward(q, k, v, o, lse, q_idx, key_idx)
+        ctx.scale = scale
+        return o
+
+    @staticmethod
+    def backward(ctx, do):
+        q, k, v, o, lse, q_idx, key_idx = ctx.saved_tensors
+        dq, dk, dv = bwd(q, k, v, o, do.contiguous(), lse, q_idx, key_idx, ctx.scale)
+        return dq, dk, dv, None, None, None
+
+
+def cluster_attention(q, k, v, q_idx, key_idx, scale: float | None = None):
+    """Autograd-aware local cluster attention (index lists are constants)."""
+    return _ClusterAttention.apply(q, k, v, q_idx, key_idx, scale)

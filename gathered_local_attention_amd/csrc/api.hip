@@ -1,0 +1,194 @@
+// C ABI of libclusterattn: argument validation and dispatch.
+// Every entry point validates synchronously (no HIP call before validation
+// has passed, so the checks also run on a machine without a GPU), then
+// enqueues its kernels on the caller's stream and returns.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "../../include/cluster_attn.h"
+#include "common.h"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+int fail(int status, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return status;
+}
+
+int ok() {
+  g_last_error[0] = '\0';
+  return CA_OK;
+}
+
+int hip_status(hipError_t e, const char* where) {
+  if (e == hipSuccess) return ok();
+  return fail(CA_ERR_HIP, "%s: %s", where, hipGetErrorString(e));
+}
+
+size_t elem_size(int dt) { return dt == CA_F32 ? 4 : 2; }
+
+struct Range {
+  const void* p;
+  size_t n;
+};
+
+bool overlaps(Range a, Range b) {
+  if (!a.p || !b.p || a.n == 0 || b.n == 0) return false;
+  const uintptr_t a0 = (uintptr_t)a.p, a1 = a0 + a.n;
+  const uintptr_t b0 = (uintptr_t)b.p, b1 = b0 + b.n;
+  return a0 < b1 && b0 < a1;
+}
+
+// outputs must not overlap each other or any input
+int check_alias(const Range* outs, int nout, const Range* ins, int nin) {
+  for (int i = 0; i < nout; ++i) {
+    for (int j = 0; j < nin; ++j)
+      if (overlaps(outs[i], ins[j])) return fail(CA_ERR_ALIAS, "output %d overlaps input %d", i, j);
+    for (int j = i + 1; j < nout; ++j)
+      if (overlaps(outs[i], outs[j])) return fail(CA_ERR_ALIAS, "outputs %d and %d overlap", i, j);
+  }
+  return CA_OK;
+}
+
+constexpr int64_t kMaxTokensPerImage = int64_t(1) << 27;   // cluster ids fit 24 bits
+
+// Shape checks common to fwd and bwd.  Returns CA_OK or an error.
+int check_attn_shape(int dt, int B, int N, int H, int D, int cs, int nk) {
+  if (dt != CA_F32 && dt != CA_BF16 && dt != CA_F16)
+    return fail(CA_ERR_UNSUPPORTED, "dtype %d is not one of CA_F32, CA_BF16, CA_F16", dt);
+  if (B < 0 || N < 0 || H < 1 || D < 1 || cs < 1 || nk < 1)
+    return fail(CA_ERR_SHAPE, "bad sizes B=%d N=%d H=%d D=%d cs=%d nk=%d", B, N, H, D, cs, nk);
+  if (cs != 8) return fail(CA_ERR_UNSUPPORTED, "cluster size %d (only 8 is supported)", cs);
+  if (D != 32) return fail(CA_ERR_UNSUPPORTED, "head dim %d (only 32 is supported)", D);
+  if (nk % cs != 0 || nk / cs > 8)
+    return fail(CA_ERR_UNSUPPORTED, "nk=%d must be cs*k with 1 <= k <= 8", nk);
+  if (N % cs != 0) return fail(CA_ERR_SHAPE, "N=%d is not a multiple of cs=%d", N, cs);
+  if (N > kMaxTokensPerImage) return fail(CA_ERR_SHAPE, "N=%d exceeds 2^27 tokens per image", N);
+  if ((int64_t)B * N * H * D > (int64_t(1) << 40)) return fail(CA_ERR_SHAPE, "tensor too large");
+  return CA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* cluster_attn_version(void) { return "clusterattn 0.1 (gfx950)"; }
+
+const char* cluster_attn_status_string(int s) {
+  switch (s) {
+    case CA_OK: return "CA_OK";
+    case CA_ERR_NULL: return "CA_ERR_NULL: a required pointer is NULL";
+    case CA_ERR_SHAPE: return "CA_ERR_SHAPE: sizes out of range or inconsistent";
+    case CA_ERR_UNSUPPORTED: return "CA_ERR_UNSUPPORTED: request outside the supported set";
+    case CA_ERR_WORKSPACE: return "CA_ERR_WORKSPACE: workspace too small";
+    case CA_ERR_ALIAS: return "CA_ERR_ALIAS: an output overlaps an input or another output";
+    case CA_ERR_HIP: return "CA_ERR_HIP: the HIP runtime reported an error";
+  }
+  return "unknown status";
+}
+
+const char* cluster_attn_last_error(void) { return g_last_error; }
+
+size_t cluster_attn_build_neighbors_workspace(int B, int N, int cs, int k) {
+  if (B < 0 || N < 0 || cs != 8 || k < 1 || k > 8 || N % cs != 0 || N > kMaxTokensPerImage)
+    return 0;
+  return ca::build_layout(nullptr, B, N).bytes;
+}
+
+int cluster_attn_build_neighbors(const float* coords, int B, int N, int grid_side, int cs, int k,
+                                 int32_t* perm, int32_t* nbr, int32_t* key_idx, void* ws,
+                                 size_t ws_bytes, void* hip_stream) {
+  if (B < 0 || N < 0) return fail(CA_ERR_SHAPE, "bad sizes B=%d N=%d", B, N);
+  if (cs != 8) return fail(CA_ERR_UNSUPPORTED, "cluster size %d (only 8 is supported)", cs);
+  if (k < 1 || k > 8) return fail(CA_ERR_UNSUPPORTED, "k=%d outside 1..8", k);
+  if (N % cs != 0) return fail(CA_ERR_SHAPE, "N=%d is not a multiple of cs=%d", N, cs);
+  if (N > kMaxTokensPerImage) return fail(CA_ERR_SHAPE, "N=%d exceeds 2^27 tokens per image", N);
+  if (grid_side < 1 || grid_side > 65536)
+    return fail(CA_ERR_SHAPE, "grid_side=%d outside [1, 65536]", grid_side);
+  if (B == 0 || N == 0) return ok();
+  if (!coords || !perm || !nbr || !key_idx) return fail(CA_ERR_NULL, "NULL tensor pointer");
+  const size_t need = ca::build_layout(nullptr, B, N).bytes;
+  if (need && !ws) return fail(CA_ERR_NULL, "NULL workspace (%zu bytes needed)", need);
+  if (ws_bytes < need) return fail(CA_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
+  const int64_t C = N / cs;
+  Range outs[] = {{perm, (size_t)B * N * 4}, {nbr, (size_t)(B * C * k) * 4},
+                  {key_idx, (size_t)(B * C * k * cs) * 4}, {ws, need}};
+  Range ins[] = {{coords, (size_t)B * N * 8}};
+  if (int s = check_alias(outs, 4, ins, 1)) return s;
+  return hip_status(ca::launch_build_neighbors(coords, B, N, grid_side, k, perm, nbr, key_idx, ws,
+                                               (hipStream_t)hip_stream),
+                    "build_neighbors launch");
+}
+
+int cluster_attn_fwd(int dt, int B, int N, int H, int D, int cs, int nk, float scale,
+                     const void* q, const void* k, const void* v, const int32_t* q_idx,
+                     const int32_t* key_idx, void* o, float* lse, void* hip_stream) {
+  if (int s = check_attn_shape(dt, B, N, H, D, cs, nk)) return s;
+  if (!(scale == scale) || scale == INFINITY || scale == -INFINITY)
+    return fail(CA_ERR_SHAPE, "scale is not finite");
+  if (B == 0 || N == 0) return ok();
+  if (!q || !k || !v || !q_idx || !key_idx || !o || !lse)
+    return fail(CA_ERR_NULL, "NULL tensor pointer");
+  const size_t tb = (size_t)B * N * H * D * elem_size(dt);
+  const int64_t C = N / cs;
+  Range outs[] = {{o, tb}, {lse, (size_t)B * N * H * 4}};
+  Range ins[] = {{q, tb}, {k, tb}, {v, tb}, {q_idx, (size_t)B * N * 4},
+                 {key_idx, (size_t)(B * C * nk) * 4}};
+  if (int s = check_alias(outs, 2, ins, 5)) return s;
+  return hip_status(ca::launch_fwd_valu(dt, B, N, H, nk, scale, q, k, v, q_idx, key_idx, o, lse,
+                                        (hipStream_t)hip_stream),
+                    "fwd launch");
+}
+
+size_t cluster_attn_bwd_workspace(int dt, int B, int N, int H, int D, int cs, int nk) {
+  const char saved = g_last_error[0];
+  if (check_attn_shape(dt, B, N, H, D, cs, nk) != CA_OK) {
+    g_last_error[0] = saved;
+    return 0;
+  }
+  return ca::bwd_layout(nullptr, B, N, H, N / cs, nk).bytes;
+}
+
+int cluster_attn_bwd(int dt, int B, int N, int H, int D, int cs, int nk, float scale,
+                     const void* q, const void* k, const void* v, const void* o,
+                     const void* dout, const float* lse, const int32_t* q_idx,
+                     const int32_t* key_idx, void* dq, void* dk, void* dv, void* ws,
+                     size_t ws_bytes, void* hip_stream) {
+  if (int s = check_attn_shape(dt, B, N, H, D, cs, nk)) return s;
+  if (!(scale == scale) || scale == INFINITY || scale == -INFINITY)
+    return fail(CA_ERR_SHAPE, "scale is not finite");
+  if (B == 0 || N == 0) return ok();
+  if (!q || !k || !v || !o || !dout || !lse || !q_idx || !key_idx || !dq || !dk || !dv)
+    return fail(CA_ERR_NULL, "NULL tensor pointer");
+  const int64_t C = N / cs;
+  const ca::BwdWorkspace need = ca::bwd_layout(nullptr, B, N, H, C, nk);
+  if (!ws) return fail(CA_ERR_NULL, "NULL workspace (%zu bytes needed)", need.bytes);
+  if (ws_bytes < need.bytes)
+    return fail(CA_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need.bytes);
+  const size_t tb = (size_t)B * N * H * D * elem_size(dt);
+  Range outs[] = {{dq, tb}, {dk, tb}, {dv, tb}, {ws, need.bytes}};
+  Range ins[] = {{q, tb},
+                 {k, tb},
+                 {v, tb},
+                 {o, tb},
+                 {dout, tb},
+                 {lse, (size_t)B * N * H * 4},
+                 {q_idx, (size_t)B * N * 4},
+                 {key_idx, (size_t)(B * C * nk) * 4}};
+  if (int s = check_alias(outs, 4, ins, 8)) return s;
+  const ca::BwdWorkspace w = ca::bwd_layout(ws, B, N, H, C, nk);
+  hipStream_t st = (hipStream_t)hip_stream;
+  hipError_t e = ca::launch_bwd_plan(B, N, nk, q_idx, key_idx, w, st);
+  if (e != hipSuccess) return hip_status(e, "bwd plan launch");
+  return hip_status(ca::launch_bwd_valu(dt, B, N, H, nk, scale, q, k, v, o, dout, lse, q_idx,
+                                        key_idx, dq, dk, dv, w, st),
+                    "bwd launch");
+}
+
+}  // extern "C"

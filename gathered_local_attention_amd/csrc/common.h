@@ -1,0 +1,120 @@
+// Internal helpers shared by the HIP translation units of libclusterattn.
+// Not part of the public ABI (see include/cluster_attn.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ca {
+
+// ---- element types -------------------------------------------------------
+// bf16 and fp16 travel as the compiler's native __bf16 / _Float16 types;
+// conversions to and from float are exact (widening) or round-to-nearest-even
+// (narrowing), which is what the outputs promise.
+typedef __bf16 bf16;
+typedef _Float16 f16;
+
+template <typename T> __device__ __forceinline__ float to_f32(T x) { return (float)x; }
+template <typename T> __device__ __forceinline__ T from_f32(float x) { return (T)x; }
+
+// ---- reverse (key-major) slot list entry ---------------------------------
+// One entry per (query cluster i, key cluster j) pair with at least one slot
+// of i's list pointing into j: `mult` holds, byte n, how many slots of i hold
+// the n-th member of j (0..255; a list has at most 64 slots).
+struct RevEntry {
+  int32_t i;
+  int32_t pad;
+  uint64_t mult;
+};
+
+// ---- workspace layout of the backward pass --------------------------------
+struct BwdWorkspace {
+  float* delta;      // [B, N, H]
+  int32_t* inv;      // [B, N]      token -> position in q_idx (c*cs + m)
+  int32_t* cnt;      // [B, C]      entries per key cluster
+  int32_t* off;      // [B, C + 1]  segment starts (per image, relative)
+  int32_t* cursor;   // [B, C]
+  int32_t* nent;     // [B, C]      staged entries per query cluster
+  RevEntry* stage;   // [B, C, nk]  per query cluster, in slot order
+  RevEntry* rev;     // [B, C*nk]   per key cluster, sorted by i
+  size_t bytes;
+};
+
+static inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+static inline BwdWorkspace bwd_layout(void* base, int64_t B, int64_t N, int64_t H, int64_t C,
+                                      int64_t nk) {
+  BwdWorkspace w;
+  size_t p = 0;
+  char* b = (char*)base;
+  auto take = [&](size_t n) {
+    size_t at = p;
+    p = align_up(p + n, 256);
+    return b ? (void*)(b + at) : (void*)nullptr;
+  };
+  w.delta = (float*)take((size_t)(B * N * H) * sizeof(float));
+  w.inv = (int32_t*)take((size_t)(B * N) * sizeof(int32_t));
+  w.cnt = (int32_t*)take((size_t)(B * C) * sizeof(int32_t));
+  w.off = (int32_t*)take((size_t)(B * (C + 1)) * sizeof(int32_t));
+  w.cursor = (int32_t*)take((size_t)(B * C) * sizeof(int32_t));
+  w.nent = (int32_t*)take((size_t)(B * C) * sizeof(int32_t));
+  w.stage = (RevEntry*)take((size_t)(B * C * nk) * sizeof(RevEntry));
+  w.rev = (RevEntry*)take((size_t)(B * C * nk) * sizeof(RevEntry));
+  w.bytes = p;
+  return w;
+}
+
+// ---- workspace layout of the neighbour build ------------------------------
+constexpr int kSortChunk = 2048;   // tokens ranked together in LDS
+
+struct BuildWorkspace {
+  uint32_t* qsorted;   // [B, N]  packed (qx | qy << 16) in cluster order
+  uint64_t* keys;      // [B, N]  sorted (code << 32 | token) per chunk (N > kSortChunk)
+  size_t bytes;
+};
+
+static inline BuildWorkspace build_layout(void* base, int64_t B, int64_t N) {
+  BuildWorkspace w;
+  size_t p = 0;
+  char* b = (char*)base;
+  auto take = [&](size_t n) {
+    size_t at = p;
+    p = align_up(p + n, 256);
+    return b ? (void*)(b + at) : (void*)nullptr;
+  };
+  w.qsorted = (uint32_t*)take((size_t)(B * N) * sizeof(uint32_t));
+  w.keys = (uint64_t*)take(N > kSortChunk ? (size_t)(B * N) * sizeof(uint64_t) : 0);
+  w.bytes = p;
+  return w;
+}
+
+// ---- wave helpers (64-lane wavefronts) ------------------------------------
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o, 64));
+  return x;
+}
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o, 64);
+  return x;
+}
+
+// ---- launchers (defined in the .hip files) ---------------------------------
+hipError_t launch_build_neighbors(const float* coords, int B, int N, int grid_side, int k,
+                                  int32_t* perm, int32_t* nbr, int32_t* key_idx, void* ws,
+                                  hipStream_t st);
+
+hipError_t launch_fwd_valu(int dt, int B, int N, int H, int nk, float scale, const void* q,
+                           const void* k, const void* v, const int32_t* q_idx,
+                           const int32_t* key_idx, void* o, float* lse, hipStream_t st);
+
+hipError_t launch_bwd_plan(int B, int N, int nk, const int32_t* q_idx, const int32_t* key_idx,
+                           const BwdWorkspace& w, hipStream_t st);
+
+hipError_t launch_bwd_valu(int dt, int B, int N, int H, int nk, float scale, const void* q,
+                           const void* k, const void* v, const void* o, const void* dout,
+                           const float* lse, const int32_t* q_idx, const int32_t* key_idx,
+                           void* dq, void* dk, void* dv, const BwdWorkspace& w, hipStream_t st);
+
+}  // namespace ca

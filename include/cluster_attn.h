@@ -1,0 +1,165 @@
+/*
+ * cluster_attn.h - C ABI of the MI355X (gfx950) local cluster attention
+ * library: neighbour-list build, gathered-KV forward, fused backward.
+ *
+ * What it computes.  The English notes page "AFFMAE: Scalable Vision
+ * Pre-Training for High-Resolution Microscopy Segmentation on Desktop
+ * Hardware" (en.papernotes.org), section "Overall Architecture", describes an
+ * encoder in which every token keeps an explicit 2D coordinate and attention
+ * is computed through local balanced clustering; the arXiv abstract of the
+ * same paper (mlsanity.com page of that title) says the attention runs in
+ * numerically stable, mixed-precision, Flash-style kernels, and the notes'
+ * "Limitations & Future Work" name off-grid gather/scatter as the cost and
+ * space-filling curves as the neighbourhood structure.  The pages fix no
+ * interface; the calls below are this library's.  Readings of the open
+ * points: Morton (Z-order, x in even bits) balanced clusters of cs = 8
+ * tokens; each cluster attends to the keys of itself plus its k-1 = 5
+ * nearest clusters by integer centroid-sum distance; plain scaled
+ * dot-product softmax over those 48 key slots; LSE is the natural
+ * log-sum-exp of the scaled logits.
+ *
+ * Conventions shared by every call.
+ *  - Tensor pointers are DEVICE pointers (hipMalloc'd or torch CUDA tensors),
+ *    owned by the caller; the library allocates nothing and keeps no state
+ *    besides its loaded code objects.
+ *  - Layouts are dense row-major.  Q, K, V, O, dO, dQ, dK, dV are
+ *    [B, N, H, D] (token-major, heads inside a token); LSE is [B, N, H] f32.
+ *    Index arrays are int32 and image-local: values in [0, N), -1 = empty
+ *    slot.  A slot repeated in one key list counts once per occurrence.
+ *  - q_idx [B, C, cs] must be a permutation of 0..N-1 per image (C = N/cs):
+ *    it partitions each image's tokens into the query clusters.
+ *  - Every call is asynchronous on `hip_stream` (a hipStream_t; NULL = the
+ *    default stream): it validates its arguments synchronously, enqueues its
+ *    kernels and returns.  Validation failures return before any launch and
+ *    write nothing.  Out-of-range indices are a precondition, not checked.
+ *  - Outputs are fully overwritten (dK and dV are not accumulated into);
+ *    tokens no slot references get dK = dV = 0.  Outputs must not overlap
+ *    inputs (CA_ERR_ALIAS where the ranges are visibly overlapping).
+ *  - Supported set: cs = 8, D = 32, nk = cs*k with 1 <= k <= 8 (the MFMA
+ *    kernels serve nk = 48 in bf16/f16; every other case runs on the
+ *    vector-ALU kernels), H >= 1, N % cs == 0, dtype f32 / bf16 / f16.
+ *    Anything else: CA_ERR_SHAPE or CA_ERR_UNSUPPORTED.
+ *  - No call throws across the ABI.  Launch or runtime failures return
+ *    CA_ERR_HIP; cluster_attn_last_error() gives the text (thread-local).
+ */
+#ifndef CLUSTER_ATTN_H
+#define CLUSTER_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  CA_OK = 0,
+  CA_ERR_NULL = 1,        /* a required pointer is NULL                        */
+  CA_ERR_SHAPE = 2,       /* sizes out of range or inconsistent                */
+  CA_ERR_UNSUPPORTED = 3, /* valid request outside the supported set           */
+  CA_ERR_WORKSPACE = 4,   /* workspace smaller than the *_workspace() query    */
+  CA_ERR_ALIAS = 5,       /* an output overlaps an input or another output     */
+  CA_ERR_HIP = 6          /* the HIP runtime reported an error                 */
+} ca_status;
+
+typedef enum { CA_F32 = 0, CA_BF16 = 1, CA_F16 = 2 } ca_dtype;
+
+/*
+ * Workspace bytes needed by cluster_attn_build_neighbors for these sizes
+ * (0 for invalid sizes).
+ */
+size_t cluster_attn_build_neighbors_workspace(int B, int N, int cs, int k);
+
+/*
+ * Neighbour-list build (notes page, "Overall Architecture": 2D coordinate per
+ * token, local balanced clustering; "Limitations & Future Work": space-filling
+ * curves).  Steps, all exact integer arithmetic after one fp64 quantisation:
+ *   1. q = clamp(floor((c + 0.5) * 2^(16 - ceil(log2 G))), 0, 65535) per axis;
+ *      Morton code with x in the even bits and y in the odd bits.
+ *   2. per image, stable sort of tokens by (code, token index) -> perm;
+ *      cluster c = perm[c*cs .. c*cs+cs-1].
+ *   3. integer centroid sums S_c = sum of the members' (qx, qy).
+ *   4. nbr[c] = c, then the k-1 clusters b != c with the smallest
+ *      ((S_c - S_b)^2 summed over axes, b), ascending; -1 pads if C < k.
+ *   5. key_idx[c][s*cs + m] = perm[nbr[c][s]*cs + m] (-1 where nbr is -1).
+ * Arguments:
+ *   coords    [B, N, 2] f32, (x = column, y = row) in patch units, device.
+ *   grid_side G >= 1, the side of the patch grid the coordinates live on
+ *             (only its ceil(log2) is used; coordinates outside [-0.5, G-0.5)
+ *             clamp).
+ *   cs        cluster size, must be 8.   k: clusters per list, 1..8.
+ *   perm      [B, N] int32 out (== q_idx [B, C, cs]).
+ *   nbr       [B, C, k] int32 out, slot 0 = self.
+ *   key_idx   [B, C, cs*k] int32 out.
+ *   ws        device workspace of at least
+ *             cluster_attn_build_neighbors_workspace(B, N, cs, k) bytes
+ *             (may be NULL when that is 0).  Contents on entry are ignored.
+ * Deterministic: the output is the unique list defined above.
+ */
+int cluster_attn_build_neighbors(const float* coords, int B, int N, int grid_side, int cs, int k,
+                                 int32_t* perm, int32_t* nbr, int32_t* key_idx, void* ws,
+                                 size_t ws_bytes, void* hip_stream);
+
+/*
+ * Forward (notes page "Overall Architecture": local cluster attention; arXiv
+ * abstract: Flash-style kernels).  For every image b, query cluster c and
+ * head h, with K_s = K[b, key_idx[b,c,s], h, :] over the valid slots s:
+ *   S_ms = scale * <Q[b, q_idx[b,c,m], h, :], K_s>
+ *   O    = sum_s exp(S_ms - LSE_m) V_s,  LSE_m = ln sum_s exp(S_ms)
+ * computed with fp32 max/sum statistics and fp32 accumulation (bf16/f16
+ * operands of the matrix products; the softmax probabilities enter the P*V
+ * product as a hi/lo pair so their rounding does not reach O).
+ *   dt        element type of q, k, v and o.
+ *   D         head dim, must be 32.  nk: slots per list (= cs*k).
+ *   scale     logit scale (1/sqrt(D) for the plain reading).
+ *   q, k, v   [B, N, H, D] dt.   q_idx [B, C, cs], key_idx [B, C, nk] int32.
+ *   o         [B, N, H, D] dt out (RNE from fp32).
+ *   lse       [B, N, H] f32 out.  A row whose list has no valid slot gets
+ *             O = 0 and LSE = -inf.
+ */
+int cluster_attn_fwd(int dt, int B, int N, int H, int D, int cs, int nk, float scale,
+                     const void* q, const void* k, const void* v, const int32_t* q_idx,
+                     const int32_t* key_idx, void* o, float* lse, void* hip_stream);
+
+/* Workspace bytes needed by cluster_attn_bwd (0 for invalid sizes). */
+size_t cluster_attn_bwd_workspace(int dt, int B, int N, int H, int D, int cs, int nk);
+
+/*
+ * Backward: gradients of L = sum(dO * O) with the index lists held fixed
+ * (training through the kernels, notes page "Loss & Training").  With P the
+ * forward's probabilities recomputed as exp(S - LSE):
+ *   Delta_m = <dO_m, O_m>;  dP_ms = <dO_m, V_s>;  dS = P * (dP - Delta)
+ *   dQ_m = scale sum_s dS_ms K_s
+ *   dK_j = scale sum over every (cluster, slot) whose key is j of dS Q
+ *   dV_j = sum over the same slots of P dO
+ * Two passes: a query-major pass writes dQ and Delta, a key-major pass over a
+ * transposed slot list (built in the workspace each call) writes dK and dV
+ * directly, so no atomics touch the gradients and the result is bitwise
+ * reproducible.  fp32 accumulation throughout; outputs RNE to dt.
+ *   q, k, v, o, dout [B, N, H, D] dt (o as returned by the forward).
+ *   lse       [B, N, H] f32 from the forward.
+ *   dq, dk, dv [B, N, H, D] dt out.
+ *   ws        device workspace of at least cluster_attn_bwd_workspace(...)
+ *             bytes; contents on entry are ignored.  Two calls that overlap
+ *             in time must not share a workspace.
+ */
+int cluster_attn_bwd(int dt, int B, int N, int H, int D, int cs, int nk, float scale,
+                     const void* q, const void* k, const void* v, const void* o,
+                     const void* dout, const float* lse, const int32_t* q_idx,
+                     const int32_t* key_idx, void* dq, void* dk, void* dv, void* ws,
+                     size_t ws_bytes, void* hip_stream);
+
+/* Static text for a status code. */
+const char* cluster_attn_status_string(int status);
+
+/* Detail of the last error on the calling thread ("" if none). */
+const char* cluster_attn_last_error(void);
+
+/* Library version string. */
+const char* cluster_attn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CLUSTER_ATTN_H */

@@ -1,0 +1,135 @@
+"""CPU checks of the C ABI: the library loads, exports every declared symbol,
+and rejects bad arguments before touching the GPU."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from gathered_local_attention_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "cluster_attn.h")
+
+CA_OK, CA_ERR_NULL, CA_ERR_SHAPE, CA_ERR_UNSUPPORTED, CA_ERR_WORKSPACE, CA_ERR_ALIAS = range(6)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return _lib.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"\b(cluster_attn_\w+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = declared_functions()
+    assert len(names) >= 8
+    for n in names:
+        assert hasattr(lib, n), n
+        assert n in _lib.SIGNATURES, f"binding lacks a signature for {n}"
+
+
+def test_status_strings(lib):
+    for s in range(7):
+        assert lib.cluster_attn_status_string(s).startswith(b"CA_")
+    assert lib.cluster_attn_version().startswith(b"clusterattn")
+
+
+P = 0x10000  # fake, never-dereferenced device pointers (validation fails first)
+
+
+def fwd(lib, dt=1, B=2, N=64, H=2, D=32, cs=8, nk=48, scale=0.17, ptrs=None):
+    p = ptrs or [P * (i + 1) for i in range(7)]
+    return lib.cluster_attn_fwd(dt, B, N, H, D, cs, nk, scale, *p, None)
+
+
+def test_fwd_validation(lib):
+    assert fwd(lib, dt=7) == CA_ERR_UNSUPPORTED
+    assert b"dtype" in lib.cluster_attn_last_error()
+    assert fwd(lib, N=60) == CA_ERR_SHAPE
+    assert fwd(lib, D=64) == CA_ERR_UNSUPPORTED
+    assert fwd(lib, cs=4, nk=24) == CA_ERR_UNSUPPORTED
+    assert fwd(lib, nk=50) == CA_ERR_UNSUPPORTED
+    assert fwd(lib, nk=72) == CA_ERR_UNSUPPORTED
+    assert fwd(lib, H=0) == CA_ERR_SHAPE
+    assert fwd(lib, B=-1) == CA_ERR_SHAPE
+    assert fwd(lib, scale=float("nan")) == CA_ERR_SHAPE
+    assert fwd(lib, ptrs=[P, 2 * P, 3 * P, None, 5 * P, 6 * P, 7 * P]) == CA_ERR_NULL
+    # empty problems are valid no-ops, even with NULL pointers
+    assert fwd(lib, B=0, ptrs=[None] * 7) == CA_OK
+    assert fwd(lib, N=0, ptrs=[None] * 7) == CA_OK
+
+
+def test_fwd_alias_detection(lib):
+    tb = 2 * 64 * 2 * 32 * 2
+    base = 1 << 30
+    q, k, v = base, base + tb, base + 2 * tb
+    qi, ki = base + 3 * tb, base + 4 * tb
+    o = base + 10 * tb
+    lse = base + 20 * tb
+    assert fwd(lib, ptrs=[q, k, v, qi, ki, q + 64, lse]) == CA_ERR_ALIAS        # o over q
+    assert fwd(lib, ptrs=[q, k, v, qi, ki, o, o + 128]) == CA_ERR_ALIAS         # lse over o
+    assert fwd(lib, ptrs=[q, k, v, qi, ki, o, ki]) == CA_ERR_ALIAS              # lse over key_idx
+
+
+def bwd(lib, ws_bytes=1 << 40, ws=P * 40, dt=1, B=2, N=64, H=2, nk=48, ptrs=None):
+    p = ptrs or [P * (i + 1) for i in range(11)]
+    return lib.cluster_attn_bwd(dt, B, N, H, 32, 8, nk, 0.17, *p, ws, ws_bytes, None)
+
+
+def test_bwd_validation_and_workspace(lib):
+    need = lib.cluster_attn_bwd_workspace(1, 2, 64, 2, 32, 8, 48)
+    assert need > 0
+    assert lib.cluster_attn_bwd_workspace(1, 2, 60, 2, 32, 8, 48) == 0
+    assert lib.cluster_attn_bwd_workspace(9, 2, 64, 2, 32, 8, 48) == 0
+    assert bwd(lib, ws_bytes=need - 1) == CA_ERR_WORKSPACE
+    assert bwd(lib, ws=None) == CA_ERR_NULL
+    assert bwd(lib, dt=3) == CA_ERR_UNSUPPORTED
+    assert bwd(lib, N=12) == CA_ERR_SHAPE
+    # dk overlapping the workspace
+    p = [P * (i + 1) for i in range(11)]
+    assert bwd(lib, ws=p[9] + 8, ptrs=p) == CA_ERR_ALIAS
+    assert bwd(lib, B=0, ptrs=[None] * 11, ws=None) == CA_OK
+
+
+def test_workspace_grows_with_problem(lib):
+    a = lib.cluster_attn_bwd_workspace(1, 32, 2048, 4, 32, 8, 48)
+    b = lib.cluster_attn_bwd_workspace(1, 64, 2048, 4, 32, 8, 48)
+    assert b > a > 0
+    assert lib.cluster_attn_build_neighbors_workspace(4, 65536, 8, 6) > \
+        lib.cluster_attn_build_neighbors_workspace(4, 2048, 8, 6) > 0
+
+
+def test_build_validation(lib):
+    def build(B=2, N=64, G=32, cs=8, k=6, ws_bytes=1 << 30, ptrs=None, ws=P * 9):
+        p = ptrs or [P, 2 * P, 3 * P, 4 * P]
+        return lib.cluster_attn_build_neighbors(p[0], B, N, G, cs, k, p[1], p[2], p[3], ws,
+                                                ws_bytes, None)
+    assert build(N=20) == CA_ERR_SHAPE
+    assert build(cs=16) == CA_ERR_UNSUPPORTED
+    assert build(k=0) == CA_ERR_UNSUPPORTED
+    assert build(k=9) == CA_ERR_UNSUPPORTED
+    assert build(G=0) == CA_ERR_SHAPE
+    assert build(G=70000) == CA_ERR_SHAPE
+    assert build(ptrs=[P, None, 3 * P, 4 * P]) == CA_ERR_NULL
+    assert build(ws_bytes=16) == CA_ERR_WORKSPACE
+    assert build(ptrs=[P, 2 * P, 2 * P + 4, 4 * P]) == CA_ERR_ALIAS
+    assert build(B=0, ptrs=[None] * 4, ws=None) == CA_OK
+
+
+def test_missing_library_raises(tmp_path):
+    with pytest.raises(_lib.LibraryMissing):
+        _lib.load(str(tmp_path / "nope.so"))
+
+
+def test_product_path_does_not_import_oracle():
+    pkg = os.path.join(ROOT, "gathered_local_attention_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".h", ".cpp")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert "oracle" not in text.replace("no oracle", ""), f
