@@ -10,30 +10,36 @@
 // Microscopy Segmentation on Desktop Hardware" ("Overall Architecture":
 // local balanced clustering) leaves to the implementation.
 //
-// One workgroup per image, five phases separated by workgroup barriers:
-//   1. inv[token] = position of the token in q_idx; zero the counters.
-//   2. per query cluster i: group its slots by key cluster j (first
-//      occurrence order), stage one entry (i, per-member multiplicities) per
-//      distinct j and count entries per j.
+// plan_small_kernel (images of at most 256 clusters) keeps the whole image
+// in LDS; see its comment.  plan_kernel handles any size:
+// one 1024-thread workgroup per image (every counter it touches belongs to
+// its image, so no global zeroing pass and no cross-workgroup ordering are
+// needed).  Phases, separated by workgroup barriers:
+//   1. inv[token] = position of the token in q_idx (c*cs + m); zero counts.
+//   2. per tile of query clusters: every slot looks up its key cluster
+//      (jn = inv[token], staged in LDS); the first slot of cluster i that
+//      points into key cluster j stages the entry (j, per-member
+//      multiplicities) at its own slot position and counts it for j.
 //   3. exclusive scan of the counts -> segment offsets.
-//   4. scatter the staged entries into their segments.
-//   5. sort every segment by i (the scatter order is not deterministic).
+//   4. staged entries are scattered into their segments (atomic cursor).
+//   5. each segment is sorted by i, which fixes the summation order of the
+//      key-major pass and makes it deterministic.
 #include "common.h"
 
 namespace ca {
 
 namespace {
 
-constexpr int kPlanThreads = 256;
+constexpr int kPlanThreads = 1024;
 constexpr int kMaxNk = 64;
+constexpr int kTileSlots = 12288;   // 48 KiB of LDS: 256 clusters of 48 slots
 
 __global__ void __launch_bounds__(kPlanThreads)
 plan_kernel(int N, int nk, const int32_t* __restrict__ q_idx, const int32_t* __restrict__ key_idx,
             int32_t* __restrict__ inv_all, int32_t* __restrict__ cnt_all,
             int32_t* __restrict__ off_all, int32_t* __restrict__ cur_all,
-            int32_t* __restrict__ nent_all, RevEntry* __restrict__ stage_all,
-            RevEntry* __restrict__ rev_all) {
-  __shared__ int32_t slots[kPlanThreads][kMaxNk + 1];
+            RevEntry* __restrict__ stage_all, RevEntry* __restrict__ rev_all) {
+  __shared__ int32_t jn[kTileSlots];
   __shared__ int32_t scan[kPlanThreads];
   const int b = blockIdx.x;
   const int C = N / 8;
@@ -44,9 +50,9 @@ plan_kernel(int N, int nk, const int32_t* __restrict__ q_idx, const int32_t* __r
   int32_t* cnt = cnt_all + (int64_t)b * C;
   int32_t* off = off_all + (int64_t)b * (C + 1);
   int32_t* cur = cur_all + (int64_t)b * C;
-  int32_t* nent = nent_all + (int64_t)b * C;
   RevEntry* stage = stage_all + (int64_t)b * C * nk;
   RevEntry* rev = rev_all + (int64_t)b * C * nk;
+  const int64_t slots = (int64_t)C * nk;
 
   // 1 (inv starts at -1 so that a q_idx that is not a permutation leaves
   //    unreached tokens marked invalid instead of holding stale values)
@@ -54,44 +60,44 @@ plan_kernel(int N, int nk, const int32_t* __restrict__ q_idx, const int32_t* __r
   for (int j = tid; j < C; j += kPlanThreads) cnt[j] = 0;
   __syncthreads();
   for (int p = tid; p < N; p += kPlanThreads) inv[qi[p]] = p;
-  __threadfence_block();
   __syncthreads();
 
   // 2
-  for (int i0 = 0; i0 < C; i0 += kPlanThreads) {
-    const int i = i0 + tid;
-    if (i < C) {
-      int32_t* my = slots[tid];
-      for (int s = 0; s < nk; ++s) {
-        const int t = ki[(int64_t)i * nk + s];
-        my[s] = t >= 0 ? inv[t] : -1;     // (j << 3) | n
-      }
-      int ne = 0;
-      for (int s = 0; s < nk; ++s) {
-        const int js = my[s];
-        if (js < 0) continue;
-        bool first = true;
-        for (int u = s - 1; u >= 0; --u) {
-          if (my[u] >= 0 && (my[u] >> 3) == (js >> 3)) { first = false; break; }
-        }
-        if (!first) continue;
-        uint64_t mult = 0;
-        for (int u = s; u < nk; ++u) {
-          if (my[u] >= 0 && (my[u] >> 3) == (js >> 3)) mult += 1ull << (8 * (my[u] & 7));
-        }
-        RevEntry e;
-        e.i = js >> 3;      // key cluster while staged
-        e.pad = 0;
-        e.mult = mult;
-        stage[(int64_t)i * nk + ne] = e;
-        ++ne;
-        atomicAdd(&cnt[js >> 3], 1);
-      }
-      nent[i] = ne;
+  const int tile_clusters = kTileSlots / nk;
+  for (int i0 = 0; i0 < C; i0 += tile_clusters) {
+    const int nc = min(tile_clusters, C - i0);
+    const int ns = nc * nk;
+    for (int x = tid; x < ns; x += kPlanThreads) {
+      const int t = ki[(int64_t)i0 * nk + x];
+      jn[x] = t >= 0 ? inv[t] : -1;          // (j << 3) | n
     }
+    __syncthreads();
+    for (int x = tid; x < ns; x += kPlanThreads) {
+      const int il = x / nk, s = x - il * nk;
+      const int* my = jn + il * nk;
+      const int js = my[s];
+      RevEntry e;
+      e.i = -1;
+      e.pad = 0;
+      e.mult = 0;
+      if (js >= 0) {
+        const int j = js >> 3;
+        bool first = true;
+        for (int u = s - 1; u >= 0; --u)
+          if (my[u] >= 0 && (my[u] >> 3) == j) { first = false; break; }
+        if (first) {
+          uint64_t mult = 0;
+          for (int u = s; u < nk; ++u)
+            if (my[u] >= 0 && (my[u] >> 3) == j) mult += 1ull << (8 * (my[u] & 7));
+          e.i = j;   // key cluster while staged
+          e.mult = mult;
+          atomicAdd(&cnt[j], 1);
+        }
+      }
+      stage[(int64_t)i0 * nk + x] = e;
+    }
+    __syncthreads();
   }
-  __threadfence_block();
-  __syncthreads();
 
   // 3
   int carry = 0;
@@ -115,31 +121,26 @@ plan_kernel(int N, int nk, const int32_t* __restrict__ q_idx, const int32_t* __r
     __syncthreads();
   }
   if (tid == 0) off[C] = carry;
-  __threadfence_block();
   __syncthreads();
 
   // 4
-  for (int i = tid; i < C; i += kPlanThreads) {
-    const int ne = nent[i];
-    for (int e = 0; e < ne; ++e) {
-      RevEntry s = stage[(int64_t)i * nk + e];
-      const int j = s.i;
-      const int pos = atomicAdd(&cur[j], 1);
-      RevEntry r;
-      r.i = i;
-      r.pad = 0;
-      r.mult = s.mult;
-      rev[pos] = r;
-    }
+  for (int64_t x = tid; x < slots; x += kPlanThreads) {
+    const RevEntry s = stage[x];
+    if (s.i < 0) continue;
+    const int pos = atomicAdd(&cur[s.i], 1);
+    RevEntry r;
+    r.i = (int32_t)(x / nk);
+    r.pad = 0;
+    r.mult = s.mult;
+    rev[pos] = r;
   }
-  __threadfence_block();
   __syncthreads();
 
   // 5
   for (int j = tid; j < C; j += kPlanThreads) {
     const int a = off[j], z = off[j + 1];
     for (int x = a + 1; x < z; ++x) {
-      RevEntry key = rev[x];
+      const RevEntry key = rev[x];
       int y = x - 1;
       while (y >= a && rev[y].i > key.i) {
         rev[y + 1] = rev[y];
@@ -150,13 +151,146 @@ plan_kernel(int N, int nk, const int32_t* __restrict__ q_idx, const int32_t* __r
   }
 }
 
+// ---------------------------------------------------------------------------
+// Images with at most 256 clusters and 12288 slots.  Every slot does O(1)
+// work: it sets bit i of key cluster j's row in an LDS bitmap (repeated
+// slots set the same bit), segment sizes are row popcounts, the entry of
+// (i, j) sits at off[j] + (set bits of row j below i), and each slot adds its
+// member count into that entry's multiplicity bytes with an integer atomic.
+// Segments come out ordered by i and the sums are order independent, so the
+// result is deterministic without a sort.
+// ---------------------------------------------------------------------------
+constexpr int kPlanMaxC = 256;
+constexpr int kPlanWords = kPlanMaxC / 32;
+
+__global__ void __launch_bounds__(kPlanThreads)
+plan_small_kernel(int N, int nk, const int32_t* __restrict__ q_idx,
+                  const int32_t* __restrict__ key_idx, int32_t* __restrict__ off_all,
+                  RevEntry* __restrict__ rev_all) {
+  __shared__ int32_t inv[kSortChunk];
+  __shared__ uint32_t bits[kPlanMaxC][kPlanWords];
+  __shared__ int32_t off[kPlanMaxC + 1];
+  __shared__ int32_t tmp[17];
+  const int b = blockIdx.x;
+  const int C = N / 8;
+  const int tid = threadIdx.x;
+  const int ns = C * nk;
+  const int32_t* qi = q_idx + (int64_t)b * N;
+  const int32_t* ki = key_idx + (int64_t)b * ns;
+  constexpr int kPer = kTileSlots / kPlanThreads;   // 12 slots per thread
+
+  // this thread's slots x = tid + r * 1024 (r < kPer), loaded up front
+  int tok[kPer];
+#pragma unroll
+  for (int r = 0; r < kPer; ++r) {
+    const int x = tid + r * kPlanThreads;
+    tok[r] = x < ns ? ki[x] : -1;
+  }
+  const int q0 = tid < N ? qi[tid] : -1;                       // N <= 2048
+  const int q1 = tid + kPlanThreads < N ? qi[tid + kPlanThreads] : -1;
+  for (int t = tid; t < N; t += kPlanThreads) inv[t] = -1;
+  for (int x = tid; x < kPlanMaxC * kPlanWords; x += kPlanThreads) (&bits[0][0])[x] = 0u;
+  __syncthreads();
+  if (q0 >= 0) inv[q0] = tid;
+  if (q1 >= 0) inv[q1] = tid + kPlanThreads;
+  __syncthreads();
+
+  int jn[kPer], ii[kPer];
+#pragma unroll
+  for (int r = 0; r < kPer; ++r) {
+    const int x = tid + r * kPlanThreads;
+    jn[r] = tok[r] >= 0 ? inv[tok[r]] : -1;        // (j << 3) | n
+    ii[r] = x / nk;
+    if (jn[r] >= 0) atomicOr(&bits[jn[r] >> 3][ii[r] >> 5], 1u << (ii[r] & 31));
+  }
+  __syncthreads();
+
+  // segment sizes and offsets (exclusive scan over j < C <= 256 < threads)
+  int v = 0;
+  if (tid < C) {
+#pragma unroll
+    for (int w = 0; w < kPlanWords; ++w) v += __popc(bits[tid][w]);
+  }
+  int total;
+  const int ex = block_exclusive_scan(v, tmp, kPlanThreads, &total);
+  if (tid < C) off[tid] = ex;
+  if (tid == 0) off[C] = total;
+  int32_t* goff = off_all + (int64_t)b * (C + 1);
+  if (tid <= C) goff[tid] = tid < C ? ex : total;
+  __syncthreads();
+
+  // entries: i from the bitmap, multiplicities accumulated below
+  RevEntry* rev = rev_all + (int64_t)b * ns;
+  for (int j = tid; j < C; j += kPlanThreads) {
+    int pos = off[j];
+    for (int w = 0; w < kPlanWords; ++w) {
+      uint32_t m = bits[j][w];
+      while (m) {
+        const int i = 32 * w + __ffs(m) - 1;
+        m &= m - 1;
+        RevEntry e;
+        e.i = i;
+        e.pad = 0;
+        e.mult = 0;
+        rev[pos++] = e;
+      }
+    }
+  }
+  // workgroup scope suffices (every entry of this image is written and
+  // updated by this workgroup); a device-scope fence would write back L2
+  __threadfence_block();
+  __syncthreads();
+  // Slot x and lane share x mod 8, and nk is a multiple of 8, so every
+  // aligned group of 8 lanes holds one slot group of one cluster; when all 8
+  // point into the same entry (the usual case) their member counts are
+  // summed with lane shuffles and a single atomic is issued.
+  const int lane = tid & 63;
+#pragma unroll
+  for (int r = 0; r < kPer; ++r) {
+    int pos = -1;
+    uint64_t add = 0;
+    if (jn[r] >= 0) {
+      const int j = jn[r] >> 3, i = ii[r];
+      pos = off[j];
+      for (int w = 0; w < (i >> 5); ++w) pos += __popc(bits[j][w]);
+      pos += __popc(bits[j][i >> 5] & ((1u << (i & 31)) - 1u));
+      add = 1ull << (8 * (jn[r] & 7));
+    }
+    bool same = true;
+    uint64_t sum = add;
+#pragma unroll
+    for (int o = 1; o < 8; o <<= 1) {
+      const int po = __shfl_xor(pos, o, 64);
+      same = same && (po == pos);
+      sum += __shfl_xor(sum, o, 64);
+    }
+    // butterfly AND: every lane of the group ends with the same verdict
+    int all_same = same ? 1 : 0;
+#pragma unroll
+    for (int o = 1; o < 8; o <<= 1) all_same &= __shfl_xor(all_same, o, 64);
+    if (pos < 0) continue;
+    if (all_same) {
+      if ((lane & 7) == 0)
+        atomicAdd(reinterpret_cast<unsigned long long*>(&rev[pos].mult), sum);
+    } else {
+      atomicAdd(reinterpret_cast<unsigned long long*>(&rev[pos].mult), add);
+    }
+  }
+}
+
 }  // namespace
 
 hipError_t launch_bwd_plan(int B, int N, int nk, const int32_t* q_idx, const int32_t* key_idx,
                            const BwdWorkspace& w, hipStream_t st) {
   if (nk > kMaxNk) return hipErrorInvalidValue;
+  const int C = N / 8;
+  if (N <= kSortChunk && C <= kPlanMaxC && C * nk <= kTileSlots) {   // <= 12 slots per thread
+    hipLaunchKernelGGL(plan_small_kernel, dim3(B), dim3(kPlanThreads), 0, st, N, nk, q_idx, key_idx,
+                       w.off, w.rev);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL(plan_kernel, dim3(B), dim3(kPlanThreads), 0, st, N, nk, q_idx, key_idx,
-                     w.inv, w.cnt, w.off, w.cursor, w.nent, w.stage, w.rev);
+                     w.inv, w.cnt, w.off, w.cursor, w.stage, w.rev);
   return hipGetLastError();
 }
 

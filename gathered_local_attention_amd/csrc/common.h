@@ -34,8 +34,7 @@ struct BwdWorkspace {
   int32_t* cnt;      // [B, C]      entries per key cluster
   int32_t* off;      // [B, C + 1]  segment starts (per image, relative)
   int32_t* cursor;   // [B, C]
-  int32_t* nent;     // [B, C]      staged entries per query cluster
-  RevEntry* stage;   // [B, C, nk]  per query cluster, in slot order
+  RevEntry* stage;   // [B, C, nk]  entry of the first slot of i pointing into j
   RevEntry* rev;     // [B, C*nk]   per key cluster, sorted by i
   size_t bytes;
 };
@@ -57,7 +56,6 @@ static inline BwdWorkspace bwd_layout(void* base, int64_t B, int64_t N, int64_t 
   w.cnt = (int32_t*)take((size_t)(B * C) * sizeof(int32_t));
   w.off = (int32_t*)take((size_t)(B * (C + 1)) * sizeof(int32_t));
   w.cursor = (int32_t*)take((size_t)(B * C) * sizeof(int32_t));
-  w.nent = (int32_t*)take((size_t)(B * C) * sizeof(int32_t));
   w.stage = (RevEntry*)take((size_t)(B * C * nk) * sizeof(RevEntry));
   w.rev = (RevEntry*)take((size_t)(B * C * nk) * sizeof(RevEntry));
   w.bytes = p;
@@ -66,10 +64,12 @@ static inline BwdWorkspace bwd_layout(void* base, int64_t B, int64_t N, int64_t 
 
 // ---- workspace layout of the neighbour build ------------------------------
 constexpr int kSortChunk = 2048;   // tokens ranked together in LDS
+constexpr int kSelectTile = 1024;  // candidate centroids staged per LDS tile
 
 struct BuildWorkspace {
   uint32_t* qsorted;   // [B, N]  packed (qx | qy << 16) in cluster order
   uint64_t* keys;      // [B, N]  sorted (code << 32 | token) per chunk (N > kSortChunk)
+  float2* cent;        // [B, C]  centroid sums (C > kSelectTile)
   size_t bytes;
 };
 
@@ -82,8 +82,9 @@ static inline BuildWorkspace build_layout(void* base, int64_t B, int64_t N) {
     p = align_up(p + n, 256);
     return b ? (void*)(b + at) : (void*)nullptr;
   };
-  w.qsorted = (uint32_t*)take((size_t)(B * N) * sizeof(uint32_t));
+  w.qsorted = (uint32_t*)take(N > kSortChunk ? (size_t)(B * N) * sizeof(uint32_t) : 0);
   w.keys = (uint64_t*)take(N > kSortChunk ? (size_t)(B * N) * sizeof(uint64_t) : 0);
+  w.cent = (float2*)take(N / 8 > kSelectTile ? (size_t)(B * (N / 8)) * sizeof(float2) : 0);
   w.bytes = p;
   return w;
 }
@@ -100,6 +101,37 @@ __device__ __forceinline__ float wave_sum(float x) {
   return x;
 }
 
+// Inclusive prefix sum across the 64 lanes of a wavefront.
+__device__ __forceinline__ int wave_inclusive_scan(int v) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(v, o, 64);
+    if (lane >= o) v += y;
+  }
+  return v;
+}
+
+// Exclusive prefix sum of one value per thread over a workgroup of
+// `nthreads` (a multiple of 64, at most 1024) with two barriers; `tmp` is
+// 16 ints of LDS.  Returns the exclusive prefix and writes the total.
+__device__ __forceinline__ int block_exclusive_scan(int v, int* tmp, int nthreads, int* total) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int inc = wave_inclusive_scan(v);
+  if (lane == 63) tmp[w] = inc;
+  __syncthreads();
+  if (w == 0) {
+    const int nw = nthreads >> 6;
+    const int t = lane < nw ? tmp[lane] : 0;
+    const int ti = wave_inclusive_scan(t);
+    if (lane < nw) tmp[lane] = ti - t;
+    if (lane == nw - 1) tmp[16 + 0] = ti;
+  }
+  __syncthreads();
+  *total = tmp[16];
+  return tmp[w] + inc - v;
+}
+
 // ---- launchers (defined in the .hip files) ---------------------------------
 hipError_t launch_build_neighbors(const float* coords, int B, int N, int grid_side, int k,
                                   int32_t* perm, int32_t* nbr, int32_t* key_idx, void* ws,
@@ -113,6 +145,17 @@ hipError_t launch_bwd_plan(int B, int N, int nk, const int32_t* q_idx, const int
                            const BwdWorkspace& w, hipStream_t st);
 
 hipError_t launch_bwd_valu(int dt, int B, int N, int H, int nk, float scale, const void* q,
+                           const void* k, const void* v, const void* o, const void* dout,
+                           const float* lse, const int32_t* q_idx, const int32_t* key_idx,
+                           void* dq, void* dk, void* dv, const BwdWorkspace& w, hipStream_t st);
+
+bool mfma_supported(int dt, int nk);
+
+hipError_t launch_fwd_mfma(int dt, int B, int N, int H, float scale, const void* q, const void* k,
+                           const void* v, const int32_t* q_idx, const int32_t* key_idx, void* o,
+                           float* lse, hipStream_t st);
+
+hipError_t launch_bwd_mfma(int dt, int B, int N, int H, int nk, float scale, const void* q,
                            const void* k, const void* v, const void* o, const void* dout,
                            const float* lse, const int32_t* q_idx, const int32_t* key_idx,
                            void* dq, void* dk, void* dv, const BwdWorkspace& w, hipStream_t st);

@@ -10,19 +10,22 @@
 // token index), and each cluster's list = itself plus the k-1 clusters with
 // the nearest integer centroid sums (ties by cluster index).
 //
-// Kernels (all integer after one exact fp64 quantisation):
-//   rank_kernel    per segment (an image, or a 2048-token chunk of a large
-//                  image): every token's rank among the segment's
-//                  (code, token) keys, counted against the whole segment
-//                  held in LDS.  Writes perm / packed coordinates directly
-//                  when the segment is the whole image, else the chunk's
-//                  keys in sorted order.
-//   merge_kernel   large images only: a token's image-wide rank is its rank
-//                  in its own chunk plus, for every other chunk, the number of
-//                  keys below it (binary search over that chunk staged in LDS).
-//   select_kernel  per cluster: brute-force scan of all clusters of the image
-//                  (candidate centroids staged in LDS tiles), keeping the k-1
-//                  smallest (d2 << 24 | index) keys; then the key lists.
+// Kernels (all integer after one exact fp64 quantisation; candidate
+// distances are screened in fp32 with a bound that never drops a tie):
+//   build_small_kernel  images of at most 2048 tokens: the whole build in one
+//                       1024-thread workgroup per image (counting sort of the
+//                       (code, token) keys on the top code bits plus in-bucket
+//                       insertion sort, bitonic fallback; centroid sums
+//                       decoded from the sorted codes; 4-lane split scan).
+//   rank_kernel         larger images: rank of every token inside its
+//                       2048-token chunk (keys held in LDS).
+//   merge_kernel        image-wide rank = rank in the own chunk plus, for every
+//                       other chunk, the number of keys below it (binary search
+//                       over that chunk staged in LDS).
+//   centroid_kernel     integer centroid sums when they exceed one LDS tile.
+//   select_kernel       per cluster: scan of all clusters of the image in LDS
+//                       tiles, keeping the k-1 smallest (d2 << 24 | index)
+//                       keys; then the key lists.
 #include "common.h"
 
 namespace ca {
@@ -30,8 +33,7 @@ namespace ca {
 namespace {
 
 constexpr int kRankThreads = 256;
-constexpr int kSelectThreads = 256;
-constexpr int kSelectTile = 1024;
+constexpr int kSelectThreads = 64;
 
 __device__ __forceinline__ uint32_t spread16(uint32_t v) {
   v &= 0xFFFFu;
@@ -50,13 +52,16 @@ __device__ __forceinline__ uint32_t quantize_axis(float c, double step) {
   return (uint32_t)q;
 }
 
-// Rank the tokens of one segment.  grid = (ceil(L / 256), segments), where a
-// segment is [seg_start, seg_start + L) of image `b`.
+// Rank the tokens of one segment.  grid = (ceil(L / 64), segments), where a
+// segment is [seg_start, seg_start + L) of image `b`.  Each workgroup ranks
+// 64 tokens (one per lane); its four wavefronts each count one quarter of
+// the segment's keys, read from LDS as broadcast 16-byte loads.
 __global__ void __launch_bounds__(kRankThreads)
 rank_kernel(const float* __restrict__ coords, int N, int seg_len, int segs_per_image, double step,
             int32_t* __restrict__ perm, uint32_t* __restrict__ qsorted,
             uint64_t* __restrict__ chunk_keys) {
-  __shared__ uint64_t keys[kSortChunk];
+  __shared__ __align__(16) uint64_t keys[kSortChunk];
+  __shared__ int part[kRankThreads / 64][64];
   const int seg = blockIdx.y;
   const int b = seg / segs_per_image;
   const int start = (seg % segs_per_image) * seg_len;
@@ -68,17 +73,26 @@ rank_kernel(const float* __restrict__ coords, int N, int seg_len, int segs_per_i
     uint32_t code = spread16(quantize_axis(c.x, step)) | (spread16(quantize_axis(c.y, step)) << 1);
     keys[e] = ((uint64_t)code << 32) | (uint32_t)(start + e);
   }
+  if (threadIdx.x == 0 && (L & 1)) keys[L] = ~0ull;   // pad to an even count
   __syncthreads();
 
-  const int e = blockIdx.x * kRankThreads + threadIdx.x;
-  if (e >= L) return;
-  const uint64_t mine = keys[e];
-  int rank = 0;
-  int u = 0;
-  for (; u + 4 <= L; u += 4) {
-    rank += (keys[u] < mine) + (keys[u + 1] < mine) + (keys[u + 2] < mine) + (keys[u + 3] < mine);
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int e = blockIdx.x * 64 + lane;
+  const uint64_t mine = e < L ? keys[e] : ~0ull;
+  const int Le = (L + 1) & ~1;                        // even, padding key is the maximum
+  const int per = ((Le / 4) + 1) & ~1;
+  const int u0 = min(Le, w * per), u1 = (w == 3) ? Le : min(Le, (w + 1) * per);
+  int cnt = 0;
+  const ulonglong2* k2 = reinterpret_cast<const ulonglong2*>(keys);
+#pragma unroll 8
+  for (int u = u0; u < u1; u += 2) {
+    const ulonglong2 kk = k2[u >> 1];
+    cnt += (kk.x < mine) + (kk.y < mine);
   }
-  for (; u < L; ++u) rank += (keys[u] < mine);
+  part[w][lane] = cnt;
+  __syncthreads();
+  if (w != 0 || e >= L) return;
+  const int rank = part[0][lane] + part[1][lane] + part[2][lane] + part[3][lane];
 
   if (segs_per_image == 1) {
     const int64_t at = (int64_t)b * N + rank;
@@ -145,55 +159,77 @@ merge_kernel(const float* __restrict__ coords, int N, double step,
   }
 }
 
-__device__ __forceinline__ int2 centroid_sum(const uint32_t* __restrict__ q8) {
+__device__ __forceinline__ float2 centroid_sum(const uint32_t* __restrict__ q8) {
+  // integer sums of eight 16-bit coordinates (< 2^19): exact as floats
+  const uint4 a = *reinterpret_cast<const uint4*>(q8);
+  const uint4 c = *reinterpret_cast<const uint4*>(q8 + 4);
+  const uint32_t w[8] = {a.x, a.y, a.z, a.w, c.x, c.y, c.z, c.w};
   int sx = 0, sy = 0;
 #pragma unroll
   for (int m = 0; m < 8; ++m) {
-    uint32_t p = q8[m];
-    sx += (int)(p & 0xFFFFu);
-    sy += (int)(p >> 16);
+    sx += (int)(w[m] & 0xFFFFu);
+    sy += (int)(w[m] >> 16);
   }
-  return make_int2(sx, sy);
+  return make_float2((float)sx, (float)sy);
 }
 
-// Nearest clusters and key lists.  grid = (ceil(C / 256), B).
+// Centroid sums of every cluster (used when an image has more clusters than
+// one LDS tile).  grid = (ceil(B*C / 256)).
+__global__ void __launch_bounds__(256)
+centroid_kernel(int64_t n_clusters, const uint32_t* __restrict__ qsorted, float2* __restrict__ cent) {
+  const int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (c < n_clusters) cent[c] = centroid_sum(qsorted + 8 * c);
+}
+
+// Nearest clusters and key lists.  grid = (ceil(C / 64), B), one thread per
+// cluster.  Candidates are screened with an fp32 distance whose error bound
+// (relative 2^-23) cannot drop a candidate at or below the current k-1-th
+// best; survivors are compared exactly as (d2 << 24 | index) in 64 bits.
 template <int KM1>
 __global__ void __launch_bounds__(kSelectThreads)
-select_kernel(int N, const uint32_t* __restrict__ qsorted, const int32_t* __restrict__ perm,
-              int32_t* __restrict__ nbr, int32_t* __restrict__ key_idx) {
-  __shared__ int2 cand[kSelectTile];
+select_kernel(int N, const uint32_t* __restrict__ qsorted, const float2* __restrict__ cent_all,
+              const int32_t* __restrict__ perm, int32_t* __restrict__ nbr,
+              int32_t* __restrict__ key_idx) {
+  __shared__ float2 cand[kSelectTile];
   const int C = N / 8;
   const int b = blockIdx.y;
   const int c = blockIdx.x * kSelectThreads + threadIdx.x;
   const uint32_t* qimg = qsorted + (int64_t)b * N;
-  const int2 me = c < C ? centroid_sum(qimg + 8 * c) : make_int2(0, 0);
+  const float2* cent = cent_all ? cent_all + (int64_t)b * C : nullptr;
+  const float2 me = c < C ? (cent ? cent[c] : centroid_sum(qimg + 8 * c)) : make_float2(0.f, 0.f);
 
-  uint64_t best[KM1 > 0 ? KM1 : 1];
+  constexpr int KB = KM1 > 0 ? KM1 : 1;
+  uint64_t best[KB];
 #pragma unroll
-  for (int r = 0; r < (KM1 > 0 ? KM1 : 1); ++r) best[r] = ~0ull;
+  for (int r = 0; r < KB; ++r) best[r] = ~0ull;
+  float thr = INFINITY;
 
   for (int t0 = 0; t0 < C; t0 += kSelectTile) {
     const int T = min(kSelectTile, C - t0);
     __syncthreads();
-    for (int e = threadIdx.x; e < T; e += kSelectThreads) cand[e] = centroid_sum(qimg + 8 * (t0 + e));
+    for (int e = threadIdx.x; e < T; e += kSelectThreads)
+      cand[e] = cent ? cent[t0 + e] : centroid_sum(qimg + 8 * (t0 + e));
     __syncthreads();
     if constexpr (KM1 > 0) {
-    if (c >= C) continue;
-    for (int e = 0; e < T; ++e) {
-      const int2 s = cand[e];
-      const int64_t dx = s.x - me.x, dy = s.y - me.y;
-      const uint64_t key = ((uint64_t)(dx * dx + dy * dy) << 24) | (uint32_t)(t0 + e);
-      if (t0 + e == c || key >= best[KM1 - 1]) continue;
-      // insertion into the sorted top list
-      uint64_t x = key;
+      if (c < C) {
+        for (int e = 0; e < T; ++e) {
+          const float dx = cand[e].x - me.x, dy = cand[e].y - me.y;   // exact
+          const float d2f = fmaf(dx, dx, dy * dy);
+          if (d2f > thr || t0 + e == c) continue;
+          const int64_t ix = (int64_t)dx, iy = (int64_t)dy;
+          const uint64_t key = ((uint64_t)(ix * ix + iy * iy) << 24) | (uint32_t)(t0 + e);
+          if (key >= best[KM1 - 1]) continue;
+          uint64_t x = key;
 #pragma unroll
-      for (int r = 0; r < KM1; ++r) {
-        const uint64_t lo = x < best[r] ? x : best[r];
-        const uint64_t hi = x < best[r] ? best[r] : x;
-        best[r] = lo;
-        x = hi;
+          for (int r = 0; r < KM1; ++r) {
+            const uint64_t lo = x < best[r] ? x : best[r];
+            const uint64_t hi = x < best[r] ? best[r] : x;
+            best[r] = lo;
+            x = hi;
+          }
+          if (best[KM1 - 1] != ~0ull) thr = (float)(best[KM1 - 1] >> 24) * (1.0f + 0x1p-20f);
+        }
       }
-    }
     }
   }
   if (c >= C) return;
@@ -204,13 +240,231 @@ select_kernel(int N, const uint32_t* __restrict__ qsorted, const int32_t* __rest
 #pragma unroll
   for (int r = 0; r < KM1; ++r) ids[r + 1] = best[r] == ~0ull ? -1 : (int32_t)(best[r] & 0xFFFFFFu);
   int32_t* nrow = nbr + ((int64_t)b * C + c) * K;
-  int32_t* krow = key_idx + ((int64_t)b * C + c) * K * 8;
-  const int32_t* pimg = perm + (int64_t)b * N;
+  int4* krow = reinterpret_cast<int4*>(key_idx + ((int64_t)b * C + c) * K * 8);
+  const int4* pimg = reinterpret_cast<const int4*>(perm + (int64_t)b * N);
+  const int4 none = make_int4(-1, -1, -1, -1);
 #pragma unroll
   for (int s = 0; s < K; ++s) {
     nrow[s] = ids[s];
+    krow[2 * s] = ids[s] >= 0 ? pimg[2 * ids[s]] : none;
+    krow[2 * s + 1] = ids[s] >= 0 ? pimg[2 * ids[s] + 1] : none;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Whole build for an image of at most 2048 tokens in one 1024-thread
+// workgroup, everything staged in LDS: (code, token) keys are sorted with a
+// bitonic network (one compare-exchange per thread per stage), the cluster
+// centroid sums are decoded from the sorted codes, and each cluster's
+// candidate scan is split over 4 lanes whose top lists are merged with
+// lane shuffles.  grid = B.
+// ---------------------------------------------------------------------------
+constexpr int kSmallThreads = 1024;
+constexpr int kSmallLanes = 4;                 // lanes per cluster in the scan
+constexpr int kSmallMaxC = kSortChunk / 8;     // 256 clusters
+
+__device__ __forceinline__ uint32_t compact16(uint32_t v) {
+  v &= 0x55555555u;
+  v = (v | (v >> 1)) & 0x33333333u;
+  v = (v | (v >> 2)) & 0x0F0F0F0Fu;
+  v = (v | (v >> 4)) & 0x00FF00FFu;
+  v = (v | (v >> 8)) & 0x0000FFFFu;
+  return v;
+}
+
+constexpr int kBuckets = 2 * kSmallThreads;       // counting-sort buckets (top 11 code bits)
+constexpr int kBucketShift = 21;
+constexpr int kMaxBucket = 32;                    // larger buckets -> bitonic fallback
+
+template <int KM1>
+__device__ __forceinline__ void top_insert(uint64_t (&best)[KM1 > 0 ? KM1 : 1], uint64_t x) {
+  if constexpr (KM1 > 0) {
+    if (x >= best[KM1 - 1]) return;
 #pragma unroll
-    for (int m = 0; m < 8; ++m) krow[s * 8 + m] = ids[s] >= 0 ? pimg[ids[s] * 8 + m] : -1;
+    for (int r = 0; r < KM1; ++r) {
+      const uint64_t lo = x < best[r] ? x : best[r];
+      const uint64_t hi = x < best[r] ? best[r] : x;
+      best[r] = lo;
+      x = hi;
+    }
+  }
+}
+
+template <int KM1>
+__global__ void __launch_bounds__(kSmallThreads)
+build_small_kernel(const float* __restrict__ coords, int N, double step, int32_t* __restrict__ perm,
+                   int32_t* __restrict__ nbr, int32_t* __restrict__ key_idx) {
+  __shared__ uint64_t keys[kSortChunk];
+  __shared__ int bcnt[kBuckets];
+  __shared__ int bstart[kBuckets];
+  __shared__ float2 cent[kSmallMaxC];
+  __shared__ int scan_tmp[17];
+  __shared__ int overflow;
+  const int b = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int C = N / 8;
+  const float2* xy = reinterpret_cast<const float2*>(coords) + (int64_t)b * N;
+
+  // Sort the (code << 32 | token) keys.  Counting sort on the top 11 code
+  // bits (2048 buckets; two keys per thread), then an insertion sort inside
+  // each bucket restores the exact (code, token) order whatever the arrival
+  // order of the atomics.  Buckets hold about one key for the grid-like
+  // layouts of the workloads; if any bucket exceeds kMaxBucket keys the
+  // workgroup falls back to an LDS bitonic sort.
+  uint64_t kk[2];
+  int bk[2], arr[2];
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+    const int e = tid + r * kSmallThreads;
+    kk[r] = ~0ull;
+    bk[r] = -1;
+    if (e < N) {
+      const float2 c = xy[e];
+      const uint32_t code = spread16(quantize_axis(c.x, step)) | (spread16(quantize_axis(c.y, step)) << 1);
+      kk[r] = ((uint64_t)code << 32) | (uint32_t)e;
+      bk[r] = (int)(code >> kBucketShift);
+    }
+  }
+  bcnt[tid] = 0;
+  bcnt[tid + kSmallThreads] = 0;
+  if (tid == 0) overflow = 0;
+  __syncthreads();
+#pragma unroll
+  for (int r = 0; r < 2; ++r) arr[r] = bk[r] >= 0 ? atomicAdd(&bcnt[bk[r]], 1) : 0;
+  __syncthreads();
+  const int c0 = bcnt[2 * tid], c1 = bcnt[2 * tid + 1];
+  if (c0 > kMaxBucket || c1 > kMaxBucket) overflow = 1;
+  int total;
+  const int ex = block_exclusive_scan(c0 + c1, scan_tmp, kSmallThreads, &total);
+  bstart[2 * tid] = ex;
+  bstart[2 * tid + 1] = ex + c0;
+  __syncthreads();
+  if (!overflow) {
+#pragma unroll
+    for (int r = 0; r < 2; ++r)
+      if (bk[r] >= 0) keys[bstart[bk[r]] + arr[r]] = kk[r];
+    __syncthreads();
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int s0 = h ? ex + c0 : ex, n = h ? c1 : c0;
+      for (int x = 1; x < n; ++x) {
+        const uint64_t key = keys[s0 + x];
+        int y = x - 1;
+        while (y >= 0 && keys[s0 + y] > key) {
+          keys[s0 + y + 1] = keys[s0 + y];
+          --y;
+        }
+        keys[s0 + y + 1] = key;
+      }
+    }
+  } else {
+    int P = 2;
+    while (P < N) P <<= 1;
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      const int e = tid + r * kSmallThreads;
+      if (e < P) keys[e] = kk[r];
+    }
+    __syncthreads();
+    for (int k = 2; k <= P; k <<= 1) {
+      for (int j = k >> 1; j > 0; j >>= 1) {
+        for (int i = tid; i < P / 2; i += kSmallThreads) {
+          const int a = ((i & ~(j - 1)) << 1) | (i & (j - 1));
+          const uint64_t x = keys[a], y = keys[a + j];
+          if ((x > y) == ((a & k) == 0)) {
+            keys[a] = y;
+            keys[a + j] = x;
+          }
+        }
+        __syncthreads();
+      }
+    }
+  }
+  __syncthreads();
+
+  // centroid sums decoded from the sorted codes
+  for (int c = tid; c < C; c += kSmallThreads) {
+    int sx = 0, sy = 0;
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+      const uint32_t code = (uint32_t)(keys[8 * c + m] >> 32);
+      sx += (int)compact16(code);
+      sy += (int)compact16(code >> 1);
+    }
+    cent[c] = make_float2((float)sx, (float)sy);
+  }
+  int32_t* pimg = perm + (int64_t)b * N;
+  for (int e = tid; e < N; e += kSmallThreads) pimg[e] = (int32_t)(uint32_t)keys[e];
+  __syncthreads();
+
+  // candidate scan: cluster c = tid / 4, lane part q scans candidates q, q+4, ...
+  constexpr int KB = KM1 > 0 ? KM1 : 1;
+  const int q = tid & (kSmallLanes - 1);
+  const int c = tid / kSmallLanes;
+  uint64_t best[KB];
+#pragma unroll
+  for (int r = 0; r < KB; ++r) best[r] = ~0ull;
+  if constexpr (KM1 > 0) {
+    if (c < C) {
+      const float2 me = cent[c];
+      float thr = INFINITY;
+      constexpr int U = 4;   // candidates read per iteration (independent LDS loads)
+      for (int e0 = q; e0 < C; e0 += U * kSmallLanes) {
+        float dx[U], dy[U], d2f[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int e = e0 + u * kSmallLanes;
+          const float2 cc = cent[e < C ? e : c];
+          dx[u] = cc.x - me.x;   // exact: integer sums below 2^20
+          dy[u] = cc.y - me.y;
+          d2f[u] = fmaf(dx[u], dx[u], dy[u] * dy[u]);
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int e = e0 + u * kSmallLanes;
+          if (e >= C || e == c || d2f[u] > thr) continue;   // thr may be +inf
+          const int64_t ix = (int64_t)dx[u], iy = (int64_t)dy[u];
+          top_insert<KM1>(best, ((uint64_t)(ix * ix + iy * iy) << 24) | (uint32_t)e);
+          if (best[KM1 - 1] != ~0ull) thr = (float)(best[KM1 - 1] >> 24) * (1.0f + 0x1p-20f);
+        }
+      }
+    }
+    // merge the four partial lists (lanes tid^1, tid^2 share the cluster)
+#pragma unroll
+    for (int o = 1; o < kSmallLanes; o <<= 1) {
+      uint64_t other[KB];
+#pragma unroll
+      for (int r = 0; r < KB; ++r) other[r] = __shfl_xor(best[r], o, 64);
+#pragma unroll
+      for (int r = 0; r < KB; ++r) top_insert<KM1>(best, other[r]);
+    }
+  }
+  if (c >= C) return;
+
+  constexpr int K = KM1 + 1;
+  int32_t ids[K];
+  ids[0] = c;
+#pragma unroll
+  for (int r = 0; r < KM1; ++r) ids[r + 1] = best[r] == ~0ull ? -1 : (int32_t)(best[r] & 0xFFFFFFu);
+  if (q == 0) {
+#pragma unroll
+    for (int s = 0; s < K; ++s) nbr[((int64_t)b * C + c) * K + s] = ids[s];
+  }
+  // each of the 4 lanes writes every 4th slot group of the key list
+  int4* krow = reinterpret_cast<int4*>(key_idx + ((int64_t)b * C + c) * K * 8);
+#pragma unroll
+  for (int s = 0; s < K; ++s) {
+    if ((s & (kSmallLanes - 1)) != q) continue;
+    int4 lo = make_int4(-1, -1, -1, -1), hi = lo;
+    if (ids[s] >= 0) {
+      const int base = 8 * ids[s];
+      lo = make_int4((int)(uint32_t)keys[base], (int)(uint32_t)keys[base + 1],
+                     (int)(uint32_t)keys[base + 2], (int)(uint32_t)keys[base + 3]);
+      hi = make_int4((int)(uint32_t)keys[base + 4], (int)(uint32_t)keys[base + 5],
+                     (int)(uint32_t)keys[base + 6], (int)(uint32_t)keys[base + 7]);
+    }
+    krow[2 * s] = lo;
+    krow[2 * s + 1] = hi;
   }
 }
 
@@ -225,23 +479,39 @@ hipError_t launch_build_neighbors(const float* coords, int B, int N, int grid_si
   BuildWorkspace w = build_layout(ws, B, N);
   const int C = N / 8;
   if (N <= kSortChunk) {
-    dim3 grid((N + kRankThreads - 1) / kRankThreads, B);
-    hipLaunchKernelGGL(rank_kernel, grid, dim3(kRankThreads), 0, st, coords, N, N, 1, step, perm,
-                       w.qsorted, (uint64_t*)nullptr);
-  } else {
-    const int chunks = (N + kSortChunk - 1) / kSortChunk;
-    dim3 grid(kSortChunk / kRankThreads, B * chunks);
-    hipLaunchKernelGGL(rank_kernel, grid, dim3(kRankThreads), 0, st, coords, N, kSortChunk, chunks,
-                       step, perm, w.qsorted, w.keys);
-    hipLaunchKernelGGL(merge_kernel, dim3(chunks, B), dim3(kRankThreads), 0, st, coords, N, step,
-                       (const uint64_t*)w.keys, perm, w.qsorted);
+    switch (k) {
+#define CA_SMALL(KK)                                                                            \
+  case KK:                                                                                      \
+    hipLaunchKernelGGL(build_small_kernel<KK - 1>, dim3(B), dim3(kSmallThreads), 0, st, coords, \
+                       N, step, perm, nbr, key_idx);                                            \
+    break;
+      CA_SMALL(1) CA_SMALL(2) CA_SMALL(3) CA_SMALL(4) CA_SMALL(5) CA_SMALL(6) CA_SMALL(7) CA_SMALL(8)
+#undef CA_SMALL
+      default:
+        return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+  }
+  // larger images: chunk ranks, image-wide merge, centroids, tiled selection
+  const int chunks = (N + kSortChunk - 1) / kSortChunk;
+  hipLaunchKernelGGL(rank_kernel, dim3(kSortChunk / 64, B * chunks), dim3(kRankThreads), 0, st,
+                     coords, N, kSortChunk, chunks, step, perm, w.qsorted, w.keys);
+  hipLaunchKernelGGL(merge_kernel, dim3(chunks, B), dim3(kRankThreads), 0, st, coords, N, step,
+                     (const uint64_t*)w.keys, perm, w.qsorted);
+  float2* cent = nullptr;
+  if (C > kSelectTile) {
+    cent = w.cent;
+    const int64_t nc = (int64_t)B * C;
+    hipLaunchKernelGGL(centroid_kernel, dim3((unsigned)((nc + 255) / 256)), dim3(256), 0, st, nc,
+                       (const uint32_t*)w.qsorted, cent);
   }
   dim3 sgrid((C + kSelectThreads - 1) / kSelectThreads, B);
   switch (k) {
 #define CA_SEL(KK)                                                                              \
   case KK:                                                                                      \
     hipLaunchKernelGGL(select_kernel<KK - 1>, sgrid, dim3(kSelectThreads), 0, st, N,            \
-                       (const uint32_t*)w.qsorted, (const int32_t*)perm, nbr, key_idx);         \
+                       (const uint32_t*)w.qsorted, (const float2*)cent, (const int32_t*)perm,  \
+                       nbr, key_idx);                                                           \
     break;
     CA_SEL(1) CA_SEL(2) CA_SEL(3) CA_SEL(4) CA_SEL(5) CA_SEL(6) CA_SEL(7) CA_SEL(8)
 #undef CA_SEL
