@@ -29,6 +29,8 @@ HIPCC_FLAGS = [
     "-Wno-unused-function",
     # Packed fp32 VALU ops are kept off for every kernel.
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA results go to VGPRs directly (no accumulation-register copies).
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
 ]
 
 

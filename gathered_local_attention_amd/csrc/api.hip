@@ -142,7 +142,7 @@ int cluster_attn_fwd(int dt, int B, int N, int H, int D, int cs, int nk, float s
                  {key_idx, (size_t)(B * C * nk) * 4}};
   if (int s = check_alias(outs, 2, ins, 5)) return s;
   hipStream_t st = (hipStream_t)hip_stream;
-  if (ca::mfma_supported(dt, nk))
+  if (ca::mfma_supported(dt, B, N, H, nk))
     return hip_status(ca::launch_fwd_mfma(dt, B, N, H, scale, q, k, v, q_idx, key_idx, o, lse, st),
                       "fwd launch");
   return hip_status(ca::launch_fwd_valu(dt, B, N, H, nk, scale, q, k, v, q_idx, key_idx, o, lse, st),
@@ -189,7 +189,7 @@ int cluster_attn_bwd(int dt, int B, int N, int H, int D, int cs, int nk, float s
   hipStream_t st = (hipStream_t)hip_stream;
   hipError_t e = ca::launch_bwd_plan(B, N, nk, q_idx, key_idx, w, st);
   if (e != hipSuccess) return hip_status(e, "bwd plan launch");
-  if (ca::mfma_supported(dt, nk))
+  if (ca::mfma_supported(dt, B, N, H, nk))
     return hip_status(ca::launch_bwd_mfma(dt, B, N, H, nk, scale, q, k, v, o, dout, lse, q_idx,
                                           key_idx, dq, dk, dv, w, st),
                       "bwd launch");

@@ -108,7 +108,7 @@ bwd_q_valu_kernel(int N, int H, int nk, float scale, const T* __restrict__ q,
                   const T* __restrict__ k, const T* __restrict__ v, const T* __restrict__ o,
                   const T* __restrict__ dout, const float* __restrict__ lse,
                   const int32_t* __restrict__ q_idx, const int32_t* __restrict__ key_idx,
-                  T* __restrict__ dq, float* __restrict__ delta) {
+                  T* __restrict__ dq, float2* __restrict__ ld) {
   __shared__ float qs[CS][kPad];
   __shared__ float dos[CS][kPad];
   __shared__ float ks[64][kPad];
@@ -146,7 +146,7 @@ bwd_q_valu_kernel(int N, int H, int nk, float scale, const T* __restrict__ q,
     if (g == 0) {
       dels[m] = part;
       lses[m] = lse[(img + qt[m]) * H + h];
-      delta[(img + qt[m]) * H + h] = part;
+      ld[(img + qt[m]) * H + h] = make_float2(lses[m] * 1.4426950408889634f, part);
     }
   }
   if (t >= 0) {
@@ -192,7 +192,7 @@ __global__ void __launch_bounds__(64)
 bwd_kv_valu_kernel(int N, int H, int nk, float scale, const T* __restrict__ q,
                    const T* __restrict__ k, const T* __restrict__ v, const T* __restrict__ dout,
                    const float* __restrict__ lse, const int32_t* __restrict__ q_idx,
-                   const float* __restrict__ delta, const int32_t* __restrict__ off_all,
+                   const float2* __restrict__ ld, const int32_t* __restrict__ off_all,
                    const RevEntry* __restrict__ rev_all, T* __restrict__ dk, T* __restrict__ dv) {
   __shared__ float kj[CS][kPad];
   __shared__ float vj[CS][kPad];
@@ -239,7 +239,7 @@ bwd_kv_valu_kernel(int N, int H, int nk, float scale, const T* __restrict__ q,
       }
       if (lo == 0) {
         lses[hi] = lse[(img + qtok) * H + h];
-        dels[hi] = delta[(img + qtok) * H + h];
+        dels[hi] = ld[(img + qtok) * H + h].y;
       }
     }
     __syncthreads();
@@ -298,10 +298,10 @@ hipError_t bwd_t(int B, int N, int H, int nk, float scale, const void* q, const 
   const int64_t blocks = (int64_t)B * (N / CS) * H;
   hipLaunchKernelGGL(bwd_q_valu_kernel<T>, dim3((unsigned)blocks), dim3(64), 0, st, N, H, nk,
                      scale, (const T*)q, (const T*)k, (const T*)v, (const T*)o, (const T*)dout, lse,
-                     q_idx, key_idx, (T*)dq, w.delta);
+                     q_idx, key_idx, (T*)dq, w.ld);
   hipLaunchKernelGGL(bwd_kv_valu_kernel<T>, dim3((unsigned)blocks), dim3(64), 0, st, N, H, nk,
                      scale, (const T*)q, (const T*)k, (const T*)v, (const T*)dout, lse, q_idx,
-                     (const float*)w.delta, (const int32_t*)w.off, (const RevEntry*)w.rev, (T*)dk,
+                     (const float2*)w.ld, (const int32_t*)w.off, (const RevEntry*)w.rev, (T*)dk,
                      (T*)dv);
   return hipGetLastError();
 }

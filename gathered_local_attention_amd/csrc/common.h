@@ -29,7 +29,7 @@ struct RevEntry {
 
 // ---- workspace layout of the backward pass --------------------------------
 struct BwdWorkspace {
-  float* delta;      // [B, N, H]
+  float2* ld;        // [B, N, H]   (LSE * log2(e), Delta) per query and head
   int32_t* inv;      // [B, N]      token -> position in q_idx (c*cs + m)
   int32_t* cnt;      // [B, C]      entries per key cluster
   int32_t* off;      // [B, C + 1]  segment starts (per image, relative)
@@ -51,7 +51,7 @@ static inline BwdWorkspace bwd_layout(void* base, int64_t B, int64_t N, int64_t 
     p = align_up(p + n, 256);
     return b ? (void*)(b + at) : (void*)nullptr;
   };
-  w.delta = (float*)take((size_t)(B * N * H) * sizeof(float));
+  w.ld = (float2*)take((size_t)(B * N * H) * sizeof(float2));
   w.inv = (int32_t*)take((size_t)(B * N) * sizeof(int32_t));
   w.cnt = (int32_t*)take((size_t)(B * C) * sizeof(int32_t));
   w.off = (int32_t*)take((size_t)(B * (C + 1)) * sizeof(int32_t));
@@ -149,7 +149,7 @@ hipError_t launch_bwd_valu(int dt, int B, int N, int H, int nk, float scale, con
                            const float* lse, const int32_t* q_idx, const int32_t* key_idx,
                            void* dq, void* dk, void* dv, const BwdWorkspace& w, hipStream_t st);
 
-bool mfma_supported(int dt, int nk);
+bool mfma_supported(int dt, int B, int N, int H, int nk);
 
 hipError_t launch_fwd_mfma(int dt, int B, int N, int H, float scale, const void* q, const void* k,
                            const void* v, const int32_t* q_idx, const int32_t* key_idx, void* o,

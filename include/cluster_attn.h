@@ -65,8 +65,9 @@ typedef enum {
 typedef enum { CA_F32 = 0, CA_BF16 = 1, CA_F16 = 2 } ca_dtype;
 
 /*
- * Workspace bytes needed by cluster_attn_build_neighbors for these sizes
- * (0 for invalid sizes).
+ * Workspace bytes needed by cluster_attn_build_neighbors for these sizes.
+ * 0 for invalid sizes, and also for valid ones with N <= 2048: such an image
+ * is built by one workgroup entirely in LDS and needs no workspace.
  */
 size_t cluster_attn_build_neighbors_workspace(int B, int N, int cs, int k);
 

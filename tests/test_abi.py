@@ -100,8 +100,10 @@ def test_workspace_grows_with_problem(lib):
     a = lib.cluster_attn_bwd_workspace(1, 32, 2048, 4, 32, 8, 48)
     b = lib.cluster_attn_bwd_workspace(1, 64, 2048, 4, 32, 8, 48)
     assert b > a > 0
+    # An image of at most 2048 tokens is built in one workgroup's LDS.
+    assert lib.cluster_attn_build_neighbors_workspace(4, 2048, 8, 6) == 0
     assert lib.cluster_attn_build_neighbors_workspace(4, 65536, 8, 6) > \
-        lib.cluster_attn_build_neighbors_workspace(4, 2048, 8, 6) > 0
+        lib.cluster_attn_build_neighbors_workspace(4, 4096, 8, 6) > 0
 
 
 def test_build_validation(lib):
@@ -116,7 +118,8 @@ def test_build_validation(lib):
     assert build(G=0) == CA_ERR_SHAPE
     assert build(G=70000) == CA_ERR_SHAPE
     assert build(ptrs=[P, None, 3 * P, 4 * P]) == CA_ERR_NULL
-    assert build(ws_bytes=16) == CA_ERR_WORKSPACE
+    assert build(N=4096, ws_bytes=16) == CA_ERR_WORKSPACE
+    assert build(N=4096, ws=None) == CA_ERR_NULL
     assert build(ptrs=[P, 2 * P, 2 * P + 4, 4 * P]) == CA_ERR_ALIAS
     assert build(B=0, ptrs=[None] * 4, ws=None) == CA_OK
 
