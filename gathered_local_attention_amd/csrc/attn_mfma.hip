@@ -164,123 +164,114 @@ __device__ __forceinline__ int wave_item() {
 // ---------------------------------------------------------------------------
 // forward
 // ---------------------------------------------------------------------------
-// A wavefront walks `ipw` consecutive items (cluster, head pair) as a
-// software pipeline: the indices of item t+2 and the gathered rows of item
-// t+1 are in flight while item t is computed, so the two dependent memory
-// round trips (list, then rows) overlap the math of earlier items.
-struct FwdIdx {
-  int bc, h0;        // wave-uniform
-  int kt[3];         // key token of A-row c16 in each 16-slot block
-  int qtok;          // query token of column c16
-};
-
+// One wavefront per item (cluster, head pair); a wavefront walks `ipw`
+// consecutive items.  Per item: 6 MFMAs for S^T = K Q^T (block-diagonal over
+// the two heads), the softmax on 12 logits per lane, 12 MFMAs transposing V,
+// 8 MFMAs for O^T = V^T P^T with one accumulator set per head (so neither
+// operand needs zeroed columns).  When all 48 slots of the list are valid
+// (the usual case) the masking is skipped by a wave-uniform branch.
 template <typename T>
-struct FwdData {
-  uint4 qv;
-  uint4 ka[3][2], va[3][2];
-  uint32_t valid[3];
-};
-
-__device__ __forceinline__ void fwd_load_idx(int item, int HP, const int32_t* __restrict__ q_idx,
-                                             const int32_t* __restrict__ key_idx, int c16,
-                                             FwdIdx& x) {
-  x.bc = item / HP;
-  x.h0 = 2 * (item - x.bc * HP);
-#pragma unroll
-  for (int b = 0; b < 3; ++b) x.kt[b] = key_idx[x.bc * NK + 16 * b + c16];
-  x.qtok = q_idx[x.bc * CS + (c16 & 7)];
-}
-
-template <typename T>
-__device__ __forceinline__ void fwd_load_rows(const FwdIdx& x, int N, int H, const T* __restrict__ q,
-                                              const T* __restrict__ k, const T* __restrict__ v,
-                                              int c16, int g, FwdData<T>& d) {
-  const int img = x.bc / (N / CS) * N;
+__device__ __forceinline__ void fwd_item(int item, int N, int H, int HP, float scale_log2,
+                                         const T* __restrict__ q, const T* __restrict__ k,
+                                         const T* __restrict__ v,
+                                         const int32_t* __restrict__ q_idx,
+                                         const int32_t* __restrict__ key_idx,
+                                         const uint4 (&id)[2], int c16, int g,
+                                         T* __restrict__ o, float* __restrict__ lse) {
+  const int bc = item / HP;
+  const int h0 = 2 * (item - bc * HP);
+  const int img = bc / (N / CS) * N;
   const bool left = c16 < 8;
-  const int hq = left ? x.h0 : x.h0 + 1;
-  const bool h1ok = x.h0 + 1 < H;
-  const uint4 zero = make_uint4(0u, 0u, 0u, 0u);
-  const uint32_t lo16 = 16u * g;
-  d.qv = (hq < H) ? ld16(q, (uint32_t)((img + x.qtok) * H + hq) * kRow + lo16) : zero;
-#pragma unroll
-  for (int b = 0; b < 3; ++b) {
-    d.valid[b] = (uint32_t)__ballot(x.kt[b] >= 0) & 0xFFFFu;
-    const uint32_t r = (uint32_t)((img + max(x.kt[b], 0)) * H + x.h0) * kRow + lo16;
-    d.ka[b][0] = ld16(k, r);
-    d.va[b][0] = ld16(v, r);
-    d.ka[b][1] = h1ok ? ld16(k, r + kRow) : zero;
-    d.va[b][1] = h1ok ? ld16(v, r + kRow) : zero;
-  }
-}
-
-template <typename T>
-__device__ __forceinline__ void fwd_compute(const FwdIdx& x, const FwdData<T>& d, int N, int H,
-                                            float scale_log2, const uint4 (&id)[2], int c16, int g,
-                                            T* __restrict__ o, float* __restrict__ lse) {
-  const int img = x.bc / (N / CS) * N;
-  const bool left = c16 < 8;
-  const int h0 = x.h0, hq = left ? h0 : h0 + 1;
+  const int hq = left ? h0 : h0 + 1;
   const bool h1ok = h0 + 1 < H;
+  const uint32_t lo16 = 16u * g;
 
-  // S^T = K Q^T, lane holds keys 16b+4g+i of column c16
-  const uint4 qL = sel(left, d.qv), qR = sel(!left, d.qv);
-  const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-  float xs[3][4];
-  float mx = -INFINITY;
+  int kt[3];
+#pragma unroll
+  for (int b = 0; b < 3; ++b) kt[b] = key_idx[bc * NK + 16 * b + c16];
+  const int qtok = q_idx[bc * CS + (c16 & 7)];
+  // With an odd head count the last pair has no second head: its rows are
+  // then re-read from the first head (finite values; the columns they feed
+  // are never stored and the second head's V product is skipped).
+  const uint32_t h1off = h1ok ? kRow : 0u;
+  const uint32_t qrow = (uint32_t)((img + qtok) * H + h0) * kRow + (left ? 0u : h1off);
+  const uint4 qv = ld16(q, qrow + lo16);
+  uint32_t valid = 0xFFFFFFFFu;
+  uint4 ka[3][2], va[3][2];
 #pragma unroll
   for (int b = 0; b < 3; ++b) {
-    f32x4 s = Mfma<T>::mma(d.ka[b][0], qL, z);
-    if (h1ok) s = Mfma<T>::mma(d.ka[b][1], qR, s);
+    valid &= (uint32_t)__ballot(kt[b] >= 0) | 0xFFFF0000u;
+    const uint32_t r = (uint32_t)((img + max(kt[b], 0)) * H + h0) * kRow + lo16;
+    ka[b][0] = ld16(k, r);
+    va[b][0] = ld16(v, r);
+    ka[b][1] = ld16(k, r + h1off);
+    va[b][1] = ld16(v, r + h1off);
+  }
+
+  // S^T = K Q^T: lane holds keys 16b+4g+i of column c16 (query c16&7, head hq)
+  const uint4 qL = sel(left, qv), qR = sel(!left, qv);
+  const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+  f32x4 s[3];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      xs[b][i] = ((d.valid[b] >> (4 * g + i)) & 1u) ? s[i] * scale_log2 : -INFINITY;
-      mx = fmaxf(mx, xs[b][i]);
+  for (int b = 0; b < 3; ++b) {
+    s[b] = Mfma<T>::mma(ka[b][0], qL, z);
+    s[b] = Mfma<T>::mma(ka[b][1], qR, s[b]);
+  }
+  if (valid != 0xFFFFFFFFu) {   // some slot of this list is empty: mask it
+#pragma unroll
+    for (int b = 0; b < 3; ++b) {
+      const uint32_t vb = (uint32_t)__ballot(kt[b] >= 0);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (!((vb >> (4 * g + i)) & 1u)) s[b][i] = -INFINITY;
     }
   }
+  float mx = fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3]));
+#pragma unroll
+  for (int b = 1; b < 3; ++b)
+    mx = fmaxf(mx, fmaxf(fmaxf(s[b][0], s[b][1]), fmaxf(s[b][2], s[b][3])));
   mx = shfl_max16_32(mx);
-  const float mref = mx == -INFINITY ? 0.f : mx;
+  // logits in log2 units; a column with no valid slot keeps mx = -inf
+  const float mref = mx == -INFINITY ? 0.f : mx * scale_log2;
   float l = 0.f;
+  float p[3][4];
 #pragma unroll
   for (int b = 0; b < 3; ++b)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      xs[b][i] = __builtin_amdgcn_exp2f(xs[b][i] - mref);
-      l += xs[b][i];
+      p[b][i] = __builtin_amdgcn_exp2f(fmaf(s[b][i], scale_log2, -mref));
+      l += p[b][i];
     }
   l = shfl_sum16_32(l);
 
-  // P as B operands over keys: step 0 = blocks 0,1 (32 keys), step 1 = block 2
-  uint2 ph[3], pl[3];
+  // P^T as B operands over keys: step 0 = blocks 0,1 (32 keys), step 1 = block 2
+  uint2 ph[3];
 #pragma unroll
-  for (int b = 0; b < 3; ++b) split4<T>(xs[b], ph[b], pl[b]);
+  for (int b = 0; b < 3; ++b) ph[b] = make_uint2(pack2<T>(p[b][0], p[b][1]), pack2<T>(p[b][2], p[b][3]));
+  const uint4 bp0 = cat(ph[0], ph[1]), bp1 = pad(ph[2]);
 
-  // V^T tiles via the selection matrix, then O^T = V^T P^T
-  f32x4 oacc[2] = {z, z};
+  // O^T = V^T P^T per head; the lane keeps the accumulator of its own head
+  f32x4 oacc[2][2] = {{z, z}, {z, z}};
 #pragma unroll
   for (int hh = 0; hh < 2; ++hh) {
     if (hh == 1 && !h1ok) break;
-    const bool mine = (hh == 0) == left;   // this head's columns
     uint2 vt[3][2];
 #pragma unroll
-    for (int b = 0; b < 3; ++b) transpose_rows<T>(d.va[b][hh], id, vt[b]);
-    const uint4 b0h = sel(mine, cat(ph[0], ph[1])), b0l = sel(mine, cat(pl[0], pl[1]));
-    const uint4 b1h = sel(mine, pad(ph[2])), b1l = sel(mine, pad(pl[2]));
+    for (int b = 0; b < 3; ++b) transpose_rows<T>(va[b][hh], id, vt[b]);
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf) {
-      const uint4 a01 = cat(vt[0][hf], vt[1][hf]), a2 = pad(vt[2][hf]);
-      oacc[hf] = Mfma<T>::mma(a01, b0h, oacc[hf]);
-      oacc[hf] = Mfma<T>::mma(a2, b1h, oacc[hf]);
-      oacc[hf] = Mfma<T>::mma(a01, b0l, oacc[hf]);
-      oacc[hf] = Mfma<T>::mma(a2, b1l, oacc[hf]);
+      oacc[hh][hf] = Mfma<T>::mma(cat(vt[0][hf], vt[1][hf]), bp0, oacc[hh][hf]);
+      oacc[hh][hf] = Mfma<T>::mma(pad(vt[2][hf]), bp1, oacc[hh][hf]);
     }
   }
 
   if (hq >= H) return;
   const float inv = l > 0.f ? 1.f / l : 0.f;
-  const uint32_t orow = (uint32_t)((img + x.qtok) * H + hq) * kRow + 8u * g;
+  const uint32_t orow = qrow + 8u * g;
 #pragma unroll
-  for (int hf = 0; hf < 2; ++hf) stv<uint2>(o, orow + 32u * hf, pack4<T>(oacc[hf] * inv));
-  if (g == 0) lse[(img + x.qtok) * H + hq] = l > 0.f ? (mx + __log2f(l)) * kLn2 : -INFINITY;
+  for (int hf = 0; hf < 2; ++hf)
+    stv<uint2>(o, orow + 32u * hf, pack4<T>((left ? oacc[0][hf] : oacc[1][hf]) * inv));
+  if (g == 0) lse[(img + qtok) * H + hq] = l > 0.f ? (mref + __log2f(l)) * kLn2 : -INFINITY;
 }
 
 template <typename T>
@@ -297,21 +288,306 @@ fwd_mfma_kernel(int N, int H, int HP, int n_items, int ipw, float scale_log2,
   uint4 id[2];
   id[0] = selector<T>(g, c16, 0);
   id[1] = selector<T>(g, c16, 1);
+  for (int it = first; it < last; ++it)
+    fwd_item<T>(it, N, H, HP, scale_log2, q, k, v, q_idx, key_idx, id, c16, g, o, lse);
+}
 
-  FwdIdx xi, xn, xnn;
-  FwdData<T> di, dn;
-  fwd_load_idx(first, HP, q_idx, key_idx, c16, xi);
-  fwd_load_rows<T>(xi, N, H, q, k, v, c16, g, di);
-  if (first + 1 < last) fwd_load_idx(first + 1, HP, q_idx, key_idx, c16, xn);
+// ---------------------------------------------------------------------------
+// forward, LDS-staged gathers
+// ---------------------------------------------------------------------------
+// The gathered K and V rows of an item go to a wavefront-private LDS tile
+// with direct-to-LDS 16-byte loads: eight consecutive lanes fetch the 128
+// contiguous bytes of one slot's head pair, so every load instruction reads
+// whole rows.  K is then read back in the MFMA A layout (ds_read_b128) and V
+// transposed (ds_read_b64_tr_b16), which replaces the selection-matrix
+// transposes.  Chunk c (16 bytes) of slot s sits at position c ^ F(s) with
+// F(s) = (s & 15) >> 1, so that the 16 lanes of one K read hit 16 different
+// bank groups.
+constexpr int kSlotBytes = 2 * kRow;            // one slot: both heads of the pair
+constexpr int kTileBytes = NK * kSlotBytes;     // 6 KiB per tensor
+constexpr int kWaveLds = 2 * kTileBytes;        // K and V
+
+typedef __attribute__((address_space(3))) void lds_void;
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+__device__ __forceinline__ uint32_t swz(int s) { return (uint32_t)((s & 15) >> 1); }
+
+__device__ __forceinline__ uint4 lds16(const char* base, uint32_t off) {
+  return *reinterpret_cast<const uint4*>(base + off);
+}
+__device__ __forceinline__ uint2 lds_tr8(const char* base, uint32_t off) {
+  const s16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_s16x4*)((__attribute__((address_space(3))) char*)(base + off)));
+  return __builtin_bit_cast(uint2, r);
+}
+
+// One 16-byte direct-to-LDS load per lane: global (base + voff) -> LDS
+// (lds + 16 * lane), lds wave-uniform.  Written as asm with no outputs so that
+// the compiler does not guard every later LDS read with a full vmcnt wait;
+// the kernels wait for these loads themselves with s_waitcnt vmcnt(n), which
+// counts them in issue order together with every other vector-memory op.
+__device__ __forceinline__ void dma16(const void* base, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
+               :
+               : "v"(voff), "s"(base), "s"(lds)
+               : "memory", "m0");
+}
+
+// s_waitcnt with vmcnt = N (0..63) and no wait on the other counters
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
+}
+
+// Direct-to-LDS 4-byte load per lane: global (base + voff) -> LDS (lds + 4 * lane).
+__device__ __forceinline__ void dma4(const void* base, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dword %0, %1"
+               :
+               : "v"(voff), "s"(base), "s"(lds)
+               : "memory", "m0");
+}
+
+// s_waitcnt vmcnt(n) for a run-time n from the few values the pipelines use
+// (a larger count is never required: any n' <= n is safe, only slower)
+__device__ __forceinline__ void wait_vm_n(int n) {
+  if (n >= 11) wait_vm<11>();
+  else if (n >= 9) wait_vm<9>();
+  else if (n >= 8) wait_vm<8>();
+  else if (n >= 6) wait_vm<6>();
+  else if (n >= 5) wait_vm<5>();
+  else if (n >= 3) wait_vm<3>();
+  else if (n >= 2) wait_vm<2>();
+  else wait_vm<0>();
+}
+
+// wait for this wave's outstanding LDS reads (before a DMA overwrites them)
+__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+
+// LDS tile of one item's indices: ints 0..47 key tokens of the 48 slots,
+// 48..55 the query tokens of the cluster, 56..63 unused.
+constexpr int kIdxBytes = 256;
+constexpr int kFwdWaves = 2;
+constexpr int kFwdWaveLds = 2 * kTileBytes + 1024 + kIdxBytes;
+
+// Two exec-masked loads (each lane writes only its own 4-byte LDS slot):
+// lanes 0..47 fetch the key_idx row of the cluster, lanes 48..63 the q_idx
+// row (48..55, repeated in 56..63).  Counts as two vector-memory operations.
+__device__ __forceinline__ void gather_idx(int bc, const int32_t* __restrict__ q_idx,
+                                           const int32_t* __restrict__ key_idx, int lane,
+                                           uint32_t lds) {
+  if (lane < NK) dma4(key_idx, (uint32_t)(bc * NK + lane) * 4u, lds);
+  else dma4(q_idx, (uint32_t)(bc * CS + ((lane - NK) & 7)) * 4u, lds);
+}
+
+// Per-lane indices of one item, read from its LDS index tile.
+struct FwdIdx2 {
+  int tj[NK / 8];   // token of slot 8j + (lane >> 3)   (K/V gathers)
+  int tq;           // query token (lane >> 3)          (Q gather)
+  int tl;           // token of slot lane (lanes 48..63: slots 32..47)
+  int qc;           // query token of column c16
+};
+
+__device__ __forceinline__ void read_idx(const char* t, int lane, FwdIdx2& x) {
+  const int* ti = reinterpret_cast<const int*>(t);
+#pragma unroll
+  for (int j = 0; j < NK / 8; ++j) x.tj[j] = ti[8 * j + (lane >> 3)];
+  x.tq = ti[NK + (lane >> 3)];
+  x.tl = ti[lane < NK ? lane : lane - 16];
+  x.qc = ti[NK + (lane & 7)];
+}
+
+// Gather one tensor's 48 slot rows (both heads of the pair) into an LDS
+// tile: instruction j fills slots 8j..8j+7; lane 8r+u fetches chunk
+// u ^ F(slot) of slot 8j+r, which lands at chunk position u.  With an odd
+// head count the missing second head re-reads the first (never used).
+template <typename T>
+__device__ __forceinline__ void gather_tile(const T* __restrict__ src, const FwdIdx2& x, int img,
+                                            int h0, int H, int lane, uint32_t lds_base) {
+  const int r = lane >> 3, u = lane & 7;
+  const uint32_t h1off = h0 + 1 < H ? kRow : 0u;
+#pragma unroll
+  for (int j = 0; j < NK / 8; ++j) {
+    const int sl = 8 * j + r;
+    const uint32_t c = (uint32_t)u ^ swz(sl);
+    const uint32_t off = (uint32_t)((img + max(x.tj[j], 0)) * H + h0) * kRow +
+                         (c < 4u ? 16u * c : h1off + 16u * (c - 4u));
+    dma16(src, off, lds_base + (uint32_t)j * 1024u);
+  }
+}
+
+// The 8 query rows (both heads of the pair) into a 1 KiB tile: lane 8r+u
+// fetches chunk u ^ F(r) of query r.
+template <typename T>
+__device__ __forceinline__ void gather_q(const T* __restrict__ q, const FwdIdx2& x, int img, int h0,
+                                         int H, int lane, uint32_t lds_base) {
+  const int r = lane >> 3, u = lane & 7;
+  const uint32_t h1off = h0 + 1 < H ? kRow : 0u;
+  const uint32_t c = (uint32_t)u ^ swz(r);
+  const uint32_t off = (uint32_t)((img + x.tq) * H + h0) * kRow +
+                       (c < 4u ? 16u * c : h1off + 16u * (c - 4u));
+  dma16(q, off, lds_base);
+}
+
+// Forward.  Each wavefront walks a run of `ipw` consecutive items (cluster,
+// head pair) as a software pipeline in which every gather goes straight to
+// LDS and every tile is refilled as soon as it has been consumed.  Memory
+// operations are issued in this order in iteration t (vmcnt retires them in
+// issue order):
+//   idx(t+2) [2], K(t+1) [6], Q(t+1) [1], V(t+1) [6], O/LSE(t) stores [3]
+// so at the top of iteration t, K(t), Q(t) and idx(t+1) are complete once
+// at most V(t) + stores(t-1) = 9 newer operations remain, and V(t) is
+// complete once at most stores(t-1) + idx(t+2) + K(t+1) = 11 remain.
+template <typename T>
+__global__ void __launch_bounds__(64 * kFwdWaves)
+fwd_lds_kernel(int N, int H, int HP, int n_items, int ipw, float scale_log2,
+               const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
+               const int32_t* __restrict__ q_idx, const int32_t* __restrict__ key_idx,
+               T* __restrict__ o, float* __restrict__ lse) {
+  __shared__ __attribute__((aligned(1024))) char lds[kFwdWaves * kFwdWaveLds];
+  const int wv = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int first = (xcd_remap(blockIdx.x, gridDim.x) * kFwdWaves + wv) * ipw;
+  if (first >= n_items) return;
+  const int last = min(first + ipw, n_items);
+  const int lane = threadIdx.x & 63;
+  const int c16 = lane & 15, g = lane >> 4;
+  const bool left = c16 < 8;
+  char* tk = lds + wv * kFwdWaveLds;
+  char* tv = tk + kTileBytes;
+  char* tq = tv + kTileBytes;
+  char* ti = tq + 1024;
+  auto lds_addr = [](char* p) {
+    return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)p;
+  };
+  const uint32_t ak = lds_addr(tk), av = lds_addr(tv), aq = lds_addr(tq), ai = lds_addr(ti);
+  const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+  const int e = c16 >> 2, qq = c16 & 3;
+  const int CperImg = N / CS;
+
+  // prologue: indices of `first`, then of `first + 1`, then the tiles of `first`
+  FwdIdx2 x, xn;
+  gather_idx(first / HP, q_idx, key_idx, lane, ai);
+  wait_vm<0>();
+  read_idx(ti, lane, x);
+  wait_lgkm0();
+  if (first + 1 < last) gather_idx((first + 1) / HP, q_idx, key_idx, lane, ai);
+  {
+    const int bc = first / HP, h0 = 2 * (first - bc * HP), img = bc / CperImg * N;
+    gather_tile<T>(k, x, img, h0, H, lane, ak);
+    gather_q<T>(q, x, img, h0, H, lane, aq);
+    gather_tile<T>(v, x, img, h0, H, lane, av);
+  }
+
   for (int it = first; it < last; ++it) {
-    if (it + 1 < last) {
-      fwd_load_rows<T>(xn, N, H, q, k, v, c16, g, dn);
-      if (it + 2 < last) fwd_load_idx(it + 2, HP, q_idx, key_idx, c16, xnn);
+    const bool more = it + 1 < last, more2 = it + 2 < last, prev = it > first;
+    const int bc = it / HP, h0 = 2 * (it - bc * HP), img = bc / CperImg * N;
+    const bool h1ok = h0 + 1 < H;
+    const int hq = left ? h0 : h0 + 1;
+
+    // K(t), Q(t) and idx(t+1) have landed
+    wait_vm_n(6 + (prev ? 3 : 0));
+    if (more) {
+      read_idx(ti, lane, xn);
+      wait_lgkm0();
+      if (more2) gather_idx((it + 2) / HP, q_idx, key_idx, lane, ai);
     }
-    fwd_compute<T>(xi, di, N, H, scale_log2, id, c16, g, o, lse);
-    xi = xn;
-    di = dn;
-    xn = xnn;
+
+    // S^T = K Q^T: lane holds keys 16b+4g+i of column c16
+    const int qm = c16 & 7;
+    const uint4 qv = lds16(tq, (uint32_t)qm * kSlotBytes +
+                                   16u * ((uint32_t)((c16 >> 3) * 4 + g) ^ swz(qm)));
+    const uint4 qL = sel(left, qv), qR = sel(!left, qv);
+    f32x4 s[3];
+#pragma unroll
+    for (int b = 0; b < 3; ++b) {
+      const int sl = 16 * b + c16;
+      const uint32_t row = (uint32_t)sl * kSlotBytes;
+      const uint4 k0 = lds16(tk, row + 16u * ((uint32_t)g ^ swz(sl)));
+      const uint4 k1 = lds16(tk, row + 16u * ((uint32_t)(4 + g) ^ swz(sl)));
+      s[b] = Mfma<T>::mma(k0, qL, z);
+      s[b] = Mfma<T>::mma(k1, qR, s[b]);
+    }
+    if (more) {   // K tile consumed: refill it for the next item
+      wait_lgkm0();
+      const int bn = (it + 1) / HP, hn = 2 * (it + 1 - bn * HP), in = bn / CperImg * N;
+      gather_tile<T>(k, xn, in, hn, H, lane, ak);
+    }
+
+    if (__ballot(x.tl < 0) != 0ull) {   // some slot of this list is empty: mask it
+      const uint64_t vb64 = __ballot(x.tl >= 0);
+#pragma unroll
+      for (int b = 0; b < 3; ++b) {
+        const uint32_t vb = (uint32_t)(vb64 >> (16 * b));
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (!((vb >> (4 * g + i)) & 1u)) s[b][i] = -INFINITY;
+      }
+    }
+    float mx = fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3]));
+#pragma unroll
+    for (int b = 1; b < 3; ++b)
+      mx = fmaxf(mx, fmaxf(fmaxf(s[b][0], s[b][1]), fmaxf(s[b][2], s[b][3])));
+    mx = shfl_max16_32(mx);
+    const float mref = mx == -INFINITY ? 0.f : mx * scale_log2;
+    float l = 0.f;
+    float p[3][4];
+#pragma unroll
+    for (int b = 0; b < 3; ++b)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        p[b][i] = __builtin_amdgcn_exp2f(fmaf(s[b][i], scale_log2, -mref));
+        l += p[b][i];
+      }
+    l = shfl_sum16_32(l);
+    uint2 ph[3];
+#pragma unroll
+    for (int b = 0; b < 3; ++b)
+      ph[b] = make_uint2(pack2<T>(p[b][0], p[b][1]), pack2<T>(p[b][2], p[b][3]));
+    const uint4 bp0 = cat(ph[0], ph[1]), bp1 = pad(ph[2]);
+
+    // V(t) has landed
+    wait_vm_n((prev ? 3 : 0) + (more2 ? 2 : 0) + (more ? 6 : 0));
+
+    // O^T = V^T P^T per head.  Transposed read: lane c16 = 4e + qq of group g
+    // addresses dims 16hf + 4qq.. of slot 16blk + 4g + e and receives dim
+    // 16hf + c16 of the four slots 16blk + 4g + e, e = 0..3.
+    f32x4 oacc[2][2] = {{z, z}, {z, z}};
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      if (hh == 1 && !h1ok) break;
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        uint2 vt[3];
+#pragma unroll
+        for (int blk = 0; blk < 3; ++blk) {
+          const int sl = 16 * blk + 4 * g + e;
+          const uint32_t c = (uint32_t)(4 * hh + 2 * hf + (qq >> 1));
+          vt[blk] = lds_tr8(tv, (uint32_t)sl * kSlotBytes + 16u * (c ^ swz(sl)) + 8u * (qq & 1));
+        }
+        oacc[hh][hf] = Mfma<T>::mma(cat(vt[0], vt[1]), bp0, oacc[hh][hf]);
+        oacc[hh][hf] = Mfma<T>::mma(pad(vt[2]), bp1, oacc[hh][hf]);
+      }
+    }
+    if (more) {   // Q and V tiles consumed: next item's
+      wait_lgkm0();
+      const int bn = (it + 1) / HP, hn = 2 * (it + 1 - bn * HP), in = bn / CperImg * N;
+      gather_q<T>(q, xn, in, hn, H, lane, aq);
+      gather_tile<T>(v, xn, in, hn, H, lane, av);
+    }
+
+    // exactly three store instructions per item (the pipeline counts them)
+    const float inv = l > 0.f ? 1.f / l : 0.f;
+    const bool st = hq < H;
+    const uint32_t orow = (uint32_t)((img + x.qc) * H + (st ? hq : h0)) * kRow + 8u * g;
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+      const uint2 ov = pack4<T>((left ? oacc[0][hf] : oacc[1][hf]) * inv);
+      if (st) stv<uint2>(o, orow + 32u * hf, ov);
+    }
+    if (st && g == 0)
+      lse[(img + x.qc) * H + hq] = l > 0.f ? (mref + __log2f(l)) * kLn2 : -INFINITY;
+    x = xn;
   }
 }
 
@@ -563,8 +839,8 @@ bwd_kv_mfma_kernel(int N, int H, int HP, int n_items, float scale, const T* __re
 // Items per wavefront: enough wavefronts to give every SIMD of the 256 CUs
 // about four, each pipelining its run of consecutive items.
 int items_per_wave(int items) {
-  constexpr int kTargetWaves = 256 * 4 * 4;
-  return std::max(1, std::min(8, (items + kTargetWaves - 1) / kTargetWaves));
+  constexpr int kTargetWaves = 256 * 12;   // resident waves: 12 per CU
+  return std::max(1, std::min(16, (items + kTargetWaves - 1) / kTargetWaves));
 }
 
 template <typename T>
@@ -575,8 +851,8 @@ hipError_t fwd_t(int B, int N, int H, float scale, const void* q, const void* k,
   const int items = B * (N / CS) * HP;
   const int ipw = items_per_wave(items);
   const int waves = (items + ipw - 1) / ipw;
-  const int wgs = (waves + kWaves - 1) / kWaves;
-  hipLaunchKernelGGL((fwd_mfma_kernel<T>), dim3(wgs), dim3(64 * kWaves), 0, st, N, H, HP, items,
+  const int wgs = (waves + kFwdWaves - 1) / kFwdWaves;
+  hipLaunchKernelGGL((fwd_lds_kernel<T>), dim3(wgs), dim3(64 * kFwdWaves), 0, st, N, H, HP, items,
                      ipw, scale * kLog2e, (const T*)q, (const T*)k, (const T*)v, q_idx, key_idx,
                      (T*)o, lse);
   return hipGetLastError();
