@@ -28,6 +28,13 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, vendor figure
+# kernels behind each entry point on the bf16/f16 path (the roofline is per
+# entry point; the committed kernel trace splits it per kernel)
+ENTRY_KERNELS = {
+    "build": ["build_small_kernel (N <= 2048) | rank, merge, centroid, select (N > 2048)"],
+    "fwd": ["fwd_lds_kernel"],
+    "bwd": ["plan_small_kernel", "bwd_q_mfma_kernel", "bwd_kv_mfma_kernel"],
+}
 BF16_MFMA_PEAK_TFLOPS = 2500.0  # dense
 
 
@@ -92,6 +99,29 @@ def cpu_baseline(cfg, case, images: int):
     }
 
 
+def measured_traffic(entry: str):
+    """HBM bytes per launch of an entry point from the committed rocprofv3
+    FETCH_SIZE / WRITE_SIZE summary, if it was taken on the current kernel
+    sources (same hash), else None."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "stage1_hbm_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    h = hashlib.sha256()
+    d = os.path.join(ROOT, "gathered_local_attention_amd", "csrc")
+    for name in sorted(os.listdir(d)):
+        if name.endswith((".hip", ".h")):
+            h.update(name.encode())
+            with open(os.path.join(d, name), "rb") as f:
+                h.update(f.read())
+    if h.hexdigest() != rec.get("source_sha256"):
+        return None
+    e = rec["entries"].get(entry)
+    return None if e is None else e["traffic_bytes"]
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -133,19 +163,11 @@ def main():
     gws = torch.empty(ca.bwd_workspace_bytes(case["q"].dtype, cfg.B, cfg.N, cfg.H, cfg.D,
                                              cfg.cs, cfg.nk), dtype=torch.uint8, device=dev)
 
-    def step(s, ev=None):
-        if ev is not None:
-            ev[0].record()
+    def step(s):
         perm, nbr, key = ca.build_neighbors(s["coords"], cfg.G, cfg.cs, cfg.k, workspace=bws)
-        if ev is not None:
-            ev[1].record()
         o, lse = ca.fwd(s["q"], s["k"], s["v"], perm, key, scale)
-        if ev is not None:
-            ev[2].record()
         dq, dk, dv = ca.bwd(s["q"], s["k"], s["v"], o, s["do"], lse, perm, key, scale,
                             workspace=gws)
-        if ev is not None:
-            ev[3].record()
         return dq
 
     for i in range(args.warmup):
@@ -160,19 +182,36 @@ def main():
     wall = time.perf_counter() - t0
     ms_per_step = wall * 1e3 / args.steps
 
-    # per-entry-point durations (HIP events on the launch stream), same rotation
+    # per-entry-point durations: HIP events on the launch stream around
+    # n_ev back-to-back calls of one entry point (rotating copies), so the
+    # per-launch average compares with the kernel trace (the gaps between
+    # back-to-back kernels, ~1-2 us each, are included)
     n_ev = min(args.steps, 100)
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(n_ev)]
-    torch.cuda.synchronize()
-    for i in range(n_ev):
-        step(sets[i % len(sets)], evs[i])
-    torch.cuda.synchronize()
-    dur = {"build": 0.0, "fwd": 0.0, "bwd": 0.0}
-    for e in evs:
-        dur["build"] += e[0].elapsed_time(e[1])
-        dur["fwd"] += e[1].elapsed_time(e[2])
-        dur["bwd"] += e[2].elapsed_time(e[3])
-    dur = {k: v / n_ev * 1e3 for k, v in dur.items()}   # microseconds
+    outs = []
+    for s in sets:
+        perm, nbr, key = ca.build_neighbors(s["coords"], cfg.G, cfg.cs, cfg.k, workspace=bws)
+        o, lse = ca.fwd(s["q"], s["k"], s["v"], perm, key, scale)
+        outs.append((perm, key, o, lse))
+    calls = {
+        "build": lambda i: ca.build_neighbors(sets[i]["coords"], cfg.G, cfg.cs, cfg.k,
+                                              workspace=bws),
+        "fwd": lambda i: ca.fwd(sets[i]["q"], sets[i]["k"], sets[i]["v"], outs[i][0],
+                                outs[i][1], scale),
+        "bwd": lambda i: ca.bwd(sets[i]["q"], sets[i]["k"], sets[i]["v"], outs[i][2],
+                                sets[i]["do"], outs[i][3], outs[i][0], outs[i][1], scale,
+                                workspace=gws),
+    }
+    dur = {}
+    for name, call in calls.items():
+        call(0)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(n_ev):
+            call(i % len(sets))
+        e1.record()
+        torch.cuda.synchronize()
+        dur[name] = e0.elapsed_time(e1) / n_ev * 1e3   # microseconds per launch
 
     # warm-cache variant: every step on the same copy
     torch.cuda.synchronize()
@@ -213,11 +252,12 @@ def main():
         "roofline": {
             "bound": "hbm",
             "kernel": f"cluster_attn_{dom}" if dom != "build" else "cluster_attn_build_neighbors",
+            "entry_point_kernels": ENTRY_KERNELS[dom],
             "achieved": achieved,
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBPS,
-            "traffic": None,
+            "traffic": measured_traffic(dom) if cfg.name == "stage1" else None,
             "algorithmic_bytes": alg[dom]["bytes"],
             "avg_us": dur[dom],
         },

@@ -10,7 +10,7 @@
 // describes: bf16/fp16 operands, fp32 statistics and accumulation, logits in
 // log2 units so every exponential is one v_exp_f32.
 //
-// Tiling (one 64-lane wavefront per (cluster, pair of heads), no LDS):
+// Tiling (one 64-lane wavefront per item = (cluster, pair of heads)):
 //  * v_mfma_f32_16x16x32 operand layout (checked on the hardware): lane
 //    l = c + 16 g holds row/column c and reduction indices [8g, 8g+8); the
 //    16x16 fp32 result puts rows 4g..4g+3 of column c in lane l.  Only this
@@ -19,21 +19,20 @@
 //    the upper half of every lane's reduction slice zeroed.
 //  * A cluster has 8 queries, half a 16-wide tile, so the two heads of a
 //    pair share one tile: columns 0-7 are head h0, 8-15 head h1.  Products
-//    whose other operand differs per head run as two MFMAs with the unused
-//    half of one operand zeroed (block-diagonal), which costs no more than
-//    a half-empty tile and keeps every lane of the softmax busy.
-//  * Products that contract over keys (P.V, dS.K) or queries (dS^T.Q,
-//    P^T.dO) need the gathered rows transposed.  A wave does that in
-//    registers by multiplying the rows, as loaded, with a 0/1 selection
-//    matrix on the MFMA unit (exact: one nonzero product per output).
-//  * Probabilities and dS enter the bf16 products as a hi + lo pair
+//    whose other operand differs per head run as two MFMAs, block-diagonal
+//    over the heads, which keeps every lane of the softmax busy.
+//  * Forward: the gathered rows go to a wavefront-private LDS tile through
+//    direct-to-LDS loads (whole 128-byte rows per eight lanes); K is read
+//    back in the MFMA layout and V through the transposing LDS read.
+//  * Backward: gathers go straight to registers in the MFMA layout; products
+//    that contract over keys or queries transpose the gathered rows on the
+//    MFMA unit with a 0/1 selection matrix (exact: one nonzero product per
+//    output).  P and dS enter the products as a hi + lo pair
 //    (x = hi + lo to ~16 bits) so their rounding stays far below the
 //    output rounding.
-//  * Gathers are 16-byte loads addressed by 32-bit byte offsets from the
-//    tensor base; per-item indices are wave-uniform and live in scalar
-//    registers.  Workgroups of 4 wavefronts are remapped so that each XCD
-//    (eight, dispatched round-robin) walks one contiguous Morton range of
-//    clusters: neighbouring clusters share their gathered rows in its L2.
+//  * Workgroups are remapped so that each XCD (eight, dispatched
+//    round-robin) walks one contiguous Morton range of clusters:
+//    neighbouring clusters share their gathered rows in its L2.
 #include "common.h"
 
 #include <algorithm>
@@ -159,137 +158,6 @@ __device__ __forceinline__ float shfl_sum16_32(float v) {
 __device__ __forceinline__ int wave_item() {
   const int w = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   return xcd_remap(blockIdx.x, gridDim.x) * kWaves + w;
-}
-
-// ---------------------------------------------------------------------------
-// forward
-// ---------------------------------------------------------------------------
-// One wavefront per item (cluster, head pair); a wavefront walks `ipw`
-// consecutive items.  Per item: 6 MFMAs for S^T = K Q^T (block-diagonal over
-// the two heads), the softmax on 12 logits per lane, 12 MFMAs transposing V,
-// 8 MFMAs for O^T = V^T P^T with one accumulator set per head (so neither
-// operand needs zeroed columns).  When all 48 slots of the list are valid
-// (the usual case) the masking is skipped by a wave-uniform branch.
-template <typename T>
-__device__ __forceinline__ void fwd_item(int item, int N, int H, int HP, float scale_log2,
-                                         const T* __restrict__ q, const T* __restrict__ k,
-                                         const T* __restrict__ v,
-                                         const int32_t* __restrict__ q_idx,
-                                         const int32_t* __restrict__ key_idx,
-                                         const uint4 (&id)[2], int c16, int g,
-                                         T* __restrict__ o, float* __restrict__ lse) {
-  const int bc = item / HP;
-  const int h0 = 2 * (item - bc * HP);
-  const int img = bc / (N / CS) * N;
-  const bool left = c16 < 8;
-  const int hq = left ? h0 : h0 + 1;
-  const bool h1ok = h0 + 1 < H;
-  const uint32_t lo16 = 16u * g;
-
-  int kt[3];
-#pragma unroll
-  for (int b = 0; b < 3; ++b) kt[b] = key_idx[bc * NK + 16 * b + c16];
-  const int qtok = q_idx[bc * CS + (c16 & 7)];
-  // With an odd head count the last pair has no second head: its rows are
-  // then re-read from the first head (finite values; the columns they feed
-  // are never stored and the second head's V product is skipped).
-  const uint32_t h1off = h1ok ? kRow : 0u;
-  const uint32_t qrow = (uint32_t)((img + qtok) * H + h0) * kRow + (left ? 0u : h1off);
-  const uint4 qv = ld16(q, qrow + lo16);
-  uint32_t valid = 0xFFFFFFFFu;
-  uint4 ka[3][2], va[3][2];
-#pragma unroll
-  for (int b = 0; b < 3; ++b) {
-    valid &= (uint32_t)__ballot(kt[b] >= 0) | 0xFFFF0000u;
-    const uint32_t r = (uint32_t)((img + max(kt[b], 0)) * H + h0) * kRow + lo16;
-    ka[b][0] = ld16(k, r);
-    va[b][0] = ld16(v, r);
-    ka[b][1] = ld16(k, r + h1off);
-    va[b][1] = ld16(v, r + h1off);
-  }
-
-  // S^T = K Q^T: lane holds keys 16b+4g+i of column c16 (query c16&7, head hq)
-  const uint4 qL = sel(left, qv), qR = sel(!left, qv);
-  const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-  f32x4 s[3];
-#pragma unroll
-  for (int b = 0; b < 3; ++b) {
-    s[b] = Mfma<T>::mma(ka[b][0], qL, z);
-    s[b] = Mfma<T>::mma(ka[b][1], qR, s[b]);
-  }
-  if (valid != 0xFFFFFFFFu) {   // some slot of this list is empty: mask it
-#pragma unroll
-    for (int b = 0; b < 3; ++b) {
-      const uint32_t vb = (uint32_t)__ballot(kt[b] >= 0);
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        if (!((vb >> (4 * g + i)) & 1u)) s[b][i] = -INFINITY;
-    }
-  }
-  float mx = fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3]));
-#pragma unroll
-  for (int b = 1; b < 3; ++b)
-    mx = fmaxf(mx, fmaxf(fmaxf(s[b][0], s[b][1]), fmaxf(s[b][2], s[b][3])));
-  mx = shfl_max16_32(mx);
-  // logits in log2 units; a column with no valid slot keeps mx = -inf
-  const float mref = mx == -INFINITY ? 0.f : mx * scale_log2;
-  float l = 0.f;
-  float p[3][4];
-#pragma unroll
-  for (int b = 0; b < 3; ++b)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      p[b][i] = __builtin_amdgcn_exp2f(fmaf(s[b][i], scale_log2, -mref));
-      l += p[b][i];
-    }
-  l = shfl_sum16_32(l);
-
-  // P^T as B operands over keys: step 0 = blocks 0,1 (32 keys), step 1 = block 2
-  uint2 ph[3];
-#pragma unroll
-  for (int b = 0; b < 3; ++b) ph[b] = make_uint2(pack2<T>(p[b][0], p[b][1]), pack2<T>(p[b][2], p[b][3]));
-  const uint4 bp0 = cat(ph[0], ph[1]), bp1 = pad(ph[2]);
-
-  // O^T = V^T P^T per head; the lane keeps the accumulator of its own head
-  f32x4 oacc[2][2] = {{z, z}, {z, z}};
-#pragma unroll
-  for (int hh = 0; hh < 2; ++hh) {
-    if (hh == 1 && !h1ok) break;
-    uint2 vt[3][2];
-#pragma unroll
-    for (int b = 0; b < 3; ++b) transpose_rows<T>(va[b][hh], id, vt[b]);
-#pragma unroll
-    for (int hf = 0; hf < 2; ++hf) {
-      oacc[hh][hf] = Mfma<T>::mma(cat(vt[0][hf], vt[1][hf]), bp0, oacc[hh][hf]);
-      oacc[hh][hf] = Mfma<T>::mma(pad(vt[2][hf]), bp1, oacc[hh][hf]);
-    }
-  }
-
-  if (hq >= H) return;
-  const float inv = l > 0.f ? 1.f / l : 0.f;
-  const uint32_t orow = qrow + 8u * g;
-#pragma unroll
-  for (int hf = 0; hf < 2; ++hf)
-    stv<uint2>(o, orow + 32u * hf, pack4<T>((left ? oacc[0][hf] : oacc[1][hf]) * inv));
-  if (g == 0) lse[(img + qtok) * H + hq] = l > 0.f ? (mref + __log2f(l)) * kLn2 : -INFINITY;
-}
-
-template <typename T>
-__global__ void __launch_bounds__(64 * kWaves)
-fwd_mfma_kernel(int N, int H, int HP, int n_items, int ipw, float scale_log2,
-                const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
-                const int32_t* __restrict__ q_idx, const int32_t* __restrict__ key_idx,
-                T* __restrict__ o, float* __restrict__ lse) {
-  const int first = wave_item() * ipw;
-  if (first >= n_items) return;
-  const int last = min(first + ipw, n_items);
-  const int lane = threadIdx.x & 63;
-  const int c16 = lane & 15, g = lane >> 4;
-  uint4 id[2];
-  id[0] = selector<T>(g, c16, 0);
-  id[1] = selector<T>(g, c16, 1);
-  for (int it = first; it < last; ++it)
-    fwd_item<T>(it, N, H, HP, scale_log2, q, k, v, q_idx, key_idx, id, c16, g, o, lse);
 }
 
 // ---------------------------------------------------------------------------

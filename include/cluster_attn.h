@@ -108,8 +108,11 @@ int cluster_attn_build_neighbors(const float* coords, int B, int N, int grid_sid
  *   S_ms = scale * <Q[b, q_idx[b,c,m], h, :], K_s>
  *   O    = sum_s exp(S_ms - LSE_m) V_s,  LSE_m = ln sum_s exp(S_ms)
  * computed with fp32 max/sum statistics and fp32 accumulation (bf16/f16
- * operands of the matrix products; the softmax probabilities enter the P*V
- * product as a hi/lo pair so their rounding does not reach O).
+ * operands of the matrix products; the unnormalised probabilities, all in
+ * [0, 1], are rounded once to dt for the P*V product: relative error at most
+ * 2^-8 (bf16) or 2^-11 (f16; absolute below 2^-25 in its subnormal range)
+ * per probability; normalisation by the fp32 row sum happens after the
+ * product).
  *   dt        element type of q, k, v and o.
  *   D         head dim, must be 32.  nk: slots per list (= cs*k).
  *   scale     logit scale (1/sqrt(D) for the plain reading).
