@@ -190,10 +190,10 @@ int cluster_attn_bwd(int dt, int B, int N, int H, int D, int cs, int nk, float s
   hipError_t e = ca::launch_bwd_plan(B, N, nk, q_idx, key_idx, w, st);
   if (e != hipSuccess) return hip_status(e, "bwd plan launch");
   if (ca::mfma_supported(dt, B, N, H, nk))
-    return hip_status(ca::launch_bwd_mfma(dt, B, N, H, nk, scale, q, k, v, o, dout, lse, q_idx,
+    return hip_status(ca::launch_bwd_mfma(3, dt, B, N, H, nk, scale, q, k, v, o, dout, lse, q_idx,
                                           key_idx, dq, dk, dv, w, st),
                       "bwd launch");
-  return hip_status(ca::launch_bwd_valu(dt, B, N, H, nk, scale, q, k, v, o, dout, lse, q_idx,
+  return hip_status(ca::launch_bwd_valu(3, dt, B, N, H, nk, scale, q, k, v, o, dout, lse, q_idx,
                                         key_idx, dq, dk, dv, w, st),
                     "bwd launch");
 }

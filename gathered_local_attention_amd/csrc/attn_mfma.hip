@@ -704,6 +704,175 @@ bwd_kv_mfma_kernel(int N, int H, int HP, int n_items, float scale, const T* __re
   }
 }
 
+// ---------------------------------------------------------------------------
+// backward pass B (key-major), LDS-staged gathers
+// ---------------------------------------------------------------------------
+// One wavefront per (key cluster j, head pair).  The entries of j (query
+// clusters i reading j, with per-member multiplicities) are taken four at a
+// time: their 32 query rows of Q and dO (both heads) are gathered into a
+// wavefront-private LDS tile with direct-to-LDS loads (instruction u holds
+// entry u's 8 rows).  S = Q K_j^T and dP = dO V_j^T read Q and dO in the
+// MFMA A layout; dV^T += dO^T P and dK^T += Q^T dS read them transposed
+// (ds_read_b64_tr_b16).  One accumulator set per head, so no operand needs
+// zeroed columns.  Summation order is fixed by the entry order (sorted by
+// i), so the result is bitwise reproducible.
+constexpr int kKvRows = 32;                             // query rows per step
+constexpr int kKvTile = kKvRows * kSlotBytes;           // 4 KiB per tensor
+constexpr int kKvWaveLds = 2 * kKvTile;                 // Q and dO
+
+template <typename T>
+__global__ void __launch_bounds__(64 * kWaves)
+bwd_kv_lds_kernel(int N, int H, int HP, int n_items, float scale, const T* __restrict__ q,
+                  const T* __restrict__ k, const T* __restrict__ v, const T* __restrict__ dout,
+                  const int32_t* __restrict__ q_idx, const float2* __restrict__ ld,
+                  const int32_t* __restrict__ off_all, const RevEntry* __restrict__ rev_all, int nk,
+                  T* __restrict__ dk, T* __restrict__ dv) {
+  __shared__ __attribute__((aligned(1024))) char lds[kWaves * kKvWaveLds];
+  const int item = wave_item();
+  if (item >= n_items) return;
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  char* tq = lds + wv * kKvWaveLds;
+  char* td = tq + kKvTile;
+  const uint32_t aq = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)tq;
+  const uint32_t ad = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)td;
+  const int C = N / CS;
+  const int bj = item / HP;
+  const int h0 = 2 * (item - bj * HP);
+  const int b = bj / C;
+  const int j = bj - b * C;
+  const int img = b * N;
+  const int c16 = lane & 15, g = lane >> 4;
+  const bool left = c16 < 8;
+  const bool h1ok = h0 + 1 < H;
+  const int hk = left ? h0 : h0 + 1;
+  const uint32_t h1off = h1ok ? kRow : 0u;
+  const float scale_log2 = scale * kLog2e;
+  const int e = c16 >> 2, qq = c16 & 3;
+
+  // own key rows as B operands (column c16 = key c16&7 of head hk)
+  const int ktok = q_idx[bj * CS + (c16 & 7)];
+  const uint32_t krow = (uint32_t)((img + ktok) * H + h0) * kRow + (left ? 0u : h1off) + 16u * g;
+  const uint4 kB = ld16(k, krow), vB = ld16(v, krow);
+  const uint4 kL = sel(left, kB), kR = sel(!left, kB);
+  const uint4 vL = sel(left, vB), vR = sel(!left, vB);
+
+  const int32_t* off = off_all + b * (C + 1);
+  const RevEntry* rev = rev_all + (int64_t)b * C * nk;
+  const int e0 = off[j], e1 = off[j + 1];
+
+  const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+  f32x4 dka[2][2] = {{z, z}, {z, z}}, dva[2][2] = {{z, z}, {z, z}};   // [head][dim half]
+  const int kcol = c16 & 7;
+
+  for (int eb = e0; eb < e1; eb += 8) {
+    // up to 8 entries: lane l holds entry eb + (l & 7); lane 8u + r the token
+    // of member r of entry u
+    const int ne = min(8, e1 - eb);
+    const RevEntry re = rev[eb + min(lane & 7, ne - 1)];
+    const int ei = re.i;
+    const uint64_t em = (lane & 7) < ne ? re.mult : 0ull;
+    const int qt = q_idx[(b * C + __shfl(ei, lane >> 3, 64)) * CS + (lane & 7)];
+
+    for (int e4 = 0; e4 < ne; e4 += 4) {
+      // gathers: instruction u holds entry e4 + u (an entry past the end
+      // repeats the last one, with zero multiplicity)
+      {
+        const int r = lane >> 3, u8 = lane & 7;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int eu = min(e4 + u, ne - 1);
+          const int t = __shfl(qt, 8 * eu + r, 64);
+          const int row = 8 * u + r;
+          const uint32_t c = (uint32_t)u8 ^ swz(row);
+          const uint32_t o = (uint32_t)((img + t) * H + h0) * kRow +
+                             (c < 4u ? 16u * c : h1off + 16u * (c - 4u));
+          dma16(q, o, aq + (uint32_t)u * 1024u);
+          dma16(dout, o, ad + (uint32_t)u * 1024u);
+        }
+      }
+      // per output row 4g+i of block qb: multiplicity and (LSE*log2e, Delta)
+      float mult[2];
+      float2 lv[2][4];
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+        const int ee = e4 + 2 * qb + (g >> 1);
+        const uint64_t m64 = __shfl(em, min(ee, 7), 64);
+        mult[qb] = ee < ne ? (float)((m64 >> (8 * kcol)) & 0xFFu) : 0.f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int t = __shfl(qt, 8 * min(ee, ne - 1) + ((4 * g + i) & 7), 64);
+          lv[qb][i] = mult[qb] != 0.f ? ld[(img + t) * H + hk] : make_float2(0.f, 0.f);
+        }
+      }
+      wait_vm<0>();
+
+      float p[2][4], ds[2][4];
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+        const int row = 16 * qb + c16;
+        const uint32_t rb = (uint32_t)row * kSlotBytes;
+        const uint4 q0 = lds16(tq, rb + 16u * ((uint32_t)g ^ swz(row)));
+        const uint4 q1 = lds16(tq, rb + 16u * ((uint32_t)(4 + g) ^ swz(row)));
+        const uint4 d0 = lds16(td, rb + 16u * ((uint32_t)g ^ swz(row)));
+        const uint4 d1 = lds16(td, rb + 16u * ((uint32_t)(4 + g) ^ swz(row)));
+        f32x4 sv = Mfma<T>::mma(q0, kL, z);
+        sv = Mfma<T>::mma(q1, kR, sv);
+        f32x4 dp = Mfma<T>::mma(d0, vL, z);
+        dp = Mfma<T>::mma(d1, vR, dp);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          p[qb][i] = mult[qb] != 0.f
+                         ? mult[qb] * __builtin_amdgcn_exp2f(fmaf(sv[i], scale_log2, -lv[qb][i].x))
+                         : 0.f;
+          ds[qb][i] = p[qb][i] * (dp[i] - lv[qb][i].y);
+        }
+      }
+      uint2 ph[2], pl[2], dh[2], dlo[2];
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+        split4<T>(p[qb], ph[qb], pl[qb]);
+        split4<T>(ds[qb], dh[qb], dlo[qb]);
+      }
+      const uint4 bph = cat(ph[0], ph[1]), bpl = cat(pl[0], pl[1]);
+      const uint4 bdh = cat(dh[0], dh[1]), bdl = cat(dlo[0], dlo[1]);
+      // transposed reads: lane c16 = 4e + qq of group g receives dim
+      // 16hf + c16 of query rows 16qb + 4g + e, e = 0..3
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        if (hh == 1 && !h1ok) break;
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+          uint2 at_d[2], at_q[2];
+#pragma unroll
+          for (int qb = 0; qb < 2; ++qb) {
+            const int row = 16 * qb + 4 * g + e;
+            const uint32_t c = (uint32_t)(4 * hh + 2 * hf + (qq >> 1));
+            const uint32_t o = (uint32_t)row * kSlotBytes + 16u * (c ^ swz(row)) + 8u * (qq & 1);
+            at_d[qb] = lds_tr8(td, o);
+            at_q[qb] = lds_tr8(tq, o);
+          }
+          const uint4 ad4 = cat(at_d[0], at_d[1]), aq4 = cat(at_q[0], at_q[1]);
+          dva[hh][hf] = Mfma<T>::mma(ad4, bph, dva[hh][hf]);
+          dva[hh][hf] = Mfma<T>::mma(ad4, bpl, dva[hh][hf]);
+          dka[hh][hf] = Mfma<T>::mma(aq4, bdh, dka[hh][hf]);
+          dka[hh][hf] = Mfma<T>::mma(aq4, bdl, dka[hh][hf]);
+        }
+      }
+      // the tiles are rewritten next step: all reads above must be complete
+      wait_lgkm0();
+    }
+  }
+
+  if (hk >= H) return;
+  const uint32_t orow = (uint32_t)((img + ktok) * H + hk) * kRow + 8u * g;
+#pragma unroll
+  for (int hf = 0; hf < 2; ++hf) {
+    stv<uint2>(dk, orow + 32u * hf, pack4<T>((left ? dka[0][hf] : dka[1][hf]) * scale));
+    stv<uint2>(dv, orow + 32u * hf, pack4<T>(left ? dva[0][hf] : dva[1][hf]));
+  }
+}
+
 // Items per wavefront: enough wavefronts to give every SIMD of the 256 CUs
 // about four, each pipelining its run of consecutive items.
 int items_per_wave(int items) {
@@ -727,20 +896,22 @@ hipError_t fwd_t(int B, int N, int H, float scale, const void* q, const void* k,
 }
 
 template <typename T>
-hipError_t bwd_t(int B, int N, int H, int nk, float scale, const void* q, const void* k,
+hipError_t bwd_t(int pass, int B, int N, int H, int nk, float scale, const void* q, const void* k,
                  const void* v, const void* o, const void* dout, const float* lse,
                  const int32_t* q_idx, const int32_t* key_idx, void* dq, void* dk, void* dv,
                  const BwdWorkspace& w, hipStream_t st) {
   const int HP = (H + 1) / 2;
   const int items = B * (N / CS) * HP;
   const int wgs = (items + kWaves - 1) / kWaves;
-  hipLaunchKernelGGL((bwd_q_mfma_kernel<T>), dim3(wgs), dim3(64 * kWaves), 0, st, N, H, HP, items,
-                     scale, (const T*)q, (const T*)k, (const T*)v, (const T*)o, (const T*)dout, lse,
-                     q_idx, key_idx, (T*)dq, w.ld);
-  hipLaunchKernelGGL((bwd_kv_mfma_kernel<T>), dim3(wgs), dim3(64 * kWaves), 0, st, N, H, HP, items,
-                     scale, (const T*)q, (const T*)k, (const T*)v, (const T*)dout, q_idx,
-                     (const float2*)w.ld, (const int32_t*)w.off, (const RevEntry*)w.rev, nk, (T*)dk,
-                     (T*)dv);
+  if (pass & 1)
+    hipLaunchKernelGGL((bwd_q_mfma_kernel<T>), dim3(wgs), dim3(64 * kWaves), 0, st, N, H, HP,
+                       items, scale, (const T*)q, (const T*)k, (const T*)v, (const T*)o,
+                       (const T*)dout, lse, q_idx, key_idx, (T*)dq, w.ld);
+  if (pass & 2)
+    hipLaunchKernelGGL((bwd_kv_lds_kernel<T>), dim3(wgs), dim3(64 * kWaves), 0, st, N, H, HP,
+                       items, scale, (const T*)q, (const T*)k, (const T*)v, (const T*)dout, q_idx,
+                       (const float2*)w.ld, (const int32_t*)w.off, (const RevEntry*)w.rev, nk,
+                       (T*)dk, (T*)dv);
   return hipGetLastError();
 }
 
@@ -762,16 +933,17 @@ hipError_t launch_fwd_mfma(int dt, int B, int N, int H, float scale, const void*
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_bwd_mfma(int dt, int B, int N, int H, int nk, float scale, const void* q,
-                           const void* k, const void* v, const void* o, const void* dout,
-                           const float* lse, const int32_t* q_idx, const int32_t* key_idx,
-                           void* dq, void* dk, void* dv, const BwdWorkspace& w, hipStream_t st) {
+hipError_t launch_bwd_mfma(int pass, int dt, int B, int N, int H, int nk, float scale,
+                           const void* q, const void* k, const void* v, const void* o,
+                           const void* dout, const float* lse, const int32_t* q_idx,
+                           const int32_t* key_idx, void* dq, void* dk, void* dv,
+                           const BwdWorkspace& w, hipStream_t st) {
   if (dt == 1)
-    return bwd_t<bf16>(B, N, H, nk, scale, q, k, v, o, dout, lse, q_idx, key_idx, dq, dk, dv, w,
-                       st);
+    return bwd_t<bf16>(pass, B, N, H, nk, scale, q, k, v, o, dout, lse, q_idx, key_idx, dq, dk,
+                       dv, w, st);
   if (dt == 2)
-    return bwd_t<f16>(B, N, H, nk, scale, q, k, v, o, dout, lse, q_idx, key_idx, dq, dk, dv, w,
-                      st);
+    return bwd_t<f16>(pass, B, N, H, nk, scale, q, k, v, o, dout, lse, q_idx, key_idx, dq, dk,
+                      dv, w, st);
   return hipErrorInvalidValue;
 }
 

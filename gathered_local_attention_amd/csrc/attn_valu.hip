@@ -291,18 +291,20 @@ hipError_t fwd_t(int B, int N, int H, int nk, float scale, const void* q, const 
 }
 
 template <typename T>
-hipError_t bwd_t(int B, int N, int H, int nk, float scale, const void* q, const void* k,
+hipError_t bwd_t(int pass, int B, int N, int H, int nk, float scale, const void* q, const void* k,
                  const void* v, const void* o, const void* dout, const float* lse,
                  const int32_t* q_idx, const int32_t* key_idx, void* dq, void* dk, void* dv,
                  const BwdWorkspace& w, hipStream_t st) {
   const int64_t blocks = (int64_t)B * (N / CS) * H;
-  hipLaunchKernelGGL(bwd_q_valu_kernel<T>, dim3((unsigned)blocks), dim3(64), 0, st, N, H, nk,
-                     scale, (const T*)q, (const T*)k, (const T*)v, (const T*)o, (const T*)dout, lse,
-                     q_idx, key_idx, (T*)dq, w.ld);
-  hipLaunchKernelGGL(bwd_kv_valu_kernel<T>, dim3((unsigned)blocks), dim3(64), 0, st, N, H, nk,
-                     scale, (const T*)q, (const T*)k, (const T*)v, (const T*)dout, lse, q_idx,
-                     (const float2*)w.ld, (const int32_t*)w.off, (const RevEntry*)w.rev, (T*)dk,
-                     (T*)dv);
+  if (pass & 1)
+    hipLaunchKernelGGL(bwd_q_valu_kernel<T>, dim3((unsigned)blocks), dim3(64), 0, st, N, H, nk,
+                       scale, (const T*)q, (const T*)k, (const T*)v, (const T*)o, (const T*)dout,
+                       lse, q_idx, key_idx, (T*)dq, w.ld);
+  if (pass & 2)
+    hipLaunchKernelGGL(bwd_kv_valu_kernel<T>, dim3((unsigned)blocks), dim3(64), 0, st, N, H, nk,
+                       scale, (const T*)q, (const T*)k, (const T*)v, (const T*)dout, lse, q_idx,
+                       (const float2*)w.ld, (const int32_t*)w.off, (const RevEntry*)w.rev,
+                       (T*)dk, (T*)dv);
   return hipGetLastError();
 }
 
@@ -319,14 +321,15 @@ hipError_t launch_fwd_valu(int dt, int B, int N, int H, int nk, float scale, con
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_bwd_valu(int dt, int B, int N, int H, int nk, float scale, const void* q,
-                           const void* k, const void* v, const void* o, const void* dout,
-                           const float* lse, const int32_t* q_idx, const int32_t* key_idx,
-                           void* dq, void* dk, void* dv, const BwdWorkspace& w, hipStream_t st) {
+hipError_t launch_bwd_valu(int pass, int dt, int B, int N, int H, int nk, float scale,
+                           const void* q, const void* k, const void* v, const void* o,
+                           const void* dout, const float* lse, const int32_t* q_idx,
+                           const int32_t* key_idx, void* dq, void* dk, void* dv,
+                           const BwdWorkspace& w, hipStream_t st) {
   switch (dt) {
-    case 0: return bwd_t<float>(B, N, H, nk, scale, q, k, v, o, dout, lse, q_idx, key_idx, dq, dk, dv, w, st);
-    case 1: return bwd_t<bf16>(B, N, H, nk, scale, q, k, v, o, dout, lse, q_idx, key_idx, dq, dk, dv, w, st);
-    case 2: return bwd_t<f16>(B, N, H, nk, scale, q, k, v, o, dout, lse, q_idx, key_idx, dq, dk, dv, w, st);
+    case 0: return bwd_t<float>(pass, B, N, H, nk, scale, q, k, v, o, dout, lse, q_idx, key_idx, dq, dk, dv, w, st);
+    case 1: return bwd_t<bf16>(pass, B, N, H, nk, scale, q, k, v, o, dout, lse, q_idx, key_idx, dq, dk, dv, w, st);
+    case 2: return bwd_t<f16>(pass, B, N, H, nk, scale, q, k, v, o, dout, lse, q_idx, key_idx, dq, dk, dv, w, st);
   }
   return hipErrorInvalidValue;
 }

@@ -144,10 +144,13 @@ hipError_t launch_fwd_valu(int dt, int B, int N, int H, int nk, float scale, con
 hipError_t launch_bwd_plan(int B, int N, int nk, const int32_t* q_idx, const int32_t* key_idx,
                            const BwdWorkspace& w, hipStream_t st);
 
-hipError_t launch_bwd_valu(int dt, int B, int N, int H, int nk, float scale, const void* q,
-                           const void* k, const void* v, const void* o, const void* dout,
-                           const float* lse, const int32_t* q_idx, const int32_t* key_idx,
-                           void* dq, void* dk, void* dv, const BwdWorkspace& w, hipStream_t st);
+// Backward launchers: pass bit 1 = pass A (Delta, dQ; needs nothing from the
+// plan), bit 2 = pass B (dK, dV; needs pass A and the plan).
+hipError_t launch_bwd_valu(int pass, int dt, int B, int N, int H, int nk, float scale,
+                           const void* q, const void* k, const void* v, const void* o,
+                           const void* dout, const float* lse, const int32_t* q_idx,
+                           const int32_t* key_idx, void* dq, void* dk, void* dv,
+                           const BwdWorkspace& w, hipStream_t st);
 
 bool mfma_supported(int dt, int B, int N, int H, int nk);
 
@@ -155,9 +158,10 @@ hipError_t launch_fwd_mfma(int dt, int B, int N, int H, float scale, const void*
                            const void* v, const int32_t* q_idx, const int32_t* key_idx, void* o,
                            float* lse, hipStream_t st);
 
-hipError_t launch_bwd_mfma(int dt, int B, int N, int H, int nk, float scale, const void* q,
-                           const void* k, const void* v, const void* o, const void* dout,
-                           const float* lse, const int32_t* q_idx, const int32_t* key_idx,
-                           void* dq, void* dk, void* dv, const BwdWorkspace& w, hipStream_t st);
+hipError_t launch_bwd_mfma(int pass, int dt, int B, int N, int H, int nk, float scale,
+                           const void* q, const void* k, const void* v, const void* o,
+                           const void* dout, const float* lse, const int32_t* q_idx,
+                           const int32_t* key_idx, void* dq, void* dk, void* dv,
+                           const BwdWorkspace& w, hipStream_t st);
 
 }  // namespace ca
