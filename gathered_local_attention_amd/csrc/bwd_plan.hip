@@ -152,16 +152,30 @@ plan_kernel(int N, int nk, const int32_t* __restrict__ q_idx, const int32_t* __r
 }
 
 // ---------------------------------------------------------------------------
-// Images with at most 256 clusters and 12288 slots.  Every slot does O(1)
-// work: it sets bit i of key cluster j's row in an LDS bitmap (repeated
-// slots set the same bit), segment sizes are row popcounts, the entry of
-// (i, j) sits at off[j] + (set bits of row j below i), and each slot adds its
-// member count into that entry's multiplicity bytes with an integer atomic.
-// Segments come out ordered by i and the sums are order independent, so the
-// result is deterministic without a sort.
+// Images with at most 256 clusters and 12288 slots, one workgroup each, all
+// in LDS.  Every slot does O(1) work: it sets bit i of key cluster j's row
+// in an LDS bitmap (repeated slots set the same bit), segment sizes are row
+// popcounts, the entry of (i, j) sits at off[j] + (set bits of row j below
+// i), and each slot adds its member count into that entry's multiplicity
+// bytes with an LDS integer atomic (a list has at most 64 slots, so a byte
+// never carries).  The eight lanes of an aligned group hold the eight slots
+// of one slot group of one cluster; when they agree (the usual case) one
+// lane issues the combined update.  Segments come out ordered by i and the
+// sums are order independent, so the result is deterministic without a sort.
 // ---------------------------------------------------------------------------
 constexpr int kPlanMaxC = 256;
 constexpr int kPlanWords = kPlanMaxC / 32;
+
+// true on every lane of an aligned group of 8 lanes iff all 8 hold the same value
+__device__ __forceinline__ bool group8_agree(int x) {
+  bool same = true;
+#pragma unroll
+  for (int o = 1; o < 8; o <<= 1) same = same && (__shfl_xor(x, o, 64) == x);
+  int all = same ? 1 : 0;
+#pragma unroll
+  for (int o = 1; o < 8; o <<= 1) all &= __shfl_xor(all, o, 64);
+  return all != 0;
+}
 
 __global__ void __launch_bounds__(kPlanThreads)
 plan_small_kernel(int N, int nk, const int32_t* __restrict__ q_idx,
@@ -170,6 +184,8 @@ plan_small_kernel(int N, int nk, const int32_t* __restrict__ q_idx,
   __shared__ int32_t inv[kSortChunk];
   __shared__ uint32_t bits[kPlanMaxC][kPlanWords];
   __shared__ int32_t off[kPlanMaxC + 1];
+  __shared__ int32_t wo[kPlanMaxC][kPlanWords];
+  __shared__ unsigned long long mult[kTileSlots];
   __shared__ int32_t tmp[17];
   const int b = blockIdx.x;
   const int C = N / 8;
@@ -196,16 +212,22 @@ plan_small_kernel(int N, int nk, const int32_t* __restrict__ q_idx,
   __syncthreads();
 
   int jn[kPer], ii[kPer];
+  const int lane = tid & 63;
 #pragma unroll
   for (int r = 0; r < kPer; ++r) {
     const int x = tid + r * kPlanThreads;
     jn[r] = tok[r] >= 0 ? inv[tok[r]] : -1;        // (j << 3) | n
     ii[r] = x / nk;
-    if (jn[r] >= 0) atomicOr(&bits[jn[r] >> 3][ii[r] >> 5], 1u << (ii[r] & 31));
+    const int key = jn[r] >= 0 ? ((jn[r] >> 3) << 16) | ii[r] : -1;
+    if (group8_agree(key)) {
+      if (key >= 0 && (lane & 7) == 0) atomicOr(&bits[jn[r] >> 3][ii[r] >> 5], 1u << (ii[r] & 31));
+    } else if (key >= 0) {
+      atomicOr(&bits[jn[r] >> 3][ii[r] >> 5], 1u << (ii[r] & 31));
+    }
   }
   __syncthreads();
 
-  // segment sizes and offsets (exclusive scan over j < C <= 256 < threads)
+  // segment sizes, offsets, per-word offsets (exclusive scan over j < C <= 256)
   int v = 0;
   if (tid < C) {
 #pragma unroll
@@ -213,67 +235,56 @@ plan_small_kernel(int N, int nk, const int32_t* __restrict__ q_idx,
   }
   int total;
   const int ex = block_exclusive_scan(v, tmp, kPlanThreads, &total);
-  if (tid < C) off[tid] = ex;
-  if (tid == 0) off[C] = total;
+  if (tid < C) {
+    off[tid] = ex;
+    int a = ex;
+#pragma unroll
+    for (int w = 0; w < kPlanWords; ++w) {
+      wo[tid][w] = a;
+      a += __popc(bits[tid][w]);
+    }
+  }
   int32_t* goff = off_all + (int64_t)b * (C + 1);
   if (tid <= C) goff[tid] = tid < C ? ex : total;
+  for (int p = tid; p < total; p += kPlanThreads) mult[p] = 0ull;
   __syncthreads();
 
-  // entries: i from the bitmap, multiplicities accumulated below
+  // multiplicities, accumulated in LDS
+#pragma unroll
+  for (int r = 0; r < kPer; ++r) {
+    int pos = -1;
+    uint64_t add = 0;
+    if (jn[r] >= 0) {
+      const int jj = jn[r] >> 3, i = ii[r];
+      pos = wo[jj][i >> 5] + __popc(bits[jj][i >> 5] & ((1u << (i & 31)) - 1u));
+      add = 1ull << (8 * (jn[r] & 7));
+    }
+    uint64_t sum = add;
+#pragma unroll
+    for (int o = 1; o < 8; o <<= 1) sum += __shfl_xor(sum, o, 64);
+    if (group8_agree(pos)) {
+      if (pos >= 0 && (lane & 7) == 0) atomicAdd(&mult[pos], (unsigned long long)sum);
+    } else if (pos >= 0) {
+      atomicAdd(&mult[pos], (unsigned long long)add);
+    }
+  }
+  __syncthreads();
+
+  // entries out: the segment of key cluster j, ordered by i
   RevEntry* rev = rev_all + (int64_t)b * ns;
-  for (int j = tid; j < C; j += kPlanThreads) {
-    int pos = off[j];
+  for (int jj = tid; jj < C; jj += kPlanThreads) {
+    int pos = off[jj];
     for (int w = 0; w < kPlanWords; ++w) {
-      uint32_t m = bits[j][w];
+      uint32_t m = bits[jj][w];
       while (m) {
         const int i = 32 * w + __ffs(m) - 1;
         m &= m - 1;
         RevEntry e;
         e.i = i;
         e.pad = 0;
-        e.mult = 0;
+        e.mult = mult[pos];
         rev[pos++] = e;
       }
-    }
-  }
-  // workgroup scope suffices (every entry of this image is written and
-  // updated by this workgroup); a device-scope fence would write back L2
-  __threadfence_block();
-  __syncthreads();
-  // Slot x and lane share x mod 8, and nk is a multiple of 8, so every
-  // aligned group of 8 lanes holds one slot group of one cluster; when all 8
-  // point into the same entry (the usual case) their member counts are
-  // summed with lane shuffles and a single atomic is issued.
-  const int lane = tid & 63;
-#pragma unroll
-  for (int r = 0; r < kPer; ++r) {
-    int pos = -1;
-    uint64_t add = 0;
-    if (jn[r] >= 0) {
-      const int j = jn[r] >> 3, i = ii[r];
-      pos = off[j];
-      for (int w = 0; w < (i >> 5); ++w) pos += __popc(bits[j][w]);
-      pos += __popc(bits[j][i >> 5] & ((1u << (i & 31)) - 1u));
-      add = 1ull << (8 * (jn[r] & 7));
-    }
-    bool same = true;
-    uint64_t sum = add;
-#pragma unroll
-    for (int o = 1; o < 8; o <<= 1) {
-      const int po = __shfl_xor(pos, o, 64);
-      same = same && (po == pos);
-      sum += __shfl_xor(sum, o, 64);
-    }
-    // butterfly AND: every lane of the group ends with the same verdict
-    int all_same = same ? 1 : 0;
-#pragma unroll
-    for (int o = 1; o < 8; o <<= 1) all_same &= __shfl_xor(all_same, o, 64);
-    if (pos < 0) continue;
-    if (all_same) {
-      if ((lane & 7) == 0)
-        atomicAdd(reinterpret_cast<unsigned long long*>(&rev[pos].mult), sum);
-    } else {
-      atomicAdd(reinterpret_cast<unsigned long long*>(&rev[pos].mult), add);
     }
   }
 }
