@@ -705,6 +705,162 @@ bwd_kv_mfma_kernel(int N, int H, int HP, int n_items, float scale, const T* __re
 }
 
 // ---------------------------------------------------------------------------
+// backward pass A (query-major), LDS-staged gathers: Delta and dQ
+// ---------------------------------------------------------------------------
+// Per item (cluster, head pair), the 48 slot rows of K and V and the 8 query
+// rows of Q, dO and O go to a wavefront-private LDS tile (direct-to-LDS
+// loads, whole 128-byte rows).  Delta = <dO, O> per (query, head);
+// S^T = K Q^T and dP^T = V dO^T read K and V in the A layout; dQ^T = K^T dS^T
+// reads K through the transposing LDS read.  dS enters as a hi + lo pair.
+constexpr int kQWaves = 2;
+constexpr int kQWaveLds = 2 * kTileBytes + 3 * 1024;   // K, V, Q, dO, O
+constexpr int kQWavesPerCU = 10;                       // LDS-limited residency
+
+template <typename T>
+__global__ void __launch_bounds__(64 * kQWaves)
+bwd_q_lds_kernel(int N, int H, int HP, int n_items, int ipw, float scale,
+                 const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
+                 const T* __restrict__ o, const T* __restrict__ dout,
+                 const float* __restrict__ lse, const int32_t* __restrict__ q_idx,
+                 const int32_t* __restrict__ key_idx, T* __restrict__ dq,
+                 float2* __restrict__ ld) {
+  __shared__ __attribute__((aligned(1024))) char lds[kQWaves * kQWaveLds];
+  const int wv = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int first = (xcd_remap(blockIdx.x, gridDim.x) * kQWaves + wv) * ipw;
+  if (first >= n_items) return;
+  const int last = min(first + ipw, n_items);
+  const int lane = threadIdx.x & 63;
+  const int c16 = lane & 15, g = lane >> 4;
+  const bool left = c16 < 8;
+  char* tk = lds + wv * kQWaveLds;
+  char* tv = tk + kTileBytes;
+  char* tq = tv + kTileBytes;
+  char* tdo = tq + 1024;
+  char* to = tdo + 1024;
+  auto lds_addr = [](char* ptr) {
+    return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)ptr;
+  };
+  const uint32_t ak = lds_addr(tk), av = lds_addr(tv), aq = lds_addr(tq), ado = lds_addr(tdo),
+                 ao = lds_addr(to);
+  const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+  const int e = c16 >> 2, qq = c16 & 3;
+  const float scale_log2 = scale * kLog2e;
+
+  for (int it = first; it < last; ++it) {
+    const int bc = it / HP;
+    const int h0 = 2 * (it - bc * HP);
+    const int img = bc / (N / CS) * N;
+    const bool h1ok = h0 + 1 < H;
+    const int hq = left ? h0 : h0 + 1;
+    const uint32_t h1off = h1ok ? kRow : 0u;
+
+    // indices: token of slot `lane` (lanes 48..63 repeat 32..47); query token
+    // of row lane>>3 (gathers) and of column c16
+    const int tok = key_idx[bc * NK + (lane < NK ? lane : lane - 16)];
+    const int qtr = q_idx[bc * CS + (lane >> 3)];
+    const int qtok = q_idx[bc * CS + (c16 & 7)];
+    const float lse2 = lse[(img + qtok) * H + (hq < H ? hq : h0)] * kLog2e;
+    {
+      const int r = lane >> 3, u = lane & 7;
+#pragma unroll
+      for (int j = 0; j < NK / 8; ++j) {
+        const int sl = 8 * j + r;
+        const int t = max(__shfl(tok, sl, 64), 0);
+        const uint32_t c = (uint32_t)u ^ swz(sl);
+        const uint32_t off = (uint32_t)((img + t) * H + h0) * kRow +
+                             (c < 4u ? 16u * c : h1off + 16u * (c - 4u));
+        dma16(k, off, ak + (uint32_t)j * 1024u);
+        dma16(v, off, av + (uint32_t)j * 1024u);
+      }
+      const uint32_t c = (uint32_t)u ^ swz(r);
+      const uint32_t off = (uint32_t)((img + qtr) * H + h0) * kRow +
+                           (c < 4u ? 16u * c : h1off + 16u * (c - 4u));
+      dma16(q, off, aq);
+      dma16(dout, off, ado);
+      dma16(o, off, ao);
+    }
+    wait_vm<0>();
+
+    // B operands (column c16 = query c16&7, head hq): Q and dO rows; Delta
+    const int qm = c16 & 7;
+    const uint32_t qoff = (uint32_t)qm * kSlotBytes +
+                          16u * ((uint32_t)((c16 >> 3) * 4 + g) ^ swz(qm));
+    const uint4 qv = lds16(tq, qoff), dov = lds16(tdo, qoff), ov = lds16(to, qoff);
+    float dl = 0.f;
+    {
+      const uint32_t a[4] = {dov.x, dov.y, dov.z, dov.w};
+      const uint32_t c[4] = {ov.x, ov.y, ov.z, ov.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const f32x2 x = Mfma<T>::unpack(a[i]), y = Mfma<T>::unpack(c[i]);
+        dl = fmaf(x[0], y[0], fmaf(x[1], y[1], dl));
+      }
+    }
+    dl = shfl_sum16_32(dl);
+    if (hq < H && g == 0) ld[(img + qtok) * H + hq] = make_float2(lse2, dl);
+
+    const uint4 qL = sel(left, qv), qR = sel(!left, qv);
+    const uint4 dL = sel(left, dov), dR = sel(!left, dov);
+    float ds[3][4];
+    const uint64_t vb64 = __ballot(tok >= 0);
+#pragma unroll
+    for (int b = 0; b < 3; ++b) {
+      const int sl = 16 * b + c16;
+      const uint32_t row = (uint32_t)sl * kSlotBytes;
+      const uint4 k0 = lds16(tk, row + 16u * ((uint32_t)g ^ swz(sl)));
+      const uint4 k1 = lds16(tk, row + 16u * ((uint32_t)(4 + g) ^ swz(sl)));
+      const uint4 v0 = lds16(tv, row + 16u * ((uint32_t)g ^ swz(sl)));
+      const uint4 v1 = lds16(tv, row + 16u * ((uint32_t)(4 + g) ^ swz(sl)));
+      f32x4 sv = Mfma<T>::mma(k0, qL, z);
+      sv = Mfma<T>::mma(k1, qR, sv);
+      f32x4 dp = Mfma<T>::mma(v0, dL, z);
+      dp = Mfma<T>::mma(v1, dR, dp);
+      const uint32_t vb = (uint32_t)(vb64 >> (16 * b));
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const bool ok = (vb >> (4 * g + i)) & 1u;
+        const float p = ok ? __builtin_amdgcn_exp2f(fmaf(sv[i], scale_log2, -lse2)) : 0.f;
+        ds[b][i] = p * (dp[i] - dl);
+      }
+    }
+    uint2 dh[3], dlo[3];
+#pragma unroll
+    for (int b = 0; b < 3; ++b) split4<T>(ds[b], dh[b], dlo[b]);
+    const uint4 b0h = cat(dh[0], dh[1]), b0l = cat(dlo[0], dlo[1]);
+    const uint4 b1h = pad(dh[2]), b1l = pad(dlo[2]);
+
+    // dQ^T = K^T dS^T per head (transposed K reads, as V in the forward)
+    f32x4 acc[2][2] = {{z, z}, {z, z}};
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      if (hh == 1 && !h1ok) break;
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        uint2 kt[3];
+#pragma unroll
+        for (int blk = 0; blk < 3; ++blk) {
+          const int sl = 16 * blk + 4 * g + e;
+          const uint32_t c = (uint32_t)(4 * hh + 2 * hf + (qq >> 1));
+          kt[blk] = lds_tr8(tk, (uint32_t)sl * kSlotBytes + 16u * (c ^ swz(sl)) + 8u * (qq & 1));
+        }
+        const uint4 a01 = cat(kt[0], kt[1]), a2 = pad(kt[2]);
+        acc[hh][hf] = Mfma<T>::mma(a01, b0h, acc[hh][hf]);
+        acc[hh][hf] = Mfma<T>::mma(a2, b1h, acc[hh][hf]);
+        acc[hh][hf] = Mfma<T>::mma(a01, b0l, acc[hh][hf]);
+        acc[hh][hf] = Mfma<T>::mma(a2, b1l, acc[hh][hf]);
+      }
+    }
+    if (hq < H) {
+      const uint32_t drow = (uint32_t)((img + qtok) * H + hq) * kRow + 8u * g;
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf)
+        stv<uint2>(dq, drow + 32u * hf, pack4<T>((left ? acc[0][hf] : acc[1][hf]) * scale));
+    }
+    wait_lgkm0();   // tiles are rewritten by the next item
+  }
+}
+
+// ---------------------------------------------------------------------------
 // backward pass B (key-major), LDS-staged gathers
 // ---------------------------------------------------------------------------
 // One wavefront per (key cluster j, head pair).  The entries of j (query
@@ -875,9 +1031,11 @@ bwd_kv_lds_kernel(int N, int H, int HP, int n_items, float scale, const T* __res
 
 // Items per wavefront: enough wavefronts to give every SIMD of the 256 CUs
 // about four, each pipelining its run of consecutive items.
-int items_per_wave(int items) {
-  constexpr int kTargetWaves = 256 * 12;   // resident waves: 12 per CU
-  return std::max(1, std::min(16, (items + kTargetWaves - 1) / kTargetWaves));
+// Items per wavefront for a kernel of which `per_cu` waves fit on a CU at
+// once: just enough waves to fill all 256 CUs in one round.
+int items_per_wave(int items, int per_cu) {
+  const int target = 256 * per_cu;
+  return std::max(1, std::min(16, (items + target - 1) / target));
 }
 
 template <typename T>
@@ -886,7 +1044,7 @@ hipError_t fwd_t(int B, int N, int H, float scale, const void* q, const void* k,
                  hipStream_t st) {
   const int HP = (H + 1) / 2;
   const int items = B * (N / CS) * HP;
-  const int ipw = items_per_wave(items);
+  const int ipw = items_per_wave(items, 12);
   const int waves = (items + ipw - 1) / ipw;
   const int wgs = (waves + kFwdWaves - 1) / kFwdWaves;
   hipLaunchKernelGGL((fwd_lds_kernel<T>), dim3(wgs), dim3(64 * kFwdWaves), 0, st, N, H, HP, items,
@@ -903,10 +1061,14 @@ hipError_t bwd_t(int pass, int B, int N, int H, int nk, float scale, const void*
   const int HP = (H + 1) / 2;
   const int items = B * (N / CS) * HP;
   const int wgs = (items + kWaves - 1) / kWaves;
-  if (pass & 1)
-    hipLaunchKernelGGL((bwd_q_mfma_kernel<T>), dim3(wgs), dim3(64 * kWaves), 0, st, N, H, HP,
-                       items, scale, (const T*)q, (const T*)k, (const T*)v, (const T*)o,
-                       (const T*)dout, lse, q_idx, key_idx, (T*)dq, w.ld);
+  if (pass & 1) {
+    const int ipw = items_per_wave(items, kQWavesPerCU);
+    const int waves = (items + ipw - 1) / ipw;
+    hipLaunchKernelGGL((bwd_q_lds_kernel<T>), dim3((waves + kQWaves - 1) / kQWaves),
+                       dim3(64 * kQWaves), 0, st, N, H, HP, items, ipw, scale, (const T*)q,
+                       (const T*)k, (const T*)v, (const T*)o, (const T*)dout, lse, q_idx, key_idx,
+                       (T*)dq, w.ld);
+  }
   if (pass & 2)
     hipLaunchKernelGGL((bwd_kv_lds_kernel<T>), dim3(wgs), dim3(64 * kWaves), 0, st, N, H, HP,
                        items, scale, (const T*)q, (const T*)k, (const T*)v, (const T*)dout, q_idx,

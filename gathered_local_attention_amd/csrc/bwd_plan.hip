@@ -152,30 +152,21 @@ plan_kernel(int N, int nk, const int32_t* __restrict__ q_idx, const int32_t* __r
 }
 
 // ---------------------------------------------------------------------------
-// Images with at most 256 clusters and 12288 slots, one workgroup each, all
-// in LDS.  Every slot does O(1) work: it sets bit i of key cluster j's row
-// in an LDS bitmap (repeated slots set the same bit), segment sizes are row
-// popcounts, the entry of (i, j) sits at off[j] + (set bits of row j below
-// i), and each slot adds its member count into that entry's multiplicity
-// bytes with an LDS integer atomic (a list has at most 64 slots, so a byte
-// never carries).  The eight lanes of an aligned group hold the eight slots
-// of one slot group of one cluster; when they agree (the usual case) one
-// lane issues the combined update.  Segments come out ordered by i and the
-// sums are order independent, so the result is deterministic without a sort.
+// Images with at most 256 clusters and 16384 slots, one workgroup each, all
+// in LDS.  A thread owns whole slot groups (8 consecutive slots of one
+// cluster's list, loaded as two 16-byte vectors) and works on each distinct
+// key cluster j its group points into (usually one): it sets bit i of row j
+// in an LDS bitmap, and later adds the group's member counts for j into the
+// multiplicity bytes of entry (i, j) with one LDS integer atomic (a list has
+// at most 64 slots, so a byte never carries).  Segment sizes are row
+// popcounts and the entry of (i, j) sits at off[j] + (set bits of row j
+// below i), so segments come out ordered by i and the sums are order
+// independent: deterministic without a sort.
 // ---------------------------------------------------------------------------
 constexpr int kPlanMaxC = 256;
 constexpr int kPlanWords = kPlanMaxC / 32;
-
-// true on every lane of an aligned group of 8 lanes iff all 8 hold the same value
-__device__ __forceinline__ bool group8_agree(int x) {
-  bool same = true;
-#pragma unroll
-  for (int o = 1; o < 8; o <<= 1) same = same && (__shfl_xor(x, o, 64) == x);
-  int all = same ? 1 : 0;
-#pragma unroll
-  for (int o = 1; o < 8; o <<= 1) all &= __shfl_xor(all, o, 64);
-  return all != 0;
-}
+constexpr int kPlanMaxSlots = 16384;
+constexpr int kGroupsPer = kPlanMaxSlots / 8 / kPlanThreads;   // 2 slot groups per thread
 
 __global__ void __launch_bounds__(kPlanThreads)
 plan_small_kernel(int N, int nk, const int32_t* __restrict__ q_idx,
@@ -185,22 +176,28 @@ plan_small_kernel(int N, int nk, const int32_t* __restrict__ q_idx,
   __shared__ uint32_t bits[kPlanMaxC][kPlanWords];
   __shared__ int32_t off[kPlanMaxC + 1];
   __shared__ int32_t wo[kPlanMaxC][kPlanWords];
-  __shared__ unsigned long long mult[kTileSlots];
+  __shared__ unsigned long long mult[kPlanMaxSlots];
   __shared__ int32_t tmp[17];
   const int b = blockIdx.x;
   const int C = N / 8;
   const int tid = threadIdx.x;
   const int ns = C * nk;
+  const int ngroups = ns / 8;
   const int32_t* qi = q_idx + (int64_t)b * N;
   const int32_t* ki = key_idx + (int64_t)b * ns;
-  constexpr int kPer = kTileSlots / kPlanThreads;   // 12 slots per thread
 
-  // this thread's slots x = tid + r * 1024 (r < kPer), loaded up front
-  int tok[kPer];
+  // this thread's slot groups gr = tid + r * 1024, loaded up front
+  int tok[kGroupsPer][8];
 #pragma unroll
-  for (int r = 0; r < kPer; ++r) {
-    const int x = tid + r * kPlanThreads;
-    tok[r] = x < ns ? ki[x] : -1;
+  for (int r = 0; r < kGroupsPer; ++r) {
+    const int gr = tid + r * kPlanThreads;
+    int4 a = make_int4(-1, -1, -1, -1), c = a;
+    if (gr < ngroups) {
+      a = reinterpret_cast<const int4*>(ki)[2 * gr];
+      c = reinterpret_cast<const int4*>(ki)[2 * gr + 1];
+    }
+    tok[r][0] = a.x; tok[r][1] = a.y; tok[r][2] = a.z; tok[r][3] = a.w;
+    tok[r][4] = c.x; tok[r][5] = c.y; tok[r][6] = c.z; tok[r][7] = c.w;
   }
   const int q0 = tid < N ? qi[tid] : -1;                       // N <= 2048
   const int q1 = tid + kPlanThreads < N ? qi[tid + kPlanThreads] : -1;
@@ -211,18 +208,20 @@ plan_small_kernel(int N, int nk, const int32_t* __restrict__ q_idx,
   if (q1 >= 0) inv[q1] = tid + kPlanThreads;
   __syncthreads();
 
-  int jn[kPer], ii[kPer];
-  const int lane = tid & 63;
+  // key position (j << 3 | member) of every slot; bitmap rows
+  int jn[kGroupsPer][8];
 #pragma unroll
-  for (int r = 0; r < kPer; ++r) {
-    const int x = tid + r * kPlanThreads;
-    jn[r] = tok[r] >= 0 ? inv[tok[r]] : -1;        // (j << 3) | n
-    ii[r] = x / nk;
-    const int key = jn[r] >= 0 ? ((jn[r] >> 3) << 16) | ii[r] : -1;
-    if (group8_agree(key)) {
-      if (key >= 0 && (lane & 7) == 0) atomicOr(&bits[jn[r] >> 3][ii[r] >> 5], 1u << (ii[r] & 31));
-    } else if (key >= 0) {
-      atomicOr(&bits[jn[r] >> 3][ii[r] >> 5], 1u << (ii[r] & 31));
+  for (int r = 0; r < kGroupsPer; ++r) {
+    const int i = (tid + r * kPlanThreads) * 8 / nk;
+#pragma unroll
+    for (int m = 0; m < 8; ++m) jn[r][m] = tok[r][m] >= 0 ? inv[tok[r][m]] : -1;
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+      if (jn[r][m] < 0) continue;
+      bool seen = false;
+#pragma unroll
+      for (int u = 0; u < m; ++u) seen = seen || (jn[r][u] >= 0 && (jn[r][u] >> 3) == (jn[r][m] >> 3));
+      if (!seen) atomicOr(&bits[jn[r][m] >> 3][i >> 5], 1u << (i & 31));
     }
   }
   __syncthreads();
@@ -249,22 +248,23 @@ plan_small_kernel(int N, int nk, const int32_t* __restrict__ q_idx,
   for (int p = tid; p < total; p += kPlanThreads) mult[p] = 0ull;
   __syncthreads();
 
-  // multiplicities, accumulated in LDS
+  // multiplicities: one LDS atomic per distinct key cluster of a group
 #pragma unroll
-  for (int r = 0; r < kPer; ++r) {
-    int pos = -1;
-    uint64_t add = 0;
-    if (jn[r] >= 0) {
-      const int jj = jn[r] >> 3, i = ii[r];
-      pos = wo[jj][i >> 5] + __popc(bits[jj][i >> 5] & ((1u << (i & 31)) - 1u));
-      add = 1ull << (8 * (jn[r] & 7));
-    }
-    uint64_t sum = add;
+  for (int r = 0; r < kGroupsPer; ++r) {
+    const int i = (tid + r * kPlanThreads) * 8 / nk;
 #pragma unroll
-    for (int o = 1; o < 8; o <<= 1) sum += __shfl_xor(sum, o, 64);
-    if (group8_agree(pos)) {
-      if (pos >= 0 && (lane & 7) == 0) atomicAdd(&mult[pos], (unsigned long long)sum);
-    } else if (pos >= 0) {
+    for (int m = 0; m < 8; ++m) {
+      if (jn[r][m] < 0) continue;
+      const int jj = jn[r][m] >> 3;
+      bool seen = false;
+#pragma unroll
+      for (int u = 0; u < m; ++u) seen = seen || (jn[r][u] >= 0 && (jn[r][u] >> 3) == jj);
+      if (seen) continue;
+      uint64_t add = 0;
+#pragma unroll
+      for (int u = m; u < 8; ++u)
+        if (jn[r][u] >= 0 && (jn[r][u] >> 3) == jj) add += 1ull << (8 * (jn[r][u] & 7));
+      const int pos = wo[jj][i >> 5] + __popc(bits[jj][i >> 5] & ((1u << (i & 31)) - 1u));
       atomicAdd(&mult[pos], (unsigned long long)add);
     }
   }
@@ -295,7 +295,7 @@ hipError_t launch_bwd_plan(int B, int N, int nk, const int32_t* q_idx, const int
                            const BwdWorkspace& w, hipStream_t st) {
   if (nk > kMaxNk) return hipErrorInvalidValue;
   const int C = N / 8;
-  if (N <= kSortChunk && C <= kPlanMaxC && C * nk <= kTileSlots) {   // <= 12 slots per thread
+  if (N <= kSortChunk && C <= kPlanMaxC && C * nk <= kPlanMaxSlots && nk % 8 == 0) {
     hipLaunchKernelGGL(plan_small_kernel, dim3(B), dim3(kPlanThreads), 0, st, N, nk, q_idx, key_idx,
                        w.off, w.rev);
     return hipGetLastError();
