@@ -145,14 +145,24 @@ __device__ __forceinline__ int xcd_remap(int w, int n) {
   return x * q + min(x, r) + i;
 }
 
-__device__ __forceinline__ float shfl_max16_32(float v) {
-  v = fmaxf(v, __shfl_xor(v, 16, 64));
-  return fmaxf(v, __shfl_xor(v, 32, 64));
+// Reductions over the four 16-lane rows (lanes c, c+16, c+32, c+48) with the
+// gfx950 row-swap moves: permlane16_swap(x, x) yields x of rows {0,0,2,2} and
+// {1,1,3,3}, permlane32_swap(x, x) x of halves {0,0} and {1,1} (checked on the
+// hardware), so two VALU swaps replace two LDS-crossbar shuffles.
+__device__ __forceinline__ float xrow16(float v, bool take_max) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                  false);
+  const float a = __uint_as_float(r[0]), b = __uint_as_float(r[1]);
+  return take_max ? fmaxf(a, b) : a + b;
 }
-__device__ __forceinline__ float shfl_sum16_32(float v) {
-  v += __shfl_xor(v, 16, 64);
-  return v + __shfl_xor(v, 32, 64);
+__device__ __forceinline__ float xrow32(float v, bool take_max) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                  false);
+  const float a = __uint_as_float(r[0]), b = __uint_as_float(r[1]);
+  return take_max ? fmaxf(a, b) : a + b;
 }
+__device__ __forceinline__ float shfl_max16_32(float v) { return xrow32(xrow16(v, true), true); }
+__device__ __forceinline__ float shfl_sum16_32(float v) { return xrow32(xrow16(v, false), false); }
 
 // wave-uniform item index of this wavefront (scalar register)
 __device__ __forceinline__ int wave_item() {
@@ -208,6 +218,30 @@ __device__ __forceinline__ void wait_vm() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
   __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
 }
+
+// Position of an item (cluster bc of the batch, head pair hp) walked
+// incrementally: a wavefront's items are consecutive, so one division at
+// the start replaces the per-item ones.
+struct ItemPos {
+  int bc, hp, cin, img;   // cluster (batch-wide), head pair, cluster in image, image base token
+  __device__ void init(int item, int HP, int C, int N) {
+    bc = item / HP;
+    hp = item - bc * HP;
+    const int b = bc / C;
+    cin = bc - b * C;
+    img = b * N;
+  }
+  __device__ void next(int HP, int C, int N) {
+    if (++hp == HP) {
+      hp = 0;
+      ++bc;
+      if (++cin == C) {
+        cin = 0;
+        img += N;
+      }
+    }
+  }
+};
 
 // Direct-to-LDS 4-byte load per lane: global (base + voff) -> LDS (lds + 4 * lane).
 __device__ __forceinline__ void dma4(const void* base, uint32_t voff, uint32_t lds) {
@@ -334,22 +368,25 @@ fwd_lds_kernel(int N, int H, int HP, int n_items, int ipw, float scale_log2,
   const int CperImg = N / CS;
 
   // prologue: indices of `first`, then of `first + 1`, then the tiles of `first`
+  ItemPos pc, pn, pnn;   // items it, it + 1, it + 2
+  pc.init(first, HP, CperImg, N);
+  pn = pc;
+  pn.next(HP, CperImg, N);
+  pnn = pn;
+  pnn.next(HP, CperImg, N);
   FwdIdx2 x, xn;
-  gather_idx(first / HP, q_idx, key_idx, lane, ai);
+  gather_idx(pc.bc, q_idx, key_idx, lane, ai);
   wait_vm<0>();
   read_idx(ti, lane, x);
   wait_lgkm0();
-  if (first + 1 < last) gather_idx((first + 1) / HP, q_idx, key_idx, lane, ai);
-  {
-    const int bc = first / HP, h0 = 2 * (first - bc * HP), img = bc / CperImg * N;
-    gather_tile<T>(k, x, img, h0, H, lane, ak);
-    gather_q<T>(q, x, img, h0, H, lane, aq);
-    gather_tile<T>(v, x, img, h0, H, lane, av);
-  }
+  if (first + 1 < last) gather_idx(pn.bc, q_idx, key_idx, lane, ai);
+  gather_tile<T>(k, x, pc.img, 2 * pc.hp, H, lane, ak);
+  gather_q<T>(q, x, pc.img, 2 * pc.hp, H, lane, aq);
+  gather_tile<T>(v, x, pc.img, 2 * pc.hp, H, lane, av);
 
   for (int it = first; it < last; ++it) {
     const bool more = it + 1 < last, more2 = it + 2 < last, prev = it > first;
-    const int bc = it / HP, h0 = 2 * (it - bc * HP), img = bc / CperImg * N;
+    const int h0 = 2 * pc.hp, img = pc.img;
     const bool h1ok = h0 + 1 < H;
     const int hq = left ? h0 : h0 + 1;
 
@@ -358,7 +395,7 @@ fwd_lds_kernel(int N, int H, int HP, int n_items, int ipw, float scale_log2,
     if (more) {
       read_idx(ti, lane, xn);
       wait_lgkm0();
-      if (more2) gather_idx((it + 2) / HP, q_idx, key_idx, lane, ai);
+      if (more2) gather_idx(pnn.bc, q_idx, key_idx, lane, ai);
     }
 
     // S^T = K Q^T: lane holds keys 16b+4g+i of column c16
@@ -378,8 +415,7 @@ fwd_lds_kernel(int N, int H, int HP, int n_items, int ipw, float scale_log2,
     }
     if (more) {   // K tile consumed: refill it for the next item
       wait_lgkm0();
-      const int bn = (it + 1) / HP, hn = 2 * (it + 1 - bn * HP), in = bn / CperImg * N;
-      gather_tile<T>(k, xn, in, hn, H, lane, ak);
+      gather_tile<T>(k, xn, pn.img, 2 * pn.hp, H, lane, ak);
     }
 
     if (__ballot(x.tl < 0) != 0ull) {   // some slot of this list is empty: mask it
@@ -439,9 +475,8 @@ fwd_lds_kernel(int N, int H, int HP, int n_items, int ipw, float scale_log2,
     }
     if (more) {   // Q and V tiles consumed: next item's
       wait_lgkm0();
-      const int bn = (it + 1) / HP, hn = 2 * (it + 1 - bn * HP), in = bn / CperImg * N;
-      gather_q<T>(q, xn, in, hn, H, lane, aq);
-      gather_tile<T>(v, xn, in, hn, H, lane, av);
+      gather_q<T>(q, xn, pn.img, 2 * pn.hp, H, lane, aq);
+      gather_tile<T>(v, xn, pn.img, 2 * pn.hp, H, lane, av);
     }
 
     // exactly three store instructions per item (the pipeline counts them)
@@ -456,6 +491,9 @@ fwd_lds_kernel(int N, int H, int HP, int n_items, int ipw, float scale_log2,
     if (st && g == 0)
       lse[(img + x.qc) * H + hq] = l > 0.f ? (mref + __log2f(l)) * kLn2 : -INFINITY;
     x = xn;
+    pc = pn;
+    pn = pnn;
+    pnn.next(HP, CperImg, N);
   }
 }
 
@@ -746,10 +784,12 @@ bwd_q_lds_kernel(int N, int H, int HP, int n_items, int ipw, float scale,
   const int e = c16 >> 2, qq = c16 & 3;
   const float scale_log2 = scale * kLog2e;
 
-  for (int it = first; it < last; ++it) {
-    const int bc = it / HP;
-    const int h0 = 2 * (it - bc * HP);
-    const int img = bc / (N / CS) * N;
+  ItemPos pos;
+  pos.init(first, HP, N / CS, N);
+  for (int it = first; it < last; ++it, pos.next(HP, N / CS, N)) {
+    const int bc = pos.bc;
+    const int h0 = 2 * pos.hp;
+    const int img = pos.img;
     const bool h1ok = h0 + 1 < H;
     const int hq = left ? h0 : h0 + 1;
     const uint32_t h1off = h1ok ? kRow : 0u;
