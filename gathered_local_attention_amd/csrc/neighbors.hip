@@ -28,6 +28,8 @@
 //                       keys; then the key lists.
 #include "common.h"
 
+#include <algorithm>
+
 namespace ca {
 
 namespace {
@@ -204,7 +206,16 @@ select_kernel(int N, const uint32_t* __restrict__ qsorted, const float2* __restr
   for (int r = 0; r < KB; ++r) best[r] = ~0ull;
   float thr = INFINITY;
 
-  for (int t0 = 0; t0 < C; t0 += kSelectTile) {
+  // Tiles are visited starting with the one holding this workgroup's
+  // clusters, and each thread starts its tile scan at its own cluster:
+  // Morton neighbours come first, so the threshold drops at once and far
+  // candidates fail the fp32 screen.  The kept set does not depend on the
+  // order (exact (d2, index) keys).
+  const int ntiles = (C + kSelectTile - 1) / kSelectTile;
+  const int tfirst = (int)(blockIdx.x * kSelectThreads) / kSelectTile;
+  for (int ti = 0; ti < ntiles; ++ti) {
+    const int tt = tfirst + ti < ntiles ? tfirst + ti : tfirst + ti - ntiles;
+    const int t0 = tt * kSelectTile;
     const int T = min(kSelectTile, C - t0);
     __syncthreads();
     for (int e = threadIdx.x; e < T; e += kSelectThreads)
@@ -212,7 +223,9 @@ select_kernel(int N, const uint32_t* __restrict__ qsorted, const float2* __restr
     __syncthreads();
     if constexpr (KM1 > 0) {
       if (c < C) {
-        for (int e = 0; e < T; ++e) {
+        const int es = (c >= t0 && c < t0 + T) ? c - t0 : 0;
+        for (int i = 0; i < T; ++i) {
+          const int e = es + i < T ? es + i : es + i - T;
           const float dx = cand[e].x - me.x, dy = cand[e].y - me.y;   // exact
           const float d2f = fmaf(dx, dx, dy * dy);
           if (d2f > thr || t0 + e == c) continue;
@@ -260,7 +273,6 @@ select_kernel(int N, const uint32_t* __restrict__ qsorted, const float2* __restr
 // lane shuffles.  grid = B.
 // ---------------------------------------------------------------------------
 constexpr int kSmallThreads = 1024;
-constexpr int kSmallLanes = 4;                 // lanes per cluster in the scan
 constexpr int kSmallMaxC = kSortChunk / 8;     // 256 clusters
 
 __device__ __forceinline__ uint32_t compact16(uint32_t v) {
@@ -292,12 +304,13 @@ __device__ __forceinline__ void top_insert(uint64_t (&best)[KM1 > 0 ? KM1 : 1], 
 
 template <int KM1>
 __global__ void __launch_bounds__(kSmallThreads)
-build_small_kernel(const float* __restrict__ coords, int N, double step, int32_t* __restrict__ perm,
-                   int32_t* __restrict__ nbr, int32_t* __restrict__ key_idx) {
+build_small_kernel(const float* __restrict__ coords, int N, double step, int parts, int lanes,
+                   int32_t* __restrict__ perm, int32_t* __restrict__ nbr,
+                   int32_t* __restrict__ key_idx) {
   __shared__ uint64_t keys[kSortChunk];
   __shared__ int bcnt[kBuckets];
   __shared__ int bstart[kBuckets];
-  __shared__ float2 cent[kSmallMaxC];
+  __shared__ int2 cent[kSmallMaxC];
   __shared__ int scan_tmp[17];
   __shared__ int overflow;
   const int b = blockIdx.x;
@@ -391,47 +404,58 @@ build_small_kernel(const float* __restrict__ coords, int N, double step, int32_t
       sx += (int)compact16(code);
       sy += (int)compact16(code >> 1);
     }
-    cent[c] = make_float2((float)sx, (float)sy);
+    cent[c] = make_int2(sx, sy);
   }
-  int32_t* pimg = perm + (int64_t)b * N;
-  for (int e = tid; e < N; e += kSmallThreads) pimg[e] = (int32_t)(uint32_t)keys[e];
+  if (blockIdx.y == 0) {
+    int32_t* pimg = perm + (int64_t)b * N;
+    for (int e = tid; e < N; e += kSmallThreads) pimg[e] = (int32_t)(uint32_t)keys[e];
+  }
   __syncthreads();
 
-  // candidate scan: cluster c = tid / 4, lane part q scans candidates q, q+4, ...
+  // Candidate scan.  Workgroup y of the image takes clusters
+  // [y*CP, (y+1)*CP) (CP = ceil(C / parts)); `lanes` lanes (a power of two
+  // <= 16) share a cluster: lane q scans the candidates at Morton offsets
+  // +1, -1, +2, -2, ... (mod C) numbered q, q + lanes, ..., so the nearest
+  // in Morton order come first.  Keys are exact (d2 << 24 | index) in 64
+  // bits from integer centroid sums (sums of eight 16-bit coordinates:
+  // |dx| < 2^19, d2 < 2^39, so d2 << 24 < 2^63), and a candidate is inserted
+  // only when it beats the lane's current k-1-th best, which after the
+  // first few near candidates is rare (the wavefront stays off the
+  // divergent insertion path).  The kept set does not depend on the order.
   constexpr int KB = KM1 > 0 ? KM1 : 1;
-  const int q = tid & (kSmallLanes - 1);
-  const int c = tid / kSmallLanes;
+  const int CP = (C + parts - 1) / parts;
+  const int q = tid & (lanes - 1);
+  const int cl = tid / lanes;
+  const int c = blockIdx.y * CP + cl;
+  const bool mine = cl < CP && c < C;
   uint64_t best[KB];
 #pragma unroll
   for (int r = 0; r < KB; ++r) best[r] = ~0ull;
   if constexpr (KM1 > 0) {
-    if (c < C) {
-      const float2 me = cent[c];
-      float thr = INFINITY;
+    if (mine) {
+      const int2 me = cent[c];
       constexpr int U = 4;   // candidates read per iteration (independent LDS loads)
-      for (int e0 = q; e0 < C; e0 += U * kSmallLanes) {
-        float dx[U], dy[U], d2f[U];
+      for (int s0 = q; s0 < C; s0 += U * lanes) {
+        uint64_t key[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-          const int e = e0 + u * kSmallLanes;
-          const float2 cc = cent[e < C ? e : c];
-          dx[u] = cc.x - me.x;   // exact: integer sums below 2^20
-          dy[u] = cc.y - me.y;
-          d2f[u] = fmaf(dx[u], dx[u], dy[u] * dy[u]);
+          const int sn = s0 + u * lanes;                  // candidate number
+          const int o = (sn + 1) >> 1;                    // Morton offset magnitude
+          int e = (sn & 1) ? c + o : c - o;
+          e = e >= C ? e - C : (e < 0 ? e + C : e);
+          const int2 cc = cent[(sn > 0 && sn < C) ? e : c];
+          const int dx = cc.x - me.x, dy = cc.y - me.y;
+          const int64_t d2 = (int64_t)dx * dx + (int64_t)dy * dy;
+          // sn == 0 is the cluster itself; sn >= C is past the end
+          key[u] = (sn > 0 && sn < C) ? ((uint64_t)d2 << 24) | (uint32_t)e : ~0ull;
         }
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-          const int e = e0 + u * kSmallLanes;
-          if (e >= C || e == c || d2f[u] > thr) continue;   // thr may be +inf
-          const int64_t ix = (int64_t)dx[u], iy = (int64_t)dy[u];
-          top_insert<KM1>(best, ((uint64_t)(ix * ix + iy * iy) << 24) | (uint32_t)e);
-          if (best[KM1 - 1] != ~0ull) thr = (float)(best[KM1 - 1] >> 24) * (1.0f + 0x1p-20f);
-        }
+        for (int u = 0; u < U; ++u)
+          if (key[u] < best[KM1 - 1]) top_insert<KM1>(best, key[u]);
       }
     }
-    // merge the four partial lists (lanes tid^1, tid^2 share the cluster)
-#pragma unroll
-    for (int o = 1; o < kSmallLanes; o <<= 1) {
+    // merge the partial lists of the lanes of a cluster (aligned lane groups)
+    for (int o = 1; o < lanes; o <<= 1) {
       uint64_t other[KB];
 #pragma unroll
       for (int r = 0; r < KB; ++r) other[r] = __shfl_xor(best[r], o, 64);
@@ -439,7 +463,7 @@ build_small_kernel(const float* __restrict__ coords, int N, double step, int32_t
       for (int r = 0; r < KB; ++r) top_insert<KM1>(best, other[r]);
     }
   }
-  if (c >= C) return;
+  if (!mine) return;
 
   constexpr int K = KM1 + 1;
   int32_t ids[K];
@@ -450,11 +474,11 @@ build_small_kernel(const float* __restrict__ coords, int N, double step, int32_t
 #pragma unroll
     for (int s = 0; s < K; ++s) nbr[((int64_t)b * C + c) * K + s] = ids[s];
   }
-  // each of the 4 lanes writes every 4th slot group of the key list
+  // the lanes of the cluster write its slot groups round-robin
   int4* krow = reinterpret_cast<int4*>(key_idx + ((int64_t)b * C + c) * K * 8);
 #pragma unroll
   for (int s = 0; s < K; ++s) {
-    if ((s & (kSmallLanes - 1)) != q) continue;
+    if ((s & (lanes - 1)) != q) continue;
     int4 lo = make_int4(-1, -1, -1, -1), hi = lo;
     if (ids[s] >= 0) {
       const int base = 8 * ids[s];
@@ -479,11 +503,17 @@ hipError_t launch_build_neighbors(const float* coords, int B, int N, int grid_si
   BuildWorkspace w = build_layout(ws, B, N);
   const int C = N / 8;
   if (N <= kSortChunk) {
+    // up to 4 workgroups per image share its clusters (each repeats the
+    // in-LDS sort), with up to 16 lanes per cluster in the candidate scan
+    const int parts = std::max(1, std::min(4, (C + 63) / 64));
+    const int cp = (C + parts - 1) / parts;
+    int lanes = 16;
+    while (lanes > 1 && lanes * cp > kSmallThreads) lanes >>= 1;
     switch (k) {
 #define CA_SMALL(KK)                                                                            \
   case KK:                                                                                      \
-    hipLaunchKernelGGL(build_small_kernel<KK - 1>, dim3(B), dim3(kSmallThreads), 0, st, coords, \
-                       N, step, perm, nbr, key_idx);                                            \
+    hipLaunchKernelGGL(build_small_kernel<KK - 1>, dim3(B, parts), dim3(kSmallThreads), 0, st,  \
+                       coords, N, step, parts, lanes, perm, nbr, key_idx);                      \
     break;
       CA_SMALL(1) CA_SMALL(2) CA_SMALL(3) CA_SMALL(4) CA_SMALL(5) CA_SMALL(6) CA_SMALL(7) CA_SMALL(8)
 #undef CA_SMALL
