@@ -924,6 +924,8 @@ bwd_kv_lds_kernel(int N, int H, int HP, int n_items, float scale, const T* __res
                   const int32_t* __restrict__ off_all, const RevEntry* __restrict__ rev_all, int nk,
                   T* __restrict__ dk, T* __restrict__ dv) {
   __shared__ __attribute__((aligned(1024))) char lds[kWaves * kKvWaveLds];
+  // 64 entries per wave: one 16-byte direct-to-LDS load writes all 64 lanes
+  __shared__ __attribute__((aligned(16))) float4 lds_ld[kWaves][64];
   const int item = wave_item();
   if (item >= n_items) return;
   const int lane = threadIdx.x & 63;
@@ -932,6 +934,8 @@ bwd_kv_lds_kernel(int N, int H, int HP, int n_items, float scale, const T* __res
   char* td = tq + kKvTile;
   const uint32_t aq = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)tq;
   const uint32_t ad = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)td;
+  const float4* tl = lds_ld[wv];
+  const uint32_t al = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) float4*)tl;
   const int C = N / CS;
   const int bj = item / HP;
   const int h0 = 2 * (item - bj * HP);
@@ -986,22 +990,33 @@ bwd_kv_lds_kernel(int N, int H, int HP, int n_items, float scale, const T* __res
           dma16(q, o, aq + (uint32_t)u * 1024u);
           dma16(dout, o, ad + (uint32_t)u * 1024u);
         }
+        // (LSE*log2e, Delta) of both heads of query row `lane` (lanes < 32;
+        // lanes 32..63 repeat rows 0..31 into their own slots): 16 bytes at
+        // ld[(img + t) * H + h0].  With
+        // an odd head count the second pair belongs to the next token (or
+        // lies in the next workspace part); it is never used then.
+        const int row = lane & 31;
+        const int t = __shfl(qt, 8 * min(e4 + (row >> 3), ne - 1) + (row & 7), 64);
+        dma16(ld, (uint32_t)((img + t) * H + h0) * 8u, al);
       }
-      // per output row 4g+i of block qb: multiplicity and (LSE*log2e, Delta)
+      // multiplicity of this lane's output rows 4g+i of block qb
       float mult[2];
-      float2 lv[2][4];
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb) {
         const int ee = e4 + 2 * qb + (g >> 1);
         const uint64_t m64 = __shfl(em, min(ee, 7), 64);
         mult[qb] = ee < ne ? (float)((m64 >> (8 * kcol)) & 0xFFu) : 0.f;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int t = __shfl(qt, 8 * min(ee, ne - 1) + ((4 * g + i) & 7), 64);
-          lv[qb][i] = mult[qb] != 0.f ? ld[(img + t) * H + hk] : make_float2(0.f, 0.f);
-        }
       }
       wait_vm<0>();
+      // (LSE*log2e, Delta) of rows 16qb + 4g + i, head hk
+      float2 lv[2][4];
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float4 x = tl[16 * qb + 4 * g + i];
+          lv[qb][i] = left ? make_float2(x.x, x.y) : make_float2(x.z, x.w);
+        }
 
       float p[2][4], ds[2][4];
 #pragma unroll
@@ -1024,14 +1039,13 @@ bwd_kv_lds_kernel(int N, int H, int HP, int n_items, float scale, const T* __res
           ds[qb][i] = p[qb][i] * (dp[i] - lv[qb][i].y);
         }
       }
-      uint2 ph[2], pl[2], dh[2], dlo[2];
+      uint2 ph[2], dh[2];
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb) {
-        split4<T>(p[qb], ph[qb], pl[qb]);
-        split4<T>(ds[qb], dh[qb], dlo[qb]);
+        ph[qb] = make_uint2(pack2<T>(p[qb][0], p[qb][1]), pack2<T>(p[qb][2], p[qb][3]));
+        dh[qb] = make_uint2(pack2<T>(ds[qb][0], ds[qb][1]), pack2<T>(ds[qb][2], ds[qb][3]));
       }
-      const uint4 bph = cat(ph[0], ph[1]), bpl = cat(pl[0], pl[1]);
-      const uint4 bdh = cat(dh[0], dh[1]), bdl = cat(dlo[0], dlo[1]);
+      const uint4 bph = cat(ph[0], ph[1]), bdh = cat(dh[0], dh[1]);
       // transposed reads: lane c16 = 4e + qq of group g receives dim
       // 16hf + c16 of query rows 16qb + 4g + e, e = 0..3
 #pragma unroll
@@ -1050,9 +1064,7 @@ bwd_kv_lds_kernel(int N, int H, int HP, int n_items, float scale, const T* __res
           }
           const uint4 ad4 = cat(at_d[0], at_d[1]), aq4 = cat(at_q[0], at_q[1]);
           dva[hh][hf] = Mfma<T>::mma(ad4, bph, dva[hh][hf]);
-          dva[hh][hf] = Mfma<T>::mma(ad4, bpl, dva[hh][hf]);
           dka[hh][hf] = Mfma<T>::mma(aq4, bdh, dka[hh][hf]);
-          dka[hh][hf] = Mfma<T>::mma(aq4, bdl, dka[hh][hf]);
         }
       }
       // the tiles are rewritten next step: all reads above must be complete
