@@ -24,12 +24,10 @@
 //  * Forward: the gathered rows go to a wavefront-private LDS tile through
 //    direct-to-LDS loads (whole 128-byte rows per eight lanes); K is read
 //    back in the MFMA layout and V through the transposing LDS read.
-//  * Backward: gathers go straight to registers in the MFMA layout; products
-//    that contract over keys or queries transpose the gathered rows on the
-//    MFMA unit with a 0/1 selection matrix (exact: one nonzero product per
-//    output).  P and dS enter the products as a hi + lo pair
-//    (x = hi + lo to ~16 bits) so their rounding stays far below the
-//    output rounding.
+//  * Backward: the same staging; the query-major pass reads K transposed for
+//    dQ, the key-major pass reads Q and dO transposed for dK and dV.  P and
+//    dS are rounded once to the operand type for those products (relative
+//    2^-8 in bf16, far below the bf16 rounding of the outputs).
 //  * Workgroups are remapped so that each XCD (eight, dispatched
 //    round-robin) walks one contiguous Morton range of clusters:
 //    neighbouring clusters share their gathered rows in its L2.
@@ -57,7 +55,6 @@ template <typename T> struct Mfma;
 template <> struct Mfma<bf16> {
   typedef __bf16 v8 __attribute__((ext_vector_type(8)));
   typedef __bf16 v2 __attribute__((ext_vector_type(2)));
-  static constexpr uint32_t kOne = 0x3F80u;
   static __device__ __forceinline__ f32x4 mma(uint4 a, uint4 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8, a),
                                                    __builtin_bit_cast(v8, b), c, 0, 0, 0);
@@ -70,7 +67,6 @@ template <> struct Mfma<bf16> {
 template <> struct Mfma<f16> {
   typedef _Float16 v8 __attribute__((ext_vector_type(8)));
   typedef _Float16 v2 __attribute__((ext_vector_type(2)));
-  static constexpr uint32_t kOne = 0x3C00u;
   static __device__ __forceinline__ f32x4 mma(uint4 a, uint4 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(v8, a),
                                                   __builtin_bit_cast(v8, b), c, 0, 0, 0);
@@ -91,14 +87,6 @@ __device__ __forceinline__ uint2 pack4(f32x4 x) {
   return make_uint2(pack2<T>(x[0], x[1]), pack2<T>(x[2], x[3]));
 }
 
-// x ~= hi + lo with hi = T(x) and lo = T(x - hi), for 4 floats
-template <typename T>
-__device__ __forceinline__ void split4(const float (&x)[4], uint2& hi, uint2& lo) {
-  hi = make_uint2(pack2<T>(x[0], x[1]), pack2<T>(x[2], x[3]));
-  const f32x2 a = Mfma<T>::unpack(hi.x), b = Mfma<T>::unpack(hi.y);
-  lo = make_uint2(pack2<T>(x[0] - a[0], x[1] - a[1]), pack2<T>(x[2] - b[0], x[3] - b[1]));
-}
-
 __device__ __forceinline__ uint4 cat(uint2 a, uint2 b) { return make_uint4(a.x, a.y, b.x, b.y); }
 __device__ __forceinline__ uint4 pad(uint2 a) { return make_uint4(a.x, a.y, 0u, 0u); }
 __device__ __forceinline__ uint4 sel(bool c, uint4 a) {
@@ -112,30 +100,6 @@ __device__ __forceinline__ uint4 ld16(const void* base, uint32_t off) {
 template <typename V>
 __device__ __forceinline__ void stv(void* base, uint32_t off, V v) {
   *reinterpret_cast<V*>(reinterpret_cast<char*>(base) + off) = v;
-}
-
-// 0/1 selection matrix as a B operand: B[k][c] = (k == c + 16 * half), the
-// reduction index k = 8g + e of element e in lane group g.
-template <typename T>
-__device__ __forceinline__ uint4 selector(int g, int c16, int half) {
-  uint32_t w[4];
-#pragma unroll
-  for (int e2 = 0; e2 < 4; ++e2) {
-    const uint32_t lo = (8 * g + 2 * e2 == c16 + 16 * half) ? Mfma<T>::kOne : 0u;
-    const uint32_t hi = (8 * g + 2 * e2 + 1 == c16 + 16 * half) ? Mfma<T>::kOne : 0u;
-    w[e2] = lo | (hi << 16);
-  }
-  return make_uint4(w[0], w[1], w[2], w[3]);
-}
-
-// Transpose a 16-row x 32-dim A-operand tile (lane c16+16g holds row c16,
-// dims [8g, 8g+8)) into two halves usable as A operands over rows: out[h]
-// holds rows 4g..4g+3 of dim c16 + 16h (packed to T).
-template <typename T>
-__device__ __forceinline__ void transpose_rows(uint4 rows, const uint4 (&id)[2], uint2 (&out)[2]) {
-  const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int hf = 0; hf < 2; ++hf) out[hf] = pack4<T>(Mfma<T>::mma(rows, id[hf], z));
 }
 
 __device__ __forceinline__ int xcd_remap(int w, int n) {
@@ -498,258 +462,14 @@ fwd_lds_kernel(int N, int H, int HP, int n_items, int ipw, float scale_log2,
 }
 
 // ---------------------------------------------------------------------------
-// backward pass A (query-major): Delta and dQ
-// ---------------------------------------------------------------------------
-template <typename T>
-__global__ void __launch_bounds__(64 * kWaves)
-bwd_q_mfma_kernel(int N, int H, int HP, int n_items, float scale, const T* __restrict__ q,
-                  const T* __restrict__ k, const T* __restrict__ v, const T* __restrict__ o,
-                  const T* __restrict__ dout, const float* __restrict__ lse,
-                  const int32_t* __restrict__ q_idx, const int32_t* __restrict__ key_idx,
-                  T* __restrict__ dq, float2* __restrict__ ld) {
-  const int item = wave_item();
-  if (item >= n_items) return;
-  const int lane = threadIdx.x & 63;
-  const int bc = item / HP;
-  const int h0 = 2 * (item - bc * HP), h1 = h0 + 1;
-  const int img = bc / (N / CS) * N;
-  const int c16 = lane & 15, g = lane >> 4;
-  const bool left = c16 < 8;
-  const int hq = left ? h0 : h1;
-  const bool h1ok = h1 < H, qok = hq < H;
-  const float scale_log2 = scale * kLog2e;
-  const uint4 zero = make_uint4(0u, 0u, 0u, 0u);
-
-  int kt[3];
-  uint32_t valid[3];
-#pragma unroll
-  for (int b = 0; b < 3; ++b) {
-    kt[b] = key_idx[bc * NK + 16 * b + c16];
-    valid[b] = (uint32_t)__ballot(kt[b] >= 0) & 0xFFFFu;
-    kt[b] = max(kt[b], 0);
-  }
-  const int qtok = q_idx[bc * CS + (c16 & 7)];
-  const uint32_t lo16 = 16u * g;
-  const int qh = (img + qtok) * H + hq;
-  const uint32_t qrow = (uint32_t)qh * kRow + lo16;
-  const uint4 qv = qok ? ld16(q, qrow) : zero;
-  const uint4 dov = qok ? ld16(dout, qrow) : zero;
-  const uint4 ov = qok ? ld16(o, qrow) : zero;
-  const float lse2 = qok ? lse[qh] * kLog2e : 0.f;
-  uint4 ka[3][2], va[3][2];
-#pragma unroll
-  for (int b = 0; b < 3; ++b) {
-    const uint32_t r = (uint32_t)((img + kt[b]) * H + h0) * kRow + lo16;
-    ka[b][0] = ld16(k, r);
-    va[b][0] = ld16(v, r);
-    ka[b][1] = h1ok ? ld16(k, r + kRow) : zero;
-    va[b][1] = h1ok ? ld16(v, r + kRow) : zero;
-  }
-
-  // Delta = <dO, O> per (query, head) column; stored with LSE for pass B
-  float dl = 0.f;
-  {
-    const uint32_t a[4] = {dov.x, dov.y, dov.z, dov.w};
-    const uint32_t c[4] = {ov.x, ov.y, ov.z, ov.w};
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const f32x2 x = Mfma<T>::unpack(a[e]), y = Mfma<T>::unpack(c[e]);
-      dl = fmaf(x[0], y[0], fmaf(x[1], y[1], dl));
-    }
-  }
-  dl = shfl_sum16_32(dl);
-  if (qok && g == 0) ld[qh] = make_float2(lse2, dl);
-
-  const uint4 qL = sel(left, qv), qR = sel(!left, qv);
-  const uint4 dL = sel(left, dov), dR = sel(!left, dov);
-  const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-  float ds[3][4];
-#pragma unroll
-  for (int b = 0; b < 3; ++b) {
-    f32x4 s = Mfma<T>::mma(ka[b][0], qL, z);
-    f32x4 dp = Mfma<T>::mma(va[b][0], dL, z);
-    if (h1ok) {
-      s = Mfma<T>::mma(ka[b][1], qR, s);
-      dp = Mfma<T>::mma(va[b][1], dR, dp);
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const bool ok = (valid[b] >> (4 * g + i)) & 1u;
-      const float p = ok ? __builtin_amdgcn_exp2f(fmaf(s[i], scale_log2, -lse2)) : 0.f;
-      ds[b][i] = p * (dp[i] - dl);
-    }
-  }
-  uint2 dh[3], dlo[3];
-#pragma unroll
-  for (int b = 0; b < 3; ++b) split4<T>(ds[b], dh[b], dlo[b]);
-
-  uint4 id[2];
-  id[0] = selector<T>(g, c16, 0);
-  id[1] = selector<T>(g, c16, 1);
-  f32x4 acc[2] = {z, z};
-#pragma unroll
-  for (int hh = 0; hh < 2; ++hh) {
-    if (hh == 1 && !h1ok) break;
-    const bool mine = (hh == 0) == left;
-    uint2 ktt[3][2];
-#pragma unroll
-    for (int b = 0; b < 3; ++b) transpose_rows<T>(ka[b][hh], id, ktt[b]);
-    const uint4 b0h = sel(mine, cat(dh[0], dh[1])), b0l = sel(mine, cat(dlo[0], dlo[1]));
-    const uint4 b1h = sel(mine, pad(dh[2])), b1l = sel(mine, pad(dlo[2]));
-#pragma unroll
-    for (int hf = 0; hf < 2; ++hf) {
-      const uint4 a01 = cat(ktt[0][hf], ktt[1][hf]), a2 = pad(ktt[2][hf]);
-      acc[hf] = Mfma<T>::mma(a01, b0h, acc[hf]);
-      acc[hf] = Mfma<T>::mma(a2, b1h, acc[hf]);
-      acc[hf] = Mfma<T>::mma(a01, b0l, acc[hf]);
-      acc[hf] = Mfma<T>::mma(a2, b1l, acc[hf]);
-    }
-  }
-  if (!qok) return;
-  const uint32_t drow = (uint32_t)qh * kRow + 8u * g;
-#pragma unroll
-  for (int hf = 0; hf < 2; ++hf) stv<uint2>(dq, drow + 32u * hf, pack4<T>(acc[hf] * scale));
-}
-
-// ---------------------------------------------------------------------------
-// backward pass B (key-major): dK and dV over the transposed lists
-// ---------------------------------------------------------------------------
-// Each iteration takes 4 referencing clusters (32 query rows in two 16-row
-// blocks): S = Q K_j^T and dP = dO V_j^T per block, then dV^T += dO^T P and
-// dK^T += Q^T dS with the 32 rows as one reduction.
-template <typename T>
-__global__ void __launch_bounds__(64 * kWaves)
-bwd_kv_mfma_kernel(int N, int H, int HP, int n_items, float scale, const T* __restrict__ q,
-                   const T* __restrict__ k, const T* __restrict__ v, const T* __restrict__ dout,
-                   const int32_t* __restrict__ q_idx, const float2* __restrict__ ld,
-                   const int32_t* __restrict__ off_all, const RevEntry* __restrict__ rev_all,
-                   int nk, T* __restrict__ dk, T* __restrict__ dv) {
-  const int item = wave_item();
-  if (item >= n_items) return;
-  const int lane = threadIdx.x & 63;
-  const int C = N / CS;
-  const int bj = item / HP;
-  const int h0 = 2 * (item - bj * HP), h1 = h0 + 1;
-  const int b = bj / C;
-  const int j = bj - b * C;
-  const int img = b * N;
-  const int c16 = lane & 15, g = lane >> 4;
-  const bool left = c16 < 8;
-  const int hk = left ? h0 : h1;
-  const bool h1ok = h1 < H, kok = hk < H;
-  const float scale_log2 = scale * kLog2e;
-  const uint4 zero = make_uint4(0u, 0u, 0u, 0u);
-  const uint32_t lo16 = 16u * g;
-
-  // own key rows as B operands (column c16 = key c16&7 of head hk)
-  const int ktok = q_idx[bj * CS + (c16 & 7)];
-  const int kh = (img + ktok) * H + hk;
-  const uint32_t krow = (uint32_t)kh * kRow + lo16;
-  const uint4 kB = kok ? ld16(k, krow) : zero;
-  const uint4 vB = kok ? ld16(v, krow) : zero;
-  const uint4 kL = sel(left, kB), kR = sel(!left, kB);
-  const uint4 vL = sel(left, vB), vR = sel(!left, vB);
-
-  const int32_t* off = off_all + b * (C + 1);
-  const RevEntry* rev = rev_all + (int64_t)b * C * nk;
-  const int e0 = off[j], e1 = off[j + 1];
-
-  uint4 id[2];
-  id[0] = selector<T>(g, c16, 0);
-  id[1] = selector<T>(g, c16, 1);
-  const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-  f32x4 dka[2] = {z, z}, dva[2] = {z, z};
-  const int kcol = c16 & 7;
-
-  for (int e = e0; e < e1; e += 4) {
-    // the (up to) 4 entries of this step, wave-uniform
-    int ei[4];
-    uint64_t em[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const RevEntry r = rev[min(e + u, e1 - 1)];
-      ei[u] = r.i;
-      em[u] = e + u < e1 ? r.mult : 0ull;
-    }
-    uint4 qa[2][2], da[2][2];
-    float p[2][4], ds[2][4];
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-      // A-operand row c16 = query c16&7 of entry 2qb + (c16>>3)
-      const int ea = (c16 >> 3) ? ei[2 * qb + 1] : ei[2 * qb];
-      const int qtok = q_idx[(b * C + ea) * CS + (c16 & 7)];
-      const uint32_t r = (uint32_t)((img + qtok) * H + h0) * kRow + lo16;
-      qa[qb][0] = ld16(q, r);
-      da[qb][0] = ld16(dout, r);
-      qa[qb][1] = h1ok ? ld16(q, r + kRow) : zero;
-      da[qb][1] = h1ok ? ld16(dout, r + kRow) : zero;
-      // this lane's output rows 4g..4g+3 belong to entry 2qb + (g>>1)
-      const uint64_t m64 = (g >> 1) ? em[2 * qb + 1] : em[2 * qb];
-      const float mult = kok ? (float)((m64 >> (8 * kcol)) & 0xFFu) : 0.f;
-      float2 lds[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int t = __shfl(qtok, 4 * g + i, 64);   // query of row 4g+i
-        lds[i] = mult != 0.f ? ld[(img + t) * H + hk] : make_float2(0.f, 0.f);
-      }
-      f32x4 s = Mfma<T>::mma(qa[qb][0], kL, z);
-      f32x4 dp = Mfma<T>::mma(da[qb][0], vL, z);
-      if (h1ok) {
-        s = Mfma<T>::mma(qa[qb][1], kR, s);
-        dp = Mfma<T>::mma(da[qb][1], vR, dp);
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        p[qb][i] = mult != 0.f ? mult * __builtin_amdgcn_exp2f(fmaf(s[i], scale_log2, -lds[i].x)) : 0.f;
-        ds[qb][i] = p[qb][i] * (dp[i] - lds[i].y);
-      }
-    }
-    uint2 ph[2], pl[2], dh[2], dlo[2];
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-      split4<T>(p[qb], ph[qb], pl[qb]);
-      split4<T>(ds[qb], dh[qb], dlo[qb]);
-    }
-#pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
-      if (hh == 1 && !h1ok) break;
-      const bool mine = (hh == 0) == left;
-      uint2 dot[2][2], qt[2][2];
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
-        transpose_rows<T>(da[qb][hh], id, dot[qb]);
-        transpose_rows<T>(qa[qb][hh], id, qt[qb]);
-      }
-      const uint4 bph = sel(mine, cat(ph[0], ph[1])), bpl = sel(mine, cat(pl[0], pl[1]));
-      const uint4 bdh = sel(mine, cat(dh[0], dh[1])), bdl = sel(mine, cat(dlo[0], dlo[1]));
-#pragma unroll
-      for (int hf = 0; hf < 2; ++hf) {
-        const uint4 ad = cat(dot[0][hf], dot[1][hf]), aq = cat(qt[0][hf], qt[1][hf]);
-        dva[hf] = Mfma<T>::mma(ad, bph, dva[hf]);
-        dva[hf] = Mfma<T>::mma(ad, bpl, dva[hf]);
-        dka[hf] = Mfma<T>::mma(aq, bdh, dka[hf]);
-        dka[hf] = Mfma<T>::mma(aq, bdl, dka[hf]);
-      }
-    }
-  }
-
-  if (!kok) return;
-  const uint32_t orow = (uint32_t)kh * kRow + 8u * g;
-#pragma unroll
-  for (int hf = 0; hf < 2; ++hf) {
-    stv<uint2>(dk, orow + 32u * hf, pack4<T>(dka[hf] * scale));
-    stv<uint2>(dv, orow + 32u * hf, pack4<T>(dva[hf]));
-  }
-}
-
-// ---------------------------------------------------------------------------
 // backward pass A (query-major), LDS-staged gathers: Delta and dQ
 // ---------------------------------------------------------------------------
 // Per item (cluster, head pair), the 48 slot rows of K and V and the 8 query
 // rows of Q, dO and O go to a wavefront-private LDS tile (direct-to-LDS
 // loads, whole 128-byte rows).  Delta = <dO, O> per (query, head);
 // S^T = K Q^T and dP^T = V dO^T read K and V in the A layout; dQ^T = K^T dS^T
-// reads K through the transposing LDS read.  dS enters as a hi + lo pair.
+// reads K through the transposing LDS read.  dS is rounded once to the
+// operand type for that product.
 constexpr int kQWaves = 2;
 constexpr int kQWaveLds = 2 * kTileBytes + 3 * 1024;   // K, V, Q, dO, O
 constexpr int kQWavesPerCU = 10;                       // LDS-limited residency
@@ -863,11 +583,11 @@ bwd_q_lds_kernel(int N, int H, int HP, int n_items, int ipw, float scale,
         ds[b][i] = p * (dp[i] - dl);
       }
     }
-    uint2 dh[3], dlo[3];
+    uint2 dh[3];
 #pragma unroll
-    for (int b = 0; b < 3; ++b) split4<T>(ds[b], dh[b], dlo[b]);
-    const uint4 b0h = cat(dh[0], dh[1]), b0l = cat(dlo[0], dlo[1]);
-    const uint4 b1h = pad(dh[2]), b1l = pad(dlo[2]);
+    for (int b = 0; b < 3; ++b)
+      dh[b] = make_uint2(pack2<T>(ds[b][0], ds[b][1]), pack2<T>(ds[b][2], ds[b][3]));
+    const uint4 b0h = cat(dh[0], dh[1]), b1h = pad(dh[2]);
 
     // dQ^T = K^T dS^T per head (transposed K reads, as V in the forward)
     f32x4 acc[2][2] = {{z, z}, {z, z}};
@@ -886,8 +606,6 @@ bwd_q_lds_kernel(int N, int H, int HP, int n_items, int ipw, float scale,
         const uint4 a01 = cat(kt[0], kt[1]), a2 = pad(kt[2]);
         acc[hh][hf] = Mfma<T>::mma(a01, b0h, acc[hh][hf]);
         acc[hh][hf] = Mfma<T>::mma(a2, b1h, acc[hh][hf]);
-        acc[hh][hf] = Mfma<T>::mma(a01, b0l, acc[hh][hf]);
-        acc[hh][hf] = Mfma<T>::mma(a2, b1l, acc[hh][hf]);
       }
     }
     if (hq < H) {
