@@ -313,9 +313,13 @@ fwd_lds_kernel(int N, int H, int HP, int n_items, int ipw, float scale_log2,
                T* __restrict__ o, float* __restrict__ lse) {
   __shared__ __attribute__((aligned(1024))) char lds[kFwdWaves * kFwdWaveLds];
   const int wv = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
-  const int first = (xcd_remap(blockIdx.x, gridDim.x) * kFwdWaves + wv) * ipw;
+  // Items are dealt round-robin over the wavefronts (stride = all of them):
+  // at any moment the wavefronts of one XCD work on one compact window of
+  // consecutive clusters, whose gathered rows then stay in that XCD's L2.
+  const int first = xcd_remap(blockIdx.x, gridDim.x) * kFwdWaves + wv;
+  const int stride = gridDim.x * kFwdWaves;
   if (first >= n_items) return;
-  const int last = min(first + ipw, n_items);
+  (void)ipw;
   const int lane = threadIdx.x & 63;
   const int c16 = lane & 15, g = lane >> 4;
   const bool left = c16 < 8;
@@ -332,24 +336,23 @@ fwd_lds_kernel(int N, int H, int HP, int n_items, int ipw, float scale_log2,
   const int CperImg = N / CS;
 
   // prologue: indices of `first`, then of `first + 1`, then the tiles of `first`
-  ItemPos pc, pn, pnn;   // items it, it + 1, it + 2
+  ItemPos pc, pn, pnn;   // items it, it + stride, it + 2 * stride
   pc.init(first, HP, CperImg, N);
-  pn = pc;
-  pn.next(HP, CperImg, N);
-  pnn = pn;
-  pnn.next(HP, CperImg, N);
+  pn.init(min(first + stride, n_items - 1), HP, CperImg, N);
+  pnn.init(min(first + 2 * stride, n_items - 1), HP, CperImg, N);
   FwdIdx2 x, xn;
   gather_idx(pc.bc, q_idx, key_idx, lane, ai);
   wait_vm<0>();
   read_idx(ti, lane, x);
   wait_lgkm0();
-  if (first + 1 < last) gather_idx(pn.bc, q_idx, key_idx, lane, ai);
+  if (first + stride < n_items) gather_idx(pn.bc, q_idx, key_idx, lane, ai);
   gather_tile<T>(k, x, pc.img, 2 * pc.hp, H, lane, ak);
   gather_q<T>(q, x, pc.img, 2 * pc.hp, H, lane, aq);
   gather_tile<T>(v, x, pc.img, 2 * pc.hp, H, lane, av);
 
-  for (int it = first; it < last; ++it) {
-    const bool more = it + 1 < last, more2 = it + 2 < last, prev = it > first;
+  for (int it = first; it < n_items; it += stride) {
+    const bool more = it + stride < n_items, more2 = it + 2 * stride < n_items;
+    const bool prev = it > first;
     const int h0 = 2 * pc.hp, img = pc.img;
     const bool h1ok = h0 + 1 < H;
     const int hq = left ? h0 : h0 + 1;
@@ -457,7 +460,7 @@ fwd_lds_kernel(int N, int H, int HP, int n_items, int ipw, float scale_log2,
     x = xn;
     pc = pn;
     pn = pnn;
-    pnn.next(HP, CperImg, N);
+    pnn.init(min(it + 3 * stride, n_items - 1), HP, CperImg, N);
   }
 }
 
@@ -484,9 +487,11 @@ bwd_q_lds_kernel(int N, int H, int HP, int n_items, int ipw, float scale,
                  float2* __restrict__ ld) {
   __shared__ __attribute__((aligned(1024))) char lds[kQWaves * kQWaveLds];
   const int wv = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
-  const int first = (xcd_remap(blockIdx.x, gridDim.x) * kQWaves + wv) * ipw;
+  // items dealt round-robin over the wavefronts (see the forward)
+  const int first = xcd_remap(blockIdx.x, gridDim.x) * kQWaves + wv;
+  const int stride = gridDim.x * kQWaves;
   if (first >= n_items) return;
-  const int last = min(first + ipw, n_items);
+  (void)ipw;
   const int lane = threadIdx.x & 63;
   const int c16 = lane & 15, g = lane >> 4;
   const bool left = c16 < 8;
@@ -504,22 +509,31 @@ bwd_q_lds_kernel(int N, int H, int HP, int n_items, int ipw, float scale,
   const int e = c16 >> 2, qq = c16 & 3;
   const float scale_log2 = scale * kLog2e;
 
+  // indices of an item: token of slot `lane` (lanes 48..63 repeat 32..47),
+  // query token of row lane>>3 (gathers) and of column c16.  Those of the
+  // next item are fetched before this item's gathers, so only one memory
+  // latency per item is exposed.
   ItemPos pos;
   pos.init(first, HP, N / CS, N);
-  for (int it = first; it < last; ++it, pos.next(HP, N / CS, N)) {
-    const int bc = pos.bc;
+  int tok = key_idx[pos.bc * NK + (lane < NK ? lane : lane - 16)];
+  int qtr = q_idx[pos.bc * CS + (lane >> 3)];
+  int qtok = q_idx[pos.bc * CS + (c16 & 7)];
+  for (int it = first; it < n_items; it += stride) {
     const int h0 = 2 * pos.hp;
     const int img = pos.img;
     const bool h1ok = h0 + 1 < H;
     const int hq = left ? h0 : h0 + 1;
     const uint32_t h1off = h1ok ? kRow : 0u;
 
-    // indices: token of slot `lane` (lanes 48..63 repeat 32..47); query token
-    // of row lane>>3 (gathers) and of column c16
-    const int tok = key_idx[bc * NK + (lane < NK ? lane : lane - 16)];
-    const int qtr = q_idx[bc * CS + (lane >> 3)];
-    const int qtok = q_idx[bc * CS + (c16 & 7)];
     const float lse2 = lse[(img + qtok) * H + (hq < H ? hq : h0)] * kLog2e;
+    ItemPos pn;
+    pn.init(min(it + stride, n_items - 1), HP, N / CS, N);
+    int tok_n = tok, qtr_n = qtr, qtok_n = qtok;
+    if (it + stride < n_items) {
+      tok_n = key_idx[pn.bc * NK + (lane < NK ? lane : lane - 16)];
+      qtr_n = q_idx[pn.bc * CS + (lane >> 3)];
+      qtok_n = q_idx[pn.bc * CS + (c16 & 7)];
+    }
     {
       const int r = lane >> 3, u = lane & 7;
 #pragma unroll
@@ -615,6 +629,10 @@ bwd_q_lds_kernel(int N, int H, int HP, int n_items, int ipw, float scale,
         stv<uint2>(dq, drow + 32u * hf, pack4<T>((left ? acc[0][hf] : acc[1][hf]) * scale));
     }
     wait_lgkm0();   // tiles are rewritten by the next item
+    pos = pn;
+    tok = tok_n;
+    qtr = qtr_n;
+    qtok = qtok_n;
   }
 }
 
