@@ -195,6 +195,15 @@ struct ItemPos {
     cin = bc - b * C;
     img = b * N;
   }
+  // head-pair-major numbering: item = hp * BC + bc (BC clusters in the batch),
+  // so consecutive items are consecutive clusters of one head pair
+  __device__ void init_hp_major(int item, int BC, int C, int N) {
+    hp = item / BC;
+    bc = item - hp * BC;
+    const int b = bc / C;
+    cin = bc - b * C;
+    img = b * N;
+  }
   __device__ void next(int HP, int C, int N) {
     if (++hp == HP) {
       hp = 0;
@@ -235,6 +244,10 @@ __device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F
 // 48..55 the query tokens of the cluster, 56..63 unused.
 constexpr int kIdxBytes = 256;
 constexpr int kFwdWaves = 2;
+// Waves per CU the launch is sized for (one round over all 256 CUs); the
+// measured optimum at the stage-1 shape is below the LDS/VGPR residency
+// limit of 12.
+constexpr int kFwdWavesPerCU = 8;
 constexpr int kFwdWaveLds = 2 * kTileBytes + 1024 + kIdxBytes;
 
 // Two exec-masked loads (each lane writes only its own 4-byte LDS slot):
@@ -337,9 +350,10 @@ fwd_lds_kernel(int N, int H, int HP, int n_items, int ipw, float scale_log2,
 
   // prologue: indices of `first`, then of `first + 1`, then the tiles of `first`
   ItemPos pc, pn, pnn;   // items it, it + stride, it + 2 * stride
-  pc.init(first, HP, CperImg, N);
-  pn.init(min(first + stride, n_items - 1), HP, CperImg, N);
-  pnn.init(min(first + 2 * stride, n_items - 1), HP, CperImg, N);
+  const int BC = n_items / HP;
+  pc.init_hp_major(first, BC, CperImg, N);
+  pn.init_hp_major(min(first + stride, n_items - 1), BC, CperImg, N);
+  pnn.init_hp_major(min(first + 2 * stride, n_items - 1), BC, CperImg, N);
   FwdIdx2 x, xn;
   gather_idx(pc.bc, q_idx, key_idx, lane, ai);
   wait_vm<0>();
@@ -460,7 +474,7 @@ fwd_lds_kernel(int N, int H, int HP, int n_items, int ipw, float scale_log2,
     x = xn;
     pc = pn;
     pn = pnn;
-    pnn.init(min(it + 3 * stride, n_items - 1), HP, CperImg, N);
+    pnn.init_hp_major(min(it + 3 * stride, n_items - 1), BC, CperImg, N);
   }
 }
 
@@ -475,7 +489,7 @@ fwd_lds_kernel(int N, int H, int HP, int n_items, int ipw, float scale_log2,
 // operand type for that product.
 constexpr int kQWaves = 2;
 constexpr int kQWaveLds = 2 * kTileBytes + 3 * 1024;   // K, V, Q, dO, O
-constexpr int kQWavesPerCU = 10;                       // LDS-limited residency
+constexpr int kQWavesPerCU = 10;                       // LDS-limited residency (5 workgroups)
 
 template <typename T>
 __global__ void __launch_bounds__(64 * kQWaves)
@@ -832,7 +846,7 @@ hipError_t fwd_t(int B, int N, int H, float scale, const void* q, const void* k,
                  hipStream_t st) {
   const int HP = (H + 1) / 2;
   const int items = B * (N / CS) * HP;
-  const int ipw = items_per_wave(items, 12);
+  const int ipw = items_per_wave(items, kFwdWavesPerCU);
   const int waves = (items + ipw - 1) / ipw;
   const int wgs = (waves + kFwdWaves - 1) / kFwdWaves;
   hipLaunchKernelGGL((fwd_lds_kernel<T>), dim3(wgs), dim3(64 * kFwdWaves), 0, st, N, H, HP, items,
