@@ -33,7 +33,7 @@ HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, vendor figure
 ENTRY_KERNELS = {
     "build": ["build_small_kernel (N <= 2048) | rank, merge, centroid, select (N > 2048)"],
     "fwd": ["fwd_lds_kernel"],
-    "bwd": ["plan_small_kernel", "bwd_q_mfma_kernel", "bwd_kv_mfma_kernel"],
+    "bwd": ["plan_small_kernel", "bwd_q_lds_kernel", "bwd_kv_lds_kernel"],
 }
 BF16_MFMA_PEAK_TFLOPS = 2500.0  # dense
 

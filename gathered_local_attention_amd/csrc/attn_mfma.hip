@@ -128,12 +128,6 @@ __device__ __forceinline__ float xrow32(float v, bool take_max) {
 __device__ __forceinline__ float shfl_max16_32(float v) { return xrow32(xrow16(v, true), true); }
 __device__ __forceinline__ float shfl_sum16_32(float v) { return xrow32(xrow16(v, false), false); }
 
-// wave-uniform item index of this wavefront (scalar register)
-__device__ __forceinline__ int wave_item() {
-  const int w = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
-  return xcd_remap(blockIdx.x, gridDim.x) * kWaves + w;
-}
-
 // ---------------------------------------------------------------------------
 // forward, LDS-staged gathers
 // ---------------------------------------------------------------------------
@@ -665,6 +659,7 @@ bwd_q_lds_kernel(int N, int H, int HP, int n_items, int ipw, float scale,
 constexpr int kKvRows = 32;                             // query rows per step
 constexpr int kKvTile = kKvRows * kSlotBytes;           // 4 KiB per tensor
 constexpr int kKvWaveLds = 2 * kKvTile;                 // Q and dO
+constexpr int kKvWavesPerCU = 16;                       // VGPR-limited residency
 
 template <typename T>
 __global__ void __launch_bounds__(64 * kWaves)
@@ -676,10 +671,11 @@ bwd_kv_lds_kernel(int N, int H, int HP, int n_items, float scale, const T* __res
   __shared__ __attribute__((aligned(1024))) char lds[kWaves * kKvWaveLds];
   // 64 entries per wave: one 16-byte direct-to-LDS load writes all 64 lanes
   __shared__ __attribute__((aligned(16))) float4 lds_ld[kWaves][64];
-  const int item = wave_item();
-  if (item >= n_items) return;
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  // items dealt round-robin over the wavefronts (see the forward)
+  const int first = xcd_remap(blockIdx.x, gridDim.x) * kWaves + wv;
+  const int stride = gridDim.x * kWaves;
   char* tq = lds + wv * kKvWaveLds;
   char* td = tq + kKvTile;
   const uint32_t aq = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)tq;
@@ -687,147 +683,150 @@ bwd_kv_lds_kernel(int N, int H, int HP, int n_items, float scale, const T* __res
   const float4* tl = lds_ld[wv];
   const uint32_t al = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) float4*)tl;
   const int C = N / CS;
-  const int bj = item / HP;
-  const int h0 = 2 * (item - bj * HP);
-  const int b = bj / C;
-  const int j = bj - b * C;
-  const int img = b * N;
-  const int c16 = lane & 15, g = lane >> 4;
-  const bool left = c16 < 8;
-  const bool h1ok = h0 + 1 < H;
-  const int hk = left ? h0 : h0 + 1;
-  const uint32_t h1off = h1ok ? kRow : 0u;
-  const float scale_log2 = scale * kLog2e;
-  const int e = c16 >> 2, qq = c16 & 3;
+  for (int item = first; item < n_items; item += stride) {
+    const int bj = item / HP;
+    const int h0 = 2 * (item - bj * HP);
+    const int b = bj / C;
+    const int j = bj - b * C;
+    const int img = b * N;
+    const int c16 = lane & 15, g = lane >> 4;
+    const bool left = c16 < 8;
+    const bool h1ok = h0 + 1 < H;
+    const int hk = left ? h0 : h0 + 1;
+    const uint32_t h1off = h1ok ? kRow : 0u;
+    const float scale_log2 = scale * kLog2e;
+    const int e = c16 >> 2, qq = c16 & 3;
 
-  // own key rows as B operands (column c16 = key c16&7 of head hk)
-  const int ktok = q_idx[bj * CS + (c16 & 7)];
-  const uint32_t krow = (uint32_t)((img + ktok) * H + h0) * kRow + (left ? 0u : h1off) + 16u * g;
-  const uint4 kB = ld16(k, krow), vB = ld16(v, krow);
-  const uint4 kL = sel(left, kB), kR = sel(!left, kB);
-  const uint4 vL = sel(left, vB), vR = sel(!left, vB);
+    // own key rows as B operands (column c16 = key c16&7 of head hk)
+    const int ktok = q_idx[bj * CS + (c16 & 7)];
+    const uint32_t krow = (uint32_t)((img + ktok) * H + h0) * kRow + (left ? 0u : h1off) + 16u * g;
+    const uint4 kB = ld16(k, krow), vB = ld16(v, krow);
+    const uint4 kL = sel(left, kB), kR = sel(!left, kB);
+    const uint4 vL = sel(left, vB), vR = sel(!left, vB);
 
-  const int32_t* off = off_all + b * (C + 1);
-  const RevEntry* rev = rev_all + (int64_t)b * C * nk;
-  const int e0 = off[j], e1 = off[j + 1];
+    const int32_t* off = off_all + b * (C + 1);
+    const RevEntry* rev = rev_all + (int64_t)b * C * nk;
+    const int e0 = off[j], e1 = off[j + 1];
 
-  const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-  f32x4 dka[2][2] = {{z, z}, {z, z}}, dva[2][2] = {{z, z}, {z, z}};   // [head][dim half]
-  const int kcol = c16 & 7;
+    const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+    f32x4 dka[2][2] = {{z, z}, {z, z}}, dva[2][2] = {{z, z}, {z, z}};   // [head][dim half]
+    const int kcol = c16 & 7;
 
-  for (int eb = e0; eb < e1; eb += 8) {
-    // up to 8 entries: lane l holds entry eb + (l & 7); lane 8u + r the token
-    // of member r of entry u
-    const int ne = min(8, e1 - eb);
-    const RevEntry re = rev[eb + min(lane & 7, ne - 1)];
-    const int ei = re.i;
-    const uint64_t em = (lane & 7) < ne ? re.mult : 0ull;
-    const int qt = q_idx[(b * C + __shfl(ei, lane >> 3, 64)) * CS + (lane & 7)];
+    for (int eb = e0; eb < e1; eb += 8) {
+      // up to 8 entries: lane l holds entry eb + (l & 7); lane 8u + r the token
+      // of member r of entry u
+      const int ne = min(8, e1 - eb);
+      const RevEntry re = rev[eb + min(lane & 7, ne - 1)];
+      const int ei = re.i;
+      const uint64_t em = (lane & 7) < ne ? re.mult : 0ull;
+      const int qt = q_idx[(b * C + __shfl(ei, lane >> 3, 64)) * CS + (lane & 7)];
 
-    for (int e4 = 0; e4 < ne; e4 += 4) {
-      // gathers: instruction u holds entry e4 + u (an entry past the end
-      // repeats the last one, with zero multiplicity)
-      {
-        const int r = lane >> 3, u8 = lane & 7;
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int eu = min(e4 + u, ne - 1);
-          const int t = __shfl(qt, 8 * eu + r, 64);
-          const int row = 8 * u + r;
-          const uint32_t c = (uint32_t)u8 ^ swz(row);
-          const uint32_t o = (uint32_t)((img + t) * H + h0) * kRow +
-                             (c < 4u ? 16u * c : h1off + 16u * (c - 4u));
-          dma16(q, o, aq + (uint32_t)u * 1024u);
-          dma16(dout, o, ad + (uint32_t)u * 1024u);
-        }
-        // (LSE*log2e, Delta) of both heads of query row `lane` (lanes < 32;
-        // lanes 32..63 repeat rows 0..31 into their own slots): 16 bytes at
-        // ld[(img + t) * H + h0].  With
-        // an odd head count the second pair belongs to the next token (or
-        // lies in the next workspace part); it is never used then.
-        const int row = lane & 31;
-        const int t = __shfl(qt, 8 * min(e4 + (row >> 3), ne - 1) + (row & 7), 64);
-        dma16(ld, (uint32_t)((img + t) * H + h0) * 8u, al);
-      }
-      // multiplicity of this lane's output rows 4g+i of block qb
-      float mult[2];
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
-        const int ee = e4 + 2 * qb + (g >> 1);
-        const uint64_t m64 = __shfl(em, min(ee, 7), 64);
-        mult[qb] = ee < ne ? (float)((m64 >> (8 * kcol)) & 0xFFu) : 0.f;
-      }
-      wait_vm<0>();
-      // (LSE*log2e, Delta) of rows 16qb + 4g + i, head hk
-      float2 lv[2][4];
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float4 x = tl[16 * qb + 4 * g + i];
-          lv[qb][i] = left ? make_float2(x.x, x.y) : make_float2(x.z, x.w);
-        }
-
-      float p[2][4], ds[2][4];
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
-        const int row = 16 * qb + c16;
-        const uint32_t rb = (uint32_t)row * kSlotBytes;
-        const uint4 q0 = lds16(tq, rb + 16u * ((uint32_t)g ^ swz(row)));
-        const uint4 q1 = lds16(tq, rb + 16u * ((uint32_t)(4 + g) ^ swz(row)));
-        const uint4 d0 = lds16(td, rb + 16u * ((uint32_t)g ^ swz(row)));
-        const uint4 d1 = lds16(td, rb + 16u * ((uint32_t)(4 + g) ^ swz(row)));
-        f32x4 sv = Mfma<T>::mma(q0, kL, z);
-        sv = Mfma<T>::mma(q1, kR, sv);
-        f32x4 dp = Mfma<T>::mma(d0, vL, z);
-        dp = Mfma<T>::mma(d1, vR, dp);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          p[qb][i] = mult[qb] != 0.f
-                         ? mult[qb] * __builtin_amdgcn_exp2f(fmaf(sv[i], scale_log2, -lv[qb][i].x))
-                         : 0.f;
-          ds[qb][i] = p[qb][i] * (dp[i] - lv[qb][i].y);
-        }
-      }
-      uint2 ph[2], dh[2];
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
-        ph[qb] = make_uint2(pack2<T>(p[qb][0], p[qb][1]), pack2<T>(p[qb][2], p[qb][3]));
-        dh[qb] = make_uint2(pack2<T>(ds[qb][0], ds[qb][1]), pack2<T>(ds[qb][2], ds[qb][3]));
-      }
-      const uint4 bph = cat(ph[0], ph[1]), bdh = cat(dh[0], dh[1]);
-      // transposed reads: lane c16 = 4e + qq of group g receives dim
-      // 16hf + c16 of query rows 16qb + 4g + e, e = 0..3
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        if (hh == 1 && !h1ok) break;
-#pragma unroll
-        for (int hf = 0; hf < 2; ++hf) {
-          uint2 at_d[2], at_q[2];
-#pragma unroll
-          for (int qb = 0; qb < 2; ++qb) {
-            const int row = 16 * qb + 4 * g + e;
-            const uint32_t c = (uint32_t)(4 * hh + 2 * hf + (qq >> 1));
-            const uint32_t o = (uint32_t)row * kSlotBytes + 16u * (c ^ swz(row)) + 8u * (qq & 1);
-            at_d[qb] = lds_tr8(td, o);
-            at_q[qb] = lds_tr8(tq, o);
+      for (int e4 = 0; e4 < ne; e4 += 4) {
+        // gathers: instruction u holds entry e4 + u (an entry past the end
+        // repeats the last one, with zero multiplicity)
+        {
+          const int r = lane >> 3, u8 = lane & 7;
+  #pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const int eu = min(e4 + u, ne - 1);
+            const int t = __shfl(qt, 8 * eu + r, 64);
+            const int row = 8 * u + r;
+            const uint32_t c = (uint32_t)u8 ^ swz(row);
+            const uint32_t o = (uint32_t)((img + t) * H + h0) * kRow +
+                               (c < 4u ? 16u * c : h1off + 16u * (c - 4u));
+            dma16(q, o, aq + (uint32_t)u * 1024u);
+            dma16(dout, o, ad + (uint32_t)u * 1024u);
           }
-          const uint4 ad4 = cat(at_d[0], at_d[1]), aq4 = cat(at_q[0], at_q[1]);
-          dva[hh][hf] = Mfma<T>::mma(ad4, bph, dva[hh][hf]);
-          dka[hh][hf] = Mfma<T>::mma(aq4, bdh, dka[hh][hf]);
+          // (LSE*log2e, Delta) of both heads of query row `lane` (lanes < 32;
+          // lanes 32..63 repeat rows 0..31 into their own slots): 16 bytes at
+          // ld[(img + t) * H + h0].  With
+          // an odd head count the second pair belongs to the next token (or
+          // lies in the next workspace part); it is never used then.
+          const int row = lane & 31;
+          const int t = __shfl(qt, 8 * min(e4 + (row >> 3), ne - 1) + (row & 7), 64);
+          dma16(ld, (uint32_t)((img + t) * H + h0) * 8u, al);
         }
-      }
-      // the tiles are rewritten next step: all reads above must be complete
-      wait_lgkm0();
-    }
-  }
+        // multiplicity of this lane's output rows 4g+i of block qb
+        float mult[2];
+  #pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+          const int ee = e4 + 2 * qb + (g >> 1);
+          const uint64_t m64 = __shfl(em, min(ee, 7), 64);
+          mult[qb] = ee < ne ? (float)((m64 >> (8 * kcol)) & 0xFFu) : 0.f;
+        }
+        wait_vm<0>();
+        // (LSE*log2e, Delta) of rows 16qb + 4g + i, head hk
+        float2 lv[2][4];
+  #pragma unroll
+        for (int qb = 0; qb < 2; ++qb)
+  #pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float4 x = tl[16 * qb + 4 * g + i];
+            lv[qb][i] = left ? make_float2(x.x, x.y) : make_float2(x.z, x.w);
+          }
 
-  if (hk >= H) return;
-  const uint32_t orow = (uint32_t)((img + ktok) * H + hk) * kRow + 8u * g;
-#pragma unroll
-  for (int hf = 0; hf < 2; ++hf) {
-    stv<uint2>(dk, orow + 32u * hf, pack4<T>((left ? dka[0][hf] : dka[1][hf]) * scale));
-    stv<uint2>(dv, orow + 32u * hf, pack4<T>(left ? dva[0][hf] : dva[1][hf]));
+        float p[2][4], ds[2][4];
+  #pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+          const int row = 16 * qb + c16;
+          const uint32_t rb = (uint32_t)row * kSlotBytes;
+          const uint4 q0 = lds16(tq, rb + 16u * ((uint32_t)g ^ swz(row)));
+          const uint4 q1 = lds16(tq, rb + 16u * ((uint32_t)(4 + g) ^ swz(row)));
+          const uint4 d0 = lds16(td, rb + 16u * ((uint32_t)g ^ swz(row)));
+          const uint4 d1 = lds16(td, rb + 16u * ((uint32_t)(4 + g) ^ swz(row)));
+          f32x4 sv = Mfma<T>::mma(q0, kL, z);
+          sv = Mfma<T>::mma(q1, kR, sv);
+          f32x4 dp = Mfma<T>::mma(d0, vL, z);
+          dp = Mfma<T>::mma(d1, vR, dp);
+  #pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            p[qb][i] = mult[qb] != 0.f
+                           ? mult[qb] * __builtin_amdgcn_exp2f(fmaf(sv[i], scale_log2, -lv[qb][i].x))
+                           : 0.f;
+            ds[qb][i] = p[qb][i] * (dp[i] - lv[qb][i].y);
+          }
+        }
+        uint2 ph[2], dh[2];
+  #pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+          ph[qb] = make_uint2(pack2<T>(p[qb][0], p[qb][1]), pack2<T>(p[qb][2], p[qb][3]));
+          dh[qb] = make_uint2(pack2<T>(ds[qb][0], ds[qb][1]), pack2<T>(ds[qb][2], ds[qb][3]));
+        }
+        const uint4 bph = cat(ph[0], ph[1]), bdh = cat(dh[0], dh[1]);
+        // transposed reads: lane c16 = 4e + qq of group g receives dim
+        // 16hf + c16 of query rows 16qb + 4g + e, e = 0..3
+  #pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          if (hh == 1 && !h1ok) break;
+  #pragma unroll
+          for (int hf = 0; hf < 2; ++hf) {
+            uint2 at_d[2], at_q[2];
+  #pragma unroll
+            for (int qb = 0; qb < 2; ++qb) {
+              const int row = 16 * qb + 4 * g + e;
+              const uint32_t c = (uint32_t)(4 * hh + 2 * hf + (qq >> 1));
+              const uint32_t o = (uint32_t)row * kSlotBytes + 16u * (c ^ swz(row)) + 8u * (qq & 1);
+              at_d[qb] = lds_tr8(td, o);
+              at_q[qb] = lds_tr8(tq, o);
+            }
+            const uint4 ad4 = cat(at_d[0], at_d[1]), aq4 = cat(at_q[0], at_q[1]);
+            dva[hh][hf] = Mfma<T>::mma(ad4, bph, dva[hh][hf]);
+            dka[hh][hf] = Mfma<T>::mma(aq4, bdh, dka[hh][hf]);
+          }
+        }
+        // the tiles are rewritten next step: all reads above must be complete
+        wait_lgkm0();
+      }
+    }
+
+    if (hk < H) {
+      const uint32_t orow = (uint32_t)((img + ktok) * H + hk) * kRow + 8u * g;
+  #pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        stv<uint2>(dk, orow + 32u * hf, pack4<T>((left ? dka[0][hf] : dka[1][hf]) * scale));
+        stv<uint2>(dv, orow + 32u * hf, pack4<T>(left ? dva[0][hf] : dva[1][hf]));
+      }
+    }
   }
 }
 
@@ -862,7 +861,8 @@ hipError_t bwd_t(int pass, int B, int N, int H, int nk, float scale, const void*
                  const BwdWorkspace& w, hipStream_t st) {
   const int HP = (H + 1) / 2;
   const int items = B * (N / CS) * HP;
-  const int wgs = (items + kWaves - 1) / kWaves;
+  const int kv_ipw = items_per_wave(items, kKvWavesPerCU);
+  const int kv_wgs = ((items + kv_ipw - 1) / kv_ipw + kWaves - 1) / kWaves;
   if (pass & 1) {
     const int ipw = items_per_wave(items, kQWavesPerCU);
     const int waves = (items + ipw - 1) / ipw;
@@ -872,7 +872,7 @@ hipError_t bwd_t(int pass, int B, int N, int H, int nk, float scale, const void*
                        (T*)dq, w.ld);
   }
   if (pass & 2)
-    hipLaunchKernelGGL((bwd_kv_lds_kernel<T>), dim3(wgs), dim3(64 * kWaves), 0, st, N, H, HP,
+    hipLaunchKernelGGL((bwd_kv_lds_kernel<T>), dim3(kv_wgs), dim3(64 * kWaves), 0, st, N, H, HP,
                        items, scale, (const T*)q, (const T*)k, (const T*)v, (const T*)dout, q_idx,
                        (const float2*)w.ld, (const int32_t*)w.off, (const RevEntry*)w.rev, nk,
                        (T*)dk, (T*)dv);

@@ -139,7 +139,8 @@ size_t cluster_attn_bwd_workspace(int dt, int B, int N, int H, int D, int cs, in
  * Two passes: a query-major pass writes dQ and Delta, a key-major pass over a
  * transposed slot list (built in the workspace each call) writes dK and dV
  * directly, so no atomics touch the gradients and the result is bitwise
- * reproducible.  fp32 accumulation throughout; outputs RNE to dt.
+ * reproducible.  fp32 accumulation throughout; P and dS are rounded once to
+ * dt as operands of the dV, dK and dQ products (bf16/f16); outputs RNE to dt.
  *   q, k, v, o, dout [B, N, H, D] dt (o as returned by the forward).
  *   lse       [B, N, H] f32 from the forward.
  *   dq, dk, dv [B, N, H, D] dt out.
