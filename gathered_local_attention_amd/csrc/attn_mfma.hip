@@ -543,23 +543,29 @@ bwd_q_lds_kernel(int N, int H, int HP, int n_items, int ipw, float scale,
       qtok_n = q_idx[pn.bc * CS + (c16 & 7)];
     }
     {
+      // all shuffled offsets first, then the loads (each load's asm block
+      // orders every LDS operation before it)
       const int r = lane >> 3, u = lane & 7;
+      uint32_t offs[NK / 8];
 #pragma unroll
       for (int j = 0; j < NK / 8; ++j) {
         const int sl = 8 * j + r;
         const int t = max(__shfl(tok, sl, 64), 0);
         const uint32_t c = (uint32_t)u ^ swz(sl);
-        const uint32_t off = (uint32_t)((img + t) * H + h0) * kRow +
-                             (c < 4u ? 16u * c : h1off + 16u * (c - 4u));
-        dma16(k, off, ak + (uint32_t)j * 1024u);
-        dma16(v, off, av + (uint32_t)j * 1024u);
+        offs[j] = (uint32_t)((img + t) * H + h0) * kRow +
+                  (c < 4u ? 16u * c : h1off + 16u * (c - 4u));
       }
       const uint32_t c = (uint32_t)u ^ swz(r);
-      const uint32_t off = (uint32_t)((img + qtr) * H + h0) * kRow +
-                           (c < 4u ? 16u * c : h1off + 16u * (c - 4u));
-      dma16(q, off, aq);
-      dma16(dout, off, ado);
-      dma16(o, off, ao);
+      const uint32_t qoffg = (uint32_t)((img + qtr) * H + h0) * kRow +
+                             (c < 4u ? 16u * c : h1off + 16u * (c - 4u));
+#pragma unroll
+      for (int j = 0; j < NK / 8; ++j) {
+        dma16(k, offs[j], ak + (uint32_t)j * 1024u);
+        dma16(v, offs[j], av + (uint32_t)j * 1024u);
+      }
+      dma16(q, qoffg, aq);
+      dma16(dout, qoffg, ado);
+      dma16(o, qoffg, ao);
     }
     wait_vm<0>();
 
@@ -725,26 +731,32 @@ bwd_kv_lds_kernel(int N, int H, int HP, int n_items, float scale, const T* __res
         // gathers: instruction u holds entry e4 + u (an entry past the end
         // repeats the last one, with zero multiplicity)
         {
+          // all shuffled offsets first, then the loads (each load's asm block
+          // orders every LDS operation before it)
           const int r = lane >> 3, u8 = lane & 7;
+          uint32_t offs[4];
   #pragma unroll
           for (int u = 0; u < 4; ++u) {
             const int eu = min(e4 + u, ne - 1);
             const int t = __shfl(qt, 8 * eu + r, 64);
             const int row = 8 * u + r;
             const uint32_t c = (uint32_t)u8 ^ swz(row);
-            const uint32_t o = (uint32_t)((img + t) * H + h0) * kRow +
-                               (c < 4u ? 16u * c : h1off + 16u * (c - 4u));
-            dma16(q, o, aq + (uint32_t)u * 1024u);
-            dma16(dout, o, ad + (uint32_t)u * 1024u);
+            offs[u] = (uint32_t)((img + t) * H + h0) * kRow +
+                      (c < 4u ? 16u * c : h1off + 16u * (c - 4u));
+          }
+          const int lrow = lane & 31;
+          const int tl_tok = __shfl(qt, 8 * min(e4 + (lrow >> 3), ne - 1) + (lrow & 7), 64);
+  #pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            dma16(q, offs[u], aq + (uint32_t)u * 1024u);
+            dma16(dout, offs[u], ad + (uint32_t)u * 1024u);
           }
           // (LSE*log2e, Delta) of both heads of query row `lane` (lanes < 32;
           // lanes 32..63 repeat rows 0..31 into their own slots): 16 bytes at
           // ld[(img + t) * H + h0].  With
           // an odd head count the second pair belongs to the next token (or
           // lies in the next workspace part); it is never used then.
-          const int row = lane & 31;
-          const int t = __shfl(qt, 8 * min(e4 + (row >> 3), ne - 1) + (row & 7), 64);
-          dma16(ld, (uint32_t)((img + t) * H + h0) * 8u, al);
+          dma16(ld, (uint32_t)((img + tl_tok) * H + h0) * 8u, al);
         }
         // multiplicity of this lane's output rows 4g+i of block qb
         float mult[2];
@@ -752,7 +764,8 @@ bwd_kv_lds_kernel(int N, int H, int HP, int n_items, float scale, const T* __res
         for (int qb = 0; qb < 2; ++qb) {
           const int ee = e4 + 2 * qb + (g >> 1);
           const uint64_t m64 = __shfl(em, min(ee, 7), 64);
-          mult[qb] = ee < ne ? (float)((m64 >> (8 * kcol)) & 0xFFu) : 0.f;
+          const uint32_t mw = kcol < 4 ? (uint32_t)m64 : (uint32_t)(m64 >> 32);
+          mult[qb] = ee < ne ? (float)((mw >> (8 * (kcol & 3))) & 0xFFu) : 0.f;
         }
         wait_vm<0>();
         // (LSE*log2e, Delta) of rows 16qb + 4g + i, head hk
