@@ -503,9 +503,9 @@ hipError_t launch_build_neighbors(const float* coords, int B, int N, int grid_si
   BuildWorkspace w = build_layout(ws, B, N);
   const int C = N / 8;
   if (N <= kSortChunk) {
-    // up to 4 workgroups per image share its clusters (each repeats the
+    // up to 8 workgroups per image share its clusters (each repeats the
     // in-LDS sort), with up to 16 lanes per cluster in the candidate scan
-    const int parts = std::max(1, std::min(4, (C + 63) / 64));
+    const int parts = std::max(1, std::min(8, (C + 31) / 32));
     const int cp = (C + parts - 1) / parts;
     int lanes = 16;
     while (lanes > 1 && lanes * cp > kSmallThreads) lanes >>= 1;
