@@ -271,36 +271,41 @@ __device__ __forceinline__ void read_idx(const char* t, int lane, FwdIdx2& x) {
   x.qc = ti[NK + (lane & 7)];
 }
 
-// Gather one tensor's 48 slot rows (both heads of the pair) into an LDS
-// tile: instruction j fills slots 8j..8j+7; lane 8r+u fetches chunk
-// u ^ F(slot) of slot 8j+r, which lands at chunk position u.  With an odd
-// head count the missing second head re-reads the first (never used).
-template <typename T>
-__device__ __forceinline__ void gather_tile(const T* __restrict__ src, const FwdIdx2& x, int img,
-                                            int h0, int H, int lane, uint32_t lds_base) {
-  const int r = lane >> 3, u = lane & 7;
-  const uint32_t h1off = h0 + 1 < H ? kRow : 0u;
-#pragma unroll
-  for (int j = 0; j < NK / 8; ++j) {
-    const int sl = 8 * j + r;
-    const uint32_t c = (uint32_t)u ^ swz(sl);
-    const uint32_t off = (uint32_t)((img + max(x.tj[j], 0)) * H + h0) * kRow +
-                         (c < 4u ? 16u * c : h1off + 16u * (c - 4u));
-    dma16(src, off, lds_base + (uint32_t)j * 1024u);
-  }
+// Byte offsets of one item's gathers.  Lane 8r + u fetches 16-byte chunk
+// u ^ F(slot) of a slot row, which lands at chunk position u of the LDS
+// tile: for slot 8j + r that is chunk u ^ F(8(j & 1) + r), so two column
+// offsets per lane serve all six K/V instructions (K and V share the row
+// offsets) and the query row r (F(r) = F(8 * 0 + r)).  With an odd head
+// count the missing second head re-reads the first (never used).
+struct FwdOffs {
+  uint32_t kv[NK / 8];   // slot rows 8j + (lane >> 3)
+  uint32_t qr;           // query row lane >> 3
+};
+
+// column offset (bytes within the token's row) of chunk position u of slot
+// parity par, for the pair starting at head h0
+__device__ __forceinline__ uint32_t chunk_col(int lane, int par, bool h1ok) {
+  const uint32_t c = (uint32_t)(lane & 7) ^ swz(8 * par + (lane >> 3));
+  return c < 4u ? 16u * c : (h1ok ? kRow : 0u) + 16u * (c - 4u);
 }
 
-// The 8 query rows (both heads of the pair) into a 1 KiB tile: lane 8r+u
-// fetches chunk u ^ F(r) of query r.
+__device__ __forceinline__ void item_offs(const FwdIdx2& x, int img, int h0, int H,
+                                          uint32_t row_bytes, uint32_t col0, uint32_t col1,
+                                          FwdOffs& o) {
+  const uint32_t base = (uint32_t)(img * H + h0) * kRow;
+#pragma unroll
+  for (int j = 0; j < NK / 8; ++j)
+    o.kv[j] = (uint32_t)__umul24((uint32_t)max(x.tj[j], 0), row_bytes) + base + ((j & 1) ? col1 : col0);
+  o.qr = (uint32_t)__umul24((uint32_t)x.tq, row_bytes) + base + col0;
+}
+
+// one tensor's 48 slot rows (both heads of the pair) into an LDS tile:
+// instruction j fills slots 8j..8j+7
 template <typename T>
-__device__ __forceinline__ void gather_q(const T* __restrict__ q, const FwdIdx2& x, int img, int h0,
-                                         int H, int lane, uint32_t lds_base) {
-  const int r = lane >> 3, u = lane & 7;
-  const uint32_t h1off = h0 + 1 < H ? kRow : 0u;
-  const uint32_t c = (uint32_t)u ^ swz(r);
-  const uint32_t off = (uint32_t)((img + x.tq) * H + h0) * kRow +
-                       (c < 4u ? 16u * c : h1off + 16u * (c - 4u));
-  dma16(q, off, lds_base);
+__device__ __forceinline__ void gather_tile(const T* __restrict__ src, const FwdOffs& o,
+                                            uint32_t lds_base) {
+#pragma unroll
+  for (int j = 0; j < NK / 8; ++j) dma16(src, o.kv[j], lds_base + (uint32_t)j * 1024u);
 }
 
 // Forward.  Each wavefront walks a run of `ipw` consecutive items (cluster,
@@ -342,21 +347,52 @@ fwd_lds_kernel(int N, int H, int HP, int n_items, int ipw, float scale_log2,
   const int e = c16 >> 2, qq = c16 & 3;
   const int CperImg = N / CS;
 
+  // Item positions (head-pair-major numbering item = hp * BC + bc) advance
+  // by the fixed stride without divisions.
+  const int BC = n_items / HP;
+  const int st_hp = stride / BC, st_bc = stride - st_hp * BC;
+  const int st_b = st_bc / CperImg, st_c = st_bc - st_b * CperImg;
+  auto step = [&](ItemPos p) {
+    p.hp += st_hp;
+    p.bc += st_bc;
+    p.cin += st_c;
+    p.img += st_b * N;
+    if (p.cin >= CperImg) {
+      p.cin -= CperImg;
+      p.img += N;
+    }
+    if (p.bc >= BC) {
+      p.bc -= BC;
+      p.img -= BC / CperImg * N;
+      ++p.hp;
+    }
+    return p;
+  };
+  const uint32_t row_bytes = (uint32_t)H * kRow;   // one token, all heads
+  // gather column offsets for a pair with / without a second head
+  const uint32_t colA0 = chunk_col(lane, 0, true), colA1 = chunk_col(lane, 1, true);
+  const uint32_t colB0 = chunk_col(lane, 0, false), colB1 = chunk_col(lane, 1, false);
+  auto offs_of = [&](const FwdIdx2& x, const ItemPos& p, FwdOffs& o) {
+    const bool two = 2 * p.hp + 1 < H;
+    item_offs(x, p.img, 2 * p.hp, H, row_bytes, two ? colA0 : colB0, two ? colA1 : colB1, o);
+  };
+
   // prologue: indices of `first`, then of `first + 1`, then the tiles of `first`
   ItemPos pc, pn, pnn;   // items it, it + stride, it + 2 * stride
-  const int BC = n_items / HP;
   pc.init_hp_major(first, BC, CperImg, N);
-  pn.init_hp_major(min(first + stride, n_items - 1), BC, CperImg, N);
-  pnn.init_hp_major(min(first + 2 * stride, n_items - 1), BC, CperImg, N);
+  pn = step(pc);
+  pnn = step(pn);
   FwdIdx2 x, xn;
+  FwdOffs ox, oxn;
   gather_idx(pc.bc, q_idx, key_idx, lane, ai);
   wait_vm<0>();
   read_idx(ti, lane, x);
   wait_lgkm0();
   if (first + stride < n_items) gather_idx(pn.bc, q_idx, key_idx, lane, ai);
-  gather_tile<T>(k, x, pc.img, 2 * pc.hp, H, lane, ak);
-  gather_q<T>(q, x, pc.img, 2 * pc.hp, H, lane, aq);
-  gather_tile<T>(v, x, pc.img, 2 * pc.hp, H, lane, av);
+  offs_of(x, pc, ox);
+  gather_tile<T>(k, ox, ak);
+  dma16(q, ox.qr, aq);
+  gather_tile<T>(v, ox, av);
 
   for (int it = first; it < n_items; it += stride) {
     const bool more = it + stride < n_items, more2 = it + 2 * stride < n_items;
@@ -366,11 +402,13 @@ fwd_lds_kernel(int N, int H, int HP, int n_items, int ipw, float scale_log2,
     const int hq = left ? h0 : h0 + 1;
 
     // K(t), Q(t) and idx(t+1) have landed
-    wait_vm_n(6 + (prev ? 3 : 0));
+    if (prev) wait_vm<9>();
+    else wait_vm<6>();
     if (more) {
       read_idx(ti, lane, xn);
       wait_lgkm0();
       if (more2) gather_idx(pnn.bc, q_idx, key_idx, lane, ai);
+      offs_of(xn, pn, oxn);
     }
 
     // S^T = K Q^T: lane holds keys 16b+4g+i of column c16
@@ -390,7 +428,7 @@ fwd_lds_kernel(int N, int H, int HP, int n_items, int ipw, float scale_log2,
     }
     if (more) {   // K tile consumed: refill it for the next item
       wait_lgkm0();
-      gather_tile<T>(k, xn, pn.img, 2 * pn.hp, H, lane, ak);
+      gather_tile<T>(k, oxn, ak);
     }
 
     if (__ballot(x.tl < 0) != 0ull) {   // some slot of this list is empty: mask it
@@ -426,7 +464,8 @@ fwd_lds_kernel(int N, int H, int HP, int n_items, int ipw, float scale_log2,
     const uint4 bp0 = cat(ph[0], ph[1]), bp1 = pad(ph[2]);
 
     // V(t) has landed
-    wait_vm_n((prev ? 3 : 0) + (more2 ? 2 : 0) + (more ? 6 : 0));
+    if (prev && more2) wait_vm<11>();
+    else wait_vm_n((prev ? 3 : 0) + (more2 ? 2 : 0) + (more ? 6 : 0));
 
     // O^T = V^T P^T per head.  Transposed read: lane c16 = 4e + qq of group g
     // addresses dims 16hf + 4qq.. of slot 16blk + 4g + e and receives dim
@@ -450,25 +489,28 @@ fwd_lds_kernel(int N, int H, int HP, int n_items, int ipw, float scale_log2,
     }
     if (more) {   // Q and V tiles consumed: next item's
       wait_lgkm0();
-      gather_q<T>(q, xn, pn.img, 2 * pn.hp, H, lane, aq);
-      gather_tile<T>(v, xn, pn.img, 2 * pn.hp, H, lane, av);
+      dma16(q, oxn.qr, aq);
+      gather_tile<T>(v, oxn, av);
     }
 
-    // exactly three store instructions per item (the pipeline counts them)
-    const float inv = l > 0.f ? 1.f / l : 0.f;
+    // exactly three store instructions per item (the pipeline counts them);
+    // 1/l through the hardware reciprocal (1 ulp)
+    const float inv = l > 0.f ? __builtin_amdgcn_rcpf(l) : 0.f;
     const bool st = hq < H;
-    const uint32_t orow = (uint32_t)((img + x.qc) * H + (st ? hq : h0)) * kRow + 8u * g;
+    const uint32_t qrow = (uint32_t)__umul24((uint32_t)x.qc, (uint32_t)H) + (uint32_t)(img * H);
+    const uint32_t orow = (qrow + (uint32_t)(st ? hq : h0)) * kRow + 8u * g;
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf) {
       const uint2 ov = pack4<T>((left ? oacc[0][hf] : oacc[1][hf]) * inv);
       if (st) stv<uint2>(o, orow + 32u * hf, ov);
     }
     if (st && g == 0)
-      lse[(img + x.qc) * H + hq] = l > 0.f ? (mref + __log2f(l)) * kLn2 : -INFINITY;
+      lse[qrow + hq] = l > 0.f ? (mref + __log2f(l)) * kLn2 : -INFINITY;
     x = xn;
+    ox = oxn;
     pc = pn;
     pn = pnn;
-    pnn.init_hp_major(min(it + 3 * stride, n_items - 1), BC, CperImg, N);
+    pnn = step(pnn);
   }
 }
 
@@ -654,26 +696,74 @@ bwd_q_lds_kernel(int N, int H, int HP, int n_items, int ipw, float scale,
 // backward pass B (key-major), LDS-staged gathers
 // ---------------------------------------------------------------------------
 // One wavefront per (key cluster j, head pair).  The entries of j (query
-// clusters i reading j, with per-member multiplicities) are taken four at a
-// time: their 32 query rows of Q and dO (both heads) are gathered into a
-// wavefront-private LDS tile with direct-to-LDS loads (instruction u holds
-// entry u's 8 rows).  S = Q K_j^T and dP = dO V_j^T read Q and dO in the
-// MFMA A layout; dV^T += dO^T P and dK^T += Q^T dS read them transposed
-// (ds_read_b64_tr_b16).  One accumulator set per head, so no operand needs
-// zeroed columns.  Summation order is fixed by the entry order (sorted by
-// i), so the result is bitwise reproducible.
+// clusters i reading j, with per-member multiplicities and the query tokens
+// of i) are taken four at a time: their 32 query rows of Q and dO (both
+// heads) are gathered into a wavefront-private LDS tile with direct-to-LDS
+// loads (instruction u holds entry u's 8 rows).  S = Q K_j^T and
+// dP = dO V_j^T read Q and dO in the MFMA A layout; dV^T += dO^T P and
+// dK^T += Q^T dS read them transposed (ds_read_b64_tr_b16).  One accumulator
+// set per head, so no operand needs zeroed columns.  Summation order is
+// fixed by the entry order (sorted by i), so the result is bitwise
+// reproducible.  A multiplicity m enters as exp2(s - LSE + log2 m), which is
+// 0 for an entry past the end of a list (m = 0).
+//
+// The per-item lookups are prefetched one item ahead: when item t starts,
+// the query tokens and multiplicities of the first eight entries of item
+// t+1 go to a wavefront-private LDS block (direct-to-LDS loads; two blocks
+// alternate), its own K/V rows and the segment bounds and key tokens of item
+// t+2 are requested, all ahead of item t's first gathers, so that one wait
+// per four entries covers them.  Loads for later items use clamped (always
+// valid) addresses.  Item positions advance by the fixed stride without
+// divisions.
 constexpr int kKvRows = 32;                             // query rows per step
 constexpr int kKvTile = kKvRows * kSlotBytes;           // 4 KiB per tensor
-constexpr int kKvWaveLds = 2 * kKvTile;                 // Q and dO
-constexpr int kKvWavesPerCU = 16;                       // VGPR-limited residency
+constexpr int kKvMeta = 2 * (64 * 4 + 8 * 8);           // two blocks of 8 entries' tokens, mults
+constexpr int kKvWaveLds = 2 * kKvTile + kKvMeta;       // Q, dO, entry blocks
+constexpr int kKvWavesPerCU = 16;                       // residency (VGPRs and LDS)
+
+// (key cluster of the batch, head pair, image, cluster in image) of an
+// item, stepped by a fixed item stride
+struct KvPos {
+  int item, bj, hp, b, j;
+};
+struct KvStep {
+  int s, s_bj, s_hp, s_b, s_j;
+};
+__device__ __forceinline__ KvPos kv_pos(int item, int HP, int C) {
+  KvPos p;
+  p.item = item;
+  p.bj = item / HP;
+  p.hp = item - p.bj * HP;
+  p.b = p.bj / C;
+  p.j = p.bj - p.b * C;
+  return p;
+}
+__device__ __forceinline__ KvPos kv_next(KvPos p, const KvStep& st, int HP, int C) {
+  p.item += st.s;
+  p.hp += st.s_hp;
+  p.bj += st.s_bj;
+  p.j += st.s_j;
+  p.b += st.s_b;
+  if (p.hp >= HP) {
+    p.hp -= HP;
+    ++p.bj;
+    ++p.j;
+  }
+  if (p.j >= C) {
+    p.j -= C;
+    ++p.b;
+  }
+  return p;
+}
 
 template <typename T>
-__global__ void __launch_bounds__(64 * kWaves)
+__global__ void __launch_bounds__(64 * kWaves, kKvWavesPerCU / 4)
 bwd_kv_lds_kernel(int N, int H, int HP, int n_items, float scale, const T* __restrict__ q,
                   const T* __restrict__ k, const T* __restrict__ v, const T* __restrict__ dout,
                   const int32_t* __restrict__ q_idx, const float2* __restrict__ ld,
-                  const int32_t* __restrict__ off_all, const RevEntry* __restrict__ rev_all, int nk,
-                  T* __restrict__ dk, T* __restrict__ dv) {
+                  const int32_t* __restrict__ off_all, const RevEntry* __restrict__ rev_all,
+                  const int32_t* __restrict__ rtok_all, int nk, T* __restrict__ dk,
+                  T* __restrict__ dv) {
   __shared__ __attribute__((aligned(1024))) char lds[kWaves * kKvWaveLds];
   // 64 entries per wave: one 16-byte direct-to-LDS load writes all 64 lanes
   __shared__ __attribute__((aligned(16))) float4 lds_ld[kWaves][64];
@@ -682,104 +772,155 @@ bwd_kv_lds_kernel(int N, int H, int HP, int n_items, float scale, const T* __res
   // items dealt round-robin over the wavefronts (see the forward)
   const int first = xcd_remap(blockIdx.x, gridDim.x) * kWaves + wv;
   const int stride = gridDim.x * kWaves;
+  if (first >= n_items) return;
   char* tq = lds + wv * kKvWaveLds;
   char* td = tq + kKvTile;
-  const uint32_t aq = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)tq;
-  const uint32_t ad = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)td;
-  const float4* tl = lds_ld[wv];
-  const uint32_t al = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) float4*)tl;
+  char* tm = td + kKvTile;   // [2] x {int tok[64]; uint64 mult[8]}
+  auto lds_addr = [](const void* ptr) {
+    return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const char*)ptr;
+  };
+  const uint32_t aq = lds_addr(tq), ad = lds_addr(td), am = lds_addr(tm);
+  const float2* tl2 = reinterpret_cast<const float2*>(lds_ld[wv]);
+  const uint32_t al = lds_addr(lds_ld[wv]);
   const int C = N / CS;
-  for (int item = first; item < n_items; item += stride) {
-    const int bj = item / HP;
-    const int h0 = 2 * (item - bj * HP);
-    const int b = bj / C;
-    const int j = bj - b * C;
-    const int img = b * N;
-    const int c16 = lane & 15, g = lane >> 4;
-    const bool left = c16 < 8;
+  const int c16 = lane & 15, g = lane >> 4;
+  const bool left = c16 < 8;
+  const int kcol = c16 & 7;
+  const int e = c16 >> 2, qq = c16 & 3;
+  const int r8 = lane >> 3, u8 = lane & 7;
+  const float scale_log2 = scale * kLog2e;
+  const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+  const uint32_t row_bytes = (uint32_t)H * kRow;   // one token, all heads
+
+  KvStep st;
+  st.s = stride;
+  st.s_bj = stride / HP;
+  st.s_hp = stride - st.s_bj * HP;
+  st.s_b = st.s_bj / C;
+  st.s_j = st.s_bj - st.s_b * C;
+
+  // Segment bounds of an item as a vector load (every lane the same 8 bytes):
+  // a scalar load would make every later LDS wait (lgkmcnt) wait for it too.
+  // Its value is first used one item later, when the load is long complete.
+  int vzero;
+  asm volatile("v_mov_b32 %0, 0" : "=v"(vzero));
+  auto seg_of = [&](const KvPos& p) {
+    const int x = p.item < n_items ? p.bj + p.b : 0;
+    return *reinterpret_cast<const int2*>(off_all + x + vzero);
+  };
+  // absolute entry range [e0, e1) of an item (indices into rev / rtok)
+  auto bounds = [&](const KvPos& p, int2 sg, int& e0, int& e1) {
+    const int base = p.b * C * nk;
+    e0 = p.item < n_items ? base + __builtin_amdgcn_readfirstlane(sg.x) : 0;
+    e1 = p.item < n_items ? base + __builtin_amdgcn_readfirstlane(sg.y) : 0;
+  };
+  // block of entries [x0, x0 + 8) (clamped to [x0, x1)) into LDS block `blk`:
+  // int 8u + r = token of member r of entry u, uint64 u = its multiplicities
+  // (two vector-memory operations)
+  auto load_block = [&](int x0, int x1, int blk) {
+    const uint32_t base = am + (uint32_t)blk * (kKvMeta / 2);
+    const int xt = min(x0 + r8, x1 - 1);
+    dma4(rtok_all, (uint32_t)((x1 > x0 ? xt : 0) * 8 + u8) * 4u, base);
+    if (lane < 16) {
+      const int xm = min(x0 + (lane >> 1), x1 - 1);
+      dma4(rev_all, (uint32_t)(x1 > x0 ? xm : 0) * 16u + 8u + 4u * (lane & 1), base + 256u);
+    }
+  };
+  auto key_row = [&](const KvPos& p, int ktok) {
+    const int h0 = 2 * p.hp;
+    const uint32_t h1off = h0 + 1 < H ? kRow : 0u;
+    return (uint32_t)((p.b * N + ktok) * H + h0) * kRow + (left ? 0u : h1off) + 16u * g;
+  };
+
+  // prologue: item `first` and the lookups of the next two
+  KvPos cur = kv_pos(first, HP, C);
+  KvPos nx = kv_next(cur, st, HP, C);
+  int e0, e1;
+  bounds(cur, seg_of(cur), e0, e1);
+  int2 sgn = seg_of(nx);
+  int ktok = q_idx[cur.bj * CS + kcol];
+  int ktok_n = q_idx[(nx.item < n_items ? nx.bj : cur.bj) * CS + kcol];
+  uint4 kB = ld16(k, key_row(cur, ktok)), vB = ld16(v, key_row(cur, ktok));
+  load_block(e0, e1, 0);
+  wait_vm<0>();
+  int blk = 0;
+
+  for (;;) {
+    const int h0 = 2 * cur.hp;
     const bool h1ok = h0 + 1 < H;
     const int hk = left ? h0 : h0 + 1;
     const uint32_t h1off = h1ok ? kRow : 0u;
-    const float scale_log2 = scale * kLog2e;
-    const int e = c16 >> 2, qq = c16 & 3;
+    const int img = cur.b * N;
 
-    // own key rows as B operands (column c16 = key c16&7 of head hk)
-    const int ktok = q_idx[bj * CS + (c16 & 7)];
-    const uint32_t krow = (uint32_t)((img + ktok) * H + h0) * kRow + (left ? 0u : h1off) + 16u * g;
-    const uint4 kB = ld16(k, krow), vB = ld16(v, krow);
+    // prefetch: next item (entry block, own K/V rows) and the one after
+    // (segment bounds, key tokens)
+    const KvPos nxx = kv_next(nx, st, HP, C);
+    int e0n, e1n;
+    bounds(nx, sgn, e0n, e1n);
+    const int2 sgnn = seg_of(nxx);
+    const int ktok_nn = q_idx[(nxx.item < n_items ? nxx.bj : cur.bj) * CS + kcol];
+    load_block(e0n, e1n, blk ^ 1);
+    const uint32_t krn = key_row(nx.item < n_items ? nx : cur, ktok_n);
+    const uint4 kBn = ld16(k, krn), vBn = ld16(v, krn);
+
     const uint4 kL = sel(left, kB), kR = sel(!left, kB);
     const uint4 vL = sel(left, vB), vR = sel(!left, vB);
-
-    const int32_t* off = off_all + b * (C + 1);
-    const RevEntry* rev = rev_all + (int64_t)b * C * nk;
-    const int e0 = off[j], e1 = off[j + 1];
-
-    const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+    // gather byte offsets: row of token t = t * row_bytes + gb[u & 1] for
+    // instruction u (lane 8r + u8 fetches chunk u8 ^ F(8u + r) of its row)
+    uint32_t gb[2];
+#pragma unroll
+    for (int par = 0; par < 2; ++par) {
+      const uint32_t c = (uint32_t)u8 ^ swz(8 * par + r8);
+      gb[par] = (uint32_t)(img * H + h0) * kRow + (c < 4u ? 16u * c : h1off + 16u * (c - 4u));
+    }
+    const uint32_t lb = (uint32_t)(img * H + h0) * 8u;
     f32x4 dka[2][2] = {{z, z}, {z, z}}, dva[2][2] = {{z, z}, {z, z}};   // [head][dim half]
-    const int kcol = c16 & 7;
+    const int* btok = reinterpret_cast<const int*>(tm + blk * (kKvMeta / 2));
+    const uint8_t* bmul = reinterpret_cast<const uint8_t*>(tm + blk * (kKvMeta / 2) + 256);
 
     for (int eb = e0; eb < e1; eb += 8) {
-      // up to 8 entries: lane l holds entry eb + (l & 7); lane 8u + r the token
-      // of member r of entry u
       const int ne = min(8, e1 - eb);
-      const RevEntry re = rev[eb + min(lane & 7, ne - 1)];
-      const int ei = re.i;
-      const uint64_t em = (lane & 7) < ne ? re.mult : 0ull;
-      const int qt = q_idx[(b * C + __shfl(ei, lane >> 3, 64)) * CS + (lane & 7)];
-
+      if (eb > e0) {   // lists with more than eight entries: not prefetched
+        load_block(eb, e1, blk);
+        wait_vm<0>();
+      }
       for (int e4 = 0; e4 < ne; e4 += 4) {
         // gathers: instruction u holds entry e4 + u (an entry past the end
-        // repeats the last one, with zero multiplicity)
+        // repeats the last one, with zero multiplicity); all offsets first,
+        // then the loads (each load's asm block orders every LDS operation
+        // before it)
         {
-          // all shuffled offsets first, then the loads (each load's asm block
-          // orders every LDS operation before it)
-          const int r = lane >> 3, u8 = lane & 7;
           uint32_t offs[4];
-  #pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            const int eu = min(e4 + u, ne - 1);
-            const int t = __shfl(qt, 8 * eu + r, 64);
-            const int row = 8 * u + r;
-            const uint32_t c = (uint32_t)u8 ^ swz(row);
-            offs[u] = (uint32_t)((img + t) * H + h0) * kRow +
-                      (c < 4u ? 16u * c : h1off + 16u * (c - 4u));
-          }
+#pragma unroll
+          for (int u = 0; u < 4; ++u)
+            offs[u] = (uint32_t)btok[8 * min(e4 + u, ne - 1) + r8] * row_bytes + gb[u & 1];
           const int lrow = lane & 31;
-          const int tl_tok = __shfl(qt, 8 * min(e4 + (lrow >> 3), ne - 1) + (lrow & 7), 64);
-  #pragma unroll
+          const int tl_tok = btok[8 * min(e4 + (lrow >> 3), ne - 1) + (lrow & 7)];
+#pragma unroll
           for (int u = 0; u < 4; ++u) {
             dma16(q, offs[u], aq + (uint32_t)u * 1024u);
             dma16(dout, offs[u], ad + (uint32_t)u * 1024u);
           }
           // (LSE*log2e, Delta) of both heads of query row `lane` (lanes < 32;
           // lanes 32..63 repeat rows 0..31 into their own slots): 16 bytes at
-          // ld[(img + t) * H + h0].  With
-          // an odd head count the second pair belongs to the next token (or
-          // lies in the next workspace part); it is never used then.
-          dma16(ld, (uint32_t)((img + tl_tok) * H + h0) * 8u, al);
+          // ld[(img + t) * H + h0].  With an odd head count the second pair
+          // belongs to the next token (or lies in the next workspace part);
+          // it is never used then.
+          dma16(ld, (uint32_t)tl_tok * (uint32_t)H * 8u + lb, al);
         }
-        // multiplicity of this lane's output rows 4g+i of block qb
-        float mult[2];
-  #pragma unroll
+        // log2 of the multiplicity of this lane's output rows 4g+i of block
+        // qb (entry e4 + 2qb + (g >> 1), key member kcol): -inf for 0
+        float lm[2];
+#pragma unroll
         for (int qb = 0; qb < 2; ++qb) {
           const int ee = e4 + 2 * qb + (g >> 1);
-          const uint64_t m64 = __shfl(em, min(ee, 7), 64);
-          const uint32_t mw = kcol < 4 ? (uint32_t)m64 : (uint32_t)(m64 >> 32);
-          mult[qb] = ee < ne ? (float)((mw >> (8 * (kcol & 3))) & 0xFFu) : 0.f;
+          const float m = ee < ne ? (float)bmul[8 * min(ee, 7) + kcol] : 0.f;
+          lm[qb] = __builtin_amdgcn_logf(m);
         }
         wait_vm<0>();
-        // (LSE*log2e, Delta) of rows 16qb + 4g + i, head hk
-        float2 lv[2][4];
-  #pragma unroll
-        for (int qb = 0; qb < 2; ++qb)
-  #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const float4 x = tl[16 * qb + 4 * g + i];
-            lv[qb][i] = left ? make_float2(x.x, x.y) : make_float2(x.z, x.w);
-          }
 
         float p[2][4], ds[2][4];
-  #pragma unroll
+#pragma unroll
         for (int qb = 0; qb < 2; ++qb) {
           const int row = 16 * qb + c16;
           const uint32_t rb = (uint32_t)row * kSlotBytes;
@@ -791,16 +932,16 @@ bwd_kv_lds_kernel(int N, int H, int HP, int n_items, float scale, const T* __res
           sv = Mfma<T>::mma(q1, kR, sv);
           f32x4 dp = Mfma<T>::mma(d0, vL, z);
           dp = Mfma<T>::mma(d1, vR, dp);
-  #pragma unroll
+#pragma unroll
           for (int i = 0; i < 4; ++i) {
-            p[qb][i] = mult[qb] != 0.f
-                           ? mult[qb] * __builtin_amdgcn_exp2f(fmaf(sv[i], scale_log2, -lv[qb][i].x))
-                           : 0.f;
-            ds[qb][i] = p[qb][i] * (dp[i] - lv[qb][i].y);
+            // (LSE*log2e, Delta) of row 16qb + 4g + i, head hk
+            const float2 lv = tl2[2 * (16 * qb + 4 * g + i) + (left ? 0 : 1)];
+            p[qb][i] = __builtin_amdgcn_exp2f(fmaf(sv[i], scale_log2, lm[qb] - lv.x));
+            ds[qb][i] = p[qb][i] * (dp[i] - lv.y);
           }
         }
         uint2 ph[2], dh[2];
-  #pragma unroll
+#pragma unroll
         for (int qb = 0; qb < 2; ++qb) {
           ph[qb] = make_uint2(pack2<T>(p[qb][0], p[qb][1]), pack2<T>(p[qb][2], p[qb][3]));
           dh[qb] = make_uint2(pack2<T>(ds[qb][0], ds[qb][1]), pack2<T>(ds[qb][2], ds[qb][3]));
@@ -808,13 +949,13 @@ bwd_kv_lds_kernel(int N, int H, int HP, int n_items, float scale, const T* __res
         const uint4 bph = cat(ph[0], ph[1]), bdh = cat(dh[0], dh[1]);
         // transposed reads: lane c16 = 4e + qq of group g receives dim
         // 16hf + c16 of query rows 16qb + 4g + e, e = 0..3
-  #pragma unroll
+#pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
           if (hh == 1 && !h1ok) break;
-  #pragma unroll
+#pragma unroll
           for (int hf = 0; hf < 2; ++hf) {
             uint2 at_d[2], at_q[2];
-  #pragma unroll
+#pragma unroll
             for (int qb = 0; qb < 2; ++qb) {
               const int row = 16 * qb + 4 * g + e;
               const uint32_t c = (uint32_t)(4 * hh + 2 * hf + (qq >> 1));
@@ -834,12 +975,23 @@ bwd_kv_lds_kernel(int N, int H, int HP, int n_items, float scale, const T* __res
 
     if (hk < H) {
       const uint32_t orow = (uint32_t)((img + ktok) * H + hk) * kRow + 8u * g;
-  #pragma unroll
+#pragma unroll
       for (int hf = 0; hf < 2; ++hf) {
         stv<uint2>(dk, orow + 32u * hf, pack4<T>((left ? dka[0][hf] : dka[1][hf]) * scale));
         stv<uint2>(dv, orow + 32u * hf, pack4<T>(left ? dva[0][hf] : dva[1][hf]));
       }
     }
+    if (nx.item >= n_items) break;
+    cur = nx;
+    nx = nxx;
+    e0 = e0n;
+    e1 = e1n;
+    sgn = sgnn;
+    ktok = ktok_n;
+    ktok_n = ktok_nn;
+    kB = kBn;
+    vB = vBn;
+    blk ^= 1;
   }
 }
 
@@ -874,8 +1026,8 @@ hipError_t bwd_t(int pass, int B, int N, int H, int nk, float scale, const void*
                  const BwdWorkspace& w, hipStream_t st) {
   const int HP = (H + 1) / 2;
   const int items = B * (N / CS) * HP;
-  const int kv_ipw = items_per_wave(items, kKvWavesPerCU);
-  const int kv_wgs = ((items + kv_ipw - 1) / kv_ipw + kWaves - 1) / kWaves;
+  const int kv_waves = std::min(items, 256 * kKvWavesPerCU);
+  const int kv_wgs = (kv_waves + kWaves - 1) / kWaves;
   if (pass & 1) {
     const int ipw = items_per_wave(items, kQWavesPerCU);
     const int waves = (items + ipw - 1) / ipw;
@@ -887,8 +1039,8 @@ hipError_t bwd_t(int pass, int B, int N, int H, int nk, float scale, const void*
   if (pass & 2)
     hipLaunchKernelGGL((bwd_kv_lds_kernel<T>), dim3(kv_wgs), dim3(64 * kWaves), 0, st, N, H, HP,
                        items, scale, (const T*)q, (const T*)k, (const T*)v, (const T*)dout, q_idx,
-                       (const float2*)w.ld, (const int32_t*)w.off, (const RevEntry*)w.rev, nk,
-                       (T*)dk, (T*)dv);
+                       (const float2*)w.ld, (const int32_t*)w.off, (const RevEntry*)w.rev,
+                       (const int32_t*)w.rtok, nk, (T*)dk, (T*)dv);
   return hipGetLastError();
 }
 

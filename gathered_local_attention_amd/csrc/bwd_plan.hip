@@ -24,6 +24,8 @@
 //   4. staged entries are scattered into their segments (atomic cursor).
 //   5. each segment is sorted by i, which fixes the summation order of the
 //      key-major pass and makes it deterministic.
+//   6. every entry gets the query tokens of its cluster i (the q_idx row),
+//      so that the key-major pass gathers without a further lookup.
 #include "common.h"
 
 namespace ca {
@@ -38,7 +40,8 @@ __global__ void __launch_bounds__(kPlanThreads)
 plan_kernel(int N, int nk, const int32_t* __restrict__ q_idx, const int32_t* __restrict__ key_idx,
             int32_t* __restrict__ inv_all, int32_t* __restrict__ cnt_all,
             int32_t* __restrict__ off_all, int32_t* __restrict__ cur_all,
-            RevEntry* __restrict__ stage_all, RevEntry* __restrict__ rev_all) {
+            RevEntry* __restrict__ stage_all, RevEntry* __restrict__ rev_all,
+            int32_t* __restrict__ rtok_all) {
   __shared__ int32_t jn[kTileSlots];
   __shared__ int32_t scan[kPlanThreads];
   const int b = blockIdx.x;
@@ -149,34 +152,48 @@ plan_kernel(int N, int nk, const int32_t* __restrict__ q_idx, const int32_t* __r
       rev[y + 1] = key;
     }
   }
+  __syncthreads();
+
+  // 6
+  int4* rt = reinterpret_cast<int4*>(rtok_all + (int64_t)b * C * nk * 8);
+  const int total = off[C];
+  for (int x = tid; x < total; x += kPlanThreads) {
+    const int4* row = reinterpret_cast<const int4*>(qi + rev[x].i * 8);
+    rt[2 * x] = row[0];
+    rt[2 * x + 1] = row[1];
+  }
 }
 
 // ---------------------------------------------------------------------------
-// Images with at most 256 clusters and 16384 slots, one workgroup each, all
+// Images with at most 256 clusters and 12288 slots, one workgroup each, all
 // in LDS.  A thread owns whole slot groups (8 consecutive slots of one
 // cluster's list, loaded as two 16-byte vectors) and works on each distinct
-// key cluster j its group points into (usually one): it sets bit i of row j
-// in an LDS bitmap, and later adds the group's member counts for j into the
-// multiplicity bytes of entry (i, j) with one LDS integer atomic (a list has
-// at most 64 slots, so a byte never carries).  Segment sizes are row
-// popcounts and the entry of (i, j) sits at off[j] + (set bits of row j
-// below i), so segments come out ordered by i and the sums are order
-// independent: deterministic without a sort.
+// key cluster j its group points into (usually one, which is checked first):
+// it sets bit i of row j in an LDS bitmap, and later adds the group's member
+// counts for j into the multiplicity bytes of entry (i, j) with one LDS
+// integer atomic (a list has at most 64 slots, so a byte never carries).
+// Segment sizes are row popcounts and the entry of (i, j) sits at off[j] +
+// (set bits of row j below i), so segments come out ordered by i and the
+// sums are order independent: deterministic without a sort.  The thread
+// that adds an entry's multiplicities also records its i, and the entries go
+// out one thread each, together with the q_idx row of their i (the eight
+// query tokens the key-major pass gathers), which the workgroup keeps in LDS.
 // ---------------------------------------------------------------------------
 constexpr int kPlanMaxC = 256;
 constexpr int kPlanWords = kPlanMaxC / 32;
-constexpr int kPlanMaxSlots = 16384;
-constexpr int kGroupsPer = kPlanMaxSlots / 8 / kPlanThreads;   // 2 slot groups per thread
+constexpr int kPlanMaxSlots = 12288;
+constexpr int kGroupsPer = (kPlanMaxSlots / 8 + kPlanThreads - 1) / kPlanThreads;   // 2
 
 __global__ void __launch_bounds__(kPlanThreads)
 plan_small_kernel(int N, int nk, const int32_t* __restrict__ q_idx,
                   const int32_t* __restrict__ key_idx, int32_t* __restrict__ off_all,
-                  RevEntry* __restrict__ rev_all) {
-  __shared__ int32_t inv[kSortChunk];
+                  RevEntry* __restrict__ rev_all, int32_t* __restrict__ rtok_all) {
+  __shared__ int32_t inv[kSortChunk];                       // token -> position c*8 + m
+  __shared__ __attribute__((aligned(16))) int32_t qp[kSortChunk];   // position -> token
   __shared__ uint32_t bits[kPlanMaxC][kPlanWords];
-  __shared__ int32_t off[kPlanMaxC + 1];
   __shared__ int32_t wo[kPlanMaxC][kPlanWords];
   __shared__ unsigned long long mult[kPlanMaxSlots];
+  __shared__ uint8_t ent_i[kPlanMaxSlots];                  // entry -> its query cluster i
   __shared__ int32_t tmp[17];
   const int b = blockIdx.x;
   const int C = N / 8;
@@ -203,18 +220,44 @@ plan_small_kernel(int N, int nk, const int32_t* __restrict__ q_idx,
   const int q1 = tid + kPlanThreads < N ? qi[tid + kPlanThreads] : -1;
   for (int t = tid; t < N; t += kPlanThreads) inv[t] = -1;
   for (int x = tid; x < kPlanMaxC * kPlanWords; x += kPlanThreads) (&bits[0][0])[x] = 0u;
+  if (tid < N) qp[tid] = q0;
+  if (tid + kPlanThreads < N) qp[tid + kPlanThreads] = q1;
   __syncthreads();
   if (q0 >= 0) inv[q0] = tid;
   if (q1 >= 0) inv[q1] = tid + kPlanThreads;
   __syncthreads();
 
-  // key position (j << 3 | member) of every slot; bitmap rows
+  // key position (j << 3 | member) of every slot.  A group that holds the
+  // whole cluster j in member order (as the neighbour build writes it) is
+  // recognised from one lookup and the cluster's q_idx row; any other group
+  // looks up all eight slots.
   int jn[kGroupsPer][8];
+  bool one[kGroupsPer];
+#pragma unroll
+  for (int r = 0; r < kGroupsPer; ++r) {
+    const int p0 = tok[r][0] >= 0 ? inv[tok[r][0]] : -1;
+    bool same = p0 >= 0 && (p0 & 7) == 0;
+    if (same) {
+      const int4 a = reinterpret_cast<const int4*>(qp + p0)[0];
+      const int4 c = reinterpret_cast<const int4*>(qp + p0)[1];
+      same = a.y == tok[r][1] && a.z == tok[r][2] && a.w == tok[r][3] && c.x == tok[r][4] &&
+             c.y == tok[r][5] && c.z == tok[r][6] && c.w == tok[r][7];
+    }
+    one[r] = same;
+    jn[r][0] = p0;
+    if (!same) {
+#pragma unroll
+      for (int m = 1; m < 8; ++m) jn[r][m] = tok[r][m] >= 0 ? inv[tok[r][m]] : -1;
+    }
+  }
+  // bitmap rows
 #pragma unroll
   for (int r = 0; r < kGroupsPer; ++r) {
     const int i = (tid + r * kPlanThreads) * 8 / nk;
-#pragma unroll
-    for (int m = 0; m < 8; ++m) jn[r][m] = tok[r][m] >= 0 ? inv[tok[r][m]] : -1;
+    if (one[r]) {
+      atomicOr(&bits[jn[r][0] >> 3][i >> 5], 1u << (i & 31));
+      continue;
+    }
 #pragma unroll
     for (int m = 0; m < 8; ++m) {
       if (jn[r][m] < 0) continue;
@@ -235,7 +278,6 @@ plan_small_kernel(int N, int nk, const int32_t* __restrict__ q_idx,
   int total;
   const int ex = block_exclusive_scan(v, tmp, kPlanThreads, &total);
   if (tid < C) {
-    off[tid] = ex;
     int a = ex;
 #pragma unroll
     for (int w = 0; w < kPlanWords; ++w) {
@@ -252,6 +294,15 @@ plan_small_kernel(int N, int nk, const int32_t* __restrict__ q_idx,
 #pragma unroll
   for (int r = 0; r < kGroupsPer; ++r) {
     const int i = (tid + r * kPlanThreads) * 8 / nk;
+    const uint32_t below = (1u << (i & 31)) - 1u;
+    if (one[r]) {   // members 0..7 once each
+      const int jj = jn[r][0] >> 3;
+      const uint64_t add = 0x0101010101010101ull;
+      const int pos = wo[jj][i >> 5] + __popc(bits[jj][i >> 5] & below);
+      atomicAdd(&mult[pos], (unsigned long long)add);
+      ent_i[pos] = (uint8_t)i;
+      continue;
+    }
 #pragma unroll
     for (int m = 0; m < 8; ++m) {
       if (jn[r][m] < 0) continue;
@@ -264,28 +315,26 @@ plan_small_kernel(int N, int nk, const int32_t* __restrict__ q_idx,
 #pragma unroll
       for (int u = m; u < 8; ++u)
         if (jn[r][u] >= 0 && (jn[r][u] >> 3) == jj) add += 1ull << (8 * (jn[r][u] & 7));
-      const int pos = wo[jj][i >> 5] + __popc(bits[jj][i >> 5] & ((1u << (i & 31)) - 1u));
+      const int pos = wo[jj][i >> 5] + __popc(bits[jj][i >> 5] & below);
       atomicAdd(&mult[pos], (unsigned long long)add);
+      ent_i[pos] = (uint8_t)i;   // groups of one i that share j store the same value
     }
   }
   __syncthreads();
 
-  // entries out: the segment of key cluster j, ordered by i
+  // entries out, one thread per entry (coalesced stores)
   RevEntry* rev = rev_all + (int64_t)b * ns;
-  for (int jj = tid; jj < C; jj += kPlanThreads) {
-    int pos = off[jj];
-    for (int w = 0; w < kPlanWords; ++w) {
-      uint32_t m = bits[jj][w];
-      while (m) {
-        const int i = 32 * w + __ffs(m) - 1;
-        m &= m - 1;
-        RevEntry e;
-        e.i = i;
-        e.pad = 0;
-        e.mult = mult[pos];
-        rev[pos++] = e;
-      }
-    }
+  int4* rt = reinterpret_cast<int4*>(rtok_all + (int64_t)b * ns * 8);
+  for (int p = tid; p < total; p += kPlanThreads) {
+    const int i = ent_i[p];
+    RevEntry e;
+    e.i = i;
+    e.pad = 0;
+    e.mult = mult[p];
+    rev[p] = e;
+    const int4* row = reinterpret_cast<const int4*>(qp + i * 8);
+    rt[2 * p] = row[0];
+    rt[2 * p + 1] = row[1];
   }
 }
 
@@ -297,11 +346,11 @@ hipError_t launch_bwd_plan(int B, int N, int nk, const int32_t* q_idx, const int
   const int C = N / 8;
   if (N <= kSortChunk && C <= kPlanMaxC && C * nk <= kPlanMaxSlots && nk % 8 == 0) {
     hipLaunchKernelGGL(plan_small_kernel, dim3(B), dim3(kPlanThreads), 0, st, N, nk, q_idx, key_idx,
-                       w.off, w.rev);
+                       w.off, w.rev, w.rtok);
     return hipGetLastError();
   }
   hipLaunchKernelGGL(plan_kernel, dim3(B), dim3(kPlanThreads), 0, st, N, nk, q_idx, key_idx,
-                     w.inv, w.cnt, w.off, w.cursor, w.stage, w.rev);
+                     w.inv, w.cnt, w.off, w.cursor, w.stage, w.rev, w.rtok);
   return hipGetLastError();
 }
 

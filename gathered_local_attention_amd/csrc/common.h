@@ -36,6 +36,7 @@ struct BwdWorkspace {
   int32_t* cursor;   // [B, C]
   RevEntry* stage;   // [B, C, nk]  entry of the first slot of i pointing into j
   RevEntry* rev;     // [B, C*nk]   per key cluster, sorted by i
+  int32_t* rtok;     // [B, C*nk, cs] query tokens of entry e (q_idx row of its i)
   size_t bytes;
 };
 
@@ -58,6 +59,7 @@ static inline BwdWorkspace bwd_layout(void* base, int64_t B, int64_t N, int64_t 
   w.cursor = (int32_t*)take((size_t)(B * C) * sizeof(int32_t));
   w.stage = (RevEntry*)take((size_t)(B * C * nk) * sizeof(RevEntry));
   w.rev = (RevEntry*)take((size_t)(B * C * nk) * sizeof(RevEntry));
+  w.rtok = (int32_t*)take((size_t)(B * C * nk) * 8 * sizeof(int32_t));
   w.bytes = p;
   return w;
 }
