@@ -514,215 +514,8 @@ fwd_lds_kernel(int N, int H, int HP, int n_items, int ipw, float scale_log2,
   }
 }
 
-// ---------------------------------------------------------------------------
-// backward pass A (query-major), LDS-staged gathers: Delta and dQ
-// ---------------------------------------------------------------------------
-// Per item (cluster, head pair), the 48 slot rows of K and V and the 8 query
-// rows of Q, dO and O go to a wavefront-private LDS tile (direct-to-LDS
-// loads, whole 128-byte rows).  Delta = <dO, O> per (query, head);
-// S^T = K Q^T and dP^T = V dO^T read K and V in the A layout; dQ^T = K^T dS^T
-// reads K through the transposing LDS read.  dS is rounded once to the
-// operand type for that product.
-constexpr int kQWaves = 2;
-constexpr int kQWaveLds = 2 * kTileBytes + 3 * 1024;   // K, V, Q, dO, O
-constexpr int kQWavesPerCU = 10;                       // LDS-limited residency (5 workgroups)
-
-template <typename T>
-__global__ void __launch_bounds__(64 * kQWaves)
-bwd_q_lds_kernel(int N, int H, int HP, int n_items, int ipw, float scale,
-                 const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
-                 const T* __restrict__ o, const T* __restrict__ dout,
-                 const float* __restrict__ lse, const int32_t* __restrict__ q_idx,
-                 const int32_t* __restrict__ key_idx, T* __restrict__ dq,
-                 float2* __restrict__ ld) {
-  __shared__ __attribute__((aligned(1024))) char lds[kQWaves * kQWaveLds];
-  const int wv = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
-  // items dealt round-robin over the wavefronts (see the forward)
-  const int first = xcd_remap(blockIdx.x, gridDim.x) * kQWaves + wv;
-  const int stride = gridDim.x * kQWaves;
-  if (first >= n_items) return;
-  (void)ipw;
-  const int lane = threadIdx.x & 63;
-  const int c16 = lane & 15, g = lane >> 4;
-  const bool left = c16 < 8;
-  char* tk = lds + wv * kQWaveLds;
-  char* tv = tk + kTileBytes;
-  char* tq = tv + kTileBytes;
-  char* tdo = tq + 1024;
-  char* to = tdo + 1024;
-  auto lds_addr = [](char* ptr) {
-    return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)ptr;
-  };
-  const uint32_t ak = lds_addr(tk), av = lds_addr(tv), aq = lds_addr(tq), ado = lds_addr(tdo),
-                 ao = lds_addr(to);
-  const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-  const int e = c16 >> 2, qq = c16 & 3;
-  const float scale_log2 = scale * kLog2e;
-
-  // indices of an item: token of slot `lane` (lanes 48..63 repeat 32..47),
-  // query token of row lane>>3 (gathers) and of column c16.  Those of the
-  // next item are fetched before this item's gathers, so only one memory
-  // latency per item is exposed.
-  ItemPos pos;
-  pos.init(first, HP, N / CS, N);
-  int tok = key_idx[pos.bc * NK + (lane < NK ? lane : lane - 16)];
-  int qtr = q_idx[pos.bc * CS + (lane >> 3)];
-  int qtok = q_idx[pos.bc * CS + (c16 & 7)];
-  for (int it = first; it < n_items; it += stride) {
-    const int h0 = 2 * pos.hp;
-    const int img = pos.img;
-    const bool h1ok = h0 + 1 < H;
-    const int hq = left ? h0 : h0 + 1;
-    const uint32_t h1off = h1ok ? kRow : 0u;
-
-    const float lse2 = lse[(img + qtok) * H + (hq < H ? hq : h0)] * kLog2e;
-    ItemPos pn;
-    pn.init(min(it + stride, n_items - 1), HP, N / CS, N);
-    int tok_n = tok, qtr_n = qtr, qtok_n = qtok;
-    if (it + stride < n_items) {
-      tok_n = key_idx[pn.bc * NK + (lane < NK ? lane : lane - 16)];
-      qtr_n = q_idx[pn.bc * CS + (lane >> 3)];
-      qtok_n = q_idx[pn.bc * CS + (c16 & 7)];
-    }
-    {
-      // all shuffled offsets first, then the loads (each load's asm block
-      // orders every LDS operation before it)
-      const int r = lane >> 3, u = lane & 7;
-      uint32_t offs[NK / 8];
-#pragma unroll
-      for (int j = 0; j < NK / 8; ++j) {
-        const int sl = 8 * j + r;
-        const int t = max(__shfl(tok, sl, 64), 0);
-        const uint32_t c = (uint32_t)u ^ swz(sl);
-        offs[j] = (uint32_t)((img + t) * H + h0) * kRow +
-                  (c < 4u ? 16u * c : h1off + 16u * (c - 4u));
-      }
-      const uint32_t c = (uint32_t)u ^ swz(r);
-      const uint32_t qoffg = (uint32_t)((img + qtr) * H + h0) * kRow +
-                             (c < 4u ? 16u * c : h1off + 16u * (c - 4u));
-#pragma unroll
-      for (int j = 0; j < NK / 8; ++j) {
-        dma16(k, offs[j], ak + (uint32_t)j * 1024u);
-        dma16(v, offs[j], av + (uint32_t)j * 1024u);
-      }
-      dma16(q, qoffg, aq);
-      dma16(dout, qoffg, ado);
-      dma16(o, qoffg, ao);
-    }
-    wait_vm<0>();
-
-    // B operands (column c16 = query c16&7, head hq): Q and dO rows; Delta
-    const int qm = c16 & 7;
-    const uint32_t qoff = (uint32_t)qm * kSlotBytes +
-                          16u * ((uint32_t)((c16 >> 3) * 4 + g) ^ swz(qm));
-    const uint4 qv = lds16(tq, qoff), dov = lds16(tdo, qoff), ov = lds16(to, qoff);
-    float dl = 0.f;
-    {
-      const uint32_t a[4] = {dov.x, dov.y, dov.z, dov.w};
-      const uint32_t c[4] = {ov.x, ov.y, ov.z, ov.w};
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const f32x2 x = Mfma<T>::unpack(a[i]), y = Mfma<T>::unpack(c[i]);
-        dl = fmaf(x[0], y[0], fmaf(x[1], y[1], dl));
-      }
-    }
-    dl = shfl_sum16_32(dl);
-    if (hq < H && g == 0) ld[(img + qtok) * H + hq] = make_float2(lse2, dl);
-
-    const uint4 qL = sel(left, qv), qR = sel(!left, qv);
-    const uint4 dL = sel(left, dov), dR = sel(!left, dov);
-    float ds[3][4];
-    const uint64_t vb64 = __ballot(tok >= 0);
-#pragma unroll
-    for (int b = 0; b < 3; ++b) {
-      const int sl = 16 * b + c16;
-      const uint32_t row = (uint32_t)sl * kSlotBytes;
-      const uint4 k0 = lds16(tk, row + 16u * ((uint32_t)g ^ swz(sl)));
-      const uint4 k1 = lds16(tk, row + 16u * ((uint32_t)(4 + g) ^ swz(sl)));
-      const uint4 v0 = lds16(tv, row + 16u * ((uint32_t)g ^ swz(sl)));
-      const uint4 v1 = lds16(tv, row + 16u * ((uint32_t)(4 + g) ^ swz(sl)));
-      f32x4 sv = Mfma<T>::mma(k0, qL, z);
-      sv = Mfma<T>::mma(k1, qR, sv);
-      f32x4 dp = Mfma<T>::mma(v0, dL, z);
-      dp = Mfma<T>::mma(v1, dR, dp);
-      const uint32_t vb = (uint32_t)(vb64 >> (16 * b));
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const bool ok = (vb >> (4 * g + i)) & 1u;
-        const float p = ok ? __builtin_amdgcn_exp2f(fmaf(sv[i], scale_log2, -lse2)) : 0.f;
-        ds[b][i] = p * (dp[i] - dl);
-      }
-    }
-    uint2 dh[3];
-#pragma unroll
-    for (int b = 0; b < 3; ++b)
-      dh[b] = make_uint2(pack2<T>(ds[b][0], ds[b][1]), pack2<T>(ds[b][2], ds[b][3]));
-    const uint4 b0h = cat(dh[0], dh[1]), b1h = pad(dh[2]);
-
-    // dQ^T = K^T dS^T per head (transposed K reads, as V in the forward)
-    f32x4 acc[2][2] = {{z, z}, {z, z}};
-#pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
-      if (hh == 1 && !h1ok) break;
-#pragma unroll
-      for (int hf = 0; hf < 2; ++hf) {
-        uint2 kt[3];
-#pragma unroll
-        for (int blk = 0; blk < 3; ++blk) {
-          const int sl = 16 * blk + 4 * g + e;
-          const uint32_t c = (uint32_t)(4 * hh + 2 * hf + (qq >> 1));
-          kt[blk] = lds_tr8(tk, (uint32_t)sl * kSlotBytes + 16u * (c ^ swz(sl)) + 8u * (qq & 1));
-        }
-        const uint4 a01 = cat(kt[0], kt[1]), a2 = pad(kt[2]);
-        acc[hh][hf] = Mfma<T>::mma(a01, b0h, acc[hh][hf]);
-        acc[hh][hf] = Mfma<T>::mma(a2, b1h, acc[hh][hf]);
-      }
-    }
-    if (hq < H) {
-      const uint32_t drow = (uint32_t)((img + qtok) * H + hq) * kRow + 8u * g;
-#pragma unroll
-      for (int hf = 0; hf < 2; ++hf)
-        stv<uint2>(dq, drow + 32u * hf, pack4<T>((left ? acc[0][hf] : acc[1][hf]) * scale));
-    }
-    wait_lgkm0();   // tiles are rewritten by the next item
-    pos = pn;
-    tok = tok_n;
-    qtr = qtr_n;
-    qtok = qtok_n;
-  }
-}
-
-// ---------------------------------------------------------------------------
-// backward pass B (key-major), LDS-staged gathers
-// ---------------------------------------------------------------------------
-// One wavefront per (key cluster j, head pair).  The entries of j (query
-// clusters i reading j, with per-member multiplicities and the query tokens
-// of i) are taken four at a time: their 32 query rows of Q and dO (both
-// heads) are gathered into a wavefront-private LDS tile with direct-to-LDS
-// loads (instruction u holds entry u's 8 rows).  S = Q K_j^T and
-// dP = dO V_j^T read Q and dO in the MFMA A layout; dV^T += dO^T P and
-// dK^T += Q^T dS read them transposed (ds_read_b64_tr_b16).  One accumulator
-// set per head, so no operand needs zeroed columns.  Summation order is
-// fixed by the entry order (sorted by i), so the result is bitwise
-// reproducible.  A multiplicity m enters as exp2(s - LSE + log2 m), which is
-// 0 for an entry past the end of a list (m = 0).
-//
-// The per-item lookups are prefetched one item ahead: when item t starts,
-// the query tokens and multiplicities of the first eight entries of item
-// t+1 go to a wavefront-private LDS block (direct-to-LDS loads; two blocks
-// alternate), its own K/V rows and the segment bounds and key tokens of item
-// t+2 are requested, all ahead of item t's first gathers, so that one wait
-// per four entries covers them.  Loads for later items use clamped (always
-// valid) addresses.  Item positions advance by the fixed stride without
-// divisions.
-constexpr int kKvRows = 32;                             // query rows per step
-constexpr int kKvTile = kKvRows * kSlotBytes;           // 4 KiB per tensor
-constexpr int kKvMeta = 2 * (64 * 4 + 8 * 8);           // two blocks of 8 entries' tokens, mults
-constexpr int kKvWaveLds = 2 * kKvTile + kKvMeta;       // Q, dO, entry blocks
-constexpr int kKvWavesPerCU = 16;                       // residency (VGPRs and LDS)
-
-// (key cluster of the batch, head pair, image, cluster in image) of an
-// item, stepped by a fixed item stride
+// (cluster of the batch, head pair, image, cluster in image) of an item
+// numbered item = cluster * HP + pair, stepped by a fixed item stride
 struct KvPos {
   int item, bj, hp, b, j;
 };
@@ -755,6 +548,248 @@ __device__ __forceinline__ KvPos kv_next(KvPos p, const KvStep& st, int HP, int 
   }
   return p;
 }
+
+// ---------------------------------------------------------------------------
+// backward pass A (query-major), LDS-staged gathers: Delta and dQ
+// ---------------------------------------------------------------------------
+// Per item (cluster, head pair), the 48 slot rows of K and V and the 8 query
+// rows of Q, dO and O go to a wavefront-private LDS tile (direct-to-LDS
+// loads, whole 128-byte rows).  Delta = <dO, O> per (query, head);
+// S^T = K Q^T and dP^T = V dO^T read K and V in the A layout; dQ^T = K^T dS^T
+// reads K through the transposing LDS read.  dS is rounded once to the
+// operand type for that product.
+//
+// Pipeline: at the top of item t every LDS operand of t is read into
+// registers at once, which frees the tiles; the gathers of item t+1 are then
+// issued and land while item t is computed from registers.  The index rows
+// (key_idx and q_idx rows, as in the forward) run one item further ahead and
+// the LSE values one item ahead, both through small LDS tiles, so that no
+// register load crosses an iteration.  The three stores of an item are the
+// last memory operations of its step: the wait at the top leaves exactly
+// them in flight.
+constexpr int kQWaves = 2;
+constexpr int kQWaveLds = 2 * kTileBytes + 3 * 1024 + kIdxBytes + 64;   // K, V, Q, dO, O, idx, LSE
+constexpr int kQWavesPerCU = 8;
+
+template <typename T>
+__global__ void __launch_bounds__(64 * kQWaves)
+bwd_q_lds_kernel(int N, int H, int HP, int n_items, int ipw, float scale,
+                 const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
+                 const T* __restrict__ o, const T* __restrict__ dout,
+                 const float* __restrict__ lse, const int32_t* __restrict__ q_idx,
+                 const int32_t* __restrict__ key_idx, T* __restrict__ dq,
+                 float2* __restrict__ ld) {
+  __shared__ __attribute__((aligned(1024))) char lds[kQWaves * kQWaveLds];
+  const int wv = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  // items dealt round-robin over the wavefronts (see the forward)
+  const int first = xcd_remap(blockIdx.x, gridDim.x) * kQWaves + wv;
+  const int stride = gridDim.x * kQWaves;
+  if (first >= n_items) return;
+  (void)ipw;
+  const int lane = threadIdx.x & 63;
+  const int c16 = lane & 15, g = lane >> 4;
+  const bool left = c16 < 8;
+  char* tk = lds + wv * kQWaveLds;
+  char* tv = tk + kTileBytes;
+  char* tq = tv + kTileBytes;
+  char* tdo = tq + 1024;
+  char* to = tdo + 1024;
+  char* ti = to + 1024;
+  const float* tls = reinterpret_cast<const float*>(ti + kIdxBytes);
+  auto lds_addr = [](const char* ptr) {
+    return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const char*)ptr;
+  };
+  const uint32_t ak = lds_addr(tk), av = lds_addr(tv), aq = lds_addr(tq), ado = lds_addr(tdo),
+                 ao = lds_addr(to), ai = lds_addr(ti), als = lds_addr(ti + kIdxBytes);
+  const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+  const int e = c16 >> 2, qq = c16 & 3;
+  const float scale_log2 = scale * kLog2e;
+  const int C = N / CS;
+  const uint32_t row_bytes = (uint32_t)H * kRow;   // one token, all heads
+  const uint32_t colA0 = chunk_col(lane, 0, true), colA1 = chunk_col(lane, 1, true);
+  const uint32_t colB0 = chunk_col(lane, 0, false), colB1 = chunk_col(lane, 1, false);
+
+  KvStep st;
+  st.s = stride;
+  st.s_bj = stride / HP;
+  st.s_hp = stride - st.s_bj * HP;
+  st.s_b = st.s_bj / C;
+  st.s_j = st.s_bj - st.s_b * C;
+  // all gathers of an item (15 vector-memory operations)
+  auto gather = [&](const KvPos& p, const FwdIdx2& x) {
+    const bool two = 2 * p.hp + 1 < H;
+    FwdOffs of;
+    item_offs(x, p.b * N, 2 * p.hp, H, row_bytes, two ? colA0 : colB0, two ? colA1 : colB1, of);
+    gather_tile<T>(k, of, ak);
+    gather_tile<T>(v, of, av);
+    dma16(q, of.qr, aq);
+    dma16(dout, of.qr, ado);
+    dma16(o, of.qr, ao);
+  };
+  // LSE of (query lane & 7, head h0 + (lane >> 3 & 1)) into the LSE tile
+  // (lanes 0..15; one vector-memory operation)
+  auto gather_lse = [&](const KvPos& p, const FwdIdx2& x) {
+    if (lane < 16) {
+      const int h = min(2 * p.hp + (lane >> 3), H - 1);
+      dma4(lse, (uint32_t)((p.b * N + x.qc) * H + h) * 4u, als);
+    }
+  };
+
+  // prologue: index rows of the first item, then its gathers and LSE, and
+  // the index rows of the second
+  KvPos pos = kv_pos(first, HP, C);
+  KvPos pn = kv_next(pos, st, HP, C);
+  FwdIdx2 x, xn;
+  gather_idx(pos.bj, q_idx, key_idx, lane, ai);
+  wait_vm<0>();
+  read_idx(ti, lane, x);
+  wait_lgkm0();
+  gather(pos, x);
+  gather_lse(pos, x);
+  if (pn.item < n_items) gather_idx(pn.bj, q_idx, key_idx, lane, ai);
+
+  for (;;) {
+    const int h0 = 2 * pos.hp;
+    const int img = pos.b * N;
+    const bool h1ok = h0 + 1 < H;
+    const int hq = left ? h0 : h0 + 1;
+    const bool more = pn.item < n_items;
+    const KvPos pnn = kv_next(pn, st, HP, C);
+
+    // this item's gathers and LSE and the next item's index rows have
+    // landed; the three stores of the previous item may still be in flight
+    if (pos.item > first) wait_vm<3>();
+    else wait_vm<0>();
+
+    // every LDS operand of the item into registers
+    const float lse2 = tls[c16] * kLog2e;   // (query c16 & 7, head hq)
+    const int qm = c16 & 7;
+    const uint32_t qoff = (uint32_t)qm * kSlotBytes +
+                          16u * ((uint32_t)((c16 >> 3) * 4 + g) ^ swz(qm));
+    const uint4 qv = lds16(tq, qoff), dov = lds16(tdo, qoff), ov = lds16(to, qoff);
+    uint4 k0[3], k1[3], v0[3], v1[3];
+#pragma unroll
+    for (int b = 0; b < 3; ++b) {
+      const int sl = 16 * b + c16;
+      const uint32_t row = (uint32_t)sl * kSlotBytes;
+      k0[b] = lds16(tk, row + 16u * ((uint32_t)g ^ swz(sl)));
+      k1[b] = lds16(tk, row + 16u * ((uint32_t)(4 + g) ^ swz(sl)));
+      v0[b] = lds16(tv, row + 16u * ((uint32_t)g ^ swz(sl)));
+      v1[b] = lds16(tv, row + 16u * ((uint32_t)(4 + g) ^ swz(sl)));
+    }
+    // K^T for dQ^T = K^T dS^T (transposed reads, as V in the forward)
+    uint2 kt[2][2][3];
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+        for (int blk = 0; blk < 3; ++blk) {
+          const int sl = 16 * blk + 4 * g + e;
+          const uint32_t c = (uint32_t)(4 * hh + 2 * hf + (qq >> 1));
+          kt[hh][hf][blk] = lds_tr8(tk, (uint32_t)sl * kSlotBytes + 16u * (c ^ swz(sl)) + 8u * (qq & 1));
+        }
+    if (more) read_idx(ti, lane, xn);
+    wait_lgkm0();
+
+    // next item's gathers and LSE, and the index rows of the one after
+    if (more) {
+      gather(pn, xn);
+      gather_lse(pn, xn);
+      if (pnn.item < n_items) gather_idx(pnn.bj, q_idx, key_idx, lane, ai);
+    }
+
+    // Delta of (query c16 & 7, head hq)
+    float dl = 0.f;
+    {
+      const uint32_t a[4] = {dov.x, dov.y, dov.z, dov.w};
+      const uint32_t c[4] = {ov.x, ov.y, ov.z, ov.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const f32x2 xa = Mfma<T>::unpack(a[i]), ya = Mfma<T>::unpack(c[i]);
+        dl = fmaf(xa[0], ya[0], fmaf(xa[1], ya[1], dl));
+      }
+    }
+    dl = shfl_sum16_32(dl);
+
+    const uint4 qL = sel(left, qv), qR = sel(!left, qv);
+    const uint4 dL = sel(left, dov), dR = sel(!left, dov);
+    float ds[3][4];
+    const uint64_t vb64 = __ballot(x.tl >= 0);
+#pragma unroll
+    for (int b = 0; b < 3; ++b) {
+      f32x4 sv = Mfma<T>::mma(k0[b], qL, z);
+      sv = Mfma<T>::mma(k1[b], qR, sv);
+      f32x4 dp = Mfma<T>::mma(v0[b], dL, z);
+      dp = Mfma<T>::mma(v1[b], dR, dp);
+      const uint32_t vb = (uint32_t)(vb64 >> (16 * b));
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const bool ok = (vb >> (4 * g + i)) & 1u;
+        const float p = ok ? __builtin_amdgcn_exp2f(fmaf(sv[i], scale_log2, -lse2)) : 0.f;
+        ds[b][i] = p * (dp[i] - dl);
+      }
+    }
+    uint2 dh[3];
+#pragma unroll
+    for (int b = 0; b < 3; ++b)
+      dh[b] = make_uint2(pack2<T>(ds[b][0], ds[b][1]), pack2<T>(ds[b][2], ds[b][3]));
+    const uint4 b0h = cat(dh[0], dh[1]), b1h = pad(dh[2]);
+
+    f32x4 acc[2][2] = {{z, z}, {z, z}};
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      if (hh == 1 && !h1ok) break;
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        acc[hh][hf] = Mfma<T>::mma(cat(kt[hh][hf][0], kt[hh][hf][1]), b0h, acc[hh][hf]);
+        acc[hh][hf] = Mfma<T>::mma(pad(kt[hh][hf][2]), b1h, acc[hh][hf]);
+      }
+    }
+    // exactly three store instructions per item (lanes 0..7 always store)
+    const uint32_t qrow = (uint32_t)__umul24((uint32_t)x.qc, (uint32_t)H) + (uint32_t)(img * H);
+    if (hq < H && g == 0) ld[qrow + hq] = make_float2(lse2, dl);
+    if (hq < H) {
+      const uint32_t drow = (qrow + (uint32_t)hq) * kRow + 8u * g;
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf)
+        stv<uint2>(dq, drow + 32u * hf, pack4<T>((left ? acc[0][hf] : acc[1][hf]) * scale));
+    }
+    if (!more) break;
+    pos = pn;
+    pn = pnn;
+    x = xn;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// backward pass B (key-major), LDS-staged gathers
+// ---------------------------------------------------------------------------
+// One wavefront per (key cluster j, head pair).  The entries of j (query
+// clusters i reading j, with per-member multiplicities and the query tokens
+// of i) are taken four at a time: their 32 query rows of Q and dO (both
+// heads) are gathered into a wavefront-private LDS tile with direct-to-LDS
+// loads (instruction u holds entry u's 8 rows).  S = Q K_j^T and
+// dP = dO V_j^T read Q and dO in the MFMA A layout; dV^T += dO^T P and
+// dK^T += Q^T dS read them transposed (ds_read_b64_tr_b16).  One accumulator
+// set per head, so no operand needs zeroed columns.  Summation order is
+// fixed by the entry order (sorted by i), so the result is bitwise
+// reproducible.  A multiplicity m enters as exp2(s - LSE + log2 m), which is
+// 0 for an entry past the end of a list (m = 0).
+//
+// The per-item lookups are prefetched one item ahead: when item t starts,
+// the query tokens and multiplicities of the first eight entries of item
+// t+1 go to a wavefront-private LDS block (direct-to-LDS loads; two blocks
+// alternate), its own K/V rows and the segment bounds and key tokens of item
+// t+2 are requested, all ahead of item t's first gathers, so that one wait
+// per four entries covers them.  Loads for later items use clamped (always
+// valid) addresses.  Item positions advance by the fixed stride without
+// divisions.
+constexpr int kKvRows = 32;                             // query rows per step
+constexpr int kKvTile = kKvRows * kSlotBytes;           // 4 KiB per tensor
+constexpr int kKvMeta = 2 * (64 * 4 + 8 * 8);           // two blocks of 8 entries' tokens, mults
+constexpr int kKvWaveLds = 2 * kKvTile + kKvMeta;       // Q, dO, entry blocks
+constexpr int kKvWavesPerCU = 16;                       // residency (VGPRs and LDS)
 
 template <typename T>
 __global__ void __launch_bounds__(64 * kWaves, kKvWavesPerCU / 4)
