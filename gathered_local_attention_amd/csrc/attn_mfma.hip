@@ -800,8 +800,8 @@ bwd_kv_lds_kernel(int N, int H, int HP, int n_items, float scale, const T* __res
                   const int32_t* __restrict__ rtok_all, int nk, T* __restrict__ dk,
                   T* __restrict__ dv) {
   __shared__ __attribute__((aligned(1024))) char lds[kWaves * kKvWaveLds];
-  // 64 entries per wave: one 16-byte direct-to-LDS load writes all 64 lanes
-  __shared__ __attribute__((aligned(16))) float4 lds_ld[kWaves][64];
+  // (LSE*log2e, Delta) of both heads of the 32 query rows of a step
+  __shared__ __attribute__((aligned(16))) float4 lds_ld[kWaves][32];
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   // items dealt round-robin over the wavefronts (see the forward)
@@ -919,7 +919,12 @@ bwd_kv_lds_kernel(int N, int H, int HP, int n_items, float scale, const T* __res
         load_block(eb, e1, blk);
         wait_vm<0>();
       }
+      // A step takes four entries (32 query rows), or two (16 rows, one
+      // MFMA row block) when at most two remain, so that a list of 4n + 2
+      // entries carries no padding; the half step feeds zeros for the upper
+      // 16 rows of the dK/dV products.
       for (int e4 = 0; e4 < ne; e4 += 4) {
+        const bool half = ne - e4 <= 2;   // wave-uniform
         // gathers: instruction u holds entry e4 + u (an entry past the end
         // repeats the last one, with zero multiplicity); all offsets first,
         // then the loads (each load's asm block orders every LDS operation
@@ -933,15 +938,16 @@ bwd_kv_lds_kernel(int N, int H, int HP, int n_items, float scale, const T* __res
           const int tl_tok = btok[8 * min(e4 + (lrow >> 3), ne - 1) + (lrow & 7)];
 #pragma unroll
           for (int u = 0; u < 4; ++u) {
+            if (u == 2 && half) break;
             dma16(q, offs[u], aq + (uint32_t)u * 1024u);
             dma16(dout, offs[u], ad + (uint32_t)u * 1024u);
           }
-          // (LSE*log2e, Delta) of both heads of query row `lane` (lanes < 32;
-          // lanes 32..63 repeat rows 0..31 into their own slots): 16 bytes at
+          // (LSE*log2e, Delta) of both heads of query row `lane` (lanes < 32,
+          // rows 16..31 only in a full step): 16 bytes at
           // ld[(img + t) * H + h0].  With an odd head count the second pair
           // belongs to the next token (or lies in the next workspace part);
           // it is never used then.
-          dma16(ld, (uint32_t)tl_tok * (uint32_t)H * 8u + lb, al);
+          if (lane < (half ? 16 : 32)) dma16(ld, (uint32_t)tl_tok * (uint32_t)H * 8u + lb, al);
         }
         // log2 of the multiplicity of this lane's output rows 4g+i of block
         // qb (entry e4 + 2qb + (g >> 1), key member kcol): -inf for 0
@@ -954,9 +960,10 @@ bwd_kv_lds_kernel(int N, int H, int HP, int n_items, float scale, const T* __res
         }
         wait_vm<0>();
 
-        float p[2][4], ds[2][4];
+        uint2 ph[2] = {make_uint2(0u, 0u), make_uint2(0u, 0u)}, dh[2] = {ph[0], ph[1]};
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb) {
+          if (qb == 1 && half) break;
           const int row = 16 * qb + c16;
           const uint32_t rb = (uint32_t)row * kSlotBytes;
           const uint4 q0 = lds16(tq, rb + 16u * ((uint32_t)g ^ swz(row)));
@@ -967,19 +974,16 @@ bwd_kv_lds_kernel(int N, int H, int HP, int n_items, float scale, const T* __res
           sv = Mfma<T>::mma(q1, kR, sv);
           f32x4 dp = Mfma<T>::mma(d0, vL, z);
           dp = Mfma<T>::mma(d1, vR, dp);
+          float p[4], ds[4];
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             // (LSE*log2e, Delta) of row 16qb + 4g + i, head hk
             const float2 lv = tl2[2 * (16 * qb + 4 * g + i) + (left ? 0 : 1)];
-            p[qb][i] = __builtin_amdgcn_exp2f(fmaf(sv[i], scale_log2, lm[qb] - lv.x));
-            ds[qb][i] = p[qb][i] * (dp[i] - lv.y);
+            p[i] = __builtin_amdgcn_exp2f(fmaf(sv[i], scale_log2, lm[qb] - lv.x));
+            ds[i] = p[i] * (dp[i] - lv.y);
           }
-        }
-        uint2 ph[2], dh[2];
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
-          ph[qb] = make_uint2(pack2<T>(p[qb][0], p[qb][1]), pack2<T>(p[qb][2], p[qb][3]));
-          dh[qb] = make_uint2(pack2<T>(ds[qb][0], ds[qb][1]), pack2<T>(ds[qb][2], ds[qb][3]));
+          ph[qb] = make_uint2(pack2<T>(p[0], p[1]), pack2<T>(p[2], p[3]));
+          dh[qb] = make_uint2(pack2<T>(ds[0], ds[1]), pack2<T>(ds[2], ds[3]));
         }
         const uint4 bph = cat(ph[0], ph[1]), bdh = cat(dh[0], dh[1]);
         // transposed reads: lane c16 = 4e + qq of group g receives dim
@@ -989,9 +993,10 @@ bwd_kv_lds_kernel(int N, int H, int HP, int n_items, float scale, const T* __res
           if (hh == 1 && !h1ok) break;
 #pragma unroll
           for (int hf = 0; hf < 2; ++hf) {
-            uint2 at_d[2], at_q[2];
+            uint2 at_d[2] = {make_uint2(0u, 0u), make_uint2(0u, 0u)}, at_q[2] = {at_d[0], at_d[1]};
 #pragma unroll
             for (int qb = 0; qb < 2; ++qb) {
+              if (qb == 1 && half) break;
               const int row = 16 * qb + 4 * g + e;
               const uint32_t c = (uint32_t)(4 * hh + 2 * hf + (qq >> 1));
               const uint32_t o = (uint32_t)row * kSlotBytes + 16u * (c ^ swz(row)) + 8u * (qq & 1);
