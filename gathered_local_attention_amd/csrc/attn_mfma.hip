@@ -346,6 +346,8 @@ fwd_lds_kernel(int N, int H, int HP, int n_items, int ipw, float scale_log2,
   const f32x4 z = {0.f, 0.f, 0.f, 0.f};
   const int e = c16 >> 2, qq = c16 & 3;
   const int CperImg = N / CS;
+  const bool neg = scale_log2 < 0.f;        // wave-uniform
+  const float csl = fabsf(scale_log2);
 
   // Item positions (head-pair-major numbering item = hp * BC + bc) advance
   // by the fixed stride without divisions.
@@ -411,10 +413,18 @@ fwd_lds_kernel(int N, int H, int HP, int n_items, int ipw, float scale_log2,
       offs_of(xn, pn, oxn);
     }
 
-    // S^T = K Q^T: lane holds keys 16b+4g+i of column c16
+    // S^T = K Q^T: lane holds keys 16b+4g+i of column c16.  A negative scale
+    // is applied as -|scale| with Q negated (exact), so that the row maximum
+    // below is that of the scaled logits.
     const int qm = c16 & 7;
-    const uint4 qv = lds16(tq, (uint32_t)qm * kSlotBytes +
-                                   16u * ((uint32_t)((c16 >> 3) * 4 + g) ^ swz(qm)));
+    uint4 qv = lds16(tq, (uint32_t)qm * kSlotBytes +
+                             16u * ((uint32_t)((c16 >> 3) * 4 + g) ^ swz(qm)));
+    if (neg) {
+      qv.x ^= 0x80008000u;
+      qv.y ^= 0x80008000u;
+      qv.z ^= 0x80008000u;
+      qv.w ^= 0x80008000u;
+    }
     const uint4 qL = sel(left, qv), qR = sel(!left, qv);
     f32x4 s[3];
 #pragma unroll
@@ -431,8 +441,11 @@ fwd_lds_kernel(int N, int H, int HP, int n_items, int ipw, float scale_log2,
       gather_tile<T>(k, oxn, ak);
     }
 
-    if (__ballot(x.tl < 0) != 0ull) {   // some slot of this list is empty: mask it
-      const uint64_t vb64 = __ballot(x.tl >= 0);
+    // some slot of this list is empty: leave it out of the maximum, and
+    // zero its probability below (exact for any finite scale, 0 included)
+    const bool holes = __ballot(x.tl < 0) != 0ull;
+    const uint64_t vb64 = __ballot(x.tl >= 0);
+    if (holes) {
 #pragma unroll
       for (int b = 0; b < 3; ++b) {
         const uint32_t vb = (uint32_t)(vb64 >> (16 * b));
@@ -446,16 +459,26 @@ fwd_lds_kernel(int N, int H, int HP, int n_items, int ipw, float scale_log2,
     for (int b = 1; b < 3; ++b)
       mx = fmaxf(mx, fmaxf(fmaxf(s[b][0], s[b][1]), fmaxf(s[b][2], s[b][3])));
     mx = shfl_max16_32(mx);
-    const float mref = mx == -INFINITY ? 0.f : mx * scale_log2;
-    float l = 0.f;
+    const float mref = mx == -INFINITY ? 0.f : mx * csl;
     float p[3][4];
 #pragma unroll
     for (int b = 0; b < 3; ++b)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        p[b][i] = __builtin_amdgcn_exp2f(fmaf(s[b][i], scale_log2, -mref));
-        l += p[b][i];
+      for (int i = 0; i < 4; ++i) p[b][i] = __builtin_amdgcn_exp2f(fmaf(s[b][i], csl, -mref));
+    if (holes) {
+#pragma unroll
+      for (int b = 0; b < 3; ++b) {
+        const uint32_t vb = (uint32_t)(vb64 >> (16 * b));
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (!((vb >> (4 * g + i)) & 1u)) p[b][i] = 0.f;
       }
+    }
+    float l = 0.f;
+#pragma unroll
+    for (int b = 0; b < 3; ++b)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) l += p[b][i];
     l = shfl_sum16_32(l);
     uint2 ph[3];
 #pragma unroll
@@ -714,22 +737,34 @@ bwd_q_lds_kernel(int N, int H, int HP, int n_items, int ipw, float scale,
 
     const uint4 qL = sel(left, qv), qR = sel(!left, qv);
     const uint4 dL = sel(left, dov), dR = sel(!left, dov);
-    float ds[3][4];
-    const uint64_t vb64 = __ballot(x.tl >= 0);
+    float p[3][4], dpv[3][4];
 #pragma unroll
     for (int b = 0; b < 3; ++b) {
       f32x4 sv = Mfma<T>::mma(k0[b], qL, z);
       sv = Mfma<T>::mma(k1[b], qR, sv);
       f32x4 dp = Mfma<T>::mma(v0[b], dL, z);
       dp = Mfma<T>::mma(v1[b], dR, dp);
-      const uint32_t vb = (uint32_t)(vb64 >> (16 * b));
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const bool ok = (vb >> (4 * g + i)) & 1u;
-        const float p = ok ? __builtin_amdgcn_exp2f(fmaf(sv[i], scale_log2, -lse2)) : 0.f;
-        ds[b][i] = p * (dp[i] - dl);
+        p[b][i] = __builtin_amdgcn_exp2f(fmaf(sv[i], scale_log2, -lse2));
+        dpv[b][i] = dp[i];
       }
     }
+    if (__ballot(x.tl < 0) != 0ull) {   // empty slots of this list: P = 0 there
+      const uint64_t vb64 = __ballot(x.tl >= 0);
+#pragma unroll
+      for (int b = 0; b < 3; ++b) {
+        const uint32_t vb = (uint32_t)(vb64 >> (16 * b));
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (!((vb >> (4 * g + i)) & 1u)) p[b][i] = 0.f;
+      }
+    }
+    float ds[3][4];
+#pragma unroll
+    for (int b = 0; b < 3; ++b)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) ds[b][i] = p[b][i] * (dpv[b][i] - dl);
     uint2 dh[3];
 #pragma unroll
     for (int b = 0; b < 3; ++b)

@@ -167,17 +167,19 @@ def test_backward_is_deterministic(ca):
     assert torch.equal(o, r["o"]) and torch.equal(lse, r["lse"])
 
 
-def test_holes_repeats_and_short_lists(ca):
+@pytest.mark.parametrize("scale", [0.2, -0.35, 0.0])
+def test_holes_repeats_and_short_lists(ca, scale):
     """Hand-made lists: -1 slots, repeated slots, a cluster with a single
-    valid slot, and k = 3 (24 slots), every dtype.  Random lists over all
-    tokens pile many slots onto some keys, so |dV| reaches ~10 where one
-    bf16 output rounding step is 0.03: the bf16/f16 bars are taken relative
-    to max(1, max|ref|)."""
+    valid slot, and k = 3 (24 slots), every dtype; a positive, a negative
+    and a zero logit scale (the API takes any finite scale).  Random lists
+    over all tokens pile many slots onto some keys, so |dV| reaches ~10
+    where one bf16 output rounding step is 0.03: the bf16/f16 bars are
+    taken relative to max(1, max|ref|)."""
     rng = np.random.default_rng(21)
     B, N, H, D = 2, 128, 3, 32
     for nk in (48, 24):
         for dt in (torch.float32, torch.bfloat16, torch.float16):
-            print(f"case hand lists nk={nk} {dt}", flush=True)
+            print(f"case hand lists nk={nk} {dt} scale={scale}", flush=True)
             q_idx = np.stack([rng.permutation(N).reshape(-1, 8) for _ in range(B)]).astype(np.int32)
             key_idx = rng.integers(0, N, size=(B, N // 8, nk)).astype(np.int32)
             key_idx[:, :, 3] = key_idx[:, :, 2]
@@ -186,7 +188,6 @@ def test_holes_repeats_and_short_lists(ca):
             key_idx[:, 5, 7] = 11
             q, k, v, do = (torch.randn(B, N, H, D, generator=torch.Generator().manual_seed(s)).to(dt)
                            for s in range(4))
-            scale = 0.2
             dev = [t.to(DEV) for t in (q, k, v, do)]
             qi, ki = torch.from_numpy(q_idx).to(DEV), torch.from_numpy(key_idx).to(DEV)
             o, lse = ca.fwd(dev[0], dev[1], dev[2], qi, ki, scale)
