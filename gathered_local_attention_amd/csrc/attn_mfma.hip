@@ -235,7 +235,7 @@ __device__ __forceinline__ void wait_vm_n(int n) {
 __device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 
 // LDS tile of one item's indices: ints 0..47 key tokens of the 48 slots,
-// 48..55 the query tokens of the cluster, 56..63 unused.
+// 48..55 the query tokens of the cluster, 56..63 unused (never written).
 constexpr int kIdxBytes = 256;
 constexpr int kFwdWaves = 2;
 // Waves per CU the launch is sized for (one round over all 256 CUs); the
@@ -244,14 +244,15 @@ constexpr int kFwdWaves = 2;
 constexpr int kFwdWavesPerCU = 8;
 constexpr int kFwdWaveLds = 2 * kTileBytes + 1024 + kIdxBytes;
 
-// Two exec-masked loads (each lane writes only its own 4-byte LDS slot):
-// lanes 0..47 fetch the key_idx row of the cluster, lanes 48..63 the q_idx
-// row (48..55, repeated in 56..63).  Counts as two vector-memory operations.
+// Two exec-masked 16-byte loads: lanes 0..11 fetch the key_idx row of the
+// cluster (ints 0..47 of the tile), lanes 12..13 its q_idx row (ints
+// 48..55).  Few active lanes keep the address work small.  Counts as two
+// vector-memory operations.
 __device__ __forceinline__ void gather_idx(int bc, const int32_t* __restrict__ q_idx,
                                            const int32_t* __restrict__ key_idx, int lane,
                                            uint32_t lds) {
-  if (lane < NK) dma4(key_idx, (uint32_t)(bc * NK + lane) * 4u, lds);
-  else dma4(q_idx, (uint32_t)(bc * CS + ((lane - NK) & 7)) * 4u, lds);
+  if (lane < 12) dma16(key_idx, (uint32_t)(bc * NK) * 4u + 16u * (uint32_t)lane, lds);
+  else if (lane < 14) dma16(q_idx, (uint32_t)(bc * CS) * 4u + 16u * (uint32_t)(lane - 12), lds);
 }
 
 // Per-lane indices of one item, read from its LDS index tile.
