@@ -11,21 +11,21 @@
 // local balanced clustering) leaves to the implementation.
 //
 // plan_small_kernel (images of at most 256 clusters) keeps the whole image
-// in LDS; see its comment.  plan_kernel handles any size:
-// one 1024-thread workgroup per image (every counter it touches belongs to
-// its image, so no global zeroing pass and no cross-workgroup ordering are
-// needed).  Phases, separated by workgroup barriers:
-//   1. inv[token] = position of the token in q_idx (c*cs + m); zero counts.
-//   2. per tile of query clusters: every slot looks up its key cluster
-//      (jn = inv[token], staged in LDS); the first slot of cluster i that
-//      points into key cluster j stages the entry (j, per-member
-//      multiplicities) at its own slot position and counts it for j.
-//   3. exclusive scan of the counts -> segment offsets.
-//   4. staged entries are scattered into their segments (atomic cursor).
-//   5. each segment is sorted by i, which fixes the summation order of the
-//      key-major pass and makes it deterministic.
-//   6. every entry gets the query tokens of its cluster i (the q_idx row),
-//      so that the key-major pass gathers without a further lookup.
+// in LDS, one workgroup per image; see its comment.  Larger images go
+// through six grid-wide kernels, each parallel over tokens, slots or
+// clusters of the whole batch:
+//   1. inv = -1, counts = 0
+//   2. inv[token] = position of the token in q_idx (c*cs + m)
+//   3. per query cluster i (one thread): every slot looks up its key cluster
+//      (jn = inv[token]); the first slot of i that points into key cluster
+//      j stages the entry (j, per-member multiplicities) at its own slot
+//      position and counts it for j (atomic)
+//   4. per image, exclusive scan of the counts -> segment offsets
+//   5. per slot, staged entries are placed in their segments (atomic cursor)
+//   6. per key cluster, its segment is sorted by i (which fixes the
+//      summation order of the key-major pass and makes it deterministic) and
+//      every entry gets the q_idx row of its i, so that the key-major pass
+//      gathers without a further lookup.
 #include "common.h"
 
 namespace ca {
@@ -34,130 +34,215 @@ namespace {
 
 constexpr int kPlanThreads = 1024;
 constexpr int kMaxNk = 64;
-constexpr int kTileSlots = 12288;   // 48 KiB of LDS: 256 clusters of 48 slots
+constexpr int kGridThreads = 256;
 
-__global__ void __launch_bounds__(kPlanThreads)
-plan_kernel(int N, int nk, const int32_t* __restrict__ q_idx, const int32_t* __restrict__ key_idx,
-            int32_t* __restrict__ inv_all, int32_t* __restrict__ cnt_all,
-            int32_t* __restrict__ off_all, int32_t* __restrict__ cur_all,
-            RevEntry* __restrict__ stage_all, RevEntry* __restrict__ rev_all,
-            int32_t* __restrict__ rtok_all) {
-  __shared__ int32_t jn[kTileSlots];
-  __shared__ int32_t scan[kPlanThreads];
-  const int b = blockIdx.x;
+__global__ void __launch_bounds__(kGridThreads)
+plan_init_kernel(int64_t n_inv, int64_t n_cnt, int32_t* __restrict__ inv, int32_t* __restrict__ cnt) {
+  const int64_t x = (int64_t)blockIdx.x * kGridThreads + threadIdx.x;
+  if (x < n_inv) inv[x] = -1;
+  if (x < n_cnt) cnt[x] = 0;
+}
+
+__global__ void __launch_bounds__(kGridThreads)
+plan_inv_kernel(int B, int N, const int32_t* __restrict__ q_idx, int32_t* __restrict__ inv) {
+  const int64_t x = (int64_t)blockIdx.x * kGridThreads + threadIdx.x;
+  if (x >= (int64_t)B * N) return;
+  const int64_t b = x / N;
+  const int t = q_idx[x];
+  if (t >= 0 && t < N) inv[b * N + t] = (int32_t)(x - b * N);
+}
+
+// one thread per query cluster; its slots' key positions are staged in LDS.
+// A group of 8 slots that all point into one key cluster (the neighbour
+// build writes whole clusters) is handled as one candidate entry; a cluster
+// with any other group takes the per-slot path.
+constexpr int kCountThreads = 64;
+
+__global__ void __launch_bounds__(kCountThreads)
+plan_count_kernel(int B, int N, int nk, const int32_t* __restrict__ key_idx,
+                  const int32_t* __restrict__ inv, int32_t* __restrict__ cnt,
+                  RevEntry* __restrict__ stage) {
+  __shared__ int32_t jn[kCountThreads][kMaxNk + 1];
   const int C = N / 8;
-  const int tid = threadIdx.x;
-  const int32_t* qi = q_idx + (int64_t)b * N;
-  const int32_t* ki = key_idx + (int64_t)b * C * nk;
-  int32_t* inv = inv_all + (int64_t)b * N;
-  int32_t* cnt = cnt_all + (int64_t)b * C;
-  int32_t* off = off_all + (int64_t)b * (C + 1);
-  int32_t* cur = cur_all + (int64_t)b * C;
-  RevEntry* stage = stage_all + (int64_t)b * C * nk;
-  RevEntry* rev = rev_all + (int64_t)b * C * nk;
-  const int64_t slots = (int64_t)C * nk;
-
-  // 1 (inv starts at -1 so that a q_idx that is not a permutation leaves
-  //    unreached tokens marked invalid instead of holding stale values)
-  for (int t = tid; t < N; t += kPlanThreads) inv[t] = -1;
-  for (int j = tid; j < C; j += kPlanThreads) cnt[j] = 0;
-  __syncthreads();
-  for (int p = tid; p < N; p += kPlanThreads) inv[qi[p]] = p;
-  __syncthreads();
-
-  // 2
-  const int tile_clusters = kTileSlots / nk;
-  for (int i0 = 0; i0 < C; i0 += tile_clusters) {
-    const int nc = min(tile_clusters, C - i0);
-    const int ns = nc * nk;
-    for (int x = tid; x < ns; x += kPlanThreads) {
-      const int t = ki[(int64_t)i0 * nk + x];
-      jn[x] = t >= 0 ? inv[t] : -1;          // (j << 3) | n
-    }
-    __syncthreads();
-    for (int x = tid; x < ns; x += kPlanThreads) {
-      const int il = x / nk, s = x - il * nk;
-      const int* my = jn + il * nk;
-      const int js = my[s];
+  const int64_t bc = (int64_t)blockIdx.x * kCountThreads + threadIdx.x;
+  if (bc >= (int64_t)B * C) return;
+  const int64_t b = bc / C;
+  int32_t* my = jn[threadIdx.x];
+  for (int s = 0; s < nk; ++s) {
+    const int t = key_idx[bc * nk + s];
+    my[s] = (t >= 0 && t < N) ? inv[b * N + t] : -1;   // (j << 3) | member, or -1
+  }
+  RevEntry* st = stage + bc * nk;
+  const int ng = nk / 8;
+  bool grouped = (nk % 8) == 0;
+  for (int g = 0; g < ng && grouped; ++g) {
+    const int j0 = my[8 * g];
+    bool same = j0 >= 0;
+    for (int m = 1; m < 8; ++m) same = same && my[8 * g + m] >= 0 && (my[8 * g + m] >> 3) == (j0 >> 3);
+    grouped = same;
+  }
+  if (grouped) {
+    for (int g = 0; g < ng; ++g) {
+      const int j = my[8 * g] >> 3;
+      bool first = true;
+      for (int h = 0; h < g; ++h) first = first && (my[8 * h] >> 3) != j;
       RevEntry e;
       e.i = -1;
       e.pad = 0;
       e.mult = 0;
-      if (js >= 0) {
-        const int j = js >> 3;
-        bool first = true;
-        for (int u = s - 1; u >= 0; --u)
-          if (my[u] >= 0 && (my[u] >> 3) == j) { first = false; break; }
-        if (first) {
-          uint64_t mult = 0;
-          for (int u = s; u < nk; ++u)
-            if (my[u] >= 0 && (my[u] >> 3) == j) mult += 1ull << (8 * (my[u] & 7));
-          e.i = j;   // key cluster while staged
-          e.mult = mult;
-          atomicAdd(&cnt[j], 1);
+      if (first) {
+        uint64_t mult = 0;
+        for (int h = g; h < ng; ++h)
+          if ((my[8 * h] >> 3) == j)
+            for (int m = 0; m < 8; ++m) mult += 1ull << (8 * (my[8 * h + m] & 7));
+        e.i = j;   // key cluster while staged
+        e.mult = mult;
+        atomicAdd(&cnt[b * C + j], 1);
+      }
+      st[8 * g] = e;
+      RevEntry none;
+      none.i = -1;
+      none.pad = 0;
+      none.mult = 0;
+      for (int m = 1; m < 8; ++m) st[8 * g + m] = none;
+    }
+    return;
+  }
+  for (int s = 0; s < nk; ++s) {
+    const int js = my[s];
+    RevEntry e;
+    e.i = -1;
+    e.pad = 0;
+    e.mult = 0;
+    if (js >= 0) {
+      const int j = js >> 3;
+      bool first = true;
+      for (int u = s - 1; u >= 0; --u)
+        if (my[u] >= 0 && (my[u] >> 3) == j) { first = false; break; }
+      if (first) {
+        uint64_t mult = 0;
+        for (int u = s; u < nk; ++u)
+          if (my[u] >= 0 && (my[u] >> 3) == j) mult += 1ull << (8 * (my[u] & 7));
+        e.i = j;   // key cluster while staged
+        e.mult = mult;
+        atomicAdd(&cnt[b * C + j], 1);
+      }
+    }
+    st[s] = e;
+  }
+}
+
+// one workgroup per image: segment offsets from the counts (each thread
+// sums a run of counts, one workgroup scan, then the run is written out)
+__global__ void __launch_bounds__(kPlanThreads)
+plan_scan_kernel(int C, const int32_t* __restrict__ cnt_all, int32_t* __restrict__ off_all,
+                 int32_t* __restrict__ cur_all) {
+  __shared__ int32_t tmp[17];
+  const int64_t b = blockIdx.x;
+  const int32_t* cnt = cnt_all + b * C;
+  int32_t* off = off_all + b * (C + 1);
+  int32_t* cur = cur_all + b * C;
+  const int per = (C + kPlanThreads - 1) / kPlanThreads;
+  const int j0 = threadIdx.x * per, j1 = min(C, j0 + per);
+  int run = 0;
+  for (int j = j0; j < j1; ++j) run += cnt[j];
+  int tot;
+  int acc = block_exclusive_scan(run, tmp, kPlanThreads, &tot);
+  for (int j = j0; j < j1; ++j) {
+    off[j] = acc;
+    cur[j] = acc;
+    acc += cnt[j];
+  }
+  if (threadIdx.x == 0) off[C] = tot;
+}
+
+// one thread per slot: staged entries into their segments
+__global__ void __launch_bounds__(kGridThreads)
+plan_place_kernel(int B, int C, int nk, const RevEntry* __restrict__ stage,
+                  int32_t* __restrict__ cur_all, RevEntry* __restrict__ rev_all) {
+  const int64_t x = (int64_t)blockIdx.x * kGridThreads + threadIdx.x;
+  if (x >= (int64_t)B * C * nk) return;
+  const RevEntry s = stage[x];
+  if (s.i < 0) return;
+  const int64_t bc = x / nk;
+  const int64_t b = bc / C;
+  const int pos = atomicAdd(&cur_all[b * C + s.i], 1);
+  RevEntry r;
+  r.i = (int32_t)(bc - b * C);
+  r.pad = 0;
+  r.mult = s.mult;
+  rev_all[b * C * nk + pos] = r;
+}
+
+// one thread per key cluster: sort its segment by i (in registers when it
+// holds at most kSortRegs entries), then the query tokens of every entry
+constexpr int kSortRegs = 16;
+
+__global__ void __launch_bounds__(kGridThreads)
+plan_sort_kernel(int B, int N, int nk, const int32_t* __restrict__ q_idx,
+                 const int32_t* __restrict__ off_all, RevEntry* __restrict__ rev_all,
+                 int32_t* __restrict__ rtok_all) {
+  const int C = N / 8;
+  const int64_t bj = (int64_t)blockIdx.x * kGridThreads + threadIdx.x;
+  if (bj >= (int64_t)B * C) return;
+  const int64_t b = bj / C;
+  const int j = (int)(bj - b * C);
+  const int32_t* off = off_all + b * (C + 1);
+  RevEntry* rev = rev_all + b * C * nk;
+  const int a = off[j], z = off[j + 1];
+  int4* rt = reinterpret_cast<int4*>(rtok_all + b * C * nk * 8);
+  const int32_t* qi = q_idx + b * N;
+  if (z - a <= kSortRegs) {
+    int ii[kSortRegs];
+    uint64_t mm[kSortRegs];
+#pragma unroll
+    for (int x = 0; x < kSortRegs; ++x) {
+      if (a + x < z) {
+        const RevEntry e = rev[a + x];
+        ii[x] = e.i;
+        mm[x] = e.mult;
+      } else {
+        ii[x] = 0x7fffffff;
+        mm[x] = 0;
+      }
+    }
+    // odd-even transposition sort (the i are distinct)
+#pragma unroll
+    for (int r = 0; r < kSortRegs; ++r)
+#pragma unroll
+      for (int x = r & 1; x + 1 < kSortRegs; x += 2)
+        if (ii[x] > ii[x + 1]) {
+          const int ti = ii[x];
+          ii[x] = ii[x + 1];
+          ii[x + 1] = ti;
+          const uint64_t tm = mm[x];
+          mm[x] = mm[x + 1];
+          mm[x + 1] = tm;
         }
-      }
-      stage[(int64_t)i0 * nk + x] = e;
+#pragma unroll
+    for (int x = 0; x < kSortRegs; ++x) {
+      if (a + x >= z) break;
+      RevEntry e;
+      e.i = ii[x];
+      e.pad = 0;
+      e.mult = mm[x];
+      rev[a + x] = e;
+      const int4* row = reinterpret_cast<const int4*>(qi + ii[x] * 8);
+      rt[2 * (a + x)] = row[0];
+      rt[2 * (a + x) + 1] = row[1];
     }
-    __syncthreads();
+    return;
   }
-
-  // 3
-  int carry = 0;
-  for (int j0 = 0; j0 < C; j0 += kPlanThreads) {
-    const int j = j0 + tid;
-    const int v = j < C ? cnt[j] : 0;
-    scan[tid] = v;
-    __syncthreads();
-    for (int o = 1; o < kPlanThreads; o <<= 1) {
-      const int add = tid >= o ? scan[tid - o] : 0;
-      __syncthreads();
-      scan[tid] += add;
-      __syncthreads();
+  for (int x = a + 1; x < z; ++x) {
+    const RevEntry key = rev[x];
+    int y = x - 1;
+    while (y >= a && rev[y].i > key.i) {
+      rev[y + 1] = rev[y];
+      --y;
     }
-    if (j < C) {
-      const int start = carry + scan[tid] - v;
-      off[j] = start;
-      cur[j] = start;
-    }
-    carry += scan[kPlanThreads - 1];
-    __syncthreads();
+    rev[y + 1] = key;
   }
-  if (tid == 0) off[C] = carry;
-  __syncthreads();
-
-  // 4
-  for (int64_t x = tid; x < slots; x += kPlanThreads) {
-    const RevEntry s = stage[x];
-    if (s.i < 0) continue;
-    const int pos = atomicAdd(&cur[s.i], 1);
-    RevEntry r;
-    r.i = (int32_t)(x / nk);
-    r.pad = 0;
-    r.mult = s.mult;
-    rev[pos] = r;
-  }
-  __syncthreads();
-
-  // 5
-  for (int j = tid; j < C; j += kPlanThreads) {
-    const int a = off[j], z = off[j + 1];
-    for (int x = a + 1; x < z; ++x) {
-      const RevEntry key = rev[x];
-      int y = x - 1;
-      while (y >= a && rev[y].i > key.i) {
-        rev[y + 1] = rev[y];
-        --y;
-      }
-      rev[y + 1] = key;
-    }
-  }
-  __syncthreads();
-
-  // 6
-  int4* rt = reinterpret_cast<int4*>(rtok_all + (int64_t)b * C * nk * 8);
-  const int total = off[C];
-  for (int x = tid; x < total; x += kPlanThreads) {
+  for (int x = a; x < z; ++x) {
     const int4* row = reinterpret_cast<const int4*>(qi + rev[x].i * 8);
     rt[2 * x] = row[0];
     rt[2 * x + 1] = row[1];
@@ -349,8 +434,20 @@ hipError_t launch_bwd_plan(int B, int N, int nk, const int32_t* q_idx, const int
                        w.off, w.rev, w.rtok);
     return hipGetLastError();
   }
-  hipLaunchKernelGGL(plan_kernel, dim3(B), dim3(kPlanThreads), 0, st, N, nk, q_idx, key_idx,
-                     w.inv, w.cnt, w.off, w.cursor, w.stage, w.rev, w.rtok);
+  const int64_t tokens = (int64_t)B * N, clusters = (int64_t)B * C, slots = clusters * nk;
+  auto grid = [](int64_t n) { return dim3((unsigned)((n + kGridThreads - 1) / kGridThreads)); };
+  hipLaunchKernelGGL(plan_init_kernel, grid(tokens), dim3(kGridThreads), 0, st, tokens, clusters,
+                     w.inv, w.cnt);
+  hipLaunchKernelGGL(plan_inv_kernel, grid(tokens), dim3(kGridThreads), 0, st, B, N, q_idx, w.inv);
+  hipLaunchKernelGGL(plan_count_kernel, dim3((unsigned)((clusters + kCountThreads - 1) / kCountThreads)),
+                     dim3(kCountThreads), 0, st, B, N, nk, key_idx, (const int32_t*)w.inv, w.cnt,
+                     w.stage);
+  hipLaunchKernelGGL(plan_scan_kernel, dim3(B), dim3(kPlanThreads), 0, st, C,
+                     (const int32_t*)w.cnt, w.off, w.cursor);
+  hipLaunchKernelGGL(plan_place_kernel, grid(slots), dim3(kGridThreads), 0, st, B, C, nk,
+                     (const RevEntry*)w.stage, w.cursor, w.rev);
+  hipLaunchKernelGGL(plan_sort_kernel, grid(clusters), dim3(kGridThreads), 0, st, B, N, nk, q_idx,
+                     (const int32_t*)w.off, w.rev, w.rtok);
   return hipGetLastError();
 }
 

@@ -203,6 +203,42 @@ def test_holes_repeats_and_short_lists(ca, scale):
                 check_close(nm, g, r, t[2], rel)
 
 
+def test_grid_plan_random_lists(ca):
+    """Images above the single-workgroup plan limit (2304 tokens, 288
+    clusters) take the grid-wide transposition: random lists with -1
+    slots, repeated slots and groups that mix clusters (its per-slot path),
+    plus build-style lists of whole clusters (its grouped path)."""
+    rng = np.random.default_rng(33)
+    B, N, H, D, nk = 2, 2304, 2, 32, 48
+    C = N // 8
+    q_idx = np.stack([rng.permutation(N).reshape(-1, 8) for _ in range(B)]).astype(np.int32)
+    key_rand = rng.integers(0, N, size=(B, C, nk)).astype(np.int32)
+    key_rand[:, :, 5] = key_rand[:, :, 4]
+    key_rand[:, ::3, -2:] = -1
+    nb = (np.arange(C)[:, None] + np.array([0, 1, -1, 2, -2, 5])[None, :]) % C
+    key_grp = np.stack([q_idx[b][nb].reshape(C, nk) for b in range(B)]).astype(np.int32)
+    key_grp[:, 7] = key_rand[:, 7]   # one cluster with mixed groups in a grouped image
+    for name, key_idx in (("random", key_rand), ("grouped", key_grp)):
+        for dt in (torch.bfloat16, torch.float32):
+            print(f"case grid plan {name} {dt}", flush=True)
+            q, k, v, do = (torch.randn(B, N, H, D, generator=torch.Generator().manual_seed(40 + s)).to(dt)
+                           for s in range(4))
+            scale = 0.2
+            dev = [t.to(DEV) for t in (q, k, v, do)]
+            qi, ki = torch.from_numpy(q_idx).to(DEV), torch.from_numpy(key_idx).to(DEV)
+            o, lse = ca.fwd(dev[0], dev[1], dev[2], qi, ki, scale)
+            dq, dk, dv = ca.bwd(dev[0], dev[1], dev[2], o, dev[3], lse, qi, ki, scale)
+            torch.cuda.synchronize()
+            o_r, lse_r = O.attn_fwd_gathered(q, k, v, q_idx, key_idx, scale)
+            g_r = O.attn_bwd_gathered(q, k, v, do, q_idx, key_idx, scale)
+            t = {torch.float32: (1e-5, 1e-5, 1e-5)}.get(dt, (1e-2, 1e-3, 2e-2))
+            rel = dt != torch.float32
+            check_close("O", o, o_r, t[0], rel)
+            check_close("LSE", lse, lse_r, t[1], False)
+            for nm, g, r in zip(("dQ", "dK", "dV"), (dq, dk, dv), g_r):
+                check_close(nm, g, r, t[2], rel)
+
+
 def test_fully_masked_cluster(ca):
     B, N, H = 1, 64, 2
     q_idx = np.arange(N, dtype=np.int32).reshape(1, -1, 8)
