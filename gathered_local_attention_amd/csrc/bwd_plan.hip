@@ -18,10 +18,11 @@
 //   2. inv[token] = position of the token in q_idx (c*cs + m)
 //   3. per query cluster i (one thread): every slot looks up its key cluster
 //      (jn = inv[token]); the first slot of i that points into key cluster
-//      j stages the entry (j, per-member multiplicities) at its own slot
-//      position and counts it for j (atomic)
+//      j stages the entry (j, per-member multiplicities) in i's staging row
+//      (compact, ended by a sentinel) and counts it for j (atomic)
 //   4. per image, exclusive scan of the counts -> segment offsets
-//   5. per slot, staged entries are placed in their segments (atomic cursor)
+//   5. per query cluster, its staged entries are placed in their segments
+//      (atomic cursor)
 //   6. per key cluster, its segment is sorted by i (which fixes the
 //      summation order of the key-major pass and makes it deterministic) and
 //      every entry gets the q_idx row of its i, so that the key-major pass
@@ -81,97 +82,115 @@ plan_count_kernel(int B, int N, int nk, const int32_t* __restrict__ key_idx,
     for (int m = 1; m < 8; ++m) same = same && my[8 * g + m] >= 0 && (my[8 * g + m] >> 3) == (j0 >> 3);
     grouped = same;
   }
+  int ne = 0;   // entries staged so far (compactly, then a sentinel)
   if (grouped) {
     for (int g = 0; g < ng; ++g) {
       const int j = my[8 * g] >> 3;
       bool first = true;
       for (int h = 0; h < g; ++h) first = first && (my[8 * h] >> 3) != j;
+      if (!first) continue;
+      uint64_t mult = 0;
+      for (int h = g; h < ng; ++h)
+        if ((my[8 * h] >> 3) == j)
+          for (int m = 0; m < 8; ++m) mult += 1ull << (8 * (my[8 * h + m] & 7));
       RevEntry e;
-      e.i = -1;
+      e.i = j;   // key cluster while staged
       e.pad = 0;
-      e.mult = 0;
-      if (first) {
-        uint64_t mult = 0;
-        for (int h = g; h < ng; ++h)
-          if ((my[8 * h] >> 3) == j)
-            for (int m = 0; m < 8; ++m) mult += 1ull << (8 * (my[8 * h + m] & 7));
-        e.i = j;   // key cluster while staged
-        e.mult = mult;
-        atomicAdd(&cnt[b * C + j], 1);
-      }
-      st[8 * g] = e;
-      RevEntry none;
-      none.i = -1;
-      none.pad = 0;
-      none.mult = 0;
-      for (int m = 1; m < 8; ++m) st[8 * g + m] = none;
+      e.mult = mult;
+      st[ne++] = e;
+      atomicAdd(&cnt[b * C + j], 1);
     }
-    return;
-  }
-  for (int s = 0; s < nk; ++s) {
-    const int js = my[s];
-    RevEntry e;
-    e.i = -1;
-    e.pad = 0;
-    e.mult = 0;
-    if (js >= 0) {
+  } else {
+    for (int s = 0; s < nk; ++s) {
+      const int js = my[s];
+      if (js < 0) continue;
       const int j = js >> 3;
       bool first = true;
       for (int u = s - 1; u >= 0; --u)
         if (my[u] >= 0 && (my[u] >> 3) == j) { first = false; break; }
-      if (first) {
-        uint64_t mult = 0;
-        for (int u = s; u < nk; ++u)
-          if (my[u] >= 0 && (my[u] >> 3) == j) mult += 1ull << (8 * (my[u] & 7));
-        e.i = j;   // key cluster while staged
-        e.mult = mult;
-        atomicAdd(&cnt[b * C + j], 1);
-      }
+      if (!first) continue;
+      uint64_t mult = 0;
+      for (int u = s; u < nk; ++u)
+        if (my[u] >= 0 && (my[u] >> 3) == j) mult += 1ull << (8 * (my[u] & 7));
+      RevEntry e;
+      e.i = j;
+      e.pad = 0;
+      e.mult = mult;
+      st[ne++] = e;
+      atomicAdd(&cnt[b * C + j], 1);
     }
-    st[s] = e;
+  }
+  if (ne < nk) {
+    RevEntry end;
+    end.i = -1;
+    end.pad = 0;
+    end.mult = 0;
+    st[ne] = end;
   }
 }
 
-// one workgroup per image: segment offsets from the counts (each thread
-// sums a run of counts, one workgroup scan, then the run is written out)
+// one workgroup per image: segment offsets from the counts.  Counts are
+// staged through LDS in chunks of kScanChunk (coalesced), each thread scans
+// a contiguous run of the chunk, one workgroup scan joins the runs.
+constexpr int kScanChunk = 8192;
+
 __global__ void __launch_bounds__(kPlanThreads)
 plan_scan_kernel(int C, const int32_t* __restrict__ cnt_all, int32_t* __restrict__ off_all,
                  int32_t* __restrict__ cur_all) {
+  __shared__ int32_t v[kScanChunk];
   __shared__ int32_t tmp[17];
   const int64_t b = blockIdx.x;
   const int32_t* cnt = cnt_all + b * C;
   int32_t* off = off_all + b * (C + 1);
   int32_t* cur = cur_all + b * C;
-  const int per = (C + kPlanThreads - 1) / kPlanThreads;
-  const int j0 = threadIdx.x * per, j1 = min(C, j0 + per);
-  int run = 0;
-  for (int j = j0; j < j1; ++j) run += cnt[j];
-  int tot;
-  int acc = block_exclusive_scan(run, tmp, kPlanThreads, &tot);
-  for (int j = j0; j < j1; ++j) {
-    off[j] = acc;
-    cur[j] = acc;
-    acc += cnt[j];
+  constexpr int kPer = kScanChunk / kPlanThreads;
+  int carry = 0;
+  for (int c0 = 0; c0 < C; c0 += kScanChunk) {
+    const int n = min(kScanChunk, C - c0);
+    for (int x = threadIdx.x; x < n; x += kPlanThreads) v[x] = cnt[c0 + x];
+    __syncthreads();
+    const int r0 = threadIdx.x * kPer;
+    int run = 0;
+#pragma unroll
+    for (int r = 0; r < kPer; ++r) run += r0 + r < n ? v[r0 + r] : 0;
+    int tot;
+    int acc = carry + block_exclusive_scan(run, tmp, kPlanThreads, &tot);
+#pragma unroll
+    for (int r = 0; r < kPer; ++r) {
+      if (r0 + r < n) {
+        const int c = v[r0 + r];
+        v[r0 + r] = acc;
+        acc += c;
+      }
+    }
+    __syncthreads();
+    for (int x = threadIdx.x; x < n; x += kPlanThreads) {
+      off[c0 + x] = v[x];
+      cur[c0 + x] = v[x];
+    }
+    carry += tot;
+    __syncthreads();   // v and tmp are reused by the next chunk
   }
-  if (threadIdx.x == 0) off[C] = tot;
+  if (threadIdx.x == 0) off[C] = carry;
 }
 
-// one thread per slot: staged entries into their segments
+// one thread per query cluster: its staged entries into their segments
 __global__ void __launch_bounds__(kGridThreads)
 plan_place_kernel(int B, int C, int nk, const RevEntry* __restrict__ stage,
                   int32_t* __restrict__ cur_all, RevEntry* __restrict__ rev_all) {
-  const int64_t x = (int64_t)blockIdx.x * kGridThreads + threadIdx.x;
-  if (x >= (int64_t)B * C * nk) return;
-  const RevEntry s = stage[x];
-  if (s.i < 0) return;
-  const int64_t bc = x / nk;
+  const int64_t bc = (int64_t)blockIdx.x * kGridThreads + threadIdx.x;
+  if (bc >= (int64_t)B * C) return;
   const int64_t b = bc / C;
-  const int pos = atomicAdd(&cur_all[b * C + s.i], 1);
-  RevEntry r;
-  r.i = (int32_t)(bc - b * C);
-  r.pad = 0;
-  r.mult = s.mult;
-  rev_all[b * C * nk + pos] = r;
+  for (int e = 0; e < nk; ++e) {
+    const RevEntry s = stage[bc * nk + e];
+    if (s.i < 0) break;
+    const int pos = atomicAdd(&cur_all[b * C + s.i], 1);
+    RevEntry r;
+    r.i = (int32_t)(bc - b * C);
+    r.pad = 0;
+    r.mult = s.mult;
+    rev_all[b * C * nk + pos] = r;
+  }
 }
 
 // one thread per key cluster: sort its segment by i (in registers when it
@@ -434,7 +453,7 @@ hipError_t launch_bwd_plan(int B, int N, int nk, const int32_t* q_idx, const int
                        w.off, w.rev, w.rtok);
     return hipGetLastError();
   }
-  const int64_t tokens = (int64_t)B * N, clusters = (int64_t)B * C, slots = clusters * nk;
+  const int64_t tokens = (int64_t)B * N, clusters = (int64_t)B * C;
   auto grid = [](int64_t n) { return dim3((unsigned)((n + kGridThreads - 1) / kGridThreads)); };
   hipLaunchKernelGGL(plan_init_kernel, grid(tokens), dim3(kGridThreads), 0, st, tokens, clusters,
                      w.inv, w.cnt);
@@ -444,7 +463,7 @@ hipError_t launch_bwd_plan(int B, int N, int nk, const int32_t* q_idx, const int
                      w.stage);
   hipLaunchKernelGGL(plan_scan_kernel, dim3(B), dim3(kPlanThreads), 0, st, C,
                      (const int32_t*)w.cnt, w.off, w.cursor);
-  hipLaunchKernelGGL(plan_place_kernel, grid(slots), dim3(kGridThreads), 0, st, B, C, nk,
+  hipLaunchKernelGGL(plan_place_kernel, grid(clusters), dim3(kGridThreads), 0, st, B, C, nk,
                      (const RevEntry*)w.stage, w.cursor, w.rev);
   hipLaunchKernelGGL(plan_sort_kernel, grid(clusters), dim3(kGridThreads), 0, st, B, N, nk, q_idx,
                      (const int32_t*)w.off, w.rev, w.rtok);
