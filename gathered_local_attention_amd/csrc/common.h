@@ -65,16 +65,19 @@ static inline BwdWorkspace bwd_layout(void* base, int64_t B, int64_t N, int64_t 
 }
 
 // ---- workspace layout of the neighbour build ------------------------------
-constexpr int kSortChunk = 2048;   // tokens ranked together in LDS
-constexpr int kSelectTile = 1024;  // candidate centroids staged per LDS tile
+constexpr int kSortChunk = 2048;   // images up to this many tokens are built in LDS
+constexpr int kRankSeg = 512;      // larger images: tokens ranked together before merging
+constexpr int kBoxTile = 64;       // consecutive clusters per bounding box
 
 struct BuildWorkspace {
   uint32_t* qsorted;   // [B, N]  packed (qx | qy << 16) in cluster order
-  uint64_t* keys;      // [B, N]  sorted (code << 32 | token) per chunk (N > kSortChunk)
-  float2* cent;        // [B, C]  centroid sums (C > kSelectTile)
+  uint64_t* keys[2];   // [B, N]  (code << 32 | token) in sorted runs, two buffers
+  float2* cent;        // [B, C]  centroid sums
+  float4* box;         // [B, ceil(C / kBoxTile)]  centroid bounding boxes
   size_t bytes;
 };
 
+// Everything is only needed for images above kSortChunk tokens.
 static inline BuildWorkspace build_layout(void* base, int64_t B, int64_t N) {
   BuildWorkspace w;
   size_t p = 0;
@@ -84,9 +87,13 @@ static inline BuildWorkspace build_layout(void* base, int64_t B, int64_t N) {
     p = align_up(p + n, 256);
     return b ? (void*)(b + at) : (void*)nullptr;
   };
-  w.qsorted = (uint32_t*)take(N > kSortChunk ? (size_t)(B * N) * sizeof(uint32_t) : 0);
-  w.keys = (uint64_t*)take(N > kSortChunk ? (size_t)(B * N) * sizeof(uint64_t) : 0);
-  w.cent = (float2*)take(N / 8 > kSelectTile ? (size_t)(B * (N / 8)) * sizeof(float2) : 0);
+  const bool big = N > kSortChunk;
+  const int64_t C = N / 8, tiles = (C + kBoxTile - 1) / kBoxTile;
+  w.qsorted = (uint32_t*)take(big ? (size_t)(B * N) * sizeof(uint32_t) : 0);
+  w.keys[0] = (uint64_t*)take(big ? (size_t)(B * N) * sizeof(uint64_t) : 0);
+  w.keys[1] = (uint64_t*)take(big ? (size_t)(B * N) * sizeof(uint64_t) : 0);
+  w.cent = (float2*)take(big ? (size_t)(B * C) * sizeof(float2) : 0);
+  w.box = (float4*)take(big ? (size_t)(B * tiles) * sizeof(float4) : 0);
   w.bytes = p;
   return w;
 }

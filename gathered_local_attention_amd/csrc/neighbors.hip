@@ -18,14 +18,18 @@
 //                       insertion sort, bitonic fallback; centroid sums
 //                       decoded from the sorted codes; 4-lane split scan).
 //   rank_kernel         larger images: rank of every token inside its
-//                       2048-token chunk (keys held in LDS).
-//   merge_kernel        image-wide rank = rank in the own chunk plus, for every
-//                       other chunk, the number of keys below it (binary search
-//                       over that chunk staged in LDS).
-//   centroid_kernel     integer centroid sums when they exceed one LDS tile.
-//   select_kernel       per cluster: scan of all clusters of the image in LDS
-//                       tiles, keeping the k-1 smallest (d2 << 24 | index)
-//                       keys; then the key lists.
+//                       512-token segment (keys held in LDS).
+//   merge_round_kernel  pairwise merge of sorted runs (512, 1024, ... tokens):
+//                       a key's place is its place in its own run plus the
+//                       count of partner-run keys below it (binary search).
+//                       The last round writes the token order.
+//   centroid_box_kernel integer centroid sums, and the bounding box of every
+//                       64 consecutive clusters (one tile).
+//   select_box_kernel   per cluster: candidate scan of its own tile, then of
+//                       every other tile whose box lies within the current
+//                       (k-1)-th best distance of some cluster of the wave;
+//                       keeps the k-1 smallest (d2 << 24 | index) keys, then
+//                       writes the key lists.
 #include "common.h"
 
 #include <algorithm>
@@ -35,7 +39,6 @@ namespace ca {
 namespace {
 
 constexpr int kRankThreads = 256;
-constexpr int kSelectThreads = 64;
 
 __device__ __forceinline__ uint32_t spread16(uint32_t v) {
   v &= 0xFFFFu;
@@ -43,6 +46,15 @@ __device__ __forceinline__ uint32_t spread16(uint32_t v) {
   v = (v | (v << 4)) & 0x0F0F0F0Fu;
   v = (v | (v << 2)) & 0x33333333u;
   v = (v | (v << 1)) & 0x55555555u;
+  return v;
+}
+
+__device__ __forceinline__ uint32_t compact16(uint32_t v) {
+  v &= 0x55555555u;
+  v = (v | (v >> 1)) & 0x33333333u;
+  v = (v | (v >> 2)) & 0x0F0F0F0Fu;
+  v = (v | (v >> 4)) & 0x00FF00FFu;
+  v = (v | (v >> 8)) & 0x0000FFFFu;
   return v;
 }
 
@@ -57,12 +69,12 @@ __device__ __forceinline__ uint32_t quantize_axis(float c, double step) {
 // Rank the tokens of one segment.  grid = (ceil(L / 64), segments), where a
 // segment is [seg_start, seg_start + L) of image `b`.  Each workgroup ranks
 // 64 tokens (one per lane); its four wavefronts each count one quarter of
-// the segment's keys, read from LDS as broadcast 16-byte loads.
+// the segment's keys, read from LDS as broadcast 16-byte loads.  The keys
+// land sorted inside their segment.
 __global__ void __launch_bounds__(kRankThreads)
 rank_kernel(const float* __restrict__ coords, int N, int seg_len, int segs_per_image, double step,
-            int32_t* __restrict__ perm, uint32_t* __restrict__ qsorted,
-            uint64_t* __restrict__ chunk_keys) {
-  __shared__ __align__(16) uint64_t keys[kSortChunk];
+            uint64_t* __restrict__ run_keys) {
+  __shared__ __align__(16) uint64_t keys[kRankSeg];
   __shared__ int part[kRankThreads / 64][64];
   const int seg = blockIdx.y;
   const int b = seg / segs_per_image;
@@ -95,69 +107,41 @@ rank_kernel(const float* __restrict__ coords, int N, int seg_len, int segs_per_i
   __syncthreads();
   if (w != 0 || e >= L) return;
   const int rank = part[0][lane] + part[1][lane] + part[2][lane] + part[3][lane];
-
-  if (segs_per_image == 1) {
-    const int64_t at = (int64_t)b * N + rank;
-    perm[at] = (int32_t)(uint32_t)mine;
-    float2 c = xy[e];
-    qsorted[at] = quantize_axis(c.x, step) | (quantize_axis(c.y, step) << 16);
-  } else {
-    chunk_keys[(int64_t)b * N + start + rank] = mine;
-  }
+  run_keys[(int64_t)b * N + start + rank] = mine;
 }
 
-// Image-wide ranks for images split into chunks.  grid = (chunks, B); each
-// block owns one chunk (up to 2048 tokens, 8 per thread).
+// One round of the image-wide merge sort.  Sorted runs of `run` keys (a
+// power of two) are merged pairwise; grid = (ceil(N / 256), B), one thread
+// per key.  Keys are unique (they hold the token index), so a key's place in
+// the merged run is its place in its own run plus the number of keys of the
+// partner run below it.  The last round (out == nullptr) writes the token
+// order and the packed quantised coordinates, decoded from the code.
 __global__ void __launch_bounds__(kRankThreads)
-merge_kernel(const float* __restrict__ coords, int N, double step,
-             const uint64_t* __restrict__ chunk_keys, int32_t* __restrict__ perm,
-             uint32_t* __restrict__ qsorted) {
-  __shared__ uint64_t other[kSortChunk];
-  constexpr int kPer = kSortChunk / kRankThreads;
-  const int a = blockIdx.x;
-  const int b = blockIdx.y;
-  const int nchunks = (N + kSortChunk - 1) / kSortChunk;
-  const uint64_t* img = chunk_keys + (int64_t)b * N;
-  const int a0 = a * kSortChunk;
-  const int La = min(kSortChunk, N - a0);
-
-  uint64_t mine[kPer];
-  int rank[kPer];
-#pragma unroll
-  for (int r = 0; r < kPer; ++r) {
-    const int e = threadIdx.x + r * kRankThreads;
-    mine[r] = e < La ? img[a0 + e] : ~0ull;
-    rank[r] = e;   // position inside its own (sorted) chunk
+merge_round_kernel(int N, int run, const uint64_t* __restrict__ in, uint64_t* __restrict__ out,
+                   int32_t* __restrict__ perm, uint32_t* __restrict__ qsorted) {
+  const int x = blockIdx.x * kRankThreads + threadIdx.x;
+  const int64_t b = blockIdx.y;
+  if (x >= N) return;
+  const uint64_t* img = in + b * N;
+  const uint64_t key = img[x];
+  const int p0 = x & ~(2 * run - 1);
+  const bool first = x - p0 < run;
+  const int own0 = first ? p0 : p0 + run;
+  int lo = first ? p0 + run : p0;
+  int hi = first ? min(p0 + 2 * run, N) : p0 + run;
+  hi = max(hi, lo);   // a last run without partner
+  const int base = lo;
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (img[mid] < key) lo = mid + 1; else hi = mid;
   }
-
-  for (int c = 0; c < nchunks; ++c) {
-    if (c == a) continue;
-    const int c0 = c * kSortChunk;
-    const int Lc = min(kSortChunk, N - c0);
-    __syncthreads();
-    for (int e = threadIdx.x; e < Lc; e += kRankThreads) other[e] = img[c0 + e];
-    __syncthreads();
-#pragma unroll
-    for (int r = 0; r < kPer; ++r) {
-      int lo = 0, hi = Lc;   // number of keys < mine[r]
-      while (lo < hi) {
-        int mid = (lo + hi) >> 1;
-        if (other[mid] < mine[r]) lo = mid + 1; else hi = mid;
-      }
-      rank[r] += lo;
-    }
-  }
-
-  const float2* xy = reinterpret_cast<const float2*>(coords) + (int64_t)b * N;
-#pragma unroll
-  for (int r = 0; r < kPer; ++r) {
-    const int e = threadIdx.x + r * kRankThreads;
-    if (e >= La) continue;
-    const int tok = (int)(uint32_t)mine[r];
-    const int64_t at = (int64_t)b * N + rank[r];
-    perm[at] = tok;
-    float2 c = xy[tok];
-    qsorted[at] = quantize_axis(c.x, step) | (quantize_axis(c.y, step) << 16);
+  const int64_t at = b * N + p0 + (x - own0) + (lo - base);
+  if (out) {
+    out[at] = key;
+  } else {
+    const uint32_t code = (uint32_t)(key >> 32);
+    perm[at] = (int32_t)(uint32_t)key;
+    qsorted[at] = compact16(code) | (compact16(code >> 1) << 16);
   }
 }
 
@@ -175,77 +159,194 @@ __device__ __forceinline__ float2 centroid_sum(const uint32_t* __restrict__ q8) 
   return make_float2((float)sx, (float)sy);
 }
 
-// Centroid sums of every cluster (used when an image has more clusters than
-// one LDS tile).  grid = (ceil(B*C / 256)).
-__global__ void __launch_bounds__(256)
-centroid_kernel(int64_t n_clusters, const uint32_t* __restrict__ qsorted, float2* __restrict__ cent) {
-  const int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (c < n_clusters) cent[c] = centroid_sum(qsorted + 8 * c);
+// Centroid sums of every cluster and the bounding box (min x, min y, max x,
+// max y) of every tile of kBoxTile consecutive clusters.  grid =
+// (ceil(C / kBoxTile), B), one wavefront per tile.
+__global__ void __launch_bounds__(kBoxTile)
+centroid_box_kernel(int C, const uint32_t* __restrict__ qsorted, float2* __restrict__ cent_all,
+                    float4* __restrict__ box_all) {
+  const int t = blockIdx.x;
+  const int64_t b = blockIdx.y;
+  const int c = t * kBoxTile + threadIdx.x;
+  float lx = INFINITY, ly = INFINITY, hx = -INFINITY, hy = -INFINITY;
+  if (c < C) {
+    const float2 s = centroid_sum(qsorted + (b * C + c) * 8);
+    cent_all[b * C + c] = s;
+    lx = hx = s.x;
+    ly = hy = s.y;
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    lx = fminf(lx, __shfl_xor(lx, o, 64));
+    ly = fminf(ly, __shfl_xor(ly, o, 64));
+    hx = fmaxf(hx, __shfl_xor(hx, o, 64));
+    hy = fmaxf(hy, __shfl_xor(hy, o, 64));
+  }
+  if (threadIdx.x == 0) box_all[b * gridDim.x + t] = make_float4(lx, ly, hx, hy);
 }
 
-// Nearest clusters and key lists.  grid = (ceil(C / 64), B), one thread per
-// cluster.  Candidates are screened with an fp32 distance whose error bound
-// (relative 2^-23) cannot drop a candidate at or below the current k-1-th
-// best; survivors are compared exactly as (d2 << 24 | index) in 64 bits.
 template <int KM1>
-__global__ void __launch_bounds__(kSelectThreads)
-select_kernel(int N, const uint32_t* __restrict__ qsorted, const float2* __restrict__ cent_all,
-              const int32_t* __restrict__ perm, int32_t* __restrict__ nbr,
-              int32_t* __restrict__ key_idx) {
-  __shared__ float2 cand[kSelectTile];
-  const int C = N / 8;
-  const int b = blockIdx.y;
-  const int c = blockIdx.x * kSelectThreads + threadIdx.x;
-  const uint32_t* qimg = qsorted + (int64_t)b * N;
-  const float2* cent = cent_all ? cent_all + (int64_t)b * C : nullptr;
-  const float2 me = c < C ? (cent ? cent[c] : centroid_sum(qimg + 8 * c)) : make_float2(0.f, 0.f);
+__device__ __forceinline__ void top_insert(uint64_t (&best)[KM1 > 0 ? KM1 : 1], uint64_t x) {
+  if constexpr (KM1 > 0) {
+    if (x >= best[KM1 - 1]) return;
+#pragma unroll
+    for (int r = 0; r < KM1; ++r) {
+      const uint64_t lo = x < best[r] ? x : best[r];
+      const uint64_t hi = x < best[r] ? best[r] : x;
+      best[r] = lo;
+      x = hi;
+    }
+  }
+}
 
+// Scan one tile of candidate centroids (staged in this wave's LDS row) for
+// the lanes with `need`, keeping the KM1 smallest (d2 << 24 | index) keys.
+// Candidates are screened with an fp32 distance whose error bound (relative
+// 2^-23) cannot drop a candidate at or below the current KM1-th best; the
+// survivors are compared exactly in 64 bits, so the kept set does not depend
+// on the order of the scan.
+template <int KM1>
+__device__ __forceinline__ void scan_tile(const float2* __restrict__ cent, float2* __restrict__ row,
+                                          int t0, int T, int c, float2 me, bool need,
+                                          uint64_t (&best)[KM1 > 0 ? KM1 : 1], float& thr) {
+  const int lane = threadIdx.x & 63;
+  const float2 mine = lane < T ? cent[t0 + lane] : make_float2(0.f, 0.f);
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // earlier reads of the row are done
+  row[lane] = mine;
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // the row is written (one wave)
+  if (!need) return;
+  const float4* row4 = reinterpret_cast<const float4*>(row);
+  for (int i0 = 0; i0 < T; i0 += 8) {
+    float2 cc[8];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const float4 q = row4[(i0 >> 1) + u];
+      cc[2 * u] = make_float2(q.x, q.y);
+      cc[2 * u + 1] = make_float2(q.z, q.w);
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int e = i0 + u;
+      const float dx = cc[u].x - me.x, dy = cc[u].y - me.y;   // exact
+      const float d2f = fmaf(dx, dx, dy * dy);
+      if (e >= T || d2f > thr || t0 + e == c) continue;
+      const int ix = (int)dx, iy = (int)dy;
+      const uint64_t key = ((uint64_t)((int64_t)ix * ix + (int64_t)iy * iy) << 24) | (uint32_t)(t0 + e);
+      if (key >= best[KM1 - 1]) continue;
+      uint64_t x = key;
+#pragma unroll
+      for (int r = 0; r < KM1; ++r) {
+        const uint64_t lo = x < best[r] ? x : best[r];
+        const uint64_t hi = x < best[r] ? best[r] : x;
+        best[r] = lo;
+        x = hi;
+      }
+      if (best[KM1 - 1] != ~0ull) thr = (float)(best[KM1 - 1] >> 24) * (1.0f + 0x1p-20f);
+    }
+  }
+}
+
+__device__ __forceinline__ float wave_minf(float x) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x = fminf(x, __shfl_xor(x, o, 64));
+  return x;
+}
+__device__ __forceinline__ float wave_maxf(float x) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o, 64));
+  return x;
+}
+
+// Nearest clusters and key lists.  grid = (ceil(C / kBoxTile), B); the
+// kSelWaves wavefronts of a workgroup serve the same tile of clusters, one
+// lane per cluster.  Every wave scans the own tile (which sets each lane's
+// threshold, its current KM1-th best distance), then the tiles whose
+// bounding box lies within the largest threshold of the wave from the
+// bounding box of the wave's clusters are dealt round-robin to the waves;
+// each scans a dealt tile for the lanes whose own threshold still reaches
+// the tile's box.  The waves' lists are merged at the end.
+constexpr int kSelWaves = 4;
+
+template <int KM1>
+__global__ void __launch_bounds__(kBoxTile * kSelWaves)
+select_box_kernel(int N, const float2* __restrict__ cent_all, const float4* __restrict__ box_all,
+                  const int32_t* __restrict__ perm, int32_t* __restrict__ nbr,
+                  int32_t* __restrict__ key_idx) {
   constexpr int KB = KM1 > 0 ? KM1 : 1;
+  __shared__ __align__(16) float2 cand[kSelWaves][kBoxTile];
+  __shared__ uint64_t part[kSelWaves - 1][KB][kBoxTile];
+  const int C = N / 8;
+  const int ntiles = gridDim.x;
+  const int b = blockIdx.y;
+  const int own = blockIdx.x;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int c = own * kBoxTile + lane;
+  const bool valid = c < C;
+  const float2* cent = cent_all + (int64_t)b * C;
+  const float4* box = box_all + (int64_t)b * ntiles;
+  const float2 me = valid ? cent[c] : make_float2(0.f, 0.f);
+
   uint64_t best[KB];
 #pragma unroll
   for (int r = 0; r < KB; ++r) best[r] = ~0ull;
   float thr = INFINITY;
 
-  // Tiles are visited starting with the one holding this workgroup's
-  // clusters, and each thread starts its tile scan at its own cluster:
-  // Morton neighbours come first, so the threshold drops at once and far
-  // candidates fail the fp32 screen.  The kept set does not depend on the
-  // order (exact (d2, index) keys).
-  const int ntiles = (C + kSelectTile - 1) / kSelectTile;
-  const int tfirst = (int)(blockIdx.x * kSelectThreads) / kSelectTile;
-  for (int ti = 0; ti < ntiles; ++ti) {
-    const int tt = tfirst + ti < ntiles ? tfirst + ti : tfirst + ti - ntiles;
-    const int t0 = tt * kSelectTile;
-    const int T = min(kSelectTile, C - t0);
-    __syncthreads();
-    for (int e = threadIdx.x; e < T; e += kSelectThreads)
-      cand[e] = cent ? cent[t0 + e] : centroid_sum(qimg + 8 * (t0 + e));
-    __syncthreads();
-    if constexpr (KM1 > 0) {
-      if (c < C) {
-        const int es = (c >= t0 && c < t0 + T) ? c - t0 : 0;
-        for (int i = 0; i < T; ++i) {
-          const int e = es + i < T ? es + i : es + i - T;
-          const float dx = cand[e].x - me.x, dy = cand[e].y - me.y;   // exact
-          const float d2f = fmaf(dx, dx, dy * dy);
-          if (d2f > thr || t0 + e == c) continue;
-          const int64_t ix = (int64_t)dx, iy = (int64_t)dy;
-          const uint64_t key = ((uint64_t)(ix * ix + iy * iy) << 24) | (uint32_t)(t0 + e);
-          if (key >= best[KM1 - 1]) continue;
-          uint64_t x = key;
-#pragma unroll
-          for (int r = 0; r < KM1; ++r) {
-            const uint64_t lo = x < best[r] ? x : best[r];
-            const uint64_t hi = x < best[r] ? best[r] : x;
-            best[r] = lo;
-            x = hi;
-          }
-          if (best[KM1 - 1] != ~0ull) thr = (float)(best[KM1 - 1] >> 24) * (1.0f + 0x1p-20f);
-        }
+  if constexpr (KM1 > 0) {
+    scan_tile<KM1>(cent, cand[w], own * kBoxTile, min(kBoxTile, C - own * kBoxTile), c, me, valid,
+                   best, thr);
+    // bounding box of the wave's clusters and its largest threshold
+    const float mlx = wave_minf(valid ? me.x : INFINITY), mly = wave_minf(valid ? me.y : INFINITY);
+    const float mhx = wave_maxf(valid ? me.x : -INFINITY), mhy = wave_maxf(valid ? me.y : -INFINITY);
+    const float mthr = wave_maxf(valid ? thr : -INFINITY);
+    int dealt = 0;   // candidate tiles seen so far (all waves agree)
+    for (int g0 = 0; g0 < ntiles; g0 += 64) {
+      const int tl = g0 + lane;
+      bool cand_tile = false;
+      if (tl < ntiles && tl != own) {
+        const float4 bx = box[tl];
+        const float dx = fmaxf(fmaxf(bx.x - mhx, mlx - bx.z), 0.f);   // exact
+        const float dy = fmaxf(fmaxf(bx.y - mhy, mly - bx.w), 0.f);
+        cand_tile = fmaf(dx, dx, dy * dy) <= mthr;
+      }
+      uint64_t mask = __ballot(cand_tile);
+      while (mask) {
+        const int bit = __builtin_ctzll(mask);
+        mask &= mask - 1;
+        if (dealt++ % kSelWaves != w) continue;
+        const int tt = g0 + bit;
+        const float4 bx = box[tt];
+        const float dx = fmaxf(fmaxf(bx.x - me.x, me.x - bx.z), 0.f);   // exact
+        const float dy = fmaxf(fmaxf(bx.y - me.y, me.y - bx.w), 0.f);
+        const bool need = valid && fmaf(dx, dx, dy * dy) <= thr;
+        if (!__any(need)) continue;
+        scan_tile<KM1>(cent, cand[w], tt * kBoxTile, min(kBoxTile, C - tt * kBoxTile), c, me, need,
+                       best, thr);
       }
     }
+    // merge the waves' lists into wave 0; every wave holds the own tile's
+    // survivors, so keys already present are skipped (keys are unique per
+    // candidate)
+    if (w > 0) {
+#pragma unroll
+      for (int r = 0; r < KM1; ++r) part[w - 1][r][lane] = best[r];
+    }
+    __syncthreads();
+    if (w > 0) return;
+#pragma unroll
+    for (int v = 0; v < kSelWaves - 1; ++v) {
+#pragma unroll
+      for (int r = 0; r < KM1; ++r) {
+        const uint64_t x = part[v][r][lane];
+        bool dup = false;
+#pragma unroll
+        for (int q = 0; q < KM1; ++q) dup = dup || best[q] == x;
+        if (!dup) top_insert<KM1>(best, x);
+      }
+    }
+  } else {
+    if (w > 0) return;
   }
-  if (c >= C) return;
+  if (!valid) return;
 
   constexpr int K = KM1 + 1;
   int32_t ids[K];
@@ -275,32 +376,10 @@ select_kernel(int N, const uint32_t* __restrict__ qsorted, const float2* __restr
 constexpr int kSmallThreads = 1024;
 constexpr int kSmallMaxC = kSortChunk / 8;     // 256 clusters
 
-__device__ __forceinline__ uint32_t compact16(uint32_t v) {
-  v &= 0x55555555u;
-  v = (v | (v >> 1)) & 0x33333333u;
-  v = (v | (v >> 2)) & 0x0F0F0F0Fu;
-  v = (v | (v >> 4)) & 0x00FF00FFu;
-  v = (v | (v >> 8)) & 0x0000FFFFu;
-  return v;
-}
-
 constexpr int kBuckets = 2 * kSmallThreads;       // counting-sort buckets (top 11 code bits)
 constexpr int kBucketShift = 21;
 constexpr int kMaxBucket = 32;                    // larger buckets -> bitonic fallback
 
-template <int KM1>
-__device__ __forceinline__ void top_insert(uint64_t (&best)[KM1 > 0 ? KM1 : 1], uint64_t x) {
-  if constexpr (KM1 > 0) {
-    if (x >= best[KM1 - 1]) return;
-#pragma unroll
-    for (int r = 0; r < KM1; ++r) {
-      const uint64_t lo = x < best[r] ? x : best[r];
-      const uint64_t hi = x < best[r] ? best[r] : x;
-      best[r] = lo;
-      x = hi;
-    }
-  }
-}
 
 template <int KM1>
 __global__ void __launch_bounds__(kSmallThreads)
@@ -522,26 +601,28 @@ hipError_t launch_build_neighbors(const float* coords, int B, int N, int grid_si
     }
     return hipGetLastError();
   }
-  // larger images: chunk ranks, image-wide merge, centroids, tiled selection
-  const int chunks = (N + kSortChunk - 1) / kSortChunk;
-  hipLaunchKernelGGL(rank_kernel, dim3(kSortChunk / 64, B * chunks), dim3(kRankThreads), 0, st,
-                     coords, N, kSortChunk, chunks, step, perm, w.qsorted, w.keys);
-  hipLaunchKernelGGL(merge_kernel, dim3(chunks, B), dim3(kRankThreads), 0, st, coords, N, step,
-                     (const uint64_t*)w.keys, perm, w.qsorted);
-  float2* cent = nullptr;
-  if (C > kSelectTile) {
-    cent = w.cent;
-    const int64_t nc = (int64_t)B * C;
-    hipLaunchKernelGGL(centroid_kernel, dim3((unsigned)((nc + 255) / 256)), dim3(256), 0, st, nc,
-                       (const uint32_t*)w.qsorted, cent);
+  // larger images: segment ranks, merge rounds, centroids and boxes, selection
+  const int segs = (N + kRankSeg - 1) / kRankSeg;
+  hipLaunchKernelGGL(rank_kernel, dim3(kRankSeg / 64, B * segs), dim3(kRankThreads), 0, st,
+                     coords, N, kRankSeg, segs, step, w.keys[0]);
+  int cur = 0;
+  const dim3 mgrid((N + kRankThreads - 1) / kRankThreads, B);
+  for (int run = kRankSeg; run < N; run *= 2) {
+    const bool last = 2 * run >= N;
+    hipLaunchKernelGGL(merge_round_kernel, mgrid, dim3(kRankThreads), 0, st, N, run,
+                       (const uint64_t*)w.keys[cur], last ? nullptr : w.keys[cur ^ 1], perm,
+                       w.qsorted);
+    cur ^= 1;
   }
-  dim3 sgrid((C + kSelectThreads - 1) / kSelectThreads, B);
+  const dim3 tgrid((C + kBoxTile - 1) / kBoxTile, B);
+  hipLaunchKernelGGL(centroid_box_kernel, tgrid, dim3(kBoxTile), 0, st, C,
+                     (const uint32_t*)w.qsorted, w.cent, w.box);
   switch (k) {
 #define CA_SEL(KK)                                                                              \
   case KK:                                                                                      \
-    hipLaunchKernelGGL(select_kernel<KK - 1>, sgrid, dim3(kSelectThreads), 0, st, N,            \
-                       (const uint32_t*)w.qsorted, (const float2*)cent, (const int32_t*)perm,  \
-                       nbr, key_idx);                                                           \
+    hipLaunchKernelGGL(select_box_kernel<KK - 1>, tgrid, dim3(kBoxTile * kSelWaves), 0, st, N, \
+                       (const float2*)w.cent, (const float4*)w.box, (const int32_t*)perm, nbr,  \
+                       key_idx);                                                                \
     break;
     CA_SEL(1) CA_SEL(2) CA_SEL(3) CA_SEL(4) CA_SEL(5) CA_SEL(6) CA_SEL(7) CA_SEL(8)
 #undef CA_SEL

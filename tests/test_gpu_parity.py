@@ -76,6 +76,24 @@ def test_neighbours_ragged_chunks_and_k(ca, G, k):
     assert_lists_equal(gpu_lists(ca, coords, G, k=k), ref, f"G={G}")
 
 
+@pytest.mark.parametrize("N,k", [(9000, 6), (2056, 4)])
+def test_neighbours_blobs_and_outliers(ca, N, k):
+    """Uneven density (dense blobs of several widths, sparse background):
+    the candidate search of large images skips tiles by their bounding
+    boxes, and the lists must still be the exact ones."""
+    rng = np.random.default_rng(N + k)
+    G = 128
+    centres = rng.uniform(0, G, (5, 2))
+    widths = rng.uniform(0.3, 6.0, 5)
+    lab = rng.integers(0, 5, N)
+    xy = centres[lab] + rng.normal(0.0, 1.0, (N, 2)) * widths[lab, None]
+    xy[: N // 50] = rng.uniform(0, G, (N // 50, 2))
+    coords = np.stack([xy, xy[rng.permutation(N)]]).astype(np.float32)
+    print(f"case blobs N={N} k={k}", flush=True)
+    ref = O.build_neighbors(coords, G, k=k)
+    assert_lists_equal(gpu_lists(ca, coords, G, k=k), ref, f"blobs N={N}")
+
+
 def test_neighbours_with_code_ties_and_few_clusters(ca):
     rng = np.random.default_rng(3)
     # many tokens share a coordinate -> equal Morton codes, order by index
