@@ -31,9 +31,11 @@ HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, vendor figure
 # kernels behind each entry point on the bf16/f16 path (the roofline is per
 # entry point; the committed kernel trace splits it per kernel)
 ENTRY_KERNELS = {
-    "build": ["build_small_kernel (N <= 2048) | rank, merge, centroid, select (N > 2048)"],
+    "build": ["build_small_kernel (N <= 2048) | rank_kernel, merge_round_kernel, "
+              "centroid_box_kernel, select_box_kernel (N > 2048)"],
     "fwd": ["fwd_lds_kernel"],
-    "bwd": ["plan_small_kernel", "bwd_q_lds_kernel", "bwd_kv_lds_kernel"],
+    "bwd": ["plan_small_kernel (small images) | plan_init/inv/count/scan/place/sort_kernel",
+            "bwd_q_lds_kernel", "bwd_kv_lds_kernel"],
 }
 BF16_MFMA_PEAK_TFLOPS = 2500.0  # dense
 
