@@ -533,14 +533,26 @@ build_small_kernel(const float* __restrict__ coords, int N, double step, int par
           if (key[u] < best[KM1 - 1]) top_insert<KM1>(best, key[u]);
       }
     }
-    // merge the partial lists of the lanes of a cluster (aligned lane groups)
-    for (int o = 1; o < lanes; o <<= 1) {
-      uint64_t other[KB];
+    // Merge the sorted partial lists of the lanes of a cluster (aligned lane
+    // groups) by a tournament: KM1 times, the smallest head over the group
+    // is taken and its lane (keys are unique) drops its head.
+    uint64_t merged[KB];
 #pragma unroll
-      for (int r = 0; r < KB; ++r) other[r] = __shfl_xor(best[r], o, 64);
+    for (int r = 0; r < KM1; ++r) {
+      uint64_t m = best[0];
+      for (int o = 1; o < lanes; o <<= 1) {
+        const uint64_t x = __shfl_xor(m, o, 64);
+        m = x < m ? x : m;
+      }
+      merged[r] = m;
+      if (best[0] == m && m != ~0ull) {
 #pragma unroll
-      for (int r = 0; r < KB; ++r) top_insert<KM1>(best, other[r]);
+        for (int u = 0; u + 1 < KM1; ++u) best[u] = best[u + 1];
+        best[KM1 - 1] = ~0ull;
+      }
     }
+#pragma unroll
+    for (int r = 0; r < KM1; ++r) best[r] = merged[r];
   }
   if (!mine) return;
 
