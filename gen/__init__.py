@@ -14,3 +14,4 @@ from .synth import (  # noqa: F401
     stress_copy_rows,
     to_dtype,
 )
+from .sampler import SAMPLER_CONFIGS, SamplerConfig, make_sampler_case  # noqa: F401

@@ -5,8 +5,9 @@ TEST INFRASTRUCTURE ONLY.  This package is imported by ``tests/``, by
 the product path (``gathered_local_attention_amd``) never imports, calls or
 links it, and it imports nothing from the product path.
 
-See :mod:`oracle.cluster_attention` for the functions and the passages of
-the pages each one follows.
+See :mod:`oracle.cluster_attention` (neighbour build and attention) and
+:mod:`oracle.knn_sampler` (the decoder's KNN-cache point sampler) for the
+functions and the passages of the pages each one follows.
 """
 
 from .cluster_attention import (  # noqa: F401
@@ -23,4 +24,14 @@ from .cluster_attention import (  # noqa: F401
     attn_fwd_gathered,
     attn_bwd_dense,
     attn_bwd_gathered,
+)
+from .knn_sampler import (  # noqa: F401
+    knn_table,
+    query_cells,
+    knn_weights,
+    knn_sample_fwd,
+    knn_sample_bwd,
+    knn_table_batch,
+    knn_sample_fwd_batch,
+    knn_sample_bwd_batch,
 )
