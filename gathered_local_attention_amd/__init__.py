@@ -12,6 +12,10 @@ build_neighbors(coords, grid_side, cs=8, k=6) -> (perm, nbr, key_idx)
 fwd(q, k, v, q_idx, key_idx, scale=None) -> (o, lse)
 bwd(q, k, v, o, do, lse, q_idx, key_idx, scale=None) -> (dq, dk, dv)
 cluster_attention(q, k, v, q_idx, key_idx, scale=None) -> o   (autograd)
+knn_table(coords, grid_side, K) -> table
+knn_sample_fwd(feats, coords, queries, table, p) -> out
+knn_sample_bwd(feats, coords, queries, table, p, dout) -> (dfeats, dq, dp)
+knn_sample(feats, coords, queries, table, p) -> out   (autograd: feats, queries)
 """
 
 from __future__ import annotations
@@ -29,6 +33,11 @@ __all__ = [
     "cluster_attention",
     "bwd_workspace_bytes",
     "build_workspace_bytes",
+    "knn_table",
+    "knn_sample_fwd",
+    "knn_sample_bwd",
+    "knn_sample",
+    "knn_bwd_workspace_bytes",
     "ClusterAttnError",
     "CA_OK",
 ]
@@ -172,3 +181,97 @@ class _ClusterAttention(torch.autograd.Function):
 def cluster_attention(q, k, v, q_idx, key_idx, scale: float | None = None):
     """Autograd-aware local cluster attention (index lists are constants)."""
     return _ClusterAttention.apply(q, k, v, q_idx, key_idx, scale)
+
+
+# ---------------------------------------------------------------------------
+# KNN-cache point sampler (decoder)
+# ---------------------------------------------------------------------------
+
+def knn_table(coords: torch.Tensor, grid_side: int, K: int) -> torch.Tensor:
+    """[B, G, G, K] int32 table of the K nearest tokens of every grid cell.
+
+    coords: [B, N, 2] float32 device tensor (x = column, y = row)."""
+    lib = _lib.load()
+    B, N, two = coords.shape
+    if two != 2:
+        raise ValueError("coords must be [B, N, 2]")
+    G = int(grid_side)
+    table = torch.empty((B, G, G, K), dtype=torch.int32, device=coords.device)
+    _check(lib.cluster_attn_knn_table(_dev(coords, "coords", torch.float32), B, N, G, K,
+                                      table.data_ptr(), _stream(coords)), "cluster_attn_knn_table")
+    return table
+
+
+def _knn_shapes(feats, coords, queries, table):
+    if feats.dim() != 3 or coords.dim() != 3 or queries.dim() != 3 or table.dim() != 4:
+        raise ValueError("feats [B, N, C], coords [B, N, 2], queries [B, M, 2], table [B, G, G, K]")
+    B, N, C = feats.shape
+    M = queries.shape[1]
+    G, K = table.shape[1], table.shape[3]
+    if coords.shape != (B, N, 2) or queries.shape != (B, M, 2) or table.shape != (B, G, G, K):
+        raise ValueError("inconsistent shapes")
+    if feats.dtype not in _DT:
+        raise TypeError(f"unsupported dtype {feats.dtype}")
+    return B, N, M, C, G, K
+
+
+def knn_sample_fwd(feats, coords, queries, table, p: float) -> torch.Tensor:
+    """out [B, M, C] (dtype of feats) = softmax(-p d)-weighted sum of the
+    table slots of every query's nearest cell."""
+    lib = _lib.load()
+    B, N, M, C, G, K = _knn_shapes(feats, coords, queries, table)
+    out = torch.empty((B, M, C), dtype=feats.dtype, device=feats.device)
+    _check(lib.cluster_attn_knn_sample_fwd(
+        _DT[feats.dtype], B, N, M, C, G, K, float(p), _dev(coords, "coords", torch.float32),
+        _dev(feats, "feats"), _dev(queries, "queries", torch.float32),
+        _dev(table, "table", torch.int32), out.data_ptr(), _stream(feats)),
+        "cluster_attn_knn_sample_fwd")
+    return out
+
+
+def knn_bwd_workspace_bytes(B: int, N: int, M: int, K: int) -> int:
+    return int(_lib.load().cluster_attn_knn_sample_bwd_workspace(B, N, M, K))
+
+
+def knn_sample_bwd(feats, coords, queries, table, p: float, dout,
+                   workspace: torch.Tensor | None = None):
+    """Returns dfeats [B, N, C] (dtype of feats), dq [B, M, 2] f32 and dp
+    (a one-element f32 device tensor)."""
+    lib = _lib.load()
+    B, N, M, C, G, K = _knn_shapes(feats, coords, queries, table)
+    if dout.shape != (B, M, C) or dout.dtype != feats.dtype:
+        raise ValueError("dout must be [B, M, C] in the dtype of feats")
+    need = lib.cluster_attn_knn_sample_bwd_workspace(B, N, M, K)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=feats.device)
+    dfeats = torch.empty_like(feats)
+    dq = torch.empty((B, M, 2), dtype=torch.float32, device=feats.device)
+    dp = torch.empty((1,), dtype=torch.float32, device=feats.device)
+    _check(lib.cluster_attn_knn_sample_bwd(
+        _DT[feats.dtype], B, N, M, C, G, K, float(p), _dev(coords, "coords", torch.float32),
+        _dev(feats, "feats"), _dev(queries, "queries", torch.float32),
+        _dev(table, "table", torch.int32), _dev(dout, "dout"), dfeats.data_ptr(), dq.data_ptr(),
+        dp.data_ptr(), workspace.data_ptr(), workspace.numel(), _stream(feats)),
+        "cluster_attn_knn_sample_bwd")
+    return dfeats, dq, dp
+
+
+class _KnnSample(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, feats, coords, queries, table, p):
+        out = knn_sample_fwd(feats, coords, queries, table, p)
+        ctx.save_for_backward(feats, coords, queries, table)
+        ctx.p = p
+        return out
+
+    @staticmethod
+    def backward(ctx, dout):
+        feats, coords, queries, table = ctx.saved_tensors
+        dfeats, dq, _ = knn_sample_bwd(feats, coords, queries, table, ctx.p, dout.contiguous())
+        return dfeats, None, dq, None, None
+
+
+def knn_sample(feats, coords, queries, table, p: float):
+    """Autograd-aware sampler (gradients for feats and queries; the table
+    and the token coordinates are constants)."""
+    return _KnnSample.apply(feats, coords, queries, table, p)

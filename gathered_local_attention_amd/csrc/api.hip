@@ -74,6 +74,20 @@ int check_attn_shape(int dt, int B, int N, int H, int D, int cs, int nk) {
   return CA_OK;
 }
 
+
+// Shape checks of the KNN sampler calls.
+int check_knn_shape(int B, int N, int M, int Cf, int G, int K) {
+  if (B < 0 || N < 0 || M < 0) return fail(CA_ERR_SHAPE, "bad sizes B=%d N=%d M=%d", B, N, M);
+  if (G < 1 || G > 4096) return fail(CA_ERR_SHAPE, "grid_side=%d outside [1, 4096]", G);
+  if (K < 1 || K > 16) return fail(CA_ERR_UNSUPPORTED, "K=%d outside 1..16", K);
+  if (Cf < 8 || Cf > 1024 || Cf % 8 != 0)
+    return fail(CA_ERR_UNSUPPORTED, "channels %d: must be a multiple of 8 in [8, 1024]", Cf);
+  if (N > (1 << 24) || M > (1 << 24)) return fail(CA_ERR_SHAPE, "N or M above 2^24");
+  if ((int64_t)B * M * K > (int64_t(1) << 31) - 1 || (int64_t)M * K > (int64_t(1) << 31) - 1)
+    return fail(CA_ERR_SHAPE, "B*M*K too large");
+  return CA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -196,6 +210,79 @@ int cluster_attn_bwd(int dt, int B, int N, int H, int D, int cs, int nk, float s
   return hip_status(ca::launch_bwd_valu(3, dt, B, N, H, nk, scale, q, k, v, o, dout, lse, q_idx,
                                         key_idx, dq, dk, dv, w, st),
                     "bwd launch");
+}
+
+int cluster_attn_knn_table(const float* coords, int B, int N, int grid_side, int K,
+                           int32_t* table, void* hip_stream) {
+  if (B < 0 || N < 0) return fail(CA_ERR_SHAPE, "bad sizes B=%d N=%d", B, N);
+  if (grid_side < 1 || grid_side > 64)
+    return fail(CA_ERR_UNSUPPORTED, "grid_side=%d: the table build supports 1..64", grid_side);
+  if (N > 4096) return fail(CA_ERR_UNSUPPORTED, "N=%d: the table build supports up to 4096", N);
+  if (K < 1 || K > 16) return fail(CA_ERR_UNSUPPORTED, "K=%d outside 1..16", K);
+  if (B == 0) return ok();
+  if (!table || (N > 0 && !coords)) return fail(CA_ERR_NULL, "NULL tensor pointer");
+  const size_t tb = (size_t)B * grid_side * grid_side * K * 4;
+  Range outs[] = {{table, tb}};
+  Range ins[] = {{coords, (size_t)B * N * 8}};
+  if (int s = check_alias(outs, 1, ins, 1)) return s;
+  return hip_status(ca::launch_knn_table(coords, B, N, grid_side, K, table, (hipStream_t)hip_stream),
+                    "knn table launch");
+}
+
+int cluster_attn_knn_sample_fwd(int dt, int B, int N, int M, int C, int grid_side, int K, float p,
+                                const float* coords, const void* feats, const float* queries,
+                                const int32_t* table, void* out, void* hip_stream) {
+  if (dt != CA_F32 && dt != CA_BF16 && dt != CA_F16)
+    return fail(CA_ERR_UNSUPPORTED, "dtype %d is not one of CA_F32, CA_BF16, CA_F16", dt);
+  if (int s = check_knn_shape(B, N, M, C, grid_side, K)) return s;
+  if (!(p == p) || p == INFINITY || p == -INFINITY) return fail(CA_ERR_SHAPE, "p is not finite");
+  if (B == 0 || M == 0) return ok();
+  if (!queries || !table || !out || (N > 0 && (!coords || !feats)))
+    return fail(CA_ERR_NULL, "NULL tensor pointer");
+  const size_t es = elem_size(dt);
+  Range outs[] = {{out, (size_t)B * M * C * es}};
+  Range ins[] = {{coords, (size_t)B * N * 8},
+                 {feats, (size_t)B * N * C * es},
+                 {queries, (size_t)B * M * 8},
+                 {table, (size_t)B * grid_side * grid_side * K * 4}};
+  if (int s = check_alias(outs, 1, ins, 4)) return s;
+  return hip_status(ca::launch_knn_fwd(dt, B, N, M, C, grid_side, K, p, coords, feats, queries,
+                                       table, out, (hipStream_t)hip_stream),
+                    "knn fwd launch");
+}
+
+size_t cluster_attn_knn_sample_bwd_workspace(int B, int N, int M, int K) {
+  if (B < 0 || N < 0 || M < 0 || K < 1 || K > 16 || N > (1 << 24) || M > (1 << 24)) return 0;
+  return ca::knn_layout(nullptr, B, N, M, K).bytes;
+}
+
+int cluster_attn_knn_sample_bwd(int dt, int B, int N, int M, int C, int grid_side, int K, float p,
+                                const float* coords, const void* feats, const float* queries,
+                                const int32_t* table, const void* dout, void* dfeats, float* dq,
+                                float* dp, void* ws, size_t ws_bytes, void* hip_stream) {
+  if (dt != CA_F32 && dt != CA_BF16 && dt != CA_F16)
+    return fail(CA_ERR_UNSUPPORTED, "dtype %d is not one of CA_F32, CA_BF16, CA_F16", dt);
+  if (int s = check_knn_shape(B, N, M, C, grid_side, K)) return s;
+  if (!(p == p) || p == INFINITY || p == -INFINITY) return fail(CA_ERR_SHAPE, "p is not finite");
+  if (!dp) return fail(CA_ERR_NULL, "NULL dp pointer");
+  const bool some_q = B > 0 && M > 0, some_t = B > 0 && N > 0;
+  if ((some_q && (!queries || !table || !dout || !dq)) ||
+      (some_t && (!coords || !feats || !dfeats)))
+    return fail(CA_ERR_NULL, "NULL tensor pointer");
+  const size_t need = ca::knn_layout(nullptr, B, N, M, K).bytes;
+  if (need && !ws) return fail(CA_ERR_NULL, "NULL workspace (%zu bytes needed)", need);
+  if (ws_bytes < need) return fail(CA_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
+  const size_t es = elem_size(dt);
+  Range outs[] = {{dfeats, (size_t)B * N * C * es}, {dq, (size_t)B * M * 8}, {dp, 4}, {ws, need}};
+  Range ins[] = {{coords, (size_t)B * N * 8},
+                 {feats, (size_t)B * N * C * es},
+                 {queries, (size_t)B * M * 8},
+                 {table, (size_t)B * grid_side * grid_side * K * 4},
+                 {dout, (size_t)B * M * C * es}};
+  if (int s = check_alias(outs, 4, ins, 5)) return s;
+  return hip_status(ca::launch_knn_bwd(dt, B, N, M, C, grid_side, K, p, coords, feats, queries,
+                                       table, dout, dfeats, dq, dp, ws, (hipStream_t)hip_stream),
+                    "knn bwd launch");
 }
 
 }  // extern "C"

@@ -98,6 +98,38 @@ static inline BuildWorkspace build_layout(void* base, int64_t B, int64_t N) {
   return w;
 }
 
+// ---- workspace layout of the KNN sampler backward ---------------------------
+struct KnnWorkspace {
+  int32_t* cnt;     // [B, N]        entries per token
+  int32_t* off;     // [B, N + 1]    segment starts (per image, relative)
+  int32_t* cur;     // [B, N]        placement cursors
+  int32_t* slot;    // [B, M, K]     token of every (query, slot), -1 empty
+  float* wgt;       // [B, M, K]     its weight
+  int32_t* ent;     // [B, M * K]    entries (query * K + slot) by token
+  float* dpart;     // [B, M]        per-query share of dL/dp
+  size_t bytes;
+};
+
+static inline KnnWorkspace knn_layout(void* base, int64_t B, int64_t N, int64_t M, int64_t K) {
+  KnnWorkspace w;
+  size_t p = 0;
+  char* b = (char*)base;
+  auto take = [&](size_t n) {
+    size_t at = p;
+    p = align_up(p + n, 256);
+    return b ? (void*)(b + at) : (void*)nullptr;
+  };
+  w.cnt = (int32_t*)take((size_t)(B * N) * 4);
+  w.off = (int32_t*)take((size_t)(B * (N + 1)) * 4);
+  w.cur = (int32_t*)take((size_t)(B * N) * 4);
+  w.slot = (int32_t*)take((size_t)(B * M * K) * 4);
+  w.wgt = (float*)take((size_t)(B * M * K) * 4);
+  w.ent = (int32_t*)take((size_t)(B * M * K) * 4);
+  w.dpart = (float*)take((size_t)(B * M) * 4);
+  w.bytes = p;
+  return w;
+}
+
 // ---- wave helpers (64-lane wavefronts) ------------------------------------
 __device__ __forceinline__ float wave_max(float x) {
 #pragma unroll
@@ -141,6 +173,17 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* tmp, int nthread
   return tmp[w] + inc - v;
 }
 
+// 16-bit fixed-point coordinate of one axis: clamp(floor((c + 0.5) * step),
+// 0, 65535), step = 2^(16 - ceil(log2 G)) (shared by the neighbour build and
+// the KNN table).
+__device__ __forceinline__ uint32_t quantize_axis(float c, double step) {
+  // (c + 0.5) and the power-of-two step are exact in fp64, so this equals
+  // floor((c + 0.5) * step) of the real numbers.
+  double q = floor(((double)c + 0.5) * step);
+  q = q < 0.0 ? 0.0 : (q > 65535.0 ? 65535.0 : q);
+  return (uint32_t)q;
+}
+
 // ---- launchers (defined in the .hip files) ---------------------------------
 hipError_t launch_build_neighbors(const float* coords, int B, int N, int grid_side, int k,
                                   int32_t* perm, int32_t* nbr, int32_t* key_idx, void* ws,
@@ -172,5 +215,16 @@ hipError_t launch_bwd_mfma(int pass, int dt, int B, int N, int H, int nk, float 
                            const void* dout, const float* lse, const int32_t* q_idx,
                            const int32_t* key_idx, void* dq, void* dk, void* dv,
                            const BwdWorkspace& w, hipStream_t st);
+
+// KNN-cache point sampler (knn_sampler.hip)
+hipError_t launch_knn_table(const float* coords, int B, int N, int G, int K, int32_t* table,
+                            hipStream_t st);
+hipError_t launch_knn_fwd(int dt, int B, int N, int M, int Cf, int G, int K, float p,
+                          const float* coords, const void* feats, const float* queries,
+                          const int32_t* table, void* out, hipStream_t st);
+hipError_t launch_knn_bwd(int dt, int B, int N, int M, int Cf, int G, int K, float p,
+                          const float* coords, const void* feats, const float* queries,
+                          const int32_t* table, const void* dout, void* dfeat, float* dq,
+                          float* dp, void* ws, hipStream_t st);
 
 }  // namespace ca

@@ -58,13 +58,6 @@ __device__ __forceinline__ uint32_t compact16(uint32_t v) {
   return v;
 }
 
-__device__ __forceinline__ uint32_t quantize_axis(float c, double step) {
-  // (c + 0.5) and the power-of-two step are exact in fp64, so this equals
-  // floor((c + 0.5) * step) of the real numbers.
-  double q = floor(((double)c + 0.5) * step);
-  q = q < 0.0 ? 0.0 : (q > 65535.0 ? 65535.0 : q);
-  return (uint32_t)q;
-}
 
 // Rank the tokens of one segment.  grid = (ceil(L / 64), segments), where a
 // segment is [seg_start, seg_start + L) of image `b`.  Each workgroup ranks

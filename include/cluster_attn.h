@@ -154,6 +154,77 @@ int cluster_attn_bwd(int dt, int B, int N, int H, int D, int cs, int nk, float s
                      const int32_t* key_idx, void* dq, void* dk, void* dv, void* ws,
                      size_t ws_bytes, void* hip_stream);
 
+/* ------------------------------------------------------------------------
+ * KNN-cache point sampler of the point-wise decoder.
+ *
+ * Notes page, "Key Designs" item 2 (point-wise deformable cross-attention
+ * decoder: a query samples at q = r + offset and aggregates its nearest
+ * visible tokens with weights w_i = softmax_i(-p d_i), the stable
+ * replacement of inverse-power weights) and item 3 (KNN cache lookup: an
+ * H x W x K table holding, per grid cell, the K nearest visible tokens; a
+ * query is quantised to its nearest cell so that neighbour retrieval is a
+ * lookup plus a distance calculation, fused with the softmax weighting in
+ * the forward and the backward).  Readings: H = W = G, the token grid;
+ * cell (row i, column j) has its centre at (x, y) = (j, i); distances for
+ * the table are those of the 16-bit fixed-point coordinates of the neighbour
+ * build (ties to the lower token index); d_k of the weights is the Euclidean
+ * distance of the f32 coordinates.  Coordinates and queries are
+ * (x = column, y = row) in patch units, [B, N, 2] / [B, M, 2] f32.  Feature
+ * tensors are read and written in 16-byte pieces: their pointers must be
+ * 16-byte aligned (C is a multiple of 8).
+ * ------------------------------------------------------------------------ */
+
+/*
+ * Table: table[b, i, j, 0..K-1] = the K tokens of image b whose fixed-point
+ * coordinates (q = clamp(floor((c + 0.5) * 2^(16 - ceil(log2 G))), 0,
+ * 65535) per axis) are nearest to the cell centre ((j + 1/2) s, (i + 1/2) s),
+ * s = 2^(16 - ceil(log2 G)), by (squared distance, token index) ascending;
+ * -1 pads rows when N < K.  Exact integer arithmetic: the unique table.
+ *   coords  [B, N, 2] f32 device.   G: 1..64.   N: 0..4096.   K: 1..16.
+ *   table   [B, G, G, K] int32 device out.
+ */
+int cluster_attn_knn_table(const float* coords, int B, int N, int grid_side, int K,
+                           int32_t* table, void* hip_stream);
+
+/*
+ * Forward: for query m of image b at q = queries[b, m], the cell is
+ * (i, j) = (clamp(floor(q.y + 1/2), 0, G-1), clamp(floor(q.x + 1/2), 0, G-1))
+ * (fp64); over the valid slots t_k = table[b, i, j, k] >= 0,
+ *   d_k = |q - coords[b, t_k]|,  w = softmax(-p d) (fp32, max subtracted),
+ *   out[b, m, :] = sum_k w_k feats[b, t_k, :]   (fp32 accumulation, RNE to dt);
+ * a query whose row has no valid slot gets 0.
+ *   dt     element type of feats and out.   C: channels, multiple of 8, <= 1024.
+ *   p      finite real (one per level).     K: 1..16 (table's K).
+ *   feats  [B, N, C] dt.   table [B, G, G, K] int32 (any contents in [-1, N)).
+ *   out    [B, M, C] dt out.
+ */
+int cluster_attn_knn_sample_fwd(int dt, int B, int N, int M, int C, int grid_side, int K, float p,
+                                const float* coords, const void* feats, const float* queries,
+                                const int32_t* table, void* out, void* hip_stream);
+
+/* Workspace bytes needed by cluster_attn_knn_sample_bwd (0 for invalid sizes). */
+size_t cluster_attn_knn_sample_bwd_workspace(int B, int N, int M, int K);
+
+/*
+ * Backward of L = sum(dout * out) with the table held fixed: with
+ * g_k = <dout[b, m], feats[b, t_k]> and ds_k = w_k (g_k - sum_j w_j g_j),
+ *   dq[b, m]     = -p sum_k ds_k (q - x_k) / d_k   (terms with d_k = 0 are 0)
+ *   dp           = -sum over all queries and slots of ds_k d_k
+ *   dfeats[b, t] = sum over the (query, slot) pairs holding t of w_k dout[b, m]
+ * The token coordinates are constants.  dfeats is built token-major from a
+ * transposed slot list made in the workspace (entries ordered by query and
+ * slot) and written once, with no atomics on floating-point values: the
+ * result is bitwise reproducible.  fp32 accumulation; dfeats RNE to dt.
+ *   dout    [B, M, C] dt.   dfeats [B, N, C] dt out (tokens no query reaches
+ *           get 0).   dq [B, M, 2] f32 out.   dp: one f32 out (device).
+ *   ws      device workspace of cluster_attn_knn_sample_bwd_workspace bytes;
+ *           two calls that overlap in time must not share it.
+ */
+int cluster_attn_knn_sample_bwd(int dt, int B, int N, int M, int C, int grid_side, int K, float p,
+                                const float* coords, const void* feats, const float* queries,
+                                const int32_t* table, const void* dout, void* dfeats, float* dq,
+                                float* dp, void* ws, size_t ws_bytes, void* hip_stream);
+
 /* Static text for a status code. */
 const char* cluster_attn_status_string(int status);
 

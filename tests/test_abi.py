@@ -136,3 +136,44 @@ def test_product_path_does_not_import_oracle():
             if f.endswith((".py", ".hip", ".h", ".cpp")):
                 text = open(os.path.join(dirpath, f)).read()
                 assert "oracle" not in text.replace("no oracle", ""), f
+
+
+def knn_fwd(lib, dt=1, B=2, N=100, M=50, C=128, G=16, K=8, p=1.0, ptrs=None):
+    ps = ptrs or [P * (i + 1) for i in range(5)]
+    return lib.cluster_attn_knn_sample_fwd(dt, B, N, M, C, G, K, p, *ps, None)
+
+
+def test_knn_validation(lib):
+    # table build limits
+    t = lib.cluster_attn_knn_table
+    assert t(P, 2, 100, 65, 8, 2 * P, None) == CA_ERR_UNSUPPORTED     # G > 64
+    assert t(P, 2, 5000, 64, 8, 2 * P, None) == CA_ERR_UNSUPPORTED    # N > 4096
+    assert t(P, 2, 100, 64, 17, 2 * P, None) == CA_ERR_UNSUPPORTED    # K > 16
+    assert t(P, 2, 100, 0, 8, 2 * P, None) == CA_ERR_UNSUPPORTED
+    assert t(None, 2, 100, 64, 8, 2 * P, None) == CA_ERR_NULL
+    assert t(P, -1, 100, 64, 8, 2 * P, None) == CA_ERR_SHAPE
+    assert t(None, 0, 100, 64, 8, None, None) == CA_OK                # empty batch
+    assert t(P, 2, 100, 16, 8, P + 8, None) == CA_ERR_ALIAS           # table over coords
+    # sampler
+    assert knn_fwd(lib, dt=5) == CA_ERR_UNSUPPORTED
+    assert knn_fwd(lib, C=12) == CA_ERR_UNSUPPORTED
+    assert knn_fwd(lib, C=2048) == CA_ERR_UNSUPPORTED
+    assert knn_fwd(lib, K=0) == CA_ERR_UNSUPPORTED
+    assert knn_fwd(lib, G=0) == CA_ERR_SHAPE
+    assert knn_fwd(lib, M=-3) == CA_ERR_SHAPE
+    assert knn_fwd(lib, p=float("inf")) == CA_ERR_SHAPE
+    assert knn_fwd(lib, ptrs=[P, 2 * P, None, 4 * P, 5 * P]) == CA_ERR_NULL
+    assert knn_fwd(lib, M=0, ptrs=[None] * 5) == CA_OK
+    base = 1 << 30
+    fb = 2 * 100 * 128 * 2
+    ptrs = [base, base + 4096, base + 4096 + fb, base + 2 * fb, base + 4096 + 16]   # out over feats
+    assert knn_fwd(lib, ptrs=ptrs) == CA_ERR_ALIAS
+    # backward: workspace size and NULL dp
+    need = lib.cluster_attn_knn_sample_bwd_workspace(2, 100, 50, 8)
+    assert need > 2 * 50 * 8 * 12
+    assert lib.cluster_attn_knn_sample_bwd_workspace(2, 100, 50, 17) == 0
+    ten = [P * (i + 1) for i in range(7)]   # coords, feats, queries, table, dout, dfeats, dq
+    b = lib.cluster_attn_knn_sample_bwd
+    assert b(1, 2, 100, 50, 128, 16, 8, 1.0, *ten, None, P * 50, need, None) == CA_ERR_NULL
+    assert b(1, 2, 100, 50, 128, 16, 8, 1.0, *ten, P * 60, None, need, None) == CA_ERR_NULL
+    assert b(1, 2, 100, 50, 128, 16, 8, 1.0, *ten, P * 60, P * 50, need - 1, None) == CA_ERR_WORKSPACE
