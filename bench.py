@@ -37,6 +37,12 @@ ENTRY_KERNELS = {
     "bwd": ["plan_small_kernel (small images) | plan_init/inv/count/scan/place/sort_kernel",
             "bwd_q_lds_kernel", "bwd_kv_lds_kernel"],
 }
+SAMPLER_ENTRY_KERNELS = {
+    "table": ["knn_table_kernel"],
+    "fwd": ["knn_fwd_kernel"],
+    "bwd": ["knn_zero_kernel", "knn_bwd_query_kernel", "knn_scan_kernel", "knn_place_kernel",
+            "knn_sort_kernel", "knn_dfeat_kernel", "knn_dp_kernel"],
+}
 BF16_MFMA_PEAK_TFLOPS = 2500.0  # dense
 
 
@@ -144,9 +150,12 @@ def main():
     import torch
 
     import gathered_local_attention_amd as ca
-    from gen import make_case
+    from gen import SAMPLER_CONFIGS, make_case
 
     ca._lib.load()
+    if args.config in SAMPLER_CONFIGS:
+        bench_sampler(args, torch, ca)
+        return
     case = make_case(args.config)
     cfg = case["cfg"]
     scale = 1.0 / math.sqrt(cfg.D)
@@ -278,6 +287,167 @@ def main():
     }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(cfg, case, min(args.cpu_images, cfg.B))
+    print(json.dumps(line), flush=True)
+
+
+# ---------------------------------------------------------------------------
+# KNN-cache point sampler (decoder): --config knn_decoder
+# ---------------------------------------------------------------------------
+
+def sampler_algorithmic(cfg):
+    """Compulsory bytes per entry point, summed over the levels (every tensor
+    touched once; table rows re-read by several queries, workspace and the
+    token-major entry lists not counted)."""
+    es = 4 if cfg.dtype == "f32" else 2
+    B, M, G, K = cfg.B, cfg.M, cfg.G, cfg.K
+    tab = G * G * K * 4
+    out = {"table": 0, "fwd": 0, "bwd": 0}
+    for N, C in cfg.levels:
+        out["table"] += B * (N * 8 + tab)
+        out["fwd"] += B * (M * 8 + tab + N * 8 + N * C * es + M * C * es)
+        out["bwd"] += B * (M * 8 + tab + N * 8 + N * C * es + M * C * es + N * C * es + M * 8) + 4
+    return out
+
+
+def sampler_cpu_baseline(cfg, case, images: int):
+    """The fp64 oracle's sampler forward + backward on `images` images, all
+    levels, single-threaded (tables built beforehand, outside the timing)."""
+    from threadpoolctl import threadpool_limits
+
+    import oracle as O
+
+    tabs = [[O.knn_table(case["coords"][li][b], cfg.G, cfg.K) for b in range(images)]
+            for li in range(len(cfg.levels))]
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        for li in range(len(cfg.levels)):
+            F = case["feats"][li].double().numpy()
+            dO = case["dout"][li].double().numpy()
+            for b in range(images):
+                c, q = case["coords"][li][b], case["queries"][b]
+                O.knn_sample_fwd(c, F[b], q, tabs[li][b], cfg.p)
+                O.knn_sample_bwd(c, F[b], q, tabs[li][b], cfg.p, dO[b])
+        dt = time.perf_counter() - t0
+    return {
+        "value": images * cfg.M / dt,
+        "unit": "queries/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": f"{images} of {cfg.B} images ({images * cfg.M} queries x {len(cfg.levels)} "
+                  f"levels), fp64 forward+backward, tables excluded, {dt:.1f} s",
+    }
+
+
+def bench_sampler(args, torch, ca):
+    from gen import make_sampler_case
+
+    case = make_sampler_case(args.config)
+    cfg = case["cfg"]
+    dev = "cuda"
+    L = len(cfg.levels)
+    sets = []
+    for r in range(args.copies):
+        s = {"q": torch.from_numpy(case["queries"]).to(dev), "lv": []}
+        for li in range(L):
+            s["lv"].append({"coords": torch.from_numpy(case["coords"][li]).to(dev),
+                            "feats": case["feats"][li].to(dev), "dout": case["dout"][li].to(dev)})
+        sets.append(s)
+    wss = [torch.empty(max(1, ca.knn_bwd_workspace_bytes(cfg.B, N, cfg.M, cfg.K)),
+                       dtype=torch.uint8, device=dev) for N, _ in cfg.levels]
+
+    def step(s):
+        for li in range(L):
+            lv = s["lv"][li]
+            table = ca.knn_table(lv["coords"], cfg.G, cfg.K)
+            ca.knn_sample_fwd(lv["feats"], lv["coords"], s["q"], table, cfg.p)
+            ca.knn_sample_bwd(lv["feats"], lv["coords"], s["q"], table, cfg.p, lv["dout"],
+                              workspace=wss[li])
+
+    for i in range(args.warmup):
+        step(sets[i % len(sets)])
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(sets[i % len(sets)])
+    torch.cuda.synchronize()
+    ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
+
+    # per-entry-point durations (all levels of one step), HIP events on the
+    # launch stream around back-to-back calls
+    n_ev = min(args.steps, 100)
+    tables = [[ca.knn_table(s["lv"][li]["coords"], cfg.G, cfg.K) for li in range(L)] for s in sets]
+    calls = {
+        "table": lambda i: [ca.knn_table(sets[i]["lv"][li]["coords"], cfg.G, cfg.K)
+                            for li in range(L)],
+        "fwd": lambda i: [ca.knn_sample_fwd(sets[i]["lv"][li]["feats"], sets[i]["lv"][li]["coords"],
+                                            sets[i]["q"], tables[i][li], cfg.p) for li in range(L)],
+        "bwd": lambda i: [ca.knn_sample_bwd(sets[i]["lv"][li]["feats"], sets[i]["lv"][li]["coords"],
+                                            sets[i]["q"], tables[i][li], cfg.p,
+                                            sets[i]["lv"][li]["dout"], workspace=wss[li])
+                          for li in range(L)],
+    }
+    dur = {}
+    for name, call in calls.items():
+        call(0)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(n_ev):
+            call(i % len(sets))
+        e1.record()
+        torch.cuda.synchronize()
+        dur[name] = e0.elapsed_time(e1) / n_ev * 1e3
+    alg = sampler_algorithmic(cfg)
+    dom = max(("table", "fwd", "bwd"), key=lambda k: dur[k])
+    achieved = alg[dom] / (dur[dom] * 1e-6) / 1e9
+    fb_us = dur["fwd"] + dur["bwd"]
+    queries = cfg.B * cfg.M
+    line = {
+        "metric": "KNN-cache point sampler fwd+bwd queries/sec and % of HBM roofline "
+                  "(decoder, 4 levels)",
+        "value": queries / (ms_per_step * 1e-3),
+        "unit": "queries/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic",
+        "config": {
+            "workload": f"{cfg.name}: B={cfg.B} images x M={cfg.M} queries, G={cfg.G}, K={cfg.K}, "
+                        f"levels (N, C) = {list(cfg.levels)}, {cfg.dtype}; step = per level "
+                        "table build + forward + backward",
+            "B": cfg.B, "M": cfg.M, "G": cfg.G, "K": cfg.K, "p": cfg.p,
+            "levels": [list(x) for x in cfg.levels], "seed": cfg.seed,
+            "rotating_copies": args.copies,
+        },
+        "roofline": {
+            "bound": "hbm",
+            "kernel": {"table": "cluster_attn_knn_table", "fwd": "cluster_attn_knn_sample_fwd",
+                       "bwd": "cluster_attn_knn_sample_bwd"}[dom],
+            "entry_point_kernels": SAMPLER_ENTRY_KERNELS[dom],
+            "achieved": achieved,
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBPS,
+            "traffic": None,
+            "algorithmic_bytes": alg[dom],
+            "avg_us": dur[dom],
+        },
+        "fwd_bwd": {
+            "us": fb_us,
+            "queries_per_s": queries / (fb_us * 1e-6),
+            "effective_GBps": (alg["fwd"] + alg["bwd"]) / (fb_us * 1e-6) / 1e9,
+            "hbm_frac": (alg["fwd"] + alg["bwd"]) / (fb_us * 1e-6) / 1e9 / HBM_PEAK_GBPS,
+        },
+        "entry_us": dur,
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = sampler_cpu_baseline(cfg, case, min(12, cfg.B))
     print(json.dumps(line), flush=True)
 
 

@@ -99,10 +99,12 @@ static inline BuildWorkspace build_layout(void* base, int64_t B, int64_t N) {
 }
 
 // ---- workspace layout of the KNN sampler backward ---------------------------
+constexpr int kKnnPart = 256;   // entries per partition of the stable counting sort
+
 struct KnnWorkspace {
   int32_t* cnt;     // [B, N]        entries per token
   int32_t* off;     // [B, N + 1]    segment starts (per image, relative)
-  int32_t* cur;     // [B, N]        placement cursors
+  int32_t* pcnt;    // [B, P, N]     per partition of kKnnPart entries: counts, then prefixes
   int32_t* slot;    // [B, M, K]     token of every (query, slot), -1 empty
   float* wgt;       // [B, M, K]     its weight
   int32_t* ent;     // [B, M * K]    entries (query * K + slot) by token
@@ -121,7 +123,8 @@ static inline KnnWorkspace knn_layout(void* base, int64_t B, int64_t N, int64_t 
   };
   w.cnt = (int32_t*)take((size_t)(B * N) * 4);
   w.off = (int32_t*)take((size_t)(B * (N + 1)) * 4);
-  w.cur = (int32_t*)take((size_t)(B * N) * 4);
+  const int64_t P = (M * K + kKnnPart - 1) / kKnnPart;
+  w.pcnt = (int32_t*)take((size_t)(B * P * N) * 4);
   w.slot = (int32_t*)take((size_t)(B * M * K) * 4);
   w.wgt = (float*)take((size_t)(B * M * K) * 4);
   w.ent = (int32_t*)take((size_t)(B * M * K) * 4);

@@ -34,9 +34,11 @@
 //                         over the group, dq and the query's share of dp;
 //                         slots and weights kept for the feature gradient
 //                         and references counted per token.
-//   knn_scan/place/sort   token-major entry lists (entry = query * K + slot),
-//                         each token's segment ordered by entry, so that the
-//                         feature gradient is summed in a fixed order.
+//   knn_pcount/pprefix/scan/pplace  token-major entry lists (entry =
+//                         query * K + slot) by a stable counting sort over
+//                         partitions of the entries: each token's segment is
+//                         in entry order, so the feature gradient is summed
+//                         in a fixed order.
 //   knn_dfeat_kernel      a lane group per token: dF = sum over its entries
 //                         of w * dO (gathered rows), written once (0 for
 //                         tokens no query reaches).
@@ -50,7 +52,7 @@ namespace ca {
 namespace {
 
 constexpr int kKnnMaxK = 16;
-constexpr int kTabThreads = 1024;
+constexpr int kTabThreads = 256;
 constexpr int kTabMaxBuckets = 64 * 64;   // grid sides up to 64
 constexpr int kTabMaxTokens = 4096;
 constexpr int kKnnThreads = 256;          // 4 waves
@@ -62,9 +64,15 @@ __device__ __forceinline__ int ceil_log2(int v) {
 }
 
 // ---------------------------------------------------------------------------
-// Table build.  grid = (B, parts); the parts of an image split its cells and
-// each repeats the bucketing (cheap: at most 4096 tokens).
+// Table build.  grid = (B, parts): part y of an image takes kTabTiles tiles
+// of 8 x 8 cells (one wave each) and repeats the image's bucketing (cheap:
+// at most 4096 tokens).  Buckets are squares of 2^bs fixed-point units,
+// bs chosen so that an image holds about two tokens per bucket (at least a
+// cell, at most the whole range).
 // ---------------------------------------------------------------------------
+constexpr int kTabTiles = kTabThreads / 64;
+
+template <int KM>
 __global__ void __launch_bounds__(kTabThreads)
 knn_table_kernel(const float* __restrict__ coords, int N, int G, int K, int32_t* __restrict__ table) {
   __shared__ int start[kTabMaxBuckets];
@@ -72,11 +80,13 @@ knn_table_kernel(const float* __restrict__ coords, int N, int G, int K, int32_t*
   __shared__ int tmp[17];
   const int b = blockIdx.x;
   const int tid = threadIdx.x;
-  const int bits = ceil_log2(G);
-  const int shift = 16 - bits;             // fixed-point units per cell: s = 2^shift
-  const int P = 1 << bits;                 // bucket grid side (>= G)
-  const int nb = P * P;
+  const int shift = 16 - ceil_log2(G);     // fixed-point units per cell: s = 2^shift
   const double step = (double)(1 << shift);
+  int pb = 0;                              // bucket grid side 2^pb: about N / 2 buckets
+  while (pb < 16 - shift && (1 << (2 * pb + 2)) <= max(N, 1) / 2) ++pb;
+  const int bs = 16 - pb;                  // bucket side 2^bs units (>= one cell)
+  const int Pb = 1 << pb;
+  const int nb = Pb * Pb;
   const float2* xy = reinterpret_cast<const float2*>(coords) + (int64_t)b * N;
 
   for (int x = tid; x < nb; x += kTabThreads) start[x] = 0;
@@ -92,12 +102,12 @@ knn_table_kernel(const float* __restrict__ coords, int N, int G, int K, int32_t*
       const float2 c = xy[e];
       const uint32_t qx = quantize_axis(c.x, step), qy = quantize_axis(c.y, step);
       pk[r] = qx | (qy << 16);
-      bk[r] = (int)((qy >> shift) * (uint32_t)P + (qx >> shift));
+      bk[r] = (int)((qy >> bs) * (uint32_t)Pb + (qx >> bs));
       rk[r] = atomicAdd(&start[bk[r]], 1);
     }
   }
   __syncthreads();
-  // exclusive scan of the counts (up to 4 buckets per thread)
+  // exclusive scan of the counts
   constexpr int kBPer = kTabMaxBuckets / kTabThreads;
   int cnt[kBPer];
   int run = 0;
@@ -121,55 +131,80 @@ knn_table_kernel(const float* __restrict__ coords, int N, int G, int K, int32_t*
     if (bk[r] >= 0) tok[start[bk[r]] + rk[r]] = make_uint2(pk[r], (uint32_t)(tid + r * kTabThreads));
   __syncthreads();
 
-  const int cells = G * G;
-  const int per = (cells + gridDim.y - 1) / gridDim.y;
-  const int cbeg = blockIdx.y * per, cend = min(cells, cbeg + per);
-  for (int cell = cbeg + tid; cell < cend; cell += kTabThreads) {
-    const int i = cell / G, j = cell - (cell / G) * G;
-    const int64_t cx = (int64_t)(2 * j + 1) << (shift - 1);   // (j + 1/2) s
-    const int64_t cy = (int64_t)(2 * i + 1) << (shift - 1);
-    // keys (d2 << 12 | token): d2 < 2^33, tokens < 2^12
-    uint64_t best[kKnnMaxK];
+  // One wave per tile (lane = cell).  The wave scans a window of buckets
+  // around its tile that grows one ring at a time, every lane testing every
+  // token of the window (uniform loops: no divergence but the insertions).
+  // It stops once every lane's K-th best is strictly closer than any token
+  // outside the window can be: a token beyond the window's top edge at
+  // fixed-point row R0 * 2^bs has Y <= R0 * 2^bs - 1, so |Y - cy| >=
+  // cy - R0 * 2^bs + 1; likewise on the other three sides.
+  const int lane = tid & 63;
+  const int tiles_side = (G + 7) >> 3;
+  const int tile = blockIdx.y * kTabTiles + (tid >> 6);
+  if (tile >= tiles_side * tiles_side) return;
+  const int i0 = (tile / tiles_side) * 8, j0 = (tile % tiles_side) * 8;
+  const int i = i0 + (lane >> 3), j = j0 + (lane & 7);
+  const bool valid = i < G && j < G;
+  const int64_t cx = (int64_t)(2 * j + 1) << (shift - 1);   // (j + 1/2) s
+  const int64_t cy = (int64_t)(2 * i + 1) << (shift - 1);
+  // the tile's own buckets (cells up to min(G, i0 + 8) - 1)
+  const int ilast = min(G, i0 + 8) - 1, jlast = min(G, j0 + 8) - 1;
+  const int tr0 = (i0 << shift) >> bs, tr1 = (((ilast + 1) << shift) - 1) >> bs;
+  const int tc0 = (j0 << shift) >> bs, tc1 = (((jlast + 1) << shift) - 1) >> bs;
+  // keys (d2 << 12 | token): d2 < 2^33, tokens < 2^12
+  uint64_t best[KM];
 #pragma unroll
-    for (int r = 0; r < kKnnMaxK; ++r) best[r] = ~0ull;
-    uint64_t worst = ~0ull;   // best[K - 1], kept apart (K is a runtime value)
-    for (int R = 0; R < P; ++R) {
-      const int y0 = i - R, y1 = i + R;
-      for (int by = max(y0, 0); by <= min(y1, P - 1); ++by) {
-        const bool edge = by == y0 || by == y1;
-        const int dxs = (edge || R == 0) ? 1 : 2 * R;   // inner rows: the two end buckets
-        for (int bx = j - R; bx <= j + R; bx += dxs) {
-          if (bx < 0 || bx >= P) continue;
-          const int bb = by * P + bx;
-          const int t0 = start[bb], t1 = bb + 1 < nb ? start[bb + 1] : total;
-          for (int t = t0; t < t1; ++t) {
-            const uint2 e = tok[t];
-            const int64_t dx = (int64_t)(e.x & 0xFFFFu) - cx, dy = (int64_t)(e.x >> 16) - cy;
-            uint64_t x = ((uint64_t)(dx * dx + dy * dy) << 12) | e.y;
-            if (x >= worst) continue;
+  for (int r = 0; r < KM; ++r) best[r] = ~0ull;
+  uint64_t worst = ~0ull;   // best[K - 1]
+  auto scan_bucket = [&](int by, int bx) {
+    const int bb = by * Pb + bx;
+    const int t0 = start[bb], t1 = bb + 1 < nb ? start[bb + 1] : total;
+    for (int t = t0; t < t1; ++t) {
+      const uint2 e = tok[t];
+      const int64_t dx = (int64_t)(e.x & 0xFFFFu) - cx, dy = (int64_t)(e.x >> 16) - cy;
+      uint64_t x = ((uint64_t)(dx * dx + dy * dy) << 12) | e.y;
+      if (x >= worst) continue;
 #pragma unroll
-            for (int r = 0; r < kKnnMaxK; ++r) {
-              if (r < K) {
-                const uint64_t lo = x < best[r] ? x : best[r];
-                const uint64_t hi = x < best[r] ? best[r] : x;
-                best[r] = lo;
-                x = hi;
-              }
-              if (r == K - 1) worst = best[r];
-            }
-          }
+      for (int r = 0; r < KM; ++r) {
+        if (r < K) {
+          const uint64_t lo = x < best[r] ? x : best[r];
+          const uint64_t hi = x < best[r] ? best[r] : x;
+          best[r] = lo;
+          x = hi;
         }
+        if (r == K - 1) worst = best[r];
       }
-      // every bucket of ring R + 1 lies at least (R + 1/2) s from the centre
-      // along one axis: stop once the K-th best is strictly closer
-      const int64_t lb = (int64_t)(2 * R + 1) << (shift - 1);
-      if (worst != ~0ull && (int64_t)(worst >> 12) < lb * lb) break;
     }
-    int32_t* row = table + ((int64_t)b * cells + cell) * K;
-#pragma unroll
-    for (int r = 0; r < kKnnMaxK; ++r)
-      if (r < K) row[r] = best[r] == ~0ull ? -1 : (int32_t)(best[r] & 0xFFFu);
+  };
+  for (int m = 0;; ++m) {
+    const int r0 = tr0 - m, r1 = tr1 + m, c0 = tc0 - m, c1 = tc1 + m;   // window (buckets)
+    if (m == 0) {
+      for (int by = r0; by <= r1; ++by)
+        for (int bx = c0; bx <= c1; ++bx) scan_bucket(by, bx);
+    } else {
+      for (int bx = max(c0, 0); bx <= min(c1, Pb - 1); ++bx) {
+        if (r0 >= 0) scan_bucket(r0, bx);
+        if (r1 <= Pb - 1) scan_bucket(r1, bx);
+      }
+      for (int by = max(r0 + 1, 0); by <= min(r1 - 1, Pb - 1); ++by) {
+        if (c0 >= 0) scan_bucket(by, c0);
+        if (c1 <= Pb - 1) scan_bucket(by, c1);
+      }
+    }
+    if (r0 <= 0 && c0 <= 0 && r1 >= Pb - 1 && c1 >= Pb - 1) break;   // every bucket seen
+    int64_t lb = INT64_MAX;
+    if (r0 > 0) lb = min(lb, cy - ((int64_t)r0 << bs) + 1);
+    if (r1 < Pb - 1) lb = min(lb, ((int64_t)(r1 + 1) << bs) - cy);
+    if (c0 > 0) lb = min(lb, cx - ((int64_t)c0 << bs) + 1);
+    if (c1 < Pb - 1) lb = min(lb, ((int64_t)(c1 + 1) << bs) - cx);
+    const bool done = !valid || (worst != ~0ull && (int64_t)(worst >> 12) < lb * lb);
+    if (__all(done)) break;
   }
+  if (!valid) return;
+  int32_t* row = table + (((int64_t)b * G + i) * G + j) * K;
+#pragma unroll
+  for (int r = 0; r < KM; ++r)
+    if (r < K) row[r] = best[r] == ~0ull ? -1 : (int32_t)(best[r] & 0xFFFu);
 }
 
 // ---------------------------------------------------------------------------
@@ -330,8 +365,7 @@ knn_bwd_query_kernel(int N, int M, int Cf, int G, int K, int lg, float p, int64_
                      const float* __restrict__ coords, const T* __restrict__ feats,
                      const float* __restrict__ queries, const int32_t* __restrict__ table,
                      const T* __restrict__ dout, float* __restrict__ dq, float* __restrict__ dpart,
-                     int32_t* __restrict__ ent_slot, float* __restrict__ ent_w,
-                     int32_t* __restrict__ cnt) {
+                     int32_t* __restrict__ ent_slot, float* __restrict__ ent_w) {
   using Ck = Chunk<T>;
   const Group g = group_of(lg, total);
   const int L = 1 << lg;
@@ -384,13 +418,11 @@ knn_bwd_query_kernel(int N, int M, int Cf, int G, int K, int lg, float p, int64_
   }
   reinterpret_cast<float2*>(dq)[id] = make_float2(dqx, dqy);
   dpart[id] = dps;
-  int32_t* cimg = cnt + b * N;
 #pragma unroll
   for (int k = 0; k < KM; ++k) {
     if (k >= K) break;
     ent_slot[id * K + k] = qw.slot[k];
     ent_w[id * K + k] = qw.w[k];
-    if (qw.slot[k] >= 0) atomicAdd(&cimg[qw.slot[k]], 1);
   }
 }
 
@@ -405,14 +437,12 @@ knn_zero_kernel(int64_t n, int32_t* __restrict__ x) {
 constexpr int kScanThreads = 1024;
 constexpr int kScanChunk = 8192;
 __global__ void __launch_bounds__(kScanThreads)
-knn_scan_kernel(int N, const int32_t* __restrict__ cnt_all, int32_t* __restrict__ off_all,
-                int32_t* __restrict__ cur_all) {
+knn_scan_kernel(int N, const int32_t* __restrict__ cnt_all, int32_t* __restrict__ off_all) {
   __shared__ int32_t v[kScanChunk];
   __shared__ int tmp[17];
   const int64_t b = blockIdx.x;
   const int32_t* cnt = cnt_all + b * N;
   int32_t* off = off_all + b * (N + 1);
-  int32_t* cur = cur_all + b * N;
   constexpr int kPer = kScanChunk / kScanThreads;
   int carry = 0;
   for (int c0 = 0; c0 < N; c0 += kScanChunk) {
@@ -434,95 +464,95 @@ knn_scan_kernel(int N, const int32_t* __restrict__ cnt_all, int32_t* __restrict_
       }
     }
     __syncthreads();
-    for (int x = threadIdx.x; x < n; x += kScanThreads) {
-      off[c0 + x] = v[x];
-      cur[c0 + x] = v[x];
-    }
+    for (int x = threadIdx.x; x < n; x += kScanThreads) off[c0 + x] = v[x];
     carry += tot;
     __syncthreads();
   }
   if (threadIdx.x == 0) off[N] = carry;
 }
 
-// one thread per (query, slot): the entry into its token's segment
+// Token-major entry lists, in entry order (entry = query * K + slot), by a
+// stable counting sort.  The entries of an image are cut into partitions of
+// kPart consecutive entries: (1) per partition and token, the count of its
+// entries (integer atomics: the counts do not depend on their order);
+// (2) per token, the counts turned into exclusive prefixes over the
+// partitions, and the token's total; (3) the totals scanned into segment
+// starts (knn_scan_kernel); (4) per partition, one wave places every entry
+// at segment start + the partition's prefix + the number of earlier entries
+// of the same token in the partition.
+constexpr int kPart = kKnnPart;
+
 __global__ void __launch_bounds__(kKnnThreads)
-knn_place_kernel(int N, int M, int K, int64_t n_ent, const int32_t* __restrict__ ent_slot,
-                 int32_t* __restrict__ cur_all, int32_t* __restrict__ ent_all) {
+knn_pcount_kernel(int N, int64_t MK, int P, int64_t n_ent, const int32_t* __restrict__ ent_slot,
+                  int32_t* __restrict__ pcnt) {
   const int64_t x = (int64_t)blockIdx.x * kKnnThreads + threadIdx.x;
   if (x >= n_ent) return;
-  const int s = ent_slot[x];
-  if (s < 0) return;
-  const int64_t per = (int64_t)M * K;
-  const int64_t b = x / per;
-  const int pos = atomicAdd(&cur_all[b * N + s], 1);
-  ent_all[b * per + pos] = (int32_t)(x - b * per);
+  const int t = ent_slot[x];
+  if (t < 0) return;
+  const int64_t b = x / MK;
+  const int s = (int)((x - b * MK) / kPart);
+  atomicAdd(&pcnt[(b * P + s) * N + t], 1);
 }
 
-// One thread per token sorts its segment by entry.  Short segments are
-// sorted by their thread in LDS; longer ones afterwards by the whole wave,
-// each lane ranking its entries by counting.
-constexpr int kSortShort = 32;
 __global__ void __launch_bounds__(kKnnThreads)
-knn_sort_kernel(int N, int M, int K, int64_t n_tok, const int32_t* __restrict__ off_all,
-                int32_t* __restrict__ ent_all) {
-  __shared__ int32_t buf[kKnnThreads / 64][64 * kSortShort];
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+knn_pprefix_kernel(int N, int P, int64_t n_tok, int32_t* __restrict__ pcnt, int32_t* __restrict__ cnt) {
   const int64_t x = (int64_t)blockIdx.x * kKnnThreads + threadIdx.x;
-  const bool valid = x < n_tok;
-  const int64_t b = valid ? x / N : 0;
-  const int t = valid ? (int)(x - b * N) : 0;
-  const int64_t per = (int64_t)M * K;
-  int32_t* ent = ent_all + b * per;
-  const int a = valid ? off_all[b * (N + 1) + t] : 0;
-  const int z = valid ? off_all[b * (N + 1) + t + 1] : 0;
-  const int n = z - a;
-  int32_t* mine = &buf[w][lane * kSortShort];
-  if (n <= kSortShort) {
-    for (int u = 0; u < n; ++u) {
-      const int32_t key = ent[a + u];
-      int y = u - 1;
-      while (y >= 0 && mine[y] > key) {
-        mine[y + 1] = mine[y];
-        --y;
-      }
-      mine[y + 1] = key;
-    }
-    for (int u = 0; u < n; ++u) ent[a + u] = mine[u];
+  if (x >= n_tok) return;
+  const int64_t b = x / N;
+  const int t = (int)(x - b * N);
+  int acc = 0;
+  for (int s = 0; s < P; ++s) {
+    int32_t* c = &pcnt[(b * P + s) * N + t];
+    const int v = *c;
+    *c = acc;
+    acc += v;
   }
-  // long segments: the wave ranks them one after the other
-  uint64_t longs = __ballot(n > kSortShort);
-  int32_t* wbuf = &buf[w][0];
-  while (longs) {
-    const int src = __builtin_ctzll(longs);
-    longs &= longs - 1;
-    const int la = __shfl(a, src, 64), ln = __shfl(n, src, 64);
-    const int64_t lb = __shfl((int)b, src, 64);
-    int32_t* le = ent_all + lb * per + la;
-    if (ln <= 64 * kSortShort) {
-      __builtin_amdgcn_s_waitcnt(0);   // earlier LDS traffic of the wave is done
-      for (int u = lane; u < ln; u += 64) wbuf[u] = le[u];
-      __builtin_amdgcn_s_waitcnt(0);
-      __builtin_amdgcn_wave_barrier();
-      for (int u = lane; u < ln; u += 64) {   // ranks from the LDS copy, distinct entries
-        const int32_t key = wbuf[u];
-        int r = 0;
-        for (int y = 0; y < ln; ++y) r += wbuf[y] < key;
-        le[r] = key;
-      }
-      __builtin_amdgcn_s_waitcnt(0);
-      __builtin_amdgcn_wave_barrier();
-    } else if (lane == 0) {   // very long: one lane, in place
-      for (int u = 1; u < ln; ++u) {
-        const int32_t key = le[u];
-        int y = u - 1;
-        while (y >= 0 && le[y] > key) {
-          le[y + 1] = le[y];
-          --y;
-        }
-        le[y + 1] = key;
-      }
+  cnt[x] = acc;
+}
+
+// one wave per partition (four partitions per workgroup)
+__global__ void __launch_bounds__(kKnnThreads)
+knn_pplace_kernel(int N, int64_t MK, int P, int64_t n_part, const int32_t* __restrict__ ent_slot,
+                  const int32_t* __restrict__ off_all, const int32_t* __restrict__ pcnt,
+                  int32_t* __restrict__ ent_all) {
+  __shared__ __align__(16) int32_t tok[kKnnThreads / 64][kPart];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int64_t part = (int64_t)blockIdx.x * (kKnnThreads / 64) + w;
+  if (part >= n_part) return;
+  const int64_t b = part / P;
+  const int s = (int)(part - b * P);
+  const int64_t e0 = (int64_t)s * kPart;
+  const int n = (int)min((int64_t)kPart, MK - e0);
+  const int32_t* sl = ent_slot + b * MK + e0;
+  constexpr int R = kPart / 64;
+  int t[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int u = lane + 64 * r;
+    t[r] = u < n ? sl[u] : -1;
+    tok[w][u] = t[r];
+  }
+  __builtin_amdgcn_wave_barrier();   // the wave's LDS writes precede its reads (in order)
+  int rank[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) rank[r] = 0;
+  const int4* t4 = reinterpret_cast<const int4*>(tok[w]);
+  for (int y4 = 0; y4 < kPart / 4; ++y4) {
+    const int4 v = t4[y4];
+    const int ys[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      const int y = 4 * y4 + h;
+#pragma unroll
+      for (int r = 0; r < R; ++r) rank[r] += (ys[h] == t[r] && y < lane + 64 * r) ? 1 : 0;
     }
   }
+  const int32_t* off = off_all + b * (N + 1);
+  const int32_t* pc = pcnt + (b * P + s) * N;
+  int32_t* ent = ent_all + b * MK;
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+    if (t[r] >= 0) ent[off[t[r]] + pc[t[r]] + rank[r]] = (int32_t)(e0 + lane + 64 * r);
 }
 
 // ---------------------------------------------------------------------------
@@ -582,9 +612,13 @@ knn_dfeat_kernel(int N, int M, int Cf, int K, int lg, int64_t total, const T* __
 __global__ void __launch_bounds__(1024)
 knn_dp_kernel(int64_t n, const float* __restrict__ dpart, float* __restrict__ dp) {
   __shared__ float red[1024];
-  float s = 0.f;
-  for (int64_t i = threadIdx.x; i < n; i += 1024) s += dpart[i];
-  red[threadIdx.x] = s;
+  float a[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};   // eight loads in flight
+  int64_t i = threadIdx.x;
+  for (; i + 7 * 1024 < n; i += 8 * 1024)
+#pragma unroll
+    for (int u = 0; u < 8; ++u) a[u] += dpart[i + u * 1024];
+  for (; i < n; i += 1024) a[0] += dpart[i];
+  red[threadIdx.x] = ((a[0] + a[1]) + (a[2] + a[3])) + ((a[4] + a[5]) + (a[6] + a[7]));
   __syncthreads();
   for (int o = 512; o >= 1; o >>= 1) {
     if ((int)threadIdx.x < o) red[threadIdx.x] += red[threadIdx.x + o];
@@ -629,26 +663,34 @@ hipError_t bwd_t(int B, int N, int M, int Cf, int G, int K, float p, const float
   const int lg = group_log2(Cf, Chunk<T>::E);
   const int64_t nq = (int64_t)B * M, ntok = (int64_t)B * N, nent = nq * K;
   auto grid1 = [](int64_t n) { return dim3((unsigned)((n + kKnnThreads - 1) / kKnnThreads)); };
-  // empty sizes launch nothing but the dp reduction (which then writes 0)
-  if (ntok > 0) hipLaunchKernelGGL(knn_zero_kernel, grid1(ntok), dim3(kKnnThreads), 0, st, ntok, w.cnt);
+  const int64_t MK = (int64_t)M * K;
+  const int P = (int)((MK + kPart - 1) / kPart);
+  const int64_t npc = (int64_t)B * P * N, nparts = (int64_t)B * P;
   auto go = [&](auto kern) {
     hipLaunchKernelGGL(kern, dim3(waves_grid(nq, lg)), dim3(kKnnThreads), 0, st, N, M, Cf, G, K,
                        lg, p, nq, coords, (const T*)feats, queries, table, (const T*)dout, dq,
-                       w.dpart, w.slot, w.wgt, w.cnt);
+                       w.dpart, w.slot, w.wgt);
   };
+  // empty sizes launch nothing but what writes outputs (dF, dp)
   if (nq > 0) {
     if (K <= 4) go(knn_bwd_query_kernel<T, 4>);
     else if (K <= 8) go(knn_bwd_query_kernel<T, 8>);
     else go(knn_bwd_query_kernel<T, 16>);
   }
   if (ntok > 0) {
+    if (npc > 0) {
+      hipLaunchKernelGGL(knn_zero_kernel, grid1(npc), dim3(kKnnThreads), 0, st, npc, w.pcnt);
+      hipLaunchKernelGGL(knn_pcount_kernel, grid1(nent), dim3(kKnnThreads), 0, st, N, MK, P, nent,
+                         (const int32_t*)w.slot, w.pcnt);
+    }
+    hipLaunchKernelGGL(knn_pprefix_kernel, grid1(ntok), dim3(kKnnThreads), 0, st, N, P, ntok,
+                       w.pcnt, w.cnt);
     hipLaunchKernelGGL(knn_scan_kernel, dim3(B), dim3(kScanThreads), 0, st, N,
-                       (const int32_t*)w.cnt, w.off, w.cur);
-    if (nq > 0)
-      hipLaunchKernelGGL(knn_place_kernel, grid1(nent), dim3(kKnnThreads), 0, st, N, M, K, nent,
-                         (const int32_t*)w.slot, w.cur, w.ent);
-    hipLaunchKernelGGL(knn_sort_kernel, grid1(ntok), dim3(kKnnThreads), 0, st, N, M, K, ntok,
-                       (const int32_t*)w.off, w.ent);
+                       (const int32_t*)w.cnt, w.off);
+    if (nparts > 0)
+      hipLaunchKernelGGL(knn_pplace_kernel, dim3((unsigned)((nparts + 3) / 4)), dim3(kKnnThreads), 0,
+                         st, N, MK, P, nparts, (const int32_t*)w.slot, (const int32_t*)w.off,
+                         (const int32_t*)w.pcnt, w.ent);
     hipLaunchKernelGGL(knn_dfeat_kernel<T>, dim3(waves_grid(ntok, lg)), dim3(kKnnThreads), 0, st,
                        N, M, Cf, K, lg, ntok, (const T*)dout, (const int32_t*)w.off,
                        (const int32_t*)w.ent, (const float*)w.wgt, (T*)dfeat);
@@ -661,9 +703,14 @@ hipError_t bwd_t(int B, int N, int M, int Cf, int G, int K, float p, const float
 
 hipError_t launch_knn_table(const float* coords, int B, int N, int G, int K, int32_t* table,
                             hipStream_t st) {
-  const int parts = std::max(1, std::min(8, (G * G + kTabThreads - 1) / kTabThreads));
-  hipLaunchKernelGGL(knn_table_kernel, dim3(B, parts), dim3(kTabThreads), 0, st, coords, N, G, K,
-                     table);
+  const int tiles_side = (G + 7) / 8;
+  const int parts = (tiles_side * tiles_side + kTabTiles - 1) / kTabTiles;
+  auto go = [&](auto kern) {
+    hipLaunchKernelGGL(kern, dim3(B, parts), dim3(kTabThreads), 0, st, coords, N, G, K, table);
+  };
+  if (K <= 4) go(knn_table_kernel<4>);
+  else if (K <= 8) go(knn_table_kernel<8>);
+  else go(knn_table_kernel<16>);
   return hipGetLastError();
 }
 
