@@ -102,12 +102,6 @@ __device__ __forceinline__ void stv(void* base, uint32_t off, V v) {
   *reinterpret_cast<V*>(reinterpret_cast<char*>(base) + off) = v;
 }
 
-__device__ __forceinline__ int xcd_remap(int w, int n) {
-  // dispatch sends workgroup w to XCD w % 8; give XCD x a contiguous range
-  const int x = w & 7, i = w >> 3;
-  const int q = n >> 3, r = n & 7;
-  return x * q + min(x, r) + i;
-}
 
 // Reductions over the four 16-lane rows (lanes c, c+16, c+32, c+48) with the
 // gfx950 row-swap moves: permlane16_swap(x, x) yields x of rows {0,0,2,2} and

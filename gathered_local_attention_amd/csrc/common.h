@@ -176,6 +176,15 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* tmp, int nthread
   return tmp[w] + inc - v;
 }
 
+// Workgroup w of n is dispatched to XCD w % 8; this numbering gives XCD x a
+// contiguous range of n/8 workgroups (their data then shares that XCD's L2).
+__device__ __forceinline__ int xcd_remap(int w, int n) {
+  // dispatch sends workgroup w to XCD w % 8; give XCD x a contiguous range
+  const int x = w & 7, i = w >> 3;
+  const int q = n >> 3, r = n & 7;
+  return x * q + min(x, r) + i;
+}
+
 // 16-bit fixed-point coordinate of one axis: clamp(floor((c + 0.5) * step),
 // 0, 65535), step = 2^(16 - ceil(log2 G)) (shared by the neighbour build and
 // the KNN table).

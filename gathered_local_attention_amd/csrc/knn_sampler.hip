@@ -316,99 +316,183 @@ __device__ __forceinline__ Group group_of(int lg, int64_t total) {
 }
 
 // ---------------------------------------------------------------------------
-// Forward.  out[b, m] = sum_k w_k F[b, slot_k].
+// Forward.  out[b, m] = sum_k w_k F[b, slot_k].  A wave serves qwv
+// consecutive queries (eight passes of its lane groups): first one lane per
+// query works out the slots and weights (the dependent chain query -> table
+// row -> token coordinates is paid once per wave) and leaves them in LDS;
+// then lane groups of L lanes (16 bytes of the row each) gather and sum the
+// rows, 64 / L queries at a time.
 // ---------------------------------------------------------------------------
+template <int KM>
+struct WaveSlots {
+  int slot[64][KM];
+  float w[64][KM];
+};
+
+template <int KM>
+__device__ __forceinline__ void wave_slots(int64_t base, int64_t total, int qwv, int N, int M, int G, int K,
+                                           float p, const float* __restrict__ coords,
+                                           const float* __restrict__ queries,
+                                           const int32_t* __restrict__ table, WaveSlots<KM>& ws,
+                                           QueryWeights<KM>& qw) {
+  const int lane = threadIdx.x & 63;
+  const int64_t id = base + lane;
+#pragma unroll
+  for (int k = 0; k < KM; ++k) {
+    qw.slot[k] = -1;
+    qw.w[k] = 0.f;
+    qw.d[k] = 0.f;
+    qw.diff[k] = make_float2(0.f, 0.f);
+  }
+  if (lane < qwv && id < total) {
+    const int64_t b = id / M;
+    const float2 q = reinterpret_cast<const float2*>(queries)[id];
+    query_weights(q, (int)b, G, K, N, p, reinterpret_cast<const float2*>(coords) + b * N, table, qw);
+  }
+#pragma unroll
+  for (int k = 0; k < KM; ++k) {
+    ws.slot[lane][k] = qw.slot[k];
+    ws.w[lane][k] = qw.w[k];
+  }
+  __builtin_amdgcn_wave_barrier();   // one wave: its LDS writes precede its reads
+}
+
 template <typename T, int KM>
 __global__ void __launch_bounds__(kKnnThreads)
-knn_fwd_kernel(int N, int M, int Cf, int G, int K, int lg, float p, int64_t total,
+knn_fwd_kernel(int N, int M, int Cf, int G, int K, int lg, float p, int64_t total, int qwv,
                const float* __restrict__ coords, const T* __restrict__ feats,
                const float* __restrict__ queries, const int32_t* __restrict__ table,
                T* __restrict__ out) {
   using Ck = Chunk<T>;
-  const Group g = group_of(lg, total);
-  if (!g.valid) return;
-  const int L = 1 << lg;
-  const int64_t b = g.id / M;
-  const float2 q = reinterpret_cast<const float2*>(queries)[g.id];
-  const float2* xy = reinterpret_cast<const float2*>(coords) + b * N;
+  __shared__ WaveSlots<KM> sw[kKnnThreads / 64];
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int64_t base = ((int64_t)xcd_remap(blockIdx.x, gridDim.x) * (kKnnThreads / 64) + wv) * qwv;
+  if (base >= total) return;
   QueryWeights<KM> qw;
-  query_weights(q, (int)b, G, K, N, p, xy, table, qw);
+  wave_slots<KM>(base, total, qwv, N, M, G, K, p, coords, queries, table, sw[wv], qw);
+  const int L = 1 << lg;
+  const int grp = lane >> lg, sub = lane & (L - 1);
   const int nch = Cf / Ck::E;
-  const T* fimg = feats + b * N * Cf;
+#pragma unroll 2
+  for (int u0 = 0; u0 < qwv; u0 += 64 >> lg) {
+    const int u = u0 + grp;
+    const int64_t id = base + u;
+    if (id >= total) break;
+    const int64_t b = id / M;
+    const T* fimg = feats + b * N * Cf;
+    int sl[KM];
+    float wt[KM];
 #pragma unroll
-  for (int r = 0; r < kMaxChunksPerLane; ++r) {
-    const int c = g.sub + r * L;
-    if (c >= nch) break;
-    float acc[Ck::E];
+    for (int k = 0; k < KM; ++k) {
+      sl[k] = sw[wv].slot[u][k];
+      wt[k] = sw[wv].w[u][k];
+    }
 #pragma unroll
-    for (int e = 0; e < Ck::E; ++e) acc[e] = 0.f;
-    // all K rows in flight before the sums
-    float v[KM][Ck::E];
+    for (int r = 0; r < kMaxChunksPerLane; ++r) {
+      const int c = sub + r * L;
+      if (c >= nch) break;
+      float v[KM][Ck::E];
 #pragma unroll
-    for (int k = 0; k < KM; ++k)
-      if (qw.slot[k] >= 0) Ck::load(fimg + (int64_t)qw.slot[k] * Cf + c * Ck::E, v[k]);
+      for (int k = 0; k < KM; ++k)
+        if (sl[k] >= 0) Ck::load(fimg + (int64_t)sl[k] * Cf + c * Ck::E, v[k]);
+      float acc[Ck::E];
 #pragma unroll
-    for (int k = 0; k < KM; ++k)
-      if (qw.slot[k] >= 0)
+      for (int e = 0; e < Ck::E; ++e) acc[e] = 0.f;
 #pragma unroll
-        for (int e = 0; e < Ck::E; ++e) acc[e] = fmaf(qw.w[k], v[k][e], acc[e]);
-    Ck::store(out + g.id * Cf + c * Ck::E, acc);
+      for (int k = 0; k < KM; ++k)
+        if (sl[k] >= 0)
+#pragma unroll
+          for (int e = 0; e < Ck::E; ++e) acc[e] = fmaf(wt[k], v[k][e], acc[e]);
+      Ck::store(out + id * Cf + c * Ck::E, acc);
+    }
   }
 }
 
 // ---------------------------------------------------------------------------
-// Backward, query-major part.
+// Backward, query-major part.  Same wave layout as the forward: (1) lane =
+// query: slots and weights (kept in registers, in LDS for the groups, and
+// in the workspace for the feature gradient); (2) lane groups: <dO, F_k>
+// reduced over the group, into LDS; (3) lane = query again: dq and the
+// query's share of dp.
 // ---------------------------------------------------------------------------
 template <typename T, int KM>
 __global__ void __launch_bounds__(kKnnThreads)
-knn_bwd_query_kernel(int N, int M, int Cf, int G, int K, int lg, float p, int64_t total,
+knn_bwd_query_kernel(int N, int M, int Cf, int G, int K, int lg, float p, int64_t total, int qwv,
                      const float* __restrict__ coords, const T* __restrict__ feats,
                      const float* __restrict__ queries, const int32_t* __restrict__ table,
                      const T* __restrict__ dout, float* __restrict__ dq, float* __restrict__ dpart,
                      int32_t* __restrict__ ent_slot, float* __restrict__ ent_w) {
   using Ck = Chunk<T>;
-  const Group g = group_of(lg, total);
-  const int L = 1 << lg;
-  const int64_t id = g.valid ? g.id : 0;   // idle lanes mirror query 0 (shuffles need them)
-  const int64_t b = id / M;
-  const float2 q = reinterpret_cast<const float2*>(queries)[id];
-  const float2* xy = reinterpret_cast<const float2*>(coords) + b * N;
+  __shared__ WaveSlots<KM> sw[kKnnThreads / 64];
+  __shared__ float sg[kKnnThreads / 64][64][KM];
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int64_t base = ((int64_t)xcd_remap(blockIdx.x, gridDim.x) * (kKnnThreads / 64) + wv) * qwv;
+  if (base >= total) return;
   QueryWeights<KM> qw;
-  query_weights(q, (int)b, G, K, N, p, xy, table, qw);
-  const int nch = Cf / Ck::E;
-  const T* fimg = feats + b * N * Cf;
-  float gk[KM];
+  wave_slots<KM>(base, total, qwv, N, M, G, K, p, coords, queries, table, sw[wv], qw);
+  {
+    const int64_t id = base + lane;
+    if (lane < qwv && id < total) {
 #pragma unroll
-  for (int k = 0; k < KM; ++k) gk[k] = 0.f;
-#pragma unroll
-  for (int r = 0; r < kMaxChunksPerLane; ++r) {
-    const int c = g.sub + r * L;
-    if (c >= nch) break;
-    float o[Ck::E];
-    Ck::load(dout + id * Cf + c * Ck::E, o);
-    float v[KM][Ck::E];
-#pragma unroll
-    for (int k = 0; k < KM; ++k)
-      if (qw.slot[k] >= 0) Ck::load(fimg + (int64_t)qw.slot[k] * Cf + c * Ck::E, v[k]);
-#pragma unroll
-    for (int k = 0; k < KM; ++k)
-      if (qw.slot[k] >= 0)
-#pragma unroll
-        for (int e = 0; e < Ck::E; ++e) gk[k] = fmaf(o[e], v[k][e], gk[k]);
+      for (int k = 0; k < KM; ++k) {
+        if (k >= K) break;
+        ent_slot[id * K + k] = qw.slot[k];
+        ent_w[id * K + k] = qw.w[k];
+      }
+    }
   }
-  // <dO, F_k> over the group's lanes (aligned groups of L lanes)
-  for (int off = 1; off < L; off <<= 1)
+  const int L = 1 << lg;
+  const int grp = lane >> lg, sub = lane & (L - 1);
+  const int nch = Cf / Ck::E;
+  for (int u0 = 0; u0 < qwv; u0 += 64 >> lg) {   // uniform trip count: shuffles below
+    const int u = u0 + grp;
+    const int64_t id = base + u;
+    const bool live = id < total;
+    const int64_t b = (live ? id : base) / M;
+    const T* fimg = feats + b * N * Cf;
+    int sl[KM];
 #pragma unroll
-    for (int k = 0; k < KM; ++k) gk[k] += __shfl_xor(gk[k], off, 64);
-  if (!g.valid || g.sub != 0) return;
+    for (int k = 0; k < KM; ++k) sl[k] = live ? sw[wv].slot[u][k] : -1;
+    float gk[KM];
+#pragma unroll
+    for (int k = 0; k < KM; ++k) gk[k] = 0.f;
+#pragma unroll
+    for (int r = 0; r < kMaxChunksPerLane; ++r) {
+      const int c = sub + r * L;
+      if (c >= nch || !live) break;
+      float o[Ck::E];
+      Ck::load(dout + id * Cf + c * Ck::E, o);
+      float v[KM][Ck::E];
+#pragma unroll
+      for (int k = 0; k < KM; ++k)
+        if (sl[k] >= 0) Ck::load(fimg + (int64_t)sl[k] * Cf + c * Ck::E, v[k]);
+#pragma unroll
+      for (int k = 0; k < KM; ++k)
+        if (sl[k] >= 0)
+#pragma unroll
+          for (int e = 0; e < Ck::E; ++e) gk[k] = fmaf(o[e], v[k][e], gk[k]);
+    }
+    for (int off = 1; off < L; off <<= 1)
+#pragma unroll
+      for (int k = 0; k < KM; ++k) gk[k] += __shfl_xor(gk[k], off, 64);
+    if (sub == 0)
+#pragma unroll
+      for (int k = 0; k < KM; ++k) sg[wv][u][k] = gk[k];
+  }
+  __builtin_amdgcn_wave_barrier();
+  const int64_t id = base + lane;
+  if (lane >= qwv || id >= total) return;
+  float g[KM];
+#pragma unroll
+  for (int k = 0; k < KM; ++k) g[k] = sg[wv][lane][k];
   float delta = 0.f;
 #pragma unroll
-  for (int k = 0; k < KM; ++k) delta = fmaf(qw.w[k], gk[k], delta);
+  for (int k = 0; k < KM; ++k) delta = fmaf(qw.w[k], g[k], delta);
   float dqx = 0.f, dqy = 0.f, dps = 0.f;
 #pragma unroll
   for (int k = 0; k < KM; ++k) {
     if (qw.slot[k] < 0) continue;
-    const float ds = qw.w[k] * (gk[k] - delta);   // dL / d(-p d_k)
+    const float ds = qw.w[k] * (g[k] - delta);   // dL / d(-p d_k)
     dps = fmaf(-ds, qw.d[k], dps);
     if (qw.d[k] > 0.f) {
       const float f = -p * ds / qw.d[k];
@@ -418,12 +502,6 @@ knn_bwd_query_kernel(int N, int M, int Cf, int G, int K, int lg, float p, int64_
   }
   reinterpret_cast<float2*>(dq)[id] = make_float2(dqx, dqy);
   dpart[id] = dps;
-#pragma unroll
-  for (int k = 0; k < KM; ++k) {
-    if (k >= K) break;
-    ent_slot[id * K + k] = qw.slot[k];
-    ent_w[id * K + k] = qw.w[k];
-  }
 }
 
 __global__ void __launch_bounds__(kKnnThreads)
@@ -564,11 +642,16 @@ knn_dfeat_kernel(int N, int M, int Cf, int K, int lg, int64_t total, const T* __
                  const int32_t* __restrict__ off_all, const int32_t* __restrict__ ent_all,
                  const float* __restrict__ ent_w, T* __restrict__ dfeat) {
   using Ck = Chunk<T>;
-  const Group g = group_of(lg, total);
-  if (!g.valid) return;
-  const int L = 1 << lg;
-  const int64_t b = g.id / N;
-  const int t = (int)(g.id - b * N);
+  constexpr int kB = 8;   // entries (rows) in flight per batch
+  const int lane = threadIdx.x & 63;
+  // tokens dealt XCD-major: the waves of one XCD walk consecutive tokens of
+  // one image, whose dO rows then stay in that XCD's L2
+  const int64_t wave = (int64_t)xcd_remap(blockIdx.x, gridDim.x) * (kKnnThreads / 64) + (threadIdx.x >> 6);
+  const int64_t id = wave * (64 >> lg) + (lane >> lg);
+  if (id >= total) return;
+  const int L = 1 << lg, sub = lane & (L - 1);
+  const int64_t b = id / N;
+  const int t = (int)(id - b * N);
   const int64_t per = (int64_t)M * K;
   const int a = off_all[b * (N + 1) + t], z = off_all[b * (N + 1) + t + 1];
   const int32_t* ent = ent_all + b * per;
@@ -577,34 +660,32 @@ knn_dfeat_kernel(int N, int M, int Cf, int K, int lg, int64_t total, const T* __
   const int nch = Cf / Ck::E;
 #pragma unroll
   for (int r = 0; r < kMaxChunksPerLane; ++r) {
-    const int c = g.sub + r * L;
+    const int c = sub + r * L;
     if (c >= nch) break;
     float acc[Ck::E];
 #pragma unroll
     for (int e = 0; e < Ck::E; ++e) acc[e] = 0.f;
-    int u = a;
-    for (; u + 4 <= z; u += 4) {   // four rows in flight
-      float v[4][Ck::E], wt[4];
+    for (int u = a; u < z; u += kB) {
+      int e[kB];
+      float wt[kB];
+      float v[kB][Ck::E];
 #pragma unroll
-      for (int h = 0; h < 4; ++h) {
-        const int e = ent[u + h];
-        wt[h] = wimg[e];
-        Ck::load(oimg + (int64_t)(e / K) * Cf + c * Ck::E, v[h]);
+      for (int h = 0; h < kB; ++h) e[h] = u + h < z ? ent[u + h] : -1;
+#pragma unroll
+      for (int h = 0; h < kB; ++h) {
+        wt[h] = 0.f;
+        if (e[h] >= 0) {
+          wt[h] = wimg[e[h]];
+          Ck::load(oimg + (int64_t)(e[h] / K) * Cf + c * Ck::E, v[h]);
+        }
       }
 #pragma unroll
-      for (int h = 0; h < 4; ++h)
+      for (int h = 0; h < kB; ++h)
+        if (e[h] >= 0)
 #pragma unroll
-        for (int e = 0; e < Ck::E; ++e) acc[e] = fmaf(wt[h], v[h][e], acc[e]);
+          for (int q = 0; q < Ck::E; ++q) acc[q] = fmaf(wt[h], v[h][q], acc[q]);
     }
-    for (; u < z; ++u) {
-      const int e = ent[u];
-      float v[Ck::E];
-      Ck::load(oimg + (int64_t)(e / K) * Cf + c * Ck::E, v);
-      const float wt = wimg[e];
-#pragma unroll
-      for (int h = 0; h < Ck::E; ++h) acc[h] = fmaf(wt, v[h], acc[h]);
-    }
-    Ck::store(dfeat + g.id * Cf + c * Ck::E, acc);
+    Ck::store(dfeat + id * Cf + c * Ck::E, acc);
   }
 }
 
@@ -634,6 +715,15 @@ int group_log2(int Cf, int E) {
   return lg;
 }
 
+// Queries per wave of the forward and the query-major backward: eight
+// passes of 64 / L queries (L lanes per query), at most 64.
+int queries_per_wave(int lg) { return std::min(64, 512 >> lg); }
+
+unsigned blocks_for(int64_t total, int qwv) {
+  const int64_t waves = (total + qwv - 1) / qwv;
+  return (unsigned)((waves + kKnnThreads / 64 - 1) / (kKnnThreads / 64));
+}
+
 unsigned waves_grid(int64_t groups, int lg) {
   const int64_t per_wave = 64 >> lg;
   const int64_t waves = (groups + per_wave - 1) / per_wave;
@@ -646,9 +736,11 @@ hipError_t fwd_t(int B, int N, int M, int Cf, int G, int K, float p, const float
                  hipStream_t st) {
   const int lg = group_log2(Cf, Chunk<T>::E);
   const int64_t total = (int64_t)B * M;
+  const int qwv = queries_per_wave(lg);
+  const dim3 grid = dim3(blocks_for(total, qwv));
   auto go = [&](auto kern) {
-    hipLaunchKernelGGL(kern, dim3(waves_grid(total, lg)), dim3(kKnnThreads), 0, st, N, M, Cf, G, K,
-                       lg, p, total, coords, (const T*)feats, queries, table, (T*)out);
+    hipLaunchKernelGGL(kern, grid, dim3(kKnnThreads), 0, st, N, M, Cf, G, K, lg, p, total, qwv,
+                       coords, (const T*)feats, queries, table, (T*)out);
   };
   if (K <= 4) go(knn_fwd_kernel<T, 4>);
   else if (K <= 8) go(knn_fwd_kernel<T, 8>);
@@ -666,9 +758,10 @@ hipError_t bwd_t(int B, int N, int M, int Cf, int G, int K, float p, const float
   const int64_t MK = (int64_t)M * K;
   const int P = (int)((MK + kPart - 1) / kPart);
   const int64_t npc = (int64_t)B * P * N, nparts = (int64_t)B * P;
+  const int qwv = queries_per_wave(lg);
   auto go = [&](auto kern) {
-    hipLaunchKernelGGL(kern, dim3(waves_grid(nq, lg)), dim3(kKnnThreads), 0, st, N, M, Cf, G, K,
-                       lg, p, nq, coords, (const T*)feats, queries, table, (const T*)dout, dq,
+    hipLaunchKernelGGL(kern, dim3(blocks_for(nq, qwv)), dim3(kKnnThreads), 0, st, N, M, Cf, G, K,
+                       lg, p, nq, qwv, coords, (const T*)feats, queries, table, (const T*)dout, dq,
                        w.dpart, w.slot, w.wgt);
   };
   // empty sizes launch nothing but what writes outputs (dF, dp)
