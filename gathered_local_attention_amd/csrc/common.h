@@ -109,6 +109,7 @@ struct KnnWorkspace {
   float* wgt;       // [B, M, K]     its weight
   int32_t* ent;     // [B, M * K]    entries (query * K + slot) by token
   float* dpart;     // [B, M]        per-query share of dL/dp
+  int32_t* order;   // [B, N]        walk order of the tokens (feature gradient)
   size_t bytes;
 };
 
@@ -129,6 +130,7 @@ static inline KnnWorkspace knn_layout(void* base, int64_t B, int64_t N, int64_t 
   w.wgt = (float*)take((size_t)(B * M * K) * 4);
   w.ent = (int32_t*)take((size_t)(B * M * K) * 4);
   w.dpart = (float*)take((size_t)(B * M) * 4);
+  w.order = (int32_t*)take((size_t)(B * N) * 4);
   w.bytes = p;
   return w;
 }

@@ -266,6 +266,12 @@ struct Chunk;
 template <>
 struct Chunk<float> {
   static constexpr int E = 4;
+  static constexpr int NR = 4;   // chunks per lane at most (1024 channels)
+  __device__ static uint4 raw(const float* p) { return *reinterpret_cast<const uint4*>(p); }
+  __device__ static void cvt(uint4 a, float* v) {
+    v[0] = __uint_as_float(a.x); v[1] = __uint_as_float(a.y);
+    v[2] = __uint_as_float(a.z); v[3] = __uint_as_float(a.w);
+  }
   __device__ static void load(const float* p, float* v) {
     const float4 a = *reinterpret_cast<const float4*>(p);
     v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
@@ -281,6 +287,13 @@ typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 template <typename H, typename V>
 struct HalfChunk {
   static constexpr int E = 8;
+  static constexpr int NR = 2;   // chunks per lane at most (1024 channels)
+  __device__ static uint4 raw(const H* p) { return *reinterpret_cast<const uint4*>(p); }
+  __device__ static void cvt(uint4 a, float* v) {
+    const f32x8 f = __builtin_convertvector(__builtin_bit_cast(V, a), f32x8);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = f[e];
+  }
   __device__ static void load(const H* p, float* v) {
     const f32x8 f = __builtin_convertvector(__builtin_bit_cast(V, *reinterpret_cast<const uint4*>(p)), f32x8);
 #pragma unroll
@@ -373,6 +386,7 @@ knn_fwd_kernel(int N, int M, int Cf, int G, int K, int lg, float p, int64_t tota
   const int L = 1 << lg;
   const int grp = lane >> lg, sub = lane & (L - 1);
   const int nch = Cf / Ck::E;
+  const int nr = (nch - sub + L - 1) / L;   // chunks of this lane
 #pragma unroll 2
   for (int u0 = 0; u0 < qwv; u0 += 64 >> lg) {
     const int u = u0 + grp;
@@ -387,23 +401,27 @@ knn_fwd_kernel(int N, int M, int Cf, int G, int K, int lg, float p, int64_t tota
       sl[k] = sw[wv].slot[u][k];
       wt[k] = sw[wv].w[u][k];
     }
+    uint4 raw[Ck::NR][KM];   // every chunk's rows in flight before the sums
 #pragma unroll
-    for (int r = 0; r < kMaxChunksPerLane; ++r) {
-      const int c = sub + r * L;
-      if (c >= nch) break;
-      float v[KM][Ck::E];
+    for (int r = 0; r < Ck::NR; ++r)
 #pragma unroll
       for (int k = 0; k < KM; ++k)
-        if (sl[k] >= 0) Ck::load(fimg + (int64_t)sl[k] * Cf + c * Ck::E, v[k]);
+        if (r < nr && sl[k] >= 0) raw[r][k] = Ck::raw(fimg + (int64_t)sl[k] * Cf + (sub + r * L) * Ck::E);
+#pragma unroll
+    for (int r = 0; r < Ck::NR; ++r) {
+      if (r >= nr) break;
       float acc[Ck::E];
 #pragma unroll
       for (int e = 0; e < Ck::E; ++e) acc[e] = 0.f;
 #pragma unroll
-      for (int k = 0; k < KM; ++k)
-        if (sl[k] >= 0)
+      for (int k = 0; k < KM; ++k) {
+        if (sl[k] < 0) continue;
+        float v[Ck::E];
+        Ck::cvt(raw[r][k], v);
 #pragma unroll
-          for (int e = 0; e < Ck::E; ++e) acc[e] = fmaf(wt[k], v[k][e], acc[e]);
-      Ck::store(out + id * Cf + c * Ck::E, acc);
+        for (int e = 0; e < Ck::E; ++e) acc[e] = fmaf(wt[k], v[e], acc[e]);
+      }
+      Ck::store(out + id * Cf + (sub + r * L) * Ck::E, acc);
     }
   }
 }
@@ -444,6 +462,7 @@ knn_bwd_query_kernel(int N, int M, int Cf, int G, int K, int lg, float p, int64_
   const int L = 1 << lg;
   const int grp = lane >> lg, sub = lane & (L - 1);
   const int nch = Cf / Ck::E;
+  const int nr = (nch - sub + L - 1) / L;   // chunks of this lane
   for (int u0 = 0; u0 < qwv; u0 += 64 >> lg) {   // uniform trip count: shuffles below
     const int u = u0 + grp;
     const int64_t id = base + u;
@@ -456,21 +475,27 @@ knn_bwd_query_kernel(int N, int M, int Cf, int G, int K, int lg, float p, int64_
     float gk[KM];
 #pragma unroll
     for (int k = 0; k < KM; ++k) gk[k] = 0.f;
+    uint4 raw[Ck::NR][KM], oraw[Ck::NR];   // every chunk's rows in flight before the sums
 #pragma unroll
-    for (int r = 0; r < kMaxChunksPerLane; ++r) {
-      const int c = sub + r * L;
-      if (c >= nch || !live) break;
+    for (int r = 0; r < Ck::NR; ++r) {
+      if (r < nr && live) oraw[r] = Ck::raw(dout + id * Cf + (sub + r * L) * Ck::E);
+#pragma unroll
+      for (int k = 0; k < KM; ++k)
+        if (r < nr && sl[k] >= 0) raw[r][k] = Ck::raw(fimg + (int64_t)sl[k] * Cf + (sub + r * L) * Ck::E);
+    }
+#pragma unroll
+    for (int r = 0; r < Ck::NR; ++r) {
+      if (r >= nr || !live) break;
       float o[Ck::E];
-      Ck::load(dout + id * Cf + c * Ck::E, o);
-      float v[KM][Ck::E];
+      Ck::cvt(oraw[r], o);
 #pragma unroll
-      for (int k = 0; k < KM; ++k)
-        if (sl[k] >= 0) Ck::load(fimg + (int64_t)sl[k] * Cf + c * Ck::E, v[k]);
+      for (int k = 0; k < KM; ++k) {
+        if (sl[k] < 0) continue;
+        float v[Ck::E];
+        Ck::cvt(raw[r][k], v);
 #pragma unroll
-      for (int k = 0; k < KM; ++k)
-        if (sl[k] >= 0)
-#pragma unroll
-          for (int e = 0; e < Ck::E; ++e) gk[k] = fmaf(o[e], v[k][e], gk[k]);
+        for (int e = 0; e < Ck::E; ++e) gk[k] = fmaf(o[e], v[e], gk[k]);
+      }
     }
     for (int off = 1; off < L; off <<= 1)
 #pragma unroll
@@ -579,11 +604,15 @@ knn_pprefix_kernel(int N, int P, int64_t n_tok, int32_t* __restrict__ pcnt, int3
   const int64_t b = x / N;
   const int t = (int)(x - b * N);
   int acc = 0;
-  for (int s = 0; s < P; ++s) {
-    int32_t* c = &pcnt[(b * P + s) * N + t];
-    const int v = *c;
-    *c = acc;
-    acc += v;
+  for (int s0 = 0; s0 < P; s0 += 16) {   // sixteen loads in flight
+    int v[16];
+#pragma unroll
+    for (int h = 0; h < 16; ++h) v[h] = s0 + h < P ? pcnt[(b * P + s0 + h) * N + t] : 0;
+#pragma unroll
+    for (int h = 0; h < 16; ++h) {
+      if (s0 + h < P) pcnt[(b * P + s0 + h) * N + t] = acc;
+      acc += v[h];
+    }
   }
   cnt[x] = acc;
 }
@@ -633,59 +662,161 @@ knn_pplace_kernel(int N, int64_t MK, int P, int64_t n_part, const int32_t* __res
     if (t[r] >= 0) ent[off[t[r]] + pc[t[r]] + rank[r]] = (int32_t)(e0 + lane + 64 * r);
 }
 
+// Spatial walk order of the tokens for the feature gradient: the tokens of
+// an image bucketed on a coarse grid (about two per bucket) in LDS, so that
+// the waves resident at one time work on neighbouring tokens, which share
+// most of their queries (and so the dO rows they gather stay in L2).  Any
+// order gives the same result: each token's sum has its own fixed order.
+// grid = B, for images of at most kTabMaxTokens tokens.
+__global__ void __launch_bounds__(kTabThreads)
+knn_order_kernel(const float* __restrict__ coords, int N, int G, int32_t* __restrict__ order) {
+  __shared__ int start[kTabMaxBuckets];
+  const int b = blockIdx.x, tid = threadIdx.x;
+  const int shift = 16 - ceil_log2(G);
+  const double step = (double)(1 << shift);
+  int pb = 0;
+  while (pb < 16 - shift && (1 << (2 * pb + 2)) <= max(N, 1) / 2) ++pb;
+  const int bs = 16 - pb, Pb = 1 << pb, nb = Pb * Pb;
+  const float2* xy = reinterpret_cast<const float2*>(coords) + (int64_t)b * N;
+  for (int x = tid; x < nb; x += kTabThreads) start[x] = 0;
+  __syncthreads();
+  constexpr int kPer = kTabMaxTokens / kTabThreads;
+  int bk[kPer], rk[kPer];
+#pragma unroll
+  for (int r = 0; r < kPer; ++r) {
+    const int e = tid + r * kTabThreads;
+    bk[r] = -1;
+    if (e < N) {
+      const float2 c = xy[e];
+      const uint32_t qx = quantize_axis(c.x, step), qy = quantize_axis(c.y, step);
+      // buckets in row-major order of the coarse grid
+      bk[r] = (int)((qy >> bs) * (uint32_t)Pb + (qx >> bs));
+      rk[r] = atomicAdd(&start[bk[r]], 1);
+    }
+  }
+  __syncthreads();
+  __shared__ int tmp[17];
+  constexpr int kBPer = kTabMaxBuckets / kTabThreads;
+  int cnt[kBPer];
+  int run = 0;
+#pragma unroll
+  for (int r = 0; r < kBPer; ++r) {
+    const int x = tid * kBPer + r;
+    cnt[r] = x < nb ? start[x] : 0;
+    run += cnt[r];
+  }
+  int total;
+  int acc = block_exclusive_scan(run, tmp, kTabThreads, &total);
+#pragma unroll
+  for (int r = 0; r < kBPer; ++r) {
+    const int x = tid * kBPer + r;
+    if (x < nb) start[x] = acc;
+    acc += cnt[r];
+  }
+  __syncthreads();
+  int32_t* ord = order + (int64_t)b * N;
+#pragma unroll
+  for (int r = 0; r < kPer; ++r)
+    if (bk[r] >= 0) ord[start[bk[r]] + rk[r]] = tid + r * kTabThreads;
+}
+
 // ---------------------------------------------------------------------------
 // Backward, token-major part: dF[b, t] = sum over its entries of w dO[b, m].
 // ---------------------------------------------------------------------------
+// Workgroup = one group of 64 / L tokens (L lanes per token, 16 bytes of the
+// row per lane) and its four waves split each token's entries: wave w takes
+// the batches w, w + 4, ... of kB entries, and the four partial sums are
+// added in wave order through LDS, so every token's sum has one fixed order.
+// Workgroups are dealt XCD-aware: workgroup 8 i + x (dispatched to XCD x)
+// takes token group i of the images x, x + 8, x + 16, ... one after the
+// other, so that the workgroups of one XCD work on one image at a time and
+// its dO rows stay in that XCD's L2 (with fewer than 8 images, X = B
+// streams).
 template <typename T>
 __global__ void __launch_bounds__(kKnnThreads)
-knn_dfeat_kernel(int N, int M, int Cf, int K, int lg, int64_t total, const T* __restrict__ dout,
+knn_dfeat_kernel(int B, int N, int M, int Cf, int K, int lg, int split, const T* __restrict__ dout,
                  const int32_t* __restrict__ off_all, const int32_t* __restrict__ ent_all,
-                 const float* __restrict__ ent_w, T* __restrict__ dfeat) {
+                 const float* __restrict__ ent_w, const int32_t* __restrict__ order,
+                 T* __restrict__ dfeat) {
   using Ck = Chunk<T>;
-  constexpr int kB = 8;   // entries (rows) in flight per batch
-  const int lane = threadIdx.x & 63;
-  // tokens dealt XCD-major: the waves of one XCD walk consecutive tokens of
-  // one image, whose dO rows then stay in that XCD's L2
-  const int64_t wave = (int64_t)xcd_remap(blockIdx.x, gridDim.x) * (kKnnThreads / 64) + (threadIdx.x >> 6);
-  const int64_t id = wave * (64 >> lg) + (lane >> lg);
-  if (id >= total) return;
+  constexpr int kB = 8;                          // entries (rows) per batch
+  constexpr int kW = kKnnThreads / 64;           // waves per workgroup
+  __shared__ float part[kW][Ck::NR * Ck::E][64];
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int X = min(B, 8);                      // image streams (one per XCD when B >= 8)
+  const int x = (int)(blockIdx.x % X), gi = (int)(blockIdx.x / X);
   const int L = 1 << lg, sub = lane & (L - 1);
-  const int64_t b = id / N;
-  const int t = (int)(id - b * N);
-  const int64_t per = (int64_t)M * K;
-  const int a = off_all[b * (N + 1) + t], z = off_all[b * (N + 1) + t + 1];
-  const int32_t* ent = ent_all + b * per;
-  const float* wimg = ent_w + b * per;
-  const T* oimg = dout + b * M * Cf;
+  // `split` waves share a token group; the workgroup covers kW / split groups
+  const int grp = gi * (kW / split) + wv / split, sw = wv % split;
+  const int pos = grp * (64 >> lg) + (lane >> lg);   // token position in the walk order
   const int nch = Cf / Ck::E;
+  const int nr = (nch - sub + L - 1) / L;            // chunks of this lane
+  const int64_t per = (int64_t)M * K;
+  for (int img = x; img < B; img += X) {
+    const int64_t b = img;
+    const bool live = pos < N;
+    const int t = live ? (order ? order[b * N + pos] : pos) : 0;
+    const int a = live ? off_all[b * (N + 1) + t] : 0;
+    const int z = live ? off_all[b * (N + 1) + t + 1] : 0;
+    const int32_t* ent = ent_all + b * per;
+    const float* wimg = ent_w + b * per;
+    const T* oimg = dout + b * M * Cf;
+    float acc[Ck::NR][Ck::E];
 #pragma unroll
-  for (int r = 0; r < kMaxChunksPerLane; ++r) {
-    const int c = sub + r * L;
-    if (c >= nch) break;
-    float acc[Ck::E];
+    for (int r = 0; r < Ck::NR; ++r)
 #pragma unroll
-    for (int e = 0; e < Ck::E; ++e) acc[e] = 0.f;
-    for (int u = a; u < z; u += kB) {
+      for (int e = 0; e < Ck::E; ++e) acc[r][e] = 0.f;
+    for (int u = a + sw * kB; u < z; u += split * kB) {
       int e[kB];
       float wt[kB];
-      float v[kB][Ck::E];
 #pragma unroll
       for (int h = 0; h < kB; ++h) e[h] = u + h < z ? ent[u + h] : -1;
 #pragma unroll
-      for (int h = 0; h < kB; ++h) {
-        wt[h] = 0.f;
-        if (e[h] >= 0) {
-          wt[h] = wimg[e[h]];
-          Ck::load(oimg + (int64_t)(e[h] / K) * Cf + c * Ck::E, v[h]);
+      for (int h = 0; h < kB; ++h) wt[h] = e[h] >= 0 ? wimg[e[h]] : 0.f;
+      uint4 raw[Ck::NR][kB];   // every chunk's rows in flight before the sums
+#pragma unroll
+      for (int r = 0; r < Ck::NR; ++r)
+#pragma unroll
+        for (int h = 0; h < kB; ++h)
+          if (r < nr && e[h] >= 0) raw[r][h] = Ck::raw(oimg + (int64_t)(e[h] / K) * Cf + (sub + r * L) * Ck::E);
+#pragma unroll
+      for (int r = 0; r < Ck::NR; ++r) {
+        if (r >= nr) break;
+#pragma unroll
+        for (int h = 0; h < kB; ++h) {
+          if (e[h] < 0) continue;
+          float v[Ck::E];
+          Ck::cvt(raw[r][h], v);
+#pragma unroll
+          for (int q = 0; q < Ck::E; ++q) acc[r][q] = fmaf(wt[h], v[q], acc[r][q]);
         }
       }
-#pragma unroll
-      for (int h = 0; h < kB; ++h)
-        if (e[h] >= 0)
-#pragma unroll
-          for (int q = 0; q < Ck::E; ++q) acc[q] = fmaf(wt[h], v[h][q], acc[q]);
     }
-    Ck::store(dfeat + id * Cf + c * Ck::E, acc);
+    // partial sums of the group's other waves to its first, added in wave order
+    if (split > 1) {
+      if (sw > 0) {
+#pragma unroll
+        for (int r = 0; r < Ck::NR; ++r)
+#pragma unroll
+          for (int q = 0; q < Ck::E; ++q) part[wv][r * Ck::E + q][lane] = acc[r][q];
+      }
+      __syncthreads();
+      if (sw == 0) {
+        for (int v2 = 1; v2 < split; ++v2)
+#pragma unroll
+          for (int r = 0; r < Ck::NR; ++r)
+#pragma unroll
+            for (int q = 0; q < Ck::E; ++q) acc[r][q] += part[wv + v2][r * Ck::E + q][lane];
+      }
+      __syncthreads();   // part is reused by the next image
+    }
+    if (sw == 0 && live) {
+#pragma unroll
+      for (int r = 0; r < Ck::NR; ++r) {
+        if (r >= nr) break;
+        Ck::store(dfeat + (b * N + t) * Cf + (sub + r * L) * Ck::E, acc[r]);
+      }
+    }
   }
 }
 
@@ -784,9 +915,18 @@ hipError_t bwd_t(int B, int N, int M, int Cf, int G, int K, float p, const float
       hipLaunchKernelGGL(knn_pplace_kernel, dim3((unsigned)((nparts + 3) / 4)), dim3(kKnnThreads), 0,
                          st, N, MK, P, nparts, (const int32_t*)w.slot, (const int32_t*)w.off,
                          (const int32_t*)w.pcnt, w.ent);
-    hipLaunchKernelGGL(knn_dfeat_kernel<T>, dim3(waves_grid(ntok, lg)), dim3(kKnnThreads), 0, st,
-                       N, M, Cf, K, lg, ntok, (const T*)dout, (const int32_t*)w.off,
-                       (const int32_t*)w.ent, (const float*)w.wgt, (T*)dfeat);
+    const bool ordered = N <= kTabMaxTokens && G <= 65536;
+    if (ordered)
+      hipLaunchKernelGGL(knn_order_kernel, dim3(B), dim3(kTabThreads), 0, st, coords, N, G, w.order);
+    // waves per token group: one when tokens have few entries, more when many
+    const int64_t ept = N > 0 ? MK / N : 0;   // entries per token, on average
+    const int split = ept < 16 ? 1 : (ept < 48 ? 2 : 4);
+    const int groups = (N + (64 >> lg) - 1) / (64 >> lg);   // token groups per image
+    const int wgs = (groups * split + kKnnThreads / 64 - 1) / (kKnnThreads / 64);
+    hipLaunchKernelGGL(knn_dfeat_kernel<T>, dim3((unsigned)(std::min(B, 8) * wgs)), dim3(kKnnThreads), 0, st,
+                       B, N, M, Cf, K, lg, split, (const T*)dout, (const int32_t*)w.off,
+                       (const int32_t*)w.ent, (const float*)w.wgt,
+                       ordered ? (const int32_t*)w.order : nullptr, (T*)dfeat);
   }
   hipLaunchKernelGGL(knn_dp_kernel, dim3(1), dim3(1024), 0, st, nq, (const float*)w.dpart, dp);
   return hipGetLastError();
