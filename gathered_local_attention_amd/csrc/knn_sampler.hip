@@ -228,23 +228,23 @@ __device__ __forceinline__ void query_weights(const float2 q, int b, int G, int 
   int j = (int)fmin(fmax(floor((double)q.x + 0.5), 0.0), (double)(G - 1));
   int i = (int)fmin(fmax(floor((double)q.y + 0.5), 0.0), (double)(G - 1));
   const int32_t* row = table + (((int64_t)b * G + i) * G + j) * K;
+  // the row, then every slot's coordinates, loaded unconditionally (clamped
+  // indices, masked below) so that the loads are issued together
+  int sl[KM];
+#pragma unroll
+  for (int k = 0; k < KM; ++k) sl[k] = row[min(k, K - 1)];
+  float2 x[KM];
+#pragma unroll
+  for (int k = 0; k < KM; ++k) x[k] = N > 0 ? xy[min(max(sl[k], 0), N - 1)] : make_float2(0.f, 0.f);
   float mx = -INFINITY;
 #pragma unroll
   for (int k = 0; k < KM; ++k) {
-    qw.slot[k] = -1;
-    qw.d[k] = 0.f;
-    qw.diff[k] = make_float2(0.f, 0.f);
-    if (k < K) {
-      const int s = row[k];
-      if (s >= 0 && s < N) {
-        const float2 x = xy[s];
-        const float dx = q.x - x.x, dy = q.y - x.y;
-        qw.slot[k] = s;
-        qw.diff[k] = make_float2(dx, dy);
-        qw.d[k] = sqrtf(fmaf(dx, dx, dy * dy));
-        mx = fmaxf(mx, -p * qw.d[k]);
-      }
-    }
+    const bool ok = k < K && sl[k] >= 0 && sl[k] < N;
+    const float dx = q.x - x[k].x, dy = q.y - x[k].y;
+    qw.slot[k] = ok ? sl[k] : -1;
+    qw.diff[k] = ok ? make_float2(dx, dy) : make_float2(0.f, 0.f);
+    qw.d[k] = ok ? sqrtf(fmaf(dx, dx, dy * dy)) : 0.f;
+    if (ok) mx = fmaxf(mx, -p * qw.d[k]);
   }
   float sum = 0.f;
 #pragma unroll
@@ -401,12 +401,17 @@ knn_fwd_kernel(int N, int M, int Cf, int G, int K, int lg, float p, int64_t tota
       sl[k] = sw[wv].slot[u][k];
       wt[k] = sw[wv].w[u][k];
     }
-    uint4 raw[Ck::NR][KM];   // every chunk's rows in flight before the sums
+    // every chunk's rows in flight before the sums: the loads are
+    // unconditional (an empty slot or a chunk past the row reads a valid
+    // place, the data is then masked), so that no branch splits them
+    uint4 raw[Ck::NR][KM];
+    if (N > 0) {
 #pragma unroll
-    for (int r = 0; r < Ck::NR; ++r)
+      for (int r = 0; r < Ck::NR; ++r)
 #pragma unroll
-      for (int k = 0; k < KM; ++k)
-        if (r < nr && sl[k] >= 0) raw[r][k] = Ck::raw(fimg + (int64_t)sl[k] * Cf + (sub + r * L) * Ck::E);
+        for (int k = 0; k < KM; ++k)
+          raw[r][k] = Ck::raw(fimg + (int64_t)max(sl[k], 0) * Cf + (r < nr ? sub + r * L : sub) * Ck::E);
+    }
 #pragma unroll
     for (int r = 0; r < Ck::NR; ++r) {
       if (r >= nr) break;
@@ -415,7 +420,7 @@ knn_fwd_kernel(int N, int M, int Cf, int G, int K, int lg, float p, int64_t tota
       for (int e = 0; e < Ck::E; ++e) acc[e] = 0.f;
 #pragma unroll
       for (int k = 0; k < KM; ++k) {
-        if (sl[k] < 0) continue;
+        if (sl[k] < 0) raw[r][k] = make_uint4(0u, 0u, 0u, 0u);
         float v[Ck::E];
         Ck::cvt(raw[r][k], v);
 #pragma unroll
@@ -475,13 +480,17 @@ knn_bwd_query_kernel(int N, int M, int Cf, int G, int K, int lg, float p, int64_
     float gk[KM];
 #pragma unroll
     for (int k = 0; k < KM; ++k) gk[k] = 0.f;
-    uint4 raw[Ck::NR][KM], oraw[Ck::NR];   // every chunk's rows in flight before the sums
+    // unconditional loads (see the forward), masked afterwards
+    uint4 raw[Ck::NR][KM], oraw[Ck::NR];
+    const int64_t oid = live ? id : base;
 #pragma unroll
     for (int r = 0; r < Ck::NR; ++r) {
-      if (r < nr && live) oraw[r] = Ck::raw(dout + id * Cf + (sub + r * L) * Ck::E);
+      const int c = r < nr ? sub + r * L : sub;
+      oraw[r] = Ck::raw(dout + oid * Cf + c * Ck::E);
+      if (N > 0) {
 #pragma unroll
-      for (int k = 0; k < KM; ++k)
-        if (r < nr && sl[k] >= 0) raw[r][k] = Ck::raw(fimg + (int64_t)sl[k] * Cf + (sub + r * L) * Ck::E);
+        for (int k = 0; k < KM; ++k) raw[r][k] = Ck::raw(fimg + (int64_t)max(sl[k], 0) * Cf + c * Ck::E);
+      }
     }
 #pragma unroll
     for (int r = 0; r < Ck::NR; ++r) {
@@ -490,19 +499,48 @@ knn_bwd_query_kernel(int N, int M, int Cf, int G, int K, int lg, float p, int64_
       Ck::cvt(oraw[r], o);
 #pragma unroll
       for (int k = 0; k < KM; ++k) {
-        if (sl[k] < 0) continue;
+        if (sl[k] < 0) raw[r][k] = make_uint4(0u, 0u, 0u, 0u);
         float v[Ck::E];
         Ck::cvt(raw[r][k], v);
 #pragma unroll
         for (int e = 0; e < Ck::E; ++e) gk[k] = fmaf(o[e], v[e], gk[k]);
       }
     }
-    for (int off = 1; off < L; off <<= 1)
+    if (L >= KM) {
+      // Sum over the group with the values split as they go: at offsets
+      // 1, 2, 4, ... a lane keeps half of its values (the half picked by the
+      // offset's bit of its lane number) and adds the partner's copy of that
+      // half; after log2(KM) such rounds lane l holds one value, index
+      // rev(l mod KM), summed over KM lanes, and the remaining offsets add
+      // the group's other lanes.  A fixed pattern: deterministic.
+      float vv[KM];
 #pragma unroll
-      for (int k = 0; k < KM; ++k) gk[k] += __shfl_xor(gk[k], off, 64);
-    if (sub == 0)
+      for (int k = 0; k < KM; ++k) vv[k] = gk[k];
 #pragma unroll
-      for (int k = 0; k < KM; ++k) sg[wv][u][k] = gk[k];
+      for (int o = 1, V = KM; o < KM; o <<= 1, V >>= 1) {
+        const bool hi = (lane & o) != 0;
+#pragma unroll
+        for (int i = 0; i < V / 2; ++i) {
+          const float send = hi ? vv[i] : vv[i + V / 2];
+          const float keep = hi ? vv[i + V / 2] : vv[i];
+          vv[i] = keep + __shfl_xor(send, o, 64);
+        }
+      }
+      for (int o = KM; o < L; o <<= 1) vv[0] += __shfl_xor(vv[0], o, 64);
+      if ((sub & ~(KM - 1)) == 0) {
+        int idx = 0;   // value index held by this lane: bit j of the lane -> KM / 2^(j+1)
+#pragma unroll
+        for (int o = 1, h = KM / 2; o < KM; o <<= 1, h >>= 1) idx += (lane & o) ? h : 0;
+        sg[wv][u][idx] = vv[0];
+      }
+    } else {
+      for (int off = 1; off < L; off <<= 1)
+#pragma unroll
+        for (int k = 0; k < KM; ++k) gk[k] += __shfl_xor(gk[k], off, 64);
+      if (sub == 0)
+#pragma unroll
+        for (int k = 0; k < KM; ++k) sg[wv][u][k] = gk[k];
+    }
   }
   __builtin_amdgcn_wave_barrier();
   const int64_t id = base + lane;
@@ -769,22 +807,24 @@ knn_dfeat_kernel(int B, int N, int M, int Cf, int K, int lg, int split, const T*
     for (int u = a + sw * kB; u < z; u += split * kB) {
       int e[kB];
       float wt[kB];
+      // unconditional loads (a batch past the segment end re-reads entry u),
+      // masked afterwards
 #pragma unroll
-      for (int h = 0; h < kB; ++h) e[h] = u + h < z ? ent[u + h] : -1;
+      for (int h = 0; h < kB; ++h) e[h] = ent[u + h < z ? u + h : u];
 #pragma unroll
-      for (int h = 0; h < kB; ++h) wt[h] = e[h] >= 0 ? wimg[e[h]] : 0.f;
-      uint4 raw[Ck::NR][kB];   // every chunk's rows in flight before the sums
+      for (int h = 0; h < kB; ++h) wt[h] = wimg[e[h]];
+      uint4 raw[Ck::NR][kB];
 #pragma unroll
       for (int r = 0; r < Ck::NR; ++r)
 #pragma unroll
         for (int h = 0; h < kB; ++h)
-          if (r < nr && e[h] >= 0) raw[r][h] = Ck::raw(oimg + (int64_t)(e[h] / K) * Cf + (sub + r * L) * Ck::E);
+          raw[r][h] = Ck::raw(oimg + (int64_t)(e[h] / K) * Cf + (r < nr ? sub + r * L : sub) * Ck::E);
 #pragma unroll
       for (int r = 0; r < Ck::NR; ++r) {
         if (r >= nr) break;
 #pragma unroll
         for (int h = 0; h < kB; ++h) {
-          if (e[h] < 0) continue;
+          if (u + h >= z) raw[r][h] = make_uint4(0u, 0u, 0u, 0u);
           float v[Ck::E];
           Ck::cvt(raw[r][h], v);
 #pragma unroll
