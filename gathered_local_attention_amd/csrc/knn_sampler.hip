@@ -34,7 +34,7 @@
 //                         over the group, dq and the query's share of dp;
 //                         slots and weights kept for the feature gradient
 //                         and references counted per token.
-//   knn_pcount/pprefix/scan/pplace  token-major entry lists (entry =
+//   knn_pprefix/scan/pplace  token-major entry lists (entry =
 //                         query * K + slot) by a stable counting sort over
 //                         partitions of the entries: each token's segment is
 //                         in entry order, so the feature gradient is summed
@@ -42,7 +42,7 @@
 //   knn_dfeat_kernel      a lane group per token: dF = sum over its entries
 //                         of w * dO (gathered rows), written once (0 for
 //                         tokens no query reaches).
-//   knn_dp_kernel         fixed-order reduction of the per-query dp shares.
+//   knn_dp_kernel         fixed-order reduction of the per-wave dp shares.
 // Nothing in the backward uses floating-point atomics: the results are
 // bitwise reproducible.
 #include "common.h"
@@ -56,6 +56,7 @@ constexpr int kTabThreads = 256;
 constexpr int kTabMaxBuckets = 64 * 64;   // grid sides up to 64
 constexpr int kTabMaxTokens = 4096;
 constexpr int kKnnThreads = 256;          // 4 waves
+constexpr int kPart = kKnnPart;           // entries per partition of the stable counting sort
 
 __device__ __forceinline__ int ceil_log2(int v) {
   int b = 0;
@@ -444,7 +445,8 @@ knn_bwd_query_kernel(int N, int M, int Cf, int G, int K, int lg, float p, int64_
                      const float* __restrict__ coords, const T* __restrict__ feats,
                      const float* __restrict__ queries, const int32_t* __restrict__ table,
                      const T* __restrict__ dout, float* __restrict__ dq, float* __restrict__ dpart,
-                     int32_t* __restrict__ ent_slot, float* __restrict__ ent_w) {
+                     int32_t* __restrict__ ent_slot, float* __restrict__ ent_w, int P,
+                     int32_t* __restrict__ pcnt) {
   using Ck = Chunk<T>;
   __shared__ WaveSlots<KM> sw[kKnnThreads / 64];
   __shared__ float sg[kKnnThreads / 64][64][KM];
@@ -543,8 +545,9 @@ knn_bwd_query_kernel(int N, int M, int Cf, int G, int K, int lg, float p, int64_
     }
   }
   __builtin_amdgcn_wave_barrier();
-  const int64_t id = base + lane;
-  if (lane >= qwv || id >= total) return;
+  const int64_t id0 = base + lane;
+  const bool mine = lane < qwv && id0 < total;
+  const int64_t id = mine ? id0 : base;   // idle lanes mirror the first query (shuffle below)
   float g[KM];
 #pragma unroll
   for (int k = 0; k < KM; ++k) g[k] = sg[wv][lane][k];
@@ -563,8 +566,21 @@ knn_bwd_query_kernel(int N, int M, int Cf, int G, int K, int lg, float p, int64_
       dqy = fmaf(f, qw.diff[k].y, dqy);
     }
   }
-  reinterpret_cast<float2*>(dq)[id] = make_float2(dqx, dqy);
-  dpart[id] = dps;
+  if (mine) reinterpret_cast<float2*>(dq)[id] = make_float2(dqx, dqy);
+  // the wave's dp shares summed in a fixed order (lanes past the end add 0)
+  float sdp = mine ? dps : 0.f;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) sdp += __shfl_xor(sdp, o, 64);
+  if (lane == 0) dpart[base / qwv] = sdp;
+  // the entries' counts per partition of kPart entries and token (integer
+  // atomics, order independent), last: nothing in this wave waits on them
+  if (mine) {
+    const int64_t b = id / M;
+    const int64_t e0 = (id - b * M) * K;   // first entry of this query in its image
+#pragma unroll
+    for (int k = 0; k < KM; ++k)
+      if (k < K && qw.slot[k] >= 0) atomicAdd(&pcnt[(b * P + (e0 + k) / kPart) * N + qw.slot[k]], 1);
+  }
 }
 
 __global__ void __launch_bounds__(kKnnThreads)
@@ -615,25 +631,12 @@ knn_scan_kernel(int N, const int32_t* __restrict__ cnt_all, int32_t* __restrict_
 // Token-major entry lists, in entry order (entry = query * K + slot), by a
 // stable counting sort.  The entries of an image are cut into partitions of
 // kPart consecutive entries: (1) per partition and token, the count of its
-// entries (integer atomics: the counts do not depend on their order);
-// (2) per token, the counts turned into exclusive prefixes over the
-// partitions, and the token's total; (3) the totals scanned into segment
-// starts (knn_scan_kernel); (4) per partition, one wave places every entry
-// at segment start + the partition's prefix + the number of earlier entries
-// of the same token in the partition.
-constexpr int kPart = kKnnPart;
-
-__global__ void __launch_bounds__(kKnnThreads)
-knn_pcount_kernel(int N, int64_t MK, int P, int64_t n_ent, const int32_t* __restrict__ ent_slot,
-                  int32_t* __restrict__ pcnt) {
-  const int64_t x = (int64_t)blockIdx.x * kKnnThreads + threadIdx.x;
-  if (x >= n_ent) return;
-  const int t = ent_slot[x];
-  if (t < 0) return;
-  const int64_t b = x / MK;
-  const int s = (int)((x - b * MK) / kPart);
-  atomicAdd(&pcnt[(b * P + s) * N + t], 1);
-}
+// entries (integer atomics in the query-major kernel: the counts do not
+// depend on their order); (2) per token, the counts turned into exclusive
+// prefixes over the partitions, and the token's total; (3) the totals
+// scanned into segment starts (knn_scan_kernel); (4) per partition, every
+// entry placed at segment start + the partition's prefix + the number of
+// earlier entries of the same token in the partition.
 
 __global__ void __launch_bounds__(kKnnThreads)
 knn_pprefix_kernel(int N, int P, int64_t n_tok, int32_t* __restrict__ pcnt, int32_t* __restrict__ cnt) {
@@ -655,49 +658,34 @@ knn_pprefix_kernel(int N, int P, int64_t n_tok, int32_t* __restrict__ pcnt, int3
   cnt[x] = acc;
 }
 
-// one wave per partition (four partitions per workgroup)
+// one workgroup per partition; wave w ranks the partition's entries
+// w*64 .. w*64+63 (one per lane) against the earlier entries of the partition
 __global__ void __launch_bounds__(kKnnThreads)
-knn_pplace_kernel(int N, int64_t MK, int P, int64_t n_part, const int32_t* __restrict__ ent_slot,
+knn_pplace_kernel(int N, int64_t MK, int P, const int32_t* __restrict__ ent_slot,
                   const int32_t* __restrict__ off_all, const int32_t* __restrict__ pcnt,
                   int32_t* __restrict__ ent_all) {
-  __shared__ __align__(16) int32_t tok[kKnnThreads / 64][kPart];
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int64_t part = (int64_t)blockIdx.x * (kKnnThreads / 64) + w;
-  if (part >= n_part) return;
+  static_assert(kPart == kKnnThreads, "one entry per thread");
+  __shared__ __align__(16) int32_t tok[kPart];
+  const int64_t part = blockIdx.x;
   const int64_t b = part / P;
   const int s = (int)(part - b * P);
   const int64_t e0 = (int64_t)s * kPart;
   const int n = (int)min((int64_t)kPart, MK - e0);
-  const int32_t* sl = ent_slot + b * MK + e0;
-  constexpr int R = kPart / 64;
-  int t[R];
-#pragma unroll
-  for (int r = 0; r < R; ++r) {
-    const int u = lane + 64 * r;
-    t[r] = u < n ? sl[u] : -1;
-    tok[w][u] = t[r];
-  }
-  __builtin_amdgcn_wave_barrier();   // the wave's LDS writes precede its reads (in order)
-  int rank[R];
-#pragma unroll
-  for (int r = 0; r < R; ++r) rank[r] = 0;
-  const int4* t4 = reinterpret_cast<const int4*>(tok[w]);
-  for (int y4 = 0; y4 < kPart / 4; ++y4) {
+  const int u = threadIdx.x;
+  const int t = u < n ? ent_slot[b * MK + e0 + u] : -1;
+  tok[u] = t;
+  __syncthreads();
+  const int ymax = (threadIdx.x & ~63) + 64;   // the wave's entries are below this
+  int rank = 0;
+  const int4* t4 = reinterpret_cast<const int4*>(tok);
+  for (int y4 = 0; y4 < ymax / 4; ++y4) {
     const int4 v = t4[y4];
-    const int ys[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-    for (int h = 0; h < 4; ++h) {
-      const int y = 4 * y4 + h;
-#pragma unroll
-      for (int r = 0; r < R; ++r) rank[r] += (ys[h] == t[r] && y < lane + 64 * r) ? 1 : 0;
-    }
+    const int y = 4 * y4;
+    rank += (v.x == t && y < u) + (v.y == t && y + 1 < u) + (v.z == t && y + 2 < u) +
+            (v.w == t && y + 3 < u);
   }
-  const int32_t* off = off_all + b * (N + 1);
-  const int32_t* pc = pcnt + (b * P + s) * N;
-  int32_t* ent = ent_all + b * MK;
-#pragma unroll
-  for (int r = 0; r < R; ++r)
-    if (t[r] >= 0) ent[off[t[r]] + pc[t[r]] + rank[r]] = (int32_t)(e0 + lane + 64 * r);
+  if (t >= 0)
+    ent_all[b * MK + off_all[b * (N + 1) + t] + pcnt[(b * P + s) * N + t] + rank] = (int32_t)(e0 + u);
 }
 
 // Spatial walk order of the tokens for the feature gradient: the tokens of
@@ -933,28 +921,24 @@ hipError_t bwd_t(int B, int N, int M, int Cf, int G, int K, float p, const float
   auto go = [&](auto kern) {
     hipLaunchKernelGGL(kern, dim3(blocks_for(nq, qwv)), dim3(kKnnThreads), 0, st, N, M, Cf, G, K,
                        lg, p, nq, qwv, coords, (const T*)feats, queries, table, (const T*)dout, dq,
-                       w.dpart, w.slot, w.wgt);
+                       w.dpart, w.slot, w.wgt, P, w.pcnt);
   };
   // empty sizes launch nothing but what writes outputs (dF, dp)
+  if (npc > 0) hipLaunchKernelGGL(knn_zero_kernel, grid1(npc), dim3(kKnnThreads), 0, st, npc, w.pcnt);
   if (nq > 0) {
     if (K <= 4) go(knn_bwd_query_kernel<T, 4>);
     else if (K <= 8) go(knn_bwd_query_kernel<T, 8>);
     else go(knn_bwd_query_kernel<T, 16>);
   }
   if (ntok > 0) {
-    if (npc > 0) {
-      hipLaunchKernelGGL(knn_zero_kernel, grid1(npc), dim3(kKnnThreads), 0, st, npc, w.pcnt);
-      hipLaunchKernelGGL(knn_pcount_kernel, grid1(nent), dim3(kKnnThreads), 0, st, N, MK, P, nent,
-                         (const int32_t*)w.slot, w.pcnt);
-    }
     hipLaunchKernelGGL(knn_pprefix_kernel, grid1(ntok), dim3(kKnnThreads), 0, st, N, P, ntok,
                        w.pcnt, w.cnt);
     hipLaunchKernelGGL(knn_scan_kernel, dim3(B), dim3(kScanThreads), 0, st, N,
                        (const int32_t*)w.cnt, w.off);
     if (nparts > 0)
-      hipLaunchKernelGGL(knn_pplace_kernel, dim3((unsigned)((nparts + 3) / 4)), dim3(kKnnThreads), 0,
-                         st, N, MK, P, nparts, (const int32_t*)w.slot, (const int32_t*)w.off,
-                         (const int32_t*)w.pcnt, w.ent);
+      hipLaunchKernelGGL(knn_pplace_kernel, dim3((unsigned)nparts), dim3(kKnnThreads), 0, st, N, MK,
+                         P, (const int32_t*)w.slot, (const int32_t*)w.off, (const int32_t*)w.pcnt,
+                         w.ent);
     const bool ordered = N <= kTabMaxTokens && G <= 65536;
     if (ordered)
       hipLaunchKernelGGL(knn_order_kernel, dim3(B), dim3(kTabThreads), 0, st, coords, N, G, w.order);
@@ -968,7 +952,9 @@ hipError_t bwd_t(int B, int N, int M, int Cf, int G, int K, float p, const float
                        (const int32_t*)w.ent, (const float*)w.wgt,
                        ordered ? (const int32_t*)w.order : nullptr, (T*)dfeat);
   }
-  hipLaunchKernelGGL(knn_dp_kernel, dim3(1), dim3(1024), 0, st, nq, (const float*)w.dpart, dp);
+  const int64_t nwaves = (nq + qwv - 1) / qwv;   // one dp share per wave of the query kernel
+  hipLaunchKernelGGL(knn_dp_kernel, dim3(1), dim3(1024), 0, st, nq > 0 ? nwaves : 0,
+                     (const float*)w.dpart, dp);
   return hipGetLastError();
 }
 
