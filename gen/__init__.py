@@ -15,3 +15,4 @@ from .synth import (  # noqa: F401
     to_dtype,
 )
 from .sampler import SAMPLER_CONFIGS, SamplerConfig, make_sampler_case  # noqa: F401
+from .merge import MERGE_CONFIGS, MergeConfig, make_merge_case  # noqa: F401

@@ -6,7 +6,8 @@ the product path (``gathered_local_attention_amd``) never imports, calls or
 links it, and it imports nothing from the product path.
 
 See :mod:`oracle.cluster_attention` (neighbour build and attention) and
-:mod:`oracle.knn_sampler` (the decoder's KNN-cache point sampler) for the
+:mod:`oracle.knn_sampler` (the decoder's KNN-cache point sampler) and
+:mod:`oracle.token_merge` (adaptive off-grid token merging) for the
 functions and the passages of the pages each one follows.
 """
 
@@ -34,4 +35,11 @@ from .knn_sampler import (  # noqa: F401
     knn_table_batch,
     knn_sample_fwd_batch,
     knn_sample_bwd_batch,
+)
+from .token_merge import (  # noqa: F401
+    merge_anchors,
+    merge_assign,
+    merge_weights,
+    merge_fwd,
+    merge_bwd,
 )
