@@ -16,6 +16,10 @@ knn_table(coords, grid_side, K) -> table
 knn_sample_fwd(feats, coords, queries, table, p) -> out
 knn_sample_bwd(feats, coords, queries, table, p, dout) -> (dfeats, dq, dp)
 knn_sample(feats, coords, queries, table, p) -> out   (autograd: feats, queries)
+merge_plan(coords, scores, k, grid_side) -> (anchors, assign, members, offsets)
+merge_fwd(feats, coords, scores, members, offsets, k) -> (out_feats, out_coords)
+merge_bwd(feats, coords, scores, members, offsets, dout_feats, dout_coords)
+    -> (dfeats, dcoords, dscores)
 """
 
 from __future__ import annotations
@@ -38,6 +42,9 @@ __all__ = [
     "knn_sample_bwd",
     "knn_sample",
     "knn_bwd_workspace_bytes",
+    "merge_plan",
+    "merge_fwd",
+    "merge_bwd",
     "ClusterAttnError",
     "CA_OK",
 ]
@@ -275,3 +282,62 @@ def knn_sample(feats, coords, queries, table, p: float):
     """Autograd-aware sampler (gradients for feats and queries; the table
     and the token coordinates are constants)."""
     return _KnnSample.apply(feats, coords, queries, table, p)
+
+
+# ---------------------------------------------------------------------------
+# Adaptive token merging
+# ---------------------------------------------------------------------------
+
+def merge_plan(coords: torch.Tensor, scores: torch.Tensor, k: int, grid_side: int):
+    """Anchors [B, k], assignment [B, N], member lists [B, N] and group
+    offsets [B, k + 1] (all int32)."""
+    lib = _lib.load()
+    B, N, two = coords.shape
+    if two != 2 or scores.shape != (B, N):
+        raise ValueError("coords [B, N, 2] and scores [B, N] expected")
+    dev = coords.device
+    anchors = torch.empty((B, k), dtype=torch.int32, device=dev)
+    assign = torch.empty((B, N), dtype=torch.int32, device=dev)
+    members = torch.empty((B, N), dtype=torch.int32, device=dev)
+    offsets = torch.empty((B, k + 1), dtype=torch.int32, device=dev)
+    _check(lib.cluster_attn_merge_plan(
+        _dev(coords, "coords", torch.float32), _dev(scores, "scores", torch.float32), B, N, int(k),
+        int(grid_side), anchors.data_ptr(), assign.data_ptr(), members.data_ptr(),
+        offsets.data_ptr(), _stream(coords)), "cluster_attn_merge_plan")
+    return anchors, assign, members, offsets
+
+
+def merge_fwd(feats, coords, scores, members, offsets):
+    """Merged features [B, k, C] (dtype of feats) and coordinates [B, k, 2] f32."""
+    lib = _lib.load()
+    B, N, C = feats.shape
+    k = offsets.shape[1] - 1
+    if feats.dtype not in _DT:
+        raise TypeError(f"unsupported dtype {feats.dtype}")
+    out_f = torch.empty((B, k, C), dtype=feats.dtype, device=feats.device)
+    out_x = torch.empty((B, k, 2), dtype=torch.float32, device=feats.device)
+    _check(lib.cluster_attn_merge_fwd(
+        _DT[feats.dtype], B, N, k, C, _dev(feats, "feats"), _dev(coords, "coords", torch.float32),
+        _dev(scores, "scores", torch.float32), _dev(members, "members", torch.int32),
+        _dev(offsets, "offsets", torch.int32), out_f.data_ptr(), out_x.data_ptr(),
+        _stream(feats)), "cluster_attn_merge_fwd")
+    return out_f, out_x
+
+
+def merge_bwd(feats, coords, scores, members, offsets, dout_feats, dout_coords):
+    """Gradients of features (dtype of feats), coordinates and scores (f32)."""
+    lib = _lib.load()
+    B, N, C = feats.shape
+    k = offsets.shape[1] - 1
+    if dout_feats.shape != (B, k, C) or dout_feats.dtype != feats.dtype:
+        raise ValueError("dout_feats must be [B, k, C] in the dtype of feats")
+    dfeats = torch.empty_like(feats)
+    dcoords = torch.empty((B, N, 2), dtype=torch.float32, device=feats.device)
+    dscores = torch.empty((B, N), dtype=torch.float32, device=feats.device)
+    _check(lib.cluster_attn_merge_bwd(
+        _DT[feats.dtype], B, N, k, C, _dev(feats, "feats"), _dev(coords, "coords", torch.float32),
+        _dev(scores, "scores", torch.float32), _dev(members, "members", torch.int32),
+        _dev(offsets, "offsets", torch.int32), _dev(dout_feats, "dout_feats"),
+        _dev(dout_coords, "dout_coords", torch.float32), dfeats.data_ptr(), dcoords.data_ptr(),
+        dscores.data_ptr(), _stream(feats)), "cluster_attn_merge_bwd")
+    return dfeats, dcoords, dscores

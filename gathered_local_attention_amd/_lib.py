@@ -30,6 +30,13 @@ SIGNATURES = {
     "cluster_attn_knn_sample_bwd": (
         _c_int, [_c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _f,
                  _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _c_size, _vp]),
+    "cluster_attn_merge_plan": (
+        _c_int, [_vp, _vp, _c_int, _c_int, _c_int, _c_int, _vp, _vp, _vp, _vp, _vp]),
+    "cluster_attn_merge_fwd": (
+        _c_int, [_c_int, _c_int, _c_int, _c_int, _c_int, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
+    "cluster_attn_merge_bwd": (
+        _c_int, [_c_int, _c_int, _c_int, _c_int, _c_int, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                 _vp, _vp, _vp, _vp]),
     "cluster_attn_status_string": (ctypes.c_char_p, [_c_int]),
     "cluster_attn_last_error": (ctypes.c_char_p, []),
     "cluster_attn_version": (ctypes.c_char_p, []),

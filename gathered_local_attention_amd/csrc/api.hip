@@ -88,6 +88,18 @@ int check_knn_shape(int B, int N, int M, int Cf, int G, int K) {
   return CA_OK;
 }
 
+
+int check_merge_shape(int dt, int B, int N, int k, int C) {
+  if (dt != CA_F32 && dt != CA_BF16 && dt != CA_F16)
+    return fail(CA_ERR_UNSUPPORTED, "dtype %d is not one of CA_F32, CA_BF16, CA_F16", dt);
+  if (B < 0 || N < 0 || k < 0) return fail(CA_ERR_SHAPE, "bad sizes B=%d N=%d k=%d", B, N, k);
+  if (N > 4096) return fail(CA_ERR_UNSUPPORTED, "N=%d: merging supports up to 4096 tokens", N);
+  if (k > N || (N > 0 && k < 1)) return fail(CA_ERR_SHAPE, "k=%d must be in [1, N=%d]", k, N);
+  if (C < 8 || C > 1024 || C % 8 != 0)
+    return fail(CA_ERR_UNSUPPORTED, "channels %d: must be a multiple of 8 in [8, 1024]", C);
+  return CA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -283,6 +295,69 @@ int cluster_attn_knn_sample_bwd(int dt, int B, int N, int M, int C, int grid_sid
   return hip_status(ca::launch_knn_bwd(dt, B, N, M, C, grid_side, K, p, coords, feats, queries,
                                        table, dout, dfeats, dq, dp, ws, (hipStream_t)hip_stream),
                     "knn bwd launch");
+}
+
+int cluster_attn_merge_plan(const float* coords, const float* scores, int B, int N, int k,
+                            int grid_side, int32_t* anchors, int32_t* assign, int32_t* members,
+                            int32_t* offsets, void* hip_stream) {
+  if (B < 0 || N < 0 || k < 0) return fail(CA_ERR_SHAPE, "bad sizes B=%d N=%d k=%d", B, N, k);
+  if (N > 4096) return fail(CA_ERR_UNSUPPORTED, "N=%d: merging supports up to 4096 tokens", N);
+  if (k > N || (N > 0 && k < 1)) return fail(CA_ERR_SHAPE, "k=%d must be in [1, N=%d]", k, N);
+  if (grid_side < 1 || grid_side > 65536)
+    return fail(CA_ERR_SHAPE, "grid_side=%d outside [1, 65536]", grid_side);
+  if (B == 0 || N == 0) return ok();
+  if (!coords || !scores || !anchors || !assign || !members || !offsets)
+    return fail(CA_ERR_NULL, "NULL tensor pointer");
+  Range outs[] = {{anchors, (size_t)B * k * 4}, {assign, (size_t)B * N * 4},
+                  {members, (size_t)B * N * 4}, {offsets, (size_t)B * (k + 1) * 4}};
+  Range ins[] = {{coords, (size_t)B * N * 8}, {scores, (size_t)B * N * 4}};
+  if (int s = check_alias(outs, 4, ins, 2)) return s;
+  return hip_status(ca::launch_merge_plan(coords, scores, B, N, k, grid_side, anchors, assign,
+                                          members, offsets, (hipStream_t)hip_stream),
+                    "merge plan launch");
+}
+
+int cluster_attn_merge_fwd(int dt, int B, int N, int k, int C, const void* feats,
+                           const float* coords, const float* scores, const int32_t* members,
+                           const int32_t* offsets, void* out_feats, float* out_coords,
+                           void* hip_stream) {
+  if (int s = check_merge_shape(dt, B, N, k, C)) return s;
+  if (B == 0 || N == 0) return ok();
+  if (!feats || !coords || !scores || !members || !offsets || !out_feats || !out_coords)
+    return fail(CA_ERR_NULL, "NULL tensor pointer");
+  const size_t es = elem_size(dt);
+  Range outs[] = {{out_feats, (size_t)B * k * C * es}, {out_coords, (size_t)B * k * 8}};
+  Range ins[] = {{feats, (size_t)B * N * C * es}, {coords, (size_t)B * N * 8},
+                 {scores, (size_t)B * N * 4}, {members, (size_t)B * N * 4},
+                 {offsets, (size_t)B * (k + 1) * 4}};
+  if (int s = check_alias(outs, 2, ins, 5)) return s;
+  return hip_status(ca::launch_merge_fwd(dt, B, N, k, C, feats, coords, scores, members, offsets,
+                                         out_feats, out_coords, (hipStream_t)hip_stream),
+                    "merge fwd launch");
+}
+
+int cluster_attn_merge_bwd(int dt, int B, int N, int k, int C, const void* feats,
+                           const float* coords, const float* scores, const int32_t* members,
+                           const int32_t* offsets, const void* dout_feats,
+                           const float* dout_coords, void* dfeats, float* dcoords,
+                           float* dscores, void* hip_stream) {
+  if (int s = check_merge_shape(dt, B, N, k, C)) return s;
+  if (B == 0 || N == 0) return ok();
+  if (!feats || !coords || !scores || !members || !offsets || !dout_feats || !dout_coords ||
+      !dfeats || !dcoords || !dscores)
+    return fail(CA_ERR_NULL, "NULL tensor pointer");
+  const size_t es = elem_size(dt);
+  Range outs[] = {{dfeats, (size_t)B * N * C * es}, {dcoords, (size_t)B * N * 8},
+                  {dscores, (size_t)B * N * 4}};
+  Range ins[] = {{feats, (size_t)B * N * C * es},   {coords, (size_t)B * N * 8},
+                 {scores, (size_t)B * N * 4},       {members, (size_t)B * N * 4},
+                 {offsets, (size_t)B * (k + 1) * 4}, {dout_feats, (size_t)B * k * C * es},
+                 {dout_coords, (size_t)B * k * 8}};
+  if (int s = check_alias(outs, 3, ins, 7)) return s;
+  return hip_status(ca::launch_merge_bwd(dt, B, N, k, C, feats, coords, scores, members, offsets,
+                                         dout_feats, dout_coords, dfeats, dcoords, dscores,
+                                         (hipStream_t)hip_stream),
+                    "merge bwd launch");
 }
 
 }  // extern "C"

@@ -241,4 +241,16 @@ hipError_t launch_knn_bwd(int dt, int B, int N, int M, int Cf, int G, int K, flo
                           const int32_t* table, const void* dout, void* dfeat, float* dq,
                           float* dp, void* ws, hipStream_t st);
 
+// Adaptive token merging (token_merge.hip)
+hipError_t launch_merge_plan(const float* coords, const float* scores, int B, int N, int k, int G,
+                             int32_t* anchors, int32_t* assign, int32_t* members,
+                             int32_t* offsets, hipStream_t st);
+hipError_t launch_merge_fwd(int dt, int B, int N, int k, int Cf, const void* feats,
+                            const float* coords, const float* scores, const int32_t* members,
+                            const int32_t* offsets, void* out_f, float* out_x, hipStream_t st);
+hipError_t launch_merge_bwd(int dt, int B, int N, int k, int Cf, const void* feats,
+                            const float* coords, const float* scores, const int32_t* members,
+                            const int32_t* offsets, const void* dout_f, const float* dout_x,
+                            void* dfeats, float* dcoords, float* dscores, hipStream_t st);
+
 }  // namespace ca

@@ -1,0 +1,413 @@
+// Adaptive off-grid token merging on gfx950.
+//
+// Source: English notes page "AFFMAE: Scalable Vision Pre-Training for
+// High-Resolution Microscopy Segmentation on Desktop Hardware", "Key Designs"
+// item 1 (adaptive off-grid token merging: every token keeps its 2D
+// coordinate; a lightweight MLP scores the tokens, the top-k by the
+// retention rate become anchors, and the other tokens are merged,
+// differentiably, into their nearest anchors, features and spatial support
+// alike).  The library's readings of what the page leaves open:
+//   scores    an input (the scoring MLP is outside); k given by the caller;
+//   anchors   the k largest scores, ties to the lower token index, listed in
+//             ascending token index;
+//   assign    an anchor to itself, any other token to the anchor nearest by
+//             squared distance of the 16-bit fixed-point coordinates (the
+//             neighbour build's quantisation), ties to the earlier anchor;
+//   merge     within a group the softmax of the members' scores weighs
+//             features and coordinates: F'_a = sum w_i F_i, X'_a = sum w_i X_i;
+//   backward  gradients of F, X and the scores (anchors, assignment fixed).
+//
+// Kernels:
+//   merge_plan_kernel  one workgroup per image (up to 4096 tokens, all in
+//                      LDS): ranks by counting (score, index), anchors by a
+//                      workgroup scan in token order, nearest anchors by a
+//                      scan of the anchor list (fp32 screen, exact int64
+//                      keys), and the groups' member lists by a bitonic sort
+//                      of (anchor, token) keys: members in token order.
+//   merge_fwd_kernel   a lane group per anchor (16 bytes of the row per
+//                      lane): the group's softmax, then the weighted sums.
+//   merge_bwd_kernel   the same groups: g_i = <dF'_a, F_i> + <dX'_a, X_i>
+//                      (group reductions), dF_i = w_i dF'_a, dX_i = w_i dX'_a,
+//                      ds_i = w_i (g_i - sum_j w_j g_j); every token written
+//                      once (it belongs to one group): no atomics.
+#include "common.h"
+
+#include <algorithm>
+
+namespace ca {
+
+namespace {
+
+constexpr int kPlanT = 1024;
+constexpr int kMaxTok = 4096;
+constexpr int kMergeThreads = 256;
+
+typedef float mf32x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 mbf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 mf16x8 __attribute__((ext_vector_type(8)));
+
+// 16 bytes of a row as floats (exact widening; RNE narrowing on store)
+template <typename T> struct Row16;
+template <> struct Row16<float> {
+  static constexpr int E = 4;
+  __device__ static void load(const float* p, float* v) {
+    const float4 a = *reinterpret_cast<const float4*>(p);
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+  }
+  __device__ static void store(float* p, const float* v) {
+    *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
+  }
+};
+template <typename H, typename V> struct Row16Half {
+  static constexpr int E = 8;
+  __device__ static void load(const H* p, float* v) {
+    const mf32x8 f = __builtin_convertvector(__builtin_bit_cast(V, *reinterpret_cast<const uint4*>(p)), mf32x8);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = f[e];
+  }
+  __device__ static void store(H* p, const float* v) {
+    const mf32x8 f = {v[0], v[1], v[2], v[3], v[4], v[5], v[6], v[7]};
+    *reinterpret_cast<uint4*>(p) = __builtin_bit_cast(uint4, __builtin_convertvector(f, V));
+  }
+};
+template <> struct Row16<bf16> : Row16Half<bf16, mbf16x8> {};
+template <> struct Row16<f16> : Row16Half<f16, mf16x8> {};
+
+constexpr int kMaxChunks = 4;   // chunks of 16 bytes per lane (1024 channels of f32)
+
+// ---------------------------------------------------------------------------
+// Plan: anchors, assignment, member lists.  grid = B, 1024 threads.
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(kPlanT)
+merge_plan_kernel(const float* __restrict__ coords, const float* __restrict__ scores, int N, int k,
+                  int G, int32_t* __restrict__ anchors, int32_t* __restrict__ assign,
+                  int32_t* __restrict__ members, int32_t* __restrict__ offsets) {
+  __shared__ __align__(16) float sc[kMaxTok];
+  __shared__ __align__(16) uint32_t qc[kMaxTok];     // token fixed-point (qx | qy << 16)
+  __shared__ __align__(16) uint32_t ac[kMaxTok];     // anchor fixed-point, by position
+  __shared__ int32_t apos[kMaxTok];                   // token -> anchor position, or -1
+  __shared__ uint32_t key[kMaxTok];                   // (assign << 12 | token), sorted
+  __shared__ int tmp[17];
+  const int b = blockIdx.x, tid = threadIdx.x;
+  const int bits = [&] { int v = 0; while ((1 << v) < G) ++v; return v; }();
+  const double step = (double)(1u << (16 - bits));
+  const float* s = scores + (int64_t)b * N;
+  const float2* xy = reinterpret_cast<const float2*>(coords) + (int64_t)b * N;
+  for (int i = tid; i < N; i += kPlanT) {
+    sc[i] = s[i];
+    const float2 c = xy[i];
+    qc[i] = quantize_axis(c.x, step) | (quantize_axis(c.y, step) << 16);
+  }
+  __syncthreads();
+
+  // rank of token i by (score descending, index ascending); anchor iff < k.
+  // Thread t owns tokens 4t .. 4t+3 (consecutive: the scan below is in
+  // token order).
+  constexpr int R = kMaxTok / kPlanT;
+  bool an[R];
+  int nan_ = 0;
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int i = tid * R + r;
+    an[r] = false;
+    if (i < N) {
+      const float si = sc[i];
+      int rank = 0;
+      for (int j = 0; j < N; ++j) {
+        const float sj = sc[j];
+        rank += (sj > si || (sj == si && j < i)) ? 1 : 0;
+      }
+      an[r] = rank < k;
+    }
+    nan_ += an[r] ? 1 : 0;
+  }
+  int tot;
+  int pos = block_exclusive_scan(nan_, tmp, kPlanT, &tot);
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int i = tid * R + r;
+    if (i < N) {
+      apos[i] = an[r] ? pos : -1;
+      if (an[r]) {
+        anchors[(int64_t)b * k + pos] = i;
+        ac[pos] = qc[i];
+        ++pos;
+      }
+    }
+  }
+  __syncthreads();
+
+  // nearest anchor: fp32 screen (coordinates < 2^16, exact as floats; a
+  // relative bound of 2^-20 keeps every candidate at or below the best),
+  // exact (d2 << 12 | position) keys in 64 bits
+  for (int i = tid; i < N; i += kPlanT) {
+    int a = apos[i];
+    if (a < 0) {
+      const uint32_t q = qc[i];
+      const int64_t x = q & 0xFFFFu, y = q >> 16;
+      const float fx = (float)x, fy = (float)y;
+      uint64_t best = ~0ull;
+      float thr = INFINITY;
+      for (int p = 0; p < k; ++p) {
+        const uint32_t c = ac[p];
+        const float dx = (float)(c & 0xFFFFu) - fx, dy = (float)(c >> 16) - fy;
+        if (fmaf(dx, dx, dy * dy) > thr) continue;
+        const int64_t ix = (int64_t)(c & 0xFFFFu) - x, iy = (int64_t)(c >> 16) - y;
+        const uint64_t kk = ((uint64_t)(ix * ix + iy * iy) << 12) | (uint32_t)p;
+        if (kk < best) {
+          best = kk;
+          thr = (float)(best >> 12) * (1.0f + 0x1p-20f);
+        }
+      }
+      a = (int)(best & 0xFFFu);
+    }
+    assign[(int64_t)b * N + i] = a;
+    key[i] = ((uint32_t)a << 12) | (uint32_t)i;
+  }
+  // members: bitonic sort of the keys (padded with the maximum)
+  int P2 = 1;
+  while (P2 < N) P2 <<= 1;
+  for (int i = N + tid; i < P2; i += kPlanT) key[i] = 0xFFFFFFFFu;
+  __syncthreads();
+  for (int kk = 2; kk <= P2; kk <<= 1) {
+    for (int j = kk >> 1; j > 0; j >>= 1) {
+      for (int i = tid; i < P2 / 2; i += kPlanT) {
+        const int lo = ((i & ~(j - 1)) << 1) | (i & (j - 1));
+        const uint32_t x = key[lo], y = key[lo + j];
+        if ((x > y) == ((lo & kk) == 0)) {
+          key[lo] = y;
+          key[lo + j] = x;
+        }
+      }
+      __syncthreads();
+    }
+  }
+  int32_t* mem = members + (int64_t)b * N;
+  int32_t* off = offsets + (int64_t)b * (k + 1);
+  for (int i = tid; i < N; i += kPlanT) {
+    const uint32_t kv = key[i];
+    mem[i] = (int32_t)(kv & 0xFFFu);
+    const int g = (int)(kv >> 12);
+    if (i == 0 || (key[i - 1] >> 12) != (uint32_t)g) off[g] = i;   // every group holds its anchor
+  }
+  if (tid == 0) off[k] = N;
+}
+
+// Lane groups: L = 2^lg lanes per anchor, 64 / L anchors per wave.
+struct MGroup {
+  int64_t id;
+  int sub;
+  bool valid;
+};
+__device__ __forceinline__ MGroup mgroup(int lg, int64_t total) {
+  const int lane = threadIdx.x & 63;
+  const int64_t wave = (int64_t)blockIdx.x * (kMergeThreads / 64) + (threadIdx.x >> 6);
+  MGroup g;
+  g.id = wave * (64 >> lg) + (lane >> lg);
+  g.sub = lane & ((1 << lg) - 1);
+  g.valid = g.id < total;
+  return g;
+}
+
+// softmax statistics of a group's scores: max and 1 / sum of exp
+__device__ __forceinline__ void group_softmax(const int32_t* __restrict__ mem, int a, int z,
+                                              const float* __restrict__ s, float& mx, float& inv) {
+  mx = -INFINITY;
+  for (int u = a; u < z; ++u) mx = fmaxf(mx, s[mem[u]]);
+  float sum = 0.f;
+  for (int u = a; u < z; ++u) sum += __builtin_amdgcn_exp2f((s[mem[u]] - mx) * 1.4426950408889634f);
+  inv = sum > 0.f ? 1.f / sum : 0.f;
+}
+
+template <typename T>
+__global__ void __launch_bounds__(kMergeThreads)
+merge_fwd_kernel(int N, int k, int Cf, int lg, int64_t total, const T* __restrict__ feats,
+                 const float* __restrict__ coords, const float* __restrict__ scores,
+                 const int32_t* __restrict__ members, const int32_t* __restrict__ offsets,
+                 T* __restrict__ out_f, float* __restrict__ out_x) {
+  using Rw = Row16<T>;
+  const MGroup g = mgroup(lg, total);
+  if (!g.valid) return;
+  const int L = 1 << lg;
+  const int64_t b = g.id / k;
+  const int an = (int)(g.id - b * k);
+  const int32_t* mem = members + b * N;
+  const int a = offsets[b * (k + 1) + an], z = offsets[b * (k + 1) + an + 1];
+  const float* s = scores + b * N;
+  float mx, inv;
+  group_softmax(mem, a, z, s, mx, inv);
+  const int nch = Cf / Rw::E;
+  const T* fimg = feats + b * N * Cf;
+  const float2* xy = reinterpret_cast<const float2*>(coords) + b * N;
+  float acc[kMaxChunks][Rw::E];
+#pragma unroll
+  for (int r = 0; r < kMaxChunks; ++r)
+#pragma unroll
+    for (int e = 0; e < Rw::E; ++e) acc[r][e] = 0.f;
+  float ax = 0.f, ay = 0.f;
+  for (int u = a; u < z; ++u) {
+    const int i = mem[u];
+    const float w = __builtin_amdgcn_exp2f((s[i] - mx) * 1.4426950408889634f) * inv;
+#pragma unroll
+    for (int r = 0; r < kMaxChunks; ++r) {
+      const int c = g.sub + r * L;
+      if (c >= nch) break;
+      float v[Rw::E];
+      Rw::load(fimg + (int64_t)i * Cf + c * Rw::E, v);
+#pragma unroll
+      for (int e = 0; e < Rw::E; ++e) acc[r][e] = fmaf(w, v[e], acc[r][e]);
+    }
+    const float2 x = xy[i];
+    ax = fmaf(w, x.x, ax);
+    ay = fmaf(w, x.y, ay);
+  }
+#pragma unroll
+  for (int r = 0; r < kMaxChunks; ++r) {
+    const int c = g.sub + r * L;
+    if (c >= nch) break;
+    Rw::store(out_f + g.id * Cf + c * Rw::E, acc[r]);
+  }
+  if (g.sub == 0) reinterpret_cast<float2*>(out_x)[g.id] = make_float2(ax, ay);
+}
+
+template <typename T>
+__global__ void __launch_bounds__(kMergeThreads)
+merge_bwd_kernel(int N, int k, int Cf, int lg, int64_t total, const T* __restrict__ feats,
+                 const float* __restrict__ coords, const float* __restrict__ scores,
+                 const int32_t* __restrict__ members, const int32_t* __restrict__ offsets,
+                 const T* __restrict__ dout_f, const float* __restrict__ dout_x,
+                 T* __restrict__ dfeats, float* __restrict__ dcoords, float* __restrict__ dscores) {
+  using Rw = Row16<T>;
+  const MGroup g = mgroup(lg, total);
+  const int L = 1 << lg;
+  const int64_t id = g.valid ? g.id : 0;   // idle lanes mirror anchor 0 (group shuffles)
+  const int64_t b = id / k;
+  const int an = (int)(id - b * k);
+  const int32_t* mem = members + b * N;
+  const int a = offsets[b * (k + 1) + an], z = offsets[b * (k + 1) + an + 1];
+  const float* s = scores + b * N;
+  float mx, inv;
+  group_softmax(mem, a, z, s, mx, inv);
+  const int nch = Cf / Rw::E;
+  const T* fimg = feats + b * N * Cf;
+  const float2* xy = reinterpret_cast<const float2*>(coords) + b * N;
+  float dof[kMaxChunks][Rw::E];
+#pragma unroll
+  for (int r = 0; r < kMaxChunks; ++r) {
+    const int c = g.sub + r * L;
+#pragma unroll
+    for (int e = 0; e < Rw::E; ++e) dof[r][e] = 0.f;
+    if (c < nch) Rw::load(dout_f + id * Cf + c * Rw::E, dof[r]);
+  }
+  const float2 dox = reinterpret_cast<const float2*>(dout_x)[id];
+  float gbar = 0.f;
+  for (int u = a; u < z; ++u) {   // same trip count for the whole group
+    const int i = mem[u];
+    const float w = __builtin_amdgcn_exp2f((s[i] - mx) * 1.4426950408889634f) * inv;
+    float dot = 0.f;
+#pragma unroll
+    for (int r = 0; r < kMaxChunks; ++r) {
+      const int c = g.sub + r * L;
+      if (c >= nch) break;
+      float v[Rw::E], d[Rw::E];
+      Rw::load(fimg + (int64_t)i * Cf + c * Rw::E, v);
+#pragma unroll
+      for (int e = 0; e < Rw::E; ++e) {
+        dot = fmaf(dof[r][e], v[e], dot);
+        d[e] = w * dof[r][e];
+      }
+      if (g.valid) Rw::store(dfeats + (b * N + i) * Cf + c * Rw::E, d);
+    }
+    for (int o = 1; o < L; o <<= 1) dot += __shfl_xor(dot, o, 64);
+    const float2 x = xy[i];
+    const float gi = dot + dox.x * x.x + dox.y * x.y;
+    gbar = fmaf(w, gi, gbar);
+    if (g.valid && g.sub == 0) {
+      dscores[b * N + i] = gi;   // g_i for now; finished below by the same lane
+      reinterpret_cast<float2*>(dcoords)[b * N + i] = make_float2(w * dox.x, w * dox.y);
+    }
+  }
+  if (!g.valid || g.sub != 0) return;
+  for (int u = a; u < z; ++u) {
+    const int i = mem[u];
+    const float w = __builtin_amdgcn_exp2f((s[i] - mx) * 1.4426950408889634f) * inv;
+    dscores[b * N + i] = w * (dscores[b * N + i] - gbar);
+  }
+}
+
+int mgroup_log2(int Cf, int E) {
+  const int nch = Cf / E;
+  int lg = 0;
+  while ((1 << lg) < nch && lg < 6) ++lg;
+  return lg;
+}
+
+unsigned mgrid(int64_t groups, int lg) {
+  const int64_t per_wave = 64 >> lg;
+  const int64_t waves = (groups + per_wave - 1) / per_wave;
+  return (unsigned)((waves + kMergeThreads / 64 - 1) / (kMergeThreads / 64));
+}
+
+template <typename T>
+hipError_t fwd_t(int B, int N, int k, int Cf, const void* feats, const float* coords,
+                 const float* scores, const int32_t* members, const int32_t* offsets, void* out_f,
+                 float* out_x, hipStream_t st) {
+  const int lg = mgroup_log2(Cf, Row16<T>::E);
+  const int64_t total = (int64_t)B * k;
+  hipLaunchKernelGGL(merge_fwd_kernel<T>, dim3(mgrid(total, lg)), dim3(kMergeThreads), 0, st, N, k,
+                     Cf, lg, total, (const T*)feats, coords, scores, members, offsets, (T*)out_f,
+                     out_x);
+  return hipGetLastError();
+}
+
+template <typename T>
+hipError_t bwd_t(int B, int N, int k, int Cf, const void* feats, const float* coords,
+                 const float* scores, const int32_t* members, const int32_t* offsets,
+                 const void* dout_f, const float* dout_x, void* dfeats, float* dcoords,
+                 float* dscores, hipStream_t st) {
+  const int lg = mgroup_log2(Cf, Row16<T>::E);
+  const int64_t total = (int64_t)B * k;
+  hipLaunchKernelGGL(merge_bwd_kernel<T>, dim3(mgrid(total, lg)), dim3(kMergeThreads), 0, st, N, k,
+                     Cf, lg, total, (const T*)feats, coords, scores, members, offsets,
+                     (const T*)dout_f, dout_x, (T*)dfeats, dcoords, dscores);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_merge_plan(const float* coords, const float* scores, int B, int N, int k, int G,
+                             int32_t* anchors, int32_t* assign, int32_t* members,
+                             int32_t* offsets, hipStream_t st) {
+  hipLaunchKernelGGL(merge_plan_kernel, dim3(B), dim3(kPlanT), 0, st, coords, scores, N, k, G,
+                     anchors, assign, members, offsets);
+  return hipGetLastError();
+}
+
+hipError_t launch_merge_fwd(int dt, int B, int N, int k, int Cf, const void* feats,
+                            const float* coords, const float* scores, const int32_t* members,
+                            const int32_t* offsets, void* out_f, float* out_x, hipStream_t st) {
+  switch (dt) {
+    case 0: return fwd_t<float>(B, N, k, Cf, feats, coords, scores, members, offsets, out_f, out_x, st);
+    case 1: return fwd_t<bf16>(B, N, k, Cf, feats, coords, scores, members, offsets, out_f, out_x, st);
+    default: return fwd_t<f16>(B, N, k, Cf, feats, coords, scores, members, offsets, out_f, out_x, st);
+  }
+}
+
+hipError_t launch_merge_bwd(int dt, int B, int N, int k, int Cf, const void* feats,
+                            const float* coords, const float* scores, const int32_t* members,
+                            const int32_t* offsets, const void* dout_f, const float* dout_x,
+                            void* dfeats, float* dcoords, float* dscores, hipStream_t st) {
+  switch (dt) {
+    case 0:
+      return bwd_t<float>(B, N, k, Cf, feats, coords, scores, members, offsets, dout_f, dout_x,
+                          dfeats, dcoords, dscores, st);
+    case 1:
+      return bwd_t<bf16>(B, N, k, Cf, feats, coords, scores, members, offsets, dout_f, dout_x,
+                         dfeats, dcoords, dscores, st);
+    default:
+      return bwd_t<f16>(B, N, k, Cf, feats, coords, scores, members, offsets, dout_f, dout_x,
+                        dfeats, dcoords, dscores, st);
+  }
+}
+
+}  // namespace ca

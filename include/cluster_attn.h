@@ -225,6 +225,61 @@ int cluster_attn_knn_sample_bwd(int dt, int B, int N, int M, int C, int grid_sid
                                 const int32_t* table, const void* dout, void* dfeats, float* dq,
                                 float* dp, void* ws, size_t ws_bytes, void* hip_stream);
 
+/* ------------------------------------------------------------------------
+ * Adaptive off-grid token merging.
+ *
+ * Notes page, "Key Designs" item 1: every token keeps its 2D coordinate; a
+ * lightweight MLP scores the tokens, the top-k by the retention rate are
+ * kept as anchors, and the other tokens are merged, differentiably, into
+ * their nearest anchors, features and spatial support alike ("A Complete
+ * Example": retention 0.4, 2048 -> 819 -> 328 -> 131 tokens).  Readings: the
+ * scores are an input; anchors are the k largest scores (ties to the lower
+ * token index) in ascending token order; an anchor is assigned to itself and
+ * every other token to the anchor nearest by squared distance of the 16-bit
+ * fixed-point coordinates of the neighbour build (ties to the earlier
+ * anchor); within a group the softmax of the members' scores weighs the
+ * features and the coordinates.  N <= 4096 tokens per image; scores finite.
+ * ------------------------------------------------------------------------ */
+
+/*
+ * Plan (exact integers; the unique result of the rules above):
+ *   coords [B, N, 2] f32, scores [B, N] f32.   1 <= k <= N.   grid_side: G.
+ *   anchors [B, k] int32 out: token index of anchor a, ascending.
+ *   assign  [B, N] int32 out: anchor position of every token.
+ *   members [B, N] int32 out, offsets [B, k + 1] int32 out: the tokens of
+ *           group a are members[offsets[a] .. offsets[a+1]), in token order.
+ */
+int cluster_attn_merge_plan(const float* coords, const float* scores, int B, int N, int k,
+                            int grid_side, int32_t* anchors, int32_t* assign, int32_t* members,
+                            int32_t* offsets, void* hip_stream);
+
+/*
+ * Forward: w_i = exp(s_i) / sum over the group of exp(s_j) (max subtracted,
+ * fp32);  out_feats[b, a] = sum_i w_i feats[b, i]  (dt, RNE from fp32),
+ * out_coords[b, a] = sum_i w_i coords[b, i]  (f32).
+ *   feats [B, N, C] dt (16-byte aligned, C a multiple of 8 up to 1024);
+ *   members/offsets as returned by cluster_attn_merge_plan.
+ */
+int cluster_attn_merge_fwd(int dt, int B, int N, int k, int C, const void* feats,
+                           const float* coords, const float* scores, const int32_t* members,
+                           const int32_t* offsets, void* out_feats, float* out_coords,
+                           void* hip_stream);
+
+/*
+ * Backward of L = sum(dout_feats * out_feats) + sum(dout_coords * out_coords)
+ * with the plan held fixed: for token i of group a, with
+ * g_i = <dout_feats[a], feats[i]> + <dout_coords[a], coords[i]>,
+ *   dfeats[i] = w_i dout_feats[a],  dcoords[i] = w_i dout_coords[a],
+ *   dscores[i] = w_i (g_i - sum_{j in a} w_j g_j).
+ * Every token belongs to one group and is written once (no atomics):
+ * bitwise reproducible.  dfeats dt; dcoords, dscores f32.
+ */
+int cluster_attn_merge_bwd(int dt, int B, int N, int k, int C, const void* feats,
+                           const float* coords, const float* scores, const int32_t* members,
+                           const int32_t* offsets, const void* dout_feats,
+                           const float* dout_coords, void* dfeats, float* dcoords,
+                           float* dscores, void* hip_stream);
+
 /* Static text for a status code. */
 const char* cluster_attn_status_string(int status);
 

@@ -177,3 +177,23 @@ def test_knn_validation(lib):
     assert b(1, 2, 100, 50, 128, 16, 8, 1.0, *ten, None, P * 50, need, None) == CA_ERR_NULL
     assert b(1, 2, 100, 50, 128, 16, 8, 1.0, *ten, P * 60, None, need, None) == CA_ERR_NULL
     assert b(1, 2, 100, 50, 128, 16, 8, 1.0, *ten, P * 60, P * 50, need - 1, None) == CA_ERR_WORKSPACE
+
+
+def test_merge_validation(lib):
+    pl = lib.cluster_attn_merge_plan
+    ptr = [P * (i + 1) for i in range(6)]
+    assert pl(*ptr[:2], 2, 5000, 100, 64, *ptr[2:], None) == CA_ERR_UNSUPPORTED   # N > 4096
+    assert pl(*ptr[:2], 2, 100, 0, 64, *ptr[2:], None) == CA_ERR_SHAPE            # k < 1
+    assert pl(*ptr[:2], 2, 100, 101, 64, *ptr[2:], None) == CA_ERR_SHAPE          # k > N
+    assert pl(*ptr[:2], 2, 100, 40, 0, *ptr[2:], None) == CA_ERR_SHAPE            # grid side
+    assert pl(None, P, 2, 100, 40, 64, *ptr[2:], None) == CA_ERR_NULL
+    assert pl(None, None, 0, 100, 40, 64, None, None, None, None, None) == CA_OK
+    fw = lib.cluster_attn_merge_fwd
+    t = [P * (i + 1) for i in range(7)]
+    assert fw(9, 2, 100, 40, 64, *t, None) == CA_ERR_UNSUPPORTED
+    assert fw(1, 2, 100, 40, 60, *t, None) == CA_ERR_UNSUPPORTED                  # C % 8
+    assert fw(1, 2, 100, 40, 64, *t[:6], None, None) == CA_ERR_NULL
+    bw = lib.cluster_attn_merge_bwd
+    u = [P * (i + 1) for i in range(10)]
+    assert bw(1, 2, 100, 140, 64, *u, None) == CA_ERR_SHAPE
+    assert bw(1, 2, 100, 40, 64, *u[:9], None, None) == CA_ERR_NULL
