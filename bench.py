@@ -37,6 +37,8 @@ ENTRY_KERNELS = {
     "bwd": ["plan_small_kernel (small images) | plan_init/inv/count/scan/place/sort_kernel",
             "bwd_q_lds_kernel", "bwd_kv_lds_kernel"],
 }
+MERGE_ENTRY_KERNELS = {"plan": ["merge_plan_kernel"], "fwd": ["merge_fwd_kernel"],
+                       "bwd": ["merge_bwd_kernel"]}
 SAMPLER_ENTRY_KERNELS = {
     "table": ["knn_table_kernel"],
     "fwd": ["knn_fwd_kernel"],
@@ -150,11 +152,14 @@ def main():
     import torch
 
     import gathered_local_attention_amd as ca
-    from gen import SAMPLER_CONFIGS, make_case
+    from gen import MERGE_CONFIGS, SAMPLER_CONFIGS, make_case
 
     ca._lib.load()
     if args.config in SAMPLER_CONFIGS:
         bench_sampler(args, torch, ca)
+        return
+    if args.config in MERGE_CONFIGS:
+        bench_merge(args, torch, ca)
         return
     case = make_case(args.config)
     cfg = case["cfg"]
@@ -448,6 +453,157 @@ def bench_sampler(args, torch, ca):
     }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = sampler_cpu_baseline(cfg, case, min(12, cfg.B))
+    print(json.dumps(line), flush=True)
+
+
+# ---------------------------------------------------------------------------
+# Adaptive token merging: --config merge_stages
+# ---------------------------------------------------------------------------
+
+def merge_algorithmic(cfg):
+    """Compulsory bytes per entry point, summed over the levels."""
+    es = 4 if cfg.dtype == "f32" else 2
+    B = cfg.B
+    out = {"plan": 0, "fwd": 0, "bwd": 0}
+    for N, k, C in cfg.levels:
+        plan_io = N * 12 + k * 4 + N * 8 + (k + 1) * 4
+        lists = N * 4 + (k + 1) * 4
+        out["plan"] += B * plan_io
+        out["fwd"] += B * (N * C * es + N * 12 + lists + k * C * es + k * 8)
+        out["bwd"] += B * (N * C * es + N * 12 + lists + k * C * es + k * 8 + N * C * es + N * 12)
+    return out
+
+
+def merge_cpu_baseline(cfg, case, images: int):
+    """The fp64 oracle (plan + forward + backward, all levels) on `images`
+    images, single-threaded."""
+    from threadpoolctl import threadpool_limits
+
+    import oracle as O
+
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        for li, (N, k, C) in enumerate(cfg.levels):
+            F = case["feats"][li].double().numpy()
+            dF = case["dfeat"][li].double().numpy()
+            for b in range(images):
+                c, s = case["coords"][li][b], case["scores"][li][b]
+                anchors = O.merge_anchors(s, k)
+                assign = O.merge_assign(c, anchors, cfg.G)
+                O.merge_fwd(F[b], c, s, assign, k)
+                O.merge_bwd(F[b], c, s, assign, k, dF[b], case["dcoord"][li][b])
+        dt = time.perf_counter() - t0
+    tokens = images * cfg.levels[0][0]
+    return {
+        "value": tokens / dt,
+        "unit": "tokens/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": f"{images} of {cfg.B} images ({tokens} first-level tokens, {len(cfg.levels)} levels), "
+                  f"fp64 plan+forward+backward, {dt:.1f} s",
+    }
+
+
+def bench_merge(args, torch, ca):
+    from gen import make_merge_case
+
+    case = make_merge_case(args.config)
+    cfg = case["cfg"]
+    dev = "cuda"
+    L = len(cfg.levels)
+    sets = []
+    for r in range(args.copies):
+        sets.append([{"coords": torch.from_numpy(case["coords"][li]).to(dev),
+                      "scores": torch.from_numpy(case["scores"][li]).to(dev),
+                      "feats": case["feats"][li].to(dev), "dfeat": case["dfeat"][li].to(dev),
+                      "dcoord": torch.from_numpy(case["dcoord"][li]).to(dev)} for li in range(L)])
+
+    def step(s):
+        for li, (N, k, C) in enumerate(cfg.levels):
+            lv = s[li]
+            _, _, mem, off = ca.merge_plan(lv["coords"], lv["scores"], k, cfg.G)
+            ca.merge_fwd(lv["feats"], lv["coords"], lv["scores"], mem, off)
+            ca.merge_bwd(lv["feats"], lv["coords"], lv["scores"], mem, off, lv["dfeat"], lv["dcoord"])
+
+    for i in range(args.warmup):
+        step(sets[i % len(sets)])
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(sets[i % len(sets)])
+    torch.cuda.synchronize()
+    ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    n_ev = min(args.steps, 100)
+    plans = [[ca.merge_plan(s[li]["coords"], s[li]["scores"], k, cfg.G)
+              for li, (N, k, C) in enumerate(cfg.levels)] for s in sets]
+    calls = {
+        "plan": lambda i: [ca.merge_plan(sets[i][li]["coords"], sets[i][li]["scores"], k, cfg.G)
+                           for li, (N, k, C) in enumerate(cfg.levels)],
+        "fwd": lambda i: [ca.merge_fwd(sets[i][li]["feats"], sets[i][li]["coords"], sets[i][li]["scores"],
+                                       plans[i][li][2], plans[i][li][3]) for li in range(L)],
+        "bwd": lambda i: [ca.merge_bwd(sets[i][li]["feats"], sets[i][li]["coords"], sets[i][li]["scores"],
+                                       plans[i][li][2], plans[i][li][3], sets[i][li]["dfeat"],
+                                       sets[i][li]["dcoord"]) for li in range(L)],
+    }
+    dur = {}
+    for name, call in calls.items():
+        call(0)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(n_ev):
+            call(i % len(sets))
+        e1.record()
+        torch.cuda.synchronize()
+        dur[name] = e0.elapsed_time(e1) / n_ev * 1e3
+    alg = merge_algorithmic(cfg)
+    dom = max(("plan", "fwd", "bwd"), key=lambda k: dur[k])
+    achieved = alg[dom] / (dur[dom] * 1e-6) / 1e9
+    fb_us = dur["fwd"] + dur["bwd"]
+    tokens = cfg.B * cfg.levels[0][0]
+    line = {
+        "metric": "adaptive token merging plan+fwd+bwd tokens/sec and % of HBM roofline "
+                  "(3 stage transitions)",
+        "value": tokens / (ms_per_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic",
+        "config": {
+            "workload": f"{cfg.name}: B={cfg.B} images, levels (N, k, C) = {list(cfg.levels)}, G={cfg.G}, "
+                        f"{cfg.dtype}; step = per level plan + forward + backward",
+            "B": cfg.B, "levels": [list(x) for x in cfg.levels], "G": cfg.G, "seed": cfg.seed,
+            "rotating_copies": args.copies,
+        },
+        "roofline": {
+            "bound": "hbm",
+            "kernel": {"plan": "cluster_attn_merge_plan", "fwd": "cluster_attn_merge_fwd",
+                       "bwd": "cluster_attn_merge_bwd"}[dom],
+            "entry_point_kernels": MERGE_ENTRY_KERNELS[dom],
+            "achieved": achieved,
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBPS,
+            "traffic": None,
+            "algorithmic_bytes": alg[dom],
+            "avg_us": dur[dom],
+        },
+        "fwd_bwd": {
+            "us": fb_us,
+            "effective_GBps": (alg["fwd"] + alg["bwd"]) / (fb_us * 1e-6) / 1e9,
+            "hbm_frac": (alg["fwd"] + alg["bwd"]) / (fb_us * 1e-6) / 1e9 / HBM_PEAK_GBPS,
+        },
+        "entry_us": dur,
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = merge_cpu_baseline(cfg, case, cfg.B)
     print(json.dumps(line), flush=True)
 
 

@@ -19,11 +19,12 @@
 //
 // Kernels:
 //   merge_plan_kernel  one workgroup per image (up to 4096 tokens, all in
-//                      LDS): ranks by counting (score, index), anchors by a
-//                      workgroup scan in token order, nearest anchors by a
-//                      scan of the anchor list (fp32 screen, exact int64
-//                      keys), and the groups' member lists by a bitonic sort
-//                      of (anchor, token) keys: members in token order.
+//                      LDS): top-k by a radix select of the score keys,
+//                      anchors by a workgroup scan in token order, nearest
+//                      anchors by a ring search over a bucket grid of the
+//                      anchors (exact int64 keys), and the groups' member
+//                      lists by a counting sort on the anchor, each group
+//                      then sorted by token index.
 //   merge_fwd_kernel   a lane group per anchor (16 bytes of the row per
 //                      lane): the group's softmax, then the weighted sums.
 //   merge_bwd_kernel   the same groups: g_i = <dF'_a, F_i> + <dX'_a, X_i>
@@ -76,17 +77,37 @@ template <> struct Row16<f16> : Row16Half<f16, mf16x8> {};
 constexpr int kMaxChunks = 4;   // chunks of 16 bytes per lane (1024 channels of f32)
 
 // ---------------------------------------------------------------------------
-// Plan: anchors, assignment, member lists.  grid = B, 1024 threads.
+// Plan: anchors, assignment, member lists.  grid = B, 1024 threads, the
+// image in LDS.
+//  1. top-k by a radix select on order-preserving 32-bit keys of the scores
+//     (8-bit digits from the top): the k-th largest key, then the tokens
+//     above it and the first ones (in token order) equal to it;
+//  2. anchor positions by a workgroup scan in token order;
+//  3. the anchors bucketed on a coarse grid (about two per bucket); every
+//     other token searches rings of buckets around its own until its best
+//     is strictly closer than anything outside the searched window can be;
+//  4. member lists by a counting sort on the anchor (LDS atomics), each
+//     group's members then sorted by token index (a thread per group when
+//     no group exceeds 32 tokens, else a bitonic sort of all the keys).
 // ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t score_key(float x) {
+  // larger float -> larger key; -0 and +0 share one key (they compare equal)
+  const uint32_t u = __float_as_uint(x == 0.f ? 0.f : x);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
 __global__ void __launch_bounds__(kPlanT)
 merge_plan_kernel(const float* __restrict__ coords, const float* __restrict__ scores, int N, int k,
                   int G, int32_t* __restrict__ anchors, int32_t* __restrict__ assign,
                   int32_t* __restrict__ members, int32_t* __restrict__ offsets) {
-  __shared__ __align__(16) float sc[kMaxTok];
-  __shared__ __align__(16) uint32_t qc[kMaxTok];     // token fixed-point (qx | qy << 16)
-  __shared__ __align__(16) uint32_t ac[kMaxTok];     // anchor fixed-point, by position
+  __shared__ uint32_t sk[kMaxTok];                    // score keys
+  __shared__ uint32_t qc[kMaxTok];                    // token fixed-point (qx | qy << 16)
   __shared__ int32_t apos[kMaxTok];                   // token -> anchor position, or -1
-  __shared__ uint32_t key[kMaxTok];                   // (assign << 12 | token), sorted
+  __shared__ uint2 abk[kMaxTok];                      // anchors in bucket order: (qc, position)
+  __shared__ int32_t bstart[kMaxTok];                 // bucket starts (<= 4096 buckets)
+  __shared__ uint32_t key[kMaxTok];                   // group counts, then sort keys
+  __shared__ int hist[256];
+  __shared__ uint32_t sel[2];                         // selected prefix, still wanted
   __shared__ int tmp[17];
   const int b = blockIdx.x, tid = threadIdx.x;
   const int bits = [&] { int v = 0; while ((1 << v) < G) ++v; return v; }();
@@ -94,103 +115,244 @@ merge_plan_kernel(const float* __restrict__ coords, const float* __restrict__ sc
   const float* s = scores + (int64_t)b * N;
   const float2* xy = reinterpret_cast<const float2*>(coords) + (int64_t)b * N;
   for (int i = tid; i < N; i += kPlanT) {
-    sc[i] = s[i];
+    sk[i] = score_key(s[i]);
     const float2 c = xy[i];
     qc[i] = quantize_axis(c.x, step) | (quantize_axis(c.y, step) << 16);
   }
-  __syncthreads();
-
-  // rank of token i by (score descending, index ascending); anchor iff < k.
-  // Thread t owns tokens 4t .. 4t+3 (consecutive: the scan below is in
-  // token order).
+  if (tid == 0) {
+    sel[0] = 0u;
+    sel[1] = (uint32_t)k;
+  }
+  // 1. radix select of the k-th largest key
+  for (int dg = 3; dg >= 0; --dg) {
+    if (tid < 256) hist[tid] = 0;
+    __syncthreads();
+    const uint32_t pre = sel[0];
+    const uint32_t hmask = dg == 3 ? 0u : (0xFFFFFFFFu << (8 * (dg + 1)));
+    for (int i = tid; i < N; i += kPlanT)
+      if ((sk[i] & hmask) == pre) atomicAdd(&hist[(sk[i] >> (8 * dg)) & 255u], 1);
+    __syncthreads();
+    if (tid < 64) {
+      // the digit where the count from the top reaches `want`: lane l holds
+      // bins 255 - 4l .. 252 - 4l, a wave scan gives the counts above them
+      const uint32_t want = sel[1];
+      int h[4];
+      int sum = 0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        h[j] = hist[255 - 4 * tid - j];
+        sum += h[j];
+      }
+      const int incl = wave_inclusive_scan(sum);
+      int cum = incl - sum;
+      if ((uint32_t)cum < want && (uint32_t)incl >= want) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          if ((uint32_t)(cum + h[j]) >= want) {
+            sel[0] = pre | ((uint32_t)(255 - 4 * tid - j) << (8 * dg));
+            sel[1] = want - (uint32_t)cum;
+            break;
+          }
+          cum += h[j];
+        }
+      }
+    }
+    __syncthreads();
+  }
+  const uint32_t kth = sel[0], n_eq = sel[1];   // take n_eq of the keys equal to kth
+  // 2. flags in token order (thread t owns tokens 4t .. 4t+3), then positions
   constexpr int R = kMaxTok / kPlanT;
+  int eq_local = 0;
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int i = tid * R + r;
+    eq_local += (i < N && sk[i] == kth) ? 1 : 0;
+  }
+  int tot;
+  int eq_before = block_exclusive_scan(eq_local, tmp, kPlanT, &tot);
   bool an[R];
-  int nan_ = 0;
+  int n_an = 0;
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     const int i = tid * R + r;
     an[r] = false;
     if (i < N) {
-      const float si = sc[i];
-      int rank = 0;
-      for (int j = 0; j < N; ++j) {
-        const float sj = sc[j];
-        rank += (sj > si || (sj == si && j < i)) ? 1 : 0;
-      }
-      an[r] = rank < k;
+      if (sk[i] > kth) an[r] = true;
+      else if (sk[i] == kth) an[r] = (uint32_t)(eq_before++) < n_eq;
     }
-    nan_ += an[r] ? 1 : 0;
+    n_an += an[r] ? 1 : 0;
   }
-  int tot;
-  int pos = block_exclusive_scan(nan_, tmp, kPlanT, &tot);
+  __syncthreads();   // tmp is reused by the next scan
+  int pos = block_exclusive_scan(n_an, tmp, kPlanT, &tot);
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     const int i = tid * R + r;
     if (i < N) {
       apos[i] = an[r] ? pos : -1;
-      if (an[r]) {
-        anchors[(int64_t)b * k + pos] = i;
-        ac[pos] = qc[i];
-        ++pos;
-      }
+      if (an[r]) anchors[(int64_t)b * k + pos++] = i;
+    }
+  }
+  // 3. anchors bucketed: side 2^bsh fixed-point units, about two per bucket
+  int pb = 0;
+  while (pb < 6 && (1 << (2 * pb + 2)) <= max(k, 1) / 2) ++pb;
+  const int bsh = 16 - pb, Pb = 1 << pb, nb = Pb * Pb;
+  for (int x = tid; x < nb; x += kPlanT) bstart[x] = 0;
+  __syncthreads();
+  int abkt[R], arank[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int i = tid * R + r;
+    abkt[r] = -1;
+    if (i < N && an[r]) {
+      const uint32_t q = qc[i];
+      abkt[r] = (int)(((q >> 16) >> bsh) * (uint32_t)Pb + ((q & 0xFFFFu) >> bsh));
+      arank[r] = atomicAdd(&bstart[abkt[r]], 1);
     }
   }
   __syncthreads();
-
-  // nearest anchor: fp32 screen (coordinates < 2^16, exact as floats; a
-  // relative bound of 2^-20 keeps every candidate at or below the best),
-  // exact (d2 << 12 | position) keys in 64 bits
-  for (int i = tid; i < N; i += kPlanT) {
+  int cnt[R];
+  int run = 0;
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int x = tid * R + r;
+    cnt[r] = x < nb ? bstart[x] : 0;
+    run += cnt[r];
+  }
+  __syncthreads();
+  int acc = block_exclusive_scan(run, tmp, kPlanT, &tot);
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int x = tid * R + r;
+    if (x < nb) bstart[x] = acc;
+    acc += cnt[r];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int i = tid * R + r;
+    if (abkt[r] >= 0) abk[bstart[abkt[r]] + arank[r]] = make_uint2(qc[i], (uint32_t)apos[i]);
+  }
+  __syncthreads();
+  // nearest anchor of every other token: rings of buckets around its own;
+  // keys (d2 << 12 | position) exact in 64 bits
+  int ga[R], gslot[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) ga[r] = -1;
+  __syncthreads();   // key[] holds the group counts below
+  for (int x = tid; x < k; x += kPlanT) key[x] = 0u;
+  __syncthreads();
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int i = tid + r * kPlanT;
+    if (i >= N) break;
     int a = apos[i];
     if (a < 0) {
       const uint32_t q = qc[i];
       const int64_t x = q & 0xFFFFu, y = q >> 16;
-      const float fx = (float)x, fy = (float)y;
+      const int bx0 = (int)(x >> bsh), by0 = (int)(y >> bsh);
       uint64_t best = ~0ull;
-      float thr = INFINITY;
-      for (int p = 0; p < k; ++p) {
-        const uint32_t c = ac[p];
-        const float dx = (float)(c & 0xFFFFu) - fx, dy = (float)(c >> 16) - fy;
-        if (fmaf(dx, dx, dy * dy) > thr) continue;
-        const int64_t ix = (int64_t)(c & 0xFFFFu) - x, iy = (int64_t)(c >> 16) - y;
-        const uint64_t kk = ((uint64_t)(ix * ix + iy * iy) << 12) | (uint32_t)p;
-        if (kk < best) {
-          best = kk;
-          thr = (float)(best >> 12) * (1.0f + 0x1p-20f);
+      for (int Rg = 0; Rg < Pb; ++Rg) {
+        const int y0 = by0 - Rg, y1 = by0 + Rg;
+        for (int by = max(y0, 0); by <= min(y1, Pb - 1); ++by) {
+          const bool edge = by == y0 || by == y1;
+          const int dxs = (edge || Rg == 0) ? 1 : 2 * Rg;
+          for (int bx = bx0 - Rg; bx <= bx0 + Rg; bx += dxs) {
+            if (bx < 0 || bx >= Pb) continue;
+            const int bb = by * Pb + bx;
+            const int t0 = bstart[bb], t1 = bb + 1 < nb ? bstart[bb + 1] : k;
+            for (int t = t0; t < t1; ++t) {
+              const uint2 e = abk[t];
+              const int64_t ix = (int64_t)(e.x & 0xFFFFu) - x, iy = (int64_t)(e.x >> 16) - y;
+              const uint64_t kk = ((uint64_t)(ix * ix + iy * iy) << 12) | e.y;
+              best = kk < best ? kk : best;
+            }
+          }
         }
+        // a token outside the searched window lies beyond one of its edges
+        int64_t lb = INT64_MAX;
+        if (y0 > 0) lb = min(lb, y - ((int64_t)y0 << bsh) + 1);
+        if (y1 < Pb - 1) lb = min(lb, ((int64_t)(y1 + 1) << bsh) - y);
+        if (bx0 - Rg > 0) lb = min(lb, x - ((int64_t)(bx0 - Rg) << bsh) + 1);
+        if (bx0 + Rg < Pb - 1) lb = min(lb, ((int64_t)(bx0 + Rg + 1) << bsh) - x);
+        if (best != ~0ull && (lb == INT64_MAX || (int64_t)(best >> 12) < lb * lb)) break;
       }
       a = (int)(best & 0xFFFu);
     }
     assign[(int64_t)b * N + i] = a;
-    key[i] = ((uint32_t)a << 12) | (uint32_t)i;
+    ga[r] = a;
+    gslot[r] = (int)atomicAdd(&key[a], 1u);   // arrival order; fixed by the sort below
   }
-  // members: bitonic sort of the keys (padded with the maximum)
-  int P2 = 1;
-  while (P2 < N) P2 <<= 1;
-  for (int i = N + tid; i < P2; i += kPlanT) key[i] = 0xFFFFFFFFu;
+  // 4. members: group starts by a scan of the counts, members placed in
+  //    arrival order, then every group's few members sorted by token index
   __syncthreads();
-  for (int kk = 2; kk <= P2; kk <<= 1) {
-    for (int j = kk >> 1; j > 0; j >>= 1) {
-      for (int i = tid; i < P2 / 2; i += kPlanT) {
-        const int lo = ((i & ~(j - 1)) << 1) | (i & (j - 1));
-        const uint32_t x = key[lo], y = key[lo + j];
-        if ((x > y) == ((lo & kk) == 0)) {
-          key[lo] = y;
-          key[lo + j] = x;
-        }
-      }
-      __syncthreads();
-    }
+  int gc[R];
+  int grun = 0;
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int x = tid * R + r;
+    gc[r] = x < k ? (int)key[x] : 0;
+    grun += gc[r];
   }
-  int32_t* mem = members + (int64_t)b * N;
+  __syncthreads();
+  int gacc = block_exclusive_scan(grun, tmp, kPlanT, &tot);
   int32_t* off = offsets + (int64_t)b * (k + 1);
-  for (int i = tid; i < N; i += kPlanT) {
-    const uint32_t kv = key[i];
-    mem[i] = (int32_t)(kv & 0xFFFu);
-    const int g = (int)(kv >> 12);
-    if (i == 0 || (key[i - 1] >> 12) != (uint32_t)g) off[g] = i;   // every group holds its anchor
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int x = tid * R + r;
+    if (x < k) {
+      bstart[x] = gacc;   // bucket starts are no longer needed
+      off[x] = gacc;
+    }
+    gacc += gc[r];
   }
   if (tid == 0) off[k] = N;
+  __syncthreads();
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+    if (ga[r] >= 0) sk[bstart[ga[r]] + gslot[r]] = (uint32_t)(tid + r * kPlanT);   // score keys are done
+  __syncthreads();
+  int32_t* mem = members + (int64_t)b * N;
+  int gmax = 0;
+#pragma unroll
+  for (int r = 0; r < R; ++r) gmax = max(gmax, gc[r]);
+  if (__syncthreads_or(gmax > 32)) {
+    // some group is large: bitonic sort of all (group << 12 | token) keys
+    int P2 = 1;
+    while (P2 < N) P2 <<= 1;
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+      if (ga[r] >= 0) key[tid + r * kPlanT] = ((uint32_t)ga[r] << 12) | (uint32_t)(tid + r * kPlanT);
+    for (int i = N + tid; i < P2; i += kPlanT) key[i] = 0xFFFFFFFFu;
+    __syncthreads();
+    for (int kk = 2; kk <= P2; kk <<= 1) {
+      for (int j = kk >> 1; j > 0; j >>= 1) {
+        for (int i = tid; i < P2 / 2; i += kPlanT) {
+          const int lo = ((i & ~(j - 1)) << 1) | (i & (j - 1));
+          const uint32_t xk = key[lo], yk = key[lo + j];
+          if ((xk > yk) == ((lo & kk) == 0)) {
+            key[lo] = yk;
+            key[lo + j] = xk;
+          }
+        }
+        __syncthreads();
+      }
+    }
+    for (int i = tid; i < N; i += kPlanT) mem[i] = (int32_t)(key[i] & 0xFFFu);
+    return;
+  }
+  for (int g = tid; g < k; g += kPlanT) {
+    const int g0 = bstart[g], g1 = g + 1 < k ? bstart[g + 1] : N;
+    for (int u = g0 + 1; u < g1; ++u) {   // insertion sort of at most 32 tokens
+      const uint32_t v = sk[u];
+      int y = u - 1;
+      while (y >= g0 && sk[y] > v) {
+        sk[y + 1] = sk[y];
+        --y;
+      }
+      sk[y + 1] = v;
+    }
+    for (int u = g0; u < g1; ++u) mem[u] = (int32_t)sk[u];
+  }
 }
 
 // Lane groups: L = 2^lg lanes per anchor, 64 / L anchors per wave.
