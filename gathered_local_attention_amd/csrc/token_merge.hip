@@ -371,13 +371,27 @@ __device__ __forceinline__ MGroup mgroup(int lg, int64_t total) {
   return g;
 }
 
-// softmax statistics of a group's scores: max and 1 / sum of exp
+// softmax statistics of a group's scores: max and 1 / sum of exp.  Members
+// are read four at a time with clamped indices (every load of a batch
+// issues together), the extra ones masked.
+constexpr int kMB = 4;
 __device__ __forceinline__ void group_softmax(const int32_t* __restrict__ mem, int a, int z,
                                               const float* __restrict__ s, float& mx, float& inv) {
   mx = -INFINITY;
-  for (int u = a; u < z; ++u) mx = fmaxf(mx, s[mem[u]]);
   float sum = 0.f;
-  for (int u = a; u < z; ++u) sum += __builtin_amdgcn_exp2f((s[mem[u]] - mx) * 1.4426950408889634f);
+  for (int u = a; u < z; u += kMB) {
+    float v[kMB];
+#pragma unroll
+    for (int h = 0; h < kMB; ++h) v[h] = s[mem[min(u + h, z - 1)]];
+    float m2 = mx;
+#pragma unroll
+    for (int h = 0; h < kMB; ++h) m2 = u + h < z ? fmaxf(m2, v[h]) : m2;
+    sum *= __builtin_amdgcn_exp2f((mx - m2) * 1.4426950408889634f);   // rescale to the new max
+    mx = m2;
+#pragma unroll
+    for (int h = 0; h < kMB; ++h)
+      sum += u + h < z ? __builtin_amdgcn_exp2f((v[h] - mx) * 1.4426950408889634f) : 0.f;
+  }
   inv = sum > 0.f ? 1.f / sum : 0.f;
 }
 
@@ -407,21 +421,35 @@ merge_fwd_kernel(int N, int k, int Cf, int lg, int64_t total, const T* __restric
 #pragma unroll
     for (int e = 0; e < Rw::E; ++e) acc[r][e] = 0.f;
   float ax = 0.f, ay = 0.f;
-  for (int u = a; u < z; ++u) {
-    const int i = mem[u];
-    const float w = __builtin_amdgcn_exp2f((s[i] - mx) * 1.4426950408889634f) * inv;
+  const int nr = (nch - g.sub + L - 1) / L;   // chunks of this lane
+  for (int u = a; u < z; u += kMB) {   // four members at a time, loads first
+    int mi[kMB];
+    float w[kMB];
+#pragma unroll
+    for (int h = 0; h < kMB; ++h) mi[h] = mem[min(u + h, z - 1)];
+#pragma unroll
+    for (int h = 0; h < kMB; ++h)
+      w[h] = u + h < z ? __builtin_amdgcn_exp2f((s[mi[h]] - mx) * 1.4426950408889634f) * inv : 0.f;
+    float2 x[kMB];
+#pragma unroll
+    for (int h = 0; h < kMB; ++h) x[h] = xy[mi[h]];
 #pragma unroll
     for (int r = 0; r < kMaxChunks; ++r) {
+      if (r >= nr) break;
       const int c = g.sub + r * L;
-      if (c >= nch) break;
-      float v[Rw::E];
-      Rw::load(fimg + (int64_t)i * Cf + c * Rw::E, v);
+      float v[kMB][Rw::E];
 #pragma unroll
-      for (int e = 0; e < Rw::E; ++e) acc[r][e] = fmaf(w, v[e], acc[r][e]);
+      for (int h = 0; h < kMB; ++h) Rw::load(fimg + (int64_t)mi[h] * Cf + c * Rw::E, v[h]);
+#pragma unroll
+      for (int h = 0; h < kMB; ++h)
+#pragma unroll
+        for (int e = 0; e < Rw::E; ++e) acc[r][e] = fmaf(w[h], v[h][e], acc[r][e]);
     }
-    const float2 x = xy[i];
-    ax = fmaf(w, x.x, ax);
-    ay = fmaf(w, x.y, ay);
+#pragma unroll
+    for (int h = 0; h < kMB; ++h) {
+      ax = fmaf(w[h], x[h].x, ax);
+      ay = fmaf(w[h], x[h].y, ay);
+    }
   }
 #pragma unroll
   for (int r = 0; r < kMaxChunks; ++r) {
@@ -463,30 +491,49 @@ merge_bwd_kernel(int N, int k, int Cf, int lg, int64_t total, const T* __restric
   }
   const float2 dox = reinterpret_cast<const float2*>(dout_x)[id];
   float gbar = 0.f;
-  for (int u = a; u < z; ++u) {   // same trip count for the whole group
-    const int i = mem[u];
-    const float w = __builtin_amdgcn_exp2f((s[i] - mx) * 1.4426950408889634f) * inv;
-    float dot = 0.f;
+  const int nr = (nch - g.sub + L - 1) / L;   // chunks of this lane
+  for (int u = a; u < z; u += kMB) {   // same trip count for the whole group
+    int mi[kMB];
+    float w[kMB], dot[kMB];
+#pragma unroll
+    for (int h = 0; h < kMB; ++h) mi[h] = mem[min(u + h, z - 1)];
+#pragma unroll
+    for (int h = 0; h < kMB; ++h) {
+      w[h] = u + h < z ? __builtin_amdgcn_exp2f((s[mi[h]] - mx) * 1.4426950408889634f) * inv : 0.f;
+      dot[h] = 0.f;
+    }
+    float2 x[kMB];
+#pragma unroll
+    for (int h = 0; h < kMB; ++h) x[h] = xy[mi[h]];
 #pragma unroll
     for (int r = 0; r < kMaxChunks; ++r) {
+      if (r >= nr) break;
       const int c = g.sub + r * L;
-      if (c >= nch) break;
-      float v[Rw::E], d[Rw::E];
-      Rw::load(fimg + (int64_t)i * Cf + c * Rw::E, v);
+      float v[kMB][Rw::E];
 #pragma unroll
-      for (int e = 0; e < Rw::E; ++e) {
-        dot = fmaf(dof[r][e], v[e], dot);
-        d[e] = w * dof[r][e];
+      for (int h = 0; h < kMB; ++h) Rw::load(fimg + (int64_t)mi[h] * Cf + c * Rw::E, v[h]);
+#pragma unroll
+      for (int h = 0; h < kMB; ++h) {
+        float d[Rw::E];
+#pragma unroll
+        for (int e = 0; e < Rw::E; ++e) {
+          dot[h] = fmaf(dof[r][e], v[h][e], dot[h]);
+          d[e] = w[h] * dof[r][e];
+        }
+        if (g.valid && u + h < z) Rw::store(dfeats + (b * N + mi[h]) * Cf + c * Rw::E, d);
       }
-      if (g.valid) Rw::store(dfeats + (b * N + i) * Cf + c * Rw::E, d);
     }
-    for (int o = 1; o < L; o <<= 1) dot += __shfl_xor(dot, o, 64);
-    const float2 x = xy[i];
-    const float gi = dot + dox.x * x.x + dox.y * x.y;
-    gbar = fmaf(w, gi, gbar);
-    if (g.valid && g.sub == 0) {
-      dscores[b * N + i] = gi;   // g_i for now; finished below by the same lane
-      reinterpret_cast<float2*>(dcoords)[b * N + i] = make_float2(w * dox.x, w * dox.y);
+    for (int o = 1; o < L; o <<= 1)
+#pragma unroll
+      for (int h = 0; h < kMB; ++h) dot[h] += __shfl_xor(dot[h], o, 64);
+#pragma unroll
+    for (int h = 0; h < kMB; ++h) {
+      const float gi = dot[h] + dox.x * x[h].x + dox.y * x[h].y;
+      gbar = fmaf(w[h], gi, gbar);
+      if (g.valid && g.sub == 0 && u + h < z) {
+        dscores[b * N + mi[h]] = gi;   // g_i for now; finished below by the same lane
+        reinterpret_cast<float2*>(dcoords)[b * N + mi[h]] = make_float2(w[h] * dox.x, w[h] * dox.y);
+      }
     }
   }
   if (!g.valid || g.sub != 0) return;
