@@ -16,10 +16,14 @@ from .cluster_attention import (  # noqa: F401
     morton_code,
     balanced_clusters,
     centroid_sums,
+    cluster_rows,
+    centroid_keys,
     nearest_clusters,
     nearest_clusters_fullsort,
     key_lists,
     build_neighbors,
+    build_image,
+    build_neighbors_varlen,
     count_matrix,
     attn_fwd_dense,
     attn_fwd_gathered,

@@ -30,7 +30,16 @@ precision open.  The readings taken here (all listed in the design doc):
 5. attention is plain scaled-dot-product softmax attention restricted to the
    gathered key slots, scale supplied by the caller (1/sqrt(D) in every
    workload), a repeated slot counting with multiplicity, slot -1 masked;
-6. LSE is the natural log-sum-exp of the scaled logits.
+6. LSE is the natural log-sum-exp of the scaled logits;
+7. ragged images: when N is not a multiple of cs the last run of the order
+   is one partial cluster of n = N - cs*(C-1) members (C = ceil(N/cs)); its
+   q_idx row, and every key slot standing for an absent member, is -1.
+   Clusters are compared through their centroids (means), written as exact
+   integers by scaling every coordinate sum by L/n with L = lcm(1..cs)
+   (840 for cs = 8), which for full clusters is a constant factor and so
+   leaves the full-cluster order unchanged.  Images of different sizes are
+   packed one after another (per-image token and cluster offsets) and then
+   use batch-global token and cluster ids.
 
 Forward and backward are exact softmax attention, so the oracle writes the
 plain definition (a count-masked dense form and an equivalent per-cluster
@@ -40,6 +49,8 @@ steps, in order.  All floating point is fp64; integer steps are exact.
 
 from __future__ import annotations
 
+import math
+
 import numpy as np
 
 __all__ = [
@@ -47,10 +58,14 @@ __all__ = [
     "morton_code",
     "balanced_clusters",
     "centroid_sums",
+    "cluster_rows",
+    "centroid_keys",
     "nearest_clusters",
     "nearest_clusters_fullsort",
     "key_lists",
     "build_neighbors",
+    "build_image",
+    "build_neighbors_varlen",
     "count_matrix",
     "attn_fwd_dense",
     "attn_fwd_gathered",
@@ -121,19 +136,44 @@ def centroid_sums(perm: np.ndarray, qx: np.ndarray, qy: np.ndarray, cs: int) -> 
     return np.stack([qx[members].sum(axis=1), qy[members].sum(axis=1)], axis=1)
 
 
+def cluster_rows(perm: np.ndarray, cs: int) -> np.ndarray:
+    """Reading 7: the order cut into runs of cs, the last run padded with -1.
+    Returns q_idx [ceil(N/cs), cs] int64."""
+    perm = np.asarray(perm, dtype=np.int64)
+    N = perm.shape[0]
+    C = -(-N // cs)
+    rows = np.full(C * cs, -1, dtype=np.int64)
+    rows[:N] = perm
+    return rows.reshape(C, cs)
+
+
+def centroid_keys(q_idx: np.ndarray, qx: np.ndarray, qy: np.ndarray, cs: int) -> np.ndarray:
+    """Reading 7: every cluster's mean fixed-point coordinate times
+    L = lcm(1..cs), as exact integers: (sum of the n members) * (L / n).
+    [C, 2] int64 (below 2**26 for cs = 8, so squared distances fit int64)."""
+    L = math.lcm(*range(1, cs + 1))
+    live = q_idx >= 0
+    safe = np.where(live, q_idx, 0)
+    n = live.sum(axis=1)                      # members per cluster, >= 1
+    sx = np.where(live, qx[safe], 0).sum(axis=1)
+    sy = np.where(live, qy[safe], 0).sum(axis=1)
+    return np.stack([sx * (L // n), sy * (L // n)], axis=1).astype(np.int64)
+
+
 def _sq_dist(S: np.ndarray, rows: np.ndarray) -> np.ndarray:
     dx = S[rows, 0][:, None] - S[None, :, 0]
     dy = S[rows, 1][:, None] - S[None, :, 1]
-    return dx * dx + dy * dy  # exact int64: |d|^2 < 2**40
+    return dx * dx + dy * dy  # exact int64 (scaled sums below 2**26)
 
 
 def nearest_clusters(S: np.ndarray, k: int, block: int = 512) -> np.ndarray:
     """Reading 4: slot 0 = self, then the k-1 other clusters with the smallest
-    (squared centroid-sum distance, cluster index), ascending; -1 pads when
+    (squared centroid distance, cluster index), ascending; -1 pads when
     the image has fewer than k clusters.  Returns [C, k] int64.
 
-    Brute force over all clusters of the image; the (d2, index) pair is
-    folded into one int64 key d2*C + index so the order is total."""
+    Brute force over all clusters of the image: every cluster whose distance
+    is at most the (k-1)-th smallest is a candidate (ties included), and the
+    candidates, listed by index, are sorted stably by distance."""
     C = S.shape[0]
     out = np.full((C, k), -1, dtype=np.int64)
     out[:, 0] = np.arange(C)
@@ -143,12 +183,12 @@ def nearest_clusters(S: np.ndarray, k: int, block: int = 512) -> np.ndarray:
     for r0 in range(0, C, block):
         rows = np.arange(r0, min(C, r0 + block))
         d2 = _sq_dist(S, rows)
-        key = d2 * C + np.arange(C)[None, :]
-        key[np.arange(rows.size), rows] = np.iinfo(np.int64).max  # exclude self
-        part = np.argpartition(key, take - 1, axis=1)[:, :take]
-        pk = np.take_along_axis(key, part, axis=1)
-        order = np.argsort(pk, axis=1)
-        out[rows, 1:1 + take] = np.take_along_axis(part, order, axis=1)
+        d2[np.arange(rows.size), rows] = np.iinfo(np.int64).max  # exclude self
+        kth = np.partition(d2, take - 1, axis=1)[:, take - 1]
+        for i, r in enumerate(rows):
+            cand = np.nonzero(d2[i] <= kth[i])[0]
+            order = cand[np.argsort(d2[i, cand], kind="stable")]
+            out[r, 1:1 + take] = order[:take]
     return out
 
 
@@ -169,10 +209,13 @@ def nearest_clusters_fullsort(S: np.ndarray, k: int) -> np.ndarray:
 
 
 def key_lists(perm: np.ndarray, nbr: np.ndarray, cs: int) -> tuple[np.ndarray, np.ndarray]:
-    """q_idx[c, m] = perm[c*cs + m]; key_idx[c, s*cs + m] = perm[nbr[c,s]*cs + m]
-    (or -1 where nbr is -1).  Returns int64 arrays [C, cs] and [C, k*cs]."""
+    """q_idx[c, m] = perm[c*cs + m] (-1 past the end of the order);
+    key_idx[c, s*cs + m] = q_idx[nbr[c,s], m] (or -1 where nbr is -1).
+    ``perm`` may be given as the order [N] or as q_idx rows [C, cs].
+    Returns int64 arrays [C, cs] and [C, k*cs]."""
     C, k = nbr.shape
-    q_idx = perm.reshape(C, cs)
+    perm = np.asarray(perm, dtype=np.int64)
+    q_idx = perm if perm.ndim == 2 else cluster_rows(perm, cs)
     key_idx = np.full((C, k * cs), -1, dtype=np.int64)
     for s in range(k):
         valid = nbr[:, s] >= 0
@@ -180,30 +223,61 @@ def key_lists(perm: np.ndarray, nbr: np.ndarray, cs: int) -> tuple[np.ndarray, n
     return q_idx, key_idx
 
 
-def build_neighbors(coords: np.ndarray, grid_side: int, cs: int = 8, k: int = 6):
-    """Whole neighbour build for a batch.
+def build_image(coords: np.ndarray, grid_side: int, cs: int = 8, k: int = 6):
+    """Readings 1-4 and 7 for one image of any size N >= 0: returns q_idx
+    [C, cs], nbr [C, k] and key_idx [C, k*cs] (int64, image-local ids,
+    C = ceil(N/cs), -1 padding)."""
+    coords = np.asarray(coords)
+    qx, qy = quantize(coords, grid_side)
+    perm = balanced_clusters(morton_code(qx, qy))
+    q_idx = cluster_rows(perm, cs)
+    S = centroid_keys(q_idx, qx, qy, cs)
+    nbr = nearest_clusters(S, k)
+    _, key_idx = key_lists(q_idx, nbr, cs)
+    return q_idx, nbr, key_idx
 
-    coords [B, N, 2] float32  ->  perm [B, N], nbr [B, C, k],
-    key_idx [B, C, k*cs], all int32 and image-local.  N must be a multiple
-    of cs."""
+
+def build_neighbors(coords: np.ndarray, grid_side: int, cs: int = 8, k: int = 6):
+    """Whole neighbour build for a batch of equal-size images.
+
+    coords [B, N, 2] float32  ->  perm [B, C*cs] (the q_idx rows [B, C, cs]
+    flattened; equal to the token order when cs divides N, -1 padded
+    otherwise), nbr [B, C, k], key_idx [B, C, k*cs], all int32 and
+    image-local, C = ceil(N/cs)."""
     coords = np.asarray(coords)
     B, N, two = coords.shape
-    assert two == 2 and N % cs == 0
-    C = N // cs
-    perm = np.empty((B, N), dtype=np.int32)
+    assert two == 2
+    C = -(-N // cs)
+    perm = np.empty((B, C * cs), dtype=np.int32)
     nbr = np.empty((B, C, k), dtype=np.int32)
     key_idx = np.empty((B, C, k * cs), dtype=np.int32)
     for b in range(B):
-        qx, qy = quantize(coords[b], grid_side)
-        code = morton_code(qx, qy)
-        p = balanced_clusters(code)
-        S = centroid_sums(p, qx, qy, cs)
-        nb = nearest_clusters(S, k)
-        _, kl = key_lists(p, nb, cs)
-        perm[b] = p
+        qi, nb, kl = build_image(coords[b], grid_side, cs, k)
+        perm[b] = qi.reshape(-1)
         nbr[b] = nb
         key_idx[b] = kl
     return perm, nbr, key_idx
+
+
+def build_neighbors_varlen(coords: np.ndarray, lengths, grid_side: int, cs: int = 8, k: int = 6):
+    """Reading 7, packed batch: coords [T, 2] float32 holds the images one
+    after another, image b having lengths[b] tokens.  Every image is built
+    on its own; the results are concatenated with batch-global ids (token
+    ids offset by the image's first token, cluster ids by its first
+    cluster).  Returns q_idx [Ct, cs], nbr [Ct, k], key_idx [Ct, k*cs]
+    (int32, -1 padding), tok_off [B+1] and clu_off [B+1] (int64)."""
+    coords = np.asarray(coords)
+    lengths = [int(n) for n in lengths]
+    tok_off = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int64)
+    clu_off = np.concatenate([[0], np.cumsum([-(-n // cs) for n in lengths])]).astype(np.int64)
+    qs, ns, ks = [], [], []
+    for b, n in enumerate(lengths):
+        qi, nb, kl = build_image(coords[tok_off[b]:tok_off[b + 1]], grid_side, cs, k)
+        qs.append(np.where(qi >= 0, qi + tok_off[b], -1))
+        ns.append(np.where(nb >= 0, nb + clu_off[b], -1))
+        ks.append(np.where(kl >= 0, kl + tok_off[b], -1))
+    cat = lambda xs, w: (np.concatenate(xs) if xs else np.zeros((0, w), np.int64)).astype(np.int32)
+    return cat(qs, cs), cat(ns, k), cat(ks, k * cs), tok_off, clu_off
 
 
 # ---------------------------------------------------------------------------
@@ -231,7 +305,8 @@ def count_matrix(q_idx: np.ndarray, key_idx: np.ndarray, N: int) -> np.ndarray:
             if j >= 0:
                 row[j] += 1.0
         for i in q_idx[c]:
-            M[i] = row
+            if i >= 0:                      # -1: absent member of a partial cluster
+                M[i] = row
     return M
 
 
@@ -288,7 +363,7 @@ def attn_fwd_gathered(q, k, v, q_idx, key_idx, scale, cluster_block: int = 1024)
         C = qi.shape[0]
         for c0 in range(0, C, cluster_block):
             qb, kb = qi[c0:c0 + cluster_block], ki[c0:c0 + cluster_block]
-            Qc = Q[b][qb]                      # [c, cs, H, D]
+            Qc = _gather_rows(Q[b], qb)        # [c, cs, H, D]; absent members: 0
             Kg = _gather_rows(K[b], kb)        # [c, nk, H, D]
             Vg = _gather_rows(V[b], kb)
             S = scale * np.einsum("cmhd,cshd->chms", Qc, Kg)
@@ -302,8 +377,9 @@ def attn_fwd_gathered(q, k, v, q_idx, key_idx, scale, cluster_block: int = 1024)
             P = E / Zs[..., None]
             Oc = np.einsum("chms,cshd->cmhd", P, Vg)
             L = np.where(has, m + np.log(Zs), -np.inf)   # [c, H, cs]
-            O[b][qb] = Oc
-            LSE[b][qb] = np.transpose(L, (0, 2, 1))
+            live = qb >= 0                     # absent members write nothing
+            O[b][qb[live]] = Oc[live]
+            LSE[b][qb[live]] = np.transpose(L, (0, 2, 1))[live]
     return O, LSE
 
 
@@ -355,7 +431,7 @@ def attn_bwd_gathered(q, k, v, do, q_idx, key_idx, scale, cluster_block: int = 1
         C = qi.shape[0]
         for c0 in range(0, C, cluster_block):
             qb, kb = qi[c0:c0 + cluster_block], ki[c0:c0 + cluster_block]
-            Qc, dOc = Q[b][qb], dO[b][qb]          # [c, cs, H, D]
+            Qc, dOc = _gather_rows(Q[b], qb), _gather_rows(dO[b], qb)   # [c, cs, H, D]
             Kg = _gather_rows(K[b], kb)            # [c, nk, H, D]
             Vg = _gather_rows(V[b], kb)
             S = scale * np.einsum("cmhd,cshd->chms", Qc, Kg)
@@ -365,11 +441,13 @@ def attn_bwd_gathered(q, k, v, do, q_idx, key_idx, scale, cluster_block: int = 1
             E = np.where(valid, np.exp(S - m[..., None]), 0.0)
             Z = np.where(has, E.sum(axis=-1), 1.0)
             P = E / Z[..., None]                   # [c, H, cs, nk]
+            P = P * (qb >= 0)[:, None, :, None]    # absent members: no query
             Oc = np.einsum("chms,cshd->cmhd", P, Vg)
             delta = np.einsum("cmhd,cmhd->chm", dOc, Oc)
             dP = np.einsum("cmhd,cshd->chms", dOc, Vg)
             dS = P * (dP - delta[..., None])
-            dQ[b][qb] = scale * np.einsum("chms,cshd->cmhd", dS, Kg)
+            live = qb >= 0
+            dQ[b][qb[live]] = scale * np.einsum("chms,cshd->cmhd", dS, Kg)[live]
             dKg = scale * np.einsum("chms,cmhd->cshd", dS, Qc)   # [c, nk, H, D]
             dVg = np.einsum("chms,cmhd->cshd", P, dOc)
             sel = kb >= 0
