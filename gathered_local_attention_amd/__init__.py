@@ -12,6 +12,10 @@ build_neighbors(coords, grid_side, cs=8, k=6) -> (perm, nbr, key_idx)
 fwd(q, k, v, q_idx, key_idx, scale=None) -> (o, lse)
 bwd(q, k, v, o, do, lse, q_idx, key_idx, scale=None) -> (dq, dk, dv)
 cluster_attention(q, k, v, q_idx, key_idx, scale=None) -> o   (autograd)
+build_neighbors_varlen(coords, lengths, grid_side, cs=8, k=6)
+    -> (q_idx, nbr, key_idx, tok_off, clu_off)        (packed batches)
+fwd_varlen(q, k, v, q_idx, key_idx, scale=None) -> (o, lse)
+bwd_varlen(q, k, v, o, do, lse, q_idx, key_idx, scale=None) -> (dq, dk, dv)
 knn_table(coords, grid_side, K) -> table
 knn_sample_fwd(feats, coords, queries, table, p) -> out
 knn_sample_bwd(feats, coords, queries, table, p, dout) -> (dfeats, dq, dp)
@@ -35,6 +39,10 @@ __all__ = [
     "fwd",
     "bwd",
     "cluster_attention",
+    "build_neighbors_varlen",
+    "fwd_varlen",
+    "bwd_varlen",
+    "varlen_offsets",
     "bwd_workspace_bytes",
     "build_workspace_bytes",
     "knn_table",
@@ -95,15 +103,16 @@ def build_neighbors(coords: torch.Tensor, grid_side: int, cs: int = 8, k: int = 
     """Morton-order balanced clusters and nearest-cluster key lists.
 
     coords: [B, N, 2] float32 device tensor (x = column, y = row).
-    Returns perm [B, N] (== q_idx [B, C, cs] as a view), nbr [B, C, k] and
+    Returns perm [B, C*cs] (== q_idx [B, C, cs] as a view, C = ceil(N/cs);
+    -1 after the members of a partial last cluster), nbr [B, C, k] and
     key_idx [B, C, cs*k], all int32."""
     lib = _lib.load()
     B, N, two = coords.shape
     if two != 2:
         raise ValueError("coords must be [B, N, 2]")
     _dev(coords, "coords", torch.float32)
-    C = N // cs if cs else 0
-    perm = torch.empty((B, N), dtype=torch.int32, device=coords.device)
+    C = -(-N // cs) if cs else 0
+    perm = torch.empty((B, C * cs), dtype=torch.int32, device=coords.device)
     nbr = torch.empty((B, C, k), dtype=torch.int32, device=coords.device)
     key_idx = torch.empty((B, C, cs * k), dtype=torch.int32, device=coords.device)
     need = lib.cluster_attn_build_neighbors_workspace(B, N, cs, k)
@@ -188,6 +197,107 @@ class _ClusterAttention(torch.autograd.Function):
 def cluster_attention(q, k, v, q_idx, key_idx, scale: float | None = None):
     """Autograd-aware local cluster attention (index lists are constants)."""
     return _ClusterAttention.apply(q, k, v, q_idx, key_idx, scale)
+
+
+# ---------------------------------------------------------------------------
+# Packed batches of images of different sizes
+# ---------------------------------------------------------------------------
+
+def varlen_offsets(lengths, cs: int = 8):
+    """Host-side token and cluster offsets [B+1] (lists of ints) of a packed
+    batch with the given per-image token counts."""
+    tok, clu = [0], [0]
+    for n in lengths:
+        n = int(n)
+        if n < 0:
+            raise ValueError("negative image size")
+        tok.append(tok[-1] + n)
+        clu.append(clu[-1] + (-(-n // cs)))
+    return tok, clu
+
+
+def build_neighbors_varlen(coords: torch.Tensor, lengths, grid_side: int, cs: int = 8, k: int = 6,
+                           workspace: torch.Tensor | None = None):
+    """Neighbour lists of a packed batch: coords [T, 2] float32 (device)
+    holds the images one after another, image b having lengths[b] tokens.
+    Returns q_idx [Ct, cs], nbr [Ct, k], key_idx [Ct, cs*k] (int32,
+    batch-global ids, -1 padding) and the device offsets tok_off, clu_off
+    [B+1] int32."""
+    lib = _lib.load()
+    if coords.dim() != 2 or coords.shape[1] != 2:
+        raise ValueError("coords must be [T, 2]")
+    _dev(coords, "coords", torch.float32)
+    tok, clu = varlen_offsets(lengths, cs)
+    B, T, Ct = len(tok) - 1, tok[-1], clu[-1]
+    if T != coords.shape[0]:
+        raise ValueError(f"lengths sum to {T}, coords has {coords.shape[0]} rows")
+    max_n = max((tok[b + 1] - tok[b] for b in range(B)), default=0)
+    dev = coords.device
+    tok_off = torch.tensor(tok, dtype=torch.int32).to(dev)
+    clu_off = torch.tensor(clu, dtype=torch.int32).to(dev)
+    q_idx = torch.empty((Ct, cs), dtype=torch.int32, device=dev)
+    nbr = torch.empty((Ct, k), dtype=torch.int32, device=dev)
+    key_idx = torch.empty((Ct, cs * k), dtype=torch.int32, device=dev)
+    need = lib.cluster_attn_build_neighbors_varlen_workspace(B, T, Ct, max_n, cs, k)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    _check(lib.cluster_attn_build_neighbors_varlen(
+        coords.data_ptr(), B, T, Ct, max_n, tok_off.data_ptr(), clu_off.data_ptr(),
+        int(grid_side), cs, k, q_idx.data_ptr(), nbr.data_ptr(), key_idx.data_ptr(),
+        workspace.data_ptr(), workspace.numel(), _stream(coords)),
+        "cluster_attn_build_neighbors_varlen")
+    return q_idx, nbr, key_idx, tok_off, clu_off
+
+
+def _varlen_shapes(q, q_idx, key_idx):
+    if q.dim() != 3 or q_idx.dim() != 2 or key_idx.dim() != 2:
+        raise ValueError("q/k/v must be [T, H, D], q_idx [Ct, cs], key_idx [Ct, nk]")
+    if q.dtype not in _DT:
+        raise TypeError(f"unsupported dtype {q.dtype}")
+    T, H, D = q.shape
+    Ct, cs = q_idx.shape
+    if key_idx.shape[0] != Ct:
+        raise ValueError("q_idx and key_idx must have one row per cluster")
+    return T, H, D, Ct, cs, key_idx.shape[1]
+
+
+def fwd_varlen(q, k, v, q_idx, key_idx, scale: float | None = None):
+    """Forward of a packed batch: O [T, H, D] (dtype of q), LSE [T, H] f32."""
+    lib = _lib.load()
+    T, H, D, Ct, cs, nk = _varlen_shapes(q, q_idx, key_idx)
+    for t, n in ((k, "k"), (v, "v")):
+        if t.shape != q.shape or t.dtype != q.dtype:
+            raise ValueError(f"{n} must match q in shape and dtype")
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    o = torch.empty_like(q)
+    lse = torch.empty((T, H), dtype=torch.float32, device=q.device)
+    _check(lib.cluster_attn_fwd_varlen(
+        _DT[q.dtype], T, Ct, H, D, cs, nk, scale, _dev(q, "q"), _dev(k, "k"), _dev(v, "v"),
+        _dev(q_idx, "q_idx", torch.int32), _dev(key_idx, "key_idx", torch.int32),
+        o.data_ptr(), lse.data_ptr(), _stream(q)), "cluster_attn_fwd_varlen")
+    return o, lse
+
+
+def bwd_varlen(q, k, v, o, do, lse, q_idx, key_idx, scale: float | None = None,
+               workspace: torch.Tensor | None = None):
+    """Backward of a packed batch: dQ, dK, dV [T, H, D] (dtype of q)."""
+    lib = _lib.load()
+    T, H, D, Ct, cs, nk = _varlen_shapes(q, q_idx, key_idx)
+    for t, n in ((k, "k"), (v, "v"), (o, "o"), (do, "do")):
+        if t.shape != q.shape or t.dtype != q.dtype:
+            raise ValueError(f"{n} must match q in shape and dtype")
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    dt = _DT[q.dtype]
+    need = lib.cluster_attn_bwd_varlen_workspace(dt, T, Ct, H, D, cs, nk)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+    _check(lib.cluster_attn_bwd_varlen(
+        dt, T, Ct, H, D, cs, nk, scale, _dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(o, "o"),
+        _dev(do, "do"), _dev(lse, "lse", torch.float32), _dev(q_idx, "q_idx", torch.int32),
+        _dev(key_idx, "key_idx", torch.int32), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+        workspace.data_ptr(), workspace.numel(), _stream(q)), "cluster_attn_bwd_varlen")
+    return dq, dk, dv
 
 
 # ---------------------------------------------------------------------------

@@ -22,6 +22,19 @@ SIGNATURES = {
     "cluster_attn_bwd": (
         _c_int, [_c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _f,
                  _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _c_size, _vp]),
+    "cluster_attn_build_neighbors_varlen_workspace": (
+        _c_size, [_c_int, _c_int, _c_int, _c_int, _c_int, _c_int]),
+    "cluster_attn_build_neighbors_varlen": (
+        _c_int, [_vp, _c_int, _c_int, _c_int, _c_int, _vp, _vp, _c_int, _c_int, _c_int,
+                 _vp, _vp, _vp, _vp, _c_size, _vp]),
+    "cluster_attn_fwd_varlen": (
+        _c_int, [_c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _f,
+                 _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
+    "cluster_attn_bwd_varlen_workspace": (
+        _c_size, [_c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int]),
+    "cluster_attn_bwd_varlen": (
+        _c_int, [_c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _f,
+                 _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _c_size, _vp]),
     "cluster_attn_knn_table": (_c_int, [_vp, _c_int, _c_int, _c_int, _c_int, _vp, _vp]),
     "cluster_attn_knn_sample_fwd": (
         _c_int, [_c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _f,

@@ -56,7 +56,7 @@ int check_alias(const Range* outs, int nout, const Range* ins, int nin) {
   return CA_OK;
 }
 
-constexpr int64_t kMaxTokensPerImage = int64_t(1) << 27;   // cluster ids fit 24 bits
+using ca::kMaxTokensPerImage;   // 2^22: cluster ids of a (distance, index) key fit 19 bits
 
 // Shape checks common to fwd and bwd.  Returns CA_OK or an error.
 int check_attn_shape(int dt, int B, int N, int H, int D, int cs, int nk) {
@@ -68,11 +68,12 @@ int check_attn_shape(int dt, int B, int N, int H, int D, int cs, int nk) {
   if (D != 32) return fail(CA_ERR_UNSUPPORTED, "head dim %d (only 32 is supported)", D);
   if (nk % cs != 0 || nk / cs > 8)
     return fail(CA_ERR_UNSUPPORTED, "nk=%d must be cs*k with 1 <= k <= 8", nk);
-  if (N % cs != 0) return fail(CA_ERR_SHAPE, "N=%d is not a multiple of cs=%d", N, cs);
-  if (N > kMaxTokensPerImage) return fail(CA_ERR_SHAPE, "N=%d exceeds 2^27 tokens per image", N);
   if ((int64_t)B * N * H * D > (int64_t(1) << 40)) return fail(CA_ERR_SHAPE, "tensor too large");
+  if ((int64_t)B * N > (int64_t(1) << 31) - 1) return fail(CA_ERR_SHAPE, "B*N above 2^31 - 1");
   return CA_OK;
 }
+
+int64_t clusters_of(int64_t N, int cs) { return (N + cs - 1) / cs; }
 
 
 // Shape checks of the KNN sampler calls.
@@ -122,9 +123,8 @@ const char* cluster_attn_status_string(int s) {
 const char* cluster_attn_last_error(void) { return g_last_error; }
 
 size_t cluster_attn_build_neighbors_workspace(int B, int N, int cs, int k) {
-  if (B < 0 || N < 0 || cs != 8 || k < 1 || k > 8 || N % cs != 0 || N > kMaxTokensPerImage)
-    return 0;
-  return ca::build_layout(nullptr, B, N).bytes;
+  if (B < 0 || N < 0 || cs != 8 || k < 1 || k > 8 || N > kMaxTokensPerImage) return 0;
+  return ca::build_layout(nullptr, B, (int64_t)B * N, B * clusters_of(N, cs), N).bytes;
 }
 
 int cluster_attn_build_neighbors(const float* coords, int B, int N, int grid_side, int cs, int k,
@@ -133,69 +133,103 @@ int cluster_attn_build_neighbors(const float* coords, int B, int N, int grid_sid
   if (B < 0 || N < 0) return fail(CA_ERR_SHAPE, "bad sizes B=%d N=%d", B, N);
   if (cs != 8) return fail(CA_ERR_UNSUPPORTED, "cluster size %d (only 8 is supported)", cs);
   if (k < 1 || k > 8) return fail(CA_ERR_UNSUPPORTED, "k=%d outside 1..8", k);
-  if (N % cs != 0) return fail(CA_ERR_SHAPE, "N=%d is not a multiple of cs=%d", N, cs);
-  if (N > kMaxTokensPerImage) return fail(CA_ERR_SHAPE, "N=%d exceeds 2^27 tokens per image", N);
+  if (N > kMaxTokensPerImage) return fail(CA_ERR_SHAPE, "N=%d exceeds 2^22 tokens per image", N);
+  if ((int64_t)B * N > (int64_t(1) << 31) - 1) return fail(CA_ERR_SHAPE, "B*N above 2^31 - 1");
   if (grid_side < 1 || grid_side > 65536)
     return fail(CA_ERR_SHAPE, "grid_side=%d outside [1, 65536]", grid_side);
   if (B == 0 || N == 0) return ok();
   if (!coords || !perm || !nbr || !key_idx) return fail(CA_ERR_NULL, "NULL tensor pointer");
-  const size_t need = ca::build_layout(nullptr, B, N).bytes;
+  const int64_t C = clusters_of(N, cs);
+  const size_t need = ca::build_layout(nullptr, B, (int64_t)B * N, B * C, N).bytes;
   if (need && !ws) return fail(CA_ERR_NULL, "NULL workspace (%zu bytes needed)", need);
   if (ws_bytes < need) return fail(CA_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
-  const int64_t C = N / cs;
-  Range outs[] = {{perm, (size_t)B * N * 4}, {nbr, (size_t)(B * C * k) * 4},
+  Range outs[] = {{perm, (size_t)(B * C * cs) * 4}, {nbr, (size_t)(B * C * k) * 4},
                   {key_idx, (size_t)(B * C * k * cs) * 4}, {ws, need}};
   Range ins[] = {{coords, (size_t)B * N * 8}};
   if (int s = check_alias(outs, 4, ins, 1)) return s;
-  return hip_status(ca::launch_build_neighbors(coords, B, N, grid_side, k, perm, nbr, key_idx, ws,
-                                               (hipStream_t)hip_stream),
+  const ca::Geom g{nullptr, nullptr, N, (int)C};
+  return hip_status(ca::launch_build_neighbors(coords, g, B, (int64_t)B * N, B * C, grid_side, k,
+                                               perm, nbr, key_idx, ws, (hipStream_t)hip_stream),
                     "build_neighbors launch");
 }
 
-int cluster_attn_fwd(int dt, int B, int N, int H, int D, int cs, int nk, float scale,
-                     const void* q, const void* k, const void* v, const int32_t* q_idx,
-                     const int32_t* key_idx, void* o, float* lse, void* hip_stream) {
-  if (int s = check_attn_shape(dt, B, N, H, D, cs, nk)) return s;
+size_t cluster_attn_build_neighbors_varlen_workspace(int B, int T, int Ct, int max_n, int cs,
+                                                     int k) {
+  if (B < 0 || T < 0 || Ct < 0 || max_n < 0 || max_n > T || cs != 8 || k < 1 || k > 8 ||
+      max_n > kMaxTokensPerImage)
+    return 0;
+  return ca::build_layout(nullptr, B, T, Ct, max_n).bytes;
+}
+
+int cluster_attn_build_neighbors_varlen(const float* coords, int B, int T, int Ct, int max_n,
+                                        const int32_t* tok_off, const int32_t* clu_off,
+                                        int grid_side, int cs, int k, int32_t* q_idx,
+                                        int32_t* nbr, int32_t* key_idx, void* ws,
+                                        size_t ws_bytes, void* hip_stream) {
+  if (B < 0 || T < 0 || Ct < 0 || max_n < 0 || max_n > T)
+    return fail(CA_ERR_SHAPE, "bad sizes B=%d T=%d Ct=%d max_n=%d", B, T, Ct, max_n);
+  if (cs != 8) return fail(CA_ERR_UNSUPPORTED, "cluster size %d (only 8 is supported)", cs);
+  if (k < 1 || k > 8) return fail(CA_ERR_UNSUPPORTED, "k=%d outside 1..8", k);
+  if (max_n > kMaxTokensPerImage)
+    return fail(CA_ERR_SHAPE, "max_n=%d exceeds 2^22 tokens per image", max_n);
+  if (Ct < clusters_of(T, cs) || Ct > T || (int64_t)Ct * cs * k > (int64_t(1) << 31) - 1)
+    return fail(CA_ERR_SHAPE, "Ct=%d is inconsistent with T=%d tokens", Ct, T);
+  if (grid_side < 1 || grid_side > 65536)
+    return fail(CA_ERR_SHAPE, "grid_side=%d outside [1, 65536]", grid_side);
+  if (B == 0 || T == 0) return ok();
+  if (!coords || !tok_off || !clu_off || !q_idx || !nbr || !key_idx)
+    return fail(CA_ERR_NULL, "NULL tensor pointer");
+  const size_t need = ca::build_layout(nullptr, B, T, Ct, max_n).bytes;
+  if (need && !ws) return fail(CA_ERR_NULL, "NULL workspace (%zu bytes needed)", need);
+  if (ws_bytes < need) return fail(CA_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
+  Range outs[] = {{q_idx, (size_t)Ct * cs * 4}, {nbr, (size_t)Ct * k * 4},
+                  {key_idx, (size_t)Ct * k * cs * 4}, {ws, need}};
+  Range ins[] = {{coords, (size_t)T * 8}, {tok_off, (size_t)(B + 1) * 4},
+                 {clu_off, (size_t)(B + 1) * 4}};
+  if (int s = check_alias(outs, 4, ins, 3)) return s;
+  const ca::Geom g{tok_off, clu_off, max_n, (int)clusters_of(max_n, cs)};
+  return hip_status(ca::launch_build_neighbors(coords, g, B, T, Ct, grid_side, k, q_idx, nbr,
+                                               key_idx, ws, (hipStream_t)hip_stream),
+                    "build_neighbors_varlen launch");
+}
+
+}  // extern "C"
+
+namespace {
+
+// Forward on B images of N tokens and C clusters each (q_idx [B, C, cs]).
+int attn_fwd(int dt, int B, int N, int64_t C, int H, int D, int cs, int nk, float scale,
+             const void* q, const void* k, const void* v, const int32_t* q_idx,
+             const int32_t* key_idx, void* o, float* lse, void* hip_stream) {
   if (!(scale == scale) || scale == INFINITY || scale == -INFINITY)
     return fail(CA_ERR_SHAPE, "scale is not finite");
-  if (B == 0 || N == 0) return ok();
+  if (B == 0 || N == 0 || C == 0) return ok();
   if (!q || !k || !v || !q_idx || !key_idx || !o || !lse)
     return fail(CA_ERR_NULL, "NULL tensor pointer");
   const size_t tb = (size_t)B * N * H * D * elem_size(dt);
-  const int64_t C = N / cs;
   Range outs[] = {{o, tb}, {lse, (size_t)B * N * H * 4}};
-  Range ins[] = {{q, tb}, {k, tb}, {v, tb}, {q_idx, (size_t)B * N * 4},
+  Range ins[] = {{q, tb}, {k, tb}, {v, tb}, {q_idx, (size_t)(B * C * cs) * 4},
                  {key_idx, (size_t)(B * C * nk) * 4}};
   if (int s = check_alias(outs, 2, ins, 5)) return s;
   hipStream_t st = (hipStream_t)hip_stream;
-  if (ca::mfma_supported(dt, B, N, H, nk))
-    return hip_status(ca::launch_fwd_mfma(dt, B, N, H, scale, q, k, v, q_idx, key_idx, o, lse, st),
+  if (ca::mfma_supported(dt, B, N, (int)C, H, nk))
+    return hip_status(ca::launch_fwd_mfma(dt, B, N, (int)C, H, scale, q, k, v, q_idx, key_idx, o,
+                                          lse, st),
                       "fwd launch");
-  return hip_status(ca::launch_fwd_valu(dt, B, N, H, nk, scale, q, k, v, q_idx, key_idx, o, lse, st),
+  return hip_status(ca::launch_fwd_valu(dt, B, N, (int)C, H, nk, scale, q, k, v, q_idx, key_idx,
+                                        o, lse, st),
                     "fwd launch");
 }
 
-size_t cluster_attn_bwd_workspace(int dt, int B, int N, int H, int D, int cs, int nk) {
-  const char saved = g_last_error[0];
-  if (check_attn_shape(dt, B, N, H, D, cs, nk) != CA_OK) {
-    g_last_error[0] = saved;
-    return 0;
-  }
-  return ca::bwd_layout(nullptr, B, N, H, N / cs, nk).bytes;
-}
-
-int cluster_attn_bwd(int dt, int B, int N, int H, int D, int cs, int nk, float scale,
-                     const void* q, const void* k, const void* v, const void* o,
-                     const void* dout, const float* lse, const int32_t* q_idx,
-                     const int32_t* key_idx, void* dq, void* dk, void* dv, void* ws,
-                     size_t ws_bytes, void* hip_stream) {
-  if (int s = check_attn_shape(dt, B, N, H, D, cs, nk)) return s;
+int attn_bwd(int dt, int B, int N, int64_t C, int H, int D, int cs, int nk, float scale,
+             const void* q, const void* k, const void* v, const void* o, const void* dout,
+             const float* lse, const int32_t* q_idx, const int32_t* key_idx, void* dq, void* dk,
+             void* dv, void* ws, size_t ws_bytes, void* hip_stream) {
   if (!(scale == scale) || scale == INFINITY || scale == -INFINITY)
     return fail(CA_ERR_SHAPE, "scale is not finite");
-  if (B == 0 || N == 0) return ok();
+  if (B == 0 || N == 0 || C == 0) return ok();
   if (!q || !k || !v || !o || !dout || !lse || !q_idx || !key_idx || !dq || !dk || !dv)
     return fail(CA_ERR_NULL, "NULL tensor pointer");
-  const int64_t C = N / cs;
   const ca::BwdWorkspace need = ca::bwd_layout(nullptr, B, N, H, C, nk);
   if (!ws) return fail(CA_ERR_NULL, "NULL workspace (%zu bytes needed)", need.bytes);
   if (ws_bytes < need.bytes)
@@ -208,20 +242,85 @@ int cluster_attn_bwd(int dt, int B, int N, int H, int D, int cs, int nk, float s
                  {o, tb},
                  {dout, tb},
                  {lse, (size_t)B * N * H * 4},
-                 {q_idx, (size_t)B * N * 4},
+                 {q_idx, (size_t)(B * C * cs) * 4},
                  {key_idx, (size_t)(B * C * nk) * 4}};
   if (int s = check_alias(outs, 4, ins, 8)) return s;
   const ca::BwdWorkspace w = ca::bwd_layout(ws, B, N, H, C, nk);
   hipStream_t st = (hipStream_t)hip_stream;
-  hipError_t e = ca::launch_bwd_plan(B, N, nk, q_idx, key_idx, w, st);
+  hipError_t e = ca::launch_bwd_plan(B, N, (int)C, nk, q_idx, key_idx, w, st);
   if (e != hipSuccess) return hip_status(e, "bwd plan launch");
-  if (ca::mfma_supported(dt, B, N, H, nk))
-    return hip_status(ca::launch_bwd_mfma(3, dt, B, N, H, nk, scale, q, k, v, o, dout, lse, q_idx,
-                                          key_idx, dq, dk, dv, w, st),
+  if (ca::mfma_supported(dt, B, N, (int)C, H, nk))
+    return hip_status(ca::launch_bwd_mfma(3, dt, B, N, (int)C, H, nk, scale, q, k, v, o, dout, lse,
+                                          q_idx, key_idx, dq, dk, dv, w, st),
                       "bwd launch");
-  return hip_status(ca::launch_bwd_valu(3, dt, B, N, H, nk, scale, q, k, v, o, dout, lse, q_idx,
-                                        key_idx, dq, dk, dv, w, st),
+  return hip_status(ca::launch_bwd_valu(3, dt, B, N, (int)C, H, nk, scale, q, k, v, o, dout, lse,
+                                        q_idx, key_idx, dq, dk, dv, w, st),
                     "bwd launch");
+}
+
+// Packed batches run as one image of T tokens and Ct clusters.
+int check_varlen(int dt, int T, int Ct, int H, int D, int cs, int nk) {
+  if (int s = check_attn_shape(dt, 1, T, H, D, cs, nk)) return s;
+  if (Ct < 0 || Ct < clusters_of(T, cs) || Ct > T)
+    return fail(CA_ERR_SHAPE, "Ct=%d is inconsistent with T=%d tokens", Ct, T);
+  return CA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int cluster_attn_fwd(int dt, int B, int N, int H, int D, int cs, int nk, float scale,
+                     const void* q, const void* k, const void* v, const int32_t* q_idx,
+                     const int32_t* key_idx, void* o, float* lse, void* hip_stream) {
+  if (int s = check_attn_shape(dt, B, N, H, D, cs, nk)) return s;
+  return attn_fwd(dt, B, N, clusters_of(N, cs), H, D, cs, nk, scale, q, k, v, q_idx, key_idx, o,
+                  lse, hip_stream);
+}
+
+size_t cluster_attn_bwd_workspace(int dt, int B, int N, int H, int D, int cs, int nk) {
+  const char saved = g_last_error[0];
+  if (check_attn_shape(dt, B, N, H, D, cs, nk) != CA_OK) {
+    g_last_error[0] = saved;
+    return 0;
+  }
+  return ca::bwd_layout(nullptr, B, N, H, clusters_of(N, cs), nk).bytes;
+}
+
+int cluster_attn_bwd(int dt, int B, int N, int H, int D, int cs, int nk, float scale,
+                     const void* q, const void* k, const void* v, const void* o,
+                     const void* dout, const float* lse, const int32_t* q_idx,
+                     const int32_t* key_idx, void* dq, void* dk, void* dv, void* ws,
+                     size_t ws_bytes, void* hip_stream) {
+  if (int s = check_attn_shape(dt, B, N, H, D, cs, nk)) return s;
+  return attn_bwd(dt, B, N, clusters_of(N, cs), H, D, cs, nk, scale, q, k, v, o, dout, lse, q_idx,
+                  key_idx, dq, dk, dv, ws, ws_bytes, hip_stream);
+}
+
+int cluster_attn_fwd_varlen(int dt, int T, int Ct, int H, int D, int cs, int nk, float scale,
+                            const void* q, const void* k, const void* v, const int32_t* q_idx,
+                            const int32_t* key_idx, void* o, float* lse, void* hip_stream) {
+  if (int s = check_varlen(dt, T, Ct, H, D, cs, nk)) return s;
+  return attn_fwd(dt, 1, T, Ct, H, D, cs, nk, scale, q, k, v, q_idx, key_idx, o, lse, hip_stream);
+}
+
+size_t cluster_attn_bwd_varlen_workspace(int dt, int T, int Ct, int H, int D, int cs, int nk) {
+  const char saved = g_last_error[0];
+  if (check_varlen(dt, T, Ct, H, D, cs, nk) != CA_OK) {
+    g_last_error[0] = saved;
+    return 0;
+  }
+  return ca::bwd_layout(nullptr, 1, T, H, Ct, nk).bytes;
+}
+
+int cluster_attn_bwd_varlen(int dt, int T, int Ct, int H, int D, int cs, int nk, float scale,
+                            const void* q, const void* k, const void* v, const void* o,
+                            const void* dout, const float* lse, const int32_t* q_idx,
+                            const int32_t* key_idx, void* dq, void* dk, void* dv, void* ws,
+                            size_t ws_bytes, void* hip_stream) {
+  if (int s = check_varlen(dt, T, Ct, H, D, cs, nk)) return s;
+  return attn_bwd(dt, 1, T, Ct, H, D, cs, nk, scale, q, k, v, o, dout, lse, q_idx, key_idx, dq,
+                  dk, dv, ws, ws_bytes, hip_stream);
 }
 
 int cluster_attn_knn_table(const float* coords, int B, int N, int grid_side, int K,

@@ -31,6 +31,13 @@
 //  * Workgroups are remapped so that each XCD (eight, dispatched
 //    round-robin) walks one contiguous Morton range of clusters:
 //    neighbouring clusters share their gathered rows in its L2.
+//  * Partial clusters (images whose size is not a multiple of 8, packed
+//    batches of images of different sizes): a -1 member of a q_idx row is
+//    no query.  Its Q/dO/O rows are gathered from a clamped (valid) token
+//    and nothing is stored for it; in the key-major pass it reads an
+//    (LSE = +inf, Delta = 0) pair, so its P and dS are exactly 0.  Member 0
+//    of every row is a token, so each store instruction keeps at least one
+//    active lane (the pipelines count store instructions).
 #include "common.h"
 
 #include <algorithm>
@@ -291,7 +298,7 @@ __device__ __forceinline__ void item_offs(const FwdIdx2& x, int img, int h0, int
 #pragma unroll
   for (int j = 0; j < NK / 8; ++j)
     o.kv[j] = (uint32_t)__umul24((uint32_t)max(x.tj[j], 0), row_bytes) + base + ((j & 1) ? col1 : col0);
-  o.qr = (uint32_t)__umul24((uint32_t)x.tq, row_bytes) + base + col0;
+  o.qr = (uint32_t)__umul24((uint32_t)max(x.tq, 0), row_bytes) + base + col0;
 }
 
 // one tensor's 48 slot rows (both heads of the pair) into an LDS tile:
@@ -314,7 +321,7 @@ __device__ __forceinline__ void gather_tile(const T* __restrict__ src, const Fwd
 // complete once at most stores(t-1) + idx(t+2) + K(t+1) = 11 remain.
 template <typename T>
 __global__ void __launch_bounds__(64 * kFwdWaves)
-fwd_lds_kernel(int N, int H, int HP, int n_items, int ipw, float scale_log2,
+fwd_lds_kernel(int N, int C, int H, int HP, int n_items, int ipw, float scale_log2,
                const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
                const int32_t* __restrict__ q_idx, const int32_t* __restrict__ key_idx,
                T* __restrict__ o, float* __restrict__ lse) {
@@ -340,7 +347,7 @@ fwd_lds_kernel(int N, int H, int HP, int n_items, int ipw, float scale_log2,
   const uint32_t ak = lds_addr(tk), av = lds_addr(tv), aq = lds_addr(tq), ai = lds_addr(ti);
   const f32x4 z = {0.f, 0.f, 0.f, 0.f};
   const int e = c16 >> 2, qq = c16 & 3;
-  const int CperImg = N / CS;
+  const int CperImg = C;
   const bool neg = scale_log2 < 0.f;        // wave-uniform
   const float csl = fabsf(scale_log2);
 
@@ -514,7 +521,7 @@ fwd_lds_kernel(int N, int H, int HP, int n_items, int ipw, float scale_log2,
     // exactly three store instructions per item (the pipeline counts them);
     // 1/l through the hardware reciprocal (1 ulp)
     const float inv = l > 0.f ? __builtin_amdgcn_rcpf(l) : 0.f;
-    const bool st = hq < H;
+    const bool st = hq < H && x.qc >= 0;
     const uint32_t qrow = (uint32_t)__umul24((uint32_t)x.qc, (uint32_t)H) + (uint32_t)(img * H);
     const uint32_t orow = (qrow + (uint32_t)(st ? hq : h0)) * kRow + 8u * g;
 #pragma unroll
@@ -591,7 +598,7 @@ constexpr int kQWavesPerCU = 8;
 
 template <typename T>
 __global__ void __launch_bounds__(64 * kQWaves)
-bwd_q_lds_kernel(int N, int H, int HP, int n_items, int ipw, float scale,
+bwd_q_lds_kernel(int N, int C, int H, int HP, int n_items, int ipw, float scale,
                  const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
                  const T* __restrict__ o, const T* __restrict__ dout,
                  const float* __restrict__ lse, const int32_t* __restrict__ q_idx,
@@ -622,7 +629,6 @@ bwd_q_lds_kernel(int N, int H, int HP, int n_items, int ipw, float scale,
   const f32x4 z = {0.f, 0.f, 0.f, 0.f};
   const int e = c16 >> 2, qq = c16 & 3;
   const float scale_log2 = scale * kLog2e;
-  const int C = N / CS;
   const uint32_t row_bytes = (uint32_t)H * kRow;   // one token, all heads
   const uint32_t colA0 = chunk_col(lane, 0, true), colA1 = chunk_col(lane, 1, true);
   const uint32_t colB0 = chunk_col(lane, 0, false), colB1 = chunk_col(lane, 1, false);
@@ -649,7 +655,7 @@ bwd_q_lds_kernel(int N, int H, int HP, int n_items, int ipw, float scale,
   auto gather_lse = [&](const KvPos& p, const FwdIdx2& x) {
     if (lane < 16) {
       const int h = min(2 * p.hp + (lane >> 3), H - 1);
-      dma4(lse, (uint32_t)((p.b * N + x.qc) * H + h) * 4u, als);
+      dma4(lse, (uint32_t)((p.b * N + max(x.qc, 0)) * H + h) * 4u, als);
     }
   };
 
@@ -776,10 +782,12 @@ bwd_q_lds_kernel(int N, int H, int HP, int n_items, int ipw, float scale,
         acc[hh][hf] = Mfma<T>::mma(pad(kt[hh][hf][2]), b1h, acc[hh][hf]);
       }
     }
-    // exactly three store instructions per item (lanes 0..7 always store)
+    // exactly three store instructions per item (lane 0, member 0 of the
+    // cluster, always stores)
     const uint32_t qrow = (uint32_t)__umul24((uint32_t)x.qc, (uint32_t)H) + (uint32_t)(img * H);
-    if (hq < H && g == 0) ld[qrow + hq] = make_float2(lse2, dl);
-    if (hq < H) {
+    const bool live = hq < H && x.qc >= 0;
+    if (live && g == 0) ld[qrow + hq] = make_float2(lse2, dl);
+    if (live) {
       const uint32_t drow = (qrow + (uint32_t)hq) * kRow + 8u * g;
 #pragma unroll
       for (int hf = 0; hf < 2; ++hf)
@@ -823,9 +831,10 @@ constexpr int kKvWavesPerCU = 16;                       // residency (VGPRs and 
 
 template <typename T>
 __global__ void __launch_bounds__(64 * kWaves, kKvWavesPerCU / 4)
-bwd_kv_lds_kernel(int N, int H, int HP, int n_items, float scale, const T* __restrict__ q,
+bwd_kv_lds_kernel(int N, int C, int H, int HP, int n_items, float scale, const T* __restrict__ q,
                   const T* __restrict__ k, const T* __restrict__ v, const T* __restrict__ dout,
                   const int32_t* __restrict__ q_idx, const float2* __restrict__ ld,
+                  uint32_t ld_none,
                   const int32_t* __restrict__ off_all, const RevEntry* __restrict__ rev_all,
                   const int32_t* __restrict__ rtok_all, int nk, T* __restrict__ dk,
                   T* __restrict__ dv) {
@@ -847,7 +856,6 @@ bwd_kv_lds_kernel(int N, int H, int HP, int n_items, float scale, const T* __res
   const uint32_t aq = lds_addr(tq), ad = lds_addr(td), am = lds_addr(tm);
   const float2* tl2 = reinterpret_cast<const float2*>(lds_ld[wv]);
   const uint32_t al = lds_addr(lds_ld[wv]);
-  const int C = N / CS;
   const int c16 = lane & 15, g = lane >> 4;
   const bool left = c16 < 8;
   const int kcol = c16 & 7;
@@ -894,7 +902,7 @@ bwd_kv_lds_kernel(int N, int H, int HP, int n_items, float scale, const T* __res
   auto key_row = [&](const KvPos& p, int ktok) {
     const int h0 = 2 * p.hp;
     const uint32_t h1off = h0 + 1 < H ? kRow : 0u;
-    return (uint32_t)((p.b * N + ktok) * H + h0) * kRow + (left ? 0u : h1off) + 16u * g;
+    return (uint32_t)((p.b * N + max(ktok, 0)) * H + h0) * kRow + (left ? 0u : h1off) + 16u * g;
   };
 
   // prologue: item `first` and the lookups of the next two
@@ -963,7 +971,7 @@ bwd_kv_lds_kernel(int N, int H, int HP, int n_items, float scale, const T* __res
           uint32_t offs[4];
 #pragma unroll
           for (int u = 0; u < 4; ++u)
-            offs[u] = (uint32_t)btok[8 * min(e4 + u, ne - 1) + r8] * row_bytes + gb[u & 1];
+            offs[u] = (uint32_t)max(btok[8 * min(e4 + u, ne - 1) + r8], 0) * row_bytes + gb[u & 1];
           const int lrow = lane & 31;
           const int tl_tok = btok[8 * min(e4 + (lrow >> 3), ne - 1) + (lrow & 7)];
 #pragma unroll
@@ -976,8 +984,10 @@ bwd_kv_lds_kernel(int N, int H, int HP, int n_items, float scale, const T* __res
           // rows 16..31 only in a full step): 16 bytes at
           // ld[(img + t) * H + h0].  With an odd head count the second pair
           // belongs to the next token (or lies in the next workspace part);
-          // it is never used then.
-          if (lane < (half ? 16 : 32)) dma16(ld, (uint32_t)tl_tok * (uint32_t)H * 8u + lb, al);
+          // it is never used then.  An absent query (-1) reads the
+          // (+inf, 0) pairs at byte offset ld_none instead.
+          const uint32_t lo_ = tl_tok >= 0 ? (uint32_t)tl_tok * (uint32_t)H * 8u + lb : ld_none;
+          if (lane < (half ? 16 : 32)) dma16(ld, lo_, al);
         }
         // log2 of the multiplicity of this lane's output rows 4g+i of block
         // qb (entry e4 + 2qb + (g >> 1), key member kcol): -inf for 0
@@ -1043,7 +1053,7 @@ bwd_kv_lds_kernel(int N, int H, int HP, int n_items, float scale, const T* __res
       }
     }
 
-    if (hk < H) {
+    if (hk < H && ktok >= 0) {   // -1: absent member of a partial key cluster
       const uint32_t orow = (uint32_t)((img + ktok) * H + hk) * kRow + 8u * g;
 #pragma unroll
       for (int hf = 0; hf < 2; ++hf) {
@@ -1075,74 +1085,76 @@ int items_per_wave(int items, int per_cu) {
 }
 
 template <typename T>
-hipError_t fwd_t(int B, int N, int H, float scale, const void* q, const void* k, const void* v,
-                 const int32_t* q_idx, const int32_t* key_idx, void* o, float* lse,
+hipError_t fwd_t(int B, int N, int C, int H, float scale, const void* q, const void* k,
+                 const void* v, const int32_t* q_idx, const int32_t* key_idx, void* o, float* lse,
                  hipStream_t st) {
   const int HP = (H + 1) / 2;
-  const int items = B * (N / CS) * HP;
+  const int items = B * C * HP;
   const int ipw = items_per_wave(items, kFwdWavesPerCU);
   const int waves = (items + ipw - 1) / ipw;
   const int wgs = (waves + kFwdWaves - 1) / kFwdWaves;
-  hipLaunchKernelGGL((fwd_lds_kernel<T>), dim3(wgs), dim3(64 * kFwdWaves), 0, st, N, H, HP, items,
-                     ipw, scale * kLog2e, (const T*)q, (const T*)k, (const T*)v, q_idx, key_idx,
-                     (T*)o, lse);
+  hipLaunchKernelGGL((fwd_lds_kernel<T>), dim3(wgs), dim3(64 * kFwdWaves), 0, st, N, C, H, HP,
+                     items, ipw, scale * kLog2e, (const T*)q, (const T*)k, (const T*)v, q_idx,
+                     key_idx, (T*)o, lse);
   return hipGetLastError();
 }
 
 template <typename T>
-hipError_t bwd_t(int pass, int B, int N, int H, int nk, float scale, const void* q, const void* k,
-                 const void* v, const void* o, const void* dout, const float* lse,
+hipError_t bwd_t(int pass, int B, int N, int C, int H, int nk, float scale, const void* q,
+                 const void* k, const void* v, const void* o, const void* dout, const float* lse,
                  const int32_t* q_idx, const int32_t* key_idx, void* dq, void* dk, void* dv,
                  const BwdWorkspace& w, hipStream_t st) {
   const int HP = (H + 1) / 2;
-  const int items = B * (N / CS) * HP;
+  const int items = B * C * HP;
   const int kv_waves = std::min(items, 256 * kKvWavesPerCU);
   const int kv_wgs = (kv_waves + kWaves - 1) / kWaves;
   if (pass & 1) {
     const int ipw = items_per_wave(items, kQWavesPerCU);
     const int waves = (items + ipw - 1) / ipw;
     hipLaunchKernelGGL((bwd_q_lds_kernel<T>), dim3((waves + kQWaves - 1) / kQWaves),
-                       dim3(64 * kQWaves), 0, st, N, H, HP, items, ipw, scale, (const T*)q,
+                       dim3(64 * kQWaves), 0, st, N, C, H, HP, items, ipw, scale, (const T*)q,
                        (const T*)k, (const T*)v, (const T*)o, (const T*)dout, lse, q_idx, key_idx,
                        (T*)dq, w.ld);
   }
-  if (pass & 2)
-    hipLaunchKernelGGL((bwd_kv_lds_kernel<T>), dim3(kv_wgs), dim3(64 * kWaves), 0, st, N, H, HP,
+  if (pass & 2) {
+    const uint32_t ld_none = (uint32_t)((const char*)w.ld_none - (const char*)w.ld);
+    hipLaunchKernelGGL((bwd_kv_lds_kernel<T>), dim3(kv_wgs), dim3(64 * kWaves), 0, st, N, C, H, HP,
                        items, scale, (const T*)q, (const T*)k, (const T*)v, (const T*)dout, q_idx,
-                       (const float2*)w.ld, (const int32_t*)w.off, (const RevEntry*)w.rev,
-                       (const int32_t*)w.rtok, nk, (T*)dk, (T*)dv);
+                       (const float2*)w.ld, ld_none, (const int32_t*)w.off,
+                       (const RevEntry*)w.rev, (const int32_t*)w.rtok, nk, (T*)dk, (T*)dv);
+  }
   return hipGetLastError();
 }
 
 }  // namespace
 
-bool mfma_supported(int dt, int B, int N, int H, int nk) {
-  // 32-bit byte offsets and item counts
+bool mfma_supported(int dt, int B, int N, int C, int H, int nk) {
+  // 32-bit byte offsets (the workspace's LSE/Delta pairs included) and item counts
   const int64_t bytes = (int64_t)B * N * H * D * 2;
-  const int64_t items = (int64_t)B * (N / CS) * ((H + 1) / 2);
+  const int64_t items = (int64_t)B * C * ((H + 1) / 2);
   return (dt == 1 || dt == 2) && nk == NK && bytes < (int64_t(1) << 31) &&
          items < (int64_t(1) << 30);
 }
 
-hipError_t launch_fwd_mfma(int dt, int B, int N, int H, float scale, const void* q, const void* k,
-                           const void* v, const int32_t* q_idx, const int32_t* key_idx, void* o,
-                           float* lse, hipStream_t st) {
-  if (dt == 1) return fwd_t<bf16>(B, N, H, scale, q, k, v, q_idx, key_idx, o, lse, st);
-  if (dt == 2) return fwd_t<f16>(B, N, H, scale, q, k, v, q_idx, key_idx, o, lse, st);
+hipError_t launch_fwd_mfma(int dt, int B, int N, int C, int H, float scale, const void* q,
+                           const void* k, const void* v, const int32_t* q_idx,
+                           const int32_t* key_idx, void* o, float* lse, hipStream_t st) {
+  if (dt == 1) return fwd_t<bf16>(B, N, C, H, scale, q, k, v, q_idx, key_idx, o, lse, st);
+  if (dt == 2) return fwd_t<f16>(B, N, C, H, scale, q, k, v, q_idx, key_idx, o, lse, st);
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_bwd_mfma(int pass, int dt, int B, int N, int H, int nk, float scale,
+hipError_t launch_bwd_mfma(int pass, int dt, int B, int N, int C, int H, int nk, float scale,
                            const void* q, const void* k, const void* v, const void* o,
                            const void* dout, const float* lse, const int32_t* q_idx,
                            const int32_t* key_idx, void* dq, void* dk, void* dv,
                            const BwdWorkspace& w, hipStream_t st) {
   if (dt == 1)
-    return bwd_t<bf16>(pass, B, N, H, nk, scale, q, k, v, o, dout, lse, q_idx, key_idx, dq, dk,
-                       dv, w, st);
+    return bwd_t<bf16>(pass, B, N, C, H, nk, scale, q, k, v, o, dout, lse, q_idx, key_idx, dq,
+                       dk, dv, w, st);
   if (dt == 2)
-    return bwd_t<f16>(pass, B, N, H, nk, scale, q, k, v, o, dout, lse, q_idx, key_idx, dq, dk,
-                      dv, w, st);
+    return bwd_t<f16>(pass, B, N, C, H, nk, scale, q, k, v, o, dout, lse, q_idx, key_idx, dq,
+                      dk, dv, w, st);
   return hipErrorInvalidValue;
 }
 

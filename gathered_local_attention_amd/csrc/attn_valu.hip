@@ -11,7 +11,10 @@
 //
 // Mapping: one 64-lane wavefront per (image, cluster, head).  In the slot
 // phase lane s owns key slot s (its gathered K/V row lives in LDS); in the
-// row phase lane (m, g) owns query m and dims [4g, 4g+4).
+// row phase lane (m, g) owns query m and dims [4g, 4g+4).  A -1 member of a
+// partial cluster is no query: its rows are read from a clamped (valid)
+// token and nothing is written for it; as a key it only appears as -1
+// slots.
 #include "common.h"
 
 namespace ca {
@@ -33,7 +36,7 @@ __device__ __forceinline__ void load_row(const T* __restrict__ src, float* dst) 
 // ---------------------------------------------------------------------------
 template <typename T>
 __global__ void __launch_bounds__(64)
-fwd_valu_kernel(int N, int H, int nk, float scale, const T* __restrict__ q,
+fwd_valu_kernel(int N, int C, int H, int nk, float scale, const T* __restrict__ q,
                 const T* __restrict__ k, const T* __restrict__ v, const int32_t* __restrict__ q_idx,
                 const int32_t* __restrict__ key_idx, T* __restrict__ o, float* __restrict__ lse) {
   __shared__ float qs[CS][kPad];
@@ -42,7 +45,6 @@ fwd_valu_kernel(int N, int H, int nk, float scale, const T* __restrict__ q,
   __shared__ int32_t ts[64];
   __shared__ int32_t qt[CS];
 
-  const int C = N / CS;
   const int h = blockIdx.x % H;
   const int bc = blockIdx.x / H;          // b * C + c
   const int b = bc / C;
@@ -55,7 +57,7 @@ fwd_valu_kernel(int N, int H, int nk, float scale, const T* __restrict__ q,
   __syncthreads();
   {
     const int m = lane >> 3, g = lane & 7;
-    const T* src = q + ((img + qt[m]) * H + h) * D + 4 * g;
+    const T* src = q + ((img + max(qt[m], 0)) * H + h) * D + 4 * g;
 #pragma unroll
     for (int e = 0; e < 4; ++e) qs[m][4 * g + e] = to_f32(src[e]);
   }
@@ -93,6 +95,7 @@ fwd_valu_kernel(int N, int H, int nk, float scale, const T* __restrict__ q,
 #pragma unroll
   for (int r = 0; r < CS; ++r) if (r == m) { lm = l[r]; mm = mx[r]; }
   const float inv = lm > 0.f ? 1.f / lm : 0.f;
+  if (qt[m] < 0) return;   // absent member
   T* dst = o + ((img + qt[m]) * H + h) * D + 4 * g;
 #pragma unroll
   for (int e = 0; e < 4; ++e) dst[e] = from_f32<T>(acc[e] * inv);
@@ -104,7 +107,7 @@ fwd_valu_kernel(int N, int H, int nk, float scale, const T* __restrict__ q,
 // ---------------------------------------------------------------------------
 template <typename T>
 __global__ void __launch_bounds__(64)
-bwd_q_valu_kernel(int N, int H, int nk, float scale, const T* __restrict__ q,
+bwd_q_valu_kernel(int N, int C, int H, int nk, float scale, const T* __restrict__ q,
                   const T* __restrict__ k, const T* __restrict__ v, const T* __restrict__ o,
                   const T* __restrict__ dout, const float* __restrict__ lse,
                   const int32_t* __restrict__ q_idx, const int32_t* __restrict__ key_idx,
@@ -118,7 +121,6 @@ bwd_q_valu_kernel(int N, int H, int nk, float scale, const T* __restrict__ q,
   __shared__ int32_t ts[64];
   __shared__ int32_t qt[CS];
 
-  const int C = N / CS;
   const int h = blockIdx.x % H;
   const int bc = blockIdx.x / H;
   const int b = bc / C;
@@ -130,8 +132,9 @@ bwd_q_valu_kernel(int N, int H, int nk, float scale, const T* __restrict__ q,
   ts[lane] = t;
   __syncthreads();
   const int m = lane >> 3, g = lane & 7;
+  const int qm = max(qt[m], 0);   // absent member: any valid row, never written
   {
-    const int64_t row = ((img + qt[m]) * H + h) * D + 4 * g;
+    const int64_t row = ((img + qm) * H + h) * D + 4 * g;
     float part = 0.f;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -145,8 +148,8 @@ bwd_q_valu_kernel(int N, int H, int nk, float scale, const T* __restrict__ q,
     part += __shfl_xor(part, 4, 64);
     if (g == 0) {
       dels[m] = part;
-      lses[m] = lse[(img + qt[m]) * H + h];
-      ld[(img + qt[m]) * H + h] = make_float2(lses[m] * 1.4426950408889634f, part);
+      lses[m] = lse[(img + qm) * H + h];
+      if (qt[m] >= 0) ld[(img + qm) * H + h] = make_float2(lses[m] * 1.4426950408889634f, part);
     }
   }
   if (t >= 0) {
@@ -179,6 +182,7 @@ bwd_q_valu_kernel(int N, int H, int nk, float scale, const T* __restrict__ q,
 #pragma unroll
     for (int e = 0; e < 4; ++e) acc[e] = fmaf(ds, ks[s][4 * g + e], acc[e]);
   }
+  if (qt[m] < 0) return;
   T* dst = dq + ((img + qt[m]) * H + h) * D + 4 * g;
 #pragma unroll
   for (int e = 0; e < 4; ++e) dst[e] = from_f32<T>(acc[e] * scale);
@@ -189,7 +193,7 @@ bwd_q_valu_kernel(int N, int H, int nk, float scale, const T* __restrict__ q,
 // ---------------------------------------------------------------------------
 template <typename T>
 __global__ void __launch_bounds__(64)
-bwd_kv_valu_kernel(int N, int H, int nk, float scale, const T* __restrict__ q,
+bwd_kv_valu_kernel(int N, int C, int H, int nk, float scale, const T* __restrict__ q,
                    const T* __restrict__ k, const T* __restrict__ v, const T* __restrict__ dout,
                    const float* __restrict__ lse, const int32_t* __restrict__ q_idx,
                    const float2* __restrict__ ld, const int32_t* __restrict__ off_all,
@@ -202,7 +206,6 @@ bwd_kv_valu_kernel(int N, int H, int nk, float scale, const T* __restrict__ q,
   __shared__ float lses[CS], dels[CS];
   __shared__ int32_t kt[CS];
 
-  const int C = N / CS;
   const int h = blockIdx.x % H;
   const int bj = blockIdx.x / H;
   const int b = bj / C;
@@ -214,7 +217,7 @@ bwd_kv_valu_kernel(int N, int H, int nk, float scale, const T* __restrict__ q,
   if (lane < CS) kt[lane] = q_idx[(int64_t)bj * CS + lane];
   __syncthreads();
   {
-    const int64_t row = ((img + kt[hi]) * H + h) * D + 4 * lo;
+    const int64_t row = ((img + max(kt[hi], 0)) * H + h) * D + 4 * lo;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       kj[hi][4 * lo + e] = to_f32(k[row + e]);
@@ -229,8 +232,9 @@ bwd_kv_valu_kernel(int N, int H, int nk, float scale, const T* __restrict__ q,
   for (int e = e0; e < e1; ++e) {
     const RevEntry ent = rev[e];
     __syncthreads();
+    const int qraw = q_idx[((int64_t)b * C + ent.i) * CS + hi];   // -1: absent query
     {
-      const int qtok = q_idx[((int64_t)b * C + ent.i) * CS + hi];
+      const int qtok = max(qraw, 0);
       const int64_t row = ((img + qtok) * H + h) * D + 4 * lo;
 #pragma unroll
       for (int x = 0; x < 4; ++x) {
@@ -245,7 +249,7 @@ bwd_kv_valu_kernel(int N, int H, int nk, float scale, const T* __restrict__ q,
     __syncthreads();
     {
       // lane (m = hi, n = lo): query m of cluster ent.i against key n of j
-      const int mult = (int)((ent.mult >> (8 * lo)) & 0xFFu);
+      const int mult = qraw >= 0 ? (int)((ent.mult >> (8 * lo)) & 0xFFu) : 0;
       float p = 0.f, ds = 0.f;
       if (mult) {
         float sacc = 0.f, pacc = 0.f;
@@ -272,6 +276,7 @@ bwd_kv_valu_kernel(int N, int H, int nk, float scale, const T* __restrict__ q,
       }
     }
   }
+  if (kt[hi] < 0) return;   // absent member of a partial key cluster
   const int64_t row = ((img + kt[hi]) * H + h) * D + 4 * lo;
 #pragma unroll
   for (int x = 0; x < 4; ++x) {
@@ -281,27 +286,27 @@ bwd_kv_valu_kernel(int N, int H, int nk, float scale, const T* __restrict__ q,
 }
 
 template <typename T>
-hipError_t fwd_t(int B, int N, int H, int nk, float scale, const void* q, const void* k,
+hipError_t fwd_t(int B, int N, int C, int H, int nk, float scale, const void* q, const void* k,
                  const void* v, const int32_t* q_idx, const int32_t* key_idx, void* o, float* lse,
                  hipStream_t st) {
-  const int64_t blocks = (int64_t)B * (N / CS) * H;
-  hipLaunchKernelGGL(fwd_valu_kernel<T>, dim3((unsigned)blocks), dim3(64), 0, st, N, H, nk, scale,
-                     (const T*)q, (const T*)k, (const T*)v, q_idx, key_idx, (T*)o, lse);
+  const int64_t blocks = (int64_t)B * C * H;
+  hipLaunchKernelGGL(fwd_valu_kernel<T>, dim3((unsigned)blocks), dim3(64), 0, st, N, C, H, nk,
+                     scale, (const T*)q, (const T*)k, (const T*)v, q_idx, key_idx, (T*)o, lse);
   return hipGetLastError();
 }
 
 template <typename T>
-hipError_t bwd_t(int pass, int B, int N, int H, int nk, float scale, const void* q, const void* k,
-                 const void* v, const void* o, const void* dout, const float* lse,
+hipError_t bwd_t(int pass, int B, int N, int C, int H, int nk, float scale, const void* q,
+                 const void* k, const void* v, const void* o, const void* dout, const float* lse,
                  const int32_t* q_idx, const int32_t* key_idx, void* dq, void* dk, void* dv,
                  const BwdWorkspace& w, hipStream_t st) {
-  const int64_t blocks = (int64_t)B * (N / CS) * H;
+  const int64_t blocks = (int64_t)B * C * H;
   if (pass & 1)
-    hipLaunchKernelGGL(bwd_q_valu_kernel<T>, dim3((unsigned)blocks), dim3(64), 0, st, N, H, nk,
+    hipLaunchKernelGGL(bwd_q_valu_kernel<T>, dim3((unsigned)blocks), dim3(64), 0, st, N, C, H, nk,
                        scale, (const T*)q, (const T*)k, (const T*)v, (const T*)o, (const T*)dout,
                        lse, q_idx, key_idx, (T*)dq, w.ld);
   if (pass & 2)
-    hipLaunchKernelGGL(bwd_kv_valu_kernel<T>, dim3((unsigned)blocks), dim3(64), 0, st, N, H, nk,
+    hipLaunchKernelGGL(bwd_kv_valu_kernel<T>, dim3((unsigned)blocks), dim3(64), 0, st, N, C, H, nk,
                        scale, (const T*)q, (const T*)k, (const T*)v, (const T*)dout, lse, q_idx,
                        (const float2*)w.ld, (const int32_t*)w.off, (const RevEntry*)w.rev,
                        (T*)dk, (T*)dv);
@@ -310,26 +315,26 @@ hipError_t bwd_t(int pass, int B, int N, int H, int nk, float scale, const void*
 
 }  // namespace
 
-hipError_t launch_fwd_valu(int dt, int B, int N, int H, int nk, float scale, const void* q,
+hipError_t launch_fwd_valu(int dt, int B, int N, int C, int H, int nk, float scale, const void* q,
                            const void* k, const void* v, const int32_t* q_idx,
                            const int32_t* key_idx, void* o, float* lse, hipStream_t st) {
   switch (dt) {
-    case 0: return fwd_t<float>(B, N, H, nk, scale, q, k, v, q_idx, key_idx, o, lse, st);
-    case 1: return fwd_t<bf16>(B, N, H, nk, scale, q, k, v, q_idx, key_idx, o, lse, st);
-    case 2: return fwd_t<f16>(B, N, H, nk, scale, q, k, v, q_idx, key_idx, o, lse, st);
+    case 0: return fwd_t<float>(B, N, C, H, nk, scale, q, k, v, q_idx, key_idx, o, lse, st);
+    case 1: return fwd_t<bf16>(B, N, C, H, nk, scale, q, k, v, q_idx, key_idx, o, lse, st);
+    case 2: return fwd_t<f16>(B, N, C, H, nk, scale, q, k, v, q_idx, key_idx, o, lse, st);
   }
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_bwd_valu(int pass, int dt, int B, int N, int H, int nk, float scale,
+hipError_t launch_bwd_valu(int pass, int dt, int B, int N, int C, int H, int nk, float scale,
                            const void* q, const void* k, const void* v, const void* o,
                            const void* dout, const float* lse, const int32_t* q_idx,
                            const int32_t* key_idx, void* dq, void* dk, void* dv,
                            const BwdWorkspace& w, hipStream_t st) {
   switch (dt) {
-    case 0: return bwd_t<float>(pass, B, N, H, nk, scale, q, k, v, o, dout, lse, q_idx, key_idx, dq, dk, dv, w, st);
-    case 1: return bwd_t<bf16>(pass, B, N, H, nk, scale, q, k, v, o, dout, lse, q_idx, key_idx, dq, dk, dv, w, st);
-    case 2: return bwd_t<f16>(pass, B, N, H, nk, scale, q, k, v, o, dout, lse, q_idx, key_idx, dq, dk, dv, w, st);
+    case 0: return bwd_t<float>(pass, B, N, C, H, nk, scale, q, k, v, o, dout, lse, q_idx, key_idx, dq, dk, dv, w, st);
+    case 1: return bwd_t<bf16>(pass, B, N, C, H, nk, scale, q, k, v, o, dout, lse, q_idx, key_idx, dq, dk, dv, w, st);
+    case 2: return bwd_t<f16>(pass, B, N, C, H, nk, scale, q, k, v, o, dout, lse, q_idx, key_idx, dq, dk, dv, w, st);
   }
   return hipErrorInvalidValue;
 }

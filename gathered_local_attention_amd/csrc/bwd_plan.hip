@@ -29,6 +29,8 @@
 //      gathers without a further lookup.
 #include "common.h"
 
+#include <algorithm>
+
 namespace ca {
 
 namespace {
@@ -37,20 +39,30 @@ constexpr int kPlanThreads = 1024;
 constexpr int kMaxNk = 64;
 constexpr int kGridThreads = 256;
 
-__global__ void __launch_bounds__(kGridThreads)
-plan_init_kernel(int64_t n_inv, int64_t n_cnt, int32_t* __restrict__ inv, int32_t* __restrict__ cnt) {
-  const int64_t x = (int64_t)blockIdx.x * kGridThreads + threadIdx.x;
-  if (x < n_inv) inv[x] = -1;
-  if (x < n_cnt) cnt[x] = 0;
+// The (LSE * log2 e, Delta) pair the key-major pass reads for an absent
+// query (a -1 member of a partial cluster): P = exp2(s - inf) = 0 there.
+__device__ __forceinline__ void write_ld_none(float4* ld_none) {
+  *ld_none = make_float4(INFINITY, 0.f, INFINITY, 0.f);
 }
 
 __global__ void __launch_bounds__(kGridThreads)
-plan_inv_kernel(int B, int N, const int32_t* __restrict__ q_idx, int32_t* __restrict__ inv) {
+plan_init_kernel(int64_t n_inv, int64_t n_cnt, int32_t* __restrict__ inv, int32_t* __restrict__ cnt,
+                 float4* __restrict__ ld_none) {
   const int64_t x = (int64_t)blockIdx.x * kGridThreads + threadIdx.x;
-  if (x >= (int64_t)B * N) return;
-  const int64_t b = x / N;
+  if (x < n_inv) inv[x] = -1;
+  if (x < n_cnt) cnt[x] = 0;
+  if (x == 0) write_ld_none(ld_none);
+}
+
+// one thread per q_idx position (c*8 + m) of the batch
+__global__ void __launch_bounds__(kGridThreads)
+plan_inv_kernel(int B, int N, int C, const int32_t* __restrict__ q_idx, int32_t* __restrict__ inv) {
+  const int64_t x = (int64_t)blockIdx.x * kGridThreads + threadIdx.x;
+  const int P = 8 * C;
+  if (x >= (int64_t)B * P) return;
+  const int64_t b = x / P;
   const int t = q_idx[x];
-  if (t >= 0 && t < N) inv[b * N + t] = (int32_t)(x - b * N);
+  if (t >= 0 && t < N) inv[b * N + t] = (int32_t)(x - b * P);
 }
 
 // one thread per query cluster; its slots' key positions are staged in LDS.
@@ -60,11 +72,10 @@ plan_inv_kernel(int B, int N, const int32_t* __restrict__ q_idx, int32_t* __rest
 constexpr int kCountThreads = 64;
 
 __global__ void __launch_bounds__(kCountThreads)
-plan_count_kernel(int B, int N, int nk, const int32_t* __restrict__ key_idx,
+plan_count_kernel(int B, int N, int C, int nk, const int32_t* __restrict__ key_idx,
                   const int32_t* __restrict__ inv, int32_t* __restrict__ cnt,
                   RevEntry* __restrict__ stage) {
   __shared__ int32_t jn[kCountThreads][kMaxNk + 1];
-  const int C = N / 8;
   const int64_t bc = (int64_t)blockIdx.x * kCountThreads + threadIdx.x;
   if (bc >= (int64_t)B * C) return;
   const int64_t b = bc / C;
@@ -198,10 +209,9 @@ plan_place_kernel(int B, int C, int nk, const RevEntry* __restrict__ stage,
 constexpr int kSortRegs = 16;
 
 __global__ void __launch_bounds__(kGridThreads)
-plan_sort_kernel(int B, int N, int nk, const int32_t* __restrict__ q_idx,
+plan_sort_kernel(int B, int C, int nk, const int32_t* __restrict__ q_idx,
                  const int32_t* __restrict__ off_all, RevEntry* __restrict__ rev_all,
                  int32_t* __restrict__ rtok_all) {
-  const int C = N / 8;
   const int64_t bj = (int64_t)blockIdx.x * kGridThreads + threadIdx.x;
   if (bj >= (int64_t)B * C) return;
   const int64_t b = bj / C;
@@ -210,7 +220,7 @@ plan_sort_kernel(int B, int N, int nk, const int32_t* __restrict__ q_idx,
   RevEntry* rev = rev_all + b * C * nk;
   const int a = off[j], z = off[j + 1];
   int4* rt = reinterpret_cast<int4*>(rtok_all + b * C * nk * 8);
-  const int32_t* qi = q_idx + b * N;
+  const int32_t* qi = q_idx + b * C * 8;
   if (z - a <= kSortRegs) {
     int ii[kSortRegs];
     uint64_t mm[kSortRegs];
@@ -289,9 +299,10 @@ constexpr int kPlanMaxSlots = 12288;
 constexpr int kGroupsPer = (kPlanMaxSlots / 8 + kPlanThreads - 1) / kPlanThreads;   // 2
 
 __global__ void __launch_bounds__(kPlanThreads)
-plan_small_kernel(int N, int nk, const int32_t* __restrict__ q_idx,
+plan_small_kernel(int N, int C, int nk, const int32_t* __restrict__ q_idx,
                   const int32_t* __restrict__ key_idx, int32_t* __restrict__ off_all,
-                  RevEntry* __restrict__ rev_all, int32_t* __restrict__ rtok_all) {
+                  RevEntry* __restrict__ rev_all, int32_t* __restrict__ rtok_all,
+                  float4* __restrict__ ld_none) {
   __shared__ int32_t inv[kSortChunk];                       // token -> position c*8 + m
   __shared__ __attribute__((aligned(16))) int32_t qp[kSortChunk];   // position -> token
   __shared__ uint32_t bits[kPlanMaxC][kPlanWords];
@@ -300,11 +311,12 @@ plan_small_kernel(int N, int nk, const int32_t* __restrict__ q_idx,
   __shared__ uint8_t ent_i[kPlanMaxSlots];                  // entry -> its query cluster i
   __shared__ int32_t tmp[17];
   const int b = blockIdx.x;
-  const int C = N / 8;
   const int tid = threadIdx.x;
   const int ns = C * nk;
   const int ngroups = ns / 8;
-  const int32_t* qi = q_idx + (int64_t)b * N;
+  const int P = 8 * C;                                       // q_idx positions, <= 2048
+  const int32_t* qi = q_idx + (int64_t)b * P;
+  if (b == 0 && tid == 0) write_ld_none(ld_none);
   const int32_t* ki = key_idx + (int64_t)b * ns;
 
   // this thread's slot groups gr = tid + r * 1024, loaded up front
@@ -320,12 +332,12 @@ plan_small_kernel(int N, int nk, const int32_t* __restrict__ q_idx,
     tok[r][0] = a.x; tok[r][1] = a.y; tok[r][2] = a.z; tok[r][3] = a.w;
     tok[r][4] = c.x; tok[r][5] = c.y; tok[r][6] = c.z; tok[r][7] = c.w;
   }
-  const int q0 = tid < N ? qi[tid] : -1;                       // N <= 2048
-  const int q1 = tid + kPlanThreads < N ? qi[tid + kPlanThreads] : -1;
+  const int q0 = tid < P ? qi[tid] : -1;                       // -1: absent member
+  const int q1 = tid + kPlanThreads < P ? qi[tid + kPlanThreads] : -1;
   for (int t = tid; t < N; t += kPlanThreads) inv[t] = -1;
   for (int x = tid; x < kPlanMaxC * kPlanWords; x += kPlanThreads) (&bits[0][0])[x] = 0u;
-  if (tid < N) qp[tid] = q0;
-  if (tid + kPlanThreads < N) qp[tid + kPlanThreads] = q1;
+  if (tid < P) qp[tid] = q0;
+  if (tid + kPlanThreads < P) qp[tid + kPlanThreads] = q1;
   __syncthreads();
   if (q0 >= 0) inv[q0] = tid;
   if (q1 >= 0) inv[q1] = tid + kPlanThreads;
@@ -399,9 +411,11 @@ plan_small_kernel(int N, int nk, const int32_t* __restrict__ q_idx,
   for (int r = 0; r < kGroupsPer; ++r) {
     const int i = (tid + r * kPlanThreads) * 8 / nk;
     const uint32_t below = (1u << (i & 31)) - 1u;
-    if (one[r]) {   // members 0..7 once each
+    if (one[r]) {   // the members of j once each (absent members: -1 slots)
       const int jj = jn[r][0] >> 3;
-      const uint64_t add = 0x0101010101010101ull;
+      uint64_t add = 0;
+#pragma unroll
+      for (int m = 0; m < 8; ++m) add |= tok[r][m] >= 0 ? 1ull << (8 * m) : 0ull;
       const int pos = wo[jj][i >> 5] + __popc(bits[jj][i >> 5] & below);
       atomicAdd(&mult[pos], (unsigned long long)add);
       ent_i[pos] = (uint8_t)i;
@@ -444,28 +458,28 @@ plan_small_kernel(int N, int nk, const int32_t* __restrict__ q_idx,
 
 }  // namespace
 
-hipError_t launch_bwd_plan(int B, int N, int nk, const int32_t* q_idx, const int32_t* key_idx,
-                           const BwdWorkspace& w, hipStream_t st) {
+hipError_t launch_bwd_plan(int B, int N, int C, int nk, const int32_t* q_idx,
+                           const int32_t* key_idx, const BwdWorkspace& w, hipStream_t st) {
   if (nk > kMaxNk) return hipErrorInvalidValue;
-  const int C = N / 8;
   if (N <= kSortChunk && C <= kPlanMaxC && C * nk <= kPlanMaxSlots && nk % 8 == 0) {
-    hipLaunchKernelGGL(plan_small_kernel, dim3(B), dim3(kPlanThreads), 0, st, N, nk, q_idx, key_idx,
-                       w.off, w.rev, w.rtok);
+    hipLaunchKernelGGL(plan_small_kernel, dim3(B), dim3(kPlanThreads), 0, st, N, C, nk, q_idx,
+                       key_idx, w.off, w.rev, w.rtok, w.ld_none);
     return hipGetLastError();
   }
   const int64_t tokens = (int64_t)B * N, clusters = (int64_t)B * C;
   auto grid = [](int64_t n) { return dim3((unsigned)((n + kGridThreads - 1) / kGridThreads)); };
-  hipLaunchKernelGGL(plan_init_kernel, grid(tokens), dim3(kGridThreads), 0, st, tokens, clusters,
-                     w.inv, w.cnt);
-  hipLaunchKernelGGL(plan_inv_kernel, grid(tokens), dim3(kGridThreads), 0, st, B, N, q_idx, w.inv);
+  hipLaunchKernelGGL(plan_init_kernel, grid(std::max<int64_t>(tokens, 1)), dim3(kGridThreads), 0,
+                     st, tokens, clusters, w.inv, w.cnt, w.ld_none);
+  hipLaunchKernelGGL(plan_inv_kernel, grid(clusters * 8), dim3(kGridThreads), 0, st, B, N, C,
+                     q_idx, w.inv);
   hipLaunchKernelGGL(plan_count_kernel, dim3((unsigned)((clusters + kCountThreads - 1) / kCountThreads)),
-                     dim3(kCountThreads), 0, st, B, N, nk, key_idx, (const int32_t*)w.inv, w.cnt,
-                     w.stage);
+                     dim3(kCountThreads), 0, st, B, N, C, nk, key_idx, (const int32_t*)w.inv,
+                     w.cnt, w.stage);
   hipLaunchKernelGGL(plan_scan_kernel, dim3(B), dim3(kPlanThreads), 0, st, C,
                      (const int32_t*)w.cnt, w.off, w.cursor);
   hipLaunchKernelGGL(plan_place_kernel, grid(clusters), dim3(kGridThreads), 0, st, B, C, nk,
                      (const RevEntry*)w.stage, w.cursor, w.rev);
-  hipLaunchKernelGGL(plan_sort_kernel, grid(clusters), dim3(kGridThreads), 0, st, B, N, nk, q_idx,
+  hipLaunchKernelGGL(plan_sort_kernel, grid(clusters), dim3(kGridThreads), 0, st, B, C, nk, q_idx,
                      (const int32_t*)w.off, w.rev, w.rtok);
   return hipGetLastError();
 }

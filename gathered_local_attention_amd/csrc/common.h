@@ -30,6 +30,7 @@ struct RevEntry {
 // ---- workspace layout of the backward pass --------------------------------
 struct BwdWorkspace {
   float2* ld;        // [B, N, H]   (LSE * log2(e), Delta) per query and head
+  float4* ld_none;   // (+inf, 0, +inf, 0): the pair read for an absent query
   int32_t* inv;      // [B, N]      token -> position in q_idx (c*cs + m)
   int32_t* cnt;      // [B, C]      entries per key cluster
   int32_t* off;      // [B, C + 1]  segment starts (per image, relative)
@@ -53,6 +54,7 @@ static inline BwdWorkspace bwd_layout(void* base, int64_t B, int64_t N, int64_t 
     return b ? (void*)(b + at) : (void*)nullptr;
   };
   w.ld = (float2*)take((size_t)(B * N * H) * sizeof(float2));
+  w.ld_none = (float4*)take(sizeof(float4));
   w.inv = (int32_t*)take((size_t)(B * N) * sizeof(int32_t));
   w.cnt = (int32_t*)take((size_t)(B * C) * sizeof(int32_t));
   w.off = (int32_t*)take((size_t)(B * (C + 1)) * sizeof(int32_t));
@@ -68,17 +70,61 @@ static inline BwdWorkspace bwd_layout(void* base, int64_t B, int64_t N, int64_t 
 constexpr int kSortChunk = 2048;   // images up to this many tokens are built in LDS
 constexpr int kRankSeg = 512;      // larger images: tokens ranked together before merging
 constexpr int kBoxTile = 64;       // consecutive clusters per bounding box
+constexpr int kIdxBits = 19;       // cluster index bits of a (distance, index) key
+constexpr int64_t kMaxTokensPerImage = int64_t(8) << kIdxBits;
+
+// Where the images of a batch lie.  Equal-size images (tok_off == nullptr):
+// image b holds tokens [b*N, (b+1)*N) and clusters [b*C, (b+1)*C), and the
+// lists carry image-local ids.  Packed images of different sizes: the
+// device arrays tok_off / clu_off [B+1] give both ranges, and the lists
+// carry batch-global ids.  N and C are then the largest image's sizes.
+struct Geom {
+  const int32_t* tok_off;
+  const int32_t* clu_off;
+  int N, C;
+  __device__ __forceinline__ void image(int b, int& t0, int& n, int& c0, int& nc) const {
+    if (tok_off) {
+      t0 = tok_off[b];
+      n = tok_off[b + 1] - t0;
+      c0 = clu_off[b];
+      nc = clu_off[b + 1] - c0;
+    } else {
+      t0 = b * N;
+      n = N;
+      c0 = b * C;
+      nc = C;
+    }
+  }
+  // base added to the image-local token / cluster ids written out
+  __device__ __forceinline__ int tok_base(int t0) const { return tok_off ? t0 : 0; }
+  __device__ __forceinline__ int clu_base(int c0) const { return tok_off ? c0 : 0; }
+};
+
+// A cluster's centroid is compared through its mean; the integer sums of
+// its members' fixed-point coordinates are scaled by L / members, with L the
+// least common multiple of the two cluster sizes of the image (8, and
+// n mod 8 for the partial last cluster), which makes every centroid L times
+// the mean, exactly.  Images whose size is a multiple of 8 keep the plain
+// sums (factor 1).  Factors are at most 8 (scaled sums below 2^22).
+__host__ __device__ __forceinline__ int mean_scale(int members, int n) {
+  const int r = n & 7;
+  if (r == 0) return 1;
+  const int L = 8 * r / (r & -r);   // lcm(8, r): gcd(8, r) is r's lowest set bit
+  return L / members;
+}
 
 struct BuildWorkspace {
-  uint32_t* qsorted;   // [B, N]  packed (qx | qy << 16) in cluster order
-  uint64_t* keys[2];   // [B, N]  (code << 32 | token) in sorted runs, two buffers
-  float2* cent;        // [B, C]  centroid sums
-  float4* box;         // [B, ceil(C / kBoxTile)]  centroid bounding boxes
+  uint32_t* qsorted;   // [Ct * 8] packed (qx | qy << 16) in cluster order
+  uint64_t* keys[2];   // [T]      (code << 32 | token) in sorted runs, two buffers
+  float2* cent;        // [Ct]     scaled centroid sums
+  float4* box;         // [B, ceil(Cmax / kBoxTile)]  centroid bounding boxes
   size_t bytes;
 };
 
-// Everything is only needed for images above kSortChunk tokens.
-static inline BuildWorkspace build_layout(void* base, int64_t B, int64_t N) {
+// Everything is only needed when some image has more than kSortChunk
+// tokens: T tokens and Ct clusters in the batch, the largest image maxN.
+static inline BuildWorkspace build_layout(void* base, int64_t B, int64_t T, int64_t Ct,
+                                          int64_t maxN) {
   BuildWorkspace w;
   size_t p = 0;
   char* b = (char*)base;
@@ -87,12 +133,12 @@ static inline BuildWorkspace build_layout(void* base, int64_t B, int64_t N) {
     p = align_up(p + n, 256);
     return b ? (void*)(b + at) : (void*)nullptr;
   };
-  const bool big = N > kSortChunk;
-  const int64_t C = N / 8, tiles = (C + kBoxTile - 1) / kBoxTile;
-  w.qsorted = (uint32_t*)take(big ? (size_t)(B * N) * sizeof(uint32_t) : 0);
-  w.keys[0] = (uint64_t*)take(big ? (size_t)(B * N) * sizeof(uint64_t) : 0);
-  w.keys[1] = (uint64_t*)take(big ? (size_t)(B * N) * sizeof(uint64_t) : 0);
-  w.cent = (float2*)take(big ? (size_t)(B * C) * sizeof(float2) : 0);
+  const bool big = maxN > kSortChunk;
+  const int64_t tiles = ((maxN + 7) / 8 + kBoxTile - 1) / kBoxTile;
+  w.qsorted = (uint32_t*)take(big ? (size_t)(Ct * 8) * sizeof(uint32_t) : 0);
+  w.keys[0] = (uint64_t*)take(big ? (size_t)T * sizeof(uint64_t) : 0);
+  w.keys[1] = (uint64_t*)take(big ? (size_t)T * sizeof(uint64_t) : 0);
+  w.cent = (float2*)take(big ? (size_t)Ct * sizeof(float2) : 0);
   w.box = (float4*)take(big ? (size_t)(B * tiles) * sizeof(float4) : 0);
   w.bytes = p;
   return w;
@@ -199,32 +245,35 @@ __device__ __forceinline__ uint32_t quantize_axis(float c, double step) {
 }
 
 // ---- launchers (defined in the .hip files) ---------------------------------
-hipError_t launch_build_neighbors(const float* coords, int B, int N, int grid_side, int k,
-                                  int32_t* perm, int32_t* nbr, int32_t* key_idx, void* ws,
-                                  hipStream_t st);
+// Attention launchers take B images of N tokens and C clusters each (q_idx
+// [B, C, 8], C = ceil(N / 8)); a packed batch runs as one image (B = 1) of
+// all T tokens and Ct clusters with batch-global ids.
+hipError_t launch_build_neighbors(const float* coords, const Geom& g, int B, int64_t T, int64_t Ct,
+                                  int grid_side, int k, int32_t* q_idx, int32_t* nbr,
+                                  int32_t* key_idx, void* ws, hipStream_t st);
 
-hipError_t launch_fwd_valu(int dt, int B, int N, int H, int nk, float scale, const void* q,
+hipError_t launch_fwd_valu(int dt, int B, int N, int C, int H, int nk, float scale, const void* q,
                            const void* k, const void* v, const int32_t* q_idx,
                            const int32_t* key_idx, void* o, float* lse, hipStream_t st);
 
-hipError_t launch_bwd_plan(int B, int N, int nk, const int32_t* q_idx, const int32_t* key_idx,
-                           const BwdWorkspace& w, hipStream_t st);
+hipError_t launch_bwd_plan(int B, int N, int C, int nk, const int32_t* q_idx,
+                           const int32_t* key_idx, const BwdWorkspace& w, hipStream_t st);
 
 // Backward launchers: pass bit 1 = pass A (Delta, dQ; needs nothing from the
 // plan), bit 2 = pass B (dK, dV; needs pass A and the plan).
-hipError_t launch_bwd_valu(int pass, int dt, int B, int N, int H, int nk, float scale,
+hipError_t launch_bwd_valu(int pass, int dt, int B, int N, int C, int H, int nk, float scale,
                            const void* q, const void* k, const void* v, const void* o,
                            const void* dout, const float* lse, const int32_t* q_idx,
                            const int32_t* key_idx, void* dq, void* dk, void* dv,
                            const BwdWorkspace& w, hipStream_t st);
 
-bool mfma_supported(int dt, int B, int N, int H, int nk);
+bool mfma_supported(int dt, int B, int N, int C, int H, int nk);
 
-hipError_t launch_fwd_mfma(int dt, int B, int N, int H, float scale, const void* q, const void* k,
-                           const void* v, const int32_t* q_idx, const int32_t* key_idx, void* o,
-                           float* lse, hipStream_t st);
+hipError_t launch_fwd_mfma(int dt, int B, int N, int C, int H, float scale, const void* q,
+                           const void* k, const void* v, const int32_t* q_idx,
+                           const int32_t* key_idx, void* o, float* lse, hipStream_t st);
 
-hipError_t launch_bwd_mfma(int pass, int dt, int B, int N, int H, int nk, float scale,
+hipError_t launch_bwd_mfma(int pass, int dt, int B, int N, int C, int H, int nk, float scale,
                            const void* q, const void* k, const void* v, const void* o,
                            const void* dout, const float* lse, const int32_t* q_idx,
                            const int32_t* key_idx, void* dq, void* dk, void* dv,

@@ -28,8 +28,16 @@
 //   select_box_kernel   per cluster: candidate scan of its own tile, then of
 //                       every other tile whose box lies within the current
 //                       (k-1)-th best distance of some cluster of the wave;
-//                       keeps the k-1 smallest (d2 << 24 | index) keys, then
-//                       writes the key lists.
+//                       keeps the k-1 smallest (d2 << kIdxBits | index) keys,
+//                       then writes the key lists.
+//
+// Ragged images: an image of n tokens has ceil(n / 8) clusters, the last
+// one holding n mod 8 members when 8 does not divide n; its q_idx row and
+// the key slots of its absent members are -1.  Centroids are compared
+// through their means (sums scaled by mean_scale).  A packed batch of
+// images of different sizes (Geom with offsets) is built image by image:
+// images of at most kSortChunk tokens by the in-LDS kernel, larger ones by
+// the segment / merge path; both skip the other's images.
 #include "common.h"
 
 #include <algorithm>
@@ -59,21 +67,25 @@ __device__ __forceinline__ uint32_t compact16(uint32_t v) {
 }
 
 
-// Rank the tokens of one segment.  grid = (ceil(L / 64), segments), where a
-// segment is [seg_start, seg_start + L) of image `b`.  Each workgroup ranks
-// 64 tokens (one per lane); its four wavefronts each count one quarter of
-// the segment's keys, read from LDS as broadcast 16-byte loads.  The keys
-// land sorted inside their segment.
+// Rank the tokens of one segment.  grid = (kRankSeg / 64, B * segs), where
+// segment `seg % segs` of image `seg / segs` is [start, start + L) of that
+// image.  Each workgroup ranks 64 tokens (one per lane); its four
+// wavefronts each count one quarter of the segment's keys, read from LDS as
+// broadcast 16-byte loads.  The keys land sorted inside their segment.
 __global__ void __launch_bounds__(kRankThreads)
-rank_kernel(const float* __restrict__ coords, int N, int seg_len, int segs_per_image, double step,
+rank_kernel(const float* __restrict__ coords, Geom g, int segs_per_image, double step,
             uint64_t* __restrict__ run_keys) {
   __shared__ __align__(16) uint64_t keys[kRankSeg];
   __shared__ int part[kRankThreads / 64][64];
   const int seg = blockIdx.y;
   const int b = seg / segs_per_image;
-  const int start = (seg % segs_per_image) * seg_len;
-  const int L = min(seg_len, N - start);
-  const float2* xy = reinterpret_cast<const float2*>(coords) + (int64_t)b * N + start;
+  const int start = (seg % segs_per_image) * kRankSeg;
+  int t0, n, c0, nc;
+  g.image(b, t0, n, c0, nc);
+  if (n <= kSortChunk) return;                        // built by the in-LDS kernel
+  const int L = min(kRankSeg, n - start);
+  if (L <= 0) return;
+  const float2* xy = reinterpret_cast<const float2*>(coords) + (int64_t)t0 + start;
 
   for (int e = threadIdx.x; e < L; e += kRankThreads) {
     float2 c = xy[e];
@@ -100,73 +112,78 @@ rank_kernel(const float* __restrict__ coords, int N, int seg_len, int segs_per_i
   __syncthreads();
   if (w != 0 || e >= L) return;
   const int rank = part[0][lane] + part[1][lane] + part[2][lane] + part[3][lane];
-  run_keys[(int64_t)b * N + start + rank] = mine;
+  run_keys[(int64_t)t0 + start + rank] = mine;
 }
 
 // One round of the image-wide merge sort.  Sorted runs of `run` keys (a
-// power of two) are merged pairwise; grid = (ceil(N / 256), B), one thread
-// per key.  Keys are unique (they hold the token index), so a key's place in
-// the merged run is its place in its own run plus the number of keys of the
-// partner run below it.  The last round (out == nullptr) writes the token
-// order and the packed quantised coordinates, decoded from the code.
+// power of two) are merged pairwise; grid = (ceil(Nmax / 256), B), one
+// thread per key.  Keys are unique (they hold the token index), so a key's
+// place in the merged run is its place in its own run plus the number of
+// keys of the partner run below it (an image already in one run is
+// copied).  The last round (out == nullptr) writes the q_idx rows (token
+// ids) and the packed quantised coordinates, decoded from the code, at the
+// image's cluster slots.
 __global__ void __launch_bounds__(kRankThreads)
-merge_round_kernel(int N, int run, const uint64_t* __restrict__ in, uint64_t* __restrict__ out,
-                   int32_t* __restrict__ perm, uint32_t* __restrict__ qsorted) {
+merge_round_kernel(Geom g, int run, const uint64_t* __restrict__ in, uint64_t* __restrict__ out,
+                   int32_t* __restrict__ q_idx, uint32_t* __restrict__ qsorted) {
   const int x = blockIdx.x * kRankThreads + threadIdx.x;
-  const int64_t b = blockIdx.y;
-  if (x >= N) return;
-  const uint64_t* img = in + b * N;
+  int t0, n, c0, nc;
+  g.image(blockIdx.y, t0, n, c0, nc);
+  if (n <= kSortChunk || x >= n) return;
+  const uint64_t* img = in + t0;
   const uint64_t key = img[x];
   const int p0 = x & ~(2 * run - 1);
   const bool first = x - p0 < run;
   const int own0 = first ? p0 : p0 + run;
   int lo = first ? p0 + run : p0;
-  int hi = first ? min(p0 + 2 * run, N) : p0 + run;
+  int hi = first ? min(p0 + 2 * run, n) : p0 + run;
   hi = max(hi, lo);   // a last run without partner
   const int base = lo;
   while (lo < hi) {
     const int mid = (lo + hi) >> 1;
     if (img[mid] < key) lo = mid + 1; else hi = mid;
   }
-  const int64_t at = b * N + p0 + (x - own0) + (lo - base);
+  const int pos = p0 + (x - own0) + (lo - base);
   if (out) {
-    out[at] = key;
+    out[(int64_t)t0 + pos] = key;
   } else {
     const uint32_t code = (uint32_t)(key >> 32);
-    perm[at] = (int32_t)(uint32_t)key;
+    const int64_t at = (int64_t)c0 * 8 + pos;
+    q_idx[at] = g.tok_base(t0) + (int32_t)(uint32_t)key;
     qsorted[at] = compact16(code) | (compact16(code >> 1) << 16);
   }
 }
 
-__device__ __forceinline__ float2 centroid_sum(const uint32_t* __restrict__ q8) {
-  // integer sums of eight 16-bit coordinates (< 2^19): exact as floats
-  const uint4 a = *reinterpret_cast<const uint4*>(q8);
-  const uint4 c = *reinterpret_cast<const uint4*>(q8 + 4);
-  const uint32_t w[8] = {a.x, a.y, a.z, a.w, c.x, c.y, c.z, c.w};
-  int sx = 0, sy = 0;
-#pragma unroll
-  for (int m = 0; m < 8; ++m) {
-    sx += (int)(w[m] & 0xFFFFu);
-    sy += (int)(w[m] >> 16);
-  }
-  return make_float2((float)sx, (float)sy);
-}
-
-// Centroid sums of every cluster and the bounding box (min x, min y, max x,
-// max y) of every tile of kBoxTile consecutive clusters.  grid =
-// (ceil(C / kBoxTile), B), one wavefront per tile.
+// Scaled centroid sums of every cluster and the bounding box (min x, min
+// y, max x, max y) of every tile of kBoxTile consecutive clusters of an
+// image.  grid = (ceil(Cmax / kBoxTile), B), one wavefront per tile.  The
+// absent members of a partial last cluster get -1 in q_idx here.
 __global__ void __launch_bounds__(kBoxTile)
-centroid_box_kernel(int C, const uint32_t* __restrict__ qsorted, float2* __restrict__ cent_all,
-                    float4* __restrict__ box_all) {
+centroid_box_kernel(Geom g, const uint32_t* __restrict__ qsorted, float2* __restrict__ cent_all,
+                    float4* __restrict__ box_all, int32_t* __restrict__ q_idx) {
   const int t = blockIdx.x;
-  const int64_t b = blockIdx.y;
+  const int b = blockIdx.y;
+  int t0, n, c0, nc;
+  g.image(b, t0, n, c0, nc);
+  if (n <= kSortChunk) return;
   const int c = t * kBoxTile + threadIdx.x;
   float lx = INFINITY, ly = INFINITY, hx = -INFINITY, hy = -INFINITY;
-  if (c < C) {
-    const float2 s = centroid_sum(qsorted + (b * C + c) * 8);
-    cent_all[b * C + c] = s;
+  if (c < nc) {
+    const int members = min(8, n - 8 * c);
+    const uint32_t* q8 = qsorted + ((int64_t)c0 + c) * 8;
+    int sx = 0, sy = 0;
+    for (int m = 0; m < members; ++m) {
+      const uint32_t w = q8[m];
+      sx += (int)(w & 0xFFFFu);
+      sy += (int)(w >> 16);
+    }
+    const int f = mean_scale(members, n);
+    // below 2^22: exact as floats
+    const float2 s = make_float2((float)(sx * f), (float)(sy * f));
+    cent_all[(int64_t)c0 + c] = s;
     lx = hx = s.x;
     ly = hy = s.y;
+    for (int m = members; m < 8; ++m) q_idx[((int64_t)c0 + c) * 8 + m] = -1;
   }
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) {
@@ -175,7 +192,7 @@ centroid_box_kernel(int C, const uint32_t* __restrict__ qsorted, float2* __restr
     hx = fmaxf(hx, __shfl_xor(hx, o, 64));
     hy = fmaxf(hy, __shfl_xor(hy, o, 64));
   }
-  if (threadIdx.x == 0) box_all[b * gridDim.x + t] = make_float4(lx, ly, hx, hy);
+  if (threadIdx.x == 0) box_all[(int64_t)b * gridDim.x + t] = make_float4(lx, ly, hx, hy);
 }
 
 template <int KM1>
@@ -193,7 +210,8 @@ __device__ __forceinline__ void top_insert(uint64_t (&best)[KM1 > 0 ? KM1 : 1], 
 }
 
 // Scan one tile of candidate centroids (staged in this wave's LDS row) for
-// the lanes with `need`, keeping the KM1 smallest (d2 << 24 | index) keys.
+// the lanes with `need`, keeping the KM1 smallest (d2 << kIdxBits | index)
+// keys (scaled sums below 2^22: d2 < 2^45, so a key fits 64 bits).
 // Candidates are screened with an fp32 distance whose error bound (relative
 // 2^-23) cannot drop a candidate at or below the current KM1-th best; the
 // survivors are compared exactly in 64 bits, so the kept set does not depend
@@ -224,7 +242,7 @@ __device__ __forceinline__ void scan_tile(const float2* __restrict__ cent, float
       const float d2f = fmaf(dx, dx, dy * dy);
       if (e >= T || d2f > thr || t0 + e == c) continue;
       const int ix = (int)dx, iy = (int)dy;
-      const uint64_t key = ((uint64_t)((int64_t)ix * ix + (int64_t)iy * iy) << 24) | (uint32_t)(t0 + e);
+      const uint64_t key = ((uint64_t)((int64_t)ix * ix + (int64_t)iy * iy) << kIdxBits) | (uint32_t)(t0 + e);
       if (key >= best[KM1 - 1]) continue;
       uint64_t x = key;
 #pragma unroll
@@ -234,7 +252,7 @@ __device__ __forceinline__ void scan_tile(const float2* __restrict__ cent, float
         best[r] = lo;
         x = hi;
       }
-      if (best[KM1 - 1] != ~0ull) thr = (float)(best[KM1 - 1] >> 24) * (1.0f + 0x1p-20f);
+      if (best[KM1 - 1] != ~0ull) thr = (float)(best[KM1 - 1] >> kIdxBits) * (1.0f + 0x1p-20f);
     }
   }
 }
@@ -262,21 +280,23 @@ constexpr int kSelWaves = 4;
 
 template <int KM1>
 __global__ void __launch_bounds__(kBoxTile * kSelWaves)
-select_box_kernel(int N, const float2* __restrict__ cent_all, const float4* __restrict__ box_all,
-                  const int32_t* __restrict__ perm, int32_t* __restrict__ nbr,
+select_box_kernel(Geom g, const float2* __restrict__ cent_all, const float4* __restrict__ box_all,
+                  const int32_t* __restrict__ q_idx, int32_t* __restrict__ nbr,
                   int32_t* __restrict__ key_idx) {
   constexpr int KB = KM1 > 0 ? KM1 : 1;
   __shared__ __align__(16) float2 cand[kSelWaves][kBoxTile];
   __shared__ uint64_t part[kSelWaves - 1][KB][kBoxTile];
-  const int C = N / 8;
-  const int ntiles = gridDim.x;
   const int b = blockIdx.y;
+  int t0, n, c0, C;
+  g.image(b, t0, n, c0, C);
+  const int ntiles = (C + kBoxTile - 1) / kBoxTile;
   const int own = blockIdx.x;
+  if (n <= kSortChunk || own >= ntiles) return;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int c = own * kBoxTile + lane;
   const bool valid = c < C;
-  const float2* cent = cent_all + (int64_t)b * C;
-  const float4* box = box_all + (int64_t)b * ntiles;
+  const float2* cent = cent_all + c0;
+  const float4* box = box_all + (int64_t)b * gridDim.x;
   const float2 me = valid ? cent[c] : make_float2(0.f, 0.f);
 
   uint64_t best[KB];
@@ -342,17 +362,20 @@ select_box_kernel(int N, const float2* __restrict__ cent_all, const float4* __re
   if (!valid) return;
 
   constexpr int K = KM1 + 1;
+  constexpr uint64_t kIdxMask = (uint64_t(1) << kIdxBits) - 1;
   int32_t ids[K];
   ids[0] = c;
 #pragma unroll
-  for (int r = 0; r < KM1; ++r) ids[r + 1] = best[r] == ~0ull ? -1 : (int32_t)(best[r] & 0xFFFFFFu);
-  int32_t* nrow = nbr + ((int64_t)b * C + c) * K;
-  int4* krow = reinterpret_cast<int4*>(key_idx + ((int64_t)b * C + c) * K * 8);
-  const int4* pimg = reinterpret_cast<const int4*>(perm + (int64_t)b * N);
+  for (int r = 0; r < KM1; ++r) ids[r + 1] = best[r] == ~0ull ? -1 : (int32_t)(best[r] & kIdxMask);
+  const int cb = g.clu_base(c0);
+  int32_t* nrow = nbr + ((int64_t)c0 + c) * K;
+  int4* krow = reinterpret_cast<int4*>(key_idx + ((int64_t)c0 + c) * K * 8);
+  // q_idx rows of the image: token ids as written out, -1 for absent members
+  const int4* pimg = reinterpret_cast<const int4*>(q_idx + (int64_t)c0 * 8);
   const int4 none = make_int4(-1, -1, -1, -1);
 #pragma unroll
   for (int s = 0; s < K; ++s) {
-    nrow[s] = ids[s];
+    nrow[s] = ids[s] >= 0 ? cb + ids[s] : -1;
     krow[2 * s] = ids[s] >= 0 ? pimg[2 * ids[s]] : none;
     krow[2 * s + 1] = ids[s] >= 0 ? pimg[2 * ids[s] + 1] : none;
   }
@@ -376,8 +399,8 @@ constexpr int kMaxBucket = 32;                    // larger buckets -> bitonic f
 
 template <int KM1>
 __global__ void __launch_bounds__(kSmallThreads)
-build_small_kernel(const float* __restrict__ coords, int N, double step, int parts, int lanes,
-                   int32_t* __restrict__ perm, int32_t* __restrict__ nbr,
+build_small_kernel(const float* __restrict__ coords, Geom g, double step, int parts, int lanes,
+                   int32_t* __restrict__ q_idx, int32_t* __restrict__ nbr,
                    int32_t* __restrict__ key_idx) {
   __shared__ uint64_t keys[kSortChunk];
   __shared__ int bcnt[kBuckets];
@@ -387,8 +410,11 @@ build_small_kernel(const float* __restrict__ coords, int N, double step, int par
   __shared__ int overflow;
   const int b = blockIdx.x;
   const int tid = threadIdx.x;
-  const int C = N / 8;
-  const float2* xy = reinterpret_cast<const float2*>(coords) + (int64_t)b * N;
+  int t0, N, cl0, C;
+  g.image(b, t0, N, cl0, C);
+  if (N > kSortChunk || N == 0) return;   // larger images: segment / merge path
+  const int tb = g.tok_base(t0), cb = g.clu_base(cl0);
+  const float2* xy = reinterpret_cast<const float2*>(coords) + (int64_t)t0;
 
   // Sort the (code << 32 | token) keys.  Counting sort on the top 11 code
   // bits (2048 buckets; two keys per thread), then an insertion sort inside
@@ -467,20 +493,22 @@ build_small_kernel(const float* __restrict__ coords, int N, double step, int par
   }
   __syncthreads();
 
-  // centroid sums decoded from the sorted codes
+  // centroid sums decoded from the sorted codes, scaled to compare means
   for (int c = tid; c < C; c += kSmallThreads) {
+    const int members = min(8, N - 8 * c);
     int sx = 0, sy = 0;
-#pragma unroll
-    for (int m = 0; m < 8; ++m) {
+    for (int m = 0; m < members; ++m) {
       const uint32_t code = (uint32_t)(keys[8 * c + m] >> 32);
       sx += (int)compact16(code);
       sy += (int)compact16(code >> 1);
     }
-    cent[c] = make_int2(sx, sy);
+    const int f = mean_scale(members, N);
+    cent[c] = make_int2(sx * f, sy * f);
   }
-  if (blockIdx.y == 0) {
-    int32_t* pimg = perm + (int64_t)b * N;
-    for (int e = tid; e < N; e += kSmallThreads) pimg[e] = (int32_t)(uint32_t)keys[e];
+  if (blockIdx.y == 0) {   // q_idx rows: token ids, -1 past the end of the order
+    int32_t* qimg = q_idx + (int64_t)cl0 * 8;
+    for (int e = tid; e < 8 * C; e += kSmallThreads)
+      qimg[e] = e < N ? tb + (int32_t)(uint32_t)keys[e] : -1;
   }
   __syncthreads();
 
@@ -488,9 +516,9 @@ build_small_kernel(const float* __restrict__ coords, int N, double step, int par
   // [y*CP, (y+1)*CP) (CP = ceil(C / parts)); `lanes` lanes (a power of two
   // <= 16) share a cluster: lane q scans the candidates at Morton offsets
   // +1, -1, +2, -2, ... (mod C) numbered q, q + lanes, ..., so the nearest
-  // in Morton order come first.  Keys are exact (d2 << 24 | index) in 64
-  // bits from integer centroid sums (sums of eight 16-bit coordinates:
-  // |dx| < 2^19, d2 < 2^39, so d2 << 24 < 2^63), and a candidate is inserted
+  // in Morton order come first.  Keys are exact (d2 << kIdxBits | index)
+  // in 64 bits from integer scaled centroid sums (below 2^22: d2 < 2^45),
+  // and a candidate is inserted
   // only when it beats the lane's current k-1-th best, which after the
   // first few near candidates is rare (the wavefront stays off the
   // divergent insertion path).  The kept set does not depend on the order.
@@ -519,7 +547,7 @@ build_small_kernel(const float* __restrict__ coords, int N, double step, int par
           const int dx = cc.x - me.x, dy = cc.y - me.y;
           const int64_t d2 = (int64_t)dx * dx + (int64_t)dy * dy;
           // sn == 0 is the cluster itself; sn >= C is past the end
-          key[u] = (sn > 0 && sn < C) ? ((uint64_t)d2 << 24) | (uint32_t)e : ~0ull;
+          key[u] = (sn > 0 && sn < C) ? ((uint64_t)d2 << kIdxBits) | (uint32_t)e : ~0ull;
         }
 #pragma unroll
         for (int u = 0; u < U; ++u)
@@ -550,26 +578,26 @@ build_small_kernel(const float* __restrict__ coords, int N, double step, int par
   if (!mine) return;
 
   constexpr int K = KM1 + 1;
+  constexpr uint64_t kIdxMask = (uint64_t(1) << kIdxBits) - 1;
   int32_t ids[K];
   ids[0] = c;
 #pragma unroll
-  for (int r = 0; r < KM1; ++r) ids[r + 1] = best[r] == ~0ull ? -1 : (int32_t)(best[r] & 0xFFFFFFu);
+  for (int r = 0; r < KM1; ++r) ids[r + 1] = best[r] == ~0ull ? -1 : (int32_t)(best[r] & kIdxMask);
   if (q == 0) {
 #pragma unroll
-    for (int s = 0; s < K; ++s) nbr[((int64_t)b * C + c) * K + s] = ids[s];
+    for (int s = 0; s < K; ++s) nbr[((int64_t)cl0 + c) * K + s] = ids[s] >= 0 ? cb + ids[s] : -1;
   }
   // the lanes of the cluster write its slot groups round-robin
-  int4* krow = reinterpret_cast<int4*>(key_idx + ((int64_t)b * C + c) * K * 8);
+  int4* krow = reinterpret_cast<int4*>(key_idx + ((int64_t)cl0 + c) * K * 8);
+  auto tok = [&](int e) { return e < N ? tb + (int)(uint32_t)keys[e] : -1; };
 #pragma unroll
   for (int s = 0; s < K; ++s) {
     if ((s & (lanes - 1)) != q) continue;
     int4 lo = make_int4(-1, -1, -1, -1), hi = lo;
     if (ids[s] >= 0) {
       const int base = 8 * ids[s];
-      lo = make_int4((int)(uint32_t)keys[base], (int)(uint32_t)keys[base + 1],
-                     (int)(uint32_t)keys[base + 2], (int)(uint32_t)keys[base + 3]);
-      hi = make_int4((int)(uint32_t)keys[base + 4], (int)(uint32_t)keys[base + 5],
-                     (int)(uint32_t)keys[base + 6], (int)(uint32_t)keys[base + 7]);
+      lo = make_int4(tok(base), tok(base + 1), tok(base + 2), tok(base + 3));
+      hi = make_int4(tok(base + 4), tok(base + 5), tok(base + 6), tok(base + 7));
     }
     krow[2 * s] = lo;
     krow[2 * s + 1] = hi;
@@ -578,55 +606,58 @@ build_small_kernel(const float* __restrict__ coords, int N, double step, int par
 
 }  // namespace
 
-hipError_t launch_build_neighbors(const float* coords, int B, int N, int grid_side, int k,
-                                  int32_t* perm, int32_t* nbr, int32_t* key_idx, void* ws,
-                                  hipStream_t st) {
+hipError_t launch_build_neighbors(const float* coords, const Geom& g, int B, int64_t T, int64_t Ct,
+                                  int grid_side, int k, int32_t* q_idx, int32_t* nbr,
+                                  int32_t* key_idx, void* ws, hipStream_t st) {
   int bits = 0;   // ceil(log2(grid_side)); grid_side is validated to [1, 65536]
   while ((1 << bits) < grid_side) ++bits;
   const double step = (double)(1u << (16 - bits));
-  BuildWorkspace w = build_layout(ws, B, N);
-  const int C = N / 8;
-  if (N <= kSortChunk) {
-    // up to 8 workgroups per image share its clusters (each repeats the
-    // in-LDS sort), with up to 16 lanes per cluster in the candidate scan
-    const int parts = std::max(1, std::min(8, (C + 31) / 32));
-    const int cp = (C + parts - 1) / parts;
+  const int N = g.N, C = g.C;   // sizes of the (largest) image
+  BuildWorkspace w = build_layout(ws, B, T, Ct, N);
+  // images of at most kSortChunk tokens: up to 8 workgroups per image share
+  // its clusters (each repeats the in-LDS sort), with up to 16 lanes per
+  // cluster in the candidate scan
+  const bool packed = g.tok_off != nullptr;
+  if (N <= kSortChunk || packed) {
+    const int cs = std::min(C, kSmallMaxC);
+    const int parts = std::max(1, std::min(8, (cs + 31) / 32));
+    const int cp = (cs + parts - 1) / parts;
     int lanes = 16;
     while (lanes > 1 && lanes * cp > kSmallThreads) lanes >>= 1;
     switch (k) {
 #define CA_SMALL(KK)                                                                            \
   case KK:                                                                                      \
     hipLaunchKernelGGL(build_small_kernel<KK - 1>, dim3(B, parts), dim3(kSmallThreads), 0, st,  \
-                       coords, N, step, parts, lanes, perm, nbr, key_idx);                      \
+                       coords, g, step, parts, lanes, q_idx, nbr, key_idx);                     \
     break;
       CA_SMALL(1) CA_SMALL(2) CA_SMALL(3) CA_SMALL(4) CA_SMALL(5) CA_SMALL(6) CA_SMALL(7) CA_SMALL(8)
 #undef CA_SMALL
       default:
         return hipErrorInvalidValue;
     }
-    return hipGetLastError();
+    if (N <= kSortChunk) return hipGetLastError();
   }
   // larger images: segment ranks, merge rounds, centroids and boxes, selection
   const int segs = (N + kRankSeg - 1) / kRankSeg;
   hipLaunchKernelGGL(rank_kernel, dim3(kRankSeg / 64, B * segs), dim3(kRankThreads), 0, st,
-                     coords, N, kRankSeg, segs, step, w.keys[0]);
+                     coords, g, segs, step, w.keys[0]);
   int cur = 0;
   const dim3 mgrid((N + kRankThreads - 1) / kRankThreads, B);
   for (int run = kRankSeg; run < N; run *= 2) {
     const bool last = 2 * run >= N;
-    hipLaunchKernelGGL(merge_round_kernel, mgrid, dim3(kRankThreads), 0, st, N, run,
-                       (const uint64_t*)w.keys[cur], last ? nullptr : w.keys[cur ^ 1], perm,
+    hipLaunchKernelGGL(merge_round_kernel, mgrid, dim3(kRankThreads), 0, st, g, run,
+                       (const uint64_t*)w.keys[cur], last ? nullptr : w.keys[cur ^ 1], q_idx,
                        w.qsorted);
     cur ^= 1;
   }
   const dim3 tgrid((C + kBoxTile - 1) / kBoxTile, B);
-  hipLaunchKernelGGL(centroid_box_kernel, tgrid, dim3(kBoxTile), 0, st, C,
-                     (const uint32_t*)w.qsorted, w.cent, w.box);
+  hipLaunchKernelGGL(centroid_box_kernel, tgrid, dim3(kBoxTile), 0, st, g,
+                     (const uint32_t*)w.qsorted, w.cent, w.box, q_idx);
   switch (k) {
 #define CA_SEL(KK)                                                                              \
   case KK:                                                                                      \
-    hipLaunchKernelGGL(select_box_kernel<KK - 1>, tgrid, dim3(kBoxTile * kSelWaves), 0, st, N, \
-                       (const float2*)w.cent, (const float4*)w.box, (const int32_t*)perm, nbr,  \
+    hipLaunchKernelGGL(select_box_kernel<KK - 1>, tgrid, dim3(kBoxTile * kSelWaves), 0, st, g,  \
+                       (const float2*)w.cent, (const float4*)w.box, (const int32_t*)q_idx, nbr, \
                        key_idx);                                                                \
     break;
     CA_SEL(1) CA_SEL(2) CA_SEL(3) CA_SEL(4) CA_SEL(5) CA_SEL(6) CA_SEL(7) CA_SEL(8)

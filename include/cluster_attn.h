@@ -26,8 +26,12 @@
  *    [B, N, H, D] (token-major, heads inside a token); LSE is [B, N, H] f32.
  *    Index arrays are int32 and image-local: values in [0, N), -1 = empty
  *    slot.  A slot repeated in one key list counts once per occurrence.
- *  - q_idx [B, C, cs] must be a permutation of 0..N-1 per image (C = N/cs):
- *    it partitions each image's tokens into the query clusters.
+ *  - q_idx [B, C, cs] (C = ceil(N/cs)) partitions each image's tokens into
+ *    the query clusters: every token appears exactly once, and the cs - n
+ *    unused places of a cluster of n < cs members hold -1 (after its
+ *    members; member 0 of every row is a token).  When cs divides N this is
+ *    a permutation of 0..N-1.  A -1 member is no query and no key: nothing
+ *    is written for it.
  *  - Every call is asynchronous on `hip_stream` (a hipStream_t; NULL = the
  *    default stream): it validates its arguments synchronously, enqueues its
  *    kernels and returns.  Validation failures return before any launch and
@@ -37,7 +41,7 @@
  *    inputs (CA_ERR_ALIAS where the ranges are visibly overlapping).
  *  - Supported set: cs = 8, D = 32, nk = cs*k with 1 <= k <= 8 (the MFMA
  *    kernels serve nk = 48 in bf16/f16; every other case runs on the
- *    vector-ALU kernels), H >= 1, N % cs == 0, dtype f32 / bf16 / f16.
+ *    vector-ALU kernels), H >= 1, any N >= 0, dtype f32 / bf16 / f16.
  *    Anything else: CA_ERR_SHAPE or CA_ERR_UNSUPPORTED.
  *  - No call throws across the ABI.  Launch or runtime failures return
  *    CA_ERR_HIP; cluster_attn_last_error() gives the text (thread-local).
@@ -68,6 +72,7 @@ typedef enum { CA_F32 = 0, CA_BF16 = 1, CA_F16 = 2 } ca_dtype;
  * Workspace bytes needed by cluster_attn_build_neighbors for these sizes.
  * 0 for invalid sizes, and also for valid ones with N <= 2048: such an image
  * is built by one workgroup entirely in LDS and needs no workspace.
+ * Supported: N <= 2^22 tokens per image.
  */
 size_t cluster_attn_build_neighbors_workspace(int B, int N, int cs, int k);
 
@@ -77,19 +82,25 @@ size_t cluster_attn_build_neighbors_workspace(int B, int N, int cs, int k);
  * curves).  Steps, all exact integer arithmetic after one fp64 quantisation:
  *   1. q = clamp(floor((c + 0.5) * 2^(16 - ceil(log2 G))), 0, 65535) per axis;
  *      Morton code with x in the even bits and y in the odd bits.
- *   2. per image, stable sort of tokens by (code, token index) -> perm;
- *      cluster c = perm[c*cs .. c*cs+cs-1].
- *   3. integer centroid sums S_c = sum of the members' (qx, qy).
+ *   2. per image, stable sort of tokens by (code, token index) -> order;
+ *      cluster c = order[c*cs .. c*cs+cs-1], C = ceil(N/cs) clusters, the
+ *      last one partial (N mod cs members) when cs does not divide N.
+ *   3. centroids compared through their means: integer sums of the
+ *      members' (qx, qy), scaled to a common multiple of the means (for
+ *      cs = 8: sum * lcm(8, N mod 8) / members; plain sums when 8 | N).
  *   4. nbr[c] = c, then the k-1 clusters b != c with the smallest
- *      ((S_c - S_b)^2 summed over axes, b), ascending; -1 pads if C < k.
- *   5. key_idx[c][s*cs + m] = perm[nbr[c][s]*cs + m] (-1 where nbr is -1).
+ *      (squared centroid distance, b), ascending; -1 pads if C < k.
+ *   5. key_idx[c][s*cs + m] = q_idx[nbr[c][s]][m] (-1 where nbr is -1 or
+ *      the member is absent).
  * Arguments:
  *   coords    [B, N, 2] f32, (x = column, y = row) in patch units, device.
  *   grid_side G >= 1, the side of the patch grid the coordinates live on
  *             (only its ceil(log2) is used; coordinates outside [-0.5, G-0.5)
  *             clamp).
  *   cs        cluster size, must be 8.   k: clusters per list, 1..8.
- *   perm      [B, N] int32 out (== q_idx [B, C, cs]).
+ *   perm      [B, C*cs] int32 out: the q_idx rows [B, C, cs] (the token
+ *             order itself when cs divides N; -1 after the members of a
+ *             partial last cluster).
  *   nbr       [B, C, k] int32 out, slot 0 = self.
  *   key_idx   [B, C, cs*k] int32 out.
  *   ws        device workspace of at least
@@ -100,6 +111,33 @@ size_t cluster_attn_build_neighbors_workspace(int B, int N, int cs, int k);
 int cluster_attn_build_neighbors(const float* coords, int B, int N, int grid_side, int cs, int k,
                                  int32_t* perm, int32_t* nbr, int32_t* key_idx, void* ws,
                                  size_t ws_bytes, void* hip_stream);
+
+/*
+ * Packed batch of images of different sizes (ragged geometry).  Image b holds
+ * tokens [tok_off[b], tok_off[b+1]) of the packed arrays and clusters
+ * [clu_off[b], clu_off[b+1]), with clu_off[b+1] - clu_off[b] =
+ * ceil((tok_off[b+1] - tok_off[b]) / cs).  Each image is built exactly as by
+ * cluster_attn_build_neighbors on its own; the lists carry batch-global
+ * ids (token ids offset by tok_off[b], cluster ids by clu_off[b]), so that
+ * the packed batch can be handed to cluster_attn_fwd_varlen /
+ * cluster_attn_bwd_varlen as one index space.
+ *   coords    [T, 2] f32 device, the images one after another.
+ *   B, T, Ct  images, total tokens (tok_off[B]), total clusters (clu_off[B]).
+ *   max_n     the largest image's token count (sizes the launch; <= 2^22).
+ *   tok_off, clu_off  [B + 1] int32 device, starting at 0, nondecreasing and
+ *             consistent with T, Ct and max_n: a precondition, not checked
+ *             (the Python binding computes them).
+ *   q_idx     [Ct, cs], nbr [Ct, k], key_idx [Ct, cs*k] int32 out.
+ *   ws        at least cluster_attn_build_neighbors_varlen_workspace(...)
+ *             bytes (0 when max_n <= 2048).
+ */
+size_t cluster_attn_build_neighbors_varlen_workspace(int B, int T, int Ct, int max_n, int cs,
+                                                     int k);
+int cluster_attn_build_neighbors_varlen(const float* coords, int B, int T, int Ct, int max_n,
+                                        const int32_t* tok_off, const int32_t* clu_off,
+                                        int grid_side, int cs, int k, int32_t* q_idx,
+                                        int32_t* nbr, int32_t* key_idx, void* ws,
+                                        size_t ws_bytes, void* hip_stream);
 
 /*
  * Forward (notes page "Overall Architecture": local cluster attention; arXiv
@@ -153,6 +191,25 @@ int cluster_attn_bwd(int dt, int B, int N, int H, int D, int cs, int nk, float s
                      const void* dout, const float* lse, const int32_t* q_idx,
                      const int32_t* key_idx, void* dq, void* dk, void* dv, void* ws,
                      size_t ws_bytes, void* hip_stream);
+
+/*
+ * Forward and backward of a packed batch (see
+ * cluster_attn_build_neighbors_varlen): the same computation as
+ * cluster_attn_fwd / cluster_attn_bwd with the whole batch as one index
+ * space of T tokens and Ct clusters (lists never cross images, so nothing
+ * mixes images).  q, k, v, o, dout, dq, dk, dv are [T, H, D] dt, lse
+ * [T, H] f32, q_idx [Ct, cs] and key_idx [Ct, nk] int32 with batch-global
+ * token ids; ceil(T / cs) <= Ct <= T.
+ */
+int cluster_attn_fwd_varlen(int dt, int T, int Ct, int H, int D, int cs, int nk, float scale,
+                            const void* q, const void* k, const void* v, const int32_t* q_idx,
+                            const int32_t* key_idx, void* o, float* lse, void* hip_stream);
+size_t cluster_attn_bwd_varlen_workspace(int dt, int T, int Ct, int H, int D, int cs, int nk);
+int cluster_attn_bwd_varlen(int dt, int T, int Ct, int H, int D, int cs, int nk, float scale,
+                            const void* q, const void* k, const void* v, const void* o,
+                            const void* dout, const float* lse, const int32_t* q_idx,
+                            const int32_t* key_idx, void* dq, void* dk, void* dv, void* ws,
+                            size_t ws_bytes, void* hip_stream);
 
 /* ------------------------------------------------------------------------
  * KNN-cache point sampler of the point-wise decoder.

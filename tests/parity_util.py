@@ -65,6 +65,7 @@ def sampled_oracle(q, k, v, do, q_idx, key_idx, scale, clusters, key_tokens, wit
     sel_q = qi[clusters]
     o, lse = O.attn_fwd_gathered(q, k, v, sel_q[None], ki[clusters][None], scale)
     tok = sel_q.reshape(-1)
+    tok = tok[tok >= 0]                      # -1: absent member of a partial cluster
     out["q_tokens"] = tok
     out["o"], out["lse"] = o[0, tok], lse[0, tok]
     if with_bwd:

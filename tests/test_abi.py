@@ -50,7 +50,8 @@ def fwd(lib, dt=1, B=2, N=64, H=2, D=32, cs=8, nk=48, scale=0.17, ptrs=None):
 def test_fwd_validation(lib):
     assert fwd(lib, dt=7) == CA_ERR_UNSUPPORTED
     assert b"dtype" in lib.cluster_attn_last_error()
-    assert fwd(lib, N=60) == CA_ERR_SHAPE
+    assert fwd(lib, N=-8) == CA_ERR_SHAPE
+    assert fwd(lib, B=1 << 20, N=1 << 12) == CA_ERR_SHAPE          # B*N beyond int32
     assert fwd(lib, D=64) == CA_ERR_UNSUPPORTED
     assert fwd(lib, cs=4, nk=24) == CA_ERR_UNSUPPORTED
     assert fwd(lib, nk=50) == CA_ERR_UNSUPPORTED
@@ -84,12 +85,14 @@ def bwd(lib, ws_bytes=1 << 40, ws=P * 40, dt=1, B=2, N=64, H=2, nk=48, ptrs=None
 def test_bwd_validation_and_workspace(lib):
     need = lib.cluster_attn_bwd_workspace(1, 2, 64, 2, 32, 8, 48)
     assert need > 0
-    assert lib.cluster_attn_bwd_workspace(1, 2, 60, 2, 32, 8, 48) == 0
+    # a partial last cluster (60 = 7*8 + 4) is a valid size
+    assert lib.cluster_attn_bwd_workspace(1, 2, 60, 2, 32, 8, 48) > 0
+    assert lib.cluster_attn_bwd_workspace(1, 2, -4, 2, 32, 8, 48) == 0
     assert lib.cluster_attn_bwd_workspace(9, 2, 64, 2, 32, 8, 48) == 0
     assert bwd(lib, ws_bytes=need - 1) == CA_ERR_WORKSPACE
     assert bwd(lib, ws=None) == CA_ERR_NULL
     assert bwd(lib, dt=3) == CA_ERR_UNSUPPORTED
-    assert bwd(lib, N=12) == CA_ERR_SHAPE
+    assert bwd(lib, N=-1) == CA_ERR_SHAPE
     # dk overlapping the workspace
     p = [P * (i + 1) for i in range(11)]
     assert bwd(lib, ws=p[9] + 8, ptrs=p) == CA_ERR_ALIAS
@@ -111,7 +114,8 @@ def test_build_validation(lib):
         p = ptrs or [P, 2 * P, 3 * P, 4 * P]
         return lib.cluster_attn_build_neighbors(p[0], B, N, G, cs, k, p[1], p[2], p[3], ws,
                                                 ws_bytes, None)
-    assert build(N=20) == CA_ERR_SHAPE
+    assert build(N=(1 << 22) + 8) == CA_ERR_SHAPE                   # beyond 2^22 per image
+    assert build(N=-3) == CA_ERR_SHAPE
     assert build(cs=16) == CA_ERR_UNSUPPORTED
     assert build(k=0) == CA_ERR_UNSUPPORTED
     assert build(k=9) == CA_ERR_UNSUPPORTED
@@ -122,6 +126,38 @@ def test_build_validation(lib):
     assert build(N=4096, ws=None) == CA_ERR_NULL
     assert build(ptrs=[P, 2 * P, 2 * P + 4, 4 * P]) == CA_ERR_ALIAS
     assert build(B=0, ptrs=[None] * 4, ws=None) == CA_OK
+
+
+def test_varlen_validation(lib):
+    def build(B=3, T=100, Ct=14, max_n=50, G=32, k=6, ws_bytes=1 << 30, ptrs=None, ws=P * 9):
+        p = ptrs or [P, 2 * P, 3 * P, 4 * P, 5 * P, 6 * P]
+        return lib.cluster_attn_build_neighbors_varlen(p[0], B, T, Ct, max_n, p[1], p[2], G, 8, k,
+                                                       p[3], p[4], p[5], ws, ws_bytes, None)
+    assert build(max_n=101) == CA_ERR_SHAPE                         # an image above T
+    assert build(Ct=12) == CA_ERR_SHAPE                             # fewer than ceil(T/8)
+    assert build(Ct=101) == CA_ERR_SHAPE                            # more clusters than tokens
+    assert build(k=9) == CA_ERR_UNSUPPORTED
+    assert build(ptrs=[P, None, 3 * P, 4 * P, 5 * P, 6 * P]) == CA_ERR_NULL
+    assert build(ptrs=[P, 2 * P, 3 * P, 4 * P, 4 * P + 8, 6 * P]) == CA_ERR_ALIAS
+    assert build(max_n=3000, T=6000, Ct=760, ws_bytes=8) == CA_ERR_WORKSPACE
+    assert build(B=0, T=0, Ct=0, max_n=0, ptrs=[None] * 6, ws=None) == CA_OK
+    assert lib.cluster_attn_build_neighbors_varlen_workspace(3, 100, 14, 50, 8, 6) == 0
+    assert lib.cluster_attn_build_neighbors_varlen_workspace(3, 6000, 760, 3000, 8, 6) > 0
+    assert lib.cluster_attn_build_neighbors_varlen_workspace(3, 100, 14, 101, 8, 6) == 0
+
+    p7 = [P * (i + 1) for i in range(7)]
+    f = lambda T=100, Ct=14, nk=48, ptrs=p7: lib.cluster_attn_fwd_varlen(
+        1, T, Ct, 2, 32, 8, nk, 0.17, *ptrs, None)
+    assert f(Ct=12) == CA_ERR_SHAPE
+    assert f(Ct=101) == CA_ERR_SHAPE
+    assert f(nk=50) == CA_ERR_UNSUPPORTED
+    assert f(ptrs=[P, 2 * P, None, 4 * P, 5 * P, 6 * P, 7 * P]) == CA_ERR_NULL
+    assert f(T=0, Ct=0, ptrs=[None] * 7) == CA_OK
+    need = lib.cluster_attn_bwd_varlen_workspace(1, 100, 14, 2, 32, 8, 48)
+    assert need > 0 and lib.cluster_attn_bwd_varlen_workspace(1, 100, 12, 2, 32, 8, 48) == 0
+    p11 = [P * (i + 1) for i in range(11)]
+    assert lib.cluster_attn_bwd_varlen(1, 100, 14, 2, 32, 8, 48, 0.17, *p11, P * 40, need - 1,
+                                       None) == CA_ERR_WORKSPACE
 
 
 def test_missing_library_raises(tmp_path):
