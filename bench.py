@@ -52,13 +52,18 @@ def algorithmic(cfg):
     """Compulsory bytes and matmul flops of each entry point (every tensor
     touched once; gathered re-reads, workspace and atomics not counted)."""
     T, H, D, nk = cfg.tokens, cfg.H, cfg.D, cfg.nk
-    es = 4 if cfg.dtype == "f32" else 2
-    C = T // cfg.cs
-    t = T * H * D * es                  # one [B, N, H, D] tensor
+    C = cfg.B * cfg.C
+    return algorithmic_tc(T, C, H, D, nk, cfg.k, cfg.cs, cfg.dtype)
+
+
+def algorithmic_tc(T, C, H, D, nk, k, cs, dtype):
+    """The same for T tokens in C clusters (a partial cluster counts as one)."""
+    es = 4 if dtype == "f32" else 2
+    t = T * H * D * es                  # one [tokens, H, D] tensor
     lse = T * H * 4
-    idx = T * 4 + C * nk * 4            # q_idx + key_idx
+    idx = C * cs * 4 + C * nk * 4       # q_idx + key_idx
     return {
-        "build": {"bytes": T * 8 + T * 4 + C * cfg.k * 4 + C * nk * 4, "flops": 0},
+        "build": {"bytes": T * 8 + C * cs * 4 + C * k * 4 + C * nk * 4, "flops": 0},
         "fwd": {"bytes": 3 * t + t + lse + idx, "flops": T * H * 4 * nk * D},
         "bwd": {"bytes": 5 * t + lse + 3 * t + idx, "flops": T * H * 10 * nk * D},
     }
@@ -152,9 +157,12 @@ def main():
     import torch
 
     import gathered_local_attention_amd as ca
-    from gen import MERGE_CONFIGS, SAMPLER_CONFIGS, make_case
+    from gen import MERGE_CONFIGS, RAGGED_CONFIGS, SAMPLER_CONFIGS, make_case
 
     ca._lib.load()
+    if args.config in RAGGED_CONFIGS:
+        bench_varlen(args, torch, ca)
+        return
     if args.config in SAMPLER_CONFIGS:
         bench_sampler(args, torch, ca)
         return
@@ -172,7 +180,6 @@ def main():
         s = {"coords": torch.from_numpy(case["coords"]).to(dev)}
         for n in ("q", "k", "v", "do"):
             s[n] = case[n].to(dev)
-        s["perm"] = torch.empty((cfg.B, cfg.N), dtype=torch.int32, device=dev)
         sets.append(s)
     bws = torch.empty(ca.build_workspace_bytes(cfg.B, cfg.N, cfg.cs, cfg.k) or 1,
                       dtype=torch.uint8, device=dev)
@@ -246,7 +253,9 @@ def main():
     copy_gbps = copy_bandwidth(torch)
 
     line = {
-        "metric": "cluster-attention fwd+bwd tokens/sec and % of HBM roofline (stage-1 shape)",
+        "metric": "cluster-attention fwd+bwd tokens/sec and % of HBM roofline (stage-1 shape)"
+                  if cfg.name == "stage1" else
+                  f"cluster-attention fwd+bwd tokens/sec and % of HBM roofline ({cfg.name} shape)",
         "value": cfg.tokens / (ms_per_step * 1e-3),
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -260,8 +269,8 @@ def main():
         "data": "synthetic",
         "config": {
             "workload": f"{cfg.name}: B={cfg.B} images x N={cfg.N} tokens, H={cfg.H}x{cfg.D}, "
-                        f"clusters of {cfg.cs}, {cfg.nk} key slots, {cfg.dtype}; step = "
-                        "neighbour build + forward + backward",
+                        f"clusters of {cfg.cs} ({cfg.C} per image), {cfg.nk} key slots, "
+                        f"{cfg.dtype}; step = neighbour build + forward + backward",
             "B": cfg.B, "N": cfg.N, "H": cfg.H, "D": cfg.D, "cs": cfg.cs, "nk": cfg.nk,
             "geometry": cfg.geometry, "seed": cfg.seed, "rotating_copies": args.copies,
         },
@@ -292,6 +301,166 @@ def main():
     }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(cfg, case, min(args.cpu_images, cfg.B))
+    print(json.dumps(line), flush=True)
+
+
+# ---------------------------------------------------------------------------
+# Packed batches of images of different sizes: --config varlen
+# ---------------------------------------------------------------------------
+
+def varlen_cpu_baseline(cfg, case, images: int):
+    """The fp64 oracle (gathered forward + backward) on the first `images`
+    images of the packed batch, single-threaded; build excluded."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    import oracle as O
+
+    n = sum(case["lengths"][:images])
+    q_idx, _, key_idx, _, _ = O.build_neighbors_varlen(case["coords"][:n], case["lengths"][:images],
+                                                        cfg.G)
+    args = [case[x][:n][None] for x in ("q", "k", "v", "do")]
+    scale = 1.0 / math.sqrt(cfg.D)
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        O.attn_fwd_gathered(*args[:3], q_idx[None], key_idx[None], scale)
+        O.attn_bwd_gathered(*args, q_idx[None], key_idx[None], scale)
+        dt = time.perf_counter() - t0
+    return {
+        "value": n / dt,
+        "unit": "tokens/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": f"{images} of {cfg.B} images ({n} tokens), fp64 gathered forward+backward, "
+                  f"{dt:.1f} s",
+    }
+
+
+def bench_varlen(args, torch, ca):
+    from gen import make_varlen_case
+
+    case = make_varlen_case(args.config)
+    cfg = case["cfg"]
+    lengths = case["lengths"]
+    T = case["coords"].shape[0]
+    tok, clu = ca.varlen_offsets(lengths, cfg.cs)
+    Ct = clu[-1]
+    scale = 1.0 / math.sqrt(cfg.D)
+    dev = "cuda"
+    offsets = (torch.tensor(tok, dtype=torch.int32).to(dev),
+               torch.tensor(clu, dtype=torch.int32).to(dev))
+    sets = []
+    for r in range(args.copies):
+        s = {"coords": torch.from_numpy(case["coords"]).to(dev)}
+        for n in ("q", "k", "v", "do"):
+            s[n] = case[n].to(dev)
+        sets.append(s)
+    max_n = max(lengths)
+    lib = ca._lib.load()
+    bws = torch.empty(max(1, lib.cluster_attn_build_neighbors_varlen_workspace(
+        cfg.B, T, Ct, max_n, cfg.cs, cfg.k)), dtype=torch.uint8, device=dev)
+    dt = {"f32": 0, "bf16": 1, "f16": 2}[cfg.dtype]
+    gws = torch.empty(lib.cluster_attn_bwd_varlen_workspace(dt, T, Ct, cfg.H, cfg.D, cfg.cs, cfg.nk),
+                      dtype=torch.uint8, device=dev)
+
+    def build(s):
+        return ca.build_neighbors_varlen(s["coords"], lengths, cfg.G, cfg.cs, cfg.k, workspace=bws,
+                                         offsets=offsets)
+
+    def step(s):
+        q_idx, _, key, _, _ = build(s)
+        o, lse = ca.fwd_varlen(s["q"], s["k"], s["v"], q_idx, key, scale)
+        return ca.bwd_varlen(s["q"], s["k"], s["v"], o, s["do"], lse, q_idx, key, scale,
+                             workspace=gws)
+
+    for i in range(args.warmup):
+        step(sets[i % len(sets)])
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(sets[i % len(sets)])
+    torch.cuda.synchronize()
+    ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
+
+    n_ev = min(args.steps, 100)
+    outs = []
+    for s in sets:
+        q_idx, _, key, _, _ = build(s)
+        o, lse = ca.fwd_varlen(s["q"], s["k"], s["v"], q_idx, key, scale)
+        outs.append((q_idx, key, o, lse))
+    calls = {
+        "build": lambda i: build(sets[i]),
+        "fwd": lambda i: ca.fwd_varlen(sets[i]["q"], sets[i]["k"], sets[i]["v"], outs[i][0],
+                                       outs[i][1], scale),
+        "bwd": lambda i: ca.bwd_varlen(sets[i]["q"], sets[i]["k"], sets[i]["v"], outs[i][2],
+                                       sets[i]["do"], outs[i][3], outs[i][0], outs[i][1], scale,
+                                       workspace=gws),
+    }
+    dur = {}
+    for name, call in calls.items():
+        call(0)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(n_ev):
+            call(i % len(sets))
+        e1.record()
+        torch.cuda.synchronize()
+        dur[name] = e0.elapsed_time(e1) / n_ev * 1e3
+
+    alg = algorithmic_tc(T, Ct, cfg.H, cfg.D, cfg.nk, cfg.k, cfg.cs, cfg.dtype)
+    dom = max(("build", "fwd", "bwd"), key=lambda k: dur[k])
+    achieved = alg[dom]["bytes"] / (dur[dom] * 1e-6) / 1e9
+    fb_us = dur["fwd"] + dur["bwd"]
+    fb_bytes = alg["fwd"]["bytes"] + alg["bwd"]["bytes"]
+    fb_flops = alg["fwd"]["flops"] + alg["bwd"]["flops"]
+    line = {
+        "metric": "cluster-attention fwd+bwd tokens/sec and % of HBM roofline "
+                  f"(packed batch, {cfg.name})",
+        "value": T / (ms_per_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic",
+        "config": {
+            "workload": f"{cfg.name}: B={cfg.B} images of {min(lengths)}..{max(lengths)} tokens "
+                        f"(T={T}, {Ct} clusters), H={cfg.H}x{cfg.D}, {cfg.nk} key slots, "
+                        f"{cfg.dtype}; step = packed neighbour build + forward + backward",
+            "B": cfg.B, "T": T, "clusters": Ct, "H": cfg.H, "D": cfg.D, "geometry": cfg.geometry,
+            "seed": cfg.seed, "rotating_copies": args.copies,
+        },
+        "roofline": {
+            "bound": "hbm",
+            "kernel": {"build": "cluster_attn_build_neighbors_varlen", "fwd": "cluster_attn_fwd_varlen",
+                       "bwd": "cluster_attn_bwd_varlen"}[dom],
+            "entry_point_kernels": ENTRY_KERNELS[dom],
+            "achieved": achieved,
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBPS,
+            "traffic": None,
+            "algorithmic_bytes": alg[dom]["bytes"],
+            "avg_us": dur[dom],
+        },
+        "fwd_bwd": {
+            "us": fb_us,
+            "tokens_per_s": T / (fb_us * 1e-6),
+            "effective_GBps": fb_bytes / (fb_us * 1e-6) / 1e9,
+            "hbm_frac": fb_bytes / (fb_us * 1e-6) / 1e9 / HBM_PEAK_GBPS,
+            "effective_TFLOPs": fb_flops / (fb_us * 1e-6) / 1e12,
+            "mfma_bf16_frac": fb_flops / (fb_us * 1e-6) / 1e12 / BF16_MFMA_PEAK_TFLOPS,
+        },
+        "entry_us": dur,
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = varlen_cpu_baseline(cfg, case, min(args.cpu_images, cfg.B))
     print(json.dumps(line), flush=True)
 
 

@@ -217,12 +217,13 @@ def varlen_offsets(lengths, cs: int = 8):
 
 
 def build_neighbors_varlen(coords: torch.Tensor, lengths, grid_side: int, cs: int = 8, k: int = 6,
-                           workspace: torch.Tensor | None = None):
+                           workspace: torch.Tensor | None = None, offsets=None):
     """Neighbour lists of a packed batch: coords [T, 2] float32 (device)
     holds the images one after another, image b having lengths[b] tokens.
     Returns q_idx [Ct, cs], nbr [Ct, k], key_idx [Ct, cs*k] (int32,
     batch-global ids, -1 padding) and the device offsets tok_off, clu_off
-    [B+1] int32."""
+    [B+1] int32.  ``offsets`` may pass that pair from an earlier call with
+    the same lengths (no host-to-device copy then)."""
     lib = _lib.load()
     if coords.dim() != 2 or coords.shape[1] != 2:
         raise ValueError("coords must be [T, 2]")
@@ -233,8 +234,15 @@ def build_neighbors_varlen(coords: torch.Tensor, lengths, grid_side: int, cs: in
         raise ValueError(f"lengths sum to {T}, coords has {coords.shape[0]} rows")
     max_n = max((tok[b + 1] - tok[b] for b in range(B)), default=0)
     dev = coords.device
-    tok_off = torch.tensor(tok, dtype=torch.int32).to(dev)
-    clu_off = torch.tensor(clu, dtype=torch.int32).to(dev)
+    if offsets is None:
+        tok_off = torch.tensor(tok, dtype=torch.int32).to(dev)
+        clu_off = torch.tensor(clu, dtype=torch.int32).to(dev)
+    else:
+        tok_off, clu_off = offsets
+        if tok_off.numel() != B + 1 or clu_off.numel() != B + 1:
+            raise ValueError("offsets do not match lengths")
+        _dev(tok_off, "tok_off", torch.int32)
+        _dev(clu_off, "clu_off", torch.int32)
     q_idx = torch.empty((Ct, cs), dtype=torch.int32, device=dev)
     nbr = torch.empty((Ct, k), dtype=torch.int32, device=dev)
     key_idx = torch.empty((Ct, cs * k), dtype=torch.int32, device=dev)

@@ -147,7 +147,7 @@ int cluster_attn_build_neighbors(const float* coords, int B, int N, int grid_sid
                   {key_idx, (size_t)(B * C * k * cs) * 4}, {ws, need}};
   Range ins[] = {{coords, (size_t)B * N * 8}};
   if (int s = check_alias(outs, 4, ins, 1)) return s;
-  const ca::Geom g{nullptr, nullptr, N, (int)C};
+  const ca::Geom g{nullptr, nullptr, N, (int)C, 0};
   return hip_status(ca::launch_build_neighbors(coords, g, B, (int64_t)B * N, B * C, grid_side, k,
                                                perm, nbr, key_idx, ws, (hipStream_t)hip_stream),
                     "build_neighbors launch");
@@ -187,7 +187,7 @@ int cluster_attn_build_neighbors_varlen(const float* coords, int B, int T, int C
   Range ins[] = {{coords, (size_t)T * 8}, {tok_off, (size_t)(B + 1) * 4},
                  {clu_off, (size_t)(B + 1) * 4}};
   if (int s = check_alias(outs, 4, ins, 3)) return s;
-  const ca::Geom g{tok_off, clu_off, max_n, (int)clusters_of(max_n, cs)};
+  const ca::Geom g{tok_off, clu_off, max_n, (int)clusters_of(max_n, cs), 0};
   return hip_status(ca::launch_build_neighbors(coords, g, B, T, Ct, grid_side, k, q_idx, nbr,
                                                key_idx, ws, (hipStream_t)hip_stream),
                     "build_neighbors_varlen launch");

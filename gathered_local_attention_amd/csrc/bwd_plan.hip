@@ -87,10 +87,13 @@ plan_count_kernel(int B, int N, int C, int nk, const int32_t* __restrict__ key_i
   RevEntry* st = stage + bc * nk;
   const int ng = nk / 8;
   bool grouped = (nk % 8) == 0;
+  // a group is "grouped" when its first slot is a token and every other
+  // slot is empty (-1: an absent member of a partial cluster) or in the
+  // first slot's key cluster
   for (int g = 0; g < ng && grouped; ++g) {
     const int j0 = my[8 * g];
     bool same = j0 >= 0;
-    for (int m = 1; m < 8; ++m) same = same && my[8 * g + m] >= 0 && (my[8 * g + m] >> 3) == (j0 >> 3);
+    for (int m = 1; m < 8; ++m) same = same && (my[8 * g + m] < 0 || (my[8 * g + m] >> 3) == (j0 >> 3));
     grouped = same;
   }
   int ne = 0;   // entries staged so far (compactly, then a sentinel)
@@ -103,7 +106,8 @@ plan_count_kernel(int B, int N, int C, int nk, const int32_t* __restrict__ key_i
       uint64_t mult = 0;
       for (int h = g; h < ng; ++h)
         if ((my[8 * h] >> 3) == j)
-          for (int m = 0; m < 8; ++m) mult += 1ull << (8 * (my[8 * h + m] & 7));
+          for (int m = 0; m < 8; ++m)
+            if (my[8 * h + m] >= 0) mult += 1ull << (8 * (my[8 * h + m] & 7));
       RevEntry e;
       e.i = j;   // key cluster while staged
       e.pad = 0;

@@ -67,7 +67,8 @@ static inline BwdWorkspace bwd_layout(void* base, int64_t B, int64_t N, int64_t 
 }
 
 // ---- workspace layout of the neighbour build ------------------------------
-constexpr int kSortChunk = 2048;   // images up to this many tokens are built in LDS
+constexpr int kSortChunk = 2048;   // images up to this many tokens: backward plan in LDS
+constexpr int kSmallBuild = 4096;  // images up to this many tokens are built in LDS
 constexpr int kRankSeg = 512;      // larger images: tokens ranked together before merging
 constexpr int kBoxTile = 64;       // consecutive clusters per bounding box
 constexpr int kIdxBits = 19;       // cluster index bits of a (distance, index) key
@@ -82,6 +83,7 @@ struct Geom {
   const int32_t* tok_off;
   const int32_t* clu_off;
   int N, C;
+  int small_max;   // images up to this size are built in LDS, larger ones by segments
   __device__ __forceinline__ void image(int b, int& t0, int& n, int& c0, int& nc) const {
     if (tok_off) {
       t0 = tok_off[b];
@@ -121,7 +123,7 @@ struct BuildWorkspace {
   size_t bytes;
 };
 
-// Everything is only needed when some image has more than kSortChunk
+// Everything is only needed when some image has more than kSmallBuild
 // tokens: T tokens and Ct clusters in the batch, the largest image maxN.
 static inline BuildWorkspace build_layout(void* base, int64_t B, int64_t T, int64_t Ct,
                                           int64_t maxN) {
@@ -133,7 +135,7 @@ static inline BuildWorkspace build_layout(void* base, int64_t B, int64_t T, int6
     p = align_up(p + n, 256);
     return b ? (void*)(b + at) : (void*)nullptr;
   };
-  const bool big = maxN > kSortChunk;
+  const bool big = maxN > kSmallBuild;
   const int64_t tiles = ((maxN + 7) / 8 + kBoxTile - 1) / kBoxTile;
   w.qsorted = (uint32_t*)take(big ? (size_t)(Ct * 8) * sizeof(uint32_t) : 0);
   w.keys[0] = (uint64_t*)take(big ? (size_t)T * sizeof(uint64_t) : 0);

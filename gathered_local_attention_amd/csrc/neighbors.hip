@@ -36,8 +36,9 @@
 // the key slots of its absent members are -1.  Centroids are compared
 // through their means (sums scaled by mean_scale).  A packed batch of
 // images of different sizes (Geom with offsets) is built image by image:
-// images of at most kSortChunk tokens by the in-LDS kernel, larger ones by
-// the segment / merge path; both skip the other's images.
+// images of at most Geom::small_max (2048 or 4096) tokens by the in-LDS
+// kernel, larger ones by the segment / merge path; both skip the other's
+// images.
 #include "common.h"
 
 #include <algorithm>
@@ -82,7 +83,7 @@ rank_kernel(const float* __restrict__ coords, Geom g, int segs_per_image, double
   const int start = (seg % segs_per_image) * kRankSeg;
   int t0, n, c0, nc;
   g.image(b, t0, n, c0, nc);
-  if (n <= kSortChunk) return;                        // built by the in-LDS kernel
+  if (n <= g.small_max) return;                       // built by the in-LDS kernel
   const int L = min(kRankSeg, n - start);
   if (L <= 0) return;
   const float2* xy = reinterpret_cast<const float2*>(coords) + (int64_t)t0 + start;
@@ -129,7 +130,7 @@ merge_round_kernel(Geom g, int run, const uint64_t* __restrict__ in, uint64_t* _
   const int x = blockIdx.x * kRankThreads + threadIdx.x;
   int t0, n, c0, nc;
   g.image(blockIdx.y, t0, n, c0, nc);
-  if (n <= kSortChunk || x >= n) return;
+  if (n <= g.small_max || x >= n) return;
   const uint64_t* img = in + t0;
   const uint64_t key = img[x];
   const int p0 = x & ~(2 * run - 1);
@@ -165,7 +166,7 @@ centroid_box_kernel(Geom g, const uint32_t* __restrict__ qsorted, float2* __rest
   const int b = blockIdx.y;
   int t0, n, c0, nc;
   g.image(b, t0, n, c0, nc);
-  if (n <= kSortChunk) return;
+  if (n <= g.small_max) return;
   const int c = t * kBoxTile + threadIdx.x;
   float lx = INFINITY, ly = INFINITY, hx = -INFINITY, hy = -INFINITY;
   if (c < nc) {
@@ -291,7 +292,7 @@ select_box_kernel(Geom g, const float2* __restrict__ cent_all, const float4* __r
   g.image(b, t0, n, c0, C);
   const int ntiles = (C + kBoxTile - 1) / kBoxTile;
   const int own = blockIdx.x;
-  if (n <= kSortChunk || own >= ntiles) return;
+  if (n <= g.small_max || own >= ntiles) return;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int c = own * kBoxTile + lane;
   const bool valid = c < C;
@@ -390,42 +391,43 @@ select_box_kernel(Geom g, const float2* __restrict__ cent_all, const float4* __r
 // lane shuffles.  grid = B.
 // ---------------------------------------------------------------------------
 constexpr int kSmallThreads = 1024;
-constexpr int kSmallMaxC = kSortChunk / 8;     // 256 clusters
 
 constexpr int kBuckets = 2 * kSmallThreads;       // counting-sort buckets (top 11 code bits)
 constexpr int kBucketShift = 21;
 constexpr int kMaxBucket = 32;                    // larger buckets -> bitonic fallback
 
 
-template <int KM1>
+// KPT keys per thread: images of up to KPT * 1024 tokens (2048 or 4096).
+template <int KM1, int KPT>
 __global__ void __launch_bounds__(kSmallThreads)
 build_small_kernel(const float* __restrict__ coords, Geom g, double step, int parts, int lanes,
                    int32_t* __restrict__ q_idx, int32_t* __restrict__ nbr,
                    int32_t* __restrict__ key_idx) {
-  __shared__ uint64_t keys[kSortChunk];
+  constexpr int kMaxN = KPT * kSmallThreads;
+  __shared__ uint64_t keys[kMaxN];
   __shared__ int bcnt[kBuckets];
   __shared__ int bstart[kBuckets];
-  __shared__ int2 cent[kSmallMaxC];
+  __shared__ int2 cent[kMaxN / 8];
   __shared__ int scan_tmp[17];
   __shared__ int overflow;
   const int b = blockIdx.x;
   const int tid = threadIdx.x;
   int t0, N, cl0, C;
   g.image(b, t0, N, cl0, C);
-  if (N > kSortChunk || N == 0) return;   // larger images: segment / merge path
+  if (N > kMaxN || N == 0) return;   // larger images: segment / merge path
   const int tb = g.tok_base(t0), cb = g.clu_base(cl0);
   const float2* xy = reinterpret_cast<const float2*>(coords) + (int64_t)t0;
 
   // Sort the (code << 32 | token) keys.  Counting sort on the top 11 code
-  // bits (2048 buckets; two keys per thread), then an insertion sort inside
+  // bits (2048 buckets; KPT keys per thread), then an insertion sort inside
   // each bucket restores the exact (code, token) order whatever the arrival
   // order of the atomics.  Buckets hold about one key for the grid-like
   // layouts of the workloads; if any bucket exceeds kMaxBucket keys the
   // workgroup falls back to an LDS bitonic sort.
-  uint64_t kk[2];
-  int bk[2], arr[2];
+  uint64_t kk[KPT];
+  int bk[KPT], arr[KPT];
 #pragma unroll
-  for (int r = 0; r < 2; ++r) {
+  for (int r = 0; r < KPT; ++r) {
     const int e = tid + r * kSmallThreads;
     kk[r] = ~0ull;
     bk[r] = -1;
@@ -441,7 +443,7 @@ build_small_kernel(const float* __restrict__ coords, Geom g, double step, int pa
   if (tid == 0) overflow = 0;
   __syncthreads();
 #pragma unroll
-  for (int r = 0; r < 2; ++r) arr[r] = bk[r] >= 0 ? atomicAdd(&bcnt[bk[r]], 1) : 0;
+  for (int r = 0; r < KPT; ++r) arr[r] = bk[r] >= 0 ? atomicAdd(&bcnt[bk[r]], 1) : 0;
   __syncthreads();
   const int c0 = bcnt[2 * tid], c1 = bcnt[2 * tid + 1];
   if (c0 > kMaxBucket || c1 > kMaxBucket) overflow = 1;
@@ -452,7 +454,7 @@ build_small_kernel(const float* __restrict__ coords, Geom g, double step, int pa
   __syncthreads();
   if (!overflow) {
 #pragma unroll
-    for (int r = 0; r < 2; ++r)
+    for (int r = 0; r < KPT; ++r)
       if (bk[r] >= 0) keys[bstart[bk[r]] + arr[r]] = kk[r];
     __syncthreads();
 #pragma unroll
@@ -472,7 +474,7 @@ build_small_kernel(const float* __restrict__ coords, Geom g, double step, int pa
     int P = 2;
     while (P < N) P <<= 1;
 #pragma unroll
-    for (int r = 0; r < 2; ++r) {
+    for (int r = 0; r < KPT; ++r) {
       const int e = tid + r * kSmallThreads;
       if (e < P) keys[e] = kk[r];
     }
@@ -606,36 +608,44 @@ build_small_kernel(const float* __restrict__ coords, Geom g, double step, int pa
 
 }  // namespace
 
-hipError_t launch_build_neighbors(const float* coords, const Geom& g, int B, int64_t T, int64_t Ct,
+hipError_t launch_build_neighbors(const float* coords, const Geom& geom, int B, int64_t T, int64_t Ct,
                                   int grid_side, int k, int32_t* q_idx, int32_t* nbr,
                                   int32_t* key_idx, void* ws, hipStream_t st) {
   int bits = 0;   // ceil(log2(grid_side)); grid_side is validated to [1, 65536]
   while ((1 << bits) < grid_side) ++bits;
   const double step = (double)(1u << (16 - bits));
+  Geom g = geom;
   const int N = g.N, C = g.C;   // sizes of the (largest) image
+  // 2048 keys per workgroup suffice up to 2048 tokens; 4096 up to kSmallBuild
+  g.small_max = N <= 2 * kSmallThreads ? 2 * kSmallThreads : kSmallBuild;
   BuildWorkspace w = build_layout(ws, B, T, Ct, N);
-  // images of at most kSortChunk tokens: up to 8 workgroups per image share
-  // its clusters (each repeats the in-LDS sort), with up to 16 lanes per
-  // cluster in the candidate scan
+  // images of at most g.small_max tokens: up to 8 workgroups per image
+  // share its clusters (each repeats the in-LDS sort), with up to 16 lanes
+  // per cluster in the candidate scan
   const bool packed = g.tok_off != nullptr;
-  if (N <= kSortChunk || packed) {
-    const int cs = std::min(C, kSmallMaxC);
+  if (N <= g.small_max || packed) {
+    const int cs = std::min(C, g.small_max / 8);
     const int parts = std::max(1, std::min(8, (cs + 31) / 32));
     const int cp = (cs + parts - 1) / parts;
     int lanes = 16;
     while (lanes > 1 && lanes * cp > kSmallThreads) lanes >>= 1;
+    const bool wide = g.small_max > 2 * kSmallThreads;
     switch (k) {
 #define CA_SMALL(KK)                                                                            \
   case KK:                                                                                      \
-    hipLaunchKernelGGL(build_small_kernel<KK - 1>, dim3(B, parts), dim3(kSmallThreads), 0, st,  \
-                       coords, g, step, parts, lanes, q_idx, nbr, key_idx);                     \
+    if (wide)                                                                                   \
+      hipLaunchKernelGGL((build_small_kernel<KK - 1, 4>), dim3(B, parts), dim3(kSmallThreads), 0, \
+                         st, coords, g, step, parts, lanes, q_idx, nbr, key_idx);               \
+    else                                                                                        \
+      hipLaunchKernelGGL((build_small_kernel<KK - 1, 2>), dim3(B, parts), dim3(kSmallThreads), 0, \
+                         st, coords, g, step, parts, lanes, q_idx, nbr, key_idx);               \
     break;
       CA_SMALL(1) CA_SMALL(2) CA_SMALL(3) CA_SMALL(4) CA_SMALL(5) CA_SMALL(6) CA_SMALL(7) CA_SMALL(8)
 #undef CA_SMALL
       default:
         return hipErrorInvalidValue;
     }
-    if (N <= kSortChunk) return hipGetLastError();
+    if (N <= g.small_max) return hipGetLastError();
   }
   // larger images: segment ranks, merge rounds, centroids and boxes, selection
   const int segs = (N + kRankSeg - 1) / kRankSeg;

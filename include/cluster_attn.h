@@ -70,7 +70,7 @@ typedef enum { CA_F32 = 0, CA_BF16 = 1, CA_F16 = 2 } ca_dtype;
 
 /*
  * Workspace bytes needed by cluster_attn_build_neighbors for these sizes.
- * 0 for invalid sizes, and also for valid ones with N <= 2048: such an image
+ * 0 for invalid sizes, and also for valid ones with N <= 4096: such an image
  * is built by one workgroup entirely in LDS and needs no workspace.
  * Supported: N <= 2^22 tokens per image.
  */
@@ -129,7 +129,7 @@ int cluster_attn_build_neighbors(const float* coords, int B, int N, int grid_sid
  *             (the Python binding computes them).
  *   q_idx     [Ct, cs], nbr [Ct, k], key_idx [Ct, cs*k] int32 out.
  *   ws        at least cluster_attn_build_neighbors_varlen_workspace(...)
- *             bytes (0 when max_n <= 2048).
+ *             bytes (0 when max_n <= 4096).
  */
 size_t cluster_attn_build_neighbors_varlen_workspace(int B, int T, int Ct, int max_n, int cs,
                                                      int k);

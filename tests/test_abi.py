@@ -103,10 +103,11 @@ def test_workspace_grows_with_problem(lib):
     a = lib.cluster_attn_bwd_workspace(1, 32, 2048, 4, 32, 8, 48)
     b = lib.cluster_attn_bwd_workspace(1, 64, 2048, 4, 32, 8, 48)
     assert b > a > 0
-    # An image of at most 2048 tokens is built in one workgroup's LDS.
+    # An image of at most 4096 tokens is built in one workgroup's LDS.
     assert lib.cluster_attn_build_neighbors_workspace(4, 2048, 8, 6) == 0
+    assert lib.cluster_attn_build_neighbors_workspace(4, 4096, 8, 6) == 0
     assert lib.cluster_attn_build_neighbors_workspace(4, 65536, 8, 6) > \
-        lib.cluster_attn_build_neighbors_workspace(4, 4096, 8, 6) > 0
+        lib.cluster_attn_build_neighbors_workspace(4, 8192, 8, 6) > 0
 
 
 def test_build_validation(lib):
@@ -122,8 +123,8 @@ def test_build_validation(lib):
     assert build(G=0) == CA_ERR_SHAPE
     assert build(G=70000) == CA_ERR_SHAPE
     assert build(ptrs=[P, None, 3 * P, 4 * P]) == CA_ERR_NULL
-    assert build(N=4096, ws_bytes=16) == CA_ERR_WORKSPACE
-    assert build(N=4096, ws=None) == CA_ERR_NULL
+    assert build(N=8192, ws_bytes=16) == CA_ERR_WORKSPACE
+    assert build(N=8192, ws=None) == CA_ERR_NULL
     assert build(ptrs=[P, 2 * P, 2 * P + 4, 4 * P]) == CA_ERR_ALIAS
     assert build(B=0, ptrs=[None] * 4, ws=None) == CA_OK
 
@@ -139,10 +140,11 @@ def test_varlen_validation(lib):
     assert build(k=9) == CA_ERR_UNSUPPORTED
     assert build(ptrs=[P, None, 3 * P, 4 * P, 5 * P, 6 * P]) == CA_ERR_NULL
     assert build(ptrs=[P, 2 * P, 3 * P, 4 * P, 4 * P + 8, 6 * P]) == CA_ERR_ALIAS
-    assert build(max_n=3000, T=6000, Ct=760, ws_bytes=8) == CA_ERR_WORKSPACE
+    assert build(max_n=5000, T=6000, Ct=760, ws_bytes=8) == CA_ERR_WORKSPACE
     assert build(B=0, T=0, Ct=0, max_n=0, ptrs=[None] * 6, ws=None) == CA_OK
     assert lib.cluster_attn_build_neighbors_varlen_workspace(3, 100, 14, 50, 8, 6) == 0
-    assert lib.cluster_attn_build_neighbors_varlen_workspace(3, 6000, 760, 3000, 8, 6) > 0
+    assert lib.cluster_attn_build_neighbors_varlen_workspace(3, 6000, 760, 3000, 8, 6) == 0
+    assert lib.cluster_attn_build_neighbors_varlen_workspace(3, 6000, 760, 5000, 8, 6) > 0
     assert lib.cluster_attn_build_neighbors_varlen_workspace(3, 100, 14, 101, 8, 6) == 0
 
     p7 = [P * (i + 1) for i in range(7)]
