@@ -17,3 +17,4 @@ from .synth import (  # noqa: F401
 from .sampler import SAMPLER_CONFIGS, SamplerConfig, make_sampler_case  # noqa: F401
 from .merge import MERGE_CONFIGS, MergeConfig, make_merge_case  # noqa: F401
 from .ragged import RAGGED_CONFIGS, RaggedConfig, make_varlen_case  # noqa: F401
+from .volume import VOLUME_CONFIGS, VolumeConfig, make_volume_case  # noqa: F401

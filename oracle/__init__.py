@@ -7,7 +7,8 @@ links it, and it imports nothing from the product path.
 
 See :mod:`oracle.cluster_attention` (neighbour build and attention) and
 :mod:`oracle.knn_sampler` (the decoder's KNN-cache point sampler) and
-:mod:`oracle.token_merge` (adaptive off-grid token merging) for the
+:mod:`oracle.token_merge` (adaptive off-grid token merging) and
+:mod:`oracle.volume` (the neighbour build for 3D tokens) for the
 functions and the passages of the pages each one follows.
 """
 
@@ -46,4 +47,11 @@ from .token_merge import (  # noqa: F401
     merge_weights,
     merge_fwd,
     merge_bwd,
+)
+from .volume import (  # noqa: F401
+    quantize3,
+    morton_code3,
+    build_image3,
+    build_neighbors_3d,
+    build_neighbors_varlen_3d,
 )

@@ -147,23 +147,25 @@ def cluster_rows(perm: np.ndarray, cs: int) -> np.ndarray:
     return rows.reshape(C, cs)
 
 
-def centroid_keys(q_idx: np.ndarray, qx: np.ndarray, qy: np.ndarray, cs: int) -> np.ndarray:
+def centroid_keys(q_idx: np.ndarray, *axes, cs: int = 8) -> np.ndarray:
     """Reading 7: every cluster's mean fixed-point coordinate times
-    L = lcm(1..cs), as exact integers: (sum of the n members) * (L / n).
-    [C, 2] int64 (below 2**26 for cs = 8, so squared distances fit int64)."""
+    L = lcm(1..cs), as exact integers: (sum of the n members) * (L / n),
+    one column per axis (qx, qy[, qz]).  [C, len(axes)] int64 (below 2**26
+    for cs = 8, so squared distances fit int64)."""
     L = math.lcm(*range(1, cs + 1))
     live = q_idx >= 0
     safe = np.where(live, q_idx, 0)
     n = live.sum(axis=1)                      # members per cluster, >= 1
-    sx = np.where(live, qx[safe], 0).sum(axis=1)
-    sy = np.where(live, qy[safe], 0).sum(axis=1)
-    return np.stack([sx * (L // n), sy * (L // n)], axis=1).astype(np.int64)
+    cols = [np.where(live, np.asarray(a)[safe], 0).sum(axis=1) * (L // n) for a in axes]
+    return np.stack(cols, axis=1).astype(np.int64)
 
 
 def _sq_dist(S: np.ndarray, rows: np.ndarray) -> np.ndarray:
-    dx = S[rows, 0][:, None] - S[None, :, 0]
-    dy = S[rows, 1][:, None] - S[None, :, 1]
-    return dx * dx + dy * dy  # exact int64 (scaled sums below 2**26)
+    d2 = np.zeros((rows.size, S.shape[0]), dtype=np.int64)
+    for a in range(S.shape[1]):              # every axis of the centroids
+        d = S[rows, a][:, None] - S[None, :, a]
+        d2 += d * d
+    return d2  # exact int64 (scaled sums below 2**26)
 
 
 def nearest_clusters(S: np.ndarray, k: int, block: int = 512) -> np.ndarray:
@@ -198,9 +200,7 @@ def nearest_clusters_fullsort(S: np.ndarray, k: int) -> np.ndarray:
     C = S.shape[0]
     out = np.full((C, k), -1, dtype=np.int64)
     for c in range(C):
-        dx = S[:, 0] - S[c, 0]
-        dy = S[:, 1] - S[c, 1]
-        d2 = dx * dx + dy * dy
+        d2 = ((S - S[c]) ** 2).sum(axis=1)
         cand = np.array([b for b in range(C) if b != c], dtype=np.int64)
         order = cand[np.lexsort((cand, d2[cand]))]
         row = [c] + list(order[: k - 1])
@@ -231,7 +231,7 @@ def build_image(coords: np.ndarray, grid_side: int, cs: int = 8, k: int = 6):
     qx, qy = quantize(coords, grid_side)
     perm = balanced_clusters(morton_code(qx, qy))
     q_idx = cluster_rows(perm, cs)
-    S = centroid_keys(q_idx, qx, qy, cs)
+    S = centroid_keys(q_idx, qx, qy, cs=cs)
     nbr = nearest_clusters(S, k)
     _, key_idx = key_lists(q_idx, nbr, cs)
     return q_idx, nbr, key_idx
