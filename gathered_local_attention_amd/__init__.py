@@ -8,7 +8,7 @@ no CPU fallback: if the library is missing, the calls raise.
 
 Functions
 ---------
-build_neighbors(coords, grid_side, cs=8, k=6) -> (perm, nbr, key_idx)
+build_neighbors(coords, grid_side, cs=8, k=6) -> (perm, nbr, key_idx)   (2D or 3D)
 fwd(q, k, v, q_idx, key_idx, scale=None) -> (o, lse)
 bwd(q, k, v, o, do, lse, q_idx, key_idx, scale=None) -> (dq, dk, dv)
 cluster_attention(q, k, v, q_idx, key_idx, scale=None) -> o   (autograd)
@@ -102,14 +102,15 @@ def build_neighbors(coords: torch.Tensor, grid_side: int, cs: int = 8, k: int = 
                     workspace: torch.Tensor | None = None):
     """Morton-order balanced clusters and nearest-cluster key lists.
 
-    coords: [B, N, 2] float32 device tensor (x = column, y = row).
+    coords: [B, N, 2] float32 device tensor (x = column, y = row), or
+    [B, N, 3] for 3D tokens (z = slice; 14-bit fixed point per axis).
     Returns perm [B, C*cs] (== q_idx [B, C, cs] as a view, C = ceil(N/cs);
     -1 after the members of a partial last cluster), nbr [B, C, k] and
     key_idx [B, C, cs*k], all int32."""
     lib = _lib.load()
-    B, N, two = coords.shape
-    if two != 2:
-        raise ValueError("coords must be [B, N, 2]")
+    B, N, dims = coords.shape
+    if dims not in (2, 3):
+        raise ValueError("coords must be [B, N, 2] or [B, N, 3]")
     _dev(coords, "coords", torch.float32)
     C = -(-N // cs) if cs else 0
     perm = torch.empty((B, C * cs), dtype=torch.int32, device=coords.device)
@@ -118,10 +119,10 @@ def build_neighbors(coords: torch.Tensor, grid_side: int, cs: int = 8, k: int = 
     need = lib.cluster_attn_build_neighbors_workspace(B, N, cs, k)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=coords.device)
-    _check(lib.cluster_attn_build_neighbors(
-        coords.data_ptr(), B, N, int(grid_side), cs, k, perm.data_ptr(), nbr.data_ptr(),
-        key_idx.data_ptr(), workspace.data_ptr(), workspace.numel(), _stream(coords)),
-        "cluster_attn_build_neighbors")
+    fn = lib.cluster_attn_build_neighbors if dims == 2 else lib.cluster_attn_build_neighbors_3d
+    _check(fn(coords.data_ptr(), B, N, int(grid_side), cs, k, perm.data_ptr(), nbr.data_ptr(),
+              key_idx.data_ptr(), workspace.data_ptr(), workspace.numel(), _stream(coords)),
+           "cluster_attn_build_neighbors" + ("" if dims == 2 else "_3d"))
     return perm, nbr, key_idx
 
 
@@ -218,15 +219,17 @@ def varlen_offsets(lengths, cs: int = 8):
 
 def build_neighbors_varlen(coords: torch.Tensor, lengths, grid_side: int, cs: int = 8, k: int = 6,
                            workspace: torch.Tensor | None = None, offsets=None):
-    """Neighbour lists of a packed batch: coords [T, 2] float32 (device)
-    holds the images one after another, image b having lengths[b] tokens.
+    """Neighbour lists of a packed batch: coords [T, 2] float32 (device;
+    [T, 3] for 3D tokens) holds the images one after another, image b
+    having lengths[b] tokens.
     Returns q_idx [Ct, cs], nbr [Ct, k], key_idx [Ct, cs*k] (int32,
     batch-global ids, -1 padding) and the device offsets tok_off, clu_off
     [B+1] int32.  ``offsets`` may pass that pair from an earlier call with
     the same lengths (no host-to-device copy then)."""
     lib = _lib.load()
-    if coords.dim() != 2 or coords.shape[1] != 2:
-        raise ValueError("coords must be [T, 2]")
+    if coords.dim() != 2 or coords.shape[1] not in (2, 3):
+        raise ValueError("coords must be [T, 2] or [T, 3]")
+    dims = coords.shape[1]
     _dev(coords, "coords", torch.float32)
     tok, clu = varlen_offsets(lengths, cs)
     B, T, Ct = len(tok) - 1, tok[-1], clu[-1]
@@ -249,11 +252,12 @@ def build_neighbors_varlen(coords: torch.Tensor, lengths, grid_side: int, cs: in
     need = lib.cluster_attn_build_neighbors_varlen_workspace(B, T, Ct, max_n, cs, k)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
-    _check(lib.cluster_attn_build_neighbors_varlen(
-        coords.data_ptr(), B, T, Ct, max_n, tok_off.data_ptr(), clu_off.data_ptr(),
-        int(grid_side), cs, k, q_idx.data_ptr(), nbr.data_ptr(), key_idx.data_ptr(),
-        workspace.data_ptr(), workspace.numel(), _stream(coords)),
-        "cluster_attn_build_neighbors_varlen")
+    fn = (lib.cluster_attn_build_neighbors_varlen if dims == 2
+          else lib.cluster_attn_build_neighbors_varlen_3d)
+    _check(fn(coords.data_ptr(), B, T, Ct, max_n, tok_off.data_ptr(), clu_off.data_ptr(),
+              int(grid_side), cs, k, q_idx.data_ptr(), nbr.data_ptr(), key_idx.data_ptr(),
+              workspace.data_ptr(), workspace.numel(), _stream(coords)),
+           "cluster_attn_build_neighbors_varlen" + ("" if dims == 2 else "_3d"))
     return q_idx, nbr, key_idx, tok_off, clu_off
 
 

@@ -27,6 +27,11 @@ SIGNATURES = {
     "cluster_attn_build_neighbors_varlen": (
         _c_int, [_vp, _c_int, _c_int, _c_int, _c_int, _vp, _vp, _c_int, _c_int, _c_int,
                  _vp, _vp, _vp, _vp, _c_size, _vp]),
+    "cluster_attn_build_neighbors_3d": (
+        _c_int, [_vp, _c_int, _c_int, _c_int, _c_int, _c_int, _vp, _vp, _vp, _vp, _c_size, _vp]),
+    "cluster_attn_build_neighbors_varlen_3d": (
+        _c_int, [_vp, _c_int, _c_int, _c_int, _c_int, _vp, _vp, _c_int, _c_int, _c_int,
+                 _vp, _vp, _vp, _vp, _c_size, _vp]),
     "cluster_attn_fwd_varlen": (
         _c_int, [_c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _f,
                  _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),

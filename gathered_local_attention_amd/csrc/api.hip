@@ -127,32 +127,6 @@ size_t cluster_attn_build_neighbors_workspace(int B, int N, int cs, int k) {
   return ca::build_layout(nullptr, B, (int64_t)B * N, B * clusters_of(N, cs), N).bytes;
 }
 
-int cluster_attn_build_neighbors(const float* coords, int B, int N, int grid_side, int cs, int k,
-                                 int32_t* perm, int32_t* nbr, int32_t* key_idx, void* ws,
-                                 size_t ws_bytes, void* hip_stream) {
-  if (B < 0 || N < 0) return fail(CA_ERR_SHAPE, "bad sizes B=%d N=%d", B, N);
-  if (cs != 8) return fail(CA_ERR_UNSUPPORTED, "cluster size %d (only 8 is supported)", cs);
-  if (k < 1 || k > 8) return fail(CA_ERR_UNSUPPORTED, "k=%d outside 1..8", k);
-  if (N > kMaxTokensPerImage) return fail(CA_ERR_SHAPE, "N=%d exceeds 2^22 tokens per image", N);
-  if ((int64_t)B * N > (int64_t(1) << 31) - 1) return fail(CA_ERR_SHAPE, "B*N above 2^31 - 1");
-  if (grid_side < 1 || grid_side > 65536)
-    return fail(CA_ERR_SHAPE, "grid_side=%d outside [1, 65536]", grid_side);
-  if (B == 0 || N == 0) return ok();
-  if (!coords || !perm || !nbr || !key_idx) return fail(CA_ERR_NULL, "NULL tensor pointer");
-  const int64_t C = clusters_of(N, cs);
-  const size_t need = ca::build_layout(nullptr, B, (int64_t)B * N, B * C, N).bytes;
-  if (need && !ws) return fail(CA_ERR_NULL, "NULL workspace (%zu bytes needed)", need);
-  if (ws_bytes < need) return fail(CA_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
-  Range outs[] = {{perm, (size_t)(B * C * cs) * 4}, {nbr, (size_t)(B * C * k) * 4},
-                  {key_idx, (size_t)(B * C * k * cs) * 4}, {ws, need}};
-  Range ins[] = {{coords, (size_t)B * N * 8}};
-  if (int s = check_alias(outs, 4, ins, 1)) return s;
-  const ca::Geom g{nullptr, nullptr, N, (int)C, 0};
-  return hip_status(ca::launch_build_neighbors(coords, g, B, (int64_t)B * N, B * C, grid_side, k,
-                                               perm, nbr, key_idx, ws, (hipStream_t)hip_stream),
-                    "build_neighbors launch");
-}
-
 size_t cluster_attn_build_neighbors_varlen_workspace(int B, int T, int Ct, int max_n, int cs,
                                                      int k) {
   if (B < 0 || T < 0 || Ct < 0 || max_n < 0 || max_n > T || cs != 8 || k < 1 || k > 8 ||
@@ -161,11 +135,43 @@ size_t cluster_attn_build_neighbors_varlen_workspace(int B, int T, int Ct, int m
   return ca::build_layout(nullptr, B, T, Ct, max_n).bytes;
 }
 
-int cluster_attn_build_neighbors_varlen(const float* coords, int B, int T, int Ct, int max_n,
-                                        const int32_t* tok_off, const int32_t* clu_off,
-                                        int grid_side, int cs, int k, int32_t* q_idx,
-                                        int32_t* nbr, int32_t* key_idx, void* ws,
-                                        size_t ws_bytes, void* hip_stream) {
+}  // extern "C"
+
+namespace {
+
+// Equal-size images: coords [B, N, dims].
+int build_uniform(int dims, const float* coords, int B, int N, int grid_side, int cs, int k,
+                  int32_t* perm, int32_t* nbr, int32_t* key_idx, void* ws, size_t ws_bytes,
+                  void* hip_stream) {
+  if (B < 0 || N < 0) return fail(CA_ERR_SHAPE, "bad sizes B=%d N=%d", B, N);
+  if (cs != 8) return fail(CA_ERR_UNSUPPORTED, "cluster size %d (only 8 is supported)", cs);
+  if (k < 1 || k > 8) return fail(CA_ERR_UNSUPPORTED, "k=%d outside 1..8", k);
+  if (N > kMaxTokensPerImage) return fail(CA_ERR_SHAPE, "N=%d exceeds 2^22 tokens per image", N);
+  if ((int64_t)B * N > (int64_t(1) << 31) - 1) return fail(CA_ERR_SHAPE, "B*N above 2^31 - 1");
+  const int gmax = dims == 2 ? 65536 : 16384;
+  if (grid_side < 1 || grid_side > gmax)
+    return fail(CA_ERR_SHAPE, "grid_side=%d outside [1, %d]", grid_side, gmax);
+  if (B == 0 || N == 0) return ok();
+  if (!coords || !perm || !nbr || !key_idx) return fail(CA_ERR_NULL, "NULL tensor pointer");
+  const int64_t C = clusters_of(N, cs);
+  const size_t need = ca::build_layout(nullptr, B, (int64_t)B * N, B * C, N).bytes;
+  if (need && !ws) return fail(CA_ERR_NULL, "NULL workspace (%zu bytes needed)", need);
+  if (ws_bytes < need) return fail(CA_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
+  Range outs[] = {{perm, (size_t)(B * C * cs) * 4}, {nbr, (size_t)(B * C * k) * 4},
+                  {key_idx, (size_t)(B * C * k * cs) * 4}, {ws, need}};
+  Range ins[] = {{coords, (size_t)B * N * 4 * dims}};
+  if (int s = check_alias(outs, 4, ins, 1)) return s;
+  const ca::Geom g{nullptr, nullptr, N, (int)C, 0};
+  return hip_status(ca::launch_build_neighbors(coords, g, dims, B, (int64_t)B * N, B * C, grid_side,
+                                               k, perm, nbr, key_idx, ws, (hipStream_t)hip_stream),
+                    "build_neighbors launch");
+}
+
+// Packed images: coords [T, dims] with device offsets.
+int build_packed(int dims, const float* coords, int B, int T, int Ct, int max_n,
+                 const int32_t* tok_off, const int32_t* clu_off, int grid_side, int cs, int k,
+                 int32_t* q_idx, int32_t* nbr, int32_t* key_idx, void* ws, size_t ws_bytes,
+                 void* hip_stream) {
   if (B < 0 || T < 0 || Ct < 0 || max_n < 0 || max_n > T)
     return fail(CA_ERR_SHAPE, "bad sizes B=%d T=%d Ct=%d max_n=%d", B, T, Ct, max_n);
   if (cs != 8) return fail(CA_ERR_UNSUPPORTED, "cluster size %d (only 8 is supported)", cs);
@@ -174,8 +180,9 @@ int cluster_attn_build_neighbors_varlen(const float* coords, int B, int T, int C
     return fail(CA_ERR_SHAPE, "max_n=%d exceeds 2^22 tokens per image", max_n);
   if (Ct < clusters_of(T, cs) || Ct > T || (int64_t)Ct * cs * k > (int64_t(1) << 31) - 1)
     return fail(CA_ERR_SHAPE, "Ct=%d is inconsistent with T=%d tokens", Ct, T);
-  if (grid_side < 1 || grid_side > 65536)
-    return fail(CA_ERR_SHAPE, "grid_side=%d outside [1, 65536]", grid_side);
+  const int gmax = dims == 2 ? 65536 : 16384;
+  if (grid_side < 1 || grid_side > gmax)
+    return fail(CA_ERR_SHAPE, "grid_side=%d outside [1, %d]", grid_side, gmax);
   if (B == 0 || T == 0) return ok();
   if (!coords || !tok_off || !clu_off || !q_idx || !nbr || !key_idx)
     return fail(CA_ERR_NULL, "NULL tensor pointer");
@@ -184,13 +191,49 @@ int cluster_attn_build_neighbors_varlen(const float* coords, int B, int T, int C
   if (ws_bytes < need) return fail(CA_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
   Range outs[] = {{q_idx, (size_t)Ct * cs * 4}, {nbr, (size_t)Ct * k * 4},
                   {key_idx, (size_t)Ct * k * cs * 4}, {ws, need}};
-  Range ins[] = {{coords, (size_t)T * 8}, {tok_off, (size_t)(B + 1) * 4},
+  Range ins[] = {{coords, (size_t)T * 4 * dims}, {tok_off, (size_t)(B + 1) * 4},
                  {clu_off, (size_t)(B + 1) * 4}};
   if (int s = check_alias(outs, 4, ins, 3)) return s;
   const ca::Geom g{tok_off, clu_off, max_n, (int)clusters_of(max_n, cs), 0};
-  return hip_status(ca::launch_build_neighbors(coords, g, B, T, Ct, grid_side, k, q_idx, nbr,
+  return hip_status(ca::launch_build_neighbors(coords, g, dims, B, T, Ct, grid_side, k, q_idx, nbr,
                                                key_idx, ws, (hipStream_t)hip_stream),
                     "build_neighbors_varlen launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+int cluster_attn_build_neighbors(const float* coords, int B, int N, int grid_side, int cs, int k,
+                                 int32_t* perm, int32_t* nbr, int32_t* key_idx, void* ws,
+                                 size_t ws_bytes, void* hip_stream) {
+  return build_uniform(2, coords, B, N, grid_side, cs, k, perm, nbr, key_idx, ws, ws_bytes,
+                       hip_stream);
+}
+
+int cluster_attn_build_neighbors_3d(const float* coords, int B, int N, int grid_side, int cs,
+                                    int k, int32_t* perm, int32_t* nbr, int32_t* key_idx,
+                                    void* ws, size_t ws_bytes, void* hip_stream) {
+  return build_uniform(3, coords, B, N, grid_side, cs, k, perm, nbr, key_idx, ws, ws_bytes,
+                       hip_stream);
+}
+
+int cluster_attn_build_neighbors_varlen(const float* coords, int B, int T, int Ct, int max_n,
+                                        const int32_t* tok_off, const int32_t* clu_off,
+                                        int grid_side, int cs, int k, int32_t* q_idx,
+                                        int32_t* nbr, int32_t* key_idx, void* ws,
+                                        size_t ws_bytes, void* hip_stream) {
+  return build_packed(2, coords, B, T, Ct, max_n, tok_off, clu_off, grid_side, cs, k, q_idx, nbr,
+                      key_idx, ws, ws_bytes, hip_stream);
+}
+
+int cluster_attn_build_neighbors_varlen_3d(const float* coords, int B, int T, int Ct, int max_n,
+                                           const int32_t* tok_off, const int32_t* clu_off,
+                                           int grid_side, int cs, int k, int32_t* q_idx,
+                                           int32_t* nbr, int32_t* key_idx, void* ws,
+                                           size_t ws_bytes, void* hip_stream) {
+  return build_packed(3, coords, B, T, Ct, max_n, tok_off, clu_off, grid_side, cs, k, q_idx, nbr,
+                      key_idx, ws, ws_bytes, hip_stream);
 }
 
 }  // extern "C"

@@ -116,10 +116,10 @@ __host__ __device__ __forceinline__ int mean_scale(int members, int n) {
 }
 
 struct BuildWorkspace {
-  uint32_t* qsorted;   // [Ct * 8] packed (qx | qy << 16) in cluster order
-  uint64_t* keys[2];   // [T]      (code << 32 | token) in sorted runs, two buffers
-  float2* cent;        // [Ct]     scaled centroid sums
-  float4* box;         // [B, ceil(Cmax / kBoxTile)]  centroid bounding boxes
+  void* qsorted;       // [Ct * 8] quantised coordinates in cluster order (<= 8 bytes each)
+  uint64_t* keys[2];   // [T]      (code << token bits | token) in sorted runs, two buffers
+  void* cent;          // [Ct]     scaled centroid sums (float2 in 2D, float4 in 3D)
+  void* box;           // [B, ceil(Cmax / kBoxTile), 2]  per-tile (min, max) centroid vectors
   size_t bytes;
 };
 
@@ -137,11 +137,12 @@ static inline BuildWorkspace build_layout(void* base, int64_t B, int64_t T, int6
   };
   const bool big = maxN > kSmallBuild;
   const int64_t tiles = ((maxN + 7) / 8 + kBoxTile - 1) / kBoxTile;
-  w.qsorted = (uint32_t*)take(big ? (size_t)(Ct * 8) * sizeof(uint32_t) : 0);
+  // sized for 3D (the larger vectors); 2D uses the front of each part
+  w.qsorted = take(big ? (size_t)(Ct * 8) * sizeof(uint64_t) : 0);
   w.keys[0] = (uint64_t*)take(big ? (size_t)T * sizeof(uint64_t) : 0);
   w.keys[1] = (uint64_t*)take(big ? (size_t)T * sizeof(uint64_t) : 0);
-  w.cent = (float2*)take(big ? (size_t)Ct * sizeof(float2) : 0);
-  w.box = (float4*)take(big ? (size_t)(B * tiles) * sizeof(float4) : 0);
+  w.cent = take(big ? (size_t)Ct * sizeof(float4) : 0);
+  w.box = take(big ? (size_t)(B * tiles * 2) * sizeof(float4) : 0);
   w.bytes = p;
   return w;
 }
@@ -250,8 +251,10 @@ __device__ __forceinline__ uint32_t quantize_axis(float c, double step) {
 // Attention launchers take B images of N tokens and C clusters each (q_idx
 // [B, C, 8], C = ceil(N / 8)); a packed batch runs as one image (B = 1) of
 // all T tokens and Ct clusters with batch-global ids.
-hipError_t launch_build_neighbors(const float* coords, const Geom& g, int B, int64_t T, int64_t Ct,
-                                  int grid_side, int k, int32_t* q_idx, int32_t* nbr,
+// dims = 2: coords [.., 2] (16-bit fixed point per axis); dims = 3: coords
+// [.., 3] (14-bit fixed point per axis).
+hipError_t launch_build_neighbors(const float* coords, const Geom& g, int dims, int B, int64_t T,
+                                  int64_t Ct, int grid_side, int k, int32_t* q_idx, int32_t* nbr,
                                   int32_t* key_idx, void* ws, hipStream_t st);
 
 hipError_t launch_fwd_valu(int dt, int B, int N, int C, int H, int nk, float scale, const void* q,

@@ -1,4 +1,5 @@
-// Neighbour-list build for local cluster attention on gfx950.
+// Neighbour-list build for local cluster attention on gfx950, for 2D
+// tokens and (templated on the dimension) 3D tokens.
 //
 // Source: English notes page "AFFMAE: Scalable Vision Pre-Training for
 // High-Resolution Microscopy Segmentation on Desktop Hardware", "Overall
@@ -39,6 +40,11 @@
 // images of at most Geom::small_max (2048 or 4096) tokens by the in-LDS
 // kernel, larger ones by the segment / merge path; both skip the other's
 // images.
+//
+// 3D tokens (notes page, "Limitations & Future Work": 3D voxels named as
+// the open extension): the same steps with three axes, each quantised to 14
+// bits, a 42-bit Morton code with x, y, z in bits 3b, 3b+1, 3b+2, and a
+// 64-bit sort key (code << 22 | token).
 #include "common.h"
 
 #include <algorithm>
@@ -49,7 +55,7 @@ namespace {
 
 constexpr int kRankThreads = 256;
 
-__device__ __forceinline__ uint32_t spread16(uint32_t v) {
+__host__ __device__ __forceinline__ uint32_t spread16(uint32_t v) {
   v &= 0xFFFFu;
   v = (v | (v << 8)) & 0x00FF00FFu;
   v = (v | (v << 4)) & 0x0F0F0F0Fu;
@@ -58,7 +64,7 @@ __device__ __forceinline__ uint32_t spread16(uint32_t v) {
   return v;
 }
 
-__device__ __forceinline__ uint32_t compact16(uint32_t v) {
+__host__ __device__ __forceinline__ uint32_t compact16(uint32_t v) {
   v &= 0x55555555u;
   v = (v | (v >> 1)) & 0x33333333u;
   v = (v | (v >> 2)) & 0x0F0F0F0Fu;
@@ -67,12 +73,109 @@ __device__ __forceinline__ uint32_t compact16(uint32_t v) {
   return v;
 }
 
+// bit b of v (b < 21) -> bit 3b, by shifting groups into place
+__host__ __device__ __forceinline__ uint64_t spread3(uint32_t v) {
+  uint64_t x = v & 0x1FFFFFu;
+  x = (x | (x << 32)) & 0x001F00000000FFFFull;
+  x = (x | (x << 16)) & 0x001F0000FF0000FFull;
+  x = (x | (x << 8)) & 0x100F00F00F00F00Full;
+  x = (x | (x << 4)) & 0x10C30C30C30C30C3ull;
+  x = (x | (x << 2)) & 0x1249249249249249ull;
+  return x;
+}
+
+// bits 3b of x -> bit b (the inverse of spread3)
+__host__ __device__ __forceinline__ uint32_t compact3(uint64_t x) {
+  x &= 0x1249249249249249ull;
+  x = (x | (x >> 2)) & 0x10C30C30C30C30C3ull;
+  x = (x | (x >> 4)) & 0x100F00F00F00F00Full;
+  x = (x | (x >> 8)) & 0x001F0000FF0000FFull;
+  x = (x | (x >> 16)) & 0x001F00000000FFFFull;
+  x = (x | (x >> 32)) & 0x00000000001FFFFFull;
+  return (uint32_t)x;
+}
+
+// What differs between 2D and 3D tokens: the fixed-point width, the Morton
+// interleave, the split of the 64-bit sort key into code and token, and the
+// centroid vector types.  Sort keys are (code << kTokBits | token) in both,
+// so the top 11 key bits are the top 11 code bits.
+template <int DIM> struct Space;
+
+template <> struct Space<2> {
+  static constexpr int kTokBits = 32;
+  static constexpr uint32_t kQMax = 0xFFFFu;
+  typedef uint32_t Packed;   // quantised coordinates of a sorted token: qx | qy << 16
+  typedef int2 ICent;        // scaled centroid sums (integers)
+  typedef float2 FCent;      // the same as exact floats (below 2^22)
+  static __device__ __forceinline__ uint64_t code(const float* __restrict__ c, int64_t e,
+                                                  double step) {
+    const float2 p = reinterpret_cast<const float2*>(c)[e];
+    return spread16(quantize_axis(p.x, step)) | (spread16(quantize_axis(p.y, step)) << 1);
+  }
+  static __device__ __forceinline__ void axes(uint64_t code, int (&q)[2]) {
+    q[0] = (int)compact16((uint32_t)code);
+    q[1] = (int)compact16((uint32_t)code >> 1);
+  }
+  static __device__ __forceinline__ Packed pack(uint64_t code) {
+    return compact16((uint32_t)code) | (compact16((uint32_t)code >> 1) << 16);
+  }
+  static __device__ __forceinline__ void unpack(Packed w, int (&q)[2]) {
+    q[0] = (int)(w & 0xFFFFu);
+    q[1] = (int)(w >> 16);
+  }
+  static __device__ __forceinline__ ICent icent(const int (&s)[2]) { return make_int2(s[0], s[1]); }
+  static __device__ __forceinline__ FCent fcent(const int (&s)[2]) {
+    return make_float2((float)s[0], (float)s[1]);
+  }
+};
+
+template <> struct Space<3> {
+  static constexpr int kTokBits = 22;
+  static constexpr uint32_t kQMax = 0x3FFFu;
+  typedef uint64_t Packed;   // the Morton code itself
+  typedef int4 ICent;
+  typedef float4 FCent;
+  static __device__ __forceinline__ uint32_t q14(float c, double step) {
+    double q = floor(((double)c + 0.5) * step);   // exact, as in quantize_axis
+    q = q < 0.0 ? 0.0 : (q > (double)kQMax ? (double)kQMax : q);
+    return (uint32_t)q;
+  }
+  static __device__ __forceinline__ uint64_t code(const float* __restrict__ c, int64_t e,
+                                                  double step) {
+    const float* p = c + 3 * e;
+    return spread3(q14(p[0], step)) | (spread3(q14(p[1], step)) << 1) |
+           (spread3(q14(p[2], step)) << 2);
+  }
+  static __device__ __forceinline__ void axes(uint64_t code, int (&q)[3]) {
+    q[0] = (int)compact3(code);
+    q[1] = (int)compact3(code >> 1);
+    q[2] = (int)compact3(code >> 2);
+  }
+  static __device__ __forceinline__ Packed pack(uint64_t code) { return code; }
+  static __device__ __forceinline__ void unpack(Packed w, int (&q)[3]) { axes(w, q); }
+  static __device__ __forceinline__ ICent icent(const int (&s)[3]) {
+    return make_int4(s[0], s[1], s[2], 0);
+  }
+  static __device__ __forceinline__ FCent fcent(const int (&s)[3]) {
+    return make_float4((float)s[0], (float)s[1], (float)s[2], 0.f);
+  }
+};
+
+__device__ __forceinline__ void get(int2 v, int (&a)[2]) { a[0] = v.x; a[1] = v.y; }
+__device__ __forceinline__ void get(int4 v, int (&a)[3]) { a[0] = v.x; a[1] = v.y; a[2] = v.z; }
+__device__ __forceinline__ void get(float2 v, float (&a)[2]) { a[0] = v.x; a[1] = v.y; }
+__device__ __forceinline__ void get(float4 v, float (&a)[3]) { a[0] = v.x; a[1] = v.y; a[2] = v.z; }
+
+template <int DIM> __device__ __forceinline__ uint64_t tok_mask() {
+  return (uint64_t(1) << Space<DIM>::kTokBits) - 1;
+}
 
 // Rank the tokens of one segment.  grid = (kRankSeg / 64, B * segs), where
 // segment `seg % segs` of image `seg / segs` is [start, start + L) of that
 // image.  Each workgroup ranks 64 tokens (one per lane); its four
 // wavefronts each count one quarter of the segment's keys, read from LDS as
 // broadcast 16-byte loads.  The keys land sorted inside their segment.
+template <int DIM>
 __global__ void __launch_bounds__(kRankThreads)
 rank_kernel(const float* __restrict__ coords, Geom g, int segs_per_image, double step,
             uint64_t* __restrict__ run_keys) {
@@ -86,13 +189,10 @@ rank_kernel(const float* __restrict__ coords, Geom g, int segs_per_image, double
   if (n <= g.small_max) return;                       // built by the in-LDS kernel
   const int L = min(kRankSeg, n - start);
   if (L <= 0) return;
-  const float2* xy = reinterpret_cast<const float2*>(coords) + (int64_t)t0 + start;
+  const float* img = coords + ((int64_t)t0 + start) * DIM;
 
-  for (int e = threadIdx.x; e < L; e += kRankThreads) {
-    float2 c = xy[e];
-    uint32_t code = spread16(quantize_axis(c.x, step)) | (spread16(quantize_axis(c.y, step)) << 1);
-    keys[e] = ((uint64_t)code << 32) | (uint32_t)(start + e);
-  }
+  for (int e = threadIdx.x; e < L; e += kRankThreads)
+    keys[e] = (Space<DIM>::code(img, e, step) << Space<DIM>::kTokBits) | (uint32_t)(start + e);
   if (threadIdx.x == 0 && (L & 1)) keys[L] = ~0ull;   // pad to an even count
   __syncthreads();
 
@@ -122,11 +222,12 @@ rank_kernel(const float* __restrict__ coords, Geom g, int segs_per_image, double
 // place in the merged run is its place in its own run plus the number of
 // keys of the partner run below it (an image already in one run is
 // copied).  The last round (out == nullptr) writes the q_idx rows (token
-// ids) and the packed quantised coordinates, decoded from the code, at the
-// image's cluster slots.
+// ids) and the quantised coordinates of the sorted tokens, decoded from the
+// code, at the image's cluster slots.
+template <int DIM>
 __global__ void __launch_bounds__(kRankThreads)
 merge_round_kernel(Geom g, int run, const uint64_t* __restrict__ in, uint64_t* __restrict__ out,
-                   int32_t* __restrict__ q_idx, uint32_t* __restrict__ qsorted) {
+                   int32_t* __restrict__ q_idx, typename Space<DIM>::Packed* __restrict__ qsorted) {
   const int x = blockIdx.x * kRankThreads + threadIdx.x;
   int t0, n, c0, nc;
   g.image(blockIdx.y, t0, n, c0, nc);
@@ -148,52 +249,75 @@ merge_round_kernel(Geom g, int run, const uint64_t* __restrict__ in, uint64_t* _
   if (out) {
     out[(int64_t)t0 + pos] = key;
   } else {
-    const uint32_t code = (uint32_t)(key >> 32);
     const int64_t at = (int64_t)c0 * 8 + pos;
-    q_idx[at] = g.tok_base(t0) + (int32_t)(uint32_t)key;
-    qsorted[at] = compact16(code) | (compact16(code >> 1) << 16);
+    q_idx[at] = g.tok_base(t0) + (int32_t)(key & tok_mask<DIM>());
+    qsorted[at] = Space<DIM>::pack(key >> Space<DIM>::kTokBits);
   }
 }
 
-// Scaled centroid sums of every cluster and the bounding box (min x, min
-// y, max x, max y) of every tile of kBoxTile consecutive clusters of an
-// image.  grid = (ceil(Cmax / kBoxTile), B), one wavefront per tile.  The
-// absent members of a partial last cluster get -1 in q_idx here.
+// Scaled centroid sums of every cluster and the bounding box (per axis
+// minimum and maximum, stored as two centroid vectors) of every tile of
+// kBoxTile consecutive clusters of an image.  grid = (ceil(Cmax / kBoxTile),
+// B), one wavefront per tile.  The absent members of a partial last cluster
+// get -1 in q_idx here.
+template <int DIM>
 __global__ void __launch_bounds__(kBoxTile)
-centroid_box_kernel(Geom g, const uint32_t* __restrict__ qsorted, float2* __restrict__ cent_all,
-                    float4* __restrict__ box_all, int32_t* __restrict__ q_idx) {
+centroid_box_kernel(Geom g, const typename Space<DIM>::Packed* __restrict__ qsorted,
+                    typename Space<DIM>::FCent* __restrict__ cent_all,
+                    typename Space<DIM>::FCent* __restrict__ box_all, int32_t* __restrict__ q_idx) {
+  typedef Space<DIM> S;
   const int t = blockIdx.x;
   const int b = blockIdx.y;
   int t0, n, c0, nc;
   g.image(b, t0, n, c0, nc);
   if (n <= g.small_max) return;
   const int c = t * kBoxTile + threadIdx.x;
-  float lx = INFINITY, ly = INFINITY, hx = -INFINITY, hy = -INFINITY;
+  float lo[DIM], hi[DIM];
+#pragma unroll
+  for (int a = 0; a < DIM; ++a) {
+    lo[a] = INFINITY;
+    hi[a] = -INFINITY;
+  }
   if (c < nc) {
     const int members = min(8, n - 8 * c);
-    const uint32_t* q8 = qsorted + ((int64_t)c0 + c) * 8;
-    int sx = 0, sy = 0;
+    const typename S::Packed* q8 = qsorted + ((int64_t)c0 + c) * 8;
+    int sum[DIM] = {};
     for (int m = 0; m < members; ++m) {
-      const uint32_t w = q8[m];
-      sx += (int)(w & 0xFFFFu);
-      sy += (int)(w >> 16);
+      int q[DIM];
+      S::unpack(q8[m], q);
+#pragma unroll
+      for (int a = 0; a < DIM; ++a) sum[a] += q[a];
     }
     const int f = mean_scale(members, n);
-    // below 2^22: exact as floats
-    const float2 s = make_float2((float)(sx * f), (float)(sy * f));
-    cent_all[(int64_t)c0 + c] = s;
-    lx = hx = s.x;
-    ly = hy = s.y;
+#pragma unroll
+    for (int a = 0; a < DIM; ++a) {
+      sum[a] *= f;   // below 2^22: exact as floats
+      lo[a] = hi[a] = (float)sum[a];
+    }
+    cent_all[(int64_t)c0 + c] = S::fcent(sum);
     for (int m = members; m < 8; ++m) q_idx[((int64_t)c0 + c) * 8 + m] = -1;
   }
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) {
-    lx = fminf(lx, __shfl_xor(lx, o, 64));
-    ly = fminf(ly, __shfl_xor(ly, o, 64));
-    hx = fmaxf(hx, __shfl_xor(hx, o, 64));
-    hy = fmaxf(hy, __shfl_xor(hy, o, 64));
+#pragma unroll
+    for (int a = 0; a < DIM; ++a) {
+      lo[a] = fminf(lo[a], __shfl_xor(lo[a], o, 64));
+      hi[a] = fmaxf(hi[a], __shfl_xor(hi[a], o, 64));
+    }
   }
-  if (threadIdx.x == 0) box_all[(int64_t)b * gridDim.x + t] = make_float4(lx, ly, hx, hy);
+  if (threadIdx.x == 0) {
+    int il[DIM], ih[DIM];   // the floats hold integers: the conversion is exact
+#pragma unroll
+    for (int a = 0; a < DIM; ++a) {
+      il[a] = (int)lo[a];
+      ih[a] = (int)hi[a];
+    }
+    const int64_t at = ((int64_t)b * gridDim.x + t) * 2;
+    if (nc > t * kBoxTile) {
+      box_all[at] = S::fcent(il);
+      box_all[at + 1] = S::fcent(ih);
+    }
+  }
 }
 
 template <int KM1>
@@ -212,38 +336,55 @@ __device__ __forceinline__ void top_insert(uint64_t (&best)[KM1 > 0 ? KM1 : 1], 
 
 // Scan one tile of candidate centroids (staged in this wave's LDS row) for
 // the lanes with `need`, keeping the KM1 smallest (d2 << kIdxBits | index)
-// keys (scaled sums below 2^22: d2 < 2^45, so a key fits 64 bits).
-// Candidates are screened with an fp32 distance whose error bound (relative
-// 2^-23) cannot drop a candidate at or below the current KM1-th best; the
-// survivors are compared exactly in 64 bits, so the kept set does not depend
-// on the order of the scan.
-template <int KM1>
-__device__ __forceinline__ void scan_tile(const float2* __restrict__ cent, float2* __restrict__ row,
-                                          int t0, int T, int c, float2 me, bool need,
+// keys (scaled sums below 2^22: d2 < 2^46 even in 3D, so a key fits 64
+// bits).  Candidates are screened with an fp32 distance whose error bound
+// (relative 2^-22) cannot drop a candidate at or below the current KM1-th
+// best; the survivors are compared exactly in 64 bits, so the kept set does
+// not depend on the order of the scan.
+template <int KM1, int DIM>
+__device__ __forceinline__ void scan_tile(const typename Space<DIM>::FCent* __restrict__ cent,
+                                          typename Space<DIM>::FCent* __restrict__ row, int t0,
+                                          int T, int c, const float (&me)[DIM], bool need,
                                           uint64_t (&best)[KM1 > 0 ? KM1 : 1], float& thr) {
+  typedef typename Space<DIM>::FCent FC;
   const int lane = threadIdx.x & 63;
-  const float2 mine = lane < T ? cent[t0 + lane] : make_float2(0.f, 0.f);
+  FC mine;
+  if (lane < T) mine = cent[t0 + lane];
+  else mine = FC{};
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // earlier reads of the row are done
   row[lane] = mine;
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // the row is written (one wave)
   if (!need) return;
-  const float4* row4 = reinterpret_cast<const float4*>(row);
   for (int i0 = 0; i0 < T; i0 += 8) {
-    float2 cc[8];
+    float cc[8][DIM];
+    if constexpr (DIM == 2) {
+      const float4* row4 = reinterpret_cast<const float4*>(row);
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const float4 q = row4[(i0 >> 1) + u];
-      cc[2 * u] = make_float2(q.x, q.y);
-      cc[2 * u + 1] = make_float2(q.z, q.w);
+      for (int u = 0; u < 4; ++u) {
+        const float4 q = row4[(i0 >> 1) + u];
+        cc[2 * u][0] = q.x;
+        cc[2 * u][1] = q.y;
+        cc[2 * u + 1][0] = q.z;
+        cc[2 * u + 1][1] = q.w;
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u < 8; ++u) get(row[i0 + u], cc[u]);
     }
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       const int e = i0 + u;
-      const float dx = cc[u].x - me.x, dy = cc[u].y - me.y;   // exact
-      const float d2f = fmaf(dx, dx, dy * dy);
+      float d[DIM];
+#pragma unroll
+      for (int a = 0; a < DIM; ++a) d[a] = cc[u][a] - me[a];   // exact
+      float d2f = d[0] * d[0];
+#pragma unroll
+      for (int a = 1; a < DIM; ++a) d2f = fmaf(d[a], d[a], d2f);
       if (e >= T || d2f > thr || t0 + e == c) continue;
-      const int ix = (int)dx, iy = (int)dy;
-      const uint64_t key = ((uint64_t)((int64_t)ix * ix + (int64_t)iy * iy) << kIdxBits) | (uint32_t)(t0 + e);
+      int64_t d2 = 0;
+#pragma unroll
+      for (int a = 0; a < DIM; ++a) d2 += (int64_t)(int)d[a] * (int)d[a];
+      const uint64_t key = ((uint64_t)d2 << kIdxBits) | (uint32_t)(t0 + e);
       if (key >= best[KM1 - 1]) continue;
       uint64_t x = key;
 #pragma unroll
@@ -269,6 +410,19 @@ __device__ __forceinline__ float wave_maxf(float x) {
   return x;
 }
 
+// squared distance from point p to the box [lo, hi] (exact for integer floats)
+template <int DIM>
+__device__ __forceinline__ float box_d2(const float (&lo)[DIM], const float (&hi)[DIM],
+                                        const float (&plo)[DIM], const float (&phi)[DIM]) {
+  float s = 0.f;
+#pragma unroll
+  for (int a = 0; a < DIM; ++a) {
+    const float d = fmaxf(fmaxf(lo[a] - phi[a], plo[a] - hi[a]), 0.f);
+    s = fmaf(d, d, s);
+  }
+  return s;
+}
+
 // Nearest clusters and key lists.  grid = (ceil(C / kBoxTile), B); the
 // kSelWaves wavefronts of a workgroup serve the same tile of clusters, one
 // lane per cluster.  Every wave scans the own tile (which sets each lane's
@@ -279,13 +433,15 @@ __device__ __forceinline__ float wave_maxf(float x) {
 // the tile's box.  The waves' lists are merged at the end.
 constexpr int kSelWaves = 4;
 
-template <int KM1>
+template <int KM1, int DIM>
 __global__ void __launch_bounds__(kBoxTile * kSelWaves)
-select_box_kernel(Geom g, const float2* __restrict__ cent_all, const float4* __restrict__ box_all,
+select_box_kernel(Geom g, const typename Space<DIM>::FCent* __restrict__ cent_all,
+                  const typename Space<DIM>::FCent* __restrict__ box_all,
                   const int32_t* __restrict__ q_idx, int32_t* __restrict__ nbr,
                   int32_t* __restrict__ key_idx) {
+  typedef typename Space<DIM>::FCent FC;
   constexpr int KB = KM1 > 0 ? KM1 : 1;
-  __shared__ __align__(16) float2 cand[kSelWaves][kBoxTile];
+  __shared__ __align__(16) FC cand[kSelWaves][kBoxTile];
   __shared__ uint64_t part[kSelWaves - 1][KB][kBoxTile];
   const int b = blockIdx.y;
   int t0, n, c0, C;
@@ -296,9 +452,15 @@ select_box_kernel(Geom g, const float2* __restrict__ cent_all, const float4* __r
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int c = own * kBoxTile + lane;
   const bool valid = c < C;
-  const float2* cent = cent_all + c0;
-  const float4* box = box_all + (int64_t)b * gridDim.x;
-  const float2 me = valid ? cent[c] : make_float2(0.f, 0.f);
+  const FC* cent = cent_all + c0;
+  const FC* box = box_all + (int64_t)b * gridDim.x * 2;
+  float me[DIM];
+  {
+    FC mc;
+    if (valid) mc = cent[c];
+    else mc = FC{};
+    get(mc, me);
+  }
 
   uint64_t best[KB];
 #pragma unroll
@@ -306,21 +468,25 @@ select_box_kernel(Geom g, const float2* __restrict__ cent_all, const float4* __r
   float thr = INFINITY;
 
   if constexpr (KM1 > 0) {
-    scan_tile<KM1>(cent, cand[w], own * kBoxTile, min(kBoxTile, C - own * kBoxTile), c, me, valid,
-                   best, thr);
+    scan_tile<KM1, DIM>(cent, cand[w], own * kBoxTile, min(kBoxTile, C - own * kBoxTile), c, me,
+                        valid, best, thr);
     // bounding box of the wave's clusters and its largest threshold
-    const float mlx = wave_minf(valid ? me.x : INFINITY), mly = wave_minf(valid ? me.y : INFINITY);
-    const float mhx = wave_maxf(valid ? me.x : -INFINITY), mhy = wave_maxf(valid ? me.y : -INFINITY);
+    float mlo[DIM], mhi[DIM];
+#pragma unroll
+    for (int a = 0; a < DIM; ++a) {
+      mlo[a] = wave_minf(valid ? me[a] : INFINITY);
+      mhi[a] = wave_maxf(valid ? me[a] : -INFINITY);
+    }
     const float mthr = wave_maxf(valid ? thr : -INFINITY);
     int dealt = 0;   // candidate tiles seen so far (all waves agree)
     for (int g0 = 0; g0 < ntiles; g0 += 64) {
       const int tl = g0 + lane;
       bool cand_tile = false;
       if (tl < ntiles && tl != own) {
-        const float4 bx = box[tl];
-        const float dx = fmaxf(fmaxf(bx.x - mhx, mlx - bx.z), 0.f);   // exact
-        const float dy = fmaxf(fmaxf(bx.y - mhy, mly - bx.w), 0.f);
-        cand_tile = fmaf(dx, dx, dy * dy) <= mthr;
+        float lo[DIM], hi[DIM];
+        get(box[2 * tl], lo);
+        get(box[2 * tl + 1], hi);
+        cand_tile = box_d2<DIM>(lo, hi, mlo, mhi) <= mthr;
       }
       uint64_t mask = __ballot(cand_tile);
       while (mask) {
@@ -328,13 +494,13 @@ select_box_kernel(Geom g, const float2* __restrict__ cent_all, const float4* __r
         mask &= mask - 1;
         if (dealt++ % kSelWaves != w) continue;
         const int tt = g0 + bit;
-        const float4 bx = box[tt];
-        const float dx = fmaxf(fmaxf(bx.x - me.x, me.x - bx.z), 0.f);   // exact
-        const float dy = fmaxf(fmaxf(bx.y - me.y, me.y - bx.w), 0.f);
-        const bool need = valid && fmaf(dx, dx, dy * dy) <= thr;
+        float lo[DIM], hi[DIM];
+        get(box[2 * tt], lo);
+        get(box[2 * tt + 1], hi);
+        const bool need = valid && box_d2<DIM>(lo, hi, me, me) <= thr;
         if (!__any(need)) continue;
-        scan_tile<KM1>(cent, cand[w], tt * kBoxTile, min(kBoxTile, C - tt * kBoxTile), c, me, need,
-                       best, thr);
+        scan_tile<KM1, DIM>(cent, cand[w], tt * kBoxTile, min(kBoxTile, C - tt * kBoxTile), c, me,
+                            need, best, thr);
       }
     }
     // merge the waves' lists into wave 0; every wave holds the own tile's
@@ -383,31 +549,40 @@ select_box_kernel(Geom g, const float2* __restrict__ cent_all, const float4* __r
 }
 
 // ---------------------------------------------------------------------------
-// Whole build for an image of at most 2048 tokens in one 1024-thread
-// workgroup, everything staged in LDS: (code, token) keys are sorted with a
-// bitonic network (one compare-exchange per thread per stage), the cluster
-// centroid sums are decoded from the sorted codes, and each cluster's
-// candidate scan is split over 4 lanes whose top lists are merged with
-// lane shuffles.  grid = B.
+// Whole build for an image of at most KPT * 1024 tokens (2048 or 4096) in
+// one 1024-thread workgroup, everything staged in LDS: (code, token) keys
+// are sorted (counting sort with in-bucket insertion, bitonic fallback),
+// the cluster centroid sums are decoded from the sorted codes, and each
+// cluster's candidate scan is split over up to 16 lanes whose top lists are
+// merged with lane shuffles.  grid = (B, parts).
 // ---------------------------------------------------------------------------
 constexpr int kSmallThreads = 1024;
 
-constexpr int kBuckets = 2 * kSmallThreads;       // counting-sort buckets (top 11 code bits)
-constexpr int kBucketShift = 21;
+constexpr int kBuckets = 2 * kSmallThreads;       // counting-sort buckets (top 11 key bits)
+constexpr int kBucketShift = 53;
 constexpr int kMaxBucket = 32;                    // larger buckets -> bitonic fallback
 
+__device__ __forceinline__ int64_t sq_dist(int2 a, int2 b) {
+  const int dx = a.x - b.x, dy = a.y - b.y;
+  return (int64_t)dx * dx + (int64_t)dy * dy;
+}
+__device__ __forceinline__ int64_t sq_dist(int4 a, int4 b) {
+  const int dx = a.x - b.x, dy = a.y - b.y, dz = a.z - b.z;
+  return (int64_t)dx * dx + (int64_t)dy * dy + (int64_t)dz * dz;
+}
 
-// KPT keys per thread: images of up to KPT * 1024 tokens (2048 or 4096).
-template <int KM1, int KPT>
+template <int KM1, int KPT, int DIM>
 __global__ void __launch_bounds__(kSmallThreads)
 build_small_kernel(const float* __restrict__ coords, Geom g, double step, int parts, int lanes,
                    int32_t* __restrict__ q_idx, int32_t* __restrict__ nbr,
                    int32_t* __restrict__ key_idx) {
+  typedef Space<DIM> S;
+  typedef typename S::ICent IC;
   constexpr int kMaxN = KPT * kSmallThreads;
   __shared__ uint64_t keys[kMaxN];
   __shared__ int bcnt[kBuckets];
   __shared__ int bstart[kBuckets];
-  __shared__ int2 cent[kMaxN / 8];
+  __shared__ IC cent[kMaxN / 8];
   __shared__ int scan_tmp[17];
   __shared__ int overflow;
   const int b = blockIdx.x;
@@ -416,14 +591,14 @@ build_small_kernel(const float* __restrict__ coords, Geom g, double step, int pa
   g.image(b, t0, N, cl0, C);
   if (N > kMaxN || N == 0) return;   // larger images: segment / merge path
   const int tb = g.tok_base(t0), cb = g.clu_base(cl0);
-  const float2* xy = reinterpret_cast<const float2*>(coords) + (int64_t)t0;
+  const float* img = coords + (int64_t)t0 * DIM;
 
-  // Sort the (code << 32 | token) keys.  Counting sort on the top 11 code
-  // bits (2048 buckets; KPT keys per thread), then an insertion sort inside
-  // each bucket restores the exact (code, token) order whatever the arrival
-  // order of the atomics.  Buckets hold about one key for the grid-like
-  // layouts of the workloads; if any bucket exceeds kMaxBucket keys the
-  // workgroup falls back to an LDS bitonic sort.
+  // Sort the (code << kTokBits | token) keys.  Counting sort on the top 11
+  // key bits (2048 buckets; KPT keys per thread), then an insertion sort
+  // inside each bucket restores the exact (code, token) order whatever the
+  // arrival order of the atomics.  Buckets hold about one key for the
+  // grid-like layouts of the workloads; if any bucket exceeds kMaxBucket
+  // keys the workgroup falls back to an LDS bitonic sort.
   uint64_t kk[KPT];
   int bk[KPT], arr[KPT];
 #pragma unroll
@@ -432,10 +607,8 @@ build_small_kernel(const float* __restrict__ coords, Geom g, double step, int pa
     kk[r] = ~0ull;
     bk[r] = -1;
     if (e < N) {
-      const float2 c = xy[e];
-      const uint32_t code = spread16(quantize_axis(c.x, step)) | (spread16(quantize_axis(c.y, step)) << 1);
-      kk[r] = ((uint64_t)code << 32) | (uint32_t)e;
-      bk[r] = (int)(code >> kBucketShift);
+      kk[r] = (S::code(img, e, step) << S::kTokBits) | (uint32_t)e;
+      bk[r] = (int)(kk[r] >> kBucketShift);
     }
   }
   bcnt[tid] = 0;
@@ -498,19 +671,23 @@ build_small_kernel(const float* __restrict__ coords, Geom g, double step, int pa
   // centroid sums decoded from the sorted codes, scaled to compare means
   for (int c = tid; c < C; c += kSmallThreads) {
     const int members = min(8, N - 8 * c);
-    int sx = 0, sy = 0;
+    int sum[DIM] = {};
     for (int m = 0; m < members; ++m) {
-      const uint32_t code = (uint32_t)(keys[8 * c + m] >> 32);
-      sx += (int)compact16(code);
-      sy += (int)compact16(code >> 1);
+      int q[DIM];
+      S::axes(keys[8 * c + m] >> S::kTokBits, q);
+#pragma unroll
+      for (int a = 0; a < DIM; ++a) sum[a] += q[a];
     }
     const int f = mean_scale(members, N);
-    cent[c] = make_int2(sx * f, sy * f);
+#pragma unroll
+    for (int a = 0; a < DIM; ++a) sum[a] *= f;
+    cent[c] = S::icent(sum);
   }
+  const uint64_t tmask = tok_mask<DIM>();
   if (blockIdx.y == 0) {   // q_idx rows: token ids, -1 past the end of the order
     int32_t* qimg = q_idx + (int64_t)cl0 * 8;
     for (int e = tid; e < 8 * C; e += kSmallThreads)
-      qimg[e] = e < N ? tb + (int32_t)(uint32_t)keys[e] : -1;
+      qimg[e] = e < N ? tb + (int32_t)(keys[e] & tmask) : -1;
   }
   __syncthreads();
 
@@ -519,11 +696,11 @@ build_small_kernel(const float* __restrict__ coords, Geom g, double step, int pa
   // <= 16) share a cluster: lane q scans the candidates at Morton offsets
   // +1, -1, +2, -2, ... (mod C) numbered q, q + lanes, ..., so the nearest
   // in Morton order come first.  Keys are exact (d2 << kIdxBits | index)
-  // in 64 bits from integer scaled centroid sums (below 2^22: d2 < 2^45),
-  // and a candidate is inserted
-  // only when it beats the lane's current k-1-th best, which after the
-  // first few near candidates is rare (the wavefront stays off the
-  // divergent insertion path).  The kept set does not depend on the order.
+  // in 64 bits from integer scaled centroid sums (below 2^22), and a
+  // candidate is inserted only when it beats the lane's current k-1-th
+  // best, which after the first few near candidates is rare (the wavefront
+  // stays off the divergent insertion path).  The kept set does not depend
+  // on the order.
   constexpr int KB = KM1 > 0 ? KM1 : 1;
   const int CP = (C + parts - 1) / parts;
   const int q = tid & (lanes - 1);
@@ -535,7 +712,7 @@ build_small_kernel(const float* __restrict__ coords, Geom g, double step, int pa
   for (int r = 0; r < KB; ++r) best[r] = ~0ull;
   if constexpr (KM1 > 0) {
     if (mine) {
-      const int2 me = cent[c];
+      const IC me = cent[c];
       constexpr int U = 4;   // candidates read per iteration (independent LDS loads)
       for (int s0 = q; s0 < C; s0 += U * lanes) {
         uint64_t key[U];
@@ -545,9 +722,8 @@ build_small_kernel(const float* __restrict__ coords, Geom g, double step, int pa
           const int o = (sn + 1) >> 1;                    // Morton offset magnitude
           int e = (sn & 1) ? c + o : c - o;
           e = e >= C ? e - C : (e < 0 ? e + C : e);
-          const int2 cc = cent[(sn > 0 && sn < C) ? e : c];
-          const int dx = cc.x - me.x, dy = cc.y - me.y;
-          const int64_t d2 = (int64_t)dx * dx + (int64_t)dy * dy;
+          const IC cc = cent[(sn > 0 && sn < C) ? e : c];
+          const int64_t d2 = sq_dist(cc, me);
           // sn == 0 is the cluster itself; sn >= C is past the end
           key[u] = (sn > 0 && sn < C) ? ((uint64_t)d2 << kIdxBits) | (uint32_t)e : ~0ull;
         }
@@ -591,7 +767,7 @@ build_small_kernel(const float* __restrict__ coords, Geom g, double step, int pa
   }
   // the lanes of the cluster write its slot groups round-robin
   int4* krow = reinterpret_cast<int4*>(key_idx + ((int64_t)cl0 + c) * K * 8);
-  auto tok = [&](int e) { return e < N ? tb + (int)(uint32_t)keys[e] : -1; };
+  auto tok = [&](int e) { return e < N ? tb + (int)(keys[e] & tmask) : -1; };
 #pragma unroll
   for (int s = 0; s < K; ++s) {
     if ((s & (lanes - 1)) != q) continue;
@@ -606,14 +782,15 @@ build_small_kernel(const float* __restrict__ coords, Geom g, double step, int pa
   }
 }
 
-}  // namespace
-
-hipError_t launch_build_neighbors(const float* coords, const Geom& geom, int B, int64_t T, int64_t Ct,
-                                  int grid_side, int k, int32_t* q_idx, int32_t* nbr,
-                                  int32_t* key_idx, void* ws, hipStream_t st) {
-  int bits = 0;   // ceil(log2(grid_side)); grid_side is validated to [1, 65536]
+template <int DIM>
+hipError_t build_t(const float* coords, const Geom& geom, int B, int64_t T, int64_t Ct,
+                   int grid_side, int k, int32_t* q_idx, int32_t* nbr, int32_t* key_idx,
+                   void* ws, hipStream_t st) {
+  typedef Space<DIM> S;
+  int bits = 0;   // ceil(log2(grid_side)); grid_side is validated
   while ((1 << bits) < grid_side) ++bits;
-  const double step = (double)(1u << (16 - bits));
+  const int qbits = DIM == 2 ? 16 : 14;
+  const double step = (double)(1u << (qbits - bits));
   Geom g = geom;
   const int N = g.N, C = g.C;   // sizes of the (largest) image
   // 2048 keys per workgroup suffice up to 2048 tokens; 4096 up to kSmallBuild
@@ -631,14 +808,14 @@ hipError_t launch_build_neighbors(const float* coords, const Geom& geom, int B, 
     while (lanes > 1 && lanes * cp > kSmallThreads) lanes >>= 1;
     const bool wide = g.small_max > 2 * kSmallThreads;
     switch (k) {
-#define CA_SMALL(KK)                                                                            \
-  case KK:                                                                                      \
-    if (wide)                                                                                   \
-      hipLaunchKernelGGL((build_small_kernel<KK - 1, 4>), dim3(B, parts), dim3(kSmallThreads), 0, \
-                         st, coords, g, step, parts, lanes, q_idx, nbr, key_idx);               \
-    else                                                                                        \
-      hipLaunchKernelGGL((build_small_kernel<KK - 1, 2>), dim3(B, parts), dim3(kSmallThreads), 0, \
-                         st, coords, g, step, parts, lanes, q_idx, nbr, key_idx);               \
+#define CA_SMALL(KK)                                                                               \
+  case KK:                                                                                         \
+    if (wide)                                                                                      \
+      hipLaunchKernelGGL((build_small_kernel<KK - 1, 4, DIM>), dim3(B, parts), dim3(kSmallThreads), \
+                         0, st, coords, g, step, parts, lanes, q_idx, nbr, key_idx);               \
+    else                                                                                           \
+      hipLaunchKernelGGL((build_small_kernel<KK - 1, 2, DIM>), dim3(B, parts), dim3(kSmallThreads), \
+                         0, st, coords, g, step, parts, lanes, q_idx, nbr, key_idx);               \
     break;
       CA_SMALL(1) CA_SMALL(2) CA_SMALL(3) CA_SMALL(4) CA_SMALL(5) CA_SMALL(6) CA_SMALL(7) CA_SMALL(8)
 #undef CA_SMALL
@@ -648,27 +825,29 @@ hipError_t launch_build_neighbors(const float* coords, const Geom& geom, int B, 
     if (N <= g.small_max) return hipGetLastError();
   }
   // larger images: segment ranks, merge rounds, centroids and boxes, selection
+  typedef typename S::Packed P;
+  typedef typename S::FCent FC;
   const int segs = (N + kRankSeg - 1) / kRankSeg;
-  hipLaunchKernelGGL(rank_kernel, dim3(kRankSeg / 64, B * segs), dim3(kRankThreads), 0, st,
+  hipLaunchKernelGGL(rank_kernel<DIM>, dim3(kRankSeg / 64, B * segs), dim3(kRankThreads), 0, st,
                      coords, g, segs, step, w.keys[0]);
   int cur = 0;
   const dim3 mgrid((N + kRankThreads - 1) / kRankThreads, B);
   for (int run = kRankSeg; run < N; run *= 2) {
     const bool last = 2 * run >= N;
-    hipLaunchKernelGGL(merge_round_kernel, mgrid, dim3(kRankThreads), 0, st, g, run,
+    hipLaunchKernelGGL(merge_round_kernel<DIM>, mgrid, dim3(kRankThreads), 0, st, g, run,
                        (const uint64_t*)w.keys[cur], last ? nullptr : w.keys[cur ^ 1], q_idx,
-                       w.qsorted);
+                       (P*)w.qsorted);
     cur ^= 1;
   }
   const dim3 tgrid((C + kBoxTile - 1) / kBoxTile, B);
-  hipLaunchKernelGGL(centroid_box_kernel, tgrid, dim3(kBoxTile), 0, st, g,
-                     (const uint32_t*)w.qsorted, w.cent, w.box, q_idx);
+  hipLaunchKernelGGL(centroid_box_kernel<DIM>, tgrid, dim3(kBoxTile), 0, st, g,
+                     (const P*)w.qsorted, (FC*)w.cent, (FC*)w.box, q_idx);
   switch (k) {
-#define CA_SEL(KK)                                                                              \
-  case KK:                                                                                      \
-    hipLaunchKernelGGL(select_box_kernel<KK - 1>, tgrid, dim3(kBoxTile * kSelWaves), 0, st, g,  \
-                       (const float2*)w.cent, (const float4*)w.box, (const int32_t*)q_idx, nbr, \
-                       key_idx);                                                                \
+#define CA_SEL(KK)                                                                                 \
+  case KK:                                                                                         \
+    hipLaunchKernelGGL((select_box_kernel<KK - 1, DIM>), tgrid, dim3(kBoxTile * kSelWaves), 0, st, \
+                       g, (const FC*)w.cent, (const FC*)w.box, (const int32_t*)q_idx, nbr,         \
+                       key_idx);                                                                   \
     break;
     CA_SEL(1) CA_SEL(2) CA_SEL(3) CA_SEL(4) CA_SEL(5) CA_SEL(6) CA_SEL(7) CA_SEL(8)
 #undef CA_SEL
@@ -676,6 +855,18 @@ hipError_t launch_build_neighbors(const float* coords, const Geom& geom, int B, 
       return hipErrorInvalidValue;
   }
   return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_build_neighbors(const float* coords, const Geom& g, int dims, int B, int64_t T,
+                                  int64_t Ct, int grid_side, int k, int32_t* q_idx, int32_t* nbr,
+                                  int32_t* key_idx, void* ws, hipStream_t st) {
+  if (dims == 2)
+    return build_t<2>(coords, g, B, T, Ct, grid_side, k, q_idx, nbr, key_idx, ws, st);
+  if (dims == 3)
+    return build_t<3>(coords, g, B, T, Ct, grid_side, k, q_idx, nbr, key_idx, ws, st);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace ca

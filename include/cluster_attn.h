@@ -113,6 +113,26 @@ int cluster_attn_build_neighbors(const float* coords, int B, int N, int grid_sid
                                  size_t ws_bytes, void* hip_stream);
 
 /*
+ * 3D tokens (notes page, "Limitations & Future Work": scaling to 3D voxels
+ * is named as open; this is the library's reading).  The same steps as
+ * cluster_attn_build_neighbors with three axes:
+ *   1. q = clamp(floor((c + 0.5) * 2^(14 - ceil(log2 G))), 0, 16383) per
+ *      axis (14 bits); Morton code with x, y, z in bits 3b, 3b+1, 3b+2
+ *      (42 bits).
+ *   2.-5. as in 2D (stable sort by (code, token), runs of cs, centroids as
+ *      scaled means over three axes, k-1 nearest by (squared distance,
+ *      index), key lists).
+ *   coords    [B, N, 3] f32, (x = column, y = row, z = slice) in patch units.
+ *   grid_side G in [1, 16384], the largest side of the patch grid.
+ * Outputs, workspace (cluster_attn_build_neighbors_workspace) and errors as
+ * for cluster_attn_build_neighbors.  The lists feed the same cluster_attn_fwd
+ * / cluster_attn_bwd (the attention does not depend on the dimension).
+ */
+int cluster_attn_build_neighbors_3d(const float* coords, int B, int N, int grid_side, int cs,
+                                    int k, int32_t* perm, int32_t* nbr, int32_t* key_idx,
+                                    void* ws, size_t ws_bytes, void* hip_stream);
+
+/*
  * Packed batch of images of different sizes (ragged geometry).  Image b holds
  * tokens [tok_off[b], tok_off[b+1]) of the packed arrays and clusters
  * [clu_off[b], clu_off[b+1]), with clu_off[b+1] - clu_off[b] =
@@ -138,6 +158,13 @@ int cluster_attn_build_neighbors_varlen(const float* coords, int B, int T, int C
                                         int grid_side, int cs, int k, int32_t* q_idx,
                                         int32_t* nbr, int32_t* key_idx, void* ws,
                                         size_t ws_bytes, void* hip_stream);
+/* The same for packed 3D volumes: coords [T, 3] f32 (readings of
+ * cluster_attn_build_neighbors_3d); same workspace query. */
+int cluster_attn_build_neighbors_varlen_3d(const float* coords, int B, int T, int Ct, int max_n,
+                                           const int32_t* tok_off, const int32_t* clu_off,
+                                           int grid_side, int cs, int k, int32_t* q_idx,
+                                           int32_t* nbr, int32_t* key_idx, void* ws,
+                                           size_t ws_bytes, void* hip_stream);
 
 /*
  * Forward (notes page "Overall Architecture": local cluster attention; arXiv

@@ -162,6 +162,24 @@ def test_varlen_validation(lib):
                                        None) == CA_ERR_WORKSPACE
 
 
+def test_3d_build_validation(lib):
+    def build(B=2, N=64, G=32, k=6, ptrs=None, ws_bytes=1 << 30, ws=P * 9):
+        p = ptrs or [P, 2 * P, 3 * P, 4 * P]
+        return lib.cluster_attn_build_neighbors_3d(p[0], B, N, G, 8, k, p[1], p[2], p[3], ws,
+                                                   ws_bytes, None)
+    assert build(G=16385) == CA_ERR_SHAPE            # 14-bit axes: G up to 2^14
+    assert build(G=0) == CA_ERR_SHAPE
+    assert build(k=9) == CA_ERR_UNSUPPORTED
+    assert build(N=8192, ws_bytes=16) == CA_ERR_WORKSPACE
+    assert build(ptrs=[P, None, 3 * P, 4 * P]) == CA_ERR_NULL
+    assert build(ptrs=[P + 8, 2 * P, 3 * P, 4 * P], N=(P // 12)) == CA_ERR_ALIAS   # 12 B per token
+    assert build(B=0, ptrs=[None] * 4, ws=None) == CA_OK
+    p6 = [P, 2 * P, 3 * P, 4 * P, 5 * P, 6 * P]
+    assert lib.cluster_attn_build_neighbors_varlen_3d(p6[0], 3, 100, 12, 50, p6[1], p6[2], 16, 8, 6,
+                                                      p6[3], p6[4], p6[5], P * 9, 1 << 20,
+                                                      None) == CA_ERR_SHAPE
+
+
 def test_missing_library_raises(tmp_path):
     with pytest.raises(_lib.LibraryMissing):
         _lib.load(str(tmp_path / "nope.so"))
