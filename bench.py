@@ -12,6 +12,11 @@ last-level cache, so no step reads data a recent step left in cache (the
 
 Prints one JSON line.  Usage:
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config stage1]
+
+Other configurations (parity-test workloads of the wider rows, measured the
+same way): stage2, stage3, stage4, highres, stress (2D attention), varlen
+(packed images), volume, volume_hr (3D tokens), knn_decoder (KNN-cache
+sampler), merge_stages (token merging).
 """
 
 from __future__ import annotations
@@ -95,7 +100,8 @@ def cpu_baseline(cfg, case, images: int):
     import oracle as O
 
     sub = slice(0, images)
-    perm, _, key_idx = O.build_neighbors(case["coords"][sub], cfg.G)
+    build = O.build_neighbors_3d if case["coords"].shape[-1] == 3 else O.build_neighbors
+    perm, _, key_idx = build(case["coords"][sub], cfg.G)
     q_idx = perm.reshape(images, cfg.C, cfg.cs)
     args = [case[n][sub] for n in ("q", "k", "v", "do")]
     scale = 1.0 / math.sqrt(cfg.D)
@@ -157,7 +163,8 @@ def main():
     import torch
 
     import gathered_local_attention_amd as ca
-    from gen import MERGE_CONFIGS, RAGGED_CONFIGS, SAMPLER_CONFIGS, make_case
+    from gen import (MERGE_CONFIGS, RAGGED_CONFIGS, SAMPLER_CONFIGS, VOLUME_CONFIGS, make_case,
+                     make_volume_case)
 
     ca._lib.load()
     if args.config in RAGGED_CONFIGS:
@@ -169,7 +176,7 @@ def main():
     if args.config in MERGE_CONFIGS:
         bench_merge(args, torch, ca)
         return
-    case = make_case(args.config)
+    case = make_volume_case(args.config) if args.config in VOLUME_CONFIGS else make_case(args.config)
     cfg = case["cfg"]
     scale = 1.0 / math.sqrt(cfg.D)
     dev = "cuda"
@@ -268,9 +275,10 @@ def main():
         "dtype": {"f32": "f32", "bf16": "bf16", "f16": "f16"}[cfg.dtype],
         "data": "synthetic",
         "config": {
-            "workload": f"{cfg.name}: B={cfg.B} images x N={cfg.N} tokens, H={cfg.H}x{cfg.D}, "
-                        f"clusters of {cfg.cs} ({cfg.C} per image), {cfg.nk} key slots, "
-                        f"{cfg.dtype}; step = neighbour build + forward + backward",
+            "workload": f"{cfg.name}: B={cfg.B} {'volumes' if case['coords'].shape[-1] == 3 else 'images'}"
+                        f" x N={cfg.N} tokens ({case['coords'].shape[-1]}D coordinates), "
+                        f"H={cfg.H}x{cfg.D}, clusters of {cfg.cs} ({cfg.C} per image), {cfg.nk} key "
+                        f"slots, {cfg.dtype}; step = neighbour build + forward + backward",
             "B": cfg.B, "N": cfg.N, "H": cfg.H, "D": cfg.D, "cs": cfg.cs, "nk": cfg.nk,
             "geometry": cfg.geometry, "seed": cfg.seed, "rotating_copies": args.copies,
         },

@@ -54,6 +54,14 @@ class VolumeConfig:
     def nk(self) -> int:
         return self.cs * self.k
 
+    @property
+    def C(self) -> int:
+        return -(-self.N // self.cs)
+
+    @property
+    def tokens(self) -> int:
+        return self.B * self.N
+
     def with_batch(self, B: int) -> "VolumeConfig":
         return replace(self, B=B)
 
