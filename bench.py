@@ -36,11 +36,11 @@ HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, vendor figure
 # kernels behind each entry point on the bf16/f16 path (the roofline is per
 # entry point; the committed kernel trace splits it per kernel)
 ENTRY_KERNELS = {
-    "build": ["build_small_kernel (N <= 2048) | rank_kernel, merge_round_kernel, "
-              "centroid_box_kernel, select_box_kernel (N > 2048)"],
+    "build": ["build_small_kernel (N <= 4096) | rank_kernel, merge_round_kernel, "
+              "centroid_box_kernel, select_box_kernel (N > 4096)"],
+    "plan": ["plan_small_kernel (images <= 2048 tokens) | plan_init/inv/count/scan/place/sort_kernel"],
     "fwd": ["fwd_lds_kernel"],
-    "bwd": ["plan_small_kernel (small images) | plan_init/inv/count/scan/place/sort_kernel",
-            "bwd_q_lds_kernel", "bwd_kv_lds_kernel"],
+    "bwd": ["bwd_q_lds_kernel", "bwd_kv_lds_kernel"],
 }
 MERGE_ENTRY_KERNELS = {"plan": ["merge_plan_kernel"], "fwd": ["merge_fwd_kernel"],
                        "bwd": ["merge_bwd_kernel"]}
@@ -69,6 +69,9 @@ def algorithmic_tc(T, C, H, D, nk, k, cs, dtype):
     idx = C * cs * 4 + C * nk * 4       # q_idx + key_idx
     return {
         "build": {"bytes": T * 8 + C * cs * 4 + C * k * 4 + C * nk * 4, "flops": 0},
+        # lists in; per key cluster one entry per referencing cluster out
+        # (counted at one per list slot group: 48 B of entry, tokens, mults)
+        "plan": {"bytes": idx + C * (nk // cs) * 48, "flops": 0},
         "fwd": {"bytes": 3 * t + t + lse + idx, "flops": T * H * 4 * nk * D},
         "bwd": {"bytes": 5 * t + lse + 3 * t + idx, "flops": T * H * 10 * nk * D},
     }
@@ -193,11 +196,15 @@ def main():
     gws = torch.empty(ca.bwd_workspace_bytes(case["q"].dtype, cfg.B, cfg.N, cfg.H, cfg.D,
                                              cfg.cs, cfg.nk), dtype=torch.uint8, device=dev)
 
+    # A step runs the lists' whole life once: neighbour build, the
+    # backward's transposed lists (plan), forward, backward on that plan.
+    # In a model the build and the plan serve every layer of a stage.
     def step(s):
         perm, nbr, key = ca.build_neighbors(s["coords"], cfg.G, cfg.cs, cfg.k, workspace=bws)
+        plan = ca.bwd_plan(perm, key, cfg.N)
         o, lse = ca.fwd(s["q"], s["k"], s["v"], perm, key, scale)
         dq, dk, dv = ca.bwd(s["q"], s["k"], s["v"], o, s["do"], lse, perm, key, scale,
-                            workspace=gws)
+                            workspace=gws, plan=plan)
         return dq
 
     for i in range(args.warmup):
@@ -221,15 +228,20 @@ def main():
     for s in sets:
         perm, nbr, key = ca.build_neighbors(s["coords"], cfg.G, cfg.cs, cfg.k, workspace=bws)
         o, lse = ca.fwd(s["q"], s["k"], s["v"], perm, key, scale)
-        outs.append((perm, key, o, lse))
+        outs.append((perm, key, o, lse, ca.bwd_plan(perm, key, cfg.N)))
     calls = {
         "build": lambda i: ca.build_neighbors(sets[i]["coords"], cfg.G, cfg.cs, cfg.k,
                                               workspace=bws),
+        "plan": lambda i: ca.bwd_plan(outs[i][0], outs[i][1], cfg.N),
         "fwd": lambda i: ca.fwd(sets[i]["q"], sets[i]["k"], sets[i]["v"], outs[i][0],
                                 outs[i][1], scale),
         "bwd": lambda i: ca.bwd(sets[i]["q"], sets[i]["k"], sets[i]["v"], outs[i][2],
                                 sets[i]["do"], outs[i][3], outs[i][0], outs[i][1], scale,
-                                workspace=gws),
+                                workspace=gws, plan=outs[i][4]),
+        # the self-planning backward (plan + passes in one call), for reference
+        "bwd_with_plan": lambda i: ca.bwd(sets[i]["q"], sets[i]["k"], sets[i]["v"], outs[i][2],
+                                          sets[i]["do"], outs[i][3], outs[i][0], outs[i][1],
+                                          scale, workspace=gws),
     }
     dur = {}
     for name, call in calls.items():
@@ -252,7 +264,7 @@ def main():
     warm_ms = (time.perf_counter() - t0) * 1e3 / args.steps
 
     alg = algorithmic(cfg)
-    dom = max(("build", "fwd", "bwd"), key=lambda k: dur[k])
+    dom = max(("build", "plan", "fwd", "bwd"), key=lambda k: dur[k])
     achieved = alg[dom]["bytes"] / (dur[dom] * 1e-6) / 1e9
     fb_us = dur["fwd"] + dur["bwd"]
     fb_bytes = alg["fwd"]["bytes"] + alg["bwd"]["bytes"]
@@ -278,13 +290,15 @@ def main():
             "workload": f"{cfg.name}: B={cfg.B} {'volumes' if case['coords'].shape[-1] == 3 else 'images'}"
                         f" x N={cfg.N} tokens ({case['coords'].shape[-1]}D coordinates), "
                         f"H={cfg.H}x{cfg.D}, clusters of {cfg.cs} ({cfg.C} per image), {cfg.nk} key "
-                        f"slots, {cfg.dtype}; step = neighbour build + forward + backward",
+                        f"slots, {cfg.dtype}; step = neighbour build + backward plan + forward + "
+                        "backward",
             "B": cfg.B, "N": cfg.N, "H": cfg.H, "D": cfg.D, "cs": cfg.cs, "nk": cfg.nk,
             "geometry": cfg.geometry, "seed": cfg.seed, "rotating_copies": args.copies,
         },
         "roofline": {
             "bound": "hbm",
-            "kernel": f"cluster_attn_{dom}" if dom != "build" else "cluster_attn_build_neighbors",
+            "kernel": {"build": "cluster_attn_build_neighbors", "plan": "cluster_attn_bwd_plan",
+                       "fwd": "cluster_attn_fwd", "bwd": "cluster_attn_bwd_planned"}[dom],
             "entry_point_kernels": ENTRY_KERNELS[dom],
             "achieved": achieved,
             "peak": HBM_PEAK_GBPS,
@@ -295,6 +309,9 @@ def main():
             "avg_us": dur[dom],
         },
         "fwd_bwd": {
+            "note": "forward + backward on built lists and plan (both depend on the coordinates "
+                    "only and serve every layer of a stage); the self-planning backward is "
+                    "entry_us.bwd_with_plan",
             "us": fb_us,
             "tokens_per_s": cfg.tokens / (fb_us * 1e-6),
             "effective_GBps": fb_bytes / (fb_us * 1e-6) / 1e9,
@@ -377,9 +394,10 @@ def bench_varlen(args, torch, ca):
 
     def step(s):
         q_idx, _, key, _, _ = build(s)
+        plan = ca.bwd_plan(q_idx, key, T)
         o, lse = ca.fwd_varlen(s["q"], s["k"], s["v"], q_idx, key, scale)
         return ca.bwd_varlen(s["q"], s["k"], s["v"], o, s["do"], lse, q_idx, key, scale,
-                             workspace=gws)
+                             workspace=gws, plan=plan)
 
     for i in range(args.warmup):
         step(sets[i % len(sets)])
@@ -395,14 +413,18 @@ def bench_varlen(args, torch, ca):
     for s in sets:
         q_idx, _, key, _, _ = build(s)
         o, lse = ca.fwd_varlen(s["q"], s["k"], s["v"], q_idx, key, scale)
-        outs.append((q_idx, key, o, lse))
+        outs.append((q_idx, key, o, lse, ca.bwd_plan(q_idx, key, T)))
     calls = {
         "build": lambda i: build(sets[i]),
+        "plan": lambda i: ca.bwd_plan(outs[i][0], outs[i][1], T),
         "fwd": lambda i: ca.fwd_varlen(sets[i]["q"], sets[i]["k"], sets[i]["v"], outs[i][0],
                                        outs[i][1], scale),
         "bwd": lambda i: ca.bwd_varlen(sets[i]["q"], sets[i]["k"], sets[i]["v"], outs[i][2],
                                        sets[i]["do"], outs[i][3], outs[i][0], outs[i][1], scale,
-                                       workspace=gws),
+                                       workspace=gws, plan=outs[i][4]),
+        "bwd_with_plan": lambda i: ca.bwd_varlen(sets[i]["q"], sets[i]["k"], sets[i]["v"],
+                                                 outs[i][2], sets[i]["do"], outs[i][3], outs[i][0],
+                                                 outs[i][1], scale, workspace=gws),
     }
     dur = {}
     for name, call in calls.items():
@@ -417,7 +439,7 @@ def bench_varlen(args, torch, ca):
         dur[name] = e0.elapsed_time(e1) / n_ev * 1e3
 
     alg = algorithmic_tc(T, Ct, cfg.H, cfg.D, cfg.nk, cfg.k, cfg.cs, cfg.dtype)
-    dom = max(("build", "fwd", "bwd"), key=lambda k: dur[k])
+    dom = max(("build", "plan", "fwd", "bwd"), key=lambda k: dur[k])
     achieved = alg[dom]["bytes"] / (dur[dom] * 1e-6) / 1e9
     fb_us = dur["fwd"] + dur["bwd"]
     fb_bytes = alg["fwd"]["bytes"] + alg["bwd"]["bytes"]
@@ -439,14 +461,15 @@ def bench_varlen(args, torch, ca):
         "config": {
             "workload": f"{cfg.name}: B={cfg.B} images of {min(lengths)}..{max(lengths)} tokens "
                         f"(T={T}, {Ct} clusters), H={cfg.H}x{cfg.D}, {cfg.nk} key slots, "
-                        f"{cfg.dtype}; step = packed neighbour build + forward + backward",
+                        f"{cfg.dtype}; step = packed neighbour build + backward plan + forward + "
+                        "backward",
             "B": cfg.B, "T": T, "clusters": Ct, "H": cfg.H, "D": cfg.D, "geometry": cfg.geometry,
             "seed": cfg.seed, "rotating_copies": args.copies,
         },
         "roofline": {
             "bound": "hbm",
-            "kernel": {"build": "cluster_attn_build_neighbors_varlen", "fwd": "cluster_attn_fwd_varlen",
-                       "bwd": "cluster_attn_bwd_varlen"}[dom],
+            "kernel": {"build": "cluster_attn_build_neighbors_varlen", "plan": "cluster_attn_bwd_plan",
+                       "fwd": "cluster_attn_fwd_varlen", "bwd": "cluster_attn_bwd_planned"}[dom],
             "entry_point_kernels": ENTRY_KERNELS[dom],
             "achieved": achieved,
             "peak": HBM_PEAK_GBPS,

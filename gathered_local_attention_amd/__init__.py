@@ -10,7 +10,8 @@ Functions
 ---------
 build_neighbors(coords, grid_side, cs=8, k=6) -> (perm, nbr, key_idx)   (2D or 3D)
 fwd(q, k, v, q_idx, key_idx, scale=None) -> (o, lse)
-bwd(q, k, v, o, do, lse, q_idx, key_idx, scale=None) -> (dq, dk, dv)
+bwd(q, k, v, o, do, lse, q_idx, key_idx, scale=None, plan=None) -> (dq, dk, dv)
+bwd_plan(q_idx, key_idx, N) -> plan   (transposed lists, reusable across backward calls)
 cluster_attention(q, k, v, q_idx, key_idx, scale=None) -> o   (autograd)
 build_neighbors_varlen(coords, lengths, grid_side, cs=8, k=6)
     -> (q_idx, nbr, key_idx, tok_off, clu_off)        (packed batches)
@@ -39,6 +40,7 @@ __all__ = [
     "fwd",
     "bwd",
     "cluster_attention",
+    "bwd_plan",
     "build_neighbors_varlen",
     "fwd_varlen",
     "bwd_varlen",
@@ -156,9 +158,47 @@ def fwd(q, k, v, q_idx, key_idx, scale: float | None = None):
     return o, lse
 
 
+def bwd_plan(q_idx: torch.Tensor, key_idx: torch.Tensor, N: int) -> torch.Tensor:
+    """Transposed slot lists of the backward, built once for lists that
+    several backward calls share: q_idx [B, C, cs] (or [B, C*cs]) and
+    key_idx [B, C, nk] of B images of N tokens, or q_idx [Ct, cs] and
+    key_idx [Ct, nk] of a packed batch of N = T tokens.  Returns a uint8
+    device tensor to pass as ``plan=`` to :func:`bwd` / :func:`bwd_varlen`."""
+    lib = _lib.load()
+    if key_idx.dim() == 3:
+        B, C, nk = key_idx.shape
+        cs = q_idx.numel() // max(1, B * C) if B * C else 8
+    else:
+        B, (C, nk) = 1, key_idx.shape
+        cs = q_idx.shape[-1]
+    need = lib.cluster_attn_bwd_plan_workspace(B, int(N), C, cs, nk)
+    plan = torch.empty(max(need, 1), dtype=torch.uint8, device=key_idx.device)
+    _check(lib.cluster_attn_bwd_plan(B, int(N), C, cs, nk, _dev(q_idx, "q_idx", torch.int32),
+                                     _dev(key_idx, "key_idx", torch.int32), plan.data_ptr(),
+                                     plan.numel(), _stream(key_idx)), "cluster_attn_bwd_plan")
+    return plan
+
+
+def _bwd_planned(lib, dt, B, N, C, H, D, cs, nk, scale, q, k, v, o, do, lse, q_idx, key_idx,
+                 plan, workspace):
+    need = lib.cluster_attn_bwd_planned_workspace(dt, B, N, H, D)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+    _check(lib.cluster_attn_bwd_planned(
+        dt, B, N, C, H, D, cs, nk, scale, _dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(o, "o"),
+        _dev(do, "do"), _dev(lse, "lse", torch.float32), _dev(q_idx, "q_idx", torch.int32),
+        _dev(key_idx, "key_idx", torch.int32), _dev(plan, "plan"), plan.numel(), dq.data_ptr(),
+        dk.data_ptr(), dv.data_ptr(), workspace.data_ptr(), workspace.numel(), _stream(q)),
+        "cluster_attn_bwd_planned")
+    return dq, dk, dv
+
+
 def bwd(q, k, v, o, do, lse, q_idx, key_idx, scale: float | None = None,
-        workspace: torch.Tensor | None = None):
-    """Backward: returns dQ, dK, dV (dtype of q)."""
+        workspace: torch.Tensor | None = None, plan: torch.Tensor | None = None):
+    """Backward: returns dQ, dK, dV (dtype of q).  ``plan`` (from
+    :func:`bwd_plan` on the same lists) skips rebuilding the transposed
+    lists; the result is the same bit for bit."""
     lib = _lib.load()
     B, N, H, D, cs, nk, q_idx = _shapes(q, q_idx, key_idx)
     if q.dtype not in _DT:
@@ -168,6 +208,9 @@ def bwd(q, k, v, o, do, lse, q_idx, key_idx, scale: float | None = None,
             raise ValueError(f"{n} must match q in shape and dtype")
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
     dt = _DT[q.dtype]
+    if plan is not None:
+        return _bwd_planned(lib, dt, B, N, q_idx.shape[1], H, D, cs, nk, scale, q, k, v, o, do,
+                            lse, q_idx, key_idx, plan, workspace)
     need = lib.cluster_attn_bwd_workspace(dt, B, N, H, D, cs, nk)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
@@ -291,8 +334,9 @@ def fwd_varlen(q, k, v, q_idx, key_idx, scale: float | None = None):
 
 
 def bwd_varlen(q, k, v, o, do, lse, q_idx, key_idx, scale: float | None = None,
-               workspace: torch.Tensor | None = None):
-    """Backward of a packed batch: dQ, dK, dV [T, H, D] (dtype of q)."""
+               workspace: torch.Tensor | None = None, plan: torch.Tensor | None = None):
+    """Backward of a packed batch: dQ, dK, dV [T, H, D] (dtype of q);
+    ``plan`` as for :func:`bwd` (from ``bwd_plan(q_idx, key_idx, T)``)."""
     lib = _lib.load()
     T, H, D, Ct, cs, nk = _varlen_shapes(q, q_idx, key_idx)
     for t, n in ((k, "k"), (v, "v"), (o, "o"), (do, "do")):
@@ -300,6 +344,9 @@ def bwd_varlen(q, k, v, o, do, lse, q_idx, key_idx, scale: float | None = None,
             raise ValueError(f"{n} must match q in shape and dtype")
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
     dt = _DT[q.dtype]
+    if plan is not None:
+        return _bwd_planned(lib, dt, 1, T, Ct, H, D, cs, nk, scale, q, k, v, o, do, lse, q_idx,
+                            key_idx, plan, workspace)
     need = lib.cluster_attn_bwd_varlen_workspace(dt, T, Ct, H, D, cs, nk)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)

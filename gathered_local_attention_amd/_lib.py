@@ -40,6 +40,14 @@ SIGNATURES = {
     "cluster_attn_bwd_varlen": (
         _c_int, [_c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _f,
                  _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _c_size, _vp]),
+    "cluster_attn_bwd_plan_workspace": (_c_size, [_c_int, _c_int, _c_int, _c_int, _c_int]),
+    "cluster_attn_bwd_plan": (
+        _c_int, [_c_int, _c_int, _c_int, _c_int, _c_int, _vp, _vp, _vp, _c_size, _vp]),
+    "cluster_attn_bwd_planned_workspace": (_c_size, [_c_int, _c_int, _c_int, _c_int, _c_int]),
+    "cluster_attn_bwd_planned": (
+        _c_int, [_c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _f,
+                 _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _c_size, _vp, _vp, _vp, _vp,
+                 _c_size, _vp]),
     "cluster_attn_knn_table": (_c_int, [_vp, _c_int, _c_int, _c_int, _c_int, _vp, _vp]),
     "cluster_attn_knn_sample_fwd": (
         _c_int, [_c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _f,

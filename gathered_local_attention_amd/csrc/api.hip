@@ -264,21 +264,28 @@ int attn_fwd(int dt, int B, int N, int64_t C, int H, int D, int cs, int nk, floa
                     "fwd launch");
 }
 
+// Backward; `plan` (nullptr: built here, in `ws` behind the per-call part)
+// holds the transposed lists of a cluster_attn_bwd_plan call on the same
+// q_idx / key_idx.
 int attn_bwd(int dt, int B, int N, int64_t C, int H, int D, int cs, int nk, float scale,
              const void* q, const void* k, const void* v, const void* o, const void* dout,
-             const float* lse, const int32_t* q_idx, const int32_t* key_idx, void* dq, void* dk,
-             void* dv, void* ws, size_t ws_bytes, void* hip_stream) {
+             const float* lse, const int32_t* q_idx, const int32_t* key_idx, const void* plan,
+             size_t plan_bytes, void* dq, void* dk, void* dv, void* ws, size_t ws_bytes,
+             void* hip_stream) {
   if (!(scale == scale) || scale == INFINITY || scale == -INFINITY)
     return fail(CA_ERR_SHAPE, "scale is not finite");
   if (B == 0 || N == 0 || C == 0) return ok();
   if (!q || !k || !v || !o || !dout || !lse || !q_idx || !key_idx || !dq || !dk || !dv)
     return fail(CA_ERR_NULL, "NULL tensor pointer");
-  const ca::BwdWorkspace need = ca::bwd_layout(nullptr, B, N, H, C, nk);
-  if (!ws) return fail(CA_ERR_NULL, "NULL workspace (%zu bytes needed)", need.bytes);
-  if (ws_bytes < need.bytes)
-    return fail(CA_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need.bytes);
+  const size_t need = plan ? ca::call_layout(nullptr, B, N, H).bytes
+                           : ca::bwd_layout(nullptr, B, N, H, C, nk).bytes;
+  if (!ws) return fail(CA_ERR_NULL, "NULL workspace (%zu bytes needed)", need);
+  if (ws_bytes < need) return fail(CA_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
+  const size_t pneed = ca::plan_layout(nullptr, B, N, C, nk).bytes;
+  if (plan && plan_bytes < pneed)
+    return fail(CA_ERR_WORKSPACE, "plan %zu < %zu bytes", plan_bytes, pneed);
   const size_t tb = (size_t)B * N * H * D * elem_size(dt);
-  Range outs[] = {{dq, tb}, {dk, tb}, {dv, tb}, {ws, need.bytes}};
+  Range outs[] = {{dq, tb}, {dk, tb}, {dv, tb}, {ws, need}};
   Range ins[] = {{q, tb},
                  {k, tb},
                  {v, tb},
@@ -286,12 +293,21 @@ int attn_bwd(int dt, int B, int N, int64_t C, int H, int D, int cs, int nk, floa
                  {dout, tb},
                  {lse, (size_t)B * N * H * 4},
                  {q_idx, (size_t)(B * C * cs) * 4},
-                 {key_idx, (size_t)(B * C * nk) * 4}};
-  if (int s = check_alias(outs, 4, ins, 8)) return s;
-  const ca::BwdWorkspace w = ca::bwd_layout(ws, B, N, H, C, nk);
+                 {key_idx, (size_t)(B * C * nk) * 4},
+                 {plan, plan ? pneed : 0}};
+  if (int s = check_alias(outs, 4, ins, 9)) return s;
+  ca::BwdWorkspace w;
   hipStream_t st = (hipStream_t)hip_stream;
-  hipError_t e = ca::launch_bwd_plan(B, N, (int)C, nk, q_idx, key_idx, w, st);
-  if (e != hipSuccess) return hip_status(e, "bwd plan launch");
+  if (plan) {
+    w = ca::plan_layout(const_cast<void*>(plan), B, N, C, nk);
+    const ca::BwdWorkspace a = ca::call_layout(ws, B, N, H);
+    w.ld = a.ld;
+    w.ld_none = a.ld_none;
+  } else {
+    w = ca::bwd_layout(ws, B, N, H, C, nk);
+    hipError_t e = ca::launch_bwd_plan(B, N, (int)C, nk, q_idx, key_idx, w, st);
+    if (e != hipSuccess) return hip_status(e, "bwd plan launch");
+  }
   if (ca::mfma_supported(dt, B, N, (int)C, H, nk))
     return hip_status(ca::launch_bwd_mfma(3, dt, B, N, (int)C, H, nk, scale, q, k, v, o, dout, lse,
                                           q_idx, key_idx, dq, dk, dv, w, st),
@@ -299,6 +315,21 @@ int attn_bwd(int dt, int B, int N, int64_t C, int H, int D, int cs, int nk, floa
   return hip_status(ca::launch_bwd_valu(3, dt, B, N, (int)C, H, nk, scale, q, k, v, o, dout, lse,
                                         q_idx, key_idx, dq, dk, dv, w, st),
                     "bwd launch");
+}
+
+// (B, N, C) of a plan: C = ceil(N/cs) for equal-size images, or a packed
+// batch as one image (B = 1) of N tokens in C clusters.
+int check_plan_sizes(int B, int N, int C, int cs, int nk) {
+  if (B < 0 || N < 0 || C < 0) return fail(CA_ERR_SHAPE, "bad sizes B=%d N=%d C=%d", B, N, C);
+  if (cs != 8) return fail(CA_ERR_UNSUPPORTED, "cluster size %d (only 8 is supported)", cs);
+  if (nk % cs != 0 || nk / cs < 1 || nk / cs > 8)
+    return fail(CA_ERR_UNSUPPORTED, "nk=%d must be cs*k with 1 <= k <= 8", nk);
+  const int64_t cmin = clusters_of(N, cs);
+  const bool ok_c = C == cmin || (B == 1 && C >= cmin && C <= N);
+  if (!ok_c) return fail(CA_ERR_SHAPE, "C=%d is inconsistent with B=%d, N=%d", C, B, N);
+  if ((int64_t)B * N > (int64_t(1) << 31) - 1 || (int64_t)B * C * nk * 8 > (int64_t(1) << 31) - 1)
+    return fail(CA_ERR_SHAPE, "problem too large");
+  return CA_OK;
 }
 
 // Packed batches run as one image of T tokens and Ct clusters.
@@ -337,7 +368,7 @@ int cluster_attn_bwd(int dt, int B, int N, int H, int D, int cs, int nk, float s
                      size_t ws_bytes, void* hip_stream) {
   if (int s = check_attn_shape(dt, B, N, H, D, cs, nk)) return s;
   return attn_bwd(dt, B, N, clusters_of(N, cs), H, D, cs, nk, scale, q, k, v, o, dout, lse, q_idx,
-                  key_idx, dq, dk, dv, ws, ws_bytes, hip_stream);
+                  key_idx, nullptr, 0, dq, dk, dv, ws, ws_bytes, hip_stream);
 }
 
 int cluster_attn_fwd_varlen(int dt, int T, int Ct, int H, int D, int cs, int nk, float scale,
@@ -362,8 +393,51 @@ int cluster_attn_bwd_varlen(int dt, int T, int Ct, int H, int D, int cs, int nk,
                             const int32_t* key_idx, void* dq, void* dk, void* dv, void* ws,
                             size_t ws_bytes, void* hip_stream) {
   if (int s = check_varlen(dt, T, Ct, H, D, cs, nk)) return s;
-  return attn_bwd(dt, 1, T, Ct, H, D, cs, nk, scale, q, k, v, o, dout, lse, q_idx, key_idx, dq,
-                  dk, dv, ws, ws_bytes, hip_stream);
+  return attn_bwd(dt, 1, T, Ct, H, D, cs, nk, scale, q, k, v, o, dout, lse, q_idx, key_idx,
+                  nullptr, 0, dq, dk, dv, ws, ws_bytes, hip_stream);
+}
+
+size_t cluster_attn_bwd_plan_workspace(int B, int N, int C, int cs, int nk) {
+  const char saved = g_last_error[0];
+  if (check_plan_sizes(B, N, C, cs, nk) != CA_OK) {
+    g_last_error[0] = saved;
+    return 0;
+  }
+  return ca::plan_layout(nullptr, B, N, C, nk).bytes;
+}
+
+int cluster_attn_bwd_plan(int B, int N, int C, int cs, int nk, const int32_t* q_idx,
+                          const int32_t* key_idx, void* plan, size_t plan_bytes,
+                          void* hip_stream) {
+  if (int s = check_plan_sizes(B, N, C, cs, nk)) return s;
+  if (B == 0 || N == 0 || C == 0) return ok();
+  if (!q_idx || !key_idx || !plan) return fail(CA_ERR_NULL, "NULL pointer");
+  const size_t need = ca::plan_layout(nullptr, B, N, C, nk).bytes;
+  if (plan_bytes < need) return fail(CA_ERR_WORKSPACE, "plan %zu < %zu bytes", plan_bytes, need);
+  Range outs[] = {{plan, need}};
+  Range ins[] = {{q_idx, (size_t)B * C * cs * 4}, {key_idx, (size_t)B * C * nk * 4}};
+  if (int s = check_alias(outs, 1, ins, 2)) return s;
+  const ca::BwdWorkspace w = ca::plan_layout(plan, B, N, C, nk);
+  return hip_status(ca::launch_bwd_plan(B, N, C, nk, q_idx, key_idx, w, (hipStream_t)hip_stream),
+                    "bwd plan launch");
+}
+
+size_t cluster_attn_bwd_planned_workspace(int dt, int B, int N, int H, int D) {
+  if (dt < CA_F32 || dt > CA_F16 || B < 0 || N < 0 || H < 1 || D != 32) return 0;
+  return ca::call_layout(nullptr, B, N, H).bytes;
+}
+
+int cluster_attn_bwd_planned(int dt, int B, int N, int C, int H, int D, int cs, int nk,
+                             float scale, const void* q, const void* k, const void* v,
+                             const void* o, const void* dout, const float* lse,
+                             const int32_t* q_idx, const int32_t* key_idx, const void* plan,
+                             size_t plan_bytes, void* dq, void* dk, void* dv, void* ws,
+                             size_t ws_bytes, void* hip_stream) {
+  if (int s = check_attn_shape(dt, B, N, H, D, cs, nk)) return s;
+  if (int s = check_plan_sizes(B, N, C, cs, nk)) return s;
+  if (B > 0 && N > 0 && C > 0 && !plan) return fail(CA_ERR_NULL, "NULL plan");
+  return attn_bwd(dt, B, N, C, H, D, cs, nk, scale, q, k, v, o, dout, lse, q_idx, key_idx, plan,
+                  plan_bytes, dq, dk, dv, ws, ws_bytes, hip_stream);
 }
 
 int cluster_attn_knn_table(const float* coords, int B, int N, int grid_side, int K,

@@ -603,8 +603,11 @@ bwd_q_lds_kernel(int N, int C, int H, int HP, int n_items, int ipw, float scale,
                  const T* __restrict__ o, const T* __restrict__ dout,
                  const float* __restrict__ lse, const int32_t* __restrict__ q_idx,
                  const int32_t* __restrict__ key_idx, T* __restrict__ dq,
-                 float2* __restrict__ ld) {
+                 float2* __restrict__ ld, float4* __restrict__ ld_none) {
   __shared__ __attribute__((aligned(1024))) char lds[kQWaves * kQWaveLds];
+  // the (LSE*log2e, Delta) pair the key-major pass reads for an absent
+  // query: P = exp2(s - inf) = 0 there (the first wait below covers it)
+  if (blockIdx.x == 0 && threadIdx.x == 0) *ld_none = make_float4(INFINITY, 0.f, INFINITY, 0.f);
   const int wv = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   // items dealt round-robin over the wavefronts (see the forward)
   const int first = xcd_remap(blockIdx.x, gridDim.x) * kQWaves + wv;
@@ -1114,7 +1117,7 @@ hipError_t bwd_t(int pass, int B, int N, int C, int H, int nk, float scale, cons
     hipLaunchKernelGGL((bwd_q_lds_kernel<T>), dim3((waves + kQWaves - 1) / kQWaves),
                        dim3(64 * kQWaves), 0, st, N, C, H, HP, items, ipw, scale, (const T*)q,
                        (const T*)k, (const T*)v, (const T*)o, (const T*)dout, lse, q_idx, key_idx,
-                       (T*)dq, w.ld);
+                       (T*)dq, w.ld, w.ld_none);
   }
   if (pass & 2) {
     const uint32_t ld_none = (uint32_t)((const char*)w.ld_none - (const char*)w.ld);

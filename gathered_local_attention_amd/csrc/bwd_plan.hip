@@ -39,19 +39,11 @@ constexpr int kPlanThreads = 1024;
 constexpr int kMaxNk = 64;
 constexpr int kGridThreads = 256;
 
-// The (LSE * log2 e, Delta) pair the key-major pass reads for an absent
-// query (a -1 member of a partial cluster): P = exp2(s - inf) = 0 there.
-__device__ __forceinline__ void write_ld_none(float4* ld_none) {
-  *ld_none = make_float4(INFINITY, 0.f, INFINITY, 0.f);
-}
-
 __global__ void __launch_bounds__(kGridThreads)
-plan_init_kernel(int64_t n_inv, int64_t n_cnt, int32_t* __restrict__ inv, int32_t* __restrict__ cnt,
-                 float4* __restrict__ ld_none) {
+plan_init_kernel(int64_t n_inv, int64_t n_cnt, int32_t* __restrict__ inv, int32_t* __restrict__ cnt) {
   const int64_t x = (int64_t)blockIdx.x * kGridThreads + threadIdx.x;
   if (x < n_inv) inv[x] = -1;
   if (x < n_cnt) cnt[x] = 0;
-  if (x == 0) write_ld_none(ld_none);
 }
 
 // one thread per q_idx position (c*8 + m) of the batch
@@ -305,8 +297,7 @@ constexpr int kGroupsPer = (kPlanMaxSlots / 8 + kPlanThreads - 1) / kPlanThreads
 __global__ void __launch_bounds__(kPlanThreads)
 plan_small_kernel(int N, int C, int nk, const int32_t* __restrict__ q_idx,
                   const int32_t* __restrict__ key_idx, int32_t* __restrict__ off_all,
-                  RevEntry* __restrict__ rev_all, int32_t* __restrict__ rtok_all,
-                  float4* __restrict__ ld_none) {
+                  RevEntry* __restrict__ rev_all, int32_t* __restrict__ rtok_all) {
   __shared__ int32_t inv[kSortChunk];                       // token -> position c*8 + m
   __shared__ __attribute__((aligned(16))) int32_t qp[kSortChunk];   // position -> token
   __shared__ uint32_t bits[kPlanMaxC][kPlanWords];
@@ -320,7 +311,6 @@ plan_small_kernel(int N, int C, int nk, const int32_t* __restrict__ q_idx,
   const int ngroups = ns / 8;
   const int P = 8 * C;                                       // q_idx positions, <= 2048
   const int32_t* qi = q_idx + (int64_t)b * P;
-  if (b == 0 && tid == 0) write_ld_none(ld_none);
   const int32_t* ki = key_idx + (int64_t)b * ns;
 
   // this thread's slot groups gr = tid + r * 1024, loaded up front
@@ -467,13 +457,13 @@ hipError_t launch_bwd_plan(int B, int N, int C, int nk, const int32_t* q_idx,
   if (nk > kMaxNk) return hipErrorInvalidValue;
   if (N <= kSortChunk && C <= kPlanMaxC && C * nk <= kPlanMaxSlots && nk % 8 == 0) {
     hipLaunchKernelGGL(plan_small_kernel, dim3(B), dim3(kPlanThreads), 0, st, N, C, nk, q_idx,
-                       key_idx, w.off, w.rev, w.rtok, w.ld_none);
+                       key_idx, w.off, w.rev, w.rtok);
     return hipGetLastError();
   }
   const int64_t tokens = (int64_t)B * N, clusters = (int64_t)B * C;
   auto grid = [](int64_t n) { return dim3((unsigned)((n + kGridThreads - 1) / kGridThreads)); };
   hipLaunchKernelGGL(plan_init_kernel, grid(std::max<int64_t>(tokens, 1)), dim3(kGridThreads), 0,
-                     st, tokens, clusters, w.inv, w.cnt, w.ld_none);
+                     st, tokens, clusters, w.inv, w.cnt);
   hipLaunchKernelGGL(plan_inv_kernel, grid(clusters * 8), dim3(kGridThreads), 0, st, B, N, C,
                      q_idx, w.inv);
   hipLaunchKernelGGL(plan_count_kernel, dim3((unsigned)((clusters + kCountThreads - 1) / kCountThreads)),

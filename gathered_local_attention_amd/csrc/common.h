@@ -28,9 +28,15 @@ struct RevEntry {
 };
 
 // ---- workspace layout of the backward pass --------------------------------
+// Two parts: the per-call part (LSE/Delta pairs of pass A, read by pass B)
+// and the plan (the transposed slot lists, a function of q_idx and key_idx
+// alone, so it can be built once and reused by every backward call on the
+// same lists).
 struct BwdWorkspace {
+  // per call
   float2* ld;        // [B, N, H]   (LSE * log2(e), Delta) per query and head
   float4* ld_none;   // (+inf, 0, +inf, 0): the pair read for an absent query
+  // plan
   int32_t* inv;      // [B, N]      token -> position in q_idx (c*cs + m)
   int32_t* cnt;      // [B, C]      entries per key cluster
   int32_t* off;      // [B, C + 1]  segment starts (per image, relative)
@@ -43,26 +49,49 @@ struct BwdWorkspace {
 
 static inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
-static inline BwdWorkspace bwd_layout(void* base, int64_t B, int64_t N, int64_t H, int64_t C,
-                                      int64_t nk) {
-  BwdWorkspace w;
+struct Carver {
+  char* b;
   size_t p = 0;
-  char* b = (char*)base;
-  auto take = [&](size_t n) {
+  void* take(size_t n) {
     size_t at = p;
     p = align_up(p + n, 256);
     return b ? (void*)(b + at) : (void*)nullptr;
-  };
-  w.ld = (float2*)take((size_t)(B * N * H) * sizeof(float2));
-  w.ld_none = (float4*)take(sizeof(float4));
-  w.inv = (int32_t*)take((size_t)(B * N) * sizeof(int32_t));
-  w.cnt = (int32_t*)take((size_t)(B * C) * sizeof(int32_t));
-  w.off = (int32_t*)take((size_t)(B * (C + 1)) * sizeof(int32_t));
-  w.cursor = (int32_t*)take((size_t)(B * C) * sizeof(int32_t));
-  w.stage = (RevEntry*)take((size_t)(B * C * nk) * sizeof(RevEntry));
-  w.rev = (RevEntry*)take((size_t)(B * C * nk) * sizeof(RevEntry));
-  w.rtok = (int32_t*)take((size_t)(B * C * nk) * 8 * sizeof(int32_t));
-  w.bytes = p;
+  }
+};
+
+// the per-call part at `base` (other fields left null)
+static inline BwdWorkspace call_layout(void* base, int64_t B, int64_t N, int64_t H) {
+  BwdWorkspace w{};
+  Carver c{(char*)base};
+  w.ld = (float2*)c.take((size_t)(B * N * H) * sizeof(float2));
+  w.ld_none = (float4*)c.take(sizeof(float4));
+  w.bytes = c.p;
+  return w;
+}
+
+// the plan at `base` (per-call fields left null)
+static inline BwdWorkspace plan_layout(void* base, int64_t B, int64_t N, int64_t C, int64_t nk) {
+  BwdWorkspace w{};
+  Carver c{(char*)base};
+  w.inv = (int32_t*)c.take((size_t)(B * N) * sizeof(int32_t));
+  w.cnt = (int32_t*)c.take((size_t)(B * C) * sizeof(int32_t));
+  w.off = (int32_t*)c.take((size_t)(B * (C + 1)) * sizeof(int32_t));
+  w.cursor = (int32_t*)c.take((size_t)(B * C) * sizeof(int32_t));
+  w.stage = (RevEntry*)c.take((size_t)(B * C * nk) * sizeof(RevEntry));
+  w.rev = (RevEntry*)c.take((size_t)(B * C * nk) * sizeof(RevEntry));
+  w.rtok = (int32_t*)c.take((size_t)(B * C * nk) * 8 * sizeof(int32_t));
+  w.bytes = c.p;
+  return w;
+}
+
+// both parts in one buffer: the per-call part, then the plan
+static inline BwdWorkspace bwd_layout(void* base, int64_t B, int64_t N, int64_t H, int64_t C,
+                                      int64_t nk) {
+  const BwdWorkspace a = call_layout(base, B, N, H);
+  BwdWorkspace w = plan_layout(base ? (char*)base + a.bytes : nullptr, B, N, C, nk);
+  w.ld = a.ld;
+  w.ld_none = a.ld_none;
+  w.bytes += a.bytes;
   return w;
 }
 

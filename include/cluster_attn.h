@@ -220,6 +220,35 @@ int cluster_attn_bwd(int dt, int B, int N, int H, int D, int cs, int nk, float s
                      size_t ws_bytes, void* hip_stream);
 
 /*
+ * The backward's transposed (key-major) slot lists depend on q_idx and
+ * key_idx alone, like the lists themselves (which change only where tokens
+ * are merged, so one build serves every attention layer of a stage).  A
+ * caller that runs several backward passes on the same lists can build
+ * them once:
+ *   cluster_attn_bwd_plan      writes them into `plan` (device, at least
+ *                              cluster_attn_bwd_plan_workspace bytes).
+ *   cluster_attn_bwd_planned   is cluster_attn_bwd with that plan as an
+ *                              input; its own workspace `ws` then only
+ *                              holds the per-call LSE/Delta pairs
+ *                              (cluster_attn_bwd_planned_workspace bytes).
+ * Sizes: B images of N tokens and C clusters each, C = ceil(N/cs); a packed
+ * batch (cluster_attn_*_varlen) is B = 1, N = T, C = Ct.  A plan must not
+ * be used with lists other than the ones it was built from (not checked).
+ * The result equals cluster_attn_bwd's bit for bit.
+ */
+size_t cluster_attn_bwd_plan_workspace(int B, int N, int C, int cs, int nk);
+int cluster_attn_bwd_plan(int B, int N, int C, int cs, int nk, const int32_t* q_idx,
+                          const int32_t* key_idx, void* plan, size_t plan_bytes,
+                          void* hip_stream);
+size_t cluster_attn_bwd_planned_workspace(int dt, int B, int N, int H, int D);
+int cluster_attn_bwd_planned(int dt, int B, int N, int C, int H, int D, int cs, int nk,
+                             float scale, const void* q, const void* k, const void* v,
+                             const void* o, const void* dout, const float* lse,
+                             const int32_t* q_idx, const int32_t* key_idx, const void* plan,
+                             size_t plan_bytes, void* dq, void* dk, void* dv, void* ws,
+                             size_t ws_bytes, void* hip_stream);
+
+/*
  * Forward and backward of a packed batch (see
  * cluster_attn_build_neighbors_varlen): the same computation as
  * cluster_attn_fwd / cluster_attn_bwd with the whole batch as one index

@@ -180,6 +180,27 @@ def test_3d_build_validation(lib):
                                                       None) == CA_ERR_SHAPE
 
 
+def test_plan_validation(lib):
+    assert lib.cluster_attn_bwd_plan_workspace(2, 64, 8, 8, 48) > 0
+    assert lib.cluster_attn_bwd_plan_workspace(2, 64, 9, 8, 48) == 0        # C != ceil(N/8), B > 1
+    assert lib.cluster_attn_bwd_plan_workspace(1, 100, 20, 8, 48) > 0      # packed: 13 <= C <= N
+    assert lib.cluster_attn_bwd_plan_workspace(1, 100, 101, 8, 48) == 0
+    need = lib.cluster_attn_bwd_plan_workspace(2, 64, 8, 8, 48)
+    assert lib.cluster_attn_bwd_plan(2, 64, 8, 8, 48, P, 2 * P, 3 * P, need - 1, None) == CA_ERR_WORKSPACE
+    assert lib.cluster_attn_bwd_plan(2, 64, 8, 8, 48, P, None, 3 * P, need, None) == CA_ERR_NULL
+    assert lib.cluster_attn_bwd_plan(2, 64, 8, 8, 48, P, 2 * P, 2 * P + 4, need, None) == CA_ERR_ALIAS
+    assert lib.cluster_attn_bwd_plan(0, 64, 8, 8, 48, None, None, None, 0, None) == CA_OK
+    p11 = [P * (i + 1) for i in range(11)]
+    call = lambda plan, pb, ws, wb: lib.cluster_attn_bwd_planned(
+        1, 2, 64, 8, 2, 32, 8, 48, 0.17, *p11[:8], plan, pb, *p11[8:], ws, wb, None)
+    wneed = lib.cluster_attn_bwd_planned_workspace(1, 2, 64, 2, 32)
+    assert 0 < wneed < lib.cluster_attn_bwd_workspace(1, 2, 64, 2, 32, 8, 48)
+    assert call(None, 0, P * 40, wneed) == CA_ERR_NULL
+    assert call(P * 30, need - 1, P * 40, wneed) == CA_ERR_WORKSPACE
+    assert call(P * 30, need, P * 40, wneed - 1) == CA_ERR_WORKSPACE
+    assert call(p11[9], need, P * 40, wneed) == CA_ERR_ALIAS              # plan over dk (an input over an output)
+
+
 def test_missing_library_raises(tmp_path):
     with pytest.raises(_lib.LibraryMissing):
         _lib.load(str(tmp_path / "nope.so"))

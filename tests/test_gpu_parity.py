@@ -335,3 +335,34 @@ def test_full_size_sampled(ca, name):
     sdk = dk.double().sum(dim=1).abs().max().item()
     sdv = (dv.double().sum(dim=1) - dev[3].double().sum(dim=1)).abs().max().item()
     print(f"  sum rules: |sum dK| {sdk:.3e}, |sum dV - sum dO| {sdv:.3e}", flush=True)
+
+
+def test_planned_backward_equals_backward(ca):
+    """The transposed lists built once (bwd_plan) and reused: bit-identical
+    to the self-planning backward, on the in-LDS plan (stage-1 images), the
+    grid-wide plan (a packed batch) and the vector-ALU kernels (fp32), and
+    across two calls with different output gradients."""
+    from gen import make_varlen_case
+
+    r = run_case(ca, "stage1", B=2)
+    qd, kd, vd, dod, perm, key, scale = r["inputs"]
+    plan = ca.bwd_plan(perm, key, qd.shape[1])
+    for do in (dod, dod.flip(1).contiguous()):
+        ref = ca.bwd(qd, kd, vd, r["o"], do, r["lse"], perm, key, scale)
+        got = ca.bwd(qd, kd, vd, r["o"], do, r["lse"], perm, key, scale, plan=plan)
+        torch.cuda.synchronize()
+        for a, b in zip(ref, got):
+            assert torch.equal(a, b)
+    for name in ("varlen_mixed", "varlen_tiny"):
+        case = make_varlen_case(name)
+        print(f"case planned {name}", flush=True)
+        q_idx, _, key_v, _, _ = ca.build_neighbors_varlen(torch.from_numpy(case["coords"]).to(DEV),
+                                                          case["lengths"], case["cfg"].G)
+        dev = [case[n].to(DEV) for n in ("q", "k", "v", "do")]
+        o, lse = ca.fwd_varlen(dev[0], dev[1], dev[2], q_idx, key_v)
+        plan = ca.bwd_plan(q_idx, key_v, dev[0].shape[0])
+        ref = ca.bwd_varlen(dev[0], dev[1], dev[2], o, dev[3], lse, q_idx, key_v)
+        got = ca.bwd_varlen(dev[0], dev[1], dev[2], o, dev[3], lse, q_idx, key_v, plan=plan)
+        torch.cuda.synchronize()
+        for a, b in zip(ref, got):
+            assert torch.equal(a, b)
