@@ -38,7 +38,7 @@ HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, vendor figure
 ENTRY_KERNELS = {
     "build": ["build_small_kernel (N <= 4096) | rank_kernel, merge_round_kernel, "
               "centroid_box_kernel, select_box_kernel (N > 4096)"],
-    "plan": ["plan_small_kernel (images <= 2048 tokens) | plan_init/inv/count/scan/place/sort_kernel"],
+    "plan": ["plan_small_kernel (images <= 4096 tokens) | plan_init/inv/count/scan/place/sort_kernel"],
     "fwd": ["fwd_lds_kernel"],
     "bwd": ["bwd_q_lds_kernel", "bwd_kv_lds_kernel"],
 }
@@ -392,9 +392,12 @@ def bench_varlen(args, torch, ca):
         return ca.build_neighbors_varlen(s["coords"], lengths, cfg.G, cfg.cs, cfg.k, workspace=bws,
                                          offsets=offsets)
 
+    def plan_of(q_idx, key):
+        return ca.bwd_plan_varlen(q_idx, key, lengths, offsets=offsets)
+
     def step(s):
         q_idx, _, key, _, _ = build(s)
-        plan = ca.bwd_plan(q_idx, key, T)
+        plan = plan_of(q_idx, key)
         o, lse = ca.fwd_varlen(s["q"], s["k"], s["v"], q_idx, key, scale)
         return ca.bwd_varlen(s["q"], s["k"], s["v"], o, s["do"], lse, q_idx, key, scale,
                              workspace=gws, plan=plan)
@@ -413,10 +416,10 @@ def bench_varlen(args, torch, ca):
     for s in sets:
         q_idx, _, key, _, _ = build(s)
         o, lse = ca.fwd_varlen(s["q"], s["k"], s["v"], q_idx, key, scale)
-        outs.append((q_idx, key, o, lse, ca.bwd_plan(q_idx, key, T)))
+        outs.append((q_idx, key, o, lse, plan_of(q_idx, key)))
     calls = {
         "build": lambda i: build(sets[i]),
-        "plan": lambda i: ca.bwd_plan(outs[i][0], outs[i][1], T),
+        "plan": lambda i: plan_of(outs[i][0], outs[i][1]),
         "fwd": lambda i: ca.fwd_varlen(sets[i]["q"], sets[i]["k"], sets[i]["v"], outs[i][0],
                                        outs[i][1], scale),
         "bwd": lambda i: ca.bwd_varlen(sets[i]["q"], sets[i]["k"], sets[i]["v"], outs[i][2],
@@ -468,7 +471,7 @@ def bench_varlen(args, torch, ca):
         },
         "roofline": {
             "bound": "hbm",
-            "kernel": {"build": "cluster_attn_build_neighbors_varlen", "plan": "cluster_attn_bwd_plan",
+            "kernel": {"build": "cluster_attn_build_neighbors_varlen", "plan": "cluster_attn_bwd_plan_varlen",
                        "fwd": "cluster_attn_fwd_varlen", "bwd": "cluster_attn_bwd_planned"}[dom],
             "entry_point_kernels": ENTRY_KERNELS[dom],
             "achieved": achieved,

@@ -41,6 +41,7 @@ __all__ = [
     "bwd",
     "cluster_attention",
     "bwd_plan",
+    "bwd_plan_varlen",
     "build_neighbors_varlen",
     "fwd_varlen",
     "bwd_varlen",
@@ -176,6 +177,30 @@ def bwd_plan(q_idx: torch.Tensor, key_idx: torch.Tensor, N: int) -> torch.Tensor
     _check(lib.cluster_attn_bwd_plan(B, int(N), C, cs, nk, _dev(q_idx, "q_idx", torch.int32),
                                      _dev(key_idx, "key_idx", torch.int32), plan.data_ptr(),
                                      plan.numel(), _stream(key_idx)), "cluster_attn_bwd_plan")
+    return plan
+
+
+def bwd_plan_varlen(q_idx: torch.Tensor, key_idx: torch.Tensor, lengths, offsets=None) -> torch.Tensor:
+    """The plan of a packed batch (q_idx [Ct, cs], key_idx [Ct, nk] from
+    :func:`build_neighbors_varlen`), built one image at a time; ``offsets``
+    = the (tok_off, clu_off) device pair that call returned (else uploaded
+    from ``lengths``).  Pass the result as ``plan=`` to :func:`bwd_varlen`."""
+    lib = _lib.load()
+    Ct, cs = q_idx.shape
+    nk = key_idx.shape[1]
+    tok, clu = varlen_offsets(lengths, cs)
+    B, T = len(tok) - 1, tok[-1]
+    max_n = max((tok[b + 1] - tok[b] for b in range(B)), default=0)
+    if offsets is None:
+        offsets = (torch.tensor(tok, dtype=torch.int32).to(q_idx.device),
+                   torch.tensor(clu, dtype=torch.int32).to(q_idx.device))
+    need = lib.cluster_attn_bwd_plan_workspace(1, T, Ct, cs, nk)
+    plan = torch.empty(max(need, 1), dtype=torch.uint8, device=q_idx.device)
+    _check(lib.cluster_attn_bwd_plan_varlen(
+        B, T, Ct, max_n, _dev(offsets[0], "tok_off", torch.int32),
+        _dev(offsets[1], "clu_off", torch.int32), cs, nk, _dev(q_idx, "q_idx", torch.int32),
+        _dev(key_idx, "key_idx", torch.int32), plan.data_ptr(), plan.numel(), _stream(q_idx)),
+        "cluster_attn_bwd_plan_varlen")
     return plan
 
 

@@ -43,6 +43,9 @@ SIGNATURES = {
     "cluster_attn_bwd_plan_workspace": (_c_size, [_c_int, _c_int, _c_int, _c_int, _c_int]),
     "cluster_attn_bwd_plan": (
         _c_int, [_c_int, _c_int, _c_int, _c_int, _c_int, _vp, _vp, _vp, _c_size, _vp]),
+    "cluster_attn_bwd_plan_varlen": (
+        _c_int, [_c_int, _c_int, _c_int, _c_int, _vp, _vp, _c_int, _c_int, _vp, _vp, _vp, _c_size,
+                 _vp]),
     "cluster_attn_bwd_planned_workspace": (_c_size, [_c_int, _c_int, _c_int, _c_int, _c_int]),
     "cluster_attn_bwd_planned": (
         _c_int, [_c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _f,

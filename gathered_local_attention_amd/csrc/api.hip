@@ -422,6 +422,28 @@ int cluster_attn_bwd_plan(int B, int N, int C, int cs, int nk, const int32_t* q_
                     "bwd plan launch");
 }
 
+int cluster_attn_bwd_plan_varlen(int B, int T, int Ct, int max_n, const int32_t* tok_off,
+                                 const int32_t* clu_off, int cs, int nk, const int32_t* q_idx,
+                                 const int32_t* key_idx, void* plan, size_t plan_bytes,
+                                 void* hip_stream) {
+  if (int s = check_plan_sizes(1, T, Ct, cs, nk)) return s;
+  if (B < 0 || max_n < 0 || max_n > T)
+    return fail(CA_ERR_SHAPE, "bad sizes B=%d T=%d max_n=%d", B, T, max_n);
+  if (B == 0 || T == 0 || Ct == 0) return ok();
+  if (!q_idx || !key_idx || !plan || !tok_off || !clu_off) return fail(CA_ERR_NULL, "NULL pointer");
+  const size_t need = ca::plan_layout(nullptr, 1, T, Ct, nk).bytes;
+  if (plan_bytes < need) return fail(CA_ERR_WORKSPACE, "plan %zu < %zu bytes", plan_bytes, need);
+  Range outs[] = {{plan, need}};
+  Range ins[] = {{q_idx, (size_t)Ct * cs * 4}, {key_idx, (size_t)Ct * nk * 4},
+                 {tok_off, (size_t)(B + 1) * 4}, {clu_off, (size_t)(B + 1) * 4}};
+  if (int s = check_alias(outs, 1, ins, 4)) return s;
+  const ca::BwdWorkspace w = ca::plan_layout(plan, 1, T, Ct, nk);
+  const ca::Geom g{tok_off, clu_off, max_n, (int)clusters_of(max_n, cs), 0};
+  return hip_status(ca::launch_bwd_plan(B, T, Ct, nk, q_idx, key_idx, w, (hipStream_t)hip_stream,
+                                        &g),
+                    "bwd plan launch");
+}
+
 size_t cluster_attn_bwd_planned_workspace(int dt, int B, int N, int H, int D) {
   if (dt < CA_F32 || dt > CA_F16 || B < 0 || N < 0 || H < 1 || D != 32) return 0;
   return ca::call_layout(nullptr, B, N, H).bytes;

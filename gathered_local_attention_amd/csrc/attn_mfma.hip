@@ -838,7 +838,7 @@ bwd_kv_lds_kernel(int N, int C, int H, int HP, int n_items, float scale, const T
                   const T* __restrict__ k, const T* __restrict__ v, const T* __restrict__ dout,
                   const int32_t* __restrict__ q_idx, const float2* __restrict__ ld,
                   uint32_t ld_none,
-                  const int32_t* __restrict__ off_all, const RevEntry* __restrict__ rev_all,
+                  const int2* __restrict__ seg_all, const RevEntry* __restrict__ rev_all,
                   const int32_t* __restrict__ rtok_all, int nk, T* __restrict__ dk,
                   T* __restrict__ dv) {
   __shared__ __attribute__((aligned(1024))) char lds[kWaves * kKvWaveLds];
@@ -881,14 +881,13 @@ bwd_kv_lds_kernel(int N, int C, int H, int HP, int n_items, float scale, const T
   int vzero;
   asm volatile("v_mov_b32 %0, 0" : "=v"(vzero));
   auto seg_of = [&](const KvPos& p) {
-    const int x = p.item < n_items ? p.bj + p.b : 0;
-    return *reinterpret_cast<const int2*>(off_all + x + vzero);
+    const int x = p.item < n_items ? p.bj : 0;
+    return seg_all[x + vzero];
   };
   // absolute entry range [e0, e1) of an item (indices into rev / rtok)
   auto bounds = [&](const KvPos& p, int2 sg, int& e0, int& e1) {
-    const int base = p.b * C * nk;
-    e0 = p.item < n_items ? base + __builtin_amdgcn_readfirstlane(sg.x) : 0;
-    e1 = p.item < n_items ? base + __builtin_amdgcn_readfirstlane(sg.y) : 0;
+    e0 = p.item < n_items ? __builtin_amdgcn_readfirstlane(sg.x) : 0;
+    e1 = p.item < n_items ? __builtin_amdgcn_readfirstlane(sg.y) : 0;
   };
   // block of entries [x0, x0 + 8) (clamped to [x0, x1)) into LDS block `blk`:
   // int 8u + r = token of member r of entry u, uint64 u = its multiplicities
@@ -1123,7 +1122,7 @@ hipError_t bwd_t(int pass, int B, int N, int C, int H, int nk, float scale, cons
     const uint32_t ld_none = (uint32_t)((const char*)w.ld_none - (const char*)w.ld);
     hipLaunchKernelGGL((bwd_kv_lds_kernel<T>), dim3(kv_wgs), dim3(64 * kWaves), 0, st, N, C, H, HP,
                        items, scale, (const T*)q, (const T*)k, (const T*)v, (const T*)dout, q_idx,
-                       (const float2*)w.ld, ld_none, (const int32_t*)w.off,
+                       (const float2*)w.ld, ld_none, (const int2*)w.seg,
                        (const RevEntry*)w.rev, (const int32_t*)w.rtok, nk, (T*)dk, (T*)dv);
   }
   return hipGetLastError();

@@ -196,7 +196,7 @@ __global__ void __launch_bounds__(64)
 bwd_kv_valu_kernel(int N, int C, int H, int nk, float scale, const T* __restrict__ q,
                    const T* __restrict__ k, const T* __restrict__ v, const T* __restrict__ dout,
                    const float* __restrict__ lse, const int32_t* __restrict__ q_idx,
-                   const float2* __restrict__ ld, const int32_t* __restrict__ off_all,
+                   const float2* __restrict__ ld, const int2* __restrict__ seg_all,
                    const RevEntry* __restrict__ rev_all, T* __restrict__ dk, T* __restrict__ dv) {
   __shared__ float kj[CS][kPad];
   __shared__ float vj[CS][kPad];
@@ -224,9 +224,9 @@ bwd_kv_valu_kernel(int N, int C, int H, int nk, float scale, const T* __restrict
       vj[hi][4 * lo + e] = to_f32(v[row + e]);
     }
   }
-  const int32_t* off = off_all + (int64_t)b * (C + 1);
-  const RevEntry* rev = rev_all + (int64_t)b * C * nk;
-  const int e0 = off[j], e1 = off[j + 1];
+  const RevEntry* rev = rev_all;   // absolute entry ranges
+  const int2 sg = seg_all[bj];
+  const int e0 = sg.x, e1 = sg.y;
 
   float dka[4] = {0.f, 0.f, 0.f, 0.f}, dva[4] = {0.f, 0.f, 0.f, 0.f};
   for (int e = e0; e < e1; ++e) {
@@ -308,7 +308,7 @@ hipError_t bwd_t(int pass, int B, int N, int C, int H, int nk, float scale, cons
   if (pass & 2)
     hipLaunchKernelGGL(bwd_kv_valu_kernel<T>, dim3((unsigned)blocks), dim3(64), 0, st, N, C, H, nk,
                        scale, (const T*)q, (const T*)k, (const T*)v, (const T*)dout, lse, q_idx,
-                       (const float2*)w.ld, (const int32_t*)w.off, (const RevEntry*)w.rev,
+                       (const float2*)w.ld, (const int2*)w.seg, (const RevEntry*)w.rev,
                        (T*)dk, (T*)dv);
   return hipGetLastError();
 }

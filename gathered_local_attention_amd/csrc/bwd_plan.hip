@@ -20,7 +20,8 @@
 //      (jn = inv[token]); the first slot of i that points into key cluster
 //      j stages the entry (j, per-member multiplicities) in i's staging row
 //      (compact, ended by a sentinel) and counts it for j (atomic)
-//   4. per image, exclusive scan of the counts -> segment offsets
+//   4. per image, exclusive scan of the counts -> segment (start, end)
+//      pairs, absolute in the entry arrays
 //   5. per query cluster, its staged entries are placed in their segments
 //      (atomic cursor)
 //   6. per key cluster, its segment is sorted by i (which fixes the
@@ -142,14 +143,15 @@ plan_count_kernel(int B, int N, int C, int nk, const int32_t* __restrict__ key_i
 constexpr int kScanChunk = 8192;
 
 __global__ void __launch_bounds__(kPlanThreads)
-plan_scan_kernel(int C, const int32_t* __restrict__ cnt_all, int32_t* __restrict__ off_all,
+plan_scan_kernel(int C, int nk, const int32_t* __restrict__ cnt_all, int2* __restrict__ seg_all,
                  int32_t* __restrict__ cur_all) {
   __shared__ int32_t v[kScanChunk];
   __shared__ int32_t tmp[17];
   const int64_t b = blockIdx.x;
   const int32_t* cnt = cnt_all + b * C;
-  int32_t* off = off_all + b * (C + 1);
+  int2* seg = seg_all + b * C;
   int32_t* cur = cur_all + b * C;
+  const int base = (int)(b * C * nk);   // the image's entries start here
   constexpr int kPer = kScanChunk / kPlanThreads;
   int carry = 0;
   for (int c0 = 0; c0 < C; c0 += kScanChunk) {
@@ -172,13 +174,12 @@ plan_scan_kernel(int C, const int32_t* __restrict__ cnt_all, int32_t* __restrict
     }
     __syncthreads();
     for (int x = threadIdx.x; x < n; x += kPlanThreads) {
-      off[c0 + x] = v[x];
+      seg[c0 + x] = make_int2(base + v[x], base + v[x] + cnt[c0 + x]);
       cur[c0 + x] = v[x];
     }
     carry += tot;
     __syncthreads();   // v and tmp are reused by the next chunk
   }
-  if (threadIdx.x == 0) off[C] = carry;
 }
 
 // one thread per query cluster: its staged entries into their segments
@@ -206,16 +207,14 @@ constexpr int kSortRegs = 16;
 
 __global__ void __launch_bounds__(kGridThreads)
 plan_sort_kernel(int B, int C, int nk, const int32_t* __restrict__ q_idx,
-                 const int32_t* __restrict__ off_all, RevEntry* __restrict__ rev_all,
+                 const int2* __restrict__ seg_all, RevEntry* __restrict__ rev,
                  int32_t* __restrict__ rtok_all) {
   const int64_t bj = (int64_t)blockIdx.x * kGridThreads + threadIdx.x;
   if (bj >= (int64_t)B * C) return;
   const int64_t b = bj / C;
-  const int j = (int)(bj - b * C);
-  const int32_t* off = off_all + b * (C + 1);
-  RevEntry* rev = rev_all + b * C * nk;
-  const int a = off[j], z = off[j + 1];
-  int4* rt = reinterpret_cast<int4*>(rtok_all + b * C * nk * 8);
+  const int2 sg = seg_all[bj];   // absolute entry range of key cluster j
+  const int a = sg.x, z = sg.y;
+  int4* rt = reinterpret_cast<int4*>(rtok_all);
   const int32_t* qi = q_idx + b * C * 8;
   if (z - a <= kSortRegs) {
     int ii[kSortRegs];
@@ -275,43 +274,68 @@ plan_sort_kernel(int B, int C, int nk, const int32_t* __restrict__ q_idx,
 }
 
 // ---------------------------------------------------------------------------
-// Images with at most 256 clusters and 12288 slots, one workgroup each, all
-// in LDS.  A thread owns whole slot groups (8 consecutive slots of one
-// cluster's list, loaded as two 16-byte vectors) and works on each distinct
-// key cluster j its group points into (usually one, which is checked first):
-// it sets bit i of row j in an LDS bitmap, and later adds the group's member
-// counts for j into the multiplicity bytes of entry (i, j) with one LDS
-// integer atomic (a list has at most 64 slots, so a byte never carries).
-// Segment sizes are row popcounts and the entry of (i, j) sits at off[j] +
-// (set bits of row j below i), so segments come out ordered by i and the
-// sums are order independent: deterministic without a sort.  The thread
-// that adds an entry's multiplicities also records its i, and the entries go
-// out one thread each, together with the q_idx row of their i (the eight
-// query tokens the key-major pass gathers), which the workgroup keeps in LDS.
+// Images with at most MAXC clusters (256: up to 2048 tokens and 12288
+// slots; 512: up to 4096 tokens), one workgroup each, all in LDS.  A thread
+// owns whole slot groups (8 consecutive slots of one cluster's list, loaded
+// as two 16-byte vectors) and works on each distinct key cluster j its
+// group points into (usually one, which is checked first): it sets bit i of
+// row j in an LDS bitmap, and later adds the group's member counts for j
+// into the multiplicity bytes of entry (i, j) with one integer atomic (a
+// list has at most 64 slots, so a byte never carries).  Segment sizes are
+// row popcounts and the entry of (i, j) sits at seg[j] + (set bits of row j
+// below i), so segments come out ordered by i and the sums are order
+// independent: deterministic without a sort.  The thread that adds an
+// entry's multiplicities also records its i, and the entries go out one
+// thread each, together with the q_idx row of their i (the eight query
+// tokens the key-major pass gathers), which the workgroup keeps in LDS.
+// With MAXC = 512 the multiplicities are accumulated in the entry array in
+// global memory (zeroed first) instead of LDS.  Packed batches (Geom with
+// offsets) run one workgroup per image with batch-global token ids; image
+// b's entries live at [c0 * nk, c1 * nk).
 // ---------------------------------------------------------------------------
-constexpr int kPlanMaxC = 256;
-constexpr int kPlanWords = kPlanMaxC / 32;
 constexpr int kPlanMaxSlots = 12288;
-constexpr int kGroupsPer = (kPlanMaxSlots / 8 + kPlanThreads - 1) / kPlanThreads;   // 2
 
+template <int MAXC>
+struct PlanLds;
+template <>
+struct PlanLds<256> {
+  static constexpr int kWords = 8, kTok = 2048, kGroupsPer = 2;
+  unsigned long long mult[kPlanMaxSlots];
+  uint8_t ent_i[kPlanMaxSlots];   // entry -> its query cluster i
+};
+template <>
+struct PlanLds<512> {
+  static constexpr int kWords = 16, kTok = 4096, kGroupsPer = 3;
+  uint16_t ent_i[512 * 48];
+};
+
+template <int MAXC>
 __global__ void __launch_bounds__(kPlanThreads)
-plan_small_kernel(int N, int C, int nk, const int32_t* __restrict__ q_idx,
-                  const int32_t* __restrict__ key_idx, int32_t* __restrict__ off_all,
+plan_small_kernel(Geom g, int nk, const int32_t* __restrict__ q_idx,
+                  const int32_t* __restrict__ key_idx, int2* __restrict__ seg_all,
                   RevEntry* __restrict__ rev_all, int32_t* __restrict__ rtok_all) {
-  __shared__ int32_t inv[kSortChunk];                       // token -> position c*8 + m
-  __shared__ __attribute__((aligned(16))) int32_t qp[kSortChunk];   // position -> token
-  __shared__ uint32_t bits[kPlanMaxC][kPlanWords];
-  __shared__ int32_t wo[kPlanMaxC][kPlanWords];
-  __shared__ unsigned long long mult[kPlanMaxSlots];
-  __shared__ uint8_t ent_i[kPlanMaxSlots];                  // entry -> its query cluster i
+  typedef PlanLds<MAXC> L;
+  constexpr int kWords = L::kWords, kGroupsPer = L::kGroupsPer, kQPer = L::kTok / kPlanThreads;
+  constexpr bool kGlobalMult = MAXC > 256;
+  __shared__ int32_t inv[L::kTok];                                  // token -> position c*8 + m
+  __shared__ __attribute__((aligned(16))) int32_t qp[L::kTok];      // position -> token
+  __shared__ uint32_t bits[MAXC][kWords];
+  __shared__ int32_t wo[MAXC][kWords];
+  __shared__ L lds;
   __shared__ int32_t tmp[17];
   const int b = blockIdx.x;
   const int tid = threadIdx.x;
+  int t0, N, c0, C;
+  g.image(b, t0, N, c0, C);
+  if (C == 0) return;
+  const int tb = g.tok_base(t0);                             // token id of the image's token 0
+  const int cb = g.clu_base(c0);                             // cluster id of its cluster 0
   const int ns = C * nk;
   const int ngroups = ns / 8;
-  const int P = 8 * C;                                       // q_idx positions, <= 2048
-  const int32_t* qi = q_idx + (int64_t)b * P;
-  const int32_t* ki = key_idx + (int64_t)b * ns;
+  const int P = 8 * C;                                       // q_idx positions
+  const int32_t* qi = q_idx + (int64_t)c0 * 8;
+  const int32_t* ki = key_idx + (int64_t)c0 * nk;
+  const int64_t base = (int64_t)c0 * nk;                     // the image's entries
 
   // this thread's slot groups gr = tid + r * 1024, loaded up front
   int tok[kGroupsPer][8];
@@ -326,15 +350,21 @@ plan_small_kernel(int N, int C, int nk, const int32_t* __restrict__ q_idx,
     tok[r][0] = a.x; tok[r][1] = a.y; tok[r][2] = a.z; tok[r][3] = a.w;
     tok[r][4] = c.x; tok[r][5] = c.y; tok[r][6] = c.z; tok[r][7] = c.w;
   }
-  const int q0 = tid < P ? qi[tid] : -1;                       // -1: absent member
-  const int q1 = tid + kPlanThreads < P ? qi[tid + kPlanThreads] : -1;
+  int qv[kQPer];
+#pragma unroll
+  for (int r = 0; r < kQPer; ++r) {
+    const int x = tid + r * kPlanThreads;
+    qv[r] = x < P ? qi[x] : -1;                              // -1: absent member
+  }
   for (int t = tid; t < N; t += kPlanThreads) inv[t] = -1;
-  for (int x = tid; x < kPlanMaxC * kPlanWords; x += kPlanThreads) (&bits[0][0])[x] = 0u;
-  if (tid < P) qp[tid] = q0;
-  if (tid + kPlanThreads < P) qp[tid + kPlanThreads] = q1;
+  for (int x = tid; x < MAXC * kWords; x += kPlanThreads) (&bits[0][0])[x] = 0u;
+#pragma unroll
+  for (int r = 0; r < kQPer; ++r)
+    if (tid + r * kPlanThreads < P) qp[tid + r * kPlanThreads] = qv[r];
   __syncthreads();
-  if (q0 >= 0) inv[q0] = tid;
-  if (q1 >= 0) inv[q1] = tid + kPlanThreads;
+#pragma unroll
+  for (int r = 0; r < kQPer; ++r)
+    if (qv[r] >= 0) inv[qv[r] - tb] = tid + r * kPlanThreads;
   __syncthreads();
 
   // key position (j << 3 | member) of every slot.  A group that holds the
@@ -345,7 +375,7 @@ plan_small_kernel(int N, int C, int nk, const int32_t* __restrict__ q_idx,
   bool one[kGroupsPer];
 #pragma unroll
   for (int r = 0; r < kGroupsPer; ++r) {
-    const int p0 = tok[r][0] >= 0 ? inv[tok[r][0]] : -1;
+    const int p0 = tok[r][0] >= 0 ? inv[tok[r][0] - tb] : -1;
     bool same = p0 >= 0 && (p0 & 7) == 0;
     if (same) {
       const int4 a = reinterpret_cast<const int4*>(qp + p0)[0];
@@ -357,13 +387,15 @@ plan_small_kernel(int N, int C, int nk, const int32_t* __restrict__ q_idx,
     jn[r][0] = p0;
     if (!same) {
 #pragma unroll
-      for (int m = 1; m < 8; ++m) jn[r][m] = tok[r][m] >= 0 ? inv[tok[r][m]] : -1;
+      for (int m = 1; m < 8; ++m) jn[r][m] = tok[r][m] >= 0 ? inv[tok[r][m] - tb] : -1;
     }
   }
   // bitmap rows
 #pragma unroll
   for (int r = 0; r < kGroupsPer; ++r) {
-    const int i = (tid + r * kPlanThreads) * 8 / nk;
+    const int gr = tid + r * kPlanThreads;
+    if (gr >= ngroups) continue;
+    const int i = gr * 8 / nk;
     if (one[r]) {
       atomicOr(&bits[jn[r][0] >> 3][i >> 5], 1u << (i & 31));
       continue;
@@ -379,40 +411,55 @@ plan_small_kernel(int N, int C, int nk, const int32_t* __restrict__ q_idx,
   }
   __syncthreads();
 
-  // segment sizes, offsets, per-word offsets (exclusive scan over j < C <= 256)
-  int v = 0;
+  // segment sizes, starts, per-word starts (exclusive scan over j < C <= MAXC)
+  static_assert(MAXC <= kPlanThreads, "one bitmap row per thread");
+  int vsum = 0;
   if (tid < C) {
 #pragma unroll
-    for (int w = 0; w < kPlanWords; ++w) v += __popc(bits[tid][w]);
+    for (int w = 0; w < kWords; ++w) vsum += __popc(bits[tid][w]);
   }
   int total;
-  const int ex = block_exclusive_scan(v, tmp, kPlanThreads, &total);
+  const int ex = block_exclusive_scan(vsum, tmp, kPlanThreads, &total);
   if (tid < C) {
     int a = ex;
 #pragma unroll
-    for (int w = 0; w < kPlanWords; ++w) {
+    for (int w = 0; w < kWords; ++w) {
       wo[tid][w] = a;
       a += __popc(bits[tid][w]);
     }
+    seg_all[c0 + tid] = make_int2((int)(base + ex), (int)(base + ex + vsum));
   }
-  int32_t* goff = off_all + (int64_t)b * (C + 1);
-  if (tid <= C) goff[tid] = tid < C ? ex : total;
-  for (int p = tid; p < total; p += kPlanThreads) mult[p] = 0ull;
+  RevEntry* rev = rev_all + base;
+  if constexpr (kGlobalMult) {
+    for (int p = tid; p < total; p += kPlanThreads) rev[p].mult = 0ull;
+    __threadfence_block();
+  } else {
+    for (int p = tid; p < total; p += kPlanThreads) lds.mult[p] = 0ull;
+  }
   __syncthreads();
 
-  // multiplicities: one LDS atomic per distinct key cluster of a group
+  // multiplicities: one integer atomic per distinct key cluster of a group
+  auto add_mult = [&](int pos, uint64_t add, int i) {
+    if constexpr (kGlobalMult) {
+      atomicAdd(reinterpret_cast<unsigned long long*>(&rev[pos].mult), (unsigned long long)add);
+      lds.ent_i[pos] = (uint16_t)i;
+    } else {
+      atomicAdd(&lds.mult[pos], (unsigned long long)add);
+      lds.ent_i[pos] = (uint8_t)i;   // groups of one i that share j store the same value
+    }
+  };
 #pragma unroll
   for (int r = 0; r < kGroupsPer; ++r) {
-    const int i = (tid + r * kPlanThreads) * 8 / nk;
+    const int gr = tid + r * kPlanThreads;
+    if (gr >= ngroups) continue;
+    const int i = gr * 8 / nk;
     const uint32_t below = (1u << (i & 31)) - 1u;
     if (one[r]) {   // the members of j once each (absent members: -1 slots)
       const int jj = jn[r][0] >> 3;
       uint64_t add = 0;
 #pragma unroll
       for (int m = 0; m < 8; ++m) add |= tok[r][m] >= 0 ? 1ull << (8 * m) : 0ull;
-      const int pos = wo[jj][i >> 5] + __popc(bits[jj][i >> 5] & below);
-      atomicAdd(&mult[pos], (unsigned long long)add);
-      ent_i[pos] = (uint8_t)i;
+      add_mult(wo[jj][i >> 5] + __popc(bits[jj][i >> 5] & below), add, i);
       continue;
     }
 #pragma unroll
@@ -427,23 +474,26 @@ plan_small_kernel(int N, int C, int nk, const int32_t* __restrict__ q_idx,
 #pragma unroll
       for (int u = m; u < 8; ++u)
         if (jn[r][u] >= 0 && (jn[r][u] >> 3) == jj) add += 1ull << (8 * (jn[r][u] & 7));
-      const int pos = wo[jj][i >> 5] + __popc(bits[jj][i >> 5] & below);
-      atomicAdd(&mult[pos], (unsigned long long)add);
-      ent_i[pos] = (uint8_t)i;   // groups of one i that share j store the same value
+      add_mult(wo[jj][i >> 5] + __popc(bits[jj][i >> 5] & below), add, i);
     }
   }
+  if constexpr (kGlobalMult) __threadfence_block();
   __syncthreads();
 
   // entries out, one thread per entry (coalesced stores)
-  RevEntry* rev = rev_all + (int64_t)b * ns;
-  int4* rt = reinterpret_cast<int4*>(rtok_all + (int64_t)b * ns * 8);
+  int4* rt = reinterpret_cast<int4*>(rtok_all + base * 8);
   for (int p = tid; p < total; p += kPlanThreads) {
-    const int i = ent_i[p];
-    RevEntry e;
-    e.i = i;
-    e.pad = 0;
-    e.mult = mult[p];
-    rev[p] = e;
+    const int i = lds.ent_i[p];   // image-local; the entry records the batch-wide id
+    if constexpr (kGlobalMult) {
+      rev[p].i = cb + i;
+      rev[p].pad = 0;
+    } else {
+      RevEntry e;
+      e.i = cb + i;
+      e.pad = 0;
+      e.mult = lds.mult[p];
+      rev[p] = e;
+    }
     const int4* row = reinterpret_cast<const int4*>(qp + i * 8);
     rt[2 * p] = row[0];
     rt[2 * p + 1] = row[1];
@@ -453,13 +503,26 @@ plan_small_kernel(int N, int C, int nk, const int32_t* __restrict__ q_idx,
 }  // namespace
 
 hipError_t launch_bwd_plan(int B, int N, int C, int nk, const int32_t* q_idx,
-                           const int32_t* key_idx, const BwdWorkspace& w, hipStream_t st) {
+                           const int32_t* key_idx, const BwdWorkspace& w, hipStream_t st,
+                           const Geom* packed) {
   if (nk > kMaxNk) return hipErrorInvalidValue;
-  if (N <= kSortChunk && C <= kPlanMaxC && C * nk <= kPlanMaxSlots && nk % 8 == 0) {
-    hipLaunchKernelGGL(plan_small_kernel, dim3(B), dim3(kPlanThreads), 0, st, N, C, nk, q_idx,
-                       key_idx, w.off, w.rev, w.rtok);
+  // one workgroup per image, in LDS: equal-size images, or the images of a
+  // packed batch (then every image must fit)
+  const Geom g = packed ? *packed : Geom{nullptr, nullptr, N, C, 0};
+  const int nimg = B;
+  const int mn = g.N, mc = packed ? (g.N + 7) / 8 : C;
+  if (nk % 8 == 0 && mn <= 2048 && mc <= 256 && mc * nk <= kPlanMaxSlots) {
+    hipLaunchKernelGGL(plan_small_kernel<256>, dim3(nimg), dim3(kPlanThreads), 0, st, g, nk, q_idx,
+                       key_idx, w.seg, w.rev, w.rtok);
     return hipGetLastError();
   }
+  if (nk % 8 == 0 && nk <= 48 && mn <= 4096 && mc <= 512) {
+    hipLaunchKernelGGL(plan_small_kernel<512>, dim3(nimg), dim3(kPlanThreads), 0, st, g, nk, q_idx,
+                       key_idx, w.seg, w.rev, w.rtok);
+    return hipGetLastError();
+  }
+  // grid-wide: a packed batch as one image of its N tokens and C clusters
+  if (packed) B = 1;
   const int64_t tokens = (int64_t)B * N, clusters = (int64_t)B * C;
   auto grid = [](int64_t n) { return dim3((unsigned)((n + kGridThreads - 1) / kGridThreads)); };
   hipLaunchKernelGGL(plan_init_kernel, grid(std::max<int64_t>(tokens, 1)), dim3(kGridThreads), 0,
@@ -469,12 +532,12 @@ hipError_t launch_bwd_plan(int B, int N, int C, int nk, const int32_t* q_idx,
   hipLaunchKernelGGL(plan_count_kernel, dim3((unsigned)((clusters + kCountThreads - 1) / kCountThreads)),
                      dim3(kCountThreads), 0, st, B, N, C, nk, key_idx, (const int32_t*)w.inv,
                      w.cnt, w.stage);
-  hipLaunchKernelGGL(plan_scan_kernel, dim3(B), dim3(kPlanThreads), 0, st, C,
-                     (const int32_t*)w.cnt, w.off, w.cursor);
+  hipLaunchKernelGGL(plan_scan_kernel, dim3(B), dim3(kPlanThreads), 0, st, C, nk,
+                     (const int32_t*)w.cnt, w.seg, w.cursor);
   hipLaunchKernelGGL(plan_place_kernel, grid(clusters), dim3(kGridThreads), 0, st, B, C, nk,
                      (const RevEntry*)w.stage, w.cursor, w.rev);
   hipLaunchKernelGGL(plan_sort_kernel, grid(clusters), dim3(kGridThreads), 0, st, B, C, nk, q_idx,
-                     (const int32_t*)w.off, w.rev, w.rtok);
+                     (const int2*)w.seg, w.rev, w.rtok);
   return hipGetLastError();
 }
 

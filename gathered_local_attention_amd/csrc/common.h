@@ -39,10 +39,10 @@ struct BwdWorkspace {
   // plan
   int32_t* inv;      // [B, N]      token -> position in q_idx (c*cs + m)
   int32_t* cnt;      // [B, C]      entries per key cluster
-  int32_t* off;      // [B, C + 1]  segment starts (per image, relative)
+  int2* seg;         // [B, C]      (start, end) of every key cluster's entries, absolute
   int32_t* cursor;   // [B, C]
   RevEntry* stage;   // [B, C, nk]  entry of the first slot of i pointing into j
-  RevEntry* rev;     // [B, C*nk]   per key cluster, sorted by i
+  RevEntry* rev;     // [B, C*nk]   per key cluster, sorted by i (image b from b*C*nk)
   int32_t* rtok;     // [B, C*nk, cs] query tokens of entry e (q_idx row of its i)
   size_t bytes;
 };
@@ -75,7 +75,7 @@ static inline BwdWorkspace plan_layout(void* base, int64_t B, int64_t N, int64_t
   Carver c{(char*)base};
   w.inv = (int32_t*)c.take((size_t)(B * N) * sizeof(int32_t));
   w.cnt = (int32_t*)c.take((size_t)(B * C) * sizeof(int32_t));
-  w.off = (int32_t*)c.take((size_t)(B * (C + 1)) * sizeof(int32_t));
+  w.seg = (int2*)c.take((size_t)(B * C) * sizeof(int2));
   w.cursor = (int32_t*)c.take((size_t)(B * C) * sizeof(int32_t));
   w.stage = (RevEntry*)c.take((size_t)(B * C * nk) * sizeof(RevEntry));
   w.rev = (RevEntry*)c.take((size_t)(B * C * nk) * sizeof(RevEntry));
@@ -290,8 +290,12 @@ hipError_t launch_fwd_valu(int dt, int B, int N, int C, int H, int nk, float sca
                            const void* k, const void* v, const int32_t* q_idx,
                            const int32_t* key_idx, void* o, float* lse, hipStream_t st);
 
+// `packed` (optional): the images of a packed batch (B images, N = T tokens,
+// C = Ct clusters in total; packed->N the largest image), planned one
+// workgroup per image when every image fits in LDS.
 hipError_t launch_bwd_plan(int B, int N, int C, int nk, const int32_t* q_idx,
-                           const int32_t* key_idx, const BwdWorkspace& w, hipStream_t st);
+                           const int32_t* key_idx, const BwdWorkspace& w, hipStream_t st,
+                           const Geom* packed = nullptr);
 
 // Backward launchers: pass bit 1 = pass A (Delta, dQ; needs nothing from the
 // plan), bit 2 = pass B (dK, dV; needs pass A and the plan).

@@ -240,6 +240,15 @@ size_t cluster_attn_bwd_plan_workspace(int B, int N, int C, int cs, int nk);
 int cluster_attn_bwd_plan(int B, int N, int C, int cs, int nk, const int32_t* q_idx,
                           const int32_t* key_idx, void* plan, size_t plan_bytes,
                           void* hip_stream);
+/* The plan of a packed batch from its offsets (see
+ * cluster_attn_build_neighbors_varlen): one workgroup per image when every
+ * image has at most 4096 tokens, else the batch as one index space.  The
+ * plan has the size cluster_attn_bwd_plan_workspace(1, T, Ct, cs, nk) and
+ * feeds cluster_attn_bwd_planned with B = 1, N = T, C = Ct. */
+int cluster_attn_bwd_plan_varlen(int B, int T, int Ct, int max_n, const int32_t* tok_off,
+                                 const int32_t* clu_off, int cs, int nk, const int32_t* q_idx,
+                                 const int32_t* key_idx, void* plan, size_t plan_bytes,
+                                 void* hip_stream);
 size_t cluster_attn_bwd_planned_workspace(int dt, int B, int N, int H, int D);
 int cluster_attn_bwd_planned(int dt, int B, int N, int C, int H, int D, int cs, int nk,
                              float scale, const void* q, const void* k, const void* v,

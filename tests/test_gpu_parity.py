@@ -221,13 +221,15 @@ def test_holes_repeats_and_short_lists(ca, scale):
                 check_close(nm, g, r, t[2], rel)
 
 
-def test_grid_plan_random_lists(ca):
-    """Images above the single-workgroup plan limit (2304 tokens, 288
-    clusters) take the grid-wide transposition: random lists with -1
-    slots, repeated slots and groups that mix clusters (its per-slot path),
-    plus build-style lists of whole clusters (its grouped path)."""
+@pytest.mark.parametrize("N", [2304, 4608])
+def test_grid_plan_random_lists(ca, N):
+    """Images above the 2048-token in-LDS plan: 2304 tokens (288 clusters)
+    take the 4096-token in-LDS plan (multiplicities accumulated in global
+    memory), 4608 tokens the grid-wide transposition.  Random lists with -1
+    slots, repeated slots and groups that mix clusters (the per-slot paths),
+    plus build-style lists of whole clusters (the grouped paths)."""
     rng = np.random.default_rng(33)
-    B, N, H, D, nk = 2, 2304, 2, 32, 48
+    B, H, D, nk = 2, 2, 32, 48
     C = N // 8
     q_idx = np.stack([rng.permutation(N).reshape(-1, 8) for _ in range(B)]).astype(np.int32)
     key_rand = rng.integers(0, N, size=(B, C, nk)).astype(np.int32)
@@ -238,7 +240,7 @@ def test_grid_plan_random_lists(ca):
     key_grp[:, 7] = key_rand[:, 7]   # one cluster with mixed groups in a grouped image
     for name, key_idx in (("random", key_rand), ("grouped", key_grp)):
         for dt in (torch.bfloat16, torch.float32):
-            print(f"case grid plan {name} {dt}", flush=True)
+            print(f"case plan N={N} {name} {dt}", flush=True)
             q, k, v, do = (torch.randn(B, N, H, D, generator=torch.Generator().manual_seed(40 + s)).to(dt)
                            for s in range(4))
             scale = 0.2
@@ -353,7 +355,7 @@ def test_planned_backward_equals_backward(ca):
         torch.cuda.synchronize()
         for a, b in zip(ref, got):
             assert torch.equal(a, b)
-    for name in ("varlen_mixed", "varlen_tiny"):
+    for name in ("varlen_mixed", "varlen_tiny", "varlen"):
         case = make_varlen_case(name)
         print(f"case planned {name}", flush=True)
         q_idx, _, key_v, _, _ = ca.build_neighbors_varlen(torch.from_numpy(case["coords"]).to(DEV),
@@ -361,8 +363,10 @@ def test_planned_backward_equals_backward(ca):
         dev = [case[n].to(DEV) for n in ("q", "k", "v", "do")]
         o, lse = ca.fwd_varlen(dev[0], dev[1], dev[2], q_idx, key_v)
         plan = ca.bwd_plan(q_idx, key_v, dev[0].shape[0])
+        plan_img = ca.bwd_plan_varlen(q_idx, key_v, case["lengths"])   # one workgroup per image
         ref = ca.bwd_varlen(dev[0], dev[1], dev[2], o, dev[3], lse, q_idx, key_v)
-        got = ca.bwd_varlen(dev[0], dev[1], dev[2], o, dev[3], lse, q_idx, key_v, plan=plan)
-        torch.cuda.synchronize()
-        for a, b in zip(ref, got):
-            assert torch.equal(a, b)
+        for p in (plan, plan_img):
+            got = ca.bwd_varlen(dev[0], dev[1], dev[2], o, dev[3], lse, q_idx, key_v, plan=p)
+            torch.cuda.synchronize()
+            for a, b in zip(ref, got):
+                assert torch.equal(a, b)
