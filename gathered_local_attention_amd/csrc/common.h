@@ -41,6 +41,7 @@ struct BwdWorkspace {
   int32_t* cnt;      // [B, C]      entries per key cluster
   int2* seg;         // [B, C]      (start, end) of every key cluster's entries, absolute
   int32_t* cursor;   // [B, C]
+  int32_t* nent;     // [B, C]      entries staged per query cluster
   RevEntry* stage;   // [B, C, nk]  entry of the first slot of i pointing into j
   RevEntry* rev;     // [B, C*nk]   per key cluster, sorted by i (image b from b*C*nk)
   int32_t* rtok;     // [B, C*nk, cs] query tokens of entry e (q_idx row of its i)
@@ -77,6 +78,7 @@ static inline BwdWorkspace plan_layout(void* base, int64_t B, int64_t N, int64_t
   w.cnt = (int32_t*)c.take((size_t)(B * C) * sizeof(int32_t));
   w.seg = (int2*)c.take((size_t)(B * C) * sizeof(int2));
   w.cursor = (int32_t*)c.take((size_t)(B * C) * sizeof(int32_t));
+  w.nent = (int32_t*)c.take((size_t)(B * C) * sizeof(int32_t));
   w.stage = (RevEntry*)c.take((size_t)(B * C * nk) * sizeof(RevEntry));
   w.rev = (RevEntry*)c.take((size_t)(B * C * nk) * sizeof(RevEntry));
   w.rtok = (int32_t*)c.take((size_t)(B * C * nk) * 8 * sizeof(int32_t));
