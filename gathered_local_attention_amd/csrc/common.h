@@ -100,7 +100,6 @@ static inline BwdWorkspace bwd_layout(void* base, int64_t B, int64_t N, int64_t 
 // ---- workspace layout of the neighbour build ------------------------------
 constexpr int kSortChunk = 2048;   // images up to this many tokens: backward plan in LDS
 constexpr int kSmallBuild = 4096;  // images up to this many tokens are built in LDS
-constexpr int kRankSeg = 512;      // larger images: tokens ranked together before merging
 constexpr int kBoxTile = 64;       // consecutive clusters per bounding box
 constexpr int kIdxBits = 19;       // cluster index bits of a (distance, index) key
 constexpr int64_t kMaxTokensPerImage = int64_t(8) << kIdxBits;

@@ -18,9 +18,9 @@
 //                       (code, token) keys on the top code bits plus in-bucket
 //                       insertion sort, bitonic fallback; centroid sums
 //                       decoded from the sorted codes; 4-lane split scan).
-//   rank_kernel         larger images: rank of every token inside its
-//                       512-token segment (keys held in LDS).
-//   merge_round_kernel  pairwise merge of sorted runs (512, 1024, ... tokens):
+//   segsort_kernel      larger images: every 1024-token segment sorted in
+//                       LDS (a merge sort).
+//   merge_round_kernel  pairwise merge of sorted runs (1024, 2048, ... tokens):
 //                       a key's place is its place in its own run plus the
 //                       count of partner-run keys below it (binary search).
 //                       The last round writes the token order.
@@ -168,52 +168,6 @@ __device__ __forceinline__ void get(float4 v, float (&a)[3]) { a[0] = v.x; a[1] 
 
 template <int DIM> __device__ __forceinline__ uint64_t tok_mask() {
   return (uint64_t(1) << Space<DIM>::kTokBits) - 1;
-}
-
-// Rank the tokens of one segment.  grid = (kRankSeg / 64, B * segs), where
-// segment `seg % segs` of image `seg / segs` is [start, start + L) of that
-// image.  Each workgroup ranks 64 tokens (one per lane); its four
-// wavefronts each count one quarter of the segment's keys, read from LDS as
-// broadcast 16-byte loads.  The keys land sorted inside their segment.
-template <int DIM>
-__global__ void __launch_bounds__(kRankThreads)
-rank_kernel(const float* __restrict__ coords, Geom g, int segs_per_image, double step,
-            uint64_t* __restrict__ run_keys) {
-  __shared__ __align__(16) uint64_t keys[kRankSeg];
-  __shared__ int part[kRankThreads / 64][64];
-  const int seg = blockIdx.y;
-  const int b = seg / segs_per_image;
-  const int start = (seg % segs_per_image) * kRankSeg;
-  int t0, n, c0, nc;
-  g.image(b, t0, n, c0, nc);
-  if (n <= g.small_max) return;                       // built by the in-LDS kernel
-  const int L = min(kRankSeg, n - start);
-  if (L <= 0) return;
-  const float* img = coords + ((int64_t)t0 + start) * DIM;
-
-  for (int e = threadIdx.x; e < L; e += kRankThreads)
-    keys[e] = (Space<DIM>::code(img, e, step) << Space<DIM>::kTokBits) | (uint32_t)(start + e);
-  if (threadIdx.x == 0 && (L & 1)) keys[L] = ~0ull;   // pad to an even count
-  __syncthreads();
-
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int e = blockIdx.x * 64 + lane;
-  const uint64_t mine = e < L ? keys[e] : ~0ull;
-  const int Le = (L + 1) & ~1;                        // even, padding key is the maximum
-  const int per = ((Le / 4) + 1) & ~1;
-  const int u0 = min(Le, w * per), u1 = (w == 3) ? Le : min(Le, (w + 1) * per);
-  int cnt = 0;
-  const ulonglong2* k2 = reinterpret_cast<const ulonglong2*>(keys);
-#pragma unroll 8
-  for (int u = u0; u < u1; u += 2) {
-    const ulonglong2 kk = k2[u >> 1];
-    cnt += (kk.x < mine) + (kk.y < mine);
-  }
-  part[w][lane] = cnt;
-  __syncthreads();
-  if (w != 0 || e >= L) return;
-  const int rank = part[0][lane] + part[1][lane] + part[2][lane] + part[3][lane];
-  run_keys[(int64_t)t0 + start + rank] = mine;
 }
 
 // One round of the image-wide merge sort.  Sorted runs of `run` keys (a
@@ -558,8 +512,7 @@ select_box_kernel(Geom g, const typename Space<DIM>::FCent* __restrict__ cent_al
 // ---------------------------------------------------------------------------
 constexpr int kSmallThreads = 1024;
 
-constexpr int kBuckets = 2 * kSmallThreads;       // counting-sort buckets (top 11 key bits)
-constexpr int kBucketShift = 53;
+constexpr int kBuckets = 2 * kSmallThreads;       // counting-sort buckets (11 key bits)
 constexpr int kMaxBucket = 32;                    // larger buckets -> bitonic fallback
 
 __device__ __forceinline__ int64_t sq_dist(int2 a, int2 b) {
@@ -569,6 +522,157 @@ __device__ __forceinline__ int64_t sq_dist(int2 a, int2 b) {
 __device__ __forceinline__ int64_t sq_dist(int4 a, int4 b) {
   const int dx = a.x - b.x, dy = a.y - b.y, dz = a.z - b.z;
   return (int64_t)dx * dx + (int64_t)dy * dy + (int64_t)dz * dz;
+}
+
+// Sort up to KPT * 1024 (code << token bits | token) keys of a whole image
+// in LDS, KPT per thread (kk, ~0 past the end), into keys[0 .. n).
+// Counting sort on the top 11 key bits (2048 buckets), then an insertion
+// sort inside each bucket restores the exact order whatever the arrival
+// order of the atomics.  Buckets hold about one key for the grid-like
+// layouts of the workloads; if any bucket exceeds kMaxBucket keys the
+// workgroup falls back to a bitonic sort.  Ends with a barrier.
+constexpr int kBucketShift = 53;
+
+template <int KPT>
+__device__ __forceinline__ void lds_sort_keys(const uint64_t (&kk)[KPT], int n, uint64_t* keys,
+                                              int* bcnt, int* bstart, int* scan_tmp,
+                                              int* overflow) {
+  const int tid = threadIdx.x;
+  int bk[KPT], arr[KPT];
+#pragma unroll
+  for (int r = 0; r < KPT; ++r)
+    bk[r] = tid + r * kSmallThreads < n ? (int)(kk[r] >> kBucketShift) : -1;
+  bcnt[tid] = 0;
+  bcnt[tid + kSmallThreads] = 0;
+  if (tid == 0) *overflow = 0;
+  __syncthreads();
+#pragma unroll
+  for (int r = 0; r < KPT; ++r) arr[r] = bk[r] >= 0 ? atomicAdd(&bcnt[bk[r]], 1) : 0;
+  __syncthreads();
+  const int c0 = bcnt[2 * tid], c1 = bcnt[2 * tid + 1];
+  if (c0 > kMaxBucket || c1 > kMaxBucket) *overflow = 1;
+  int total;
+  const int ex = block_exclusive_scan(c0 + c1, scan_tmp, kSmallThreads, &total);
+  bstart[2 * tid] = ex;
+  bstart[2 * tid + 1] = ex + c0;
+  __syncthreads();
+  if (!*overflow) {
+#pragma unroll
+    for (int r = 0; r < KPT; ++r)
+      if (bk[r] >= 0) keys[bstart[bk[r]] + arr[r]] = kk[r];
+    __syncthreads();
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int s0 = h ? ex + c0 : ex, m = h ? c1 : c0;
+      for (int x = 1; x < m; ++x) {
+        const uint64_t key = keys[s0 + x];
+        int y = x - 1;
+        while (y >= 0 && keys[s0 + y] > key) {
+          keys[s0 + y + 1] = keys[s0 + y];
+          --y;
+        }
+        keys[s0 + y + 1] = key;
+      }
+    }
+  } else {
+    int P = 2;
+    while (P < n) P <<= 1;
+#pragma unroll
+    for (int r = 0; r < KPT; ++r) {
+      const int e = tid + r * kSmallThreads;
+      if (e < P) keys[e] = kk[r];
+    }
+    __syncthreads();
+    for (int k = 2; k <= P; k <<= 1) {
+      for (int j = k >> 1; j > 0; j >>= 1) {
+        for (int i = tid; i < P / 2; i += kSmallThreads) {
+          const int a = ((i & ~(j - 1)) << 1) | (i & (j - 1));
+          const uint64_t x = keys[a], y = keys[a + j];
+          if ((x > y) == ((a & k) == 0)) {
+            keys[a] = y;
+            keys[a + j] = x;
+          }
+        }
+        __syncthreads();
+      }
+    }
+  }
+  __syncthreads();
+}
+
+// Larger images: every run of kSegSort consecutive tokens sorted in LDS.
+// A segment of a large image covers a narrow strip of its space, so a
+// counting sort on fixed key bits would crowd few buckets; this is a merge
+// sort instead: each thread sorts its four keys, then eight rounds merge
+// sorted runs pairwise (a key's place = its place in its run + the number
+// of partner-run keys below it, by binary search in LDS; keys are unique;
+// positions past the segment's L keys are never read).
+// grid = (B * segs), one 256-thread workgroup per 1024-key segment; the
+// sorted runs go to run_keys at the segment's place.
+constexpr int kSegThreads = 256;
+constexpr int kSegSort = 4 * kSegThreads;   // keys per segment
+
+template <int DIM>
+__global__ void __launch_bounds__(kSegThreads)
+segsort_kernel(const float* __restrict__ coords, Geom g, int segs_per_image, double step,
+               uint64_t* __restrict__ run_keys) {
+  __shared__ uint64_t buf[2][kSegSort];
+  const int b = blockIdx.x / segs_per_image;
+  const int start = (blockIdx.x % segs_per_image) * kSegSort;
+  int t0, n, c0, nc;
+  g.image(b, t0, n, c0, nc);
+  if (n <= g.small_max) return;                       // built by the in-LDS kernel
+  const int L = min(kSegSort, n - start);
+  if (L <= 0) return;
+  const float* img = coords + ((int64_t)t0 + start) * DIM;
+  const int tid = threadIdx.x;
+  // this thread's four consecutive keys (padding ~0 sorts last), sorted
+  uint64_t k[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int e = 4 * tid + r;
+    k[r] = e < L ? (Space<DIM>::code(img, e, step) << Space<DIM>::kTokBits) | (uint32_t)(start + e)
+                 : ~0ull;
+  }
+  auto cswap = [](uint64_t& a, uint64_t& c) {
+    const uint64_t lo = a < c ? a : c, hi = a < c ? c : a;
+    a = lo;
+    c = hi;
+  };
+  cswap(k[0], k[1]);
+  cswap(k[2], k[3]);
+  cswap(k[0], k[2]);
+  cswap(k[1], k[3]);
+  cswap(k[1], k[2]);
+#pragma unroll
+  for (int r = 0; r < 4; ++r) buf[0][4 * tid + r] = k[r];
+  __syncthreads();
+  int cur = 0;
+  for (int run = 4; run < kSegSort; run *= 2) {
+    const uint64_t* in = buf[cur];
+    uint64_t* out = buf[cur ^ 1];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int x = 4 * tid + r;
+      if (x >= L) continue;   // positions past the segment's keys take no part
+      const uint64_t key = in[x];
+      const int p0 = x & ~(2 * run - 1);
+      const bool first = x - p0 < run;
+      int lo = first ? p0 + run : p0;
+      int hi = first ? min(p0 + 2 * run, L) : p0 + run;
+      hi = max(hi, lo);   // a last run without partner
+      const int base = lo;
+      while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (in[mid] < key) lo = mid + 1; else hi = mid;
+      }
+      out[p0 + (x - (first ? p0 : p0 + run)) + (lo - base)] = key;
+    }
+    cur ^= 1;
+    __syncthreads();
+  }
+  uint64_t* dst = run_keys + (int64_t)t0 + start;
+  for (int e = tid; e < L; e += kSegThreads) dst[e] = buf[cur][e];
 }
 
 template <int KM1, int KPT, int DIM>
@@ -593,80 +697,14 @@ build_small_kernel(const float* __restrict__ coords, Geom g, double step, int pa
   const int tb = g.tok_base(t0), cb = g.clu_base(cl0);
   const float* img = coords + (int64_t)t0 * DIM;
 
-  // Sort the (code << kTokBits | token) keys.  Counting sort on the top 11
-  // key bits (2048 buckets; KPT keys per thread), then an insertion sort
-  // inside each bucket restores the exact (code, token) order whatever the
-  // arrival order of the atomics.  Buckets hold about one key for the
-  // grid-like layouts of the workloads; if any bucket exceeds kMaxBucket
-  // keys the workgroup falls back to an LDS bitonic sort.
+  // sort the (code << kTokBits | token) keys in LDS
   uint64_t kk[KPT];
-  int bk[KPT], arr[KPT];
 #pragma unroll
   for (int r = 0; r < KPT; ++r) {
     const int e = tid + r * kSmallThreads;
-    kk[r] = ~0ull;
-    bk[r] = -1;
-    if (e < N) {
-      kk[r] = (S::code(img, e, step) << S::kTokBits) | (uint32_t)e;
-      bk[r] = (int)(kk[r] >> kBucketShift);
-    }
+    kk[r] = e < N ? (S::code(img, e, step) << S::kTokBits) | (uint32_t)e : ~0ull;
   }
-  bcnt[tid] = 0;
-  bcnt[tid + kSmallThreads] = 0;
-  if (tid == 0) overflow = 0;
-  __syncthreads();
-#pragma unroll
-  for (int r = 0; r < KPT; ++r) arr[r] = bk[r] >= 0 ? atomicAdd(&bcnt[bk[r]], 1) : 0;
-  __syncthreads();
-  const int c0 = bcnt[2 * tid], c1 = bcnt[2 * tid + 1];
-  if (c0 > kMaxBucket || c1 > kMaxBucket) overflow = 1;
-  int total;
-  const int ex = block_exclusive_scan(c0 + c1, scan_tmp, kSmallThreads, &total);
-  bstart[2 * tid] = ex;
-  bstart[2 * tid + 1] = ex + c0;
-  __syncthreads();
-  if (!overflow) {
-#pragma unroll
-    for (int r = 0; r < KPT; ++r)
-      if (bk[r] >= 0) keys[bstart[bk[r]] + arr[r]] = kk[r];
-    __syncthreads();
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int s0 = h ? ex + c0 : ex, n = h ? c1 : c0;
-      for (int x = 1; x < n; ++x) {
-        const uint64_t key = keys[s0 + x];
-        int y = x - 1;
-        while (y >= 0 && keys[s0 + y] > key) {
-          keys[s0 + y + 1] = keys[s0 + y];
-          --y;
-        }
-        keys[s0 + y + 1] = key;
-      }
-    }
-  } else {
-    int P = 2;
-    while (P < N) P <<= 1;
-#pragma unroll
-    for (int r = 0; r < KPT; ++r) {
-      const int e = tid + r * kSmallThreads;
-      if (e < P) keys[e] = kk[r];
-    }
-    __syncthreads();
-    for (int k = 2; k <= P; k <<= 1) {
-      for (int j = k >> 1; j > 0; j >>= 1) {
-        for (int i = tid; i < P / 2; i += kSmallThreads) {
-          const int a = ((i & ~(j - 1)) << 1) | (i & (j - 1));
-          const uint64_t x = keys[a], y = keys[a + j];
-          if ((x > y) == ((a & k) == 0)) {
-            keys[a] = y;
-            keys[a + j] = x;
-          }
-        }
-        __syncthreads();
-      }
-    }
-  }
-  __syncthreads();
+  lds_sort_keys<KPT>(kk, N, keys, bcnt, bstart, scan_tmp, &overflow);
 
   // centroid sums decoded from the sorted codes, scaled to compare means
   for (int c = tid; c < C; c += kSmallThreads) {
@@ -827,12 +865,12 @@ hipError_t build_t(const float* coords, const Geom& geom, int B, int64_t T, int6
   // larger images: segment ranks, merge rounds, centroids and boxes, selection
   typedef typename S::Packed P;
   typedef typename S::FCent FC;
-  const int segs = (N + kRankSeg - 1) / kRankSeg;
-  hipLaunchKernelGGL(rank_kernel<DIM>, dim3(kRankSeg / 64, B * segs), dim3(kRankThreads), 0, st,
-                     coords, g, segs, step, w.keys[0]);
+  const int segs = (N + kSegSort - 1) / kSegSort;
+  hipLaunchKernelGGL(segsort_kernel<DIM>, dim3(B * segs), dim3(kSegThreads), 0, st, coords, g,
+                     segs, step, w.keys[0]);
   int cur = 0;
   const dim3 mgrid((N + kRankThreads - 1) / kRankThreads, B);
-  for (int run = kRankSeg; run < N; run *= 2) {
+  for (int run = kSegSort; run < N; run *= 2) {
     const bool last = 2 * run >= N;
     hipLaunchKernelGGL(merge_round_kernel<DIM>, mgrid, dim3(kRankThreads), 0, st, g, run,
                        (const uint64_t*)w.keys[cur], last ? nullptr : w.keys[cur ^ 1], q_idx,
