@@ -573,14 +573,39 @@ knn_bwd_query_kernel(int N, int M, int Cf, int G, int K, int lg, float p, int64_
   for (int o = 1; o < 64; o <<= 1) sdp += __shfl_xor(sdp, o, 64);
   if (lane == 0) dpart[base / qwv] = sdp;
   // the entries' counts per partition of kPart entries and token (integer
-  // atomics, order independent), last: nothing in this wave waits on them
-  if (mine) {
+  // atomics, order independent), last: nothing in this wave waits on them;
+  // without pcnt they are counted by knn_pcount_kernel instead
+  if (mine && pcnt) {
     const int64_t b = id / M;
     const int64_t e0 = (id - b * M) * K;   // first entry of this query in its image
 #pragma unroll
     for (int k = 0; k < KM; ++k)
       if (k < K && qw.slot[k] >= 0) atomicAdd(&pcnt[(b * P + (e0 + k) / kPart) * N + qw.slot[k]], 1);
   }
+}
+
+// Per partition of kPart entries, the count of its entries per token,
+// accumulated in LDS (images of at most kTabMaxTokens tokens) and written
+// out whole (zeros included): one workgroup per partition.
+__global__ void __launch_bounds__(kKnnThreads)
+knn_pcount_kernel(int N, int64_t MK, int P, const int32_t* __restrict__ ent_slot,
+                  int32_t* __restrict__ pcnt) {
+  static_assert(kPart == kKnnThreads, "one entry per thread");
+  __shared__ int32_t c[kTabMaxTokens];
+  const int64_t part = blockIdx.x;
+  const int64_t b = part / P;
+  const int s = (int)(part - b * P);
+  const int64_t e0 = (int64_t)s * kPart;
+  const int n = (int)min((int64_t)kPart, MK - e0);
+  for (int t = threadIdx.x; t < N; t += kKnnThreads) c[t] = 0;
+  __syncthreads();
+  if ((int)threadIdx.x < n) {
+    const int t = ent_slot[b * MK + e0 + threadIdx.x];
+    if (t >= 0) atomicAdd(&c[t], 1);
+  }
+  __syncthreads();
+  int32_t* row = pcnt + (b * P + s) * N;
+  for (int t = threadIdx.x; t < N; t += kKnnThreads) row[t] = c[t];
 }
 
 __global__ void __launch_bounds__(kKnnThreads)
@@ -632,7 +657,8 @@ knn_scan_kernel(int N, const int32_t* __restrict__ cnt_all, int32_t* __restrict_
 // stable counting sort.  The entries of an image are cut into partitions of
 // kPart consecutive entries: (1) per partition and token, the count of its
 // entries (integer atomics in the query-major kernel: the counts do not
-// depend on their order); (2) per token, the counts turned into exclusive
+// depend on their order), or per partition in LDS (knn_pcount_kernel) when
+// the image fits; (2) per token, the counts turned into exclusive
 // prefixes over the partitions, and the token's total; (3) the totals
 // scanned into segment starts (knn_scan_kernel); (4) per partition, every
 // entry placed at segment start + the partition's prefix + the number of
@@ -918,18 +944,25 @@ hipError_t bwd_t(int B, int N, int M, int Cf, int G, int K, float p, const float
   const int P = (int)((MK + kPart - 1) / kPart);
   const int64_t npc = (int64_t)B * P * N, nparts = (int64_t)B * P;
   const int qwv = queries_per_wave(lg);
+  // partition counts: in LDS per partition for images that fit, else by
+  // integer atomics in the query-major kernel into zeroed counters
+  const bool lds_count = N <= kTabMaxTokens;
   auto go = [&](auto kern) {
     hipLaunchKernelGGL(kern, dim3(blocks_for(nq, qwv)), dim3(kKnnThreads), 0, st, N, M, Cf, G, K,
                        lg, p, nq, qwv, coords, (const T*)feats, queries, table, (const T*)dout, dq,
-                       w.dpart, w.slot, w.wgt, P, w.pcnt);
+                       w.dpart, w.slot, w.wgt, P, lds_count ? nullptr : w.pcnt);
   };
   // empty sizes launch nothing but what writes outputs (dF, dp)
-  if (npc > 0) hipLaunchKernelGGL(knn_zero_kernel, grid1(npc), dim3(kKnnThreads), 0, st, npc, w.pcnt);
+  if (npc > 0 && !lds_count)
+    hipLaunchKernelGGL(knn_zero_kernel, grid1(npc), dim3(kKnnThreads), 0, st, npc, w.pcnt);
   if (nq > 0) {
     if (K <= 4) go(knn_bwd_query_kernel<T, 4>);
     else if (K <= 8) go(knn_bwd_query_kernel<T, 8>);
     else go(knn_bwd_query_kernel<T, 16>);
   }
+  if (npc > 0 && lds_count)
+    hipLaunchKernelGGL(knn_pcount_kernel, dim3((unsigned)nparts), dim3(kKnnThreads), 0, st, N, MK,
+                       P, (const int32_t*)w.slot, w.pcnt);
   if (ntok > 0) {
     hipLaunchKernelGGL(knn_pprefix_kernel, grid1(ntok), dim3(kKnnThreads), 0, st, N, P, ntok,
                        w.pcnt, w.cnt);
