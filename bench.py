@@ -48,7 +48,8 @@ SAMPLER_ENTRY_KERNELS = {
     "table": ["knn_table_kernel"],
     "fwd": ["knn_fwd_kernel"],
     "bwd": ["knn_zero_kernel", "knn_bwd_query_kernel", "knn_pprefix_kernel", "knn_scan_kernel",
-            "knn_pplace_kernel", "knn_order_kernel", "knn_dfeat_kernel", "knn_dp_kernel"],
+            "knn_pplace_kernel", "knn_order_kernel", "knn_dfeat_kernel", "knn_dp_kernel",
+            "knn_pcount_kernel"],
 }
 BF16_MFMA_PEAK_TFLOPS = 2500.0  # dense
 
