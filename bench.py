@@ -42,7 +42,7 @@ ENTRY_KERNELS = {
     "fwd": ["fwd_lds_kernel"],
     "bwd": ["bwd_q_lds_kernel", "bwd_kv_lds_kernel"],
 }
-MERGE_ENTRY_KERNELS = {"plan": ["merge_plan_kernel"], "fwd": ["merge_fwd_kernel"],
+MERGE_ENTRY_KERNELS = {"plan": ["merge_assign_kernel", "merge_members_kernel"], "fwd": ["merge_fwd_kernel"],
                        "bwd": ["merge_bwd_kernel"]}
 SAMPLER_ENTRY_KERNELS = {
     "table": ["knn_table_kernel"],

@@ -18,13 +18,15 @@
 //   backward  gradients of F, X and the scores (anchors, assignment fixed).
 //
 // Kernels:
-//   merge_plan_kernel  one workgroup per image (up to 4096 tokens, all in
-//                      LDS): top-k by a radix select of the score keys,
-//                      anchors by a workgroup scan in token order, nearest
-//                      anchors by a ring search over a bucket grid of the
-//                      anchors (exact int64 keys), and the groups' member
-//                      lists by a counting sort on the anchor, each group
-//                      then sorted by token index.
+//   merge_assign_kernel  up to 8 workgroups per image (up to 4096 tokens,
+//                      all in LDS; each workgroup repeats the selection):
+//                      top-k by a radix select of the score keys, anchors
+//                      by a workgroup scan in token order, and for its slice
+//                      of the tokens the nearest anchor by a ring search over
+//                      a bucket grid of the anchors (exact int64 keys).
+//   merge_members_kernel one workgroup per image: the groups' member lists
+//                      by a counting sort on the anchor, each group then
+//                      sorted by token index.
 //   merge_fwd_kernel   a lane group per anchor (16 bytes of the row per
 //                      lane): the group's softmax, then the weighted sums.
 //   merge_bwd_kernel   the same groups: g_i = <dF'_a, F_i> + <dX'_a, X_i>
@@ -42,6 +44,7 @@ namespace {
 constexpr int kPlanT = 1024;
 constexpr int kMaxTok = 4096;
 constexpr int kMergeThreads = 256;
+constexpr int kRingLanes = 4;   // lanes per token in the nearest-anchor search
 
 typedef float mf32x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 mbf16x8 __attribute__((ext_vector_type(8)));
@@ -77,18 +80,18 @@ template <> struct Row16<f16> : Row16Half<f16, mf16x8> {};
 constexpr int kMaxChunks = 4;   // chunks of 16 bytes per lane (1024 channels of f32)
 
 // ---------------------------------------------------------------------------
-// Plan: anchors, assignment, member lists.  grid = B, 1024 threads, the
-// image in LDS.
+// Plan: anchors, assignment, member lists.  Assignment grid = B x S
+// workgroups of 1024 threads, the image in LDS:
 //  1. top-k by a radix select on order-preserving 32-bit keys of the scores
 //     (8-bit digits from the top): the k-th largest key, then the tokens
 //     above it and the first ones (in token order) equal to it;
 //  2. anchor positions by a workgroup scan in token order;
 //  3. the anchors bucketed on a coarse grid (about two per bucket); every
-//     other token searches rings of buckets around its own until its best
-//     is strictly closer than anything outside the searched window can be;
-//  4. member lists by a counting sort on the anchor (LDS atomics), each
-//     group's members then sorted by token index (a thread per group when
-//     no group exceeds 32 tokens, else a bitonic sort of all the keys).
+//     other token of the workgroup's slice searches rings of buckets around
+//     its own until its best is strictly closer than anything outside the
+//     searched window can be;
+//  4. (members kernel) member lists by a counting sort on the anchor (LDS
+//     atomics), each group's members then sorted by token index.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ uint32_t score_key(float x) {
   // larger float -> larger key; -0 and +0 share one key (they compare equal)
@@ -97,19 +100,18 @@ __device__ __forceinline__ uint32_t score_key(float x) {
 }
 
 __global__ void __launch_bounds__(kPlanT)
-merge_plan_kernel(const float* __restrict__ coords, const float* __restrict__ scores, int N, int k,
-                  int G, int32_t* __restrict__ anchors, int32_t* __restrict__ assign,
-                  int32_t* __restrict__ members, int32_t* __restrict__ offsets) {
+merge_assign_kernel(const float* __restrict__ coords, const float* __restrict__ scores, int N,
+                    int k, int G, int S, int32_t* __restrict__ anchors,
+                    int32_t* __restrict__ assign) {
   __shared__ uint32_t sk[kMaxTok];                    // score keys
   __shared__ uint32_t qc[kMaxTok];                    // token fixed-point (qx | qy << 16)
   __shared__ int32_t apos[kMaxTok];                   // token -> anchor position, or -1
   __shared__ uint2 abk[kMaxTok];                      // anchors in bucket order: (qc, position)
   __shared__ int32_t bstart[kMaxTok];                 // bucket starts (<= 4096 buckets)
-  __shared__ uint32_t key[kMaxTok];                   // group counts, then sort keys
   __shared__ int hist[256];
   __shared__ uint32_t sel[2];                         // selected prefix, still wanted
   __shared__ int tmp[17];
-  const int b = blockIdx.x, tid = threadIdx.x;
+  const int b = blockIdx.x / S, slice = blockIdx.x % S, tid = threadIdx.x;
   const int bits = [&] { int v = 0; while ((1 << v) < G) ++v; return v; }();
   const double step = (double)(1u << (16 - bits));
   const float* s = scores + (int64_t)b * N;
@@ -189,7 +191,8 @@ merge_plan_kernel(const float* __restrict__ coords, const float* __restrict__ sc
     const int i = tid * R + r;
     if (i < N) {
       apos[i] = an[r] ? pos : -1;
-      if (an[r]) anchors[(int64_t)b * k + pos++] = i;
+      if (an[r] && slice == 0) anchors[(int64_t)b * k + pos] = i;
+      pos += an[r] ? 1 : 0;
     }
   }
   // 3. anchors bucketed: side 2^bsh fixed-point units, about two per bucket
@@ -233,18 +236,13 @@ merge_plan_kernel(const float* __restrict__ coords, const float* __restrict__ sc
     if (abkt[r] >= 0) abk[bstart[abkt[r]] + arank[r]] = make_uint2(qc[i], (uint32_t)apos[i]);
   }
   __syncthreads();
-  // nearest anchor of every other token: rings of buckets around its own;
-  // keys (d2 << 12 | position) exact in 64 bits
-  int ga[R], gslot[R];
-#pragma unroll
-  for (int r = 0; r < R; ++r) ga[r] = -1;
-  __syncthreads();   // key[] holds the group counts below
-  for (int x = tid; x < k; x += kPlanT) key[x] = 0u;
-  __syncthreads();
-#pragma unroll
-  for (int r = 0; r < R; ++r) {
-    const int i = tid + r * kPlanT;
-    if (i >= N) break;
+  // nearest anchor of the slice's tokens: rings of buckets around its own,
+  // kRingLanes lanes per token sharing each ring's buckets (group minimum
+  // after every ring, so the stop test is the same on all of them); keys
+  // (d2 << 12 | position) exact in 64 bits
+  const int per = (N + S - 1) / S, i0 = slice * per, i1 = min(N, i0 + per);
+  const int u = tid % kRingLanes;
+  for (int i = i0 + tid / kRingLanes; i < i1; i += kPlanT / kRingLanes) {
     int a = apos[i];
     if (a < 0) {
       const uint32_t q = qc[i];
@@ -252,38 +250,79 @@ merge_plan_kernel(const float* __restrict__ coords, const float* __restrict__ sc
       const int bx0 = (int)(x >> bsh), by0 = (int)(y >> bsh);
       uint64_t best = ~0ull;
       for (int Rg = 0; Rg < Pb; ++Rg) {
-        const int y0 = by0 - Rg, y1 = by0 + Rg;
-        for (int by = max(y0, 0); by <= min(y1, Pb - 1); ++by) {
-          const bool edge = by == y0 || by == y1;
-          const int dxs = (edge || Rg == 0) ? 1 : 2 * Rg;
-          for (int bx = bx0 - Rg; bx <= bx0 + Rg; bx += dxs) {
-            if (bx < 0 || bx >= Pb) continue;
-            const int bb = by * Pb + bx;
-            const int t0 = bstart[bb], t1 = bb + 1 < nb ? bstart[bb + 1] : k;
-            for (int t = t0; t < t1; ++t) {
-              const uint2 e = abk[t];
-              const int64_t ix = (int64_t)(e.x & 0xFFFFu) - x, iy = (int64_t)(e.x >> 16) - y;
-              const uint64_t kk = ((uint64_t)(ix * ix + iy * iy) << 12) | e.y;
-              best = kk < best ? kk : best;
-            }
+        const int y0 = by0 - Rg, y1 = by0 + Rg, x0 = bx0 - Rg, x1 = bx0 + Rg;
+        // ring Rg holds 8 Rg buckets (one for Rg = 0): the top row, the
+        // bottom row, then the two side columns alternately
+        const int nring = Rg == 0 ? 1 : 8 * Rg, w = 2 * Rg + 1;
+        for (int j = u; j < nring; j += kRingLanes) {
+          int by, bx;
+          if (j < w) {
+            by = y0;
+            bx = x0 + j;
+          } else if (j < 2 * w) {
+            by = y1;
+            bx = x0 + j - w;
+          } else {
+            const int m = j - 2 * w;
+            by = y0 + 1 + (m >> 1);
+            bx = (m & 1) ? x1 : x0;
           }
+          if (bx < 0 || bx >= Pb || by < 0 || by >= Pb) continue;
+          const int bb = by * Pb + bx;
+          const int t0 = bstart[bb], t1 = bb + 1 < nb ? bstart[bb + 1] : k;
+          for (int t = t0; t < t1; ++t) {
+            const uint2 e = abk[t];
+            const int64_t ix = (int64_t)(e.x & 0xFFFFu) - x, iy = (int64_t)(e.x >> 16) - y;
+            const uint64_t kk = ((uint64_t)(ix * ix + iy * iy) << 12) | e.y;
+            best = kk < best ? kk : best;
+          }
+        }
+#pragma unroll
+        for (int m = 1; m < kRingLanes; m <<= 1) {
+          const uint64_t o = ((uint64_t)(uint32_t)__shfl_xor((int)(best >> 32), m) << 32) |
+                             (uint32_t)__shfl_xor((int)(uint32_t)best, m);
+          best = o < best ? o : best;
         }
         // a token outside the searched window lies beyond one of its edges
         int64_t lb = INT64_MAX;
         if (y0 > 0) lb = min(lb, y - ((int64_t)y0 << bsh) + 1);
         if (y1 < Pb - 1) lb = min(lb, ((int64_t)(y1 + 1) << bsh) - y);
-        if (bx0 - Rg > 0) lb = min(lb, x - ((int64_t)(bx0 - Rg) << bsh) + 1);
-        if (bx0 + Rg < Pb - 1) lb = min(lb, ((int64_t)(bx0 + Rg + 1) << bsh) - x);
+        if (x0 > 0) lb = min(lb, x - ((int64_t)x0 << bsh) + 1);
+        if (x1 < Pb - 1) lb = min(lb, ((int64_t)(x1 + 1) << bsh) - x);
         if (best != ~0ull && (lb == INT64_MAX || (int64_t)(best >> 12) < lb * lb)) break;
       }
       a = (int)(best & 0xFFFu);
     }
-    assign[(int64_t)b * N + i] = a;
-    ga[r] = a;
-    gslot[r] = (int)atomicAdd(&key[a], 1u);   // arrival order; fixed by the sort below
+    if (u == 0) assign[(int64_t)b * N + i] = a;
   }
-  // 4. members: group starts by a scan of the counts, members placed in
-  //    arrival order, then every group's few members sorted by token index
+}
+
+// Member lists of every image from the assignment.  grid = B, 1024 threads:
+// group sizes by LDS counters, group starts by a scan, members placed in
+// arrival order, then every group's members sorted by token index (a thread
+// per group when no group exceeds 32 tokens, else a bitonic sort of all the
+// (group, token) keys).
+__global__ void __launch_bounds__(kPlanT)
+merge_members_kernel(int N, int k, const int32_t* __restrict__ assign,
+                     int32_t* __restrict__ members, int32_t* __restrict__ offsets) {
+  __shared__ uint32_t key[kMaxTok];                   // group counts, then sort keys
+  __shared__ int32_t gstart[kMaxTok];
+  __shared__ uint32_t tok[kMaxTok];
+  __shared__ int tmp[17];
+  constexpr int R = kMaxTok / kPlanT;
+  const int b = blockIdx.x, tid = threadIdx.x;
+  for (int x = tid; x < k; x += kPlanT) key[x] = 0u;
+  __syncthreads();
+  int ga[R], gslot[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int i = tid + r * kPlanT;
+    ga[r] = -1;
+    if (i < N) {
+      ga[r] = assign[(int64_t)b * N + i];
+      gslot[r] = (int)atomicAdd(&key[ga[r]], 1u);   // arrival order; fixed by the sort below
+    }
+  }
   __syncthreads();
   int gc[R];
   int grun = 0;
@@ -294,13 +333,14 @@ merge_plan_kernel(const float* __restrict__ coords, const float* __restrict__ sc
     grun += gc[r];
   }
   __syncthreads();
+  int tot;
   int gacc = block_exclusive_scan(grun, tmp, kPlanT, &tot);
   int32_t* off = offsets + (int64_t)b * (k + 1);
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     const int x = tid * R + r;
     if (x < k) {
-      bstart[x] = gacc;   // bucket starts are no longer needed
+      gstart[x] = gacc;
       off[x] = gacc;
     }
     gacc += gc[r];
@@ -309,7 +349,7 @@ merge_plan_kernel(const float* __restrict__ coords, const float* __restrict__ sc
   __syncthreads();
 #pragma unroll
   for (int r = 0; r < R; ++r)
-    if (ga[r] >= 0) sk[bstart[ga[r]] + gslot[r]] = (uint32_t)(tid + r * kPlanT);   // score keys are done
+    if (ga[r] >= 0) tok[gstart[ga[r]] + gslot[r]] = (uint32_t)(tid + r * kPlanT);
   __syncthreads();
   int32_t* mem = members + (int64_t)b * N;
   int gmax = 0;
@@ -341,17 +381,17 @@ merge_plan_kernel(const float* __restrict__ coords, const float* __restrict__ sc
     return;
   }
   for (int g = tid; g < k; g += kPlanT) {
-    const int g0 = bstart[g], g1 = g + 1 < k ? bstart[g + 1] : N;
+    const int g0 = gstart[g], g1 = g + 1 < k ? gstart[g + 1] : N;
     for (int u = g0 + 1; u < g1; ++u) {   // insertion sort of at most 32 tokens
-      const uint32_t v = sk[u];
+      const uint32_t v = tok[u];
       int y = u - 1;
-      while (y >= g0 && sk[y] > v) {
-        sk[y + 1] = sk[y];
+      while (y >= g0 && tok[y] > v) {
+        tok[y + 1] = tok[y];
         --y;
       }
-      sk[y + 1] = v;
+      tok[y + 1] = v;
     }
-    for (int u = g0; u < g1; ++u) mem[u] = (int32_t)sk[u];
+    for (int u = g0; u < g1; ++u) mem[u] = (int32_t)tok[u];
   }
 }
 
@@ -587,8 +627,13 @@ hipError_t bwd_t(int B, int N, int k, int Cf, const void* feats, const float* co
 hipError_t launch_merge_plan(const float* coords, const float* scores, int B, int N, int k, int G,
                              int32_t* anchors, int32_t* assign, int32_t* members,
                              int32_t* offsets, hipStream_t st) {
-  hipLaunchKernelGGL(merge_plan_kernel, dim3(B), dim3(kPlanT), 0, st, coords, scores, N, k, G,
-                     anchors, assign, members, offsets);
+  // the ring search of an image is spread over S workgroups (each repeats the
+  // selection and the bucketing) so that a batch fills the chip
+  const int S = std::max(1, std::min({8, (N + 255) / 256, std::max(1, 256 / std::max(B, 1))}));
+  hipLaunchKernelGGL(merge_assign_kernel, dim3(B * S), dim3(kPlanT), 0, st, coords, scores, N, k,
+                     G, S, anchors, assign);
+  hipLaunchKernelGGL(merge_members_kernel, dim3(B), dim3(kPlanT), 0, st, N, k, assign, members,
+                     offsets);
   return hipGetLastError();
 }
 
