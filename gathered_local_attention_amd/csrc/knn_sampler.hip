@@ -388,6 +388,7 @@ knn_fwd_kernel(int N, int M, int Cf, int G, int K, int lg, float p, int64_t tota
   const int grp = lane >> lg, sub = lane & (L - 1);
   const int nch = Cf / Ck::E;
   const int nr = (nch - sub + L - 1) / L;   // chunks of this lane
+  const int cs = min(sub, nch - 1);   // idle lanes (sub >= nch, nr = 0) load inside the row
 #pragma unroll 2
   for (int u0 = 0; u0 < qwv; u0 += 64 >> lg) {
     const int u = u0 + grp;
@@ -411,7 +412,7 @@ knn_fwd_kernel(int N, int M, int Cf, int G, int K, int lg, float p, int64_t tota
       for (int r = 0; r < Ck::NR; ++r)
 #pragma unroll
         for (int k = 0; k < KM; ++k)
-          raw[r][k] = Ck::raw(fimg + (int64_t)max(sl[k], 0) * Cf + (r < nr ? sub + r * L : sub) * Ck::E);
+          raw[r][k] = Ck::raw(fimg + (int64_t)max(sl[k], 0) * Cf + (cs + (r < nr ? r * L : 0)) * Ck::E);
     }
 #pragma unroll
     for (int r = 0; r < Ck::NR; ++r) {
@@ -427,7 +428,7 @@ knn_fwd_kernel(int N, int M, int Cf, int G, int K, int lg, float p, int64_t tota
 #pragma unroll
         for (int e = 0; e < Ck::E; ++e) acc[e] = fmaf(wt[k], v[e], acc[e]);
       }
-      Ck::store(out + id * Cf + (sub + r * L) * Ck::E, acc);
+      Ck::store(out + id * Cf + (cs + r * L) * Ck::E, acc);
     }
   }
 }
@@ -470,6 +471,7 @@ knn_bwd_query_kernel(int N, int M, int Cf, int G, int K, int lg, float p, int64_
   const int grp = lane >> lg, sub = lane & (L - 1);
   const int nch = Cf / Ck::E;
   const int nr = (nch - sub + L - 1) / L;   // chunks of this lane
+  const int cs = min(sub, nch - 1);   // idle lanes (sub >= nch, nr = 0) load inside the row
   for (int u0 = 0; u0 < qwv; u0 += 64 >> lg) {   // uniform trip count: shuffles below
     const int u = u0 + grp;
     const int64_t id = base + u;
@@ -487,7 +489,7 @@ knn_bwd_query_kernel(int N, int M, int Cf, int G, int K, int lg, float p, int64_
     const int64_t oid = live ? id : base;
 #pragma unroll
     for (int r = 0; r < Ck::NR; ++r) {
-      const int c = r < nr ? sub + r * L : sub;
+      const int c = cs + (r < nr ? r * L : 0);
       oraw[r] = Ck::raw(dout + oid * Cf + c * Ck::E);
       if (N > 0) {
 #pragma unroll
@@ -803,6 +805,7 @@ knn_dfeat_kernel(int B, int N, int M, int Cf, int K, int lg, int split, const T*
   const int pos = grp * (64 >> lg) + (lane >> lg);   // token position in the walk order
   const int nch = Cf / Ck::E;
   const int nr = (nch - sub + L - 1) / L;            // chunks of this lane
+  const int cs = min(sub, nch - 1);   // idle lanes (sub >= nch, nr = 0) load inside the row
   const int64_t per = (int64_t)M * K;
   for (int img = x; img < B; img += X) {
     const int64_t b = img;
@@ -832,7 +835,7 @@ knn_dfeat_kernel(int B, int N, int M, int Cf, int K, int lg, int split, const T*
       for (int r = 0; r < Ck::NR; ++r)
 #pragma unroll
         for (int h = 0; h < kB; ++h)
-          raw[r][h] = Ck::raw(oimg + (int64_t)(e[h] / K) * Cf + (r < nr ? sub + r * L : sub) * Ck::E);
+          raw[r][h] = Ck::raw(oimg + (int64_t)(e[h] / K) * Cf + (cs + (r < nr ? r * L : 0)) * Ck::E);
 #pragma unroll
       for (int r = 0; r < Ck::NR; ++r) {
         if (r >= nr) break;
@@ -868,7 +871,7 @@ knn_dfeat_kernel(int B, int N, int M, int Cf, int K, int lg, int split, const T*
 #pragma unroll
       for (int r = 0; r < Ck::NR; ++r) {
         if (r >= nr) break;
-        Ck::store(dfeat + (b * N + t) * Cf + (sub + r * L) * Ck::E, acc[r]);
+        Ck::store(dfeat + (b * N + t) * Cf + (cs + r * L) * Ck::E, acc[r]);
       }
     }
   }
