@@ -21,11 +21,13 @@
 //
 // Kernels:
 //   knn_table_kernel      workgroups of (image, part of its cells): the
-//                         image's tokens counting-sorted into the buckets of
-//                         the fixed-point grid (bucket side = one cell) in
-//                         LDS; one thread per cell searches rings of buckets
-//                         around its own and stops once its K-th best is
-//                         closer than any bucket of the next ring can be.
+//                         image's tokens counting-sorted into square buckets
+//                         of the fixed-point grid (about two tokens each) in
+//                         LDS; one wave per 8 x 8-cell tile (lane = cell)
+//                         grows a window of buckets around the tile ring by
+//                         ring, every lane testing every token of the window,
+//                         and stops once each lane's K-th best is strictly
+//                         closer than any token outside the window can be.
 //   knn_fwd_kernel        a group of lanes per query, 16 bytes of the
 //                         feature row per lane: cell, slots, distances and
 //                         weights (computed redundantly by the group's lanes),
