@@ -163,17 +163,22 @@ merge_assign_kernel(const float* __restrict__ coords, const float* __restrict__ 
   }
   const uint32_t kth = sel[0], n_eq = sel[1];   // take n_eq of the keys equal to kth
   // 2. flags in token order (thread t owns tokens 4t .. 4t+3), then positions
+  //    (one scan of the packed counts of keys above and equal to the k-th:
+  //    the anchors before a thread's tokens are the larger keys before them
+  //    and the first n_eq equal keys in token order)
   constexpr int R = kMaxTok / kPlanT;
-  int eq_local = 0;
+  int gt_local = 0, eq_local = 0;
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     const int i = tid * R + r;
+    gt_local += (i < N && sk[i] > kth) ? 1 : 0;
     eq_local += (i < N && sk[i] == kth) ? 1 : 0;
   }
   int tot;
-  int eq_before = block_exclusive_scan(eq_local, tmp, kPlanT, &tot);
+  const int ex = block_exclusive_scan((gt_local << 16) | eq_local, tmp, kPlanT, &tot);
+  int eq_before = ex & 0xFFFF;
+  int pos = (ex >> 16) + min(eq_before, (int)n_eq);
   bool an[R];
-  int n_an = 0;
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     const int i = tid * R + r;
@@ -182,10 +187,7 @@ merge_assign_kernel(const float* __restrict__ coords, const float* __restrict__ 
       if (sk[i] > kth) an[r] = true;
       else if (sk[i] == kth) an[r] = (uint32_t)(eq_before++) < n_eq;
     }
-    n_an += an[r] ? 1 : 0;
   }
-  __syncthreads();   // tmp is reused by the next scan
-  int pos = block_exclusive_scan(n_an, tmp, kPlanT, &tot);
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     const int i = tid * R + r;
