@@ -159,9 +159,11 @@ knn_table_kernel(const float* __restrict__ coords, int N, int G, int K, int32_t*
 #pragma unroll
   for (int r = 0; r < KM; ++r) best[r] = ~0ull;
   uint64_t worst = ~0ull;   // best[K - 1]
-  auto scan_bucket = [&](int by, int bx) {
-    const int bb = by * Pb + bx;
-    const int t0 = start[bb], t1 = bb + 1 < nb ? start[bb + 1] : total;
+  // tokens of the buckets (by, bx0 .. bx1): one contiguous range (row-major
+  // bucket order)
+  auto scan_row = [&](int by, int bx0, int bx1) {
+    const int bb0 = by * Pb + bx0, bb1 = by * Pb + bx1;
+    const int t0 = start[bb0], t1 = bb1 + 1 < nb ? start[bb1 + 1] : total;
     for (int t = t0; t < t1; ++t) {
       const uint2 e = tok[t];
       const int64_t dx = (int64_t)(e.x & 0xFFFFu) - cx, dy = (int64_t)(e.x >> 16) - cy;
@@ -182,16 +184,14 @@ knn_table_kernel(const float* __restrict__ coords, int N, int G, int K, int32_t*
   for (int m = 0;; ++m) {
     const int r0 = tr0 - m, r1 = tr1 + m, c0 = tc0 - m, c1 = tc1 + m;   // window (buckets)
     if (m == 0) {
-      for (int by = r0; by <= r1; ++by)
-        for (int bx = c0; bx <= c1; ++bx) scan_bucket(by, bx);
+      for (int by = r0; by <= r1; ++by) scan_row(by, c0, c1);
     } else {
-      for (int bx = max(c0, 0); bx <= min(c1, Pb - 1); ++bx) {
-        if (r0 >= 0) scan_bucket(r0, bx);
-        if (r1 <= Pb - 1) scan_bucket(r1, bx);
-      }
+      const int cl = max(c0, 0), ch = min(c1, Pb - 1);
+      if (r0 >= 0) scan_row(r0, cl, ch);
+      if (r1 <= Pb - 1) scan_row(r1, cl, ch);
       for (int by = max(r0 + 1, 0); by <= min(r1 - 1, Pb - 1); ++by) {
-        if (c0 >= 0) scan_bucket(by, c0);
-        if (c1 <= Pb - 1) scan_bucket(by, c1);
+        if (c0 >= 0) scan_row(by, c0, c0);
+        if (c1 <= Pb - 1) scan_row(by, c1, c1);
       }
     }
     if (r0 <= 0 && c0 <= 0 && r1 >= Pb - 1 && c1 >= Pb - 1) break;   // every bucket seen
