@@ -36,7 +36,7 @@ HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, vendor figure
 # kernels behind each entry point on the bf16/f16 path (the roofline is per
 # entry point; the committed kernel trace splits it per kernel)
 ENTRY_KERNELS = {
-    "build": ["build_small_kernel (N <= 4096) | rank_kernel, merge_round_kernel, "
+    "build": ["build_small_kernel (N <= 4096) | segsort_kernel, merge_round_kernel, "
               "centroid_box_kernel, select_box_kernel (N > 4096)"],
     "plan": ["plan_small_kernel (images <= 4096 tokens) | plan_init/inv/count/scan/place/sort_kernel"],
     "fwd": ["fwd_lds_kernel"],
