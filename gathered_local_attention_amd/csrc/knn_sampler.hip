@@ -443,7 +443,7 @@ knn_fwd_kernel(int N, int M, int Cf, int G, int K, int lg, float p, int64_t tota
 // query's share of dp.
 // ---------------------------------------------------------------------------
 template <typename T, int KM>
-__global__ void __launch_bounds__(kKnnThreads)
+__global__ void __launch_bounds__(kKnnThreads) __attribute__((amdgpu_waves_per_eu(sizeof(T) == 2 && KM <= 8 ? 4 : 1)))
 knn_bwd_query_kernel(int N, int M, int Cf, int G, int K, int lg, float p, int64_t total, int qwv,
                      const float* __restrict__ coords, const T* __restrict__ feats,
                      const float* __restrict__ queries, const int32_t* __restrict__ table,
