@@ -78,49 +78,141 @@ def algorithmic_tc(T, C, H, D, nk, k, cs, dtype):
     }
 
 
-def copy_bandwidth(torch, nbytes=1 << 30, reps=10):
+def copy_bandwidth(torch, ca, nbytes=1 << 30, reps=10):
+    """Achievable HBM bandwidth: the library's plain copy kernel
+    (cluster_attn_device_copy) moving `nbytes` (1 GiB read + 1 GiB written),
+    median over `reps` timed copies; torch's own copy_ beside it."""
     src = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
     dst = torch.empty_like(src)
     src.fill_(1)
-    dst.copy_(src)
+    ca.device_copy(dst, src)
     torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+    ev[0].record()
+    for i in range(reps):
+        ca.device_copy(dst, src)
+        ev[i + 1].record()
+    torch.cuda.synchronize()
+    ms = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(reps))
+    med = ms[reps // 2]
+    assert torch.equal(dst[:4096], src[:4096])
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
     for _ in range(reps):
         dst.copy_(src)
     e1.record()
     torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / reps
+    torch_gbps = 2 * nbytes / (e0.elapsed_time(e1) / reps * 1e-3) / 1e9
     del src, dst
-    return 2 * nbytes / (ms * 1e-3) / 1e9
+    return {"GBps": 2 * nbytes / (med * 1e-3) / 1e9, "bytes_moved": 2 * nbytes,
+            "kernel": "cluster_attn_device_copy (copy16_kernel)", "median_of": reps,
+            "torch_copy_GBps": torch_gbps}
 
 
-def cpu_baseline(cfg, case, images: int):
-    """The fp64 oracle (gathered form, forward + backward) on `images` images
-    of the same workload, single-threaded; neighbour build excluded."""
-    import numpy as np
+def entry_times(torch, calls, n_ev, n_sets):
+    """Per-launch durations of each entry point: HIP events on the launch
+    stream recorded between n_ev back-to-back calls (rotating input copies),
+    so every call has its own event pair while the queue stays full.
+    Returns name -> {mean, median, p10, p90} in microseconds."""
+    out = {}
+    for name, call in calls.items():
+        call(0)
+        torch.cuda.synchronize()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(n_ev + 1)]
+        ev[0].record()
+        for i in range(n_ev):
+            call(i % n_sets)
+            ev[i + 1].record()
+        torch.cuda.synchronize()
+        d = sorted(ev[i].elapsed_time(ev[i + 1]) * 1e3 for i in range(n_ev))
+        q = lambda f: d[min(n_ev - 1, int(round(f * (n_ev - 1))))]
+        out[name] = {"mean": ev[0].elapsed_time(ev[n_ev]) * 1e3 / n_ev, "median": q(0.5),
+                     "p10": q(0.1), "p90": q(0.9)}
+    return out
+
+
+def rotation_copies(requested, tensor_bytes, tensors_read=3, llc_bytes=256 << 20):
+    """Rotating input copies so that every timed entry point walks at least
+    twice the 256 MB last-level cache before it reads a copy again (the
+    forward reads three tensors of a copy; the backward more)."""
+    if requested:
+        return requested
+    return max(4, -(-2 * llc_bytes // (tensors_read * tensor_bytes)))
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
+def _oracle_images(args):
+    """Worker of the all-cores baseline: the oracle's gathered forward +
+    backward on some images, one thread per worker process."""
     from threadpoolctl import threadpool_limits
 
     import oracle as O
 
-    sub = slice(0, images)
-    build = O.build_neighbors_3d if case["coords"].shape[-1] == 3 else O.build_neighbors
-    perm, _, key_idx = build(case["coords"][sub], cfg.G)
-    q_idx = perm.reshape(images, cfg.C, cfg.cs)
-    args = [case[n][sub] for n in ("q", "k", "v", "do")]
-    scale = 1.0 / math.sqrt(cfg.D)
+    q, k, v, do, q_idx, key_idx, scale = args
     with threadpool_limits(limits=1):
         t0 = time.perf_counter()
-        O.attn_fwd_gathered(*args[:3], q_idx, key_idx, scale)
-        O.attn_bwd_gathered(*args, q_idx, key_idx, scale)
-        dt = time.perf_counter() - t0
+        O.attn_fwd_gathered(q, k, v, q_idx, key_idx, scale)
+        O.attn_bwd_gathered(q, k, v, do, q_idx, key_idx, scale)
+        return time.perf_counter() - t0
+
+
+def cpu_baseline(cfg, case, images: int, single_images: int = 8, runs: int = 3):
+    """The fp64 oracle (gathered form, forward + backward; neighbour build
+    excluded) timed on the host: single-threaded on `single_images` images
+    and on all cores (one worker process per core, capped at 16, each taking
+    whole images) over `images` images; median of `runs` runs each."""
+    import concurrent.futures as cf
+    import multiprocessing as mp
+    import statistics
+
+    import numpy as np
+
+    import oracle as O
+
+    build = O.build_neighbors_3d if case["coords"].shape[-1] == 3 else O.build_neighbors
+    perm, _, key_idx = build(case["coords"][:images], cfg.G)
+    q_idx = perm.reshape(images, cfg.C, cfg.cs)
+    arrs = [case[n][:images].float().numpy() for n in ("q", "k", "v", "do")]
+    scale = 1.0 / math.sqrt(cfg.D)
+    job = lambda lo, hi: tuple(a[lo:hi] for a in arrs) + (q_idx[lo:hi], key_idx[lo:hi], scale)
+
+    one = [_oracle_images(job(0, single_images)) for _ in range(runs)]
+    t1 = statistics.median(one)
+    workers = max(1, min(16, os.cpu_count() or 1, images))
+    per = -(-images // workers)
+    parts = [job(lo, min(images, lo + per)) for lo in range(0, images, per)]
+    alls = []
+    with cf.ProcessPoolExecutor(max_workers=workers, mp_context=mp.get_context("spawn")) as ex:
+        list(ex.map(_oracle_images, parts[:1]))         # start the workers (imports) untimed
+        for _ in range(runs):
+            t0 = time.perf_counter()
+            list(ex.map(_oracle_images, parts))
+            alls.append(time.perf_counter() - t0)
+    ta = statistics.median(alls)
+    del np
     return {
-        "value": images * cfg.N / dt,
+        "value": images * cfg.N / ta,
         "unit": "tokens/s",
-        "cores": 1,
+        "cores": workers,
         "kind": "oracle",
         "sample": f"{images} of {cfg.B} images ({images * cfg.N} tokens), fp64 gathered "
-                  f"forward+backward, {dt:.1f} s",
+                  f"forward+backward, {workers} worker processes x 1 thread, median of {runs}: "
+                  f"{ta:.2f} s",
+        "single_thread": {"value": single_images * cfg.N / t1, "unit": "tokens/s", "cores": 1,
+                          "sample": f"{single_images} images, median of {runs}: {t1:.2f} s"},
+        "host_cpu": cpu_model(),
+        "os_cpu_count": os.cpu_count(),
     }
 
 
@@ -153,7 +245,9 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", default="stage1")
-    ap.add_argument("--copies", type=int, default=4, help="rotating input copies")
+    ap.add_argument("--copies", type=int, default=0,
+                    help="rotating input copies (default: enough that every timed entry point "
+                         "walks at least twice the 256 MB last-level cache)")
     ap.add_argument("--cpu-images", type=int, default=32)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
@@ -170,7 +264,6 @@ def main():
     from gen import (MERGE_CONFIGS, RAGGED_CONFIGS, SAMPLER_CONFIGS, VOLUME_CONFIGS, make_case,
                      make_volume_case)
 
-    ca._lib.load()
     if args.config in RAGGED_CONFIGS:
         bench_varlen(args, torch, ca)
         return
@@ -184,6 +277,14 @@ def main():
     cfg = case["cfg"]
     scale = 1.0 / math.sqrt(cfg.D)
     dev = "cuda"
+    # The host baseline runs first, before anything touches the GPU: its
+    # worker processes are started while this process holds no GPU state.
+    cpu_line = None
+    if not args.no_cpu_baseline:
+        cpu_line = cpu_baseline(cfg, case, min(args.cpu_images, cfg.B))
+    tensor_bytes = case["q"].numel() * case["q"].element_size()
+    args.copies = rotation_copies(args.copies, tensor_bytes)
+    ca._lib.load()
 
     # rotating copies of the batch, all resident in HBM
     sets = []
@@ -244,17 +345,8 @@ def main():
                                           sets[i]["do"], outs[i][3], outs[i][0], outs[i][1],
                                           scale, workspace=gws),
     }
-    dur = {}
-    for name, call in calls.items():
-        call(0)
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for i in range(n_ev):
-            call(i % len(sets))
-        e1.record()
-        torch.cuda.synchronize()
-        dur[name] = e0.elapsed_time(e1) / n_ev * 1e3   # microseconds per launch
+    stats = entry_times(torch, calls, n_ev, len(sets))
+    dur = {name: st["mean"] for name, st in stats.items()}   # microseconds per launch
 
     # warm-cache variant: every step on the same copy
     torch.cuda.synchronize()
@@ -270,7 +362,10 @@ def main():
     fb_us = dur["fwd"] + dur["bwd"]
     fb_bytes = alg["fwd"]["bytes"] + alg["bwd"]["bytes"]
     fb_flops = alg["fwd"]["flops"] + alg["bwd"]["flops"]
-    copy_gbps = copy_bandwidth(torch)
+    copy = copy_bandwidth(torch, ca)
+    copy_gbps = copy["GBps"]
+    fb_gbps = fb_bytes / (fb_us * 1e-6) / 1e9
+    fb_med = stats["fwd"]["median"] + stats["bwd"]["median"]
 
     line = {
         "metric": "cluster-attention fwd+bwd tokens/sec and % of HBM roofline (stage-1 shape)"
@@ -295,6 +390,10 @@ def main():
                         "backward",
             "B": cfg.B, "N": cfg.N, "H": cfg.H, "D": cfg.D, "cs": cfg.cs, "nk": cfg.nk,
             "geometry": cfg.geometry, "seed": cfg.seed, "rotating_copies": args.copies,
+            "rotation_footprint_MB": {
+                "fwd": round(args.copies * 3 * tensor_bytes / 1e6, 1),
+                "bwd": round(args.copies * 6 * tensor_bytes / 1e6, 1),
+                "step": round(args.copies * 4 * tensor_bytes / 1e6, 1)},
         },
         "roofline": {
             "bound": "hbm",
@@ -314,19 +413,22 @@ def main():
                     "only and serve every layer of a stage); the self-planning backward is "
                     "entry_us.bwd_with_plan",
             "us": fb_us,
+            "us_median": fb_med,
             "tokens_per_s": cfg.tokens / (fb_us * 1e-6),
-            "effective_GBps": fb_bytes / (fb_us * 1e-6) / 1e9,
-            "hbm_frac": fb_bytes / (fb_us * 1e-6) / 1e9 / HBM_PEAK_GBPS,
+            "effective_GBps": fb_gbps,
+            "hbm_frac": fb_gbps / HBM_PEAK_GBPS,
+            "copy_frac": fb_gbps / copy_gbps,
             "effective_TFLOPs": fb_flops / (fb_us * 1e-6) / 1e12,
             "mfma_bf16_frac": fb_flops / (fb_us * 1e-6) / 1e12 / BF16_MFMA_PEAK_TFLOPS,
         },
         "entry_us": dur,
+        "entry_us_stats": stats,
         "warm_ms_per_step": warm_ms,
         "copy_GBps": copy_gbps,
-        "cpu_baseline": None,
+        "copy": copy,
+        "roofline_vs_copy": achieved / copy_gbps,
+        "cpu_baseline": cpu_line,
     }
-    if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(cfg, case, min(args.cpu_images, cfg.B))
     print(json.dumps(line), flush=True)
 
 
@@ -363,6 +465,8 @@ def varlen_cpu_baseline(cfg, case, images: int):
 
 
 def bench_varlen(args, torch, ca):
+    ca._lib.load()
+    args.copies = args.copies or 4
     from gen import make_varlen_case
 
     case = make_varlen_case(args.config)
@@ -430,17 +534,8 @@ def bench_varlen(args, torch, ca):
                                                  outs[i][2], sets[i]["do"], outs[i][3], outs[i][0],
                                                  outs[i][1], scale, workspace=gws),
     }
-    dur = {}
-    for name, call in calls.items():
-        call(0)
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for i in range(n_ev):
-            call(i % len(sets))
-        e1.record()
-        torch.cuda.synchronize()
-        dur[name] = e0.elapsed_time(e1) / n_ev * 1e3
+    stats = entry_times(torch, calls, n_ev, len(sets))
+    dur = {name: st["mean"] for name, st in stats.items()}
 
     alg = algorithmic_tc(T, Ct, cfg.H, cfg.D, cfg.nk, cfg.k, cfg.cs, cfg.dtype)
     dom = max(("build", "plan", "fwd", "bwd"), key=lambda k: dur[k])
@@ -492,6 +587,7 @@ def bench_varlen(args, torch, ca):
             "mfma_bf16_frac": fb_flops / (fb_us * 1e-6) / 1e12 / BF16_MFMA_PEAK_TFLOPS,
         },
         "entry_us": dur,
+        "entry_us_stats": stats,
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
@@ -548,6 +644,8 @@ def sampler_cpu_baseline(cfg, case, images: int):
 
 
 def bench_sampler(args, torch, ca):
+    ca._lib.load()
+    args.copies = args.copies or 4
     from gen import make_sampler_case
 
     case = make_sampler_case(args.config)
@@ -595,17 +693,8 @@ def bench_sampler(args, torch, ca):
                                             sets[i]["lv"][li]["dout"], workspace=wss[li])
                           for li in range(L)],
     }
-    dur = {}
-    for name, call in calls.items():
-        call(0)
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for i in range(n_ev):
-            call(i % len(sets))
-        e1.record()
-        torch.cuda.synchronize()
-        dur[name] = e0.elapsed_time(e1) / n_ev * 1e3
+    stats = entry_times(torch, calls, n_ev, len(sets))
+    dur = {name: st["mean"] for name, st in stats.items()}
     alg = sampler_algorithmic(cfg)
     dom = max(("table", "fwd", "bwd"), key=lambda k: dur[k])
     achieved = alg[dom] / (dur[dom] * 1e-6) / 1e9
@@ -653,6 +742,7 @@ def bench_sampler(args, torch, ca):
             "hbm_frac": (alg["fwd"] + alg["bwd"]) / (fb_us * 1e-6) / 1e9 / HBM_PEAK_GBPS,
         },
         "entry_us": dur,
+        "entry_us_stats": stats,
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
@@ -709,6 +799,8 @@ def merge_cpu_baseline(cfg, case, images: int):
 
 
 def bench_merge(args, torch, ca):
+    ca._lib.load()
+    args.copies = args.copies or 4
     from gen import make_merge_case
 
     case = make_merge_case(args.config)
@@ -749,17 +841,8 @@ def bench_merge(args, torch, ca):
                                        plans[i][li][2], plans[i][li][3], sets[i][li]["dfeat"],
                                        sets[i][li]["dcoord"]) for li in range(L)],
     }
-    dur = {}
-    for name, call in calls.items():
-        call(0)
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for i in range(n_ev):
-            call(i % len(sets))
-        e1.record()
-        torch.cuda.synchronize()
-        dur[name] = e0.elapsed_time(e1) / n_ev * 1e3
+    stats = entry_times(torch, calls, n_ev, len(sets))
+    dur = {name: st["mean"] for name, st in stats.items()}
     alg = merge_algorithmic(cfg)
     dom = max(("plan", "fwd", "bwd"), key=lambda k: dur[k])
     achieved = alg[dom] / (dur[dom] * 1e-6) / 1e9
@@ -804,6 +887,7 @@ def bench_merge(args, torch, ca):
             "hbm_frac": (alg["fwd"] + alg["bwd"]) / (fb_us * 1e-6) / 1e9 / HBM_PEAK_GBPS,
         },
         "entry_us": dur,
+        "entry_us_stats": stats,
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:

@@ -12,6 +12,7 @@ build_neighbors(coords, grid_side, cs=8, k=6) -> (perm, nbr, key_idx)   (2D or 3
 fwd(q, k, v, q_idx, key_idx, scale=None) -> (o, lse)
 bwd(q, k, v, o, do, lse, q_idx, key_idx, scale=None, plan=None) -> (dq, dk, dv)
 bwd_plan(q_idx, key_idx, N) -> plan   (transposed lists, reusable across backward calls)
+check_lists(q_idx, key_idx, N)   (host-side index validation; fwd/bwd take check=True)
 cluster_attention(q, k, v, q_idx, key_idx, scale=None) -> o   (autograd)
 build_neighbors_varlen(coords, lengths, grid_side, cs=8, k=6)
     -> (q_idx, nbr, key_idx, tok_off, clu_off)        (packed batches)
@@ -37,6 +38,8 @@ from . import _lib
 
 __all__ = [
     "build_neighbors",
+    "check_lists",
+    "device_copy",
     "fwd",
     "bwd",
     "cluster_attention",
@@ -92,6 +95,16 @@ def _stream(t: torch.Tensor) -> int:
     return torch.cuda.current_stream(t.device).cuda_stream
 
 
+def device_copy(dst: torch.Tensor, src: torch.Tensor) -> None:
+    """dst[:] = src with the library's plain copy kernel (a bandwidth probe
+    for measurement; both contiguous device tensors of equal byte size)."""
+    if dst.numel() * dst.element_size() != src.numel() * src.element_size():
+        raise ValueError("dst and src differ in size")
+    _check(_lib.load().cluster_attn_device_copy(_dev(dst, "dst"), _dev(src, "src"),
+                                                src.numel() * src.element_size(), _stream(src)),
+           "cluster_attn_device_copy")
+
+
 def build_workspace_bytes(B: int, N: int, cs: int = 8, k: int = 6) -> int:
     return int(_lib.load().cluster_attn_build_neighbors_workspace(B, N, cs, k))
 
@@ -129,19 +142,60 @@ def build_neighbors(coords: torch.Tensor, grid_side: int, cs: int = 8, k: int = 
     return perm, nbr, key_idx
 
 
-def _shapes(q, q_idx, key_idx):
+def _shapes(q, q_idx, key_idx, cs: int = 8):
+    """Sizes of a batched call, with the index lists checked against them:
+    q_idx [B, C, cs] (or its [B, C*cs] flat form) and key_idx [B, C, nk]
+    with C = ceil(N / cs).  The C entry points read B*C*cs and B*C*nk
+    indices, so a mismatch must be caught here, before any launch."""
     if q.dim() != 4:
         raise ValueError("q/k/v must be [B, N, H, D]")
     B, N, H, D = q.shape
+    C = -(-N // cs)
     if q_idx.dim() == 2:
-        q_idx = q_idx.view(B, -1, 8)
-    cs = q_idx.shape[-1]
+        if q_idx.shape != (B, C * cs):
+            raise ValueError(f"q_idx must be [B, C*cs] = [{B}, {C * cs}], got {list(q_idx.shape)}")
+        q_idx = q_idx.view(B, C, cs)
+    if q_idx.shape != (B, C, cs):
+        raise ValueError(f"q_idx must be [B, C, cs] = [{B}, {C}, {cs}], got {list(q_idx.shape)}")
+    if key_idx.dim() != 3 or key_idx.shape[:2] != (B, C):
+        raise ValueError(f"key_idx must be [B, C, nk] = [{B}, {C}, nk], got {list(key_idx.shape)}")
     nk = key_idx.shape[-1]
     return B, N, H, D, cs, nk, q_idx
 
 
-def fwd(q, k, v, q_idx, key_idx, scale: float | None = None):
-    """Forward: returns O [B, N, H, D] (dtype of q) and LSE [B, N, H] f32."""
+def _check_lse(lse, B, N, H):
+    if lse.shape != (B, N, H):
+        raise ValueError(f"lse must be [B, N, H] = [{B}, {N}, {H}], got {list(lse.shape)}")
+
+
+def check_lists(q_idx: torch.Tensor, key_idx: torch.Tensor, N: int) -> None:
+    """Validate index lists on the host (``cluster_attn_check_lists``):
+    q_idx [B, C, cs] / [B, C*cs] (or [Ct, cs] for a packed batch of N = T
+    tokens), key_idx [B, C, nk] / [Ct, nk].  Copies the lists to host memory
+    (a synchronisation for device tensors) and raises ClusterAttnError with
+    the first offending position if a value is out of range or q_idx does
+    not partition the tokens.  The kernels themselves never check."""
+    lib = _lib.load()
+    qh = q_idx.detach().to("cpu", torch.int32).contiguous()
+    kh = key_idx.detach().to("cpu", torch.int32).contiguous()
+    if kh.dim() == 3:
+        B, C, nk = kh.shape
+        cs = qh.numel() // max(1, B * C) if B * C else 8
+    elif kh.dim() == 2:
+        B, (C, nk) = 1, kh.shape
+        cs = qh.shape[-1]
+    else:
+        raise ValueError("key_idx must be [B, C, nk] or [Ct, nk]")
+    if qh.numel() != B * C * cs:
+        raise ValueError("q_idx and key_idx disagree on the number of clusters")
+    _check(lib.cluster_attn_check_lists(B, int(N), C, cs, nk, qh.data_ptr(), kh.data_ptr()),
+           "cluster_attn_check_lists")
+
+
+def fwd(q, k, v, q_idx, key_idx, scale: float | None = None, check: bool = False):
+    """Forward: returns O [B, N, H, D] (dtype of q) and LSE [B, N, H] f32.
+    ``check`` validates the index lists on the host first
+    (:func:`check_lists`; synchronises)."""
     lib = _lib.load()
     B, N, H, D, cs, nk, q_idx = _shapes(q, q_idx, key_idx)
     if q.dtype not in _DT:
@@ -149,6 +203,8 @@ def fwd(q, k, v, q_idx, key_idx, scale: float | None = None):
     for t, n in ((k, "k"), (v, "v")):
         if t.shape != q.shape or t.dtype != q.dtype:
             raise ValueError(f"{n} must match q in shape and dtype")
+    if check:
+        check_lists(q_idx, key_idx, N)
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
     o = torch.empty_like(q)
     lse = torch.empty((B, N, H), dtype=torch.float32, device=q.device)
@@ -168,10 +224,18 @@ def bwd_plan(q_idx: torch.Tensor, key_idx: torch.Tensor, N: int) -> torch.Tensor
     lib = _lib.load()
     if key_idx.dim() == 3:
         B, C, nk = key_idx.shape
-        cs = q_idx.numel() // max(1, B * C) if B * C else 8
-    else:
+        cs = 8
+        if C != -(-int(N) // cs):
+            raise ValueError(f"key_idx has {C} clusters per image, N={N} needs {-(-int(N) // cs)}")
+    elif key_idx.dim() == 2:
         B, (C, nk) = 1, key_idx.shape
         cs = q_idx.shape[-1]
+        if C < -(-int(N) // cs) or C > int(N):
+            raise ValueError(f"a packed batch of {N} tokens cannot have {C} clusters")
+    else:
+        raise ValueError("key_idx must be [B, C, nk] or [Ct, nk]")
+    if q_idx.numel() != B * C * cs:
+        raise ValueError(f"q_idx must hold B*C*cs = {B * C * cs} indices, has {q_idx.numel()}")
     need = lib.cluster_attn_bwd_plan_workspace(B, int(N), C, cs, nk)
     plan = torch.empty(max(need, 1), dtype=torch.uint8, device=key_idx.device)
     _check(lib.cluster_attn_bwd_plan(B, int(N), C, cs, nk, _dev(q_idx, "q_idx", torch.int32),
@@ -220,10 +284,12 @@ def _bwd_planned(lib, dt, B, N, C, H, D, cs, nk, scale, q, k, v, o, do, lse, q_i
 
 
 def bwd(q, k, v, o, do, lse, q_idx, key_idx, scale: float | None = None,
-        workspace: torch.Tensor | None = None, plan: torch.Tensor | None = None):
+        workspace: torch.Tensor | None = None, plan: torch.Tensor | None = None,
+        check: bool = False):
     """Backward: returns dQ, dK, dV (dtype of q).  ``plan`` (from
     :func:`bwd_plan` on the same lists) skips rebuilding the transposed
-    lists; the result is the same bit for bit."""
+    lists; the result is the same bit for bit.  ``check`` validates the
+    index lists on the host first (:func:`check_lists`; synchronises)."""
     lib = _lib.load()
     B, N, H, D, cs, nk, q_idx = _shapes(q, q_idx, key_idx)
     if q.dtype not in _DT:
@@ -231,8 +297,11 @@ def bwd(q, k, v, o, do, lse, q_idx, key_idx, scale: float | None = None,
     for t, n in ((k, "k"), (v, "v"), (o, "o"), (do, "do")):
         if t.shape != q.shape or t.dtype != q.dtype:
             raise ValueError(f"{n} must match q in shape and dtype")
+    _check_lse(lse, B, N, H)
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
     dt = _DT[q.dtype]
+    if check:
+        check_lists(q_idx, key_idx, N)
     if plan is not None:
         return _bwd_planned(lib, dt, B, N, q_idx.shape[1], H, D, cs, nk, scale, q, k, v, o, do,
                             lse, q_idx, key_idx, plan, workspace)

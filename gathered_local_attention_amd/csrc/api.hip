@@ -6,6 +6,8 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <new>
+
 #include "../../include/cluster_attn.h"
 #include "common.h"
 
@@ -13,20 +15,20 @@ namespace {
 
 thread_local char g_last_error[512] = "";
 
-int fail(int status, const char* fmt, ...) {
+ca_status fail(int status, const char* fmt, ...) {
   va_list ap;
   va_start(ap, fmt);
   vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
   va_end(ap);
-  return status;
+  return (ca_status)status;
 }
 
-int ok() {
+ca_status ok() {
   g_last_error[0] = '\0';
   return CA_OK;
 }
 
-int hip_status(hipError_t e, const char* where) {
+ca_status hip_status(hipError_t e, const char* where) {
   if (e == hipSuccess) return ok();
   return fail(CA_ERR_HIP, "%s: %s", where, hipGetErrorString(e));
 }
@@ -46,7 +48,7 @@ bool overlaps(Range a, Range b) {
 }
 
 // outputs must not overlap each other or any input
-int check_alias(const Range* outs, int nout, const Range* ins, int nin) {
+ca_status check_alias(const Range* outs, int nout, const Range* ins, int nin) {
   for (int i = 0; i < nout; ++i) {
     for (int j = 0; j < nin; ++j)
       if (overlaps(outs[i], ins[j])) return fail(CA_ERR_ALIAS, "output %d overlaps input %d", i, j);
@@ -59,7 +61,7 @@ int check_alias(const Range* outs, int nout, const Range* ins, int nin) {
 using ca::kMaxTokensPerImage;   // 2^22: cluster ids of a (distance, index) key fit 19 bits
 
 // Shape checks common to fwd and bwd.  Returns CA_OK or an error.
-int check_attn_shape(int dt, int B, int N, int H, int D, int cs, int nk) {
+ca_status check_attn_shape(int dt, int B, int N, int H, int D, int cs, int nk) {
   if (dt != CA_F32 && dt != CA_BF16 && dt != CA_F16)
     return fail(CA_ERR_UNSUPPORTED, "dtype %d is not one of CA_F32, CA_BF16, CA_F16", dt);
   if (B < 0 || N < 0 || H < 1 || D < 1 || cs < 1 || nk < 1)
@@ -77,7 +79,7 @@ int64_t clusters_of(int64_t N, int cs) { return (N + cs - 1) / cs; }
 
 
 // Shape checks of the KNN sampler calls.
-int check_knn_shape(int B, int N, int M, int Cf, int G, int K) {
+ca_status check_knn_shape(int B, int N, int M, int Cf, int G, int K) {
   if (B < 0 || N < 0 || M < 0) return fail(CA_ERR_SHAPE, "bad sizes B=%d N=%d M=%d", B, N, M);
   if (G < 1 || G > 4096) return fail(CA_ERR_SHAPE, "grid_side=%d outside [1, 4096]", G);
   if (K < 1 || K > 16) return fail(CA_ERR_UNSUPPORTED, "K=%d outside 1..16", K);
@@ -90,7 +92,7 @@ int check_knn_shape(int B, int N, int M, int Cf, int G, int K) {
 }
 
 
-int check_merge_shape(int dt, int B, int N, int k, int C) {
+ca_status check_merge_shape(int dt, int B, int N, int k, int C) {
   if (dt != CA_F32 && dt != CA_BF16 && dt != CA_F16)
     return fail(CA_ERR_UNSUPPORTED, "dtype %d is not one of CA_F32, CA_BF16, CA_F16", dt);
   if (B < 0 || N < 0 || k < 0) return fail(CA_ERR_SHAPE, "bad sizes B=%d N=%d k=%d", B, N, k);
@@ -140,7 +142,7 @@ size_t cluster_attn_build_neighbors_varlen_workspace(int B, int T, int Ct, int m
 namespace {
 
 // Equal-size images: coords [B, N, dims].
-int build_uniform(int dims, const float* coords, int B, int N, int grid_side, int cs, int k,
+ca_status build_uniform(int dims, const float* coords, int B, int N, int grid_side, int cs, int k,
                   int32_t* perm, int32_t* nbr, int32_t* key_idx, void* ws, size_t ws_bytes,
                   void* hip_stream) {
   if (B < 0 || N < 0) return fail(CA_ERR_SHAPE, "bad sizes B=%d N=%d", B, N);
@@ -160,7 +162,7 @@ int build_uniform(int dims, const float* coords, int B, int N, int grid_side, in
   Range outs[] = {{perm, (size_t)(B * C * cs) * 4}, {nbr, (size_t)(B * C * k) * 4},
                   {key_idx, (size_t)(B * C * k * cs) * 4}, {ws, need}};
   Range ins[] = {{coords, (size_t)B * N * 4 * dims}};
-  if (int s = check_alias(outs, 4, ins, 1)) return s;
+  if (ca_status s = check_alias(outs, 4, ins, 1)) return s;
   const ca::Geom g{nullptr, nullptr, N, (int)C, 0};
   return hip_status(ca::launch_build_neighbors(coords, g, dims, B, (int64_t)B * N, B * C, grid_side,
                                                k, perm, nbr, key_idx, ws, (hipStream_t)hip_stream),
@@ -168,7 +170,7 @@ int build_uniform(int dims, const float* coords, int B, int N, int grid_side, in
 }
 
 // Packed images: coords [T, dims] with device offsets.
-int build_packed(int dims, const float* coords, int B, int T, int Ct, int max_n,
+ca_status build_packed(int dims, const float* coords, int B, int T, int Ct, int max_n,
                  const int32_t* tok_off, const int32_t* clu_off, int grid_side, int cs, int k,
                  int32_t* q_idx, int32_t* nbr, int32_t* key_idx, void* ws, size_t ws_bytes,
                  void* hip_stream) {
@@ -193,7 +195,7 @@ int build_packed(int dims, const float* coords, int B, int T, int Ct, int max_n,
                   {key_idx, (size_t)Ct * k * cs * 4}, {ws, need}};
   Range ins[] = {{coords, (size_t)T * 4 * dims}, {tok_off, (size_t)(B + 1) * 4},
                  {clu_off, (size_t)(B + 1) * 4}};
-  if (int s = check_alias(outs, 4, ins, 3)) return s;
+  if (ca_status s = check_alias(outs, 4, ins, 3)) return s;
   const ca::Geom g{tok_off, clu_off, max_n, (int)clusters_of(max_n, cs), 0};
   return hip_status(ca::launch_build_neighbors(coords, g, dims, B, T, Ct, grid_side, k, q_idx, nbr,
                                                key_idx, ws, (hipStream_t)hip_stream),
@@ -204,21 +206,21 @@ int build_packed(int dims, const float* coords, int B, int T, int Ct, int max_n,
 
 extern "C" {
 
-int cluster_attn_build_neighbors(const float* coords, int B, int N, int grid_side, int cs, int k,
+ca_status cluster_attn_build_neighbors(const float* coords, int B, int N, int grid_side, int cs, int k,
                                  int32_t* perm, int32_t* nbr, int32_t* key_idx, void* ws,
                                  size_t ws_bytes, void* hip_stream) {
   return build_uniform(2, coords, B, N, grid_side, cs, k, perm, nbr, key_idx, ws, ws_bytes,
                        hip_stream);
 }
 
-int cluster_attn_build_neighbors_3d(const float* coords, int B, int N, int grid_side, int cs,
+ca_status cluster_attn_build_neighbors_3d(const float* coords, int B, int N, int grid_side, int cs,
                                     int k, int32_t* perm, int32_t* nbr, int32_t* key_idx,
                                     void* ws, size_t ws_bytes, void* hip_stream) {
   return build_uniform(3, coords, B, N, grid_side, cs, k, perm, nbr, key_idx, ws, ws_bytes,
                        hip_stream);
 }
 
-int cluster_attn_build_neighbors_varlen(const float* coords, int B, int T, int Ct, int max_n,
+ca_status cluster_attn_build_neighbors_varlen(const float* coords, int B, int T, int Ct, int max_n,
                                         const int32_t* tok_off, const int32_t* clu_off,
                                         int grid_side, int cs, int k, int32_t* q_idx,
                                         int32_t* nbr, int32_t* key_idx, void* ws,
@@ -227,7 +229,7 @@ int cluster_attn_build_neighbors_varlen(const float* coords, int B, int T, int C
                       key_idx, ws, ws_bytes, hip_stream);
 }
 
-int cluster_attn_build_neighbors_varlen_3d(const float* coords, int B, int T, int Ct, int max_n,
+ca_status cluster_attn_build_neighbors_varlen_3d(const float* coords, int B, int T, int Ct, int max_n,
                                            const int32_t* tok_off, const int32_t* clu_off,
                                            int grid_side, int cs, int k, int32_t* q_idx,
                                            int32_t* nbr, int32_t* key_idx, void* ws,
@@ -241,7 +243,7 @@ int cluster_attn_build_neighbors_varlen_3d(const float* coords, int B, int T, in
 namespace {
 
 // Forward on B images of N tokens and C clusters each (q_idx [B, C, cs]).
-int attn_fwd(int dt, int B, int N, int64_t C, int H, int D, int cs, int nk, float scale,
+ca_status attn_fwd(int dt, int B, int N, int64_t C, int H, int D, int cs, int nk, float scale,
              const void* q, const void* k, const void* v, const int32_t* q_idx,
              const int32_t* key_idx, void* o, float* lse, void* hip_stream) {
   if (!(scale == scale) || scale == INFINITY || scale == -INFINITY)
@@ -253,7 +255,7 @@ int attn_fwd(int dt, int B, int N, int64_t C, int H, int D, int cs, int nk, floa
   Range outs[] = {{o, tb}, {lse, (size_t)B * N * H * 4}};
   Range ins[] = {{q, tb}, {k, tb}, {v, tb}, {q_idx, (size_t)(B * C * cs) * 4},
                  {key_idx, (size_t)(B * C * nk) * 4}};
-  if (int s = check_alias(outs, 2, ins, 5)) return s;
+  if (ca_status s = check_alias(outs, 2, ins, 5)) return s;
   hipStream_t st = (hipStream_t)hip_stream;
   if (ca::mfma_supported(dt, B, N, (int)C, H, nk))
     return hip_status(ca::launch_fwd_mfma(dt, B, N, (int)C, H, scale, q, k, v, q_idx, key_idx, o,
@@ -267,7 +269,7 @@ int attn_fwd(int dt, int B, int N, int64_t C, int H, int D, int cs, int nk, floa
 // Backward; `plan` (nullptr: built here, in `ws` behind the per-call part)
 // holds the transposed lists of a cluster_attn_bwd_plan call on the same
 // q_idx / key_idx.
-int attn_bwd(int dt, int B, int N, int64_t C, int H, int D, int cs, int nk, float scale,
+ca_status attn_bwd(int dt, int B, int N, int64_t C, int H, int D, int cs, int nk, float scale,
              const void* q, const void* k, const void* v, const void* o, const void* dout,
              const float* lse, const int32_t* q_idx, const int32_t* key_idx, const void* plan,
              size_t plan_bytes, void* dq, void* dk, void* dv, void* ws, size_t ws_bytes,
@@ -295,7 +297,7 @@ int attn_bwd(int dt, int B, int N, int64_t C, int H, int D, int cs, int nk, floa
                  {q_idx, (size_t)(B * C * cs) * 4},
                  {key_idx, (size_t)(B * C * nk) * 4},
                  {plan, plan ? pneed : 0}};
-  if (int s = check_alias(outs, 4, ins, 9)) return s;
+  if (ca_status s = check_alias(outs, 4, ins, 9)) return s;
   ca::BwdWorkspace w;
   hipStream_t st = (hipStream_t)hip_stream;
   if (plan) {
@@ -319,7 +321,7 @@ int attn_bwd(int dt, int B, int N, int64_t C, int H, int D, int cs, int nk, floa
 
 // (B, N, C) of a plan: C = ceil(N/cs) for equal-size images, or a packed
 // batch as one image (B = 1) of N tokens in C clusters.
-int check_plan_sizes(int B, int N, int C, int cs, int nk) {
+ca_status check_plan_sizes(int B, int N, int C, int cs, int nk) {
   if (B < 0 || N < 0 || C < 0) return fail(CA_ERR_SHAPE, "bad sizes B=%d N=%d C=%d", B, N, C);
   if (cs != 8) return fail(CA_ERR_UNSUPPORTED, "cluster size %d (only 8 is supported)", cs);
   if (nk % cs != 0 || nk / cs < 1 || nk / cs > 8)
@@ -333,8 +335,8 @@ int check_plan_sizes(int B, int N, int C, int cs, int nk) {
 }
 
 // Packed batches run as one image of T tokens and Ct clusters.
-int check_varlen(int dt, int T, int Ct, int H, int D, int cs, int nk) {
-  if (int s = check_attn_shape(dt, 1, T, H, D, cs, nk)) return s;
+ca_status check_varlen(int dt, int T, int Ct, int H, int D, int cs, int nk) {
+  if (ca_status s = check_attn_shape(dt, 1, T, H, D, cs, nk)) return s;
   if (Ct < 0 || Ct < clusters_of(T, cs) || Ct > T)
     return fail(CA_ERR_SHAPE, "Ct=%d is inconsistent with T=%d tokens", Ct, T);
   return CA_OK;
@@ -344,10 +346,10 @@ int check_varlen(int dt, int T, int Ct, int H, int D, int cs, int nk) {
 
 extern "C" {
 
-int cluster_attn_fwd(int dt, int B, int N, int H, int D, int cs, int nk, float scale,
+ca_status cluster_attn_fwd(int dt, int B, int N, int H, int D, int cs, int nk, float scale,
                      const void* q, const void* k, const void* v, const int32_t* q_idx,
                      const int32_t* key_idx, void* o, float* lse, void* hip_stream) {
-  if (int s = check_attn_shape(dt, B, N, H, D, cs, nk)) return s;
+  if (ca_status s = check_attn_shape(dt, B, N, H, D, cs, nk)) return s;
   return attn_fwd(dt, B, N, clusters_of(N, cs), H, D, cs, nk, scale, q, k, v, q_idx, key_idx, o,
                   lse, hip_stream);
 }
@@ -361,20 +363,20 @@ size_t cluster_attn_bwd_workspace(int dt, int B, int N, int H, int D, int cs, in
   return ca::bwd_layout(nullptr, B, N, H, clusters_of(N, cs), nk).bytes;
 }
 
-int cluster_attn_bwd(int dt, int B, int N, int H, int D, int cs, int nk, float scale,
+ca_status cluster_attn_bwd(int dt, int B, int N, int H, int D, int cs, int nk, float scale,
                      const void* q, const void* k, const void* v, const void* o,
                      const void* dout, const float* lse, const int32_t* q_idx,
                      const int32_t* key_idx, void* dq, void* dk, void* dv, void* ws,
                      size_t ws_bytes, void* hip_stream) {
-  if (int s = check_attn_shape(dt, B, N, H, D, cs, nk)) return s;
+  if (ca_status s = check_attn_shape(dt, B, N, H, D, cs, nk)) return s;
   return attn_bwd(dt, B, N, clusters_of(N, cs), H, D, cs, nk, scale, q, k, v, o, dout, lse, q_idx,
                   key_idx, nullptr, 0, dq, dk, dv, ws, ws_bytes, hip_stream);
 }
 
-int cluster_attn_fwd_varlen(int dt, int T, int Ct, int H, int D, int cs, int nk, float scale,
+ca_status cluster_attn_fwd_varlen(int dt, int T, int Ct, int H, int D, int cs, int nk, float scale,
                             const void* q, const void* k, const void* v, const int32_t* q_idx,
                             const int32_t* key_idx, void* o, float* lse, void* hip_stream) {
-  if (int s = check_varlen(dt, T, Ct, H, D, cs, nk)) return s;
+  if (ca_status s = check_varlen(dt, T, Ct, H, D, cs, nk)) return s;
   return attn_fwd(dt, 1, T, Ct, H, D, cs, nk, scale, q, k, v, q_idx, key_idx, o, lse, hip_stream);
 }
 
@@ -387,12 +389,12 @@ size_t cluster_attn_bwd_varlen_workspace(int dt, int T, int Ct, int H, int D, in
   return ca::bwd_layout(nullptr, 1, T, H, Ct, nk).bytes;
 }
 
-int cluster_attn_bwd_varlen(int dt, int T, int Ct, int H, int D, int cs, int nk, float scale,
+ca_status cluster_attn_bwd_varlen(int dt, int T, int Ct, int H, int D, int cs, int nk, float scale,
                             const void* q, const void* k, const void* v, const void* o,
                             const void* dout, const float* lse, const int32_t* q_idx,
                             const int32_t* key_idx, void* dq, void* dk, void* dv, void* ws,
                             size_t ws_bytes, void* hip_stream) {
-  if (int s = check_varlen(dt, T, Ct, H, D, cs, nk)) return s;
+  if (ca_status s = check_varlen(dt, T, Ct, H, D, cs, nk)) return s;
   return attn_bwd(dt, 1, T, Ct, H, D, cs, nk, scale, q, k, v, o, dout, lse, q_idx, key_idx,
                   nullptr, 0, dq, dk, dv, ws, ws_bytes, hip_stream);
 }
@@ -406,27 +408,27 @@ size_t cluster_attn_bwd_plan_workspace(int B, int N, int C, int cs, int nk) {
   return ca::plan_layout(nullptr, B, N, C, nk).bytes;
 }
 
-int cluster_attn_bwd_plan(int B, int N, int C, int cs, int nk, const int32_t* q_idx,
+ca_status cluster_attn_bwd_plan(int B, int N, int C, int cs, int nk, const int32_t* q_idx,
                           const int32_t* key_idx, void* plan, size_t plan_bytes,
                           void* hip_stream) {
-  if (int s = check_plan_sizes(B, N, C, cs, nk)) return s;
+  if (ca_status s = check_plan_sizes(B, N, C, cs, nk)) return s;
   if (B == 0 || N == 0 || C == 0) return ok();
   if (!q_idx || !key_idx || !plan) return fail(CA_ERR_NULL, "NULL pointer");
   const size_t need = ca::plan_layout(nullptr, B, N, C, nk).bytes;
   if (plan_bytes < need) return fail(CA_ERR_WORKSPACE, "plan %zu < %zu bytes", plan_bytes, need);
   Range outs[] = {{plan, need}};
   Range ins[] = {{q_idx, (size_t)B * C * cs * 4}, {key_idx, (size_t)B * C * nk * 4}};
-  if (int s = check_alias(outs, 1, ins, 2)) return s;
+  if (ca_status s = check_alias(outs, 1, ins, 2)) return s;
   const ca::BwdWorkspace w = ca::plan_layout(plan, B, N, C, nk);
   return hip_status(ca::launch_bwd_plan(B, N, C, nk, q_idx, key_idx, w, (hipStream_t)hip_stream),
                     "bwd plan launch");
 }
 
-int cluster_attn_bwd_plan_varlen(int B, int T, int Ct, int max_n, const int32_t* tok_off,
+ca_status cluster_attn_bwd_plan_varlen(int B, int T, int Ct, int max_n, const int32_t* tok_off,
                                  const int32_t* clu_off, int cs, int nk, const int32_t* q_idx,
                                  const int32_t* key_idx, void* plan, size_t plan_bytes,
                                  void* hip_stream) {
-  if (int s = check_plan_sizes(1, T, Ct, cs, nk)) return s;
+  if (ca_status s = check_plan_sizes(1, T, Ct, cs, nk)) return s;
   if (B < 0 || max_n < 0 || max_n > T)
     return fail(CA_ERR_SHAPE, "bad sizes B=%d T=%d max_n=%d", B, T, max_n);
   if (B == 0 || T == 0 || Ct == 0) return ok();
@@ -436,7 +438,7 @@ int cluster_attn_bwd_plan_varlen(int B, int T, int Ct, int max_n, const int32_t*
   Range outs[] = {{plan, need}};
   Range ins[] = {{q_idx, (size_t)Ct * cs * 4}, {key_idx, (size_t)Ct * nk * 4},
                  {tok_off, (size_t)(B + 1) * 4}, {clu_off, (size_t)(B + 1) * 4}};
-  if (int s = check_alias(outs, 1, ins, 4)) return s;
+  if (ca_status s = check_alias(outs, 1, ins, 4)) return s;
   const ca::BwdWorkspace w = ca::plan_layout(plan, 1, T, Ct, nk);
   const ca::Geom g{tok_off, clu_off, max_n, (int)clusters_of(max_n, cs), 0};
   return hip_status(ca::launch_bwd_plan(B, T, Ct, nk, q_idx, key_idx, w, (hipStream_t)hip_stream,
@@ -449,20 +451,20 @@ size_t cluster_attn_bwd_planned_workspace(int dt, int B, int N, int H, int D) {
   return ca::call_layout(nullptr, B, N, H).bytes;
 }
 
-int cluster_attn_bwd_planned(int dt, int B, int N, int C, int H, int D, int cs, int nk,
+ca_status cluster_attn_bwd_planned(int dt, int B, int N, int C, int H, int D, int cs, int nk,
                              float scale, const void* q, const void* k, const void* v,
                              const void* o, const void* dout, const float* lse,
                              const int32_t* q_idx, const int32_t* key_idx, const void* plan,
                              size_t plan_bytes, void* dq, void* dk, void* dv, void* ws,
                              size_t ws_bytes, void* hip_stream) {
-  if (int s = check_attn_shape(dt, B, N, H, D, cs, nk)) return s;
-  if (int s = check_plan_sizes(B, N, C, cs, nk)) return s;
+  if (ca_status s = check_attn_shape(dt, B, N, H, D, cs, nk)) return s;
+  if (ca_status s = check_plan_sizes(B, N, C, cs, nk)) return s;
   if (B > 0 && N > 0 && C > 0 && !plan) return fail(CA_ERR_NULL, "NULL plan");
   return attn_bwd(dt, B, N, C, H, D, cs, nk, scale, q, k, v, o, dout, lse, q_idx, key_idx, plan,
                   plan_bytes, dq, dk, dv, ws, ws_bytes, hip_stream);
 }
 
-int cluster_attn_knn_table(const float* coords, int B, int N, int grid_side, int K,
+ca_status cluster_attn_knn_table(const float* coords, int B, int N, int grid_side, int K,
                            int32_t* table, void* hip_stream) {
   if (B < 0 || N < 0) return fail(CA_ERR_SHAPE, "bad sizes B=%d N=%d", B, N);
   if (grid_side < 1 || grid_side > 64)
@@ -474,17 +476,17 @@ int cluster_attn_knn_table(const float* coords, int B, int N, int grid_side, int
   const size_t tb = (size_t)B * grid_side * grid_side * K * 4;
   Range outs[] = {{table, tb}};
   Range ins[] = {{coords, (size_t)B * N * 8}};
-  if (int s = check_alias(outs, 1, ins, 1)) return s;
+  if (ca_status s = check_alias(outs, 1, ins, 1)) return s;
   return hip_status(ca::launch_knn_table(coords, B, N, grid_side, K, table, (hipStream_t)hip_stream),
                     "knn table launch");
 }
 
-int cluster_attn_knn_sample_fwd(int dt, int B, int N, int M, int C, int grid_side, int K, float p,
+ca_status cluster_attn_knn_sample_fwd(int dt, int B, int N, int M, int C, int grid_side, int K, float p,
                                 const float* coords, const void* feats, const float* queries,
                                 const int32_t* table, void* out, void* hip_stream) {
   if (dt != CA_F32 && dt != CA_BF16 && dt != CA_F16)
     return fail(CA_ERR_UNSUPPORTED, "dtype %d is not one of CA_F32, CA_BF16, CA_F16", dt);
-  if (int s = check_knn_shape(B, N, M, C, grid_side, K)) return s;
+  if (ca_status s = check_knn_shape(B, N, M, C, grid_side, K)) return s;
   if (!(p == p) || p == INFINITY || p == -INFINITY) return fail(CA_ERR_SHAPE, "p is not finite");
   if (B == 0 || M == 0) return ok();
   if (!queries || !table || !out || (N > 0 && (!coords || !feats)))
@@ -495,7 +497,7 @@ int cluster_attn_knn_sample_fwd(int dt, int B, int N, int M, int C, int grid_sid
                  {feats, (size_t)B * N * C * es},
                  {queries, (size_t)B * M * 8},
                  {table, (size_t)B * grid_side * grid_side * K * 4}};
-  if (int s = check_alias(outs, 1, ins, 4)) return s;
+  if (ca_status s = check_alias(outs, 1, ins, 4)) return s;
   return hip_status(ca::launch_knn_fwd(dt, B, N, M, C, grid_side, K, p, coords, feats, queries,
                                        table, out, (hipStream_t)hip_stream),
                     "knn fwd launch");
@@ -506,13 +508,13 @@ size_t cluster_attn_knn_sample_bwd_workspace(int B, int N, int M, int K) {
   return ca::knn_layout(nullptr, B, N, M, K).bytes;
 }
 
-int cluster_attn_knn_sample_bwd(int dt, int B, int N, int M, int C, int grid_side, int K, float p,
+ca_status cluster_attn_knn_sample_bwd(int dt, int B, int N, int M, int C, int grid_side, int K, float p,
                                 const float* coords, const void* feats, const float* queries,
                                 const int32_t* table, const void* dout, void* dfeats, float* dq,
                                 float* dp, void* ws, size_t ws_bytes, void* hip_stream) {
   if (dt != CA_F32 && dt != CA_BF16 && dt != CA_F16)
     return fail(CA_ERR_UNSUPPORTED, "dtype %d is not one of CA_F32, CA_BF16, CA_F16", dt);
-  if (int s = check_knn_shape(B, N, M, C, grid_side, K)) return s;
+  if (ca_status s = check_knn_shape(B, N, M, C, grid_side, K)) return s;
   if (!(p == p) || p == INFINITY || p == -INFINITY) return fail(CA_ERR_SHAPE, "p is not finite");
   if (!dp) return fail(CA_ERR_NULL, "NULL dp pointer");
   const bool some_q = B > 0 && M > 0, some_t = B > 0 && N > 0;
@@ -529,13 +531,13 @@ int cluster_attn_knn_sample_bwd(int dt, int B, int N, int M, int C, int grid_sid
                  {queries, (size_t)B * M * 8},
                  {table, (size_t)B * grid_side * grid_side * K * 4},
                  {dout, (size_t)B * M * C * es}};
-  if (int s = check_alias(outs, 4, ins, 5)) return s;
+  if (ca_status s = check_alias(outs, 4, ins, 5)) return s;
   return hip_status(ca::launch_knn_bwd(dt, B, N, M, C, grid_side, K, p, coords, feats, queries,
                                        table, dout, dfeats, dq, dp, ws, (hipStream_t)hip_stream),
                     "knn bwd launch");
 }
 
-int cluster_attn_merge_plan(const float* coords, const float* scores, int B, int N, int k,
+ca_status cluster_attn_merge_plan(const float* coords, const float* scores, int B, int N, int k,
                             int grid_side, int32_t* anchors, int32_t* assign, int32_t* members,
                             int32_t* offsets, void* hip_stream) {
   if (B < 0 || N < 0 || k < 0) return fail(CA_ERR_SHAPE, "bad sizes B=%d N=%d k=%d", B, N, k);
@@ -549,17 +551,17 @@ int cluster_attn_merge_plan(const float* coords, const float* scores, int B, int
   Range outs[] = {{anchors, (size_t)B * k * 4}, {assign, (size_t)B * N * 4},
                   {members, (size_t)B * N * 4}, {offsets, (size_t)B * (k + 1) * 4}};
   Range ins[] = {{coords, (size_t)B * N * 8}, {scores, (size_t)B * N * 4}};
-  if (int s = check_alias(outs, 4, ins, 2)) return s;
+  if (ca_status s = check_alias(outs, 4, ins, 2)) return s;
   return hip_status(ca::launch_merge_plan(coords, scores, B, N, k, grid_side, anchors, assign,
                                           members, offsets, (hipStream_t)hip_stream),
                     "merge plan launch");
 }
 
-int cluster_attn_merge_fwd(int dt, int B, int N, int k, int C, const void* feats,
+ca_status cluster_attn_merge_fwd(int dt, int B, int N, int k, int C, const void* feats,
                            const float* coords, const float* scores, const int32_t* members,
                            const int32_t* offsets, void* out_feats, float* out_coords,
                            void* hip_stream) {
-  if (int s = check_merge_shape(dt, B, N, k, C)) return s;
+  if (ca_status s = check_merge_shape(dt, B, N, k, C)) return s;
   if (B == 0 || N == 0) return ok();
   if (!feats || !coords || !scores || !members || !offsets || !out_feats || !out_coords)
     return fail(CA_ERR_NULL, "NULL tensor pointer");
@@ -568,18 +570,18 @@ int cluster_attn_merge_fwd(int dt, int B, int N, int k, int C, const void* feats
   Range ins[] = {{feats, (size_t)B * N * C * es}, {coords, (size_t)B * N * 8},
                  {scores, (size_t)B * N * 4}, {members, (size_t)B * N * 4},
                  {offsets, (size_t)B * (k + 1) * 4}};
-  if (int s = check_alias(outs, 2, ins, 5)) return s;
+  if (ca_status s = check_alias(outs, 2, ins, 5)) return s;
   return hip_status(ca::launch_merge_fwd(dt, B, N, k, C, feats, coords, scores, members, offsets,
                                          out_feats, out_coords, (hipStream_t)hip_stream),
                     "merge fwd launch");
 }
 
-int cluster_attn_merge_bwd(int dt, int B, int N, int k, int C, const void* feats,
+ca_status cluster_attn_merge_bwd(int dt, int B, int N, int k, int C, const void* feats,
                            const float* coords, const float* scores, const int32_t* members,
                            const int32_t* offsets, const void* dout_feats,
                            const float* dout_coords, void* dfeats, float* dcoords,
                            float* dscores, void* hip_stream) {
-  if (int s = check_merge_shape(dt, B, N, k, C)) return s;
+  if (ca_status s = check_merge_shape(dt, B, N, k, C)) return s;
   if (B == 0 || N == 0) return ok();
   if (!feats || !coords || !scores || !members || !offsets || !dout_feats || !dout_coords ||
       !dfeats || !dcoords || !dscores)
@@ -591,7 +593,7 @@ int cluster_attn_merge_bwd(int dt, int B, int N, int k, int C, const void* feats
                  {scores, (size_t)B * N * 4},       {members, (size_t)B * N * 4},
                  {offsets, (size_t)B * (k + 1) * 4}, {dout_feats, (size_t)B * k * C * es},
                  {dout_coords, (size_t)B * k * 8}};
-  if (int s = check_alias(outs, 3, ins, 7)) return s;
+  if (ca_status s = check_alias(outs, 3, ins, 7)) return s;
   return hip_status(ca::launch_merge_bwd(dt, B, N, k, C, feats, coords, scores, members, offsets,
                                          dout_feats, dout_coords, dfeats, dcoords, dscores,
                                          (hipStream_t)hip_stream),
@@ -599,3 +601,66 @@ int cluster_attn_merge_bwd(int dt, int B, int N, int k, int C, const void* feats
 }
 
 }  // extern "C"
+
+// ---------------------------------------------------------------------------
+// Host-side validation of index lists (debug helper; no GPU involved).
+// ---------------------------------------------------------------------------
+extern "C" ca_status cluster_attn_check_lists(int B, int N, int C, int cs, int nk,
+                                              const int32_t* q_idx, const int32_t* key_idx) {
+  if (B < 0 || N < 0 || C < 0 || cs < 1 || nk < 0)
+    return fail(CA_ERR_SHAPE, "bad sizes B=%d N=%d C=%d cs=%d nk=%d", B, N, C, cs, nk);
+  if ((int64_t)C * cs < N || (B > 1 && C != clusters_of(N, cs)))
+    return fail(CA_ERR_SHAPE, "C=%d clusters of %d cannot hold N=%d tokens per image", C, cs, N);
+  if ((int64_t)B * C * (cs + nk) > (int64_t(1) << 40)) return fail(CA_ERR_SHAPE, "lists too large");
+  if (B == 0 || C == 0) return ok();
+  if (!q_idx || (nk && !key_idx)) return fail(CA_ERR_NULL, "NULL list pointer");
+  char* seen = new (std::nothrow) char[N > 0 ? N : 1];
+  if (!seen) return fail(CA_ERR_SHAPE, "out of host memory for N=%d", N);
+  ca_status st = CA_OK;
+  for (int b = 0; b < B && st == CA_OK; ++b) {
+    memset(seen, 0, N > 0 ? N : 1);
+    const int32_t* qb = q_idx + (int64_t)b * C * cs;
+    const int32_t* kb = key_idx ? key_idx + (int64_t)b * C * nk : nullptr;
+    int64_t tokens = 0;
+    for (int64_t c = 0; c < C && st == CA_OK; ++c) {
+      bool ended = false;
+      for (int m = 0; m < cs; ++m) {
+        const int32_t t = qb[c * cs + m];
+        if (t == -1) {
+          if (m == 0) {
+            st = fail(CA_ERR_SHAPE, "q_idx[%d][%lld][0] is -1 (member 0 must be a token)", b,
+                      (long long)c);
+            break;
+          }
+          ended = true;
+          continue;
+        }
+        if (t < 0 || t >= N) {
+          st = fail(CA_ERR_SHAPE, "q_idx[%d][%lld][%d] = %d outside [-1, %d)", b, (long long)c, m,
+                    t, N);
+          break;
+        }
+        if (ended) {
+          st = fail(CA_ERR_SHAPE, "q_idx[%d][%lld][%d] = %d follows a -1", b, (long long)c, m, t);
+          break;
+        }
+        if (seen[t]) {
+          st = fail(CA_ERR_SHAPE, "token %d appears twice in q_idx[%d]", t, b);
+          break;
+        }
+        seen[t] = 1;
+        ++tokens;
+      }
+      for (int s = 0; s < nk && st == CA_OK; ++s) {
+        const int32_t t = kb[c * nk + s];
+        if (t < -1 || t >= N)
+          st = fail(CA_ERR_SHAPE, "key_idx[%d][%lld][%d] = %d outside [-1, %d)", b, (long long)c,
+                    s, t, N);
+      }
+    }
+    if (st == CA_OK && tokens != N)
+      st = fail(CA_ERR_SHAPE, "q_idx[%d] holds %lld of the %d tokens", b, (long long)tokens, N);
+  }
+  delete[] seen;
+  return st == CA_OK ? ok() : st;
+}

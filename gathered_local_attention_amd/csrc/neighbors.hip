@@ -290,11 +290,19 @@ __device__ __forceinline__ void top_insert(uint64_t (&best)[KM1 > 0 ? KM1 : 1], 
 
 // Scan one tile of candidate centroids (staged in this wave's LDS row) for
 // the lanes with `need`, keeping the KM1 smallest (d2 << kIdxBits | index)
-// keys (scaled sums below 2^22: d2 < 2^46 even in 3D, so a key fits 64
-// bits).  Candidates are screened with an fp32 distance whose error bound
+// keys.  A scaled centroid sum is at most lcm(8, n mod 8) <= 56 times the
+// largest fixed-point coordinate, so in 2D d2 <= 2 (56 * 65535)^2 < 2^45 and
+// in 3D d2 <= 3 (56 * 16383)^2 < 2^42: with kIdxBits = 19 index bits a key
+// fills at most all 64 bits (the static_asserts below tie the three
+// constants together).  Candidates are screened with an fp32 distance whose error bound
 // (relative 2^-22) cannot drop a candidate at or below the current KM1-th
 // best; the survivors are compared exactly in 64 bits, so the kept set does
 // not depend on the order of the scan.
+static_assert(2.0 * (56.0 * 65535.0) * (56.0 * 65535.0) < 18446744073709551616.0 / (1u << kIdxBits),
+              "2D (distance, index) sort keys overflow 64 bits");
+static_assert(3.0 * (56.0 * 16383.0) * (56.0 * 16383.0) < 18446744073709551616.0 / (1u << kIdxBits),
+              "3D (distance, index) sort keys overflow 64 bits");
+
 template <int KM1, int DIM>
 __device__ __forceinline__ void scan_tile(const typename Space<DIM>::FCent* __restrict__ cent,
                                           typename Space<DIM>::FCent* __restrict__ row, int t0,

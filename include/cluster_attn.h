@@ -35,7 +35,8 @@
  *  - Every call is asynchronous on `hip_stream` (a hipStream_t; NULL = the
  *    default stream): it validates its arguments synchronously, enqueues its
  *    kernels and returns.  Validation failures return before any launch and
- *    write nothing.  Out-of-range indices are a precondition, not checked.
+ *    write nothing.  Out-of-range indices are a precondition the kernels do
+ *    not check; cluster_attn_check_lists (host pointers) checks them.
  *  - Outputs are fully overwritten (dK and dV are not accumulated into);
  *    tokens no slot references get dK = dV = 0.  Outputs must not overlap
  *    inputs (CA_ERR_ALIAS where the ranges are visibly overlapping).
@@ -45,6 +46,7 @@
  *    Anything else: CA_ERR_SHAPE or CA_ERR_UNSUPPORTED.
  *  - No call throws across the ABI.  Launch or runtime failures return
  *    CA_ERR_HIP; cluster_attn_last_error() gives the text (thread-local).
+ *    Entry points return ca_status (an int-sized enum; 0 = CA_OK).
  */
 #ifndef CLUSTER_ATTN_H
 #define CLUSTER_ATTN_H
@@ -108,7 +110,7 @@ size_t cluster_attn_build_neighbors_workspace(int B, int N, int cs, int k);
  *             (may be NULL when that is 0).  Contents on entry are ignored.
  * Deterministic: the output is the unique list defined above.
  */
-int cluster_attn_build_neighbors(const float* coords, int B, int N, int grid_side, int cs, int k,
+ca_status cluster_attn_build_neighbors(const float* coords, int B, int N, int grid_side, int cs, int k,
                                  int32_t* perm, int32_t* nbr, int32_t* key_idx, void* ws,
                                  size_t ws_bytes, void* hip_stream);
 
@@ -128,7 +130,7 @@ int cluster_attn_build_neighbors(const float* coords, int B, int N, int grid_sid
  * for cluster_attn_build_neighbors.  The lists feed the same cluster_attn_fwd
  * / cluster_attn_bwd (the attention does not depend on the dimension).
  */
-int cluster_attn_build_neighbors_3d(const float* coords, int B, int N, int grid_side, int cs,
+ca_status cluster_attn_build_neighbors_3d(const float* coords, int B, int N, int grid_side, int cs,
                                     int k, int32_t* perm, int32_t* nbr, int32_t* key_idx,
                                     void* ws, size_t ws_bytes, void* hip_stream);
 
@@ -153,14 +155,14 @@ int cluster_attn_build_neighbors_3d(const float* coords, int B, int N, int grid_
  */
 size_t cluster_attn_build_neighbors_varlen_workspace(int B, int T, int Ct, int max_n, int cs,
                                                      int k);
-int cluster_attn_build_neighbors_varlen(const float* coords, int B, int T, int Ct, int max_n,
+ca_status cluster_attn_build_neighbors_varlen(const float* coords, int B, int T, int Ct, int max_n,
                                         const int32_t* tok_off, const int32_t* clu_off,
                                         int grid_side, int cs, int k, int32_t* q_idx,
                                         int32_t* nbr, int32_t* key_idx, void* ws,
                                         size_t ws_bytes, void* hip_stream);
 /* The same for packed 3D volumes: coords [T, 3] f32 (readings of
  * cluster_attn_build_neighbors_3d); same workspace query. */
-int cluster_attn_build_neighbors_varlen_3d(const float* coords, int B, int T, int Ct, int max_n,
+ca_status cluster_attn_build_neighbors_varlen_3d(const float* coords, int B, int T, int Ct, int max_n,
                                            const int32_t* tok_off, const int32_t* clu_off,
                                            int grid_side, int cs, int k, int32_t* q_idx,
                                            int32_t* nbr, int32_t* key_idx, void* ws,
@@ -186,7 +188,7 @@ int cluster_attn_build_neighbors_varlen_3d(const float* coords, int B, int T, in
  *   lse       [B, N, H] f32 out.  A row whose list has no valid slot gets
  *             O = 0 and LSE = -inf.
  */
-int cluster_attn_fwd(int dt, int B, int N, int H, int D, int cs, int nk, float scale,
+ca_status cluster_attn_fwd(int dt, int B, int N, int H, int D, int cs, int nk, float scale,
                      const void* q, const void* k, const void* v, const int32_t* q_idx,
                      const int32_t* key_idx, void* o, float* lse, void* hip_stream);
 
@@ -213,7 +215,7 @@ size_t cluster_attn_bwd_workspace(int dt, int B, int N, int H, int D, int cs, in
  *             bytes; contents on entry are ignored.  Two calls that overlap
  *             in time must not share a workspace.
  */
-int cluster_attn_bwd(int dt, int B, int N, int H, int D, int cs, int nk, float scale,
+ca_status cluster_attn_bwd(int dt, int B, int N, int H, int D, int cs, int nk, float scale,
                      const void* q, const void* k, const void* v, const void* o,
                      const void* dout, const float* lse, const int32_t* q_idx,
                      const int32_t* key_idx, void* dq, void* dk, void* dv, void* ws,
@@ -237,7 +239,7 @@ int cluster_attn_bwd(int dt, int B, int N, int H, int D, int cs, int nk, float s
  * The result equals cluster_attn_bwd's bit for bit.
  */
 size_t cluster_attn_bwd_plan_workspace(int B, int N, int C, int cs, int nk);
-int cluster_attn_bwd_plan(int B, int N, int C, int cs, int nk, const int32_t* q_idx,
+ca_status cluster_attn_bwd_plan(int B, int N, int C, int cs, int nk, const int32_t* q_idx,
                           const int32_t* key_idx, void* plan, size_t plan_bytes,
                           void* hip_stream);
 /* The plan of a packed batch from its offsets (see
@@ -245,12 +247,12 @@ int cluster_attn_bwd_plan(int B, int N, int C, int cs, int nk, const int32_t* q_
  * image has at most 4096 tokens, else the batch as one index space.  The
  * plan has the size cluster_attn_bwd_plan_workspace(1, T, Ct, cs, nk) and
  * feeds cluster_attn_bwd_planned with B = 1, N = T, C = Ct. */
-int cluster_attn_bwd_plan_varlen(int B, int T, int Ct, int max_n, const int32_t* tok_off,
+ca_status cluster_attn_bwd_plan_varlen(int B, int T, int Ct, int max_n, const int32_t* tok_off,
                                  const int32_t* clu_off, int cs, int nk, const int32_t* q_idx,
                                  const int32_t* key_idx, void* plan, size_t plan_bytes,
                                  void* hip_stream);
 size_t cluster_attn_bwd_planned_workspace(int dt, int B, int N, int H, int D);
-int cluster_attn_bwd_planned(int dt, int B, int N, int C, int H, int D, int cs, int nk,
+ca_status cluster_attn_bwd_planned(int dt, int B, int N, int C, int H, int D, int cs, int nk,
                              float scale, const void* q, const void* k, const void* v,
                              const void* o, const void* dout, const float* lse,
                              const int32_t* q_idx, const int32_t* key_idx, const void* plan,
@@ -266,11 +268,11 @@ int cluster_attn_bwd_planned(int dt, int B, int N, int C, int H, int D, int cs, 
  * [T, H] f32, q_idx [Ct, cs] and key_idx [Ct, nk] int32 with batch-global
  * token ids; ceil(T / cs) <= Ct <= T.
  */
-int cluster_attn_fwd_varlen(int dt, int T, int Ct, int H, int D, int cs, int nk, float scale,
+ca_status cluster_attn_fwd_varlen(int dt, int T, int Ct, int H, int D, int cs, int nk, float scale,
                             const void* q, const void* k, const void* v, const int32_t* q_idx,
                             const int32_t* key_idx, void* o, float* lse, void* hip_stream);
 size_t cluster_attn_bwd_varlen_workspace(int dt, int T, int Ct, int H, int D, int cs, int nk);
-int cluster_attn_bwd_varlen(int dt, int T, int Ct, int H, int D, int cs, int nk, float scale,
+ca_status cluster_attn_bwd_varlen(int dt, int T, int Ct, int H, int D, int cs, int nk, float scale,
                             const void* q, const void* k, const void* v, const void* o,
                             const void* dout, const float* lse, const int32_t* q_idx,
                             const int32_t* key_idx, void* dq, void* dk, void* dv, void* ws,
@@ -305,7 +307,7 @@ int cluster_attn_bwd_varlen(int dt, int T, int Ct, int H, int D, int cs, int nk,
  *   coords  [B, N, 2] f32 device.   G: 1..64.   N: 0..4096.   K: 1..16.
  *   table   [B, G, G, K] int32 device out.
  */
-int cluster_attn_knn_table(const float* coords, int B, int N, int grid_side, int K,
+ca_status cluster_attn_knn_table(const float* coords, int B, int N, int grid_side, int K,
                            int32_t* table, void* hip_stream);
 
 /*
@@ -320,7 +322,7 @@ int cluster_attn_knn_table(const float* coords, int B, int N, int grid_side, int
  *   feats  [B, N, C] dt.   table [B, G, G, K] int32 (any contents in [-1, N)).
  *   out    [B, M, C] dt out.
  */
-int cluster_attn_knn_sample_fwd(int dt, int B, int N, int M, int C, int grid_side, int K, float p,
+ca_status cluster_attn_knn_sample_fwd(int dt, int B, int N, int M, int C, int grid_side, int K, float p,
                                 const float* coords, const void* feats, const float* queries,
                                 const int32_t* table, void* out, void* hip_stream);
 
@@ -342,7 +344,7 @@ size_t cluster_attn_knn_sample_bwd_workspace(int B, int N, int M, int K);
  *   ws      device workspace of cluster_attn_knn_sample_bwd_workspace bytes;
  *           two calls that overlap in time must not share it.
  */
-int cluster_attn_knn_sample_bwd(int dt, int B, int N, int M, int C, int grid_side, int K, float p,
+ca_status cluster_attn_knn_sample_bwd(int dt, int B, int N, int M, int C, int grid_side, int K, float p,
                                 const float* coords, const void* feats, const float* queries,
                                 const int32_t* table, const void* dout, void* dfeats, float* dq,
                                 float* dp, void* ws, size_t ws_bytes, void* hip_stream);
@@ -371,7 +373,7 @@ int cluster_attn_knn_sample_bwd(int dt, int B, int N, int M, int C, int grid_sid
  *   members [B, N] int32 out, offsets [B, k + 1] int32 out: the tokens of
  *           group a are members[offsets[a] .. offsets[a+1]), in token order.
  */
-int cluster_attn_merge_plan(const float* coords, const float* scores, int B, int N, int k,
+ca_status cluster_attn_merge_plan(const float* coords, const float* scores, int B, int N, int k,
                             int grid_side, int32_t* anchors, int32_t* assign, int32_t* members,
                             int32_t* offsets, void* hip_stream);
 
@@ -382,7 +384,7 @@ int cluster_attn_merge_plan(const float* coords, const float* scores, int B, int
  *   feats [B, N, C] dt (16-byte aligned, C a multiple of 8 up to 1024);
  *   members/offsets as returned by cluster_attn_merge_plan.
  */
-int cluster_attn_merge_fwd(int dt, int B, int N, int k, int C, const void* feats,
+ca_status cluster_attn_merge_fwd(int dt, int B, int N, int k, int C, const void* feats,
                            const float* coords, const float* scores, const int32_t* members,
                            const int32_t* offsets, void* out_feats, float* out_coords,
                            void* hip_stream);
@@ -396,11 +398,40 @@ int cluster_attn_merge_fwd(int dt, int B, int N, int k, int C, const void* feats
  * Every token belongs to one group and is written once (no atomics):
  * bitwise reproducible.  dfeats dt; dcoords, dscores f32.
  */
-int cluster_attn_merge_bwd(int dt, int B, int N, int k, int C, const void* feats,
+ca_status cluster_attn_merge_bwd(int dt, int B, int N, int k, int C, const void* feats,
                            const float* coords, const float* scores, const int32_t* members,
                            const int32_t* offsets, const void* dout_feats,
                            const float* dout_coords, void* dfeats, float* dcoords,
                            float* dscores, void* hip_stream);
+
+/*
+ * Debug helper, HOST pointers: checks index lists before they reach a
+ * kernel, which reads them unchecked (the conventions above make valid
+ * lists a precondition of every attention call).  For B images of N
+ * tokens in C clusters (C = ceil(N/cs); a packed batch is B = 1, N = T,
+ * C = Ct), q_idx [B, C, cs] and key_idx [B, C, nk] (key_idx may be NULL
+ * when nk = 0):
+ *   - every q_idx value is a token in [0, N) or -1; member 0 of each row is
+ *     a token and no token follows a -1 in its row;
+ *   - every token of an image appears exactly once in its q_idx rows;
+ *   - every key_idx value is in [-1, N).
+ * Returns CA_OK, or CA_ERR_SHAPE with the first offending position in
+ * cluster_attn_last_error().  Runs on the calling thread; allocates N bytes
+ * of host memory for the duration of the call.
+ */
+ca_status cluster_attn_check_lists(int B, int N, int C, int cs, int nk, const int32_t* q_idx,
+                                   const int32_t* key_idx);
+
+/*
+ * Measurement utility: copies `bytes` bytes from `src` to `dst` (device
+ * pointers, 16-byte aligned, not overlapping) with a plain streaming kernel
+ * of 16-byte loads and stores.  Timing it gives the HBM bandwidth this
+ * device actually achieves, the second reference (beside the vendor peak)
+ * for the attention kernels' effective bandwidth.  Asynchronous on
+ * `hip_stream`.  CA_ERR_NULL / CA_ERR_UNSUPPORTED (misaligned) /
+ * CA_ERR_ALIAS (overlap) / CA_ERR_HIP.
+ */
+ca_status cluster_attn_device_copy(void* dst, const void* src, size_t bytes, void* hip_stream);
 
 /* Static text for a status code. */
 const char* cluster_attn_status_string(int status);

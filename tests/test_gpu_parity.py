@@ -16,7 +16,7 @@ import torch
 import oracle as O
 from gen import make_case, stress_copy_rows, stress_duplicate_slots
 from gen.synth import stress_rng
-from parity_util import assert_finite, check_close, sampled_oracle, to_np, tol_for
+from parity_util import assert_finite, check_close, to_np, tol_for
 
 pytestmark = pytest.mark.gpu
 
@@ -297,46 +297,8 @@ def test_autograd_wrapper(ca):
         assert torch.equal(a, b)
 
 
-# ----------------------------------------------------------------------------
-# full workload sizes: sampled outputs
-# ----------------------------------------------------------------------------
-
-@pytest.mark.parametrize("name", ["stage1", "stage3", "highres", "stress"])
-def test_full_size_sampled(ca, name):
-    case = make_case(name)
-    cfg = case["cfg"]
-    print(f"case {name} full B={cfg.B} N={cfg.N} H={cfg.H}", flush=True)
-    scale = 1.0 / math.sqrt(cfg.D)
-    perm, _, key = gpu_lists(ca, case["coords"], cfg.G)
-    key_np = key.cpu().numpy()
-    if cfg.dup_frac:
-        key_np = stress_duplicate_slots(key_np, cfg.cs, stress_rng(cfg), cfg.dup_frac)
-        key = torch.from_numpy(key_np).to(DEV)
-    dev = [case[n].to(DEV) for n in ("q", "k", "v", "do")]
-    o, lse = ca.fwd(dev[0], dev[1], dev[2], perm, key, scale)
-    dq, dk, dv = ca.bwd(dev[0], dev[1], dev[2], o, dev[3], lse, perm, key, scale)
-    torch.cuda.synchronize()
-    for nm, t in (("O", o), ("LSE", lse), ("dQ", dq), ("dK", dk), ("dV", dv)):
-        assert_finite(nm, t)
-    tol = tol_for(cfg)
-    rng = np.random.default_rng(99)
-    qi = perm.cpu().numpy().reshape(cfg.B, cfg.C, cfg.cs)
-    for b in sorted(rng.choice(cfg.B, size=min(2, cfg.B), replace=False)):
-        clusters = np.sort(rng.choice(cfg.C, size=min(24, cfg.C), replace=False))
-        key_tokens = np.sort(rng.choice(cfg.N, size=min(48, cfg.N), replace=False))
-        one = lambda t: t[b:b + 1]
-        ref = sampled_oracle(one(case["q"]), one(case["k"]), one(case["v"]), one(case["do"]),
-                             qi[b], key_np[b], scale, clusters, key_tokens)
-        tq, tk = ref["q_tokens"], ref["k_tokens"]
-        check_close("O", to_np(o[b, tq]), ref["o"], tol["o"], tol["rel"])
-        check_close("LSE", to_np(lse[b, tq]), ref["lse"], tol["lse"], False)
-        check_close("dQ", to_np(dq[b, tq]), ref["dq"], tol["g"], tol["rel"])
-        check_close("dK", to_np(dk[b, tk]), ref["dk"], tol["g"], tol["rel"])
-        check_close("dV", to_np(dv[b, tk]), ref["dv"], tol["g"], tol["rel"])
-    # properties that hold at any size: sum rules over every token
-    sdk = dk.double().sum(dim=1).abs().max().item()
-    sdv = (dv.double().sum(dim=1) - dev[3].double().sum(dim=1)).abs().max().item()
-    print(f"  sum rules: |sum dK| {sdk:.3e}, |sum dV - sum dO| {sdv:.3e}", flush=True)
+# Whole-batch, every-element parity at the benchmarked launches lives in
+# test_gpu_full_parity.py.
 
 
 def test_planned_backward_equals_backward(ca):
