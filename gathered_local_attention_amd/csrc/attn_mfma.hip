@@ -39,6 +39,7 @@
 //    of every row is a token, so each store instruction keeps at least one
 //    active lane (the pipelines count store instructions).
 #include "common.h"
+#include "mfma_util.h"
 
 #include <algorithm>
 
@@ -46,88 +47,10 @@ namespace ca {
 
 namespace {
 
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef float f32x2 __attribute__((ext_vector_type(2)));
-
-constexpr int D = 32;
 constexpr int CS = 8;
 constexpr int NK = 48;
 constexpr int kWaves = 4;
-constexpr uint32_t kRow = D * 2;   // bytes of one head row (bf16 / fp16)
-constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kLn2 = 0.6931471805599453f;
-
-template <typename T> struct Mfma;
-
-template <> struct Mfma<bf16> {
-  typedef __bf16 v8 __attribute__((ext_vector_type(8)));
-  typedef __bf16 v2 __attribute__((ext_vector_type(2)));
-  static __device__ __forceinline__ f32x4 mma(uint4 a, uint4 b, f32x4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8, a),
-                                                   __builtin_bit_cast(v8, b), c, 0, 0, 0);
-  }
-  static __device__ __forceinline__ f32x2 unpack(uint32_t w) {
-    return f32x2{__uint_as_float(w << 16), __uint_as_float(w & 0xFFFF0000u)};
-  }
-};
-
-template <> struct Mfma<f16> {
-  typedef _Float16 v8 __attribute__((ext_vector_type(8)));
-  typedef _Float16 v2 __attribute__((ext_vector_type(2)));
-  static __device__ __forceinline__ f32x4 mma(uint4 a, uint4 b, f32x4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(v8, a),
-                                                  __builtin_bit_cast(v8, b), c, 0, 0, 0);
-  }
-  static __device__ __forceinline__ f32x2 unpack(uint32_t w) {
-    return __builtin_convertvector(__builtin_bit_cast(v2, w), f32x2);
-  }
-};
-
-// two floats -> one dword of T (round to nearest even, one instruction)
-template <typename T>
-__device__ __forceinline__ uint32_t pack2(float a, float b) {
-  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{a, b}), typename Mfma<T>::v2));
-}
-
-template <typename T>
-__device__ __forceinline__ uint2 pack4(f32x4 x) {
-  return make_uint2(pack2<T>(x[0], x[1]), pack2<T>(x[2], x[3]));
-}
-
-__device__ __forceinline__ uint4 cat(uint2 a, uint2 b) { return make_uint4(a.x, a.y, b.x, b.y); }
-__device__ __forceinline__ uint4 pad(uint2 a) { return make_uint4(a.x, a.y, 0u, 0u); }
-__device__ __forceinline__ uint4 sel(bool c, uint4 a) {
-  return c ? a : make_uint4(0u, 0u, 0u, 0u);
-}
-
-// 16-byte load at a 32-bit byte offset from a (wave-uniform) base pointer
-__device__ __forceinline__ uint4 ld16(const void* base, uint32_t off) {
-  return *reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(base) + off);
-}
-template <typename V>
-__device__ __forceinline__ void stv(void* base, uint32_t off, V v) {
-  *reinterpret_cast<V*>(reinterpret_cast<char*>(base) + off) = v;
-}
-
-
-// Reductions over the four 16-lane rows (lanes c, c+16, c+32, c+48) with the
-// gfx950 row-swap moves: permlane16_swap(x, x) yields x of rows {0,0,2,2} and
-// {1,1,3,3}, permlane32_swap(x, x) x of halves {0,0} and {1,1} (checked on the
-// hardware), so two VALU swaps replace two LDS-crossbar shuffles.
-__device__ __forceinline__ float xrow16(float v, bool take_max) {
-  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false,
-                                                  false);
-  const float a = __uint_as_float(r[0]), b = __uint_as_float(r[1]);
-  return take_max ? fmaxf(a, b) : a + b;
-}
-__device__ __forceinline__ float xrow32(float v, bool take_max) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false,
-                                                  false);
-  const float a = __uint_as_float(r[0]), b = __uint_as_float(r[1]);
-  return take_max ? fmaxf(a, b) : a + b;
-}
-__device__ __forceinline__ float shfl_max16_32(float v) { return xrow32(xrow16(v, true), true); }
-__device__ __forceinline__ float shfl_sum16_32(float v) { return xrow32(xrow16(v, false), false); }
+__device__ __forceinline__ uint32_t swz(int s) { return (uint32_t)((s & 15) >> 1); }
 
 // ---------------------------------------------------------------------------
 // forward, LDS-staged gathers
@@ -144,43 +67,6 @@ constexpr int kSlotBytes = 2 * kRow;            // one slot: both heads of the p
 constexpr int kTileBytes = NK * kSlotBytes;     // 6 KiB per tensor
 constexpr int kWaveLds = 2 * kTileBytes;        // K and V
 
-typedef __attribute__((address_space(3))) void lds_void;
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-
-__device__ __forceinline__ uint32_t swz(int s) { return (uint32_t)((s & 15) >> 1); }
-
-__device__ __forceinline__ uint4 lds16(const char* base, uint32_t off) {
-  return *reinterpret_cast<const uint4*>(base + off);
-}
-__device__ __forceinline__ uint2 lds_tr8(const char* base, uint32_t off) {
-  const s16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (lds_s16x4*)((__attribute__((address_space(3))) char*)(base + off)));
-  return __builtin_bit_cast(uint2, r);
-}
-
-// One 16-byte direct-to-LDS load per lane: global (base + voff) -> LDS
-// (lds + 16 * lane), lds wave-uniform.  Written as asm with no outputs so that
-// the compiler does not guard every later LDS read with a full vmcnt wait;
-// the kernels wait for these loads themselves with s_waitcnt vmcnt(n), which
-// counts them in issue order together with every other vector-memory op.
-__device__ __forceinline__ void dma16(const void* base, uint32_t voff, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
-               :
-               : "v"(voff), "s"(base), "s"(lds)
-               : "memory", "m0");
-}
-
-// s_waitcnt with vmcnt = N (0..63) and no wait on the other counters
-template <int N>
-__device__ __forceinline__ void wait_vm() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
-}
-
-// Position of an item (cluster bc of the batch, head pair hp) walked
-// incrementally: a wavefront's items are consecutive, so one division at
-// the start replaces the per-item ones.
 struct ItemPos {
   int bc, hp, cin, img;   // cluster (batch-wide), head pair, cluster in image, image base token
   __device__ void init(int item, int HP, int C, int N) {
@@ -211,29 +97,6 @@ struct ItemPos {
   }
 };
 
-// Direct-to-LDS 4-byte load per lane: global (base + voff) -> LDS (lds + 4 * lane).
-__device__ __forceinline__ void dma4(const void* base, uint32_t voff, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dword %0, %1"
-               :
-               : "v"(voff), "s"(base), "s"(lds)
-               : "memory", "m0");
-}
-
-// s_waitcnt vmcnt(n) for a run-time n from the few values the pipelines use
-// (a larger count is never required: any n' <= n is safe, only slower)
-__device__ __forceinline__ void wait_vm_n(int n) {
-  if (n >= 11) wait_vm<11>();
-  else if (n >= 9) wait_vm<9>();
-  else if (n >= 8) wait_vm<8>();
-  else if (n >= 6) wait_vm<6>();
-  else if (n >= 5) wait_vm<5>();
-  else if (n >= 3) wait_vm<3>();
-  else if (n >= 2) wait_vm<2>();
-  else wait_vm<0>();
-}
-
-// wait for this wave's outstanding LDS reads (before a DMA overwrites them)
-__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 
 // LDS tile of one item's indices: ints 0..47 key tokens of the 48 slots,
 // 48..55 the query tokens of the cluster, 56..63 unused (never written).

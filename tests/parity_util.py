@@ -76,3 +76,72 @@ def sampled_oracle(q, k, v, do, q_idx, key_idx, scale, clusters, key_tokens, wit
         out["k_tokens"] = key_tokens
         out["dk"], out["dv"] = dk[0, key_tokens], dv[0, key_tokens]
     return out
+
+
+def term_magnitudes(q, k, v, do, q_idx, key_idx, scale, cluster_block: int = 512):
+    """Sums of the magnitudes of the terms that make up every output element,
+    for floating-point error bars of the form u * sum|terms| (the standard
+    bound for a rounded sum of products).  Returns fp64 arrays [B, N, H, D]:
+
+      o:  sum_s P_ms |V_sd|
+      dq: scale sum_s (|dS_ms| + P_ms E_m) |K_sd|
+      dk: scale sum over the (m, s) holding key j of (|dS_ms| + P_ms E_m) |Q_md|
+      dv: sum over the same (m, s) of P_ms |dO_md|
+
+    with E_m = sum_d |dO_md| (|O_md| + o_md), which bounds (in units of u) the
+    error of Delta_m = <dO_m, O_m> when O is the kernel's rounded output.
+    P, dS are the exact (fp64) probabilities and their gradients, computed
+    per cluster tile as in the gathered oracle.
+
+    Also returns absolute floors, for operands rounded to fp16 below its
+    normal range (|x| < 2^-14, absolute error up to 2^-25 whatever x is):
+      o_floor:  sum_s |V_sd|            (unnormalised probabilities, <= 1,
+                                          then divided by their sum >= 1)
+      dq_floor: scale sum_s |K_sd|      (one dS per slot)
+      dk_floor: scale sum over (m, s) holding j of |Q_md|
+      dv_floor: sum over the same (m, s) of |dO_md|"""
+    f = lambda x: x.detach().double().numpy() if hasattr(x, "detach") else np.asarray(x, np.float64)
+    Q, K, V, dO = f(q), f(k), f(v), f(do)
+    B, N, H, D = Q.shape
+    names = ("o", "dq", "dk", "dv", "o_floor", "dq_floor", "dk_floor", "dv_floor")
+    out = {n: np.zeros((B, N, H, D)) for n in names}
+
+    def rows(X, idx):
+        g = X[np.where(idx >= 0, idx, 0)]
+        g[idx < 0] = 0.0
+        return g
+
+    for b in range(B):
+        qi = np.asarray(q_idx[b]).astype(np.int64)
+        ki = np.asarray(key_idx[b]).astype(np.int64)
+        for c0 in range(0, qi.shape[0], cluster_block):
+            qb, kb = qi[c0:c0 + cluster_block], ki[c0:c0 + cluster_block]
+            Qc, dOc = rows(Q[b], qb), rows(dO[b], qb)
+            Kg, Vg = rows(K[b], kb), rows(V[b], kb)
+            S = scale * np.einsum("cmhd,cshd->chms", Qc, Kg)
+            valid = (kb >= 0)[:, None, None, :]
+            has = valid.any(axis=-1)
+            m = np.where(has, np.where(valid, S, -np.inf).max(axis=-1), 0.0)
+            E = np.where(valid, np.exp(S - m[..., None]), 0.0)
+            P = E / np.where(has, E.sum(axis=-1), 1.0)[..., None]
+            P = P * (qb >= 0)[:, None, :, None]
+            Oc = np.einsum("chms,cshd->cmhd", P, Vg)
+            magO = np.einsum("chms,cshd->cmhd", P, np.abs(Vg))
+            delta = np.einsum("cmhd,cmhd->chm", dOc, Oc)
+            dS = P * (np.einsum("cmhd,cshd->chms", dOc, Vg) - delta[..., None])
+            Em = np.einsum("cmhd,cmhd->chm", np.abs(dOc), np.abs(Oc) + magO)
+            W = np.abs(dS) + P * Em[..., None]
+            live = qb >= 0
+            out["o"][b][qb[live]] = magO[live]
+            out["dq"][b][qb[live]] = scale * np.einsum("chms,cshd->cmhd", W, np.abs(Kg))[live]
+            sel = kb >= 0
+            np.add.at(out["dk"][b], kb[sel], (scale * np.einsum("chms,cmhd->cshd", W, np.abs(Qc)))[sel])
+            np.add.at(out["dv"][b], kb[sel], np.einsum("chms,cmhd->cshd", P, np.abs(dOc))[sel])
+            one = valid * (qb >= 0)[:, None, :, None] * np.ones_like(P)
+            out["o_floor"][b][qb[live]] = np.einsum("chms,cshd->cmhd", one, np.abs(Vg))[live]
+            out["dq_floor"][b][qb[live]] = scale * np.einsum("chms,cshd->cmhd", one,
+                                                             np.abs(Kg))[live]
+            np.add.at(out["dk_floor"][b], kb[sel],
+                      (scale * np.einsum("chms,cmhd->cshd", one, np.abs(Qc)))[sel])
+            np.add.at(out["dv_floor"][b], kb[sel], np.einsum("chms,cmhd->cshd", one, np.abs(dOc))[sel])
+    return out
