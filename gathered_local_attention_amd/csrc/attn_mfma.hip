@@ -67,6 +67,9 @@ constexpr int kSlotBytes = 2 * kRow;            // one slot: both heads of the p
 constexpr int kTileBytes = NK * kSlotBytes;     // 6 KiB per tensor
 constexpr int kWaveLds = 2 * kTileBytes;        // K and V
 
+// Position of an item (cluster bc of the batch, head pair hp) walked
+// incrementally: a wavefront's items are consecutive, so one division at
+// the start replaces the per-item ones.
 struct ItemPos {
   int bc, hp, cin, img;   // cluster (batch-wide), head pair, cluster in image, image base token
   __device__ void init(int item, int HP, int C, int N) {

@@ -27,6 +27,33 @@ struct RevEntry {
   uint64_t mult;
 };
 
+// ---- window ("tile") plan of the matrix-core kernels -----------------------
+// Consecutive clusters of an image are taken kWin at a time (a Morton window;
+// for a packed batch the windows run over the whole batch).  Per window:
+//  * query record (forward and the query-major backward pass), stride
+//    qrec_stride(nk) ints: c0 (first cluster, batch-wide), nc (clusters),
+//    u (distinct key tokens of the window's lists), base (token id offset
+//    added to the image-local ids; 0 for a packed batch), the 64 query tokens
+//    (q_idx rows, -1 after nc clusters), the u key tokens ascending (padded
+//    to a multiple of 32 with a valid token), then the multiplicity table
+//    mult[8][8 nk] (bytes: how many slots of the window's cluster c hold key
+//    token x).
+//  * key record (key-major pass), kKRec ints: start, E (entries), c0, base,
+//    nc, 3 spare, the 64 key tokens of the window's clusters.
+//  * entries [start, start + E) in `kent` (kEnt ints each): the 8 query
+//    tokens of a query cluster i reading the window, then mult[64] (bytes:
+//    how many slots of i hold the window's key token 8 c + m).  Entries are
+//    ordered by i.  They live in the index space of `rev` (a window's raw
+//    entries, its key clusters' segments, are contiguous).
+constexpr int kWin = 8;
+constexpr int kQRecHead = 4 + 64;   // ints before the key tokens
+constexpr int kKRec = 96;           // ints per key record (72 used)
+constexpr int kEnt = 24;            // ints per entry: 8 tokens + 64 multiplicity bytes
+__host__ __device__ constexpr int qrec_stride(int nk) {
+  return (kQRecHead + 3 * 8 * nk + 63) / 64 * 64;
+}
+static inline int64_t windows_of(int64_t B, int64_t C) { return B * ((C + kWin - 1) / kWin); }
+
 // ---- workspace layout of the backward pass --------------------------------
 // Two parts: the per-call part (LSE/Delta pairs of pass A, read by pass B)
 // and the plan (the transposed slot lists, a function of q_idx and key_idx
@@ -45,6 +72,9 @@ struct BwdWorkspace {
   RevEntry* stage;   // [B, C, nk]  entry of the first slot of i pointing into j
   RevEntry* rev;     // [B, C*nk]   per key cluster, sorted by i (image b from b*C*nk)
   int32_t* rtok;     // [B, C*nk, cs] query tokens of entry e (q_idx row of its i)
+  int32_t* qrec;     // [NW, qrec_stride(nk)] query-window records
+  int32_t* krec;     // [NW, kKRec]            key-window records
+  int32_t* kent;     // [B, C*nk, kEnt]         key-window entries
   size_t bytes;
 };
 
@@ -82,6 +112,11 @@ static inline BwdWorkspace plan_layout(void* base, int64_t B, int64_t N, int64_t
   w.stage = (RevEntry*)c.take((size_t)(B * C * nk) * sizeof(RevEntry));
   w.rev = (RevEntry*)c.take((size_t)(B * C * nk) * sizeof(RevEntry));
   w.rtok = (int32_t*)c.take((size_t)(B * C * nk) * 8 * sizeof(int32_t));
+  const int64_t NW = windows_of(B, C);
+  // records are read in fixed-size pieces that may run past the last one
+  w.qrec = (int32_t*)c.take((size_t)(NW * qrec_stride((int)nk)) * 4 + 4096);
+  w.krec = (int32_t*)c.take((size_t)(NW * kKRec) * 4);
+  w.kent = (int32_t*)c.take((size_t)(B * C * nk) * kEnt * 4 + 4096);
   w.bytes = c.p;
   return w;
 }
@@ -311,6 +346,23 @@ bool mfma_supported(int dt, int B, int N, int C, int H, int nk);
 hipError_t launch_fwd_mfma(int dt, int B, int N, int C, int H, float scale, const void* q,
                            const void* k, const void* v, const int32_t* q_idx,
                            const int32_t* key_idx, void* o, float* lse, hipStream_t st);
+
+// Window plan (after launch_bwd_plan has built seg / rev / rtok): the query
+// and key records of every window.  `packed`: the lists hold batch-global ids.
+hipError_t launch_tile_plan(int B, int N, int C, int nk, bool packed, const int32_t* q_idx,
+                            const int32_t* key_idx, const BwdWorkspace& w, hipStream_t st);
+
+// Window-tiled matrix-core kernels (bf16 / f16, any nk = 8k, k <= 8) on a
+// window plan: forward, and the backward passes (bit 1 = query-major: Delta,
+// dQ; bit 2 = key-major: dK, dV).
+bool tile_supported(int dt, int B, int N, int C, int H, int nk);
+hipError_t launch_fwd_tile(int dt, int B, int N, int C, int H, int nk, float scale, const void* q,
+                           const void* k, const void* v, const BwdWorkspace& w, void* o,
+                           float* lse, hipStream_t st);
+hipError_t launch_bwd_tile(int pass, int dt, int B, int N, int C, int H, int nk, float scale,
+                           const void* q, const void* k, const void* v, const void* o,
+                           const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                           const BwdWorkspace& w, hipStream_t st);
 
 hipError_t launch_bwd_mfma(int pass, int dt, int B, int N, int C, int H, int nk, float scale,
                            const void* q, const void* k, const void* v, const void* o,
