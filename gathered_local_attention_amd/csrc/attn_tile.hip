@@ -62,33 +62,39 @@ __device__ __forceinline__ uint32_t row_chunk(int r, uint32_t chunk) {
   return (uint32_t)r * kRowB + 16u * (chunk ^ sw(r));
 }
 
-// Gather `nrows` (a multiple of 16, at most 16 * MAXI * 2) head rows into a
-// staged block: instruction i (of this wavefront: i = wv, wv + 2, ...)
-// fills rows 16 i .. 16 i + 15; lane l fetches chunk (l & 3) ^ sw(row) of
-// row 16 i + l / 4, so that LDS position l & 3 of that row holds it.
-// `toks` (LDS) gives the token of each row; -1 takes `fallback`.
-template <int MAXI>
-__device__ __forceinline__ void gather_rows(const void* src, const int32_t* toks, int fallback,
-                                            int nrows, uint32_t dst, int base, int H, int h,
-                                            int lane, int wv) {
-  const int ni = nrows >> 4;
-  int tk[MAXI];
-#pragma unroll
-  for (int j = 0; j < MAXI; ++j) {
-    const int i = wv + 2 * j;
-    const int t = i < ni ? toks[16 * i + (lane >> 2)] : 0;
-    tk[j] = t < 0 ? fallback : t;
+constexpr int kRecBytes = 4 * kQRecHead + 12 * 512;   // a query record, nk <= 64
+
+// Direct-to-LDS copy of `bytes` (a multiple of 16) contiguous bytes, split
+// over the workgroup's two wavefronts (instruction i by wavefront i & 1).
+__device__ __forceinline__ void copy_lds(const void* src, uint32_t src_off, int bytes, uint32_t dst,
+                                         int lane, int wv) {
+  const int n16 = bytes >> 4;
+  for (int i = wv; 64 * i < n16; i += 2) {
+    const int p = 64 * i + lane;
+    if (p < n16) dma16(src, src_off + 16u * (uint32_t)p, dst + 1024u * (uint32_t)i);
   }
-#pragma unroll
-  for (int j = 0; j < MAXI; ++j) {
-    const int i = wv + 2 * j;
-    if (i < ni) {
-      const int row = 16 * i + (lane >> 2);
-      const uint32_t chunk = (uint32_t)(lane & 3) ^ sw(row);
-      dma16(src, ((uint32_t)(base + tk[j]) * (uint32_t)H + (uint32_t)h) * kRowB + 16u * chunk,
-            dst + 1024u * (uint32_t)i);
-    }
-  }
+}
+
+// Gather the head-h rows of up to 64 tokens (`nrows` a multiple of 16) into a
+// staged block: instruction i fills rows 16 i .. 16 i + 15 (wavefront wv
+// issues i = wv and wv + 2); lane l fetches chunk (l & 3) ^ sw(row) of row
+// 16 i + l / 4, so that position l & 3 of the row holds it.  `toks` (LDS):
+// the row tokens, -1 taking `fallback`.
+__device__ __forceinline__ void gather64(const void* src, const int32_t* toks, int fallback,
+                                         int nrows, uint32_t dst, int base, int H, int h,
+                                         int lane, int wv) {
+  const int r0 = 16 * wv + (lane >> 2), r1 = r0 + 32;
+  int t0 = r0 < nrows ? toks[r0] : fallback;
+  int t1 = r1 < nrows ? toks[r1] : fallback;
+  t0 = t0 < 0 ? fallback : t0;
+  t1 = t1 < 0 ? fallback : t1;
+  const uint32_t c0 = (uint32_t)(lane & 3) ^ sw(r0), c1 = (uint32_t)(lane & 3) ^ sw(r1);
+  if (16 * wv < nrows)
+    dma16(src, ((uint32_t)(base + t0) * (uint32_t)H + (uint32_t)h) * kRowB + 16u * c0,
+          dst + 1024u * (uint32_t)wv);
+  if (16 * wv + 32 < nrows)
+    dma16(src, ((uint32_t)(base + t1) * (uint32_t)H + (uint32_t)h) * kRowB + 16u * c1,
+          dst + 1024u * (uint32_t)(wv + 2));
 }
 
 // four multiplicity bytes -> floats
@@ -96,45 +102,91 @@ __device__ __forceinline__ float mbyte(uint32_t w, int i) {
   return (float)((w >> (8 * i)) & 0xffu);
 }
 
-// query record of window w: head + key tokens and multiplicities of the
-// chunk [k0, k0 + KCH) into LDS (head and tokens by wavefront 0, the eight
-// multiplicity rows split over both)
-template <int KCH>
-__device__ __forceinline__ void load_qrec(const int32_t* qrec, int64_t rec_off, int kmax, int k0,
-                                          bool head, uint32_t l_head, uint32_t l_kt, uint32_t l_mt,
-                                          int lane, int wv) {
-  const uint32_t ro = (uint32_t)(rec_off * 4);
-  if (wv == 0) {
-    if (head && lane < kQRecHead / 4) dma16(qrec, ro + 16u * lane, l_head);
-    if (lane < KCH / 4) dma16(qrec, ro + 4u * (kQRecHead + k0) + 16u * lane, l_kt);
-  }
-  constexpr int kPer = KCH / 16;   // 16-byte pieces per multiplicity row
-#pragma unroll
-  for (int i = wv; i * 64 < 8 * kPer; i += 2) {
-    const int p = 64 * i + lane;
-    if (p < 8 * kPer) {
-      const int c = p / kPer, col = p - c * kPer;
-      dma16(qrec, ro + 4u * (kQRecHead + kmax) + (uint32_t)(c * kmax + k0 + 16 * col),
-            l_mt + 1024u * (uint32_t)i);
-    }
-  }
+// A operands of a 16-row block read transposed: lane 4e + qq of row group g
+// receives dim 16 hf + (lane & 15) of rows r0 + 4 g + e and r0 + 16 + 4 g + e
+__device__ __forceinline__ uint4 tr_pair(const char* blk, int r0, int hf, int g, int e, int qq) {
+  const uint32_t c = (uint32_t)(2 * hf + (qq >> 1));
+  const int ra = r0 + 4 * g + e, rb = ra + 16;
+  return cat(lds_tr8(blk, row_chunk(ra, c) + 8u * (qq & 1)),
+             lds_tr8(blk, row_chunk(rb, c) + 8u * (qq & 1)));
 }
 
 // ---------------------------------------------------------------------------
 // forward
 // ---------------------------------------------------------------------------
-template <int KCH>
+// Per tile: the query record (flat copy), the 64 query rows, then the key
+// rows of the window's union streamed 64 at a time through two buffers: the
+// next chunk's gathers are issued before the current chunk is computed.
 struct FwdLds {
-  static constexpr int kHead = 0, kKt = 512, kMt = kKt + 4 * KCH, kQ = kMt + 8 * KCH,
-                       kK = kQ + 64 * 64, kV = kK + 64 * KCH, kBytes = kV + 64 * KCH;
+  static constexpr int kRec = 0, kQ = kRecBytes, kKv = kQ + 4096,
+                       kBytes = kKv + 2 * 8192;   // per buffer: K 4 KiB then V 4 KiB
 };
 
-template <typename T, int KCH>
+template <typename T, int NB>
+__device__ __forceinline__ void fwd_step(const char* kbuf, const char* vbuf, const uint8_t* mt,
+                                         int kmax, int col0, const uint4 (&qv)[2],
+                                         const int (&cl)[2], float scale_log2, float (&mrun)[2],
+                                         float (&lrun)[2], f32x4 (&oacc)[2][2], int c16, int g,
+                                         int e, int qq) {
+  const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+  uint4 ka[NB];
+#pragma unroll
+  for (int kb = 0; kb < NB; ++kb) ka[kb] = lds16(kbuf, row_chunk(16 * kb + c16, (uint32_t)g));
+  uint4 vt[NB / 2][2];
+#pragma unroll
+  for (int kg = 0; kg < NB / 2; ++kg)
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) vt[kg][hf] = tr_pair(vbuf, 32 * kg, hf, g, e, qq);
+#pragma unroll
+  for (int cb = 0; cb < 2; ++cb) {
+    f32x4 s[NB];
+    uint32_t mw[NB];
+#pragma unroll
+    for (int kb = 0; kb < NB; ++kb) {
+      s[kb] = Mfma<T>::mma(ka[kb], qv[cb], z);
+      mw[kb] = *reinterpret_cast<const uint32_t*>(mt + cl[cb] * kmax + col0 + 16 * kb + 4 * g);
+    }
+    float lmax = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < NB; ++kb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float t = mbyte(mw[kb], i) != 0.f ? s[kb][i] * scale_log2 : -INFINITY;
+        s[kb][i] = t;
+        lmax = fmaxf(lmax, t);
+      }
+    const float mnew = fmaxf(mrun[cb], shfl_max16_32(lmax));
+    const float mref = mnew == -INFINITY ? 0.f : mnew;
+    const float alpha = __builtin_amdgcn_exp2f(mrun[cb] - mref);
+    mrun[cb] = mnew;
+    float lsum = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < NB; ++kb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        // a masked key has t = -inf, so its term is 0 * 0
+        const float p = mbyte(mw[kb], i) * __builtin_amdgcn_exp2f(s[kb][i] - mref);
+        s[kb][i] = p;
+        lsum += p;
+      }
+    lrun[cb] = lrun[cb] * alpha + lsum;
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) oacc[cb][hf] *= alpha;
+#pragma unroll
+    for (int kg = 0; kg < NB / 2; ++kg) {
+      const uint4 bp = cat(pack4<T>(s[2 * kg]), pack4<T>(s[2 * kg + 1]));
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) oacc[cb][hf] = Mfma<T>::mma(vt[kg][hf], bp, oacc[cb][hf]);
+    }
+  }
+}
+
+template <typename T>
 __global__ void __launch_bounds__(kTThreads)
 fwd_tile_kernel(int H, int ntiles, int kmax, int qstride, float scale_log2,
                 const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
                 const int32_t* __restrict__ qrec, T* __restrict__ o, float* __restrict__ lse) {
-  typedef FwdLds<KCH> L;
+  typedef FwdLds L;
   __shared__ __attribute__((aligned(1024))) char lds[L::kBytes];
   const int tile = xcd_remap(blockIdx.x, gridDim.x);
   if (tile >= ntiles) return;
@@ -143,134 +195,58 @@ fwd_tile_kernel(int H, int ntiles, int kmax, int qstride, float scale_log2,
   const int wv = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   const int c16 = lane & 15, g = lane >> 4;
   const int e = c16 >> 2, qq = c16 & 3;
-  const int32_t* rh = reinterpret_cast<const int32_t*>(lds + L::kHead);
-  const int32_t* kt = reinterpret_cast<const int32_t*>(lds + L::kKt);
-  const uint8_t* mt = reinterpret_cast<const uint8_t*>(lds + L::kMt);
+  const int32_t* rec = reinterpret_cast<const int32_t*>(lds + L::kRec);
+  const int32_t* ktok = rec + kQRecHead;
+  const uint8_t* mt = reinterpret_cast<const uint8_t*>(rec + kQRecHead + kmax);
   const char* sq = lds + L::kQ;
-  const char* sk = lds + L::kK;
-  const char* sv = lds + L::kV;
-  const int64_t rec_off = (int64_t)w * qstride;
 
-  load_qrec<KCH>(qrec, rec_off, kmax, 0, true, lds_addr(lds + L::kHead), lds_addr(kt),
-                 lds_addr(mt), lane, wv);
+  copy_lds(qrec, (uint32_t)((int64_t)w * qstride * 4), 4 * kQRecHead + 12 * kmax,
+           lds_addr(lds + L::kRec), lane, wv);
   wait_vm<0>();
   __syncthreads();
-  const int nc = rh[1], u = rh[2], base = rh[3];
-  const int q0 = rh[4];
-  const int32_t* qtok = rh + 4;
-  gather_rows<2>(q, qtok, q0, 64, lds_addr(sq), base, H, h, lane, wv);
-  int nrows = min(u, KCH);
-  nrows = (nrows + 31) & ~31;
-  gather_rows<KCH / 32>(k, kt, q0, nrows, lds_addr(sk), base, H, h, lane, wv);
-  gather_rows<KCH / 32>(v, kt, q0, nrows, lds_addr(sv), base, H, h, lane, wv);
-  wait_vm<0>();
-  __syncthreads();
-
-  const bool active = 4 * wv < nc;   // this wavefront's clusters exist
-  const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-  uint4 qv[2];
-  int cl[2];
-#pragma unroll
-  for (int cb = 0; cb < 2; ++cb) {
-    const int row = 32 * wv + 16 * cb + c16;
-    qv[cb] = lds16(sq, row_chunk(row, (uint32_t)g));
-    cl[cb] = 4 * wv + 2 * cb + (c16 >> 3);
+  const int nc = __builtin_amdgcn_readfirstlane(rec[1]);
+  const int u = __builtin_amdgcn_readfirstlane(rec[2]);
+  const int base = __builtin_amdgcn_readfirstlane(rec[3]);
+  const int q0 = __builtin_amdgcn_readfirstlane(rec[4]);
+  const int32_t* qtok = rec + 4;
+  const int upad = (u + 31) & ~31;
+  const int nch = (upad + 63) >> 6;
+  if (nch > 0) {
+    gather64(q, qtok, q0, 64, lds_addr(sq), base, H, h, lane, wv);
+    const int r = min(64, upad);
+    gather64(k, ktok, q0, r, lds_addr(lds + L::kKv), base, H, h, lane, wv);
+    gather64(v, ktok, q0, r, lds_addr(lds + L::kKv + 4096), base, H, h, lane, wv);
   }
+  const bool active = 4 * wv < nc;
+  const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+  uint4 qv[2] = {make_uint4(0u, 0u, 0u, 0u), make_uint4(0u, 0u, 0u, 0u)};
+  int cl[2];
   float mrun[2] = {-INFINITY, -INFINITY}, lrun[2] = {0.f, 0.f};
   f32x4 oacc[2][2] = {{z, z}, {z, z}};
+#pragma unroll
+  for (int cb = 0; cb < 2; ++cb) cl[cb] = 4 * wv + 2 * cb + (c16 >> 3);
 
-  for (int k0 = 0; k0 < u; k0 += KCH) {
-    if (k0 > 0) {   // a further chunk of the window's keys (long lists only)
-      __syncthreads();
-      load_qrec<KCH>(qrec, rec_off, kmax, k0, false, 0u, lds_addr(kt), lds_addr(mt), lane, wv);
-      wait_vm<0>();
-      __syncthreads();
-      nrows = (min(u - k0, KCH) + 31) & ~31;
-      gather_rows<KCH / 32>(k, kt, q0, nrows, lds_addr(sk), base, H, h, lane, wv);
-      gather_rows<KCH / 32>(v, kt, q0, nrows, lds_addr(sv), base, H, h, lane, wv);
-      wait_vm<0>();
-      __syncthreads();
+  for (int c = 0; c < nch; ++c) {
+    wait_vm<0>();
+    __syncthreads();
+    if (c == 0 && active) {
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb) qv[cb] = lds16(sq, row_chunk(32 * wv + 16 * cb + c16, (uint32_t)g));
+    }
+    if (c + 1 < nch) {   // the next chunk's rows land while this one is computed
+      const int r = min(64, upad - 64 * (c + 1));
+      const uint32_t nb = lds_addr(lds + L::kKv + 8192 * ((c + 1) & 1));
+      gather64(k, ktok + 64 * (c + 1), q0, r, nb, base, H, h, lane, wv);
+      gather64(v, ktok + 64 * (c + 1), q0, r, nb + 4096u, base, H, h, lane, wv);
     }
     if (!active) continue;
-    for (int s = 0; s < nrows; s += 64) {
-      const int nb = min(4, (nrows - s) >> 4);   // 4 or 2 key blocks of 16
-      f32x4 sacc[4][2];
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
-        if (kb < nb) {
-          const int kr = s + 16 * kb + c16;
-          const uint4 ka = lds16(sk, row_chunk(kr, (uint32_t)g));
-#pragma unroll
-          for (int cb = 0; cb < 2; ++cb) sacc[kb][cb] = Mfma<T>::mma(ka, qv[cb], z);
-        }
-      }
-      uint4 bp[2][2];
-#pragma unroll
-      for (int cb = 0; cb < 2; ++cb) {
-        uint32_t mw[4];
-        float t[4][4];
-        float lmax = -INFINITY;
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb) {
-          if (kb < nb) {
-            mw[kb] = *reinterpret_cast<const uint32_t*>(mt + cl[cb] * KCH + s + 16 * kb + 4 * g);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              t[kb][i] = sacc[kb][cb][i] * scale_log2;
-              if ((mw[kb] >> (8 * i)) & 0xffu) lmax = fmaxf(lmax, t[kb][i]);
-            }
-          }
-        }
-        const float mnew = fmaxf(mrun[cb], shfl_max16_32(lmax));
-        const float mref = mnew == -INFINITY ? 0.f : mnew;
-        const float alpha = __builtin_amdgcn_exp2f(mrun[cb] - mref);
-        float lsum = 0.f;
-        float p[4][4];
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb) {
-          if (kb < nb) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const float m = mbyte(mw[kb], i);
-              p[kb][i] = m != 0.f ? m * __builtin_amdgcn_exp2f(t[kb][i] - mref) : 0.f;
-              lsum += p[kb][i];
-            }
-          } else {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) p[kb][i] = 0.f;
-          }
-        }
-        lrun[cb] = lrun[cb] * alpha + lsum;
-        mrun[cb] = mnew;
-#pragma unroll
-        for (int hf = 0; hf < 2; ++hf) oacc[cb][hf] *= alpha;
-#pragma unroll
-        for (int kg = 0; kg < 2; ++kg) {
-          const f32x4 pa = {p[2 * kg][0], p[2 * kg][1], p[2 * kg][2], p[2 * kg][3]};
-          const f32x4 pb = {p[2 * kg + 1][0], p[2 * kg + 1][1], p[2 * kg + 1][2], p[2 * kg + 1][3]};
-          bp[cb][kg] = cat(pack4<T>(pa), pack4<T>(pb));
-        }
-      }
-      // O^T += V^T P^T: lane 4e + qq of row group g reads dims
-      // 16 hf + 4 qq .. of key row s + 32 kg + 16 blk + 4 g + e
-#pragma unroll
-      for (int kg = 0; kg < 2; ++kg) {
-        if (2 * kg < nb) {
-#pragma unroll
-          for (int hf = 0; hf < 2; ++hf) {
-            uint2 vt[2];
-#pragma unroll
-            for (int blk = 0; blk < 2; ++blk) {
-              const int kr = s + 32 * kg + 16 * blk + 4 * g + e;
-              vt[blk] = lds_tr8(sv, row_chunk(kr, (uint32_t)(2 * hf + (qq >> 1))) + 8u * (qq & 1));
-            }
-            const uint4 va = cat(vt[0], vt[1]);
-#pragma unroll
-            for (int cb = 0; cb < 2; ++cb) oacc[cb][hf] = Mfma<T>::mma(va, bp[cb][kg], oacc[cb][hf]);
-          }
-        }
-      }
-    }
+    const char* kb = lds + L::kKv + 8192 * (c & 1);
+    if (upad - 64 * c >= 64)
+      fwd_step<T, 4>(kb, kb + 4096, mt, kmax, 64 * c, qv, cl, scale_log2, mrun, lrun, oacc, c16, g,
+                     e, qq);
+    else
+      fwd_step<T, 2>(kb, kb + 4096, mt, kmax, 64 * c, qv, cl, scale_log2, mrun, lrun, oacc, c16, g,
+                     e, qq);
   }
   if (!active) return;
 #pragma unroll
@@ -290,21 +266,63 @@ fwd_tile_kernel(int H, int ntiles, int kmax, int qstride, float scale_log2,
 // ---------------------------------------------------------------------------
 // backward, query-major pass: Delta, dQ, and (LSE log2 e, Delta) per row
 // ---------------------------------------------------------------------------
-template <int KCH>
 struct BqLds {
-  static constexpr int kHead = 0, kKt = 512, kMt = kKt + 4 * KCH, kLse = kMt + 8 * KCH,
-                       kQ = kLse + 256, kDo = kQ + 4096, kO = kDo + 4096, kK = kO + 4096,
-                       kV = kK + 64 * KCH, kBytes = kV + 64 * KCH;
+  static constexpr int kRec = 0, kQ = kRecBytes, kDo = kQ + 4096, kLse = kDo + 4096,
+                       kKv = kLse + 256, kBytes = kKv + 2 * 8192;
 };
 
-template <typename T, int KCH>
+template <typename T, int NB>
+__device__ __forceinline__ void bwdq_step(const char* kbuf, const char* vbuf, const uint8_t* mt,
+                                          int kmax, int col0, const uint4 (&qv)[2],
+                                          const uint4 (&dov)[2], const int (&cl)[2],
+                                          const float (&lse2)[2], const float (&dl)[2],
+                                          float scale_log2, f32x4 (&acc)[2][2], int c16, int g,
+                                          int e, int qq) {
+  const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+  uint4 ka[NB], va[NB];
+#pragma unroll
+  for (int kb = 0; kb < NB; ++kb) {
+    ka[kb] = lds16(kbuf, row_chunk(16 * kb + c16, (uint32_t)g));
+    va[kb] = lds16(vbuf, row_chunk(16 * kb + c16, (uint32_t)g));
+  }
+  uint4 kt[NB / 2][2];
+#pragma unroll
+  for (int kg = 0; kg < NB / 2; ++kg)
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) kt[kg][hf] = tr_pair(kbuf, 32 * kg, hf, g, e, qq);
+#pragma unroll
+  for (int cb = 0; cb < 2; ++cb) {
+    f32x4 s[NB];
+#pragma unroll
+    for (int kb = 0; kb < NB; ++kb) {
+      s[kb] = Mfma<T>::mma(ka[kb], qv[cb], z);
+      const f32x4 dp = Mfma<T>::mma(va[kb], dov[cb], z);
+      const uint32_t mw =
+          *reinterpret_cast<const uint32_t*>(mt + cl[cb] * kmax + col0 + 16 * kb + 4 * g);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float m = mbyte(mw, i);
+        const float p = m * __builtin_amdgcn_exp2f(fmaf(s[kb][i], scale_log2, -lse2[cb]));
+        s[kb][i] = m != 0.f ? p * (dp[i] - dl[cb]) : 0.f;   // dS
+      }
+    }
+#pragma unroll
+    for (int kg = 0; kg < NB / 2; ++kg) {
+      const uint4 bd = cat(pack4<T>(s[2 * kg]), pack4<T>(s[2 * kg + 1]));
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) acc[cb][hf] = Mfma<T>::mma(kt[kg][hf], bd, acc[cb][hf]);
+    }
+  }
+}
+
+template <typename T>
 __global__ void __launch_bounds__(kTThreads)
 bwdq_tile_kernel(int H, int ntiles, int kmax, int qstride, float scale,
                  const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
                  const T* __restrict__ o, const T* __restrict__ dout,
                  const float* __restrict__ lse, const int32_t* __restrict__ qrec,
                  T* __restrict__ dq, float2* __restrict__ ld, float4* __restrict__ ld_none) {
-  typedef BqLds<KCH> L;
+  typedef BqLds L;
   __shared__ __attribute__((aligned(1024))) char lds[L::kBytes];
   // the (LSE log2 e, Delta) pair the key-major pass reads for an absent
   // query: P = exp2(s - inf) = 0 there
@@ -316,39 +334,49 @@ bwdq_tile_kernel(int H, int ntiles, int kmax, int qstride, float scale,
   const int wv = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   const int c16 = lane & 15, g = lane >> 4;
   const int e = c16 >> 2, qq = c16 & 3;
-  const int32_t* rh = reinterpret_cast<const int32_t*>(lds + L::kHead);
-  const int32_t* kt = reinterpret_cast<const int32_t*>(lds + L::kKt);
-  const uint8_t* mt = reinterpret_cast<const uint8_t*>(lds + L::kMt);
+  const int32_t* rec = reinterpret_cast<const int32_t*>(lds + L::kRec);
+  const int32_t* ktok = rec + kQRecHead;
+  const uint8_t* mt = reinterpret_cast<const uint8_t*>(rec + kQRecHead + kmax);
   const float* sl = reinterpret_cast<const float*>(lds + L::kLse);
   const char* sq = lds + L::kQ;
   const char* sdo = lds + L::kDo;
-  const char* so = lds + L::kO;
-  const char* sk = lds + L::kK;
-  const char* sv = lds + L::kV;
-  const int64_t rec_off = (int64_t)w * qstride;
   const float scale_log2 = scale * kLog2eT;
 
-  load_qrec<KCH>(qrec, rec_off, kmax, 0, true, lds_addr(lds + L::kHead), lds_addr(kt),
-                 lds_addr(mt), lane, wv);
+  copy_lds(qrec, (uint32_t)((int64_t)w * qstride * 4), 4 * kQRecHead + 12 * kmax,
+           lds_addr(lds + L::kRec), lane, wv);
   wait_vm<0>();
   __syncthreads();
-  const int nc = rh[1], u = rh[2], base = rh[3];
-  const int q0 = rh[4];
-  const int32_t* qtok = rh + 4;
-  gather_rows<2>(q, qtok, q0, 64, lds_addr(sq), base, H, h, lane, wv);
-  gather_rows<2>(dout, qtok, q0, 64, lds_addr(sdo), base, H, h, lane, wv);
-  gather_rows<2>(o, qtok, q0, 64, lds_addr(so), base, H, h, lane, wv);
+  const int nc = __builtin_amdgcn_readfirstlane(rec[1]);
+  const int u = __builtin_amdgcn_readfirstlane(rec[2]);
+  const int base = __builtin_amdgcn_readfirstlane(rec[3]);
+  const int q0 = __builtin_amdgcn_readfirstlane(rec[4]);
+  const int32_t* qtok = rec + 4;
+  const int upad = (u + 31) & ~31;
+  const int nch = (upad + 63) >> 6;
+  const bool active = 4 * wv < nc;
+  // this lane's O pieces (for Delta) straight into registers: row = query
+  // column, 16 bytes of dims 8 g .. 8 g + 7
+  uint4 ov[2];
+#pragma unroll
+  for (int cb = 0; cb < 2; ++cb) {
+    const int tq = qtok[32 * wv + 16 * cb + c16];
+    const uint32_t qrow = (uint32_t)(base + (tq < 0 ? q0 : tq)) * (uint32_t)H + (uint32_t)h;
+    ov[cb] = ld16(o, qrow * kRowB + 16u * (uint32_t)g);
+  }
+  gather64(q, qtok, q0, 64, lds_addr(sq), base, H, h, lane, wv);
+  gather64(dout, qtok, q0, 64, lds_addr(sdo), base, H, h, lane, wv);
   if (wv == 0) {
     const int t = qtok[lane] < 0 ? q0 : qtok[lane];
     dma4(lse, ((uint32_t)(base + t) * (uint32_t)H + (uint32_t)h) * 4u, lds_addr(sl));
   }
-  int nrows = (min(u, KCH) + 31) & ~31;
-  gather_rows<KCH / 32>(k, kt, q0, nrows, lds_addr(sk), base, H, h, lane, wv);
-  gather_rows<KCH / 32>(v, kt, q0, nrows, lds_addr(sv), base, H, h, lane, wv);
+  if (nch > 0) {
+    const int r = min(64, upad);
+    gather64(k, ktok, q0, r, lds_addr(lds + L::kKv), base, H, h, lane, wv);
+    gather64(v, ktok, q0, r, lds_addr(lds + L::kKv + 4096), base, H, h, lane, wv);
+  }
   wait_vm<0>();
   __syncthreads();
 
-  const bool active = 4 * wv < nc;
   const f32x4 z = {0.f, 0.f, 0.f, 0.f};
   uint4 qv[2], dov[2];
   int cl[2];
@@ -358,12 +386,11 @@ bwdq_tile_kernel(int H, int ntiles, int kmax, int qstride, float scale,
     const int row = 32 * wv + 16 * cb + c16;
     qv[cb] = lds16(sq, row_chunk(row, (uint32_t)g));
     dov[cb] = lds16(sdo, row_chunk(row, (uint32_t)g));
-    const uint4 ov = lds16(so, row_chunk(row, (uint32_t)g));
     cl[cb] = 4 * wv + 2 * cb + (c16 >> 3);
     lse2[cb] = sl[row] * kLog2eT;
     // Delta of query row `row`: eight dims per lane, summed over the 4 lanes
     const uint32_t a[4] = {dov[cb].x, dov[cb].y, dov[cb].z, dov[cb].w};
-    const uint32_t b[4] = {ov.x, ov.y, ov.z, ov.w};
+    const uint32_t b[4] = {ov[cb].x, ov[cb].y, ov[cb].z, ov[cb].w};
     float d = 0.f;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -374,83 +401,25 @@ bwdq_tile_kernel(int H, int ntiles, int kmax, int qstride, float scale,
   }
   f32x4 acc[2][2] = {{z, z}, {z, z}};   // dQ^T [cb][dim half]
 
-  for (int k0 = 0; k0 < u; k0 += KCH) {
-    if (k0 > 0) {
-      __syncthreads();
-      load_qrec<KCH>(qrec, rec_off, kmax, k0, false, 0u, lds_addr(kt), lds_addr(mt), lane, wv);
+  for (int c = 0; c < nch; ++c) {
+    if (c > 0) {
       wait_vm<0>();
       __syncthreads();
-      nrows = (min(u - k0, KCH) + 31) & ~31;
-      gather_rows<KCH / 32>(k, kt, q0, nrows, lds_addr(sk), base, H, h, lane, wv);
-      gather_rows<KCH / 32>(v, kt, q0, nrows, lds_addr(sv), base, H, h, lane, wv);
-      wait_vm<0>();
-      __syncthreads();
+    }
+    if (c + 1 < nch) {
+      const int r = min(64, upad - 64 * (c + 1));
+      const uint32_t nb = lds_addr(lds + L::kKv + 8192 * ((c + 1) & 1));
+      gather64(k, ktok + 64 * (c + 1), q0, r, nb, base, H, h, lane, wv);
+      gather64(v, ktok + 64 * (c + 1), q0, r, nb + 4096u, base, H, h, lane, wv);
     }
     if (!active) continue;
-    for (int s = 0; s < nrows; s += 64) {
-      const int nb = min(4, (nrows - s) >> 4);
-      f32x4 sacc[4][2], pacc[4][2];
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
-        if (kb < nb) {
-          const int kr = s + 16 * kb + c16;
-          const uint4 ka = lds16(sk, row_chunk(kr, (uint32_t)g));
-          const uint4 va = lds16(sv, row_chunk(kr, (uint32_t)g));
-#pragma unroll
-          for (int cb = 0; cb < 2; ++cb) {
-            sacc[kb][cb] = Mfma<T>::mma(ka, qv[cb], z);
-            pacc[kb][cb] = Mfma<T>::mma(va, dov[cb], z);
-          }
-        }
-      }
-      uint4 bds[2][2];
-#pragma unroll
-      for (int cb = 0; cb < 2; ++cb) {
-        float ds[4][4];
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb) {
-          if (kb < nb) {
-            const uint32_t mw =
-                *reinterpret_cast<const uint32_t*>(mt + cl[cb] * KCH + s + 16 * kb + 4 * g);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const float m = mbyte(mw, i);
-              const float p =
-                  m * __builtin_amdgcn_exp2f(fmaf(sacc[kb][cb][i], scale_log2, -lse2[cb]));
-              ds[kb][i] = m != 0.f ? p * (pacc[kb][cb][i] - dl[cb]) : 0.f;
-            }
-          } else {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) ds[kb][i] = 0.f;
-          }
-        }
-#pragma unroll
-        for (int kg = 0; kg < 2; ++kg) {
-          const f32x4 da = {ds[2 * kg][0], ds[2 * kg][1], ds[2 * kg][2], ds[2 * kg][3]};
-          const f32x4 db = {ds[2 * kg + 1][0], ds[2 * kg + 1][1], ds[2 * kg + 1][2],
-                            ds[2 * kg + 1][3]};
-          bds[cb][kg] = cat(pack4<T>(da), pack4<T>(db));
-        }
-      }
-      // dQ^T += K^T dS^T (K read transposed)
-#pragma unroll
-      for (int kg = 0; kg < 2; ++kg) {
-        if (2 * kg < nb) {
-#pragma unroll
-          for (int hf = 0; hf < 2; ++hf) {
-            uint2 ktr[2];
-#pragma unroll
-            for (int blk = 0; blk < 2; ++blk) {
-              const int kr = s + 32 * kg + 16 * blk + 4 * g + e;
-              ktr[blk] = lds_tr8(sk, row_chunk(kr, (uint32_t)(2 * hf + (qq >> 1))) + 8u * (qq & 1));
-            }
-            const uint4 ka = cat(ktr[0], ktr[1]);
-#pragma unroll
-            for (int cb = 0; cb < 2; ++cb) acc[cb][hf] = Mfma<T>::mma(ka, bds[cb][kg], acc[cb][hf]);
-          }
-        }
-      }
-    }
+    const char* kb = lds + L::kKv + 8192 * (c & 1);
+    if (upad - 64 * c >= 64)
+      bwdq_step<T, 4>(kb, kb + 4096, mt, kmax, 64 * c, qv, dov, cl, lse2, dl, scale_log2, acc, c16,
+                      g, e, qq);
+    else
+      bwdq_step<T, 2>(kb, kb + 4096, mt, kmax, 64 * c, qv, dov, cl, lse2, dl, scale_log2, acc, c16,
+                      g, e, qq);
   }
   if (!active) return;
 #pragma unroll
@@ -468,14 +437,103 @@ bwdq_tile_kernel(int H, int ntiles, int kmax, int qstride, float scale,
 // ---------------------------------------------------------------------------
 // backward, key-major pass: dK, dV of the window's 64 keys
 // ---------------------------------------------------------------------------
-constexpr int kEch = 24;   // entries (query clusters) staged per step
+// Entries (query clusters reading the window) are held 32 at a time; their
+// query rows stream 8 entries (64 rows) per chunk through two buffers.  The
+// window's own K/V rows are staged once (in the second buffer, which the
+// first chunk does not use) and kept in registers.
+constexpr int kEntHeld = 32;
+constexpr int kChunkEnt = 8;
 
 struct BkvLds {
-  static constexpr int kRec = 0, kKk = 512, kKv = kKk + 4096, kEn = kKv + 4096,
-                       kQ = kEn + kEch * kEnt * 4, kDo = kQ + kEch * 8 * 64,
-                       kL2 = kDo + kEch * 8 * 64, kDl = kL2 + kEch * 8 * 4,
-                       kBytes = kDl + kEch * 8 * 4;
+  // per buffer: Q 4 KiB, dO 4 KiB, LSE log2 e 256 B, Delta 256 B
+  static constexpr int kBuf = 8192 + 512;
+  static constexpr int kRec = 0, kEn = 512, kBuf0 = kEn + kEntHeld * kEnt * 4,
+                       kBuf1 = kBuf0 + kBuf, kBytes = kBuf1 + kBuf;
 };
+
+// query rows of entries [e0, e0 + n) of the held block (n <= 8): rows
+// 8 x + m = member m of entry x; rows up to a multiple of 32 (padding rows
+// take `fallback` and read the (+inf, 0) pair)
+__device__ __forceinline__ void kv_chunk_rows(const void* q, const void* dout, const float2* ld,
+                                              uint32_t ld_none, const int32_t* en, int e0, int n,
+                                              int fallback, uint32_t buf, int base, int H, int h,
+                                              int lane, int wv) {
+  const int nrows = 32 * ((8 * n + 31) >> 5);
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int i = wv + 2 * j;
+    if (16 * i < nrows) {
+      const int row = 16 * i + (lane >> 2);
+      int t = (row >> 3) < n ? en[(e0 + (row >> 3)) * kEnt + (row & 7)] : -1;
+      t = t < 0 ? fallback : t;
+      const uint32_t chunk = (uint32_t)(lane & 3) ^ sw(row);
+      const uint32_t off = ((uint32_t)(base + t) * (uint32_t)H + (uint32_t)h) * kRowB + 16u * chunk;
+      dma16(q, off, buf + 1024u * (uint32_t)i);
+      dma16(dout, off, buf + 4096u + 1024u * (uint32_t)i);
+    }
+  }
+  if (wv == 0) {   // (LSE log2 e, Delta) of the 64 rows as two 4-byte gathers
+    const int t = (lane >> 3) < n ? en[(e0 + (lane >> 3)) * kEnt + (lane & 7)] : -1;
+    const uint32_t off =
+        t >= 0 ? ((uint32_t)(base + t) * (uint32_t)H + (uint32_t)h) * 8u : ld_none;
+    dma4(ld, off, buf + 8192u);
+    dma4(ld, off + 4u, buf + 8192u + 256u);
+  }
+}
+
+template <typename T, int NQ>
+__device__ __forceinline__ void bwdkv_step(const char* buf, const uint8_t* enb, int e0,
+                                           int n, const uint4 (&kreg)[2], const uint4 (&vreg)[2],
+                                           float scale_log2, f32x4 (&dka)[2][2],
+                                           f32x4 (&dva)[2][2], int wv, int c16, int g, int e,
+                                           int qq) {
+  const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+  const char* sq = buf;
+  const char* sdo = buf + 4096;
+  const float* sl2 = reinterpret_cast<const float*>(buf + 8192);
+  const float* sdl = reinterpret_cast<const float*>(buf + 8192 + 256);
+#pragma unroll
+  for (int qg = 0; qg < NQ / 2; ++qg) {
+    f32x4 pp[2][2], dd[2][2];   // [query block of the pair][key block]
+#pragma unroll
+    for (int qh = 0; qh < 2; ++qh) {
+      const int qb = 2 * qg + qh;
+      const int row = 16 * qb + c16;
+      const uint4 qa = lds16(sq, row_chunk(row, (uint32_t)g));
+      const uint4 da = lds16(sdo, row_chunk(row, (uint32_t)g));
+      const int rr = 16 * qb + 4 * g;   // rows rr .. rr + 3 of this lane
+      const int er = rr >> 3;           // their entry (in the chunk)
+      const float4 l2 = *reinterpret_cast<const float4*>(sl2 + rr);
+      const float4 dl4 = *reinterpret_cast<const float4*>(sdl + rr);
+      const float l2a[4] = {l2.x, l2.y, l2.z, l2.w};
+      const float dla[4] = {dl4.x, dl4.y, dl4.z, dl4.w};
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const f32x4 sv = Mfma<T>::mma(qa, kreg[kb], z);
+        const f32x4 pv = Mfma<T>::mma(da, vreg[kb], z);
+        const int key = 32 * wv + 16 * kb + c16;
+        const float m = er < n ? (float)enb[(e0 + er) * (kEnt * 4) + 32 + key] : 0.f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float p = m * __builtin_amdgcn_exp2f(fmaf(sv[i], scale_log2, -l2a[i]));
+          pp[qh][kb][i] = m != 0.f ? p : 0.f;
+          dd[qh][kb][i] = m != 0.f ? p * (pv[i] - dla[i]) : 0.f;
+        }
+      }
+    }
+    // dV^T += dO^T P, dK^T += Q^T dS over these 32 rows
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+      const uint4 dt = tr_pair(sdo, 32 * qg, hf, g, e, qq);
+      const uint4 qt = tr_pair(sq, 32 * qg, hf, g, e, qq);
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        dva[hf][kb] = Mfma<T>::mma(dt, cat(pack4<T>(pp[0][kb]), pack4<T>(pp[1][kb])), dva[hf][kb]);
+        dka[hf][kb] = Mfma<T>::mma(qt, cat(pack4<T>(dd[0][kb]), pack4<T>(dd[1][kb])), dka[hf][kb]);
+      }
+    }
+  }
+}
 
 template <typename T>
 __global__ void __launch_bounds__(kTThreads)
@@ -496,155 +554,66 @@ bwdkv_tile_kernel(int H, int ntiles, float scale, const T* __restrict__ q,
   const int32_t* rk = reinterpret_cast<const int32_t*>(lds + L::kRec);
   const int32_t* en = reinterpret_cast<const int32_t*>(lds + L::kEn);
   const uint8_t* enb = reinterpret_cast<const uint8_t*>(lds + L::kEn);
-  const float* sl2 = reinterpret_cast<const float*>(lds + L::kL2);
-  const float* sdl = reinterpret_cast<const float*>(lds + L::kDl);
-  const char* skk = lds + L::kKk;
-  const char* skv = lds + L::kKv;
-  const char* sq = lds + L::kQ;
-  const char* sdo = lds + L::kDo;
   const float scale_log2 = scale * kLog2eT;
+  const uint32_t buf0 = lds_addr(lds + L::kBuf0), buf1 = lds_addr(lds + L::kBuf1);
 
-  if (wv == 0 && lane < 18) dma16(krec, (uint32_t)(w * kKRec * 4) + 16u * lane, lds_addr(rk));
+  copy_lds(krec, (uint32_t)(w * kKRec * 4), 288, lds_addr(rk), lane, wv);
   wait_vm<0>();
   __syncthreads();
-  const int start = rk[0], E = rk[1], base = rk[3], nc = rk[4];
+  const int start = __builtin_amdgcn_readfirstlane(rk[0]);
+  const int E = __builtin_amdgcn_readfirstlane(rk[1]);
+  const int base = __builtin_amdgcn_readfirstlane(rk[3]);
+  const int nc = __builtin_amdgcn_readfirstlane(rk[4]);
   const int32_t* ktok = rk + 8;
-  const int k0tok = ktok[0];
-  gather_rows<2>(k, ktok, k0tok, 64, lds_addr(skk), base, H, h, lane, wv);
-  gather_rows<2>(v, ktok, k0tok, 64, lds_addr(skv), base, H, h, lane, wv);
-
-  // entries [e0, e0 + n) into LDS: 6 sixteen-byte pieces per entry
-  auto load_entries = [&](int e0, int n) {
-    for (int i = wv; 64 * i < 6 * n; i += 2) {
-      const int p = 64 * i + lane;
-      if (p < 6 * n) dma16(kent, (uint32_t)(start + e0) * (uint32_t)(kEnt * 4) + 16u * p,
-                           lds_addr(en) + 1024u * (uint32_t)i);
-    }
-  };
-  load_entries(0, min(E, kEch));
+  const int k0tok = __builtin_amdgcn_readfirstlane(ktok[0]);
+  // own K and V rows into the second buffer, the first held entries
+  gather64(k, ktok, k0tok, 64, buf1, base, H, h, lane, wv);
+  gather64(v, ktok, k0tok, 64, buf1 + 4096u, base, H, h, lane, wv);
+  int held = min(E, kEntHeld);
+  copy_lds(kent, (uint32_t)start * (uint32_t)(kEnt * 4), held * kEnt * 4, lds_addr(en), lane, wv);
   wait_vm<0>();
   __syncthreads();
-
   const bool active = 32 * wv < 8 * nc;
-  const f32x4 z = {0.f, 0.f, 0.f, 0.f};
   uint4 kreg[2], vreg[2];
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb) {
     const int row = 32 * wv + 16 * kb + c16;
-    kreg[kb] = lds16(skk, row_chunk(row, (uint32_t)g));
-    vreg[kb] = lds16(skv, row_chunk(row, (uint32_t)g));
+    kreg[kb] = lds16(lds + L::kBuf1, row_chunk(row, (uint32_t)g));
+    vreg[kb] = lds16(lds + L::kBuf1 + 4096, row_chunk(row, (uint32_t)g));
   }
+  const f32x4 z = {0.f, 0.f, 0.f, 0.f};
   f32x4 dka[2][2] = {{z, z}, {z, z}}, dva[2][2] = {{z, z}, {z, z}};   // [dim half][key block]
 
-  for (int e0 = 0; e0 < E; e0 += kEch) {
-    const int n = min(kEch, E - e0);
-    if (e0 > 0) {
+  for (int h0 = 0; h0 < E; h0 += kEntHeld) {
+    if (h0 > 0) {   // more than kEntHeld entries: the next block of them
       __syncthreads();
-      load_entries(e0, n);
+      held = min(E - h0, kEntHeld);
+      copy_lds(kent, (uint32_t)(start + h0) * (uint32_t)(kEnt * 4), held * kEnt * 4,
+               lds_addr(en), lane, wv);
       wait_vm<0>();
       __syncthreads();
+    } else {
+      __syncthreads();   // every wavefront has read the own K/V rows from buffer 1
     }
-    const int ngr = (n + 3) >> 2;   // groups of 4 entries = 32 query rows
-    const int nrows = 32 * ngr;
-    // query rows: token of row r = member r & 7 of entry r >> 3 (past the
-    // n-th entry, or an absent member: the window's first key token)
-    {
-      const int ni = nrows >> 4;
-#pragma unroll
-      for (int j = 0; j < (kEch * 8 / 16 + 1) / 2; ++j) {
-        const int i = wv + 2 * j;
-        if (i < ni) {
-          const int row = 16 * i + (lane >> 2);
-          int t = (row >> 3) < n ? en[(row >> 3) * kEnt + (row & 7)] : -1;
-          t = t < 0 ? k0tok : t;
-          const uint32_t chunk = (uint32_t)(lane & 3) ^ sw(row);
-          const uint32_t off = ((uint32_t)(base + t) * (uint32_t)H + (uint32_t)h) * kRowB + 16u * chunk;
-          dma16(q, off, lds_addr(sq) + 1024u * (uint32_t)i);
-          dma16(dout, off, lds_addr(sdo) + 1024u * (uint32_t)i);
-        }
-      }
-      // (LSE log2 e, Delta) of every row, as two 4-byte gathers; an absent
-      // or padding row reads the (+inf, 0) pair
-#pragma unroll
-      for (int j = 0; j < (kEch * 8 / 64 + 1) / 2; ++j) {
-        const int i = wv + 2 * j;
-        if (64 * i < nrows) {
-          const int row = 64 * i + lane;
-          const int t = (row >> 3) < n ? en[(row >> 3) * kEnt + (row & 7)] : -1;
-          const uint32_t off =
-              t >= 0 ? ((uint32_t)(base + t) * (uint32_t)H + (uint32_t)h) * 8u : ld_none;
-          dma4(ld, off, lds_addr(sl2) + 256u * (uint32_t)i);
-          dma4(ld, off + 4u, lds_addr(sdl) + 256u * (uint32_t)i);
-        }
-      }
-    }
-    wait_vm<0>();
-    __syncthreads();
-    if (!active) continue;
-
-    for (int gi = 0; gi < ngr; ++gi) {
-      const int r0 = 32 * gi;
-      f32x4 sv[2][2], pv[2][2];   // [query block][key block]
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
-        const int row = r0 + 16 * qb + c16;
-        const uint4 qa = lds16(sq, row_chunk(row, (uint32_t)g));
-        const uint4 da = lds16(sdo, row_chunk(row, (uint32_t)g));
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          sv[qb][kb] = Mfma<T>::mma(qa, kreg[kb], z);
-          pv[qb][kb] = Mfma<T>::mma(da, vreg[kb], z);
-        }
-      }
-      float pp[2][2][4], dd[2][2][4];
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
-        const int rr = r0 + 16 * qb + 4 * g;   // rows rr .. rr + 3 of this lane
-        const int er = rr >> 3;                // their entry
-        const float4 l2 = *reinterpret_cast<const float4*>(sl2 + rr);
-        const float4 dl4 = *reinterpret_cast<const float4*>(sdl + rr);
-        const float l2a[4] = {l2.x, l2.y, l2.z, l2.w};
-        const float dla[4] = {dl4.x, dl4.y, dl4.z, dl4.w};
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          const int key = 32 * wv + 16 * kb + c16;
-          const float m = er < n ? (float)enb[er * (kEnt * 4) + 32 + key] : 0.f;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const float p = m * __builtin_amdgcn_exp2f(fmaf(sv[qb][kb][i], scale_log2, -l2a[i]));
-            pp[qb][kb][i] = m != 0.f ? p : 0.f;
-            dd[qb][kb][i] = m != 0.f ? p * (pv[qb][kb][i] - dla[i]) : 0.f;
-          }
-        }
-      }
-      uint4 bp[2], bd[2];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const f32x4 p0 = {pp[0][kb][0], pp[0][kb][1], pp[0][kb][2], pp[0][kb][3]};
-        const f32x4 p1 = {pp[1][kb][0], pp[1][kb][1], pp[1][kb][2], pp[1][kb][3]};
-        const f32x4 d0 = {dd[0][kb][0], dd[0][kb][1], dd[0][kb][2], dd[0][kb][3]};
-        const f32x4 d1 = {dd[1][kb][0], dd[1][kb][1], dd[1][kb][2], dd[1][kb][3]};
-        bp[kb] = cat(pack4<T>(p0), pack4<T>(p1));
-        bd[kb] = cat(pack4<T>(d0), pack4<T>(d1));
-      }
-      // dV^T += dO^T P, dK^T += Q^T dS: rows r0 + 16 blk + 4 g + e transposed
-#pragma unroll
-      for (int hf = 0; hf < 2; ++hf) {
-        uint2 dt[2], qt[2];
-#pragma unroll
-        for (int blk = 0; blk < 2; ++blk) {
-          const int row = r0 + 16 * blk + 4 * g + e;
-          const uint32_t off = row_chunk(row, (uint32_t)(2 * hf + (qq >> 1))) + 8u * (qq & 1);
-          dt[blk] = lds_tr8(sdo, off);
-          qt[blk] = lds_tr8(sq, off);
-        }
-        const uint4 da = cat(dt[0], dt[1]), qa = cat(qt[0], qt[1]);
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          dva[hf][kb] = Mfma<T>::mma(da, bp[kb], dva[hf][kb]);
-          dka[hf][kb] = Mfma<T>::mma(qa, bd[kb], dka[hf][kb]);
-        }
-      }
+    const int nchk = (held + kChunkEnt - 1) / kChunkEnt;
+    kv_chunk_rows(q, dout, ld, ld_none, en, 0, min(kChunkEnt, held), k0tok, buf0, base, H, h,
+                  lane, wv);
+    for (int c = 0; c < nchk; ++c) {
+      wait_vm<0>();
+      __syncthreads();
+      if (c + 1 < nchk)
+        kv_chunk_rows(q, dout, ld, ld_none, en, kChunkEnt * (c + 1),
+                      min(kChunkEnt, held - kChunkEnt * (c + 1)), k0tok, (c + 1) & 1 ? buf1 : buf0,
+                      base, H, h, lane, wv);
+      if (!active) continue;
+      const int n = min(kChunkEnt, held - kChunkEnt * c);
+      const char* buf = lds + ((c & 1) ? L::kBuf1 : L::kBuf0);
+      if (n > 4)
+        bwdkv_step<T, 4>(buf, enb, kChunkEnt * c, n, kreg, vreg, scale_log2, dka, dva, wv, c16, g,
+                         e, qq);
+      else
+        bwdkv_step<T, 2>(buf, enb, kChunkEnt * c, n, kreg, vreg, scale_log2, dka, dva, wv, c16, g,
+                         e, qq);
     }
   }
   if (!active) return;
@@ -661,17 +630,14 @@ bwdkv_tile_kernel(int H, int ntiles, float scale, const T* __restrict__ q,
   }
 }
 
-constexpr int kFwdKch = 256;   // key rows staged per pass (forward)
-constexpr int kBqKch = 192;    // key rows staged per pass (query-major backward)
-
 template <typename T>
 hipError_t fwd_tile_t(int B, int C, int H, int nk, float scale, const void* q, const void* k,
                       const void* v, const BwdWorkspace& w, void* o, float* lse,
                       hipStream_t st) {
   const int64_t ntiles = windows_of(B, C) * H;
   if (ntiles == 0) return hipSuccess;
-  hipLaunchKernelGGL((fwd_tile_kernel<T, kFwdKch>), dim3((unsigned)ntiles), dim3(kTThreads), 0,
-                     st, H, (int)ntiles, 8 * nk, qrec_stride(nk), scale * kLog2eT, (const T*)q,
+  hipLaunchKernelGGL((fwd_tile_kernel<T>), dim3((unsigned)ntiles), dim3(kTThreads), 0, st, H,
+                     (int)ntiles, 8 * nk, qrec_stride(nk), scale * kLog2eT, (const T*)q,
                      (const T*)k, (const T*)v, (const int32_t*)w.qrec, (T*)o, lse);
   return hipGetLastError();
 }
@@ -684,10 +650,10 @@ hipError_t bwd_tile_t(int pass, int B, int C, int H, int nk, float scale, const 
   const int64_t ntiles = windows_of(B, C) * H;
   if (ntiles == 0) return hipSuccess;
   if (pass & 1)
-    hipLaunchKernelGGL((bwdq_tile_kernel<T, kBqKch>), dim3((unsigned)ntiles), dim3(kTThreads), 0,
-                       st, H, (int)ntiles, 8 * nk, qrec_stride(nk), scale, (const T*)q,
-                       (const T*)k, (const T*)v, (const T*)o, (const T*)dout, lse,
-                       (const int32_t*)w.qrec, (T*)dq, w.ld, w.ld_none);
+    hipLaunchKernelGGL((bwdq_tile_kernel<T>), dim3((unsigned)ntiles), dim3(kTThreads), 0, st, H,
+                       (int)ntiles, 8 * nk, qrec_stride(nk), scale, (const T*)q, (const T*)k,
+                       (const T*)v, (const T*)o, (const T*)dout, lse, (const int32_t*)w.qrec,
+                       (T*)dq, w.ld, w.ld_none);
   if (pass & 2) {
     const uint32_t ld_none = (uint32_t)((const char*)w.ld_none - (const char*)w.ld);
     hipLaunchKernelGGL((bwdkv_tile_kernel<T>), dim3((unsigned)ntiles), dim3(kTThreads), 0, st, H,
