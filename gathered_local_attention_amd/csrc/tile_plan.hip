@@ -163,7 +163,9 @@ qwin_plan_kernel(int N, int C, int nk, int nwi, int packed, const int32_t* __res
   auto emit = [&](int32_t* out, int c_lo, int ncl, bool only_count) {
     const int u = write_qrec(key, lane, nk, c_lo, ncl, out, s, only_count);
     if (only_count && u > kUnionCap) return u;
-    const int q = (lane >> 3) < ncl ? __shfl(qt, lane + 8 * c_lo, 64) : -1;
+    // (every lane takes part in the shuffle: its source lanes must be active)
+    const int qs = __shfl(qt, (lane + 8 * c_lo) & 63, 64);
+    const int q = (lane >> 3) < ncl ? qs : -1;
     const int q0 = __shfl(qt, 8 * c_lo, 64);
     // pad the key tokens to a multiple of 32 with a valid token
     const int pad_tok = q0;
