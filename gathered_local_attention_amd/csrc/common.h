@@ -45,7 +45,7 @@ struct RevEntry {
 //              valid token
 //   then the slot table: u16 [8 clusters][16][4]: entry [c][x][b] = the LDS
 //   byte offset of the staged row of slot 16 b + x of cluster c,
-//   row * 64 + 16 * row_swz(row) (a 16-byte chunk k of the row sits at
+//   row * kLdsRow + 16 * row_swz(row) (16-byte chunk k of the row sits at
 //   offset ^ 16 k); empty slots point at row 0
 //   then the valid-slot masks: u64 [8] (bit s: slot s holds a token)
 // Key record (kKRec ints): [0] start (first merged entry, in the index space
@@ -70,18 +70,20 @@ constexpr int kQRec = kQMaskOff + 16;                    // ints per record (536
 constexpr int kQRecStride = 640;
 constexpr int kQSplit = 1, kQHoles = 2;
 constexpr int kKRecHead = 88;
-constexpr int kKRecEnt = 24;
-constexpr int kKRec = kKRecHead + 8 * kKRecEnt;   // 280 ints
+constexpr int kKRecEnt = 20;
+constexpr int kKRec = kKRecHead + 8 * kKRecEnt;   // 248 ints
 constexpr int kEnt = 8;
 // clusters per sub-window: sub_window(nk) * nk slots never exceed kUnionCap
 __host__ __device__ constexpr int sub_window(int nk) { return nk <= 48 ? 4 : 2; }
 // records per window (main + sub-windows)
 __host__ __device__ constexpr int qrec_slots(int nk) { return 1 + kWin / sub_window(nk); }
 static_assert(4 * 48 <= kUnionCap && 2 * 64 <= kUnionCap, "a sub-window always fits");
-// LDS row swizzle of 64-byte rows (16-byte chunk c of row r at c ^ row_swz(r))
-__host__ __device__ __forceinline__ uint32_t row_swz(int r) {
-  return (uint32_t)(((((r >> 1) ^ (r >> 2)) & 1) << 1) | (((r >> 1) ^ (r >> 3)) & 1));
-}
+// Staged rows in LDS are kLdsRow = 128 bytes (the 32-dim rows of two heads);
+// 16-byte chunk c of row r sits at position c ^ row_swz(r), which spreads the
+// chunks that one instruction reads from different rows over the LDS banks.
+constexpr int kLdsRow = 128;
+__host__ __device__ __forceinline__ uint32_t row_swz(int r) { return (uint32_t)((r ^ (r >> 3)) & 7); }
+static_assert(kUnionCap * kLdsRow <= 65536, "slot-table offsets fit 16 bits");
 static inline int64_t windows_of(int64_t B, int64_t C) { return B * ((C + kWin - 1) / kWin); }
 
 // ---- workspace layout of the backward pass --------------------------------

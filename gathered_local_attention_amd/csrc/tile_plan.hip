@@ -124,7 +124,7 @@ __device__ int write_qrec(const uint64_t (&key)[8], int lane, int nk, int c_lo, 
     const int c = sl / nk - c_lo, j = sl - (sl / nk) * nk;
     if (flag[r]) rec[kQRecHead + rank] = (int32_t)(key[r] >> 9);
     s.slot[(c * 16 + (j & 15)) * 4 + (j >> 4)] =
-        (uint16_t)(rank * 64 + 16 * (int)row_swz(rank));
+        (uint16_t)(rank * kLdsRow + 16 * (int)row_swz(rank));
     atomicOr(&s.mask[c], 1ull << j);
   }
   __syncthreads();
