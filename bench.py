@@ -38,10 +38,9 @@ HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, vendor figure
 ENTRY_KERNELS = {
     "build": ["build_small_kernel (N <= 4096) | segsort_kernel, merge_round_kernel, "
               "centroid_box_kernel, select_box_kernel (N > 4096)"],
-    "plan": ["plan_small_kernel (images <= 4096 tokens) | plan_init/inv/count/scan/place/sort_kernel",
-             "qwin_plan_kernel", "kwin_plan_kernel"],
-    "fwd": ["fwd_tile_kernel"],
-    "bwd": ["bwdq_tile_kernel", "bwdkv_tile_kernel"],
+    "plan": ["plan_small_kernel (images <= 4096 tokens) | plan_init/inv/count/scan/place/sort_kernel"],
+    "fwd": ["fwd_lds_kernel"],
+    "bwd": ["bwd_q_lds_kernel", "bwd_kv_lds_kernel"],
 }
 MERGE_ENTRY_KERNELS = {"plan": ["merge_assign_kernel", "merge_members_kernel"], "fwd": ["merge_fwd_kernel"],
                        "bwd": ["merge_bwd_kernel"]}
@@ -305,7 +304,7 @@ def main():
     def step(s):
         perm, nbr, key = ca.build_neighbors(s["coords"], cfg.G, cfg.cs, cfg.k, workspace=bws)
         plan = ca.bwd_plan(perm, key, cfg.N)
-        o, lse = ca.fwd(s["q"], s["k"], s["v"], perm, key, scale, plan=plan)
+        o, lse = ca.fwd(s["q"], s["k"], s["v"], perm, key, scale)
         dq, dk, dv = ca.bwd(s["q"], s["k"], s["v"], o, s["do"], lse, perm, key, scale,
                             workspace=gws, plan=plan)
         return dq
@@ -330,25 +329,21 @@ def main():
     outs = []
     for s in sets:
         perm, nbr, key = ca.build_neighbors(s["coords"], cfg.G, cfg.cs, cfg.k, workspace=bws)
-        plan = ca.bwd_plan(perm, key, cfg.N)
-        o, lse = ca.fwd(s["q"], s["k"], s["v"], perm, key, scale, plan=plan)
-        outs.append((perm, key, o, lse, plan))
+        o, lse = ca.fwd(s["q"], s["k"], s["v"], perm, key, scale)
+        outs.append((perm, key, o, lse, ca.bwd_plan(perm, key, cfg.N)))
     calls = {
         "build": lambda i: ca.build_neighbors(sets[i]["coords"], cfg.G, cfg.cs, cfg.k,
                                               workspace=bws),
         "plan": lambda i: ca.bwd_plan(outs[i][0], outs[i][1], cfg.N),
         "fwd": lambda i: ca.fwd(sets[i]["q"], sets[i]["k"], sets[i]["v"], outs[i][0],
-                                outs[i][1], scale, plan=outs[i][4]),
+                                outs[i][1], scale),
         "bwd": lambda i: ca.bwd(sets[i]["q"], sets[i]["k"], sets[i]["v"], outs[i][2],
                                 sets[i]["do"], outs[i][3], outs[i][0], outs[i][1], scale,
                                 workspace=gws, plan=outs[i][4]),
-        # for reference: the self-planning backward (plan + passes in one
-        # call) and the forward without a plan (per-cluster slot gathers)
+        # the self-planning backward (plan + passes in one call), for reference
         "bwd_with_plan": lambda i: ca.bwd(sets[i]["q"], sets[i]["k"], sets[i]["v"], outs[i][2],
                                           sets[i]["do"], outs[i][3], outs[i][0], outs[i][1],
                                           scale, workspace=gws),
-        "fwd_no_plan": lambda i: ca.fwd(sets[i]["q"], sets[i]["k"], sets[i]["v"], outs[i][0],
-                                        outs[i][1], scale),
     }
     stats = entry_times(torch, calls, n_ev, len(sets))
     dur = {name: st["mean"] for name, st in stats.items()}   # microseconds per launch
@@ -508,7 +503,7 @@ def bench_varlen(args, torch, ca):
     def step(s):
         q_idx, _, key, _, _ = build(s)
         plan = plan_of(q_idx, key)
-        o, lse = ca.fwd_varlen(s["q"], s["k"], s["v"], q_idx, key, scale, plan=plan)
+        o, lse = ca.fwd_varlen(s["q"], s["k"], s["v"], q_idx, key, scale)
         return ca.bwd_varlen(s["q"], s["k"], s["v"], o, s["do"], lse, q_idx, key, scale,
                              workspace=gws, plan=plan)
 
@@ -525,14 +520,13 @@ def bench_varlen(args, torch, ca):
     outs = []
     for s in sets:
         q_idx, _, key, _, _ = build(s)
-        plan = plan_of(q_idx, key)
-        o, lse = ca.fwd_varlen(s["q"], s["k"], s["v"], q_idx, key, scale, plan=plan)
-        outs.append((q_idx, key, o, lse, plan))
+        o, lse = ca.fwd_varlen(s["q"], s["k"], s["v"], q_idx, key, scale)
+        outs.append((q_idx, key, o, lse, plan_of(q_idx, key)))
     calls = {
         "build": lambda i: build(sets[i]),
         "plan": lambda i: plan_of(outs[i][0], outs[i][1]),
         "fwd": lambda i: ca.fwd_varlen(sets[i]["q"], sets[i]["k"], sets[i]["v"], outs[i][0],
-                                       outs[i][1], scale, plan=outs[i][4]),
+                                       outs[i][1], scale),
         "bwd": lambda i: ca.bwd_varlen(sets[i]["q"], sets[i]["k"], sets[i]["v"], outs[i][2],
                                        sets[i]["do"], outs[i][3], outs[i][0], outs[i][1], scale,
                                        workspace=gws, plan=outs[i][4]),

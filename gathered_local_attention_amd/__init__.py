@@ -9,7 +9,7 @@ no CPU fallback: if the library is missing, the calls raise.
 Functions
 ---------
 build_neighbors(coords, grid_side, cs=8, k=6) -> (perm, nbr, key_idx)   (2D or 3D)
-fwd(q, k, v, q_idx, key_idx, scale=None, plan=None) -> (o, lse)
+fwd(q, k, v, q_idx, key_idx, scale=None) -> (o, lse)
 bwd(q, k, v, o, do, lse, q_idx, key_idx, scale=None, plan=None) -> (dq, dk, dv)
 bwd_plan(q_idx, key_idx, N) -> plan   (transposed lists, reusable across backward calls)
 check_lists(q_idx, key_idx, N)   (host-side index validation; fwd/bwd take check=True)
@@ -192,11 +192,9 @@ def check_lists(q_idx: torch.Tensor, key_idx: torch.Tensor, N: int) -> None:
            "cluster_attn_check_lists")
 
 
-def fwd(q, k, v, q_idx, key_idx, scale: float | None = None, check: bool = False,
-        plan: torch.Tensor | None = None):
+def fwd(q, k, v, q_idx, key_idx, scale: float | None = None, check: bool = False):
     """Forward: returns O [B, N, H, D] (dtype of q) and LSE [B, N, H] f32.
-    ``plan`` (from :func:`bwd_plan` on the same lists) runs the window-tiled
-    kernels.  ``check`` validates the index lists on the host first
+    ``check`` validates the index lists on the host first
     (:func:`check_lists`; synchronises)."""
     lib = _lib.load()
     B, N, H, D, cs, nk, q_idx = _shapes(q, q_idx, key_idx)
@@ -210,22 +208,10 @@ def fwd(q, k, v, q_idx, key_idx, scale: float | None = None, check: bool = False
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
     o = torch.empty_like(q)
     lse = torch.empty((B, N, H), dtype=torch.float32, device=q.device)
-    if plan is not None:
-        return _fwd_planned(lib, B, N, q_idx.shape[1], H, D, cs, nk, scale, q, k, v, q_idx,
-                            key_idx, plan, o, lse)
     _check(lib.cluster_attn_fwd(
         _DT[q.dtype], B, N, H, D, cs, nk, scale, _dev(q, "q"), _dev(k, "k"), _dev(v, "v"),
         _dev(q_idx, "q_idx", torch.int32), _dev(key_idx, "key_idx", torch.int32),
         o.data_ptr(), lse.data_ptr(), _stream(q)), "cluster_attn_fwd")
-    return o, lse
-
-
-def _fwd_planned(lib, B, N, C, H, D, cs, nk, scale, q, k, v, q_idx, key_idx, plan, o, lse):
-    _check(lib.cluster_attn_fwd_planned(
-        _DT[q.dtype], B, N, C, H, D, cs, nk, scale, _dev(q, "q"), _dev(k, "k"), _dev(v, "v"),
-        _dev(q_idx, "q_idx", torch.int32), _dev(key_idx, "key_idx", torch.int32),
-        _dev(plan, "plan"), plan.numel(), o.data_ptr(), lse.data_ptr(), _stream(q)),
-        "cluster_attn_fwd_planned")
     return o, lse
 
 
@@ -424,10 +410,8 @@ def _varlen_shapes(q, q_idx, key_idx):
     return T, H, D, Ct, cs, key_idx.shape[1]
 
 
-def fwd_varlen(q, k, v, q_idx, key_idx, scale: float | None = None,
-               plan: torch.Tensor | None = None):
-    """Forward of a packed batch: O [T, H, D] (dtype of q), LSE [T, H] f32;
-    ``plan`` as for :func:`fwd` (from ``bwd_plan_varlen`` / ``bwd_plan``)."""
+def fwd_varlen(q, k, v, q_idx, key_idx, scale: float | None = None):
+    """Forward of a packed batch: O [T, H, D] (dtype of q), LSE [T, H] f32."""
     lib = _lib.load()
     T, H, D, Ct, cs, nk = _varlen_shapes(q, q_idx, key_idx)
     for t, n in ((k, "k"), (v, "v")):
@@ -436,9 +420,6 @@ def fwd_varlen(q, k, v, q_idx, key_idx, scale: float | None = None,
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
     o = torch.empty_like(q)
     lse = torch.empty((T, H), dtype=torch.float32, device=q.device)
-    if plan is not None:
-        return _fwd_planned(lib, 1, T, Ct, H, D, cs, nk, scale, q, k, v, q_idx, key_idx, plan, o,
-                            lse)
     _check(lib.cluster_attn_fwd_varlen(
         _DT[q.dtype], T, Ct, H, D, cs, nk, scale, _dev(q, "q"), _dev(k, "k"), _dev(v, "v"),
         _dev(q_idx, "q_idx", torch.int32), _dev(key_idx, "key_idx", torch.int32),

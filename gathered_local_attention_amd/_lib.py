@@ -47,9 +47,6 @@ SIGNATURES = {
         _c_int, [_c_int, _c_int, _c_int, _c_int, _vp, _vp, _c_int, _c_int, _vp, _vp, _vp, _c_size,
                  _vp]),
     "cluster_attn_bwd_planned_workspace": (_c_size, [_c_int, _c_int, _c_int, _c_int, _c_int]),
-    "cluster_attn_fwd_planned": (
-        _c_int, [_c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _f,
-                 _vp, _vp, _vp, _vp, _vp, _vp, _c_size, _vp, _vp, _vp]),
     "cluster_attn_bwd_planned": (
         _c_int, [_c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _f,
                  _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _c_size, _vp, _vp, _vp, _vp,

@@ -242,12 +242,10 @@ ca_status cluster_attn_build_neighbors_varlen_3d(const float* coords, int B, int
 
 namespace {
 
-// Forward on B images of N tokens and C clusters each (q_idx [B, C, cs]);
-// `plan` (optional) from cluster_attn_bwd_plan on the same lists.
+// Forward on B images of N tokens and C clusters each (q_idx [B, C, cs]).
 ca_status attn_fwd(int dt, int B, int N, int64_t C, int H, int D, int cs, int nk, float scale,
              const void* q, const void* k, const void* v, const int32_t* q_idx,
-             const int32_t* key_idx, void* o, float* lse, void* hip_stream,
-             const void* plan = nullptr, size_t plan_bytes = 0) {
+             const int32_t* key_idx, void* o, float* lse, void* hip_stream) {
   if (!(scale == scale) || scale == INFINITY || scale == -INFINITY)
     return fail(CA_ERR_SHAPE, "scale is not finite");
   if (B == 0 || N == 0 || C == 0) return ok();
@@ -259,17 +257,6 @@ ca_status attn_fwd(int dt, int B, int N, int64_t C, int H, int D, int cs, int nk
                  {key_idx, (size_t)(B * C * nk) * 4}};
   if (ca_status s = check_alias(outs, 2, ins, 5)) return s;
   hipStream_t st = (hipStream_t)hip_stream;
-  if (plan) {
-    const size_t pneed = ca::plan_layout(nullptr, B, N, C, nk).bytes;
-    if (plan_bytes < pneed) return fail(CA_ERR_WORKSPACE, "plan %zu < %zu bytes", plan_bytes, pneed);
-    Range pin[] = {{plan, pneed}};
-    if (ca_status s = check_alias(outs, 2, pin, 1)) return s;
-    if (ca::tile_supported(dt, B, N, (int)C, H, nk)) {
-      const ca::BwdWorkspace w = ca::plan_layout(const_cast<void*>(plan), B, N, C, nk);
-      return hip_status(ca::launch_fwd_tile(dt, B, N, (int)C, H, nk, scale, q, k, v, w, o, lse, st),
-                        "fwd launch");
-    }
-  }
   if (ca::mfma_supported(dt, B, N, (int)C, H, nk))
     return hip_status(ca::launch_fwd_mfma(dt, B, N, (int)C, H, scale, q, k, v, q_idx, key_idx, o,
                                           lse, st),
@@ -321,13 +308,8 @@ ca_status attn_bwd(int dt, int B, int N, int64_t C, int H, int D, int cs, int nk
   } else {
     w = ca::bwd_layout(ws, B, N, H, C, nk);
     hipError_t e = ca::launch_bwd_plan(B, N, (int)C, nk, q_idx, key_idx, w, st);
-    if (e == hipSuccess) e = ca::launch_tile_plan(B, N, (int)C, nk, B == 1, q_idx, key_idx, w, st);
     if (e != hipSuccess) return hip_status(e, "bwd plan launch");
   }
-  if (ca::tile_supported(dt, B, N, (int)C, H, nk))
-    return hip_status(ca::launch_bwd_tile(3, dt, B, N, (int)C, H, nk, scale, q, k, v, o, dout, lse,
-                                          dq, dk, dv, w, st),
-                      "bwd launch");
   if (ca::mfma_supported(dt, B, N, (int)C, H, nk))
     return hip_status(ca::launch_bwd_mfma(3, dt, B, N, (int)C, H, nk, scale, q, k, v, o, dout, lse,
                                           q_idx, key_idx, dq, dk, dv, w, st),
@@ -370,17 +352,6 @@ ca_status cluster_attn_fwd(int dt, int B, int N, int H, int D, int cs, int nk, f
   if (ca_status s = check_attn_shape(dt, B, N, H, D, cs, nk)) return s;
   return attn_fwd(dt, B, N, clusters_of(N, cs), H, D, cs, nk, scale, q, k, v, q_idx, key_idx, o,
                   lse, hip_stream);
-}
-
-ca_status cluster_attn_fwd_planned(int dt, int B, int N, int C, int H, int D, int cs, int nk,
-                                  float scale, const void* q, const void* k, const void* v,
-                                  const int32_t* q_idx, const int32_t* key_idx, const void* plan,
-                                  size_t plan_bytes, void* o, float* lse, void* hip_stream) {
-  if (ca_status s = check_attn_shape(dt, B, N, H, D, cs, nk)) return s;
-  if (ca_status s = check_plan_sizes(B, N, C, cs, nk)) return s;
-  if (B > 0 && N > 0 && C > 0 && !plan) return fail(CA_ERR_NULL, "NULL plan");
-  return attn_fwd(dt, B, N, C, H, D, cs, nk, scale, q, k, v, q_idx, key_idx, o, lse, hip_stream,
-                  plan, plan_bytes);
 }
 
 size_t cluster_attn_bwd_workspace(int dt, int B, int N, int H, int D, int cs, int nk) {
@@ -449,10 +420,8 @@ ca_status cluster_attn_bwd_plan(int B, int N, int C, int cs, int nk, const int32
   Range ins[] = {{q_idx, (size_t)B * C * cs * 4}, {key_idx, (size_t)B * C * nk * 4}};
   if (ca_status s = check_alias(outs, 1, ins, 2)) return s;
   const ca::BwdWorkspace w = ca::plan_layout(plan, B, N, C, nk);
-  hipStream_t st = (hipStream_t)hip_stream;
-  hipError_t e = ca::launch_bwd_plan(B, N, C, nk, q_idx, key_idx, w, st);
-  if (e == hipSuccess) e = ca::launch_tile_plan(B, N, C, nk, false, q_idx, key_idx, w, st);
-  return hip_status(e, "bwd plan launch");
+  return hip_status(ca::launch_bwd_plan(B, N, C, nk, q_idx, key_idx, w, (hipStream_t)hip_stream),
+                    "bwd plan launch");
 }
 
 ca_status cluster_attn_bwd_plan_varlen(int B, int T, int Ct, int max_n, const int32_t* tok_off,
@@ -472,10 +441,9 @@ ca_status cluster_attn_bwd_plan_varlen(int B, int T, int Ct, int max_n, const in
   if (ca_status s = check_alias(outs, 1, ins, 4)) return s;
   const ca::BwdWorkspace w = ca::plan_layout(plan, 1, T, Ct, nk);
   const ca::Geom g{tok_off, clu_off, max_n, (int)clusters_of(max_n, cs), 0};
-  hipStream_t st = (hipStream_t)hip_stream;
-  hipError_t e = ca::launch_bwd_plan(B, T, Ct, nk, q_idx, key_idx, w, st, &g);
-  if (e == hipSuccess) e = ca::launch_tile_plan(1, T, Ct, nk, true, q_idx, key_idx, w, st);
-  return hip_status(e, "bwd plan launch");
+  return hip_status(ca::launch_bwd_plan(B, T, Ct, nk, q_idx, key_idx, w, (hipStream_t)hip_stream,
+                                        &g),
+                    "bwd plan launch");
 }
 
 size_t cluster_attn_bwd_planned_workspace(int dt, int B, int N, int H, int D) {

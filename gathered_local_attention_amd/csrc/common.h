@@ -27,65 +27,6 @@ struct RevEntry {
   uint64_t mult;
 };
 
-// ---- window ("tile") plan of the matrix-core kernels -----------------------
-// Consecutive clusters of an image are taken kWin at a time (a Morton window;
-// for a packed batch the windows run over the whole batch).  The kernels
-// stage the distinct key rows of a window once (query-major passes) or the
-// rows of the distinct query clusters that read it (key-major pass), and
-// compute every cluster on its own list of slots out of those staged rows.
-//
-// Query record (kQRec ints; a window with more than kUnionCap distinct keys
-// also gets kWin / sub_window(nk) records of sub-windows, each small enough):
-//   [0] c0 (first cluster, batch-wide)  [1] nc (clusters)  [2] u (distinct
-//   key tokens)  [3] base (added to the token ids; 0 for a packed batch)
-//   [4] flags (kQSplit: use the sub-window records; kQHoles: some slot of the
-//   first nb*16 is empty)  [5] nsub  [6..8) 0
-//   [8, 72)    the 64 query tokens (q_idx rows; -1 after nc clusters)
-//   [72, 72 + kUnionCap)  the u key tokens, padded to a multiple of 32 with a
-//              valid token
-//   then the slot table: u16 [8 clusters][16][4]: entry [c][x][b] = the LDS
-//   byte offset of the staged row of slot 16 b + x of cluster c,
-//   row * kLdsRow + 16 * row_swz(row) (16-byte chunk k of the row sits at
-//   offset ^ 16 k); empty slots point at row 0
-//   then the valid-slot masks: u64 [8] (bit s: slot s holds a token)
-// Key record (kKRec ints): [0] start (first merged entry, in the index space
-//   of `rev`)  [1] E (merged entries)  [2] c0  [3] base  [4] nc  [5..8) 0
-//   [8, 72)  the 64 key tokens of the window's clusters
-//   [72, 88) per key cluster j: its item range in `kitem` (absolute start,
-//            count)
-//   [88, 88 + 8 kKRecEnt) the query tokens of the first kKRecEnt merged
-//            entries (the rest only in `kent`)
-// Merged entries (kEnt ints each, at start .. start + E): the query clusters
-//   that read the window, ordered by cluster: their 8 query tokens.
-// Items (`kitem`, RevEntry layout, one per (query cluster, key cluster) pair,
-//   at the same index as the pair's `rev` entry): i = index of the query
-//   cluster among the window's merged entries, mult = the multiplicities of
-//   the key cluster's members in its list.
-constexpr int kWin = 8;
-constexpr int kUnionCap = 192;       // distinct key rows staged per (sub-)window
-constexpr int kQRecHead = 72;        // ints before the key tokens
-constexpr int kQSlotOff = kQRecHead + kUnionCap;         // ints: slot table
-constexpr int kQMaskOff = kQSlotOff + 8 * 16 * 4 / 2;   // ints: valid masks
-constexpr int kQRec = kQMaskOff + 16;                    // ints per record (536)
-constexpr int kQRecStride = 640;
-constexpr int kQSplit = 1, kQHoles = 2;
-constexpr int kKRecHead = 88;
-constexpr int kKRecEnt = 20;
-constexpr int kKRec = kKRecHead + 8 * kKRecEnt;   // 248 ints
-constexpr int kEnt = 8;
-// clusters per sub-window: sub_window(nk) * nk slots never exceed kUnionCap
-__host__ __device__ constexpr int sub_window(int nk) { return nk <= 48 ? 4 : 2; }
-// records per window (main + sub-windows)
-__host__ __device__ constexpr int qrec_slots(int nk) { return 1 + kWin / sub_window(nk); }
-static_assert(4 * 48 <= kUnionCap && 2 * 64 <= kUnionCap, "a sub-window always fits");
-// Staged rows in LDS are kLdsRow = 128 bytes (the 32-dim rows of two heads);
-// 16-byte chunk c of row r sits at position c ^ row_swz(r), which spreads the
-// chunks that one instruction reads from different rows over the LDS banks.
-constexpr int kLdsRow = 128;
-__host__ __device__ __forceinline__ uint32_t row_swz(int r) { return (uint32_t)((r ^ (r >> 3)) & 7); }
-static_assert(kUnionCap * kLdsRow <= 65536, "slot-table offsets fit 16 bits");
-static inline int64_t windows_of(int64_t B, int64_t C) { return B * ((C + kWin - 1) / kWin); }
-
 // ---- workspace layout of the backward pass --------------------------------
 // Two parts: the per-call part (LSE/Delta pairs of pass A, read by pass B)
 // and the plan (the transposed slot lists, a function of q_idx and key_idx
@@ -104,10 +45,6 @@ struct BwdWorkspace {
   RevEntry* stage;   // [B, C, nk]  entry of the first slot of i pointing into j
   RevEntry* rev;     // [B, C*nk]   per key cluster, sorted by i (image b from b*C*nk)
   int32_t* rtok;     // [B, C*nk, cs] query tokens of entry e (q_idx row of its i)
-  int32_t* qrec;     // [NW, qrec_slots(nk), kQRecStride] query-window records
-  int32_t* krec;     // [NW, kKRec]            key-window records
-  int32_t* kent;     // [B, C*nk, kEnt]         merged entries of the key windows
-  RevEntry* kitem;   // [B, C*nk]               items of the key windows
   size_t bytes;
 };
 
@@ -145,11 +82,6 @@ static inline BwdWorkspace plan_layout(void* base, int64_t B, int64_t N, int64_t
   w.stage = (RevEntry*)c.take((size_t)(B * C * nk) * sizeof(RevEntry));
   w.rev = (RevEntry*)c.take((size_t)(B * C * nk) * sizeof(RevEntry));
   w.rtok = (int32_t*)c.take((size_t)(B * C * nk) * 8 * sizeof(int32_t));
-  const int64_t NW = windows_of(B, C);
-  w.qrec = (int32_t*)c.take((size_t)(NW * qrec_slots((int)nk) * kQRecStride) * 4);
-  w.krec = (int32_t*)c.take((size_t)(NW * kKRec) * 4);
-  w.kent = (int32_t*)c.take((size_t)(B * C * nk) * kEnt * 4);
-  w.kitem = (RevEntry*)c.take((size_t)(B * C * nk) * sizeof(RevEntry));
   w.bytes = c.p;
   return w;
 }
@@ -379,23 +311,6 @@ bool mfma_supported(int dt, int B, int N, int C, int H, int nk);
 hipError_t launch_fwd_mfma(int dt, int B, int N, int C, int H, float scale, const void* q,
                            const void* k, const void* v, const int32_t* q_idx,
                            const int32_t* key_idx, void* o, float* lse, hipStream_t st);
-
-// Window plan (after launch_bwd_plan has built seg / rev / rtok): the query
-// and key records of every window.  `packed`: the lists hold batch-global ids.
-hipError_t launch_tile_plan(int B, int N, int C, int nk, bool packed, const int32_t* q_idx,
-                            const int32_t* key_idx, const BwdWorkspace& w, hipStream_t st);
-
-// Window-tiled matrix-core kernels (bf16 / f16, any nk = 8k, k <= 8) on a
-// window plan: forward, and the backward passes (bit 1 = query-major: Delta,
-// dQ; bit 2 = key-major: dK, dV).
-bool tile_supported(int dt, int B, int N, int C, int H, int nk);
-hipError_t launch_fwd_tile(int dt, int B, int N, int C, int H, int nk, float scale, const void* q,
-                           const void* k, const void* v, const BwdWorkspace& w, void* o,
-                           float* lse, hipStream_t st);
-hipError_t launch_bwd_tile(int pass, int dt, int B, int N, int C, int H, int nk, float scale,
-                           const void* q, const void* k, const void* v, const void* o,
-                           const void* dout, const float* lse, void* dq, void* dk, void* dv,
-                           const BwdWorkspace& w, hipStream_t st);
 
 hipError_t launch_bwd_mfma(int pass, int dt, int B, int N, int C, int H, int nk, float scale,
                            const void* q, const void* k, const void* v, const void* o,

@@ -252,19 +252,6 @@ ca_status cluster_attn_bwd_plan_varlen(int B, int T, int Ct, int max_n, const in
                                  const int32_t* key_idx, void* plan, size_t plan_bytes,
                                  void* hip_stream);
 size_t cluster_attn_bwd_planned_workspace(int dt, int B, int N, int H, int D);
-/*
- * The forward on a plan (from cluster_attn_bwd_plan / _varlen on the same
- * lists): the same computation and outputs as cluster_attn_fwd (B, N, C as
- * for cluster_attn_bwd_planned).  The plan's window records let bf16/fp16
- * calls stage each run of 8 consecutive clusters' distinct key rows once
- * (notes page "Limitations & Future Work": the gathers are the cost); the
- * outputs agree with cluster_attn_fwd to fp32 rounding of the sums (the
- * order of the key terms differs), bit for bit from call to call.
- */
-ca_status cluster_attn_fwd_planned(int dt, int B, int N, int C, int H, int D, int cs, int nk,
-                                  float scale, const void* q, const void* k, const void* v,
-                                  const int32_t* q_idx, const int32_t* key_idx, const void* plan,
-                                  size_t plan_bytes, void* o, float* lse, void* hip_stream);
 ca_status cluster_attn_bwd_planned(int dt, int B, int N, int C, int H, int D, int cs, int nk,
                              float scale, const void* q, const void* k, const void* v,
                              const void* o, const void* dout, const float* lse,

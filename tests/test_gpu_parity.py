@@ -210,8 +210,6 @@ def test_holes_repeats_and_short_lists(ca, scale):
             qi, ki = torch.from_numpy(q_idx).to(DEV), torch.from_numpy(key_idx).to(DEV)
             o, lse = ca.fwd(dev[0], dev[1], dev[2], qi, ki, scale)
             dq, dk, dv = ca.bwd(dev[0], dev[1], dev[2], o, dev[3], lse, qi, ki, scale)
-            plan = ca.bwd_plan(qi, ki, N)
-            o2, lse2 = ca.fwd(dev[0], dev[1], dev[2], qi, ki, scale, plan=plan)
             torch.cuda.synchronize()
             o_r, lse_r = O.attn_fwd_dense(q, k, v, q_idx, key_idx, scale)
             g_r = O.attn_bwd_dense(q, k, v, do, q_idx, key_idx, scale)
@@ -219,8 +217,6 @@ def test_holes_repeats_and_short_lists(ca, scale):
             rel = dt != torch.float32
             check_close("O", o, o_r, t[0], rel)
             check_close("LSE", lse, lse_r, t[1], False)
-            check_close("O (planned)", o2, o_r, t[0], rel)
-            check_close("LSE (planned)", lse2, lse_r, t[1], False)
             for nm, g, r in zip(("dQ", "dK", "dV"), (dq, dk, dv), g_r):
                 check_close(nm, g, r, t[2], rel)
 
@@ -252,8 +248,6 @@ def test_grid_plan_random_lists(ca, N):
             qi, ki = torch.from_numpy(q_idx).to(DEV), torch.from_numpy(key_idx).to(DEV)
             o, lse = ca.fwd(dev[0], dev[1], dev[2], qi, ki, scale)
             dq, dk, dv = ca.bwd(dev[0], dev[1], dev[2], o, dev[3], lse, qi, ki, scale)
-            plan = ca.bwd_plan(qi, ki, N)
-            o2, lse2 = ca.fwd(dev[0], dev[1], dev[2], qi, ki, scale, plan=plan)
             torch.cuda.synchronize()
             o_r, lse_r = O.attn_fwd_gathered(q, k, v, q_idx, key_idx, scale)
             g_r = O.attn_bwd_gathered(q, k, v, do, q_idx, key_idx, scale)
@@ -261,8 +255,6 @@ def test_grid_plan_random_lists(ca, N):
             rel = dt != torch.float32
             check_close("O", o, o_r, t[0], rel)
             check_close("LSE", lse, lse_r, t[1], False)
-            check_close("O (planned)", o2, o_r, t[0], rel)
-            check_close("LSE (planned)", lse2, lse_r, t[1], False)
             for nm, g, r in zip(("dQ", "dK", "dV"), (dq, dk, dv), g_r):
                 check_close(nm, g, r, t[2], rel)
 

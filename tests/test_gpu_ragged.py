@@ -119,14 +119,10 @@ def test_partial_cluster_attention(ca, name, B):
     dev = [case[n].to(DEV) for n in ("q", "k", "v", "do")]
     o, lse = ca.fwd(dev[0], dev[1], dev[2], perm, key, scale)
     g = ca.bwd(dev[0], dev[1], dev[2], o, dev[3], lse, perm, key, scale)
-    plan = ca.bwd_plan(perm, key, cfg.N)
-    o2, lse2 = ca.fwd(dev[0], dev[1], dev[2], perm, key, scale, plan=plan)
     torch.cuda.synchronize()
     o_r, lse_r = O.attn_fwd_gathered(case["q"], case["k"], case["v"], qi_r, key_r, scale)
     g_r = O.attn_bwd_gathered(case["q"], case["k"], case["v"], case["do"], qi_r, key_r, scale)
     _check_all(o, lse, g, o_r, lse_r, g_r, tol_for(cfg))
-    check_close("O (planned)", o2, o_r, tol_for(cfg)["o"], tol_for(cfg)["rel"])
-    check_close("LSE (planned)", lse2, lse_r, tol_for(cfg)["lse"], False)
 
 
 @pytest.mark.parametrize("dt", [torch.float32, torch.bfloat16])
@@ -168,18 +164,11 @@ def test_varlen_attention(ca, name):
     o_r, lse_r = O.attn_fwd_gathered(one("q"), one("k"), one("v"), qi_r[None], key_r[None], scale)
     g_r = O.attn_bwd_gathered(one("q"), one("k"), one("v"), one("do"), qi_r[None], key_r[None], scale)
     _check_all(o[None], lse[None], [t[None] for t in g], o_r, lse_r, g_r, TOL[cfg.dtype])
-    # planned forward: windows of 8 clusters run across image boundaries
-    for plan in (ca.bwd_plan(q_idx, key, dev[0].shape[0]),
-                 ca.bwd_plan_varlen(q_idx, key, case["lengths"])):
-        o2, lse2 = ca.fwd_varlen(dev[0], dev[1], dev[2], q_idx, key, scale, plan=plan)
-        torch.cuda.synchronize()
-        check_close("O (planned)", o2[None], o_r, TOL[cfg.dtype]["o"], TOL[cfg.dtype]["rel"])
-        check_close("LSE (planned)", lse2[None], lse_r, TOL[cfg.dtype]["lse"], False)
 
 
 def test_varlen_full_batch_every_element(ca):
     """The 32-image packed batch as the benchmark runs it (lists, a plan
-    built one workgroup per image, planned forward and backward): every
+    built one workgroup per image, forward and planned backward): every
     element against the oracle."""
     case = make_varlen_case("varlen")
     cfg = case["cfg"]
@@ -189,7 +178,7 @@ def test_varlen_full_batch_every_element(ca):
     (q_idx, _, key, _, _), (qi_r, _, key_r, _, _) = _varlen_lists(ca, case)
     dev = [case[n].to(DEV) for n in ("q", "k", "v", "do")]
     plan = ca.bwd_plan_varlen(q_idx, key, case["lengths"])
-    o, lse = ca.fwd_varlen(dev[0], dev[1], dev[2], q_idx, key, scale, plan=plan)
+    o, lse = ca.fwd_varlen(dev[0], dev[1], dev[2], q_idx, key, scale)
     g = ca.bwd_varlen(dev[0], dev[1], dev[2], o, dev[3], lse, q_idx, key, scale, plan=plan)
     torch.cuda.synchronize()
     one = lambda n: case[n][None]
