@@ -45,6 +45,7 @@ __all__ = [
     "cluster_attention",
     "bwd_plan",
     "bwd_plan_varlen",
+    "bwd_planned_noalloc",
     "build_neighbors_varlen",
     "fwd_varlen",
     "bwd_varlen",
@@ -280,6 +281,38 @@ def _bwd_planned(lib, dt, B, N, C, H, D, cs, nk, scale, q, k, v, o, do, lse, q_i
         _dev(key_idx, "key_idx", torch.int32), _dev(plan, "plan"), plan.numel(), dq.data_ptr(),
         dk.data_ptr(), dv.data_ptr(), workspace.data_ptr(), workspace.numel(), _stream(q)),
         "cluster_attn_bwd_planned")
+    return dq, dk, dv
+
+
+def bwd_planned_noalloc(q, k, v, o, do, lse, q_idx, key_idx, plan: torch.Tensor,
+                        scale: float | None = None, out=None):
+    """The planned backward with no workspace: the library keeps the
+    per-call LSE/Delta pairs in its own per-GPU scratch (B*N*H at most
+    ``_lib.load().cluster_attn_bwd_planned_noalloc_max_rows()``).  ``out``:
+    optional (dq, dk, dv) tensors to write, so that nothing is allocated
+    here either.  Calls that overlap on one GPU share the scratch and must
+    be serialised by the caller."""
+    lib = _lib.load()
+    B, N, H, D, cs, nk, q_idx = _shapes(q, q_idx, key_idx)
+    if q.dtype not in _DT:
+        raise TypeError(f"unsupported dtype {q.dtype}")
+    for t, n in ((k, "k"), (v, "v"), (o, "o"), (do, "do")):
+        if t.shape != q.shape or t.dtype != q.dtype:
+            raise ValueError(f"{n} must match q in shape and dtype")
+    _check_lse(lse, B, N, H)
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    if out is None:
+        out = (torch.empty_like(q), torch.empty_like(q), torch.empty_like(q))
+    for t in out:
+        if t.shape != q.shape or t.dtype != q.dtype:
+            raise ValueError("out tensors must match q in shape and dtype")
+    dq, dk, dv = out
+    _check(lib.cluster_attn_bwd_planned_noalloc(
+        _DT[q.dtype], B, N, q_idx.shape[1], H, D, cs, nk, scale, _dev(q, "q"), _dev(k, "k"),
+        _dev(v, "v"), _dev(o, "o"), _dev(do, "do"), _dev(lse, "lse", torch.float32),
+        _dev(q_idx, "q_idx", torch.int32), _dev(key_idx, "key_idx", torch.int32),
+        _dev(plan, "plan"), plan.numel(), _dev(dq, "dq"), _dev(dk, "dk"), _dev(dv, "dv"),
+        _stream(q)), "cluster_attn_bwd_planned_noalloc")
     return dq, dk, dv
 
 

@@ -47,6 +47,10 @@ SIGNATURES = {
         _c_int, [_c_int, _c_int, _c_int, _c_int, _vp, _vp, _c_int, _c_int, _vp, _vp, _vp, _c_size,
                  _vp]),
     "cluster_attn_bwd_planned_workspace": (_c_size, [_c_int, _c_int, _c_int, _c_int, _c_int]),
+    "cluster_attn_bwd_planned_noalloc_max_rows": (_c_size, []),
+    "cluster_attn_bwd_planned_noalloc": (
+        _c_int, [_c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _f,
+                 _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _c_size, _vp, _vp, _vp, _vp]),
     "cluster_attn_bwd_planned": (
         _c_int, [_c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _f,
                  _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _c_size, _vp, _vp, _vp, _vp,

@@ -6,6 +6,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
 #include <new>
 
 #include "../../include/cluster_attn.h"
@@ -462,6 +463,74 @@ ca_status cluster_attn_bwd_planned(int dt, int B, int N, int C, int H, int D, in
   if (B > 0 && N > 0 && C > 0 && !plan) return fail(CA_ERR_NULL, "NULL plan");
   return attn_bwd(dt, B, N, C, H, D, cs, nk, scale, q, k, v, o, dout, lse, q_idx, key_idx, plan,
                   plan_bytes, dq, dk, dv, ws, ws_bytes, hip_stream);
+}
+
+}  // extern "C"
+
+// ---- the backward without a caller workspace ------------------------------
+// The (LSE log2 e, Delta) pairs that pass A hands to pass B live in this
+// array (8 bytes per query row and head, plus one 16-byte (+inf, 0) pair):
+// each GPU holds its own copy from module load until the process ends.
+constexpr size_t kScratchBytes = size_t(32) << 20;
+static __device__ __align__(256) char scratch[kScratchBytes];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+void* g_scratch[kMaxDevices] = {};   // device address of `scratch`, per device
+std::mutex g_scratch_mu;
+
+// The address of `scratch` on the current device, looked up once per device
+// (host code never uses the array's own name, a host-side stand-in).
+ca_status scratch_of_current_device(void** out) {
+  int dev = -1;
+  const hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(CA_ERR_UNSUPPORTED, "device %d outside 0..%d", dev, kMaxDevices - 1);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch[dev]) {
+    void* p = nullptr;
+    const hipError_t r = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (r != hipSuccess) return hip_status(r, "hipGetSymbolAddress(scratch)");
+    if (!p) return fail(CA_ERR_HIP, "hipGetSymbolAddress(scratch) returned NULL");
+    g_scratch[dev] = p;
+  }
+  *out = g_scratch[dev];
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t cluster_attn_bwd_planned_noalloc_max_rows(void) {
+  // rows (query token x head) whose pairs fit the scratch with the extra pair
+  return (kScratchBytes - 256) / sizeof(float2);
+}
+
+ca_status cluster_attn_bwd_planned_noalloc(int dt, int B, int N, int C, int H, int D, int cs,
+                                           int nk, float scale, const void* q, const void* k,
+                                           const void* v, const void* o, const void* dout,
+                                           const float* lse, const int32_t* q_idx,
+                                           const int32_t* key_idx, const void* plan,
+                                           size_t plan_bytes, void* dq, void* dk, void* dv,
+                                           void* hip_stream) {
+  if (ca_status s = check_attn_shape(dt, B, N, H, D, cs, nk)) return s;
+  if (ca_status s = check_plan_sizes(B, N, C, cs, nk)) return s;
+  if (B == 0 || N == 0 || C == 0) return ok();
+  if (!plan) return fail(CA_ERR_NULL, "NULL plan");
+  const size_t need = ca::call_layout(nullptr, B, N, H).bytes;
+  if (need > kScratchBytes)
+    return fail(CA_ERR_WORKSPACE,
+                "B*N*H = %lld query rows need %zu bytes of LSE/Delta pairs; the scratch of "
+                "cluster_attn_bwd_planned_noalloc holds %zu (at most %zu rows)",
+                (long long)B * N * H, need, kScratchBytes,
+                cluster_attn_bwd_planned_noalloc_max_rows());
+  void* ws = nullptr;
+  if (ca_status s = scratch_of_current_device(&ws)) return s;
+  return attn_bwd(dt, B, N, C, H, D, cs, nk, scale, q, k, v, o, dout, lse, q_idx, key_idx, plan,
+                  plan_bytes, dq, dk, dv, ws, kScratchBytes, hip_stream);
 }
 
 ca_status cluster_attn_knn_table(const float* coords, int B, int N, int grid_side, int K,

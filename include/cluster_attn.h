@@ -259,6 +259,28 @@ ca_status cluster_attn_bwd_planned(int dt, int B, int N, int C, int H, int D, in
                              size_t plan_bytes, void* dq, void* dk, void* dv, void* ws,
                              size_t ws_bytes, void* hip_stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc):
+ * cluster_attn_bwd_planned without the workspace argument.  The per-call
+ * LSE/Delta pairs go to a scratch array compiled into the library (32 MiB,
+ * one copy per GPU, resident from module load until the process ends, its
+ * address looked up once per device with hipGetSymbolAddress); nothing is
+ * allocated and nothing needs clearing (pass A writes every pair pass B
+ * reads).  B*N*H may be at most cluster_attn_bwd_planned_noalloc_max_rows()
+ * (4,194,272), else CA_ERR_WORKSPACE.  Every call on one GPU uses the same
+ * scratch: calls that overlap on one GPU (different streams, or host
+ * threads) race and must be serialised by the caller.  The stream must
+ * belong to the current device.  Other arguments, outputs and results are
+ * those of cluster_attn_bwd_planned, bit for bit. */
+size_t cluster_attn_bwd_planned_noalloc_max_rows(void);
+ca_status cluster_attn_bwd_planned_noalloc(int dt, int B, int N, int C, int H, int D, int cs,
+                                           int nk, float scale, const void* q, const void* k,
+                                           const void* v, const void* o, const void* dout,
+                                           const float* lse, const int32_t* q_idx,
+                                           const int32_t* key_idx, const void* plan,
+                                           size_t plan_bytes, void* dq, void* dk, void* dv,
+                                           void* hip_stream);
+
 /*
  * Forward and backward of a packed batch (see
  * cluster_attn_build_neighbors_varlen): the same computation as
