@@ -131,6 +131,54 @@ def entry_times(torch, calls, n_ev, n_sets):
     return out
 
 
+def entry_times_graph(torch, calls, n_sets, replays=10):
+    """The same entry points launched from a HIP graph: one call per
+    rotating copy captured once, the graph replayed `replays` times with HIP
+    events around each replay, so the time is the GPU's (kernels and the
+    gaps between them) without the Python launch cost.  Every captured
+    call's outputs are compared bit for bit with an eager call on the same
+    inputs after the first replay; an entry point whose graph does not match
+    is reported as None.  Returns name -> {mean, median, p10, p90} (per call,
+    microseconds) or None."""
+    out = {}
+    for name, call in calls.items():
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            call(0)                       # warm-up on the capture stream
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g):
+            got = [call(i) for i in range(n_sets)]
+        g.replay()
+        torch.cuda.synchronize()
+        flat = lambda r: [t for t in (r if isinstance(r, (tuple, list)) else (r,))
+                          if hasattr(t, "is_cuda")]
+        ok = True
+        for i in range(n_sets):
+            ref = flat(call(i))
+            torch.cuda.synchronize()
+            ok = ok and all(torch.equal(a, b) for a, b in zip(flat(got[i]), ref))
+        if not ok:
+            out[name] = None
+            continue
+        ts = []
+        for _ in range(replays):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            g.replay()
+            e1.record()
+            e1.synchronize()
+            ts.append(e0.elapsed_time(e1) * 1e3 / n_sets)
+        ts.sort()
+        q = lambda f: ts[min(len(ts) - 1, int(round(f * (len(ts) - 1))))]
+        out[name] = {"mean": sum(ts) / len(ts), "median": q(0.5), "p10": q(0.1), "p90": q(0.9)}
+        del g, got
+    return out
+
+
 def rotation_copies(requested, tensor_bytes, tensors_read=3, llc_bytes=256 << 20):
     """Rotating input copies so that every timed entry point walks at least
     twice the 256 MB last-level cache before it reads a copy again (the
@@ -216,27 +264,58 @@ def cpu_baseline(cfg, case, images: int, single_images: int = 8, runs: int = 3):
     }
 
 
-def measured_traffic(entry: str):
-    """HBM bytes per launch of an entry point from the committed rocprofv3
-    FETCH_SIZE / WRITE_SIZE summary, if it was taken on the current kernel
-    sources (same hash), else None."""
+# the kernel sources whose rocprofv3 counter summaries bench.py reports
+KERNEL_SOURCES = ("attn_mfma.hip", "attn_valu.hip", "mfma_util.h", "common.h", "bwd_plan.hip",
+                  "neighbors.hip")
+
+
+def kernel_source_hash() -> str:
     import hashlib
-    path = os.path.join(ROOT, "profiles", "stage1_hbm_traffic.json")
-    if not os.path.exists(path):
-        return None
-    with open(path) as f:
-        rec = json.load(f)
     h = hashlib.sha256()
     d = os.path.join(ROOT, "gathered_local_attention_amd", "csrc")
-    for name in sorted(os.listdir(d)):
-        if name.endswith((".hip", ".h")):
-            h.update(name.encode())
-            with open(os.path.join(d, name), "rb") as f:
-                h.update(f.read())
-    if h.hexdigest() != rec.get("source_sha256"):
-        return None
-    e = rec["entries"].get(entry)
+    for name in KERNEL_SOURCES:
+        h.update(name.encode())
+        with open(os.path.join(d, name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def counter_summary(config: str):
+    """The committed rocprofv3 summary of a configuration
+    (profiles/<config>_hbm_traffic.json or _counters.json) if it was taken on
+    the current kernel sources (same hash), else None."""
+    for suffix in ("hbm_traffic", "counters"):
+        path = os.path.join(ROOT, "profiles", f"{config}_{suffix}.json")
+        if os.path.exists(path):
+            with open(path) as f:
+                rec = json.load(f)
+            if rec.get("source_sha256") == kernel_source_hash():
+                return rec
+    return None
+
+
+def measured_traffic(config: str, entry: str):
+    """HBM bytes per launch of an entry point from FETCH_SIZE / WRITE_SIZE
+    (calibrated against the copy kernel) in the committed summary, or None."""
+    rec = counter_summary(config)
+    e = None if rec is None else rec.get("entries", {}).get(entry)
     return None if e is None else e["traffic_bytes"]
+
+
+def measured_mfma(config: str, dur_us: dict):
+    """MFMA utilisation per entry point from the committed summary's MFMA
+    counters (MfmaUtil, SQ_INSTS_VALU_MFMA_MOPS_BF16), with the flops over
+    this run's entry time; None without a current summary."""
+    rec = counter_summary(config)
+    if rec is None or "mfma" not in rec:
+        return None
+    out = {}
+    for entry, m in rec["mfma"].items():
+        tf = m["bf16_flops"] / (dur_us[entry] * 1e-6) / 1e12 if entry in dur_us else None
+        out[entry] = {"mfma_busy_pct": m["busy_pct"], "bf16_flops_per_launch": m["bf16_flops"],
+                      "TFLOPs": tf,
+                      "frac_of_bf16_peak": None if tf is None else tf / BF16_MFMA_PEAK_TFLOPS}
+    return out
 
 
 def main():
@@ -345,7 +424,11 @@ def main():
                                           sets[i]["do"], outs[i][3], outs[i][0], outs[i][1],
                                           scale, workspace=gws),
     }
-    stats = entry_times(torch, calls, n_ev, len(sets))
+    eager = entry_times(torch, calls, n_ev, len(sets))
+    graph = entry_times_graph(torch, calls, len(sets))
+    # per-launch figures: the graph replay where it matched the eager results
+    # (GPU time; the eager back-to-back calls also wait for the Python launch)
+    stats = {name: graph[name] if graph.get(name) else eager[name] for name in calls}
     dur = {name: st["mean"] for name, st in stats.items()}   # microseconds per launch
 
     # warm-cache variant: every step on the same copy
@@ -404,7 +487,7 @@ def main():
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBPS,
-            "traffic": measured_traffic(dom) if cfg.name == "stage1" else None,
+            "traffic": measured_traffic(cfg.name, dom),
             "algorithmic_bytes": alg[dom]["bytes"],
             "avg_us": dur[dom],
         },
@@ -423,6 +506,15 @@ def main():
         },
         "entry_us": dur,
         "entry_us_stats": stats,
+        "entry_timing": {name: ("graph: one call per rotating copy captured, 10 replays, "
+                                "every captured call bitwise equal to an eager call")
+                         if graph.get(name) else "eager back-to-back calls (the captured "
+                         "outputs were not bitwise equal to an eager call's: the plan buffer "
+                         "also holds scratch whose contents vary)"
+                         for name in calls},
+        "entry_us_eager": {name: st["mean"] for name, st in eager.items()},
+        "entry_us_stats_eager": eager,
+        "mfma_counters": measured_mfma(cfg.name, dur),
         "warm_ms_per_step": warm_ms,
         "copy_GBps": copy_gbps,
         "copy": copy,

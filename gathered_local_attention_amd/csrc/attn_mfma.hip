@@ -14,9 +14,9 @@
 //  * v_mfma_f32_16x16x32 operand layout (checked on the hardware): lane
 //    l = c + 16 g holds row/column c and reduction indices [8g, 8g+8); the
 //    16x16 fp32 result puts rows 4g..4g+3 of column c in lane l.  Only this
-//    one MFMA shape is used: chaining it with 16x16x16 accumulations gave
-//    wrong results on this target, so 16-deep products are run on it with
-//    the upper half of every lane's reduction slice zeroed.
+//    one MFMA shape is used (16-deep products run on it with the upper half
+//    of every lane's reduction slice zeroed); the MFMA units are far from
+//    busy in these kernels, so a second shape would save little.
 //  * A cluster has 8 queries, half a 16-wide tile, so the two heads of a
 //    pair share one tile: columns 0-7 are head h0, 8-15 head h1.  Products
 //    whose other operand differs per head run as two MFMAs, block-diagonal

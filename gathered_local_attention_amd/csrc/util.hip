@@ -1,26 +1,32 @@
 // Measurement utility of libclusterattn: a plain device-to-device copy,
 // used to measure the HBM bandwidth this device achieves, against which the
 // attention kernels' effective bandwidth is reported next to the vendor
-// peak.  16-byte loads and stores, grid-stride, no LDS.
+// peak.  Each workgroup copies one contiguous chunk, eight 16-byte loads in
+// flight per thread, with non-temporal loads and stores (streamed data is
+// not kept in the caches); no LDS.
 #include "../../include/cluster_attn.h"
 #include "common.h"
 
 namespace ca {
 namespace {
 
-__global__ void __launch_bounds__(256) copy16_kernel(const uint4* __restrict__ src,
-                                                     uint4* __restrict__ dst, size_t n16) {
-  const size_t stride = (size_t)gridDim.x * blockDim.x;
-  size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
-  // four independent 16-byte loads in flight per thread
-  for (; i + 3 * stride < n16; i += 4 * stride) {
-    const uint4 a = src[i], b = src[i + stride], c = src[i + 2 * stride], d = src[i + 3 * stride];
-    dst[i] = a;
-    dst[i + stride] = b;
-    dst[i + 2 * stride] = c;
-    dst[i + 3 * stride] = d;
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+constexpr int kCopyUnroll = 8;
+
+__global__ void __launch_bounds__(256) copy16_kernel(const u32x4* __restrict__ src,
+                                                     u32x4* __restrict__ dst, size_t n16) {
+  const size_t per = (n16 + gridDim.x - 1) / gridDim.x;
+  const size_t lo = (size_t)blockIdx.x * per;
+  const size_t hi = lo + per < n16 ? lo + per : n16;
+  size_t i = lo + threadIdx.x;
+  for (; i + (kCopyUnroll - 1) * 256 < hi; i += kCopyUnroll * 256) {
+    u32x4 r[kCopyUnroll];
+#pragma unroll
+    for (int u = 0; u < kCopyUnroll; ++u) r[u] = __builtin_nontemporal_load(src + i + u * 256);
+#pragma unroll
+    for (int u = 0; u < kCopyUnroll; ++u) __builtin_nontemporal_store(r[u], dst + i + u * 256);
   }
-  for (; i < n16; i += stride) dst[i] = src[i];
+  for (; i < hi; i += 256) dst[i] = src[i];
 }
 
 __global__ void copy1_kernel(const uint8_t* __restrict__ src, uint8_t* __restrict__ dst,
@@ -42,11 +48,12 @@ extern "C" ca_status cluster_attn_device_copy(void* dst, const void* src, size_t
   hipStream_t st = (hipStream_t)hip_stream;
   const size_t n16 = bytes / 16;
   if (n16) {
-    // 8 workgroups of 256 threads per CU over the 256 CUs
+    // up to 16 workgroups of 256 threads per CU over the 256 CUs, each on a
+    // contiguous chunk of at least 4 KiB
     const size_t want = (n16 + 255) / 256;
-    const unsigned grid = (unsigned)(want < 2048 ? want : 2048);
-    hipLaunchKernelGGL(ca::copy16_kernel, dim3(grid), dim3(256), 0, st, (const uint4*)src,
-                       (uint4*)dst, n16);
+    const unsigned grid = (unsigned)(want < 4096 ? want : 4096);
+    hipLaunchKernelGGL(ca::copy16_kernel, dim3(grid), dim3(256), 0, st, (const ca::u32x4*)src,
+                       (ca::u32x4*)dst, n16);
   }
   const size_t tail = bytes - n16 * 16;
   if (tail)
