@@ -18,7 +18,7 @@ build_neighbors_varlen(coords, lengths, grid_side, cs=8, k=6)
     -> (q_idx, nbr, key_idx, tok_off, clu_off)        (packed batches)
 fwd_varlen(q, k, v, q_idx, key_idx, scale=None) -> (o, lse)
 bwd_varlen(q, k, v, o, do, lse, q_idx, key_idx, scale=None) -> (dq, dk, dv)
-knn_table(coords, grid_side, K) -> table
+knn_table(coords, grid_side, K, workspace=None) -> table
 knn_sample_fwd(feats, coords, queries, table, p) -> out
 knn_sample_bwd(feats, coords, queries, table, p, dout) -> (dfeats, dq, dp)
 knn_sample(feats, coords, queries, table, p) -> out   (autograd: feats, queries)
@@ -53,6 +53,7 @@ __all__ = [
     "bwd_workspace_bytes",
     "build_workspace_bytes",
     "knn_table",
+    "knn_table_workspace_bytes",
     "knn_sample_fwd",
     "knn_sample_bwd",
     "knn_sample",
@@ -490,18 +491,31 @@ def bwd_varlen(q, k, v, o, do, lse, q_idx, key_idx, scale: float | None = None,
 # KNN-cache point sampler (decoder)
 # ---------------------------------------------------------------------------
 
-def knn_table(coords: torch.Tensor, grid_side: int, K: int) -> torch.Tensor:
+def knn_table_workspace_bytes(B: int, N: int, grid_side: int) -> int:
+    return int(_lib.load().cluster_attn_knn_table_workspace(B, N, grid_side))
+
+
+def knn_table(coords: torch.Tensor, grid_side: int, K: int,
+              workspace: torch.Tensor | None = None) -> torch.Tensor:
     """[B, G, G, K] int32 table of the K nearest tokens of every grid cell.
 
-    coords: [B, N, 2] float32 device tensor (x = column, y = row)."""
+    coords: [B, N, 2] float32 device tensor (x = column, y = row).  Images
+    above 4096 tokens need a workspace (allocated here when not given)."""
     lib = _lib.load()
-    B, N, two = coords.shape
-    if two != 2:
+    if coords.dim() != 3 or coords.shape[2] != 2:
         raise ValueError("coords must be [B, N, 2]")
+    B, N, _ = coords.shape
     G = int(grid_side)
+    need = lib.cluster_attn_knn_table_workspace(B, N, G)
+    ws_ptr, ws_n = 0, 0
+    if need:
+        if workspace is None:
+            workspace = torch.empty(need, dtype=torch.uint8, device=coords.device)
+        ws_ptr, ws_n = workspace.data_ptr(), workspace.numel()
     table = torch.empty((B, G, G, K), dtype=torch.int32, device=coords.device)
     _check(lib.cluster_attn_knn_table(_dev(coords, "coords", torch.float32), B, N, G, K,
-                                      table.data_ptr(), _stream(coords)), "cluster_attn_knn_table")
+                                      table.data_ptr(), ws_ptr, ws_n, _stream(coords)),
+           "cluster_attn_knn_table")
     return table
 
 

@@ -57,7 +57,9 @@ SIGNATURES = {
                  _c_size, _vp]),
     "cluster_attn_device_copy": (_c_int, [_vp, _vp, _c_size, _vp]),
     "cluster_attn_check_lists": (_c_int, [_c_int, _c_int, _c_int, _c_int, _c_int, _vp, _vp]),
-    "cluster_attn_knn_table": (_c_int, [_vp, _c_int, _c_int, _c_int, _c_int, _vp, _vp]),
+    "cluster_attn_knn_table_workspace": (_c_size, [_c_int, _c_int, _c_int]),
+    "cluster_attn_knn_table": (
+        _c_int, [_vp, _c_int, _c_int, _c_int, _c_int, _vp, _vp, _c_size, _vp]),
     "cluster_attn_knn_sample_fwd": (
         _c_int, [_c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _f,
                  _vp, _vp, _vp, _vp, _vp, _vp]),

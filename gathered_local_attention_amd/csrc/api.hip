@@ -82,7 +82,7 @@ int64_t clusters_of(int64_t N, int cs) { return (N + cs - 1) / cs; }
 // Shape checks of the KNN sampler calls.
 ca_status check_knn_shape(int B, int N, int M, int Cf, int G, int K) {
   if (B < 0 || N < 0 || M < 0) return fail(CA_ERR_SHAPE, "bad sizes B=%d N=%d M=%d", B, N, M);
-  if (G < 1 || G > 4096) return fail(CA_ERR_SHAPE, "grid_side=%d outside [1, 4096]", G);
+  if (G < 1 || G > 2048) return fail(CA_ERR_SHAPE, "grid_side=%d outside [1, 2048]", G);
   if (K < 1 || K > 16) return fail(CA_ERR_UNSUPPORTED, "K=%d outside 1..16", K);
   if (Cf < 8 || Cf > 1024 || Cf % 8 != 0)
     return fail(CA_ERR_UNSUPPORTED, "channels %d: must be a multiple of 8 in [8, 1024]", Cf);
@@ -533,20 +533,30 @@ ca_status cluster_attn_bwd_planned_noalloc(int dt, int B, int N, int C, int H, i
                   plan_bytes, dq, dk, dv, ws, kScratchBytes, hip_stream);
 }
 
+size_t cluster_attn_knn_table_workspace(int B, int N, int grid_side) {
+  if (B < 0 || N < 0 || N > (1 << 24) || grid_side < 1 || grid_side > 2048) return 0;
+  return ca::knn_table_layout(nullptr, B, N).bytes;
+}
+
 ca_status cluster_attn_knn_table(const float* coords, int B, int N, int grid_side, int K,
-                           int32_t* table, void* hip_stream) {
+                                 int32_t* table, void* ws, size_t ws_bytes, void* hip_stream) {
   if (B < 0 || N < 0) return fail(CA_ERR_SHAPE, "bad sizes B=%d N=%d", B, N);
-  if (grid_side < 1 || grid_side > 64)
-    return fail(CA_ERR_UNSUPPORTED, "grid_side=%d: the table build supports 1..64", grid_side);
-  if (N > 4096) return fail(CA_ERR_UNSUPPORTED, "N=%d: the table build supports up to 4096", N);
+  if (grid_side < 1 || grid_side > 2048)
+    return fail(CA_ERR_UNSUPPORTED, "grid_side=%d: the table build supports 1..2048", grid_side);
+  if (N > (1 << 24)) return fail(CA_ERR_SHAPE, "N=%d above 2^24", N);
+  if ((int64_t)B * N > (int64_t(1) << 31) - 1) return fail(CA_ERR_SHAPE, "B*N above 2^31 - 1");
   if (K < 1 || K > 16) return fail(CA_ERR_UNSUPPORTED, "K=%d outside 1..16", K);
   if (B == 0) return ok();
   if (!table || (N > 0 && !coords)) return fail(CA_ERR_NULL, "NULL tensor pointer");
+  const size_t need = ca::knn_table_layout(nullptr, B, N).bytes;
+  if (need && !ws) return fail(CA_ERR_NULL, "NULL workspace (%zu bytes needed)", need);
+  if (ws_bytes < need) return fail(CA_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
   const size_t tb = (size_t)B * grid_side * grid_side * K * 4;
-  Range outs[] = {{table, tb}};
+  Range outs[] = {{table, tb}, {ws, need}};
   Range ins[] = {{coords, (size_t)B * N * 8}};
-  if (ca_status s = check_alias(outs, 1, ins, 1)) return s;
-  return hip_status(ca::launch_knn_table(coords, B, N, grid_side, K, table, (hipStream_t)hip_stream),
+  if (ca_status s = check_alias(outs, 2, ins, 1)) return s;
+  return hip_status(ca::launch_knn_table(coords, B, N, grid_side, K, table, ws,
+                                         (hipStream_t)hip_stream),
                     "knn table launch");
 }
 

@@ -177,18 +177,84 @@ static inline BuildWorkspace build_layout(void* base, int64_t B, int64_t T, int6
   return w;
 }
 
-// ---- workspace layout of the KNN sampler backward ---------------------------
-constexpr int kKnnPart = 256;   // entries per partition of the stable counting sort
+// ---- spatial buckets of the KNN sampler -----------------------------------
+constexpr int kKnnPart = 256;          // entries per partition of the stable counting sort
+constexpr int kKnnSmallTokens = 4096;  // images up to this many tokens are bucketed in LDS
 
+__host__ __device__ inline int knn_ceil_log2(int v) {
+  int b = 0;
+  while ((1 << b) < v) ++b;
+  return b;
+}
+
+// Square buckets of 2^bs fixed-point units, Pb = 2^pb to a side: about two
+// tokens per bucket, a bucket at least one cell (2^shift units) wide.
+struct KnnBuckets {
+  int shift, pb, bs, Pb, nb;
+};
+__host__ __device__ inline KnnBuckets knn_buckets(int N, int G) {
+  KnnBuckets g;
+  g.shift = 16 - knn_ceil_log2(G);
+  g.pb = 0;
+  const int half = (N > 1 ? N : 1) / 2;
+  while (g.pb < 16 - g.shift && (int64_t(1) << (2 * g.pb + 2)) <= half) ++g.pb;
+  g.bs = 16 - g.pb;
+  g.Pb = 1 << g.pb;
+  g.nb = g.Pb * g.Pb;
+  return g;
+}
+// the largest bucket count of an image of N tokens over every grid side
+static inline int64_t knn_max_buckets(int64_t N) {
+  int pb = 0;
+  const int64_t half = (N > 1 ? N : 1) / 2;
+  while (pb < 16 && (int64_t(1) << (2 * pb + 2)) <= half) ++pb;
+  return int64_t(1) << (2 * pb);
+}
+
+// ---- workspace layout of the KNN table build (images above kKnnSmallTokens)
+struct KnnTableWorkspace {
+  int32_t* bcnt;    // [B, nb]       tokens per bucket, then placement cursors
+  int32_t* bstart;  // [B, nb + 1]   bucket starts
+  int32_t* brank;   // [B, N]        rank of each token in its bucket
+  uint2* tok;       // [B, N]        (qx | qy << 16, token) in bucket order
+  size_t bytes;
+};
+
+static inline KnnTableWorkspace knn_table_layout(void* base, int64_t B, int64_t N) {
+  KnnTableWorkspace w;
+  size_t p = 0;
+  char* b = (char*)base;
+  auto take = [&](size_t n) {
+    size_t at = p;
+    p = align_up(p + n, 256);
+    return b ? (void*)(b + at) : (void*)nullptr;
+  };
+  const bool large = N > kKnnSmallTokens;
+  const int64_t nb = large ? knn_max_buckets(N) : 0;
+  w.bcnt = (int32_t*)take((size_t)(B * nb) * 4);
+  w.bstart = (int32_t*)take(large ? (size_t)(B * (nb + 1)) * 4 : 0);
+  w.brank = (int32_t*)take(large ? (size_t)(B * N) * 4 : 0);
+  w.tok = (uint2*)take(large ? (size_t)(B * N) * 8 : 0);
+  w.bytes = p;
+  return w;
+}
+
+// ---- workspace layout of the KNN sampler backward ---------------------------
+// Images up to kKnnSmallTokens tokens sort the entries by token with
+// partition counts (pcnt); larger ones place them by per-token cursors into
+// lst, rank them inside each token's segment, and bucket the tokens for the
+// walk order (the table build's bucket arrays).
 struct KnnWorkspace {
-  int32_t* cnt;     // [B, N]        entries per token
+  int32_t* cnt;     // [B, N]        entries per token (then cursors, large images)
   int32_t* off;     // [B, N + 1]    segment starts (per image, relative)
   int32_t* pcnt;    // [B, P, N]     per partition of kKnnPart entries: counts, then prefixes
+  int32_t* lst;     // [B, M * K]    (large images, same place as pcnt) entries, unranked
   int32_t* slot;    // [B, M, K]     token of every (query, slot), -1 empty
   float* wgt;       // [B, M, K]     its weight
   int32_t* ent;     // [B, M * K]    entries (query * K + slot) by token
   float* dpart;     // [B, M]        per-query share of dL/dp
   int32_t* order;   // [B, N]        walk order of the tokens (feature gradient)
+  KnnTableWorkspace bk;   // large images: bucket arrays of the walk order
   size_t bytes;
 };
 
@@ -201,15 +267,20 @@ static inline KnnWorkspace knn_layout(void* base, int64_t B, int64_t N, int64_t 
     p = align_up(p + n, 256);
     return b ? (void*)(b + at) : (void*)nullptr;
   };
+  const bool large = N > kKnnSmallTokens;
   w.cnt = (int32_t*)take((size_t)(B * N) * 4);
   w.off = (int32_t*)take((size_t)(B * (N + 1)) * 4);
   const int64_t P = (M * K + kKnnPart - 1) / kKnnPart;
-  w.pcnt = (int32_t*)take((size_t)(B * P * N) * 4);
+  w.pcnt = (int32_t*)take(large ? (size_t)(B * M * K) * 4 : (size_t)(B * P * N) * 4);
+  w.lst = w.pcnt;
   w.slot = (int32_t*)take((size_t)(B * M * K) * 4);
   w.wgt = (float*)take((size_t)(B * M * K) * 4);
   w.ent = (int32_t*)take((size_t)(B * M * K) * 4);
   w.dpart = (float*)take((size_t)(B * M) * 4);
   w.order = (int32_t*)take((size_t)(B * N) * 4);
+  const KnnTableWorkspace tb = knn_table_layout(nullptr, B, N);
+  char* tb_base = (char*)take(tb.bytes);
+  w.bk = knn_table_layout(b ? tb_base : nullptr, B, N);
   w.bytes = p;
   return w;
 }
@@ -319,7 +390,7 @@ hipError_t launch_bwd_mfma(int pass, int dt, int B, int N, int C, int H, int nk,
                            const BwdWorkspace& w, hipStream_t st);
 
 // KNN-cache point sampler (knn_sampler.hip)
-hipError_t launch_knn_table(const float* coords, int B, int N, int G, int K, int32_t* table,
+hipError_t launch_knn_table(const float* coords, int B, int N, int G, int K, int32_t* table, void* ws,
                             hipStream_t st);
 hipError_t launch_knn_fwd(int dt, int B, int N, int M, int Cf, int G, int K, float p,
                           const float* coords, const void* feats, const float* queries,

@@ -55,26 +55,122 @@ namespace {
 
 constexpr int kKnnMaxK = 16;
 constexpr int kTabThreads = 256;
-constexpr int kTabMaxBuckets = 64 * 64;   // grid sides up to 64
-constexpr int kTabMaxTokens = 4096;
+constexpr int kTabMaxBuckets = 64 * 64;   // LDS buckets of the small-image build (at most 2048 used)
+constexpr int kTabMaxTokens = kKnnSmallTokens;
 constexpr int kKnnThreads = 256;          // 4 waves
 constexpr int kPart = kKnnPart;           // entries per partition of the stable counting sort
-
-__device__ __forceinline__ int ceil_log2(int v) {
-  int b = 0;
-  while ((1 << b) < v) ++b;
-  return b;
-}
+// search keys (d2 << kTokBits | token): d2 < 2^33, tokens < 2^24
+constexpr int kTokBits = 24;
+constexpr uint64_t kTokMask = (uint64_t(1) << kTokBits) - 1;
 
 // ---------------------------------------------------------------------------
-// Table build.  grid = (B, parts): part y of an image takes kTabTiles tiles
-// of 8 x 8 cells (one wave each) and repeats the image's bucketing (cheap:
-// at most 4096 tokens).  Buckets are squares of 2^bs fixed-point units,
-// bs chosen so that an image holds about two tokens per bucket (at least a
-// cell, at most the whole range).
+// Table build.  Buckets are squares of 2^bs fixed-point units (about two
+// tokens each, at least a cell: knn_buckets).  Small images (up to
+// kTabMaxTokens tokens) are bucketed in LDS by every workgroup of the image
+// (cheap); larger ones once, in global memory, by the bucket kernels below.
+// Either way one wave per 8 x 8-cell tile (lane = cell) grows a window of
+// buckets around its tile ring by ring, every lane testing every token of
+// the window (uniform loops: no divergence but the insertions), and stops
+// once every lane's K-th best is strictly closer than any token outside the
+// window can be: a token beyond the window's top edge at fixed-point row
+// R0 * 2^bs has Y <= R0 * 2^bs - 1, so |Y - cy| >= cy - R0 * 2^bs + 1;
+// likewise on the other three sides.  The keys are whole (distance, token)
+// pairs, so the order in which the bucketing left a bucket's tokens does not
+// matter: the table is unique.
 // ---------------------------------------------------------------------------
 constexpr int kTabTiles = kTabThreads / 64;
 
+// start[x] = first token of bucket x in tok (row-major buckets), the end of
+// the last bucket is `total`.  kWide: start and tok are in global memory;
+// a row's tokens are loaded 64 at a time, one per lane, and handed round the
+// wave by readlane.  Otherwise they are in LDS and read by every lane.
+template <int KM, bool kWide>
+__device__ __forceinline__ void table_tile(const int* start, const uint2* tok, int total,
+                                           const KnnBuckets& bg, int G, int K, int tile,
+                                           int32_t* __restrict__ table_img) {
+  const int lane = threadIdx.x & 63;
+  const int tiles_side = (G + 7) >> 3;
+  const int Pb = bg.Pb, nb = bg.nb, bs = bg.bs, shift = bg.shift;
+  const int i0 = (tile / tiles_side) * 8, j0 = (tile % tiles_side) * 8;
+  const int i = i0 + (lane >> 3), j = j0 + (lane & 7);
+  const bool valid = i < G && j < G;
+  const int64_t cx = (int64_t)(2 * j + 1) << (shift - 1);   // (j + 1/2) s
+  const int64_t cy = (int64_t)(2 * i + 1) << (shift - 1);
+  // the tile's own buckets (cells up to min(G, i0 + 8) - 1)
+  const int ilast = min(G, i0 + 8) - 1, jlast = min(G, j0 + 8) - 1;
+  const int tr0 = (i0 << shift) >> bs, tr1 = (((ilast + 1) << shift) - 1) >> bs;
+  const int tc0 = (j0 << shift) >> bs, tc1 = (((jlast + 1) << shift) - 1) >> bs;
+  uint64_t best[KM];
+#pragma unroll
+  for (int r = 0; r < KM; ++r) best[r] = ~0ull;
+  uint64_t worst = ~0ull;   // best[K - 1]
+  auto insert = [&](uint2 e) {
+    const int64_t dx = (int64_t)(e.x & 0xFFFFu) - cx, dy = (int64_t)(e.x >> 16) - cy;
+    uint64_t x = ((uint64_t)(dx * dx + dy * dy) << kTokBits) | e.y;
+    if (x >= worst) return;
+#pragma unroll
+    for (int r = 0; r < KM; ++r) {
+      if (r < K) {
+        const uint64_t lo = x < best[r] ? x : best[r];
+        const uint64_t hi = x < best[r] ? best[r] : x;
+        best[r] = lo;
+        x = hi;
+      }
+      if (r == K - 1) worst = best[r];
+    }
+  };
+  // tokens of the buckets (by, bx0 .. bx1): one contiguous range
+  auto scan_row = [&](int by, int bx0, int bx1) {
+    const int bb0 = by * Pb + bx0, bb1 = by * Pb + bx1;
+    if constexpr (kWide) {
+      const int t0 = __builtin_amdgcn_readfirstlane(start[bb0]);
+      const int t1 = __builtin_amdgcn_readfirstlane(start[bb1 + 1]);
+      for (int c = t0; c < t1; c += 64) {
+        const uint2 mine = c + lane < t1 ? tok[c + lane] : make_uint2(0u, 0u);
+        const int n = min(64, t1 - c);
+        for (int u = 0; u < n; ++u) {
+          uint2 e;
+          e.x = (uint32_t)__builtin_amdgcn_readlane((int)mine.x, u);
+          e.y = (uint32_t)__builtin_amdgcn_readlane((int)mine.y, u);
+          insert(e);
+        }
+      }
+    } else {
+      const int t0 = start[bb0], t1 = bb1 + 1 < nb ? start[bb1 + 1] : total;
+      for (int t = t0; t < t1; ++t) insert(tok[t]);
+    }
+  };
+  for (int m = 0;; ++m) {
+    const int r0 = tr0 - m, r1 = tr1 + m, c0 = tc0 - m, c1 = tc1 + m;   // window (buckets)
+    if (m == 0) {
+      for (int by = r0; by <= r1; ++by) scan_row(by, c0, c1);
+    } else {
+      const int cl = max(c0, 0), ch = min(c1, Pb - 1);
+      if (r0 >= 0) scan_row(r0, cl, ch);
+      if (r1 <= Pb - 1) scan_row(r1, cl, ch);
+      for (int by = max(r0 + 1, 0); by <= min(r1 - 1, Pb - 1); ++by) {
+        if (c0 >= 0) scan_row(by, c0, c0);
+        if (c1 <= Pb - 1) scan_row(by, c1, c1);
+      }
+    }
+    if (r0 <= 0 && c0 <= 0 && r1 >= Pb - 1 && c1 >= Pb - 1) break;   // every bucket seen
+    int64_t lb = INT64_MAX;
+    if (r0 > 0) lb = min(lb, cy - ((int64_t)r0 << bs) + 1);
+    if (r1 < Pb - 1) lb = min(lb, ((int64_t)(r1 + 1) << bs) - cy);
+    if (c0 > 0) lb = min(lb, cx - ((int64_t)c0 << bs) + 1);
+    if (c1 < Pb - 1) lb = min(lb, ((int64_t)(c1 + 1) << bs) - cx);
+    const bool done = !valid || (worst != ~0ull && (int64_t)(worst >> kTokBits) < lb * lb);
+    if (__all(done)) break;
+  }
+  if (!valid) return;
+  int32_t* row = table_img + ((int64_t)i * G + j) * K;
+#pragma unroll
+  for (int r = 0; r < KM; ++r)
+    if (r < K) row[r] = best[r] == ~0ull ? -1 : (int32_t)(best[r] & kTokMask);
+}
+
+// Small images.  grid = (B, parts): part y of an image takes kTabTiles tiles
+// (one wave each) and repeats the image's bucketing in LDS.
 template <int KM>
 __global__ void __launch_bounds__(kTabThreads)
 knn_table_kernel(const float* __restrict__ coords, int N, int G, int K, int32_t* __restrict__ table) {
@@ -83,13 +179,9 @@ knn_table_kernel(const float* __restrict__ coords, int N, int G, int K, int32_t*
   __shared__ int tmp[17];
   const int b = blockIdx.x;
   const int tid = threadIdx.x;
-  const int shift = 16 - ceil_log2(G);     // fixed-point units per cell: s = 2^shift
-  const double step = (double)(1 << shift);
-  int pb = 0;                              // bucket grid side 2^pb: about N / 2 buckets
-  while (pb < 16 - shift && (1 << (2 * pb + 2)) <= max(N, 1) / 2) ++pb;
-  const int bs = 16 - pb;                  // bucket side 2^bs units (>= one cell)
-  const int Pb = 1 << pb;
-  const int nb = Pb * Pb;
+  const KnnBuckets bg = knn_buckets(N, G);
+  const double step = (double)(1 << bg.shift);
+  const int nb = bg.nb, bs = bg.bs, Pb = bg.Pb;
   const float2* xy = reinterpret_cast<const float2*>(coords) + (int64_t)b * N;
 
   for (int x = tid; x < nb; x += kTabThreads) start[x] = 0;
@@ -133,81 +225,60 @@ knn_table_kernel(const float* __restrict__ coords, int N, int G, int K, int32_t*
   for (int r = 0; r < kPer; ++r)
     if (bk[r] >= 0) tok[start[bk[r]] + rk[r]] = make_uint2(pk[r], (uint32_t)(tid + r * kTabThreads));
   __syncthreads();
-
-  // One wave per tile (lane = cell).  The wave scans a window of buckets
-  // around its tile that grows one ring at a time, every lane testing every
-  // token of the window (uniform loops: no divergence but the insertions).
-  // It stops once every lane's K-th best is strictly closer than any token
-  // outside the window can be: a token beyond the window's top edge at
-  // fixed-point row R0 * 2^bs has Y <= R0 * 2^bs - 1, so |Y - cy| >=
-  // cy - R0 * 2^bs + 1; likewise on the other three sides.
-  const int lane = tid & 63;
   const int tiles_side = (G + 7) >> 3;
   const int tile = blockIdx.y * kTabTiles + (tid >> 6);
   if (tile >= tiles_side * tiles_side) return;
-  const int i0 = (tile / tiles_side) * 8, j0 = (tile % tiles_side) * 8;
-  const int i = i0 + (lane >> 3), j = j0 + (lane & 7);
-  const bool valid = i < G && j < G;
-  const int64_t cx = (int64_t)(2 * j + 1) << (shift - 1);   // (j + 1/2) s
-  const int64_t cy = (int64_t)(2 * i + 1) << (shift - 1);
-  // the tile's own buckets (cells up to min(G, i0 + 8) - 1)
-  const int ilast = min(G, i0 + 8) - 1, jlast = min(G, j0 + 8) - 1;
-  const int tr0 = (i0 << shift) >> bs, tr1 = (((ilast + 1) << shift) - 1) >> bs;
-  const int tc0 = (j0 << shift) >> bs, tc1 = (((jlast + 1) << shift) - 1) >> bs;
-  // keys (d2 << 12 | token): d2 < 2^33, tokens < 2^12
-  uint64_t best[KM];
-#pragma unroll
-  for (int r = 0; r < KM; ++r) best[r] = ~0ull;
-  uint64_t worst = ~0ull;   // best[K - 1]
-  // tokens of the buckets (by, bx0 .. bx1): one contiguous range (row-major
-  // bucket order)
-  auto scan_row = [&](int by, int bx0, int bx1) {
-    const int bb0 = by * Pb + bx0, bb1 = by * Pb + bx1;
-    const int t0 = start[bb0], t1 = bb1 + 1 < nb ? start[bb1 + 1] : total;
-    for (int t = t0; t < t1; ++t) {
-      const uint2 e = tok[t];
-      const int64_t dx = (int64_t)(e.x & 0xFFFFu) - cx, dy = (int64_t)(e.x >> 16) - cy;
-      uint64_t x = ((uint64_t)(dx * dx + dy * dy) << 12) | e.y;
-      if (x >= worst) continue;
-#pragma unroll
-      for (int r = 0; r < KM; ++r) {
-        if (r < K) {
-          const uint64_t lo = x < best[r] ? x : best[r];
-          const uint64_t hi = x < best[r] ? best[r] : x;
-          best[r] = lo;
-          x = hi;
-        }
-        if (r == K - 1) worst = best[r];
-      }
-    }
-  };
-  for (int m = 0;; ++m) {
-    const int r0 = tr0 - m, r1 = tr1 + m, c0 = tc0 - m, c1 = tc1 + m;   // window (buckets)
-    if (m == 0) {
-      for (int by = r0; by <= r1; ++by) scan_row(by, c0, c1);
-    } else {
-      const int cl = max(c0, 0), ch = min(c1, Pb - 1);
-      if (r0 >= 0) scan_row(r0, cl, ch);
-      if (r1 <= Pb - 1) scan_row(r1, cl, ch);
-      for (int by = max(r0 + 1, 0); by <= min(r1 - 1, Pb - 1); ++by) {
-        if (c0 >= 0) scan_row(by, c0, c0);
-        if (c1 <= Pb - 1) scan_row(by, c1, c1);
-      }
-    }
-    if (r0 <= 0 && c0 <= 0 && r1 >= Pb - 1 && c1 >= Pb - 1) break;   // every bucket seen
-    int64_t lb = INT64_MAX;
-    if (r0 > 0) lb = min(lb, cy - ((int64_t)r0 << bs) + 1);
-    if (r1 < Pb - 1) lb = min(lb, ((int64_t)(r1 + 1) << bs) - cy);
-    if (c0 > 0) lb = min(lb, cx - ((int64_t)c0 << bs) + 1);
-    if (c1 < Pb - 1) lb = min(lb, ((int64_t)(c1 + 1) << bs) - cx);
-    const bool done = !valid || (worst != ~0ull && (int64_t)(worst >> 12) < lb * lb);
-    if (__all(done)) break;
-  }
-  if (!valid) return;
-  int32_t* row = table + (((int64_t)b * G + i) * G + j) * K;
-#pragma unroll
-  for (int r = 0; r < KM; ++r)
-    if (r < K) row[r] = best[r] == ~0ull ? -1 : (int32_t)(best[r] & 0xFFFu);
+  table_tile<KM, false>(start, tok, total, bg, G, K, tile, table + (int64_t)b * G * G * K);
+}
+
+// Large images: the tokens counting-sorted into the buckets in global
+// memory (count with integer atomics, scan, place), then searched.
+__global__ void __launch_bounds__(kKnnThreads)
+knn_bucket_count_kernel(const float* __restrict__ coords, int64_t n_tok, int N, int G,
+                        int32_t* __restrict__ bcnt, int32_t* __restrict__ brank) {
+  const int64_t x = (int64_t)blockIdx.x * kKnnThreads + threadIdx.x;
+  if (x >= n_tok) return;
+  const int64_t b = x / N;
+  const KnnBuckets bg = knn_buckets(N, G);
+  const double step = (double)(1 << bg.shift);
+  const float2 c = reinterpret_cast<const float2*>(coords)[x];
+  const uint32_t qx = quantize_axis(c.x, step), qy = quantize_axis(c.y, step);
+  const int bk = (int)((qy >> bg.bs) * (uint32_t)bg.Pb + (qx >> bg.bs));
+  brank[x] = atomicAdd(&bcnt[b * bg.nb + bk], 1);
+}
+
+// tok (when given): (qx | qy << 16, token) at its bucket place; order (when
+// given): the token number there (the spatial walk order)
+__global__ void __launch_bounds__(kKnnThreads)
+knn_bucket_place_kernel(const float* __restrict__ coords, int64_t n_tok, int N, int G,
+                        const int32_t* __restrict__ bstart, const int32_t* __restrict__ brank,
+                        uint2* __restrict__ tok, int32_t* __restrict__ order) {
+  const int64_t x = (int64_t)blockIdx.x * kKnnThreads + threadIdx.x;
+  if (x >= n_tok) return;
+  const int64_t b = x / N;
+  const int e = (int)(x - b * N);
+  const KnnBuckets bg = knn_buckets(N, G);
+  const double step = (double)(1 << bg.shift);
+  const float2 c = reinterpret_cast<const float2*>(coords)[x];
+  const uint32_t qx = quantize_axis(c.x, step), qy = quantize_axis(c.y, step);
+  const int bk = (int)((qy >> bg.bs) * (uint32_t)bg.Pb + (qx >> bg.bs));
+  const int64_t pos = b * N + bstart[b * (bg.nb + 1) + bk] + brank[x];
+  if (tok) tok[pos] = make_uint2(qx | (qy << 16), (uint32_t)e);
+  if (order) order[pos] = e;
+}
+
+// grid = (B, parts), as the small-image kernel, reading the bucket arrays
+template <int KM>
+__global__ void __launch_bounds__(kTabThreads)
+knn_table_search_kernel(int N, int G, int K, const int32_t* __restrict__ bstart,
+                        const uint2* __restrict__ btok, int32_t* __restrict__ table) {
+  const int b = blockIdx.x;
+  const KnnBuckets bg = knn_buckets(N, G);
+  const int tiles_side = (G + 7) >> 3;
+  const int tile = blockIdx.y * kTabTiles + (threadIdx.x >> 6);
+  if (tile >= tiles_side * tiles_side) return;
+  table_tile<KM, true>(bstart + (int64_t)b * (bg.nb + 1), btok + (int64_t)b * N, N, bg, G, K, tile,
+                       table + (int64_t)b * G * G * K);
 }
 
 // ---------------------------------------------------------------------------
@@ -448,8 +519,8 @@ knn_bwd_query_kernel(int N, int M, int Cf, int G, int K, int lg, float p, int64_
                      const float* __restrict__ coords, const T* __restrict__ feats,
                      const float* __restrict__ queries, const int32_t* __restrict__ table,
                      const T* __restrict__ dout, float* __restrict__ dq, float* __restrict__ dpart,
-                     int32_t* __restrict__ ent_slot, float* __restrict__ ent_w, int P,
-                     int32_t* __restrict__ pcnt) {
+                     int32_t* __restrict__ ent_slot, float* __restrict__ ent_w,
+                     int32_t* __restrict__ cnt) {
   using Ck = Chunk<T>;
   __shared__ WaveSlots<KM> sw[kKnnThreads / 64];
   __shared__ float sg[kKnnThreads / 64][64][KM];
@@ -576,15 +647,15 @@ knn_bwd_query_kernel(int N, int M, int Cf, int G, int K, int lg, float p, int64_
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) sdp += __shfl_xor(sdp, o, 64);
   if (lane == 0) dpart[base / qwv] = sdp;
-  // the entries' counts per partition of kPart entries and token (integer
-  // atomics, order independent), last: nothing in this wave waits on them;
-  // without pcnt they are counted by knn_pcount_kernel instead
-  if (mine && pcnt) {
+  // the entries' counts per token (integer atomics, order independent),
+  // last: nothing in this wave waits on them.  Large images only (pcnt =
+  // the per-token counts); small ones count per partition in
+  // knn_pcount_kernel instead.
+  if (mine && cnt) {
     const int64_t b = id / M;
-    const int64_t e0 = (id - b * M) * K;   // first entry of this query in its image
 #pragma unroll
     for (int k = 0; k < KM; ++k)
-      if (k < K && qw.slot[k] >= 0) atomicAdd(&pcnt[(b * P + (e0 + k) / kPart) * N + qw.slot[k]], 1);
+      if (k < K && qw.slot[k] >= 0) atomicAdd(&cnt[b * N + qw.slot[k]], 1);
   }
 }
 
@@ -718,6 +789,47 @@ knn_pplace_kernel(int N, int64_t MK, int P, const int32_t* __restrict__ ent_slot
     ent_all[b * MK + off_all[b * (N + 1) + t] + pcnt[(b * P + s) * N + t] + rank] = (int32_t)(e0 + u);
 }
 
+// Large images: token-major entry lists by per-token cursors.  (1) The
+// query-major kernel counts the entries per token; (2) knn_scan_kernel
+// turns the counts into segment starts; (3) every entry takes a place in
+// its token's segment of lst from an integer atomic on the token's cursor
+// (in no fixed order); (4) every entry is moved to segment start + its rank
+// among the segment's entries by entry number.  The lists come out in
+// entry order, as from the stable counting sort of small images.
+__global__ void __launch_bounds__(kKnnThreads)
+knn_lplace_kernel(int N, int64_t MK, int64_t n_ent, const int32_t* __restrict__ ent_slot,
+                  const int32_t* __restrict__ off_all, int32_t* __restrict__ cur,
+                  int32_t* __restrict__ lst) {
+  const int64_t x = (int64_t)blockIdx.x * kKnnThreads + threadIdx.x;
+  if (x >= n_ent) return;
+  const int t = ent_slot[x];
+  if (t < 0) return;
+  const int64_t b = x / MK;
+  const int r = atomicAdd(&cur[b * N + t], 1);
+  lst[b * MK + off_all[b * (N + 1) + t] + r] = (int32_t)(x - b * MK);
+}
+
+__global__ void __launch_bounds__(kKnnThreads)
+knn_lrank_kernel(int N, int64_t MK, int64_t n_ent, const int32_t* __restrict__ ent_slot,
+                 const int32_t* __restrict__ off_all, const int32_t* __restrict__ lst,
+                 int32_t* __restrict__ ent_all) {
+  const int64_t x = (int64_t)blockIdx.x * kKnnThreads + threadIdx.x;
+  if (x >= n_ent) return;
+  const int t = ent_slot[x];
+  if (t < 0) return;
+  const int64_t b = x / MK;
+  const int e = (int)(x - b * MK);
+  const int a = off_all[b * (N + 1) + t], z = off_all[b * (N + 1) + t + 1];
+  const int32_t* seg = lst + b * MK;
+  int rank = 0, y = a;
+  for (; y + 4 <= z; y += 4) {   // four loads in flight
+    const int v0 = seg[y], v1 = seg[y + 1], v2 = seg[y + 2], v3 = seg[y + 3];
+    rank += (v0 < e) + (v1 < e) + (v2 < e) + (v3 < e);
+  }
+  for (; y < z; ++y) rank += seg[y] < e;
+  ent_all[b * MK + a + rank] = e;
+}
+
 // Spatial walk order of the tokens for the feature gradient: the tokens of
 // an image bucketed on a coarse grid (about two per bucket) in LDS, so that
 // the waves resident at one time work on neighbouring tokens, which share
@@ -728,11 +840,9 @@ __global__ void __launch_bounds__(kTabThreads)
 knn_order_kernel(const float* __restrict__ coords, int N, int G, int32_t* __restrict__ order) {
   __shared__ int start[kTabMaxBuckets];
   const int b = blockIdx.x, tid = threadIdx.x;
-  const int shift = 16 - ceil_log2(G);
-  const double step = (double)(1 << shift);
-  int pb = 0;
-  while (pb < 16 - shift && (1 << (2 * pb + 2)) <= max(N, 1) / 2) ++pb;
-  const int bs = 16 - pb, Pb = 1 << pb, nb = Pb * Pb;
+  const KnnBuckets bg = knn_buckets(N, G);
+  const double step = (double)(1 << bg.shift);
+  const int bs = bg.bs, Pb = bg.Pb, nb = bg.nb;
   const float2* xy = reinterpret_cast<const float2*>(coords) + (int64_t)b * N;
   for (int x = tid; x < nb; x += kTabThreads) start[x] = 0;
   __syncthreads();
@@ -949,37 +1059,61 @@ hipError_t bwd_t(int B, int N, int M, int Cf, int G, int K, float p, const float
   const int P = (int)((MK + kPart - 1) / kPart);
   const int64_t npc = (int64_t)B * P * N, nparts = (int64_t)B * P;
   const int qwv = queries_per_wave(lg);
-  // partition counts: in LDS per partition for images that fit, else by
-  // integer atomics in the query-major kernel into zeroed counters
-  const bool lds_count = N <= kTabMaxTokens;
+  // small images: counts per partition of kPart entries in LDS, stable
+  // counting sort; large ones: per-token counts by integer atomics in the
+  // query-major kernel, cursor placement and ranking
+  const bool large = N > kTabMaxTokens;
   auto go = [&](auto kern) {
     hipLaunchKernelGGL(kern, dim3(blocks_for(nq, qwv)), dim3(kKnnThreads), 0, st, N, M, Cf, G, K,
                        lg, p, nq, qwv, coords, (const T*)feats, queries, table, (const T*)dout, dq,
-                       w.dpart, w.slot, w.wgt, P, lds_count ? nullptr : w.pcnt);
+                       w.dpart, w.slot, w.wgt, large ? w.cnt : nullptr);
   };
   // empty sizes launch nothing but what writes outputs (dF, dp)
-  if (npc > 0 && !lds_count)
-    hipLaunchKernelGGL(knn_zero_kernel, grid1(npc), dim3(kKnnThreads), 0, st, npc, w.pcnt);
+  if (large && ntok > 0)
+    hipLaunchKernelGGL(knn_zero_kernel, grid1(ntok), dim3(kKnnThreads), 0, st, ntok, w.cnt);
   if (nq > 0) {
     if (K <= 4) go(knn_bwd_query_kernel<T, 4>);
     else if (K <= 8) go(knn_bwd_query_kernel<T, 8>);
     else go(knn_bwd_query_kernel<T, 16>);
   }
-  if (npc > 0 && lds_count)
-    hipLaunchKernelGGL(knn_pcount_kernel, dim3((unsigned)nparts), dim3(kKnnThreads), 0, st, N, MK,
-                       P, (const int32_t*)w.slot, w.pcnt);
   if (ntok > 0) {
-    hipLaunchKernelGGL(knn_pprefix_kernel, grid1(ntok), dim3(kKnnThreads), 0, st, N, P, ntok,
-                       w.pcnt, w.cnt);
-    hipLaunchKernelGGL(knn_scan_kernel, dim3(B), dim3(kScanThreads), 0, st, N,
-                       (const int32_t*)w.cnt, w.off);
-    if (nparts > 0)
-      hipLaunchKernelGGL(knn_pplace_kernel, dim3((unsigned)nparts), dim3(kKnnThreads), 0, st, N, MK,
-                         P, (const int32_t*)w.slot, (const int32_t*)w.off, (const int32_t*)w.pcnt,
-                         w.ent);
-    const bool ordered = N <= kTabMaxTokens && G <= 65536;
-    if (ordered)
-      hipLaunchKernelGGL(knn_order_kernel, dim3(B), dim3(kTabThreads), 0, st, coords, N, G, w.order);
+    if (!large) {
+      if (npc > 0)
+        hipLaunchKernelGGL(knn_pcount_kernel, dim3((unsigned)nparts), dim3(kKnnThreads), 0, st, N,
+                           MK, P, (const int32_t*)w.slot, w.pcnt);
+      hipLaunchKernelGGL(knn_pprefix_kernel, grid1(ntok), dim3(kKnnThreads), 0, st, N, P, ntok,
+                         w.pcnt, w.cnt);
+      hipLaunchKernelGGL(knn_scan_kernel, dim3(B), dim3(kScanThreads), 0, st, N,
+                         (const int32_t*)w.cnt, w.off);
+      if (nparts > 0)
+        hipLaunchKernelGGL(knn_pplace_kernel, dim3((unsigned)nparts), dim3(kKnnThreads), 0, st, N,
+                           MK, P, (const int32_t*)w.slot, (const int32_t*)w.off,
+                           (const int32_t*)w.pcnt, w.ent);
+      hipLaunchKernelGGL(knn_order_kernel, dim3(B), dim3(kTabThreads), 0, st, coords, N, G,
+                         w.order);
+    } else {
+      hipLaunchKernelGGL(knn_scan_kernel, dim3(B), dim3(kScanThreads), 0, st, N,
+                         (const int32_t*)w.cnt, w.off);
+      hipLaunchKernelGGL(knn_zero_kernel, grid1(ntok), dim3(kKnnThreads), 0, st, ntok, w.cnt);
+      if (nent > 0) {
+        hipLaunchKernelGGL(knn_lplace_kernel, grid1(nent), dim3(kKnnThreads), 0, st, N, MK, nent,
+                           (const int32_t*)w.slot, (const int32_t*)w.off, w.cnt, w.lst);
+        hipLaunchKernelGGL(knn_lrank_kernel, grid1(nent), dim3(kKnnThreads), 0, st, N, MK, nent,
+                           (const int32_t*)w.slot, (const int32_t*)w.off, (const int32_t*)w.lst,
+                           w.ent);
+      }
+      // walk order: the tokens in bucket order
+      const KnnBuckets bg = knn_buckets(N, G);
+      const int64_t nbk = (int64_t)B * bg.nb;
+      hipLaunchKernelGGL(knn_zero_kernel, grid1(nbk), dim3(kKnnThreads), 0, st, nbk, w.bk.bcnt);
+      hipLaunchKernelGGL(knn_bucket_count_kernel, grid1(ntok), dim3(kKnnThreads), 0, st, coords,
+                         ntok, N, G, w.bk.bcnt, w.bk.brank);
+      hipLaunchKernelGGL(knn_scan_kernel, dim3(B), dim3(kScanThreads), 0, st, bg.nb,
+                         (const int32_t*)w.bk.bcnt, w.bk.bstart);
+      hipLaunchKernelGGL(knn_bucket_place_kernel, grid1(ntok), dim3(kKnnThreads), 0, st, coords,
+                         ntok, N, G, (const int32_t*)w.bk.bstart, (const int32_t*)w.bk.brank,
+                         (uint2*)nullptr, w.order);
+    }
     // waves per token group: one when tokens have few entries, more when many
     const int64_t ept = N > 0 ? MK / N : 0;   // entries per token, on average
     const int split = ept < 16 ? 1 : (ept < 48 ? 2 : 4);
@@ -987,8 +1121,8 @@ hipError_t bwd_t(int B, int N, int M, int Cf, int G, int K, float p, const float
     const int wgs = (groups * split + kKnnThreads / 64 - 1) / (kKnnThreads / 64);
     hipLaunchKernelGGL(knn_dfeat_kernel<T>, dim3((unsigned)(std::min(B, 8) * wgs)), dim3(kKnnThreads), 0, st,
                        B, N, M, Cf, K, lg, split, (const T*)dout, (const int32_t*)w.off,
-                       (const int32_t*)w.ent, (const float*)w.wgt,
-                       ordered ? (const int32_t*)w.order : nullptr, (T*)dfeat);
+                       (const int32_t*)w.ent, (const float*)w.wgt, (const int32_t*)w.order,
+                       (T*)dfeat);
   }
   const int64_t nwaves = (nq + qwv - 1) / qwv;   // one dp share per wave of the query kernel
   hipLaunchKernelGGL(knn_dp_kernel, dim3(1), dim3(1024), 0, st, nq > 0 ? nwaves : 0,
@@ -999,15 +1133,37 @@ hipError_t bwd_t(int B, int N, int M, int Cf, int G, int K, float p, const float
 }  // namespace
 
 hipError_t launch_knn_table(const float* coords, int B, int N, int G, int K, int32_t* table,
-                            hipStream_t st) {
+                            void* ws, hipStream_t st) {
   const int tiles_side = (G + 7) / 8;
   const int parts = (tiles_side * tiles_side + kTabTiles - 1) / kTabTiles;
+  if (N <= kTabMaxTokens) {
+    auto go = [&](auto kern) {
+      hipLaunchKernelGGL(kern, dim3(B, parts), dim3(kTabThreads), 0, st, coords, N, G, K, table);
+    };
+    if (K <= 4) go(knn_table_kernel<4>);
+    else if (K <= 8) go(knn_table_kernel<8>);
+    else go(knn_table_kernel<16>);
+    return hipGetLastError();
+  }
+  const KnnTableWorkspace w = knn_table_layout(ws, B, N);
+  const KnnBuckets bg = knn_buckets(N, G);
+  const int64_t ntok = (int64_t)B * N, nbk = (int64_t)B * bg.nb;
+  auto grid1 = [](int64_t n) { return dim3((unsigned)((n + kKnnThreads - 1) / kKnnThreads)); };
+  hipLaunchKernelGGL(knn_zero_kernel, grid1(nbk), dim3(kKnnThreads), 0, st, nbk, w.bcnt);
+  hipLaunchKernelGGL(knn_bucket_count_kernel, grid1(ntok), dim3(kKnnThreads), 0, st, coords, ntok,
+                     N, G, w.bcnt, w.brank);
+  hipLaunchKernelGGL(knn_scan_kernel, dim3(B), dim3(kScanThreads), 0, st, bg.nb,
+                     (const int32_t*)w.bcnt, w.bstart);
+  hipLaunchKernelGGL(knn_bucket_place_kernel, grid1(ntok), dim3(kKnnThreads), 0, st, coords, ntok,
+                     N, G, (const int32_t*)w.bstart, (const int32_t*)w.brank, w.tok,
+                     (int32_t*)nullptr);
   auto go = [&](auto kern) {
-    hipLaunchKernelGGL(kern, dim3(B, parts), dim3(kTabThreads), 0, st, coords, N, G, K, table);
+    hipLaunchKernelGGL(kern, dim3(B, parts), dim3(kTabThreads), 0, st, N, G, K,
+                       (const int32_t*)w.bstart, (const uint2*)w.tok, table);
   };
-  if (K <= 4) go(knn_table_kernel<4>);
-  else if (K <= 8) go(knn_table_kernel<8>);
-  else go(knn_table_kernel<16>);
+  if (K <= 4) go(knn_table_search_kernel<4>);
+  else if (K <= 8) go(knn_table_search_kernel<8>);
+  else go(knn_table_search_kernel<16>);
   return hipGetLastError();
 }
 

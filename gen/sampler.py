@@ -52,16 +52,39 @@ SAMPLER_CONFIGS = {
     # the worked example's decoder sampling at pre-training batch 32
     "knn_decoder": SamplerConfig("knn_decoder", 2002, 32, 64, 2048,
                                  ((2048, 128), (819, 256), (328, 512), (131, 768)), 8, 1.0, "bf16"),
+    # the same decoder on the 128 x 128 token grid of a 1024-pixel image
+    # (half the cells visible, the other half queried)
+    "knn_finetune": SamplerConfig("knn_finetune", 2003, 4, 128, 8192,
+                                  ((8192, 128), (3277, 256), (1311, 512), (524, 768)), 8, 1.0,
+                                  "bf16"),
+    # and on a 256 x 256 grid (2048-pixel images)
+    "knn_highres": SamplerConfig("knn_highres", 2004, 4, 256, 32768,
+                                 ((32768, 128), (13107, 256), (5243, 512), (2097, 768)), 8, 1.0,
+                                 "bf16"),
 }
 
 
 def _nearest_anchor_means(pts: np.ndarray, anchors: np.ndarray) -> np.ndarray:
+    """Mean position of the points whose nearest anchor (smallest squared
+    distance, then lower anchor index) is each anchor.  The points are
+    integer cells, so squared distances and sums are exact; a k-d tree gives
+    each point's nearest distance and every anchor within it, and the exact
+    integer distances pick the owner among them."""
+    from scipy.spatial import cKDTree
+
     apts = pts[anchors]
-    d2 = ((pts[:, None, :] - apts[None, :, :]) ** 2).sum(-1)
-    owner = np.argmin(d2, axis=1)           # first minimum = lower anchor index
+    tree = cKDTree(apts)
+    dmin, _ = tree.query(pts, k=1)
+    near = tree.query_ball_point(pts, dmin * (1 + 1e-9) + 1e-9)
+    owner = np.empty(pts.shape[0], dtype=np.int64)
+    for i, cand in enumerate(near):
+        c = np.asarray(cand, dtype=np.int64)
+        d2 = ((apts[c] - pts[i]) ** 2).sum(-1)
+        owner[i] = c[d2 == d2.min()].min()
+    cnt = np.bincount(owner, minlength=anchors.size).astype(np.float64)
     out = np.zeros((anchors.size, 2))
-    for a in range(anchors.size):
-        out[a] = pts[owner == a].mean(axis=0)
+    for a in range(2):
+        out[:, a] = np.bincount(owner, weights=pts[:, a], minlength=anchors.size) / cnt
     return out
 
 

@@ -320,17 +320,25 @@ ca_status cluster_attn_bwd_varlen(int dt, int T, int Ct, int H, int D, int cs, i
  * 16-byte aligned (C is a multiple of 8).
  * ------------------------------------------------------------------------ */
 
+/* Workspace bytes needed by cluster_attn_knn_table (0 for images of at most
+ * 4096 tokens, and for invalid sizes). */
+size_t cluster_attn_knn_table_workspace(int B, int N, int grid_side);
+
 /*
  * Table: table[b, i, j, 0..K-1] = the K tokens of image b whose fixed-point
  * coordinates (q = clamp(floor((c + 0.5) * 2^(16 - ceil(log2 G))), 0,
  * 65535) per axis) are nearest to the cell centre ((j + 1/2) s, (i + 1/2) s),
  * s = 2^(16 - ceil(log2 G)), by (squared distance, token index) ascending;
  * -1 pads rows when N < K.  Exact integer arithmetic: the unique table.
- *   coords  [B, N, 2] f32 device.   G: 1..64.   N: 0..4096.   K: 1..16.
+ *   coords  [B, N, 2] f32 device.   G: 1..2048.   N: 0..2^24 (B*N < 2^31).
+ *   K: 1..16.
  *   table   [B, G, G, K] int32 device out.
+ *   ws      device workspace of cluster_attn_knn_table_workspace bytes
+ *           (images above 4096 tokens are bucketed there; NULL when 0);
+ *           two calls that overlap in time must not share it.
  */
 ca_status cluster_attn_knn_table(const float* coords, int B, int N, int grid_side, int K,
-                           int32_t* table, void* hip_stream);
+                                 int32_t* table, void* ws, size_t ws_bytes, void* hip_stream);
 
 /*
  * Forward: for query m of image b at q = queries[b, m], the cell is
@@ -340,7 +348,8 @@ ca_status cluster_attn_knn_table(const float* coords, int B, int N, int grid_sid
  *   out[b, m, :] = sum_k w_k feats[b, t_k, :]   (fp32 accumulation, RNE to dt);
  * a query whose row has no valid slot gets 0.
  *   dt     element type of feats and out.   C: channels, multiple of 8, <= 1024.
- *   p      finite real (one per level).     K: 1..16 (table's K).
+ *   p      finite real (one per level).     K: 1..16 (table's K).   G: 1..2048.
+ *   N, M   up to 2^24 each (B*M*K < 2^31).
  *   feats  [B, N, C] dt.   table [B, G, G, K] int32 (any contents in [-1, N)).
  *   out    [B, M, C] dt out.
  */

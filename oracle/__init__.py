@@ -33,6 +33,7 @@ from .cluster_attention import (  # noqa: F401
 )
 from .knn_sampler import (  # noqa: F401
     knn_table,
+    knn_table_cells,
     query_cells,
     knn_weights,
     knn_sample_fwd,

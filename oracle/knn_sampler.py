@@ -55,6 +55,7 @@ from .cluster_attention import quantize, grid_bits
 
 __all__ = [
     "knn_table",
+    "knn_table_cells",
     "query_cells",
     "knn_weights",
     "knn_sample_fwd",
@@ -86,6 +87,42 @@ def knn_table(coords: np.ndarray, grid_side: int, K: int) -> np.ndarray:
             order = np.lexsort((idx, d2))              # by d2, then index
             table[i, j, :take] = order[:take]
     return table
+
+
+def knn_table_cells(coords: np.ndarray, grid_side: int, K: int, rows: np.ndarray,
+                    cols: np.ndarray, chunk: int = 256) -> np.ndarray:
+    """Readings K1-K2 for the listed cells only (row ``rows[c]``, column
+    ``cols[c]``) of one image: [n, K] int64, equal to
+    ``knn_table(coords, G, K)[rows, cols]``.
+
+    For grids too large to rank every cell: each cell's tokens are ranked by
+    the single integer d2 * 2^25 + index (d2 < 2^33 and index < 2^25, so it
+    orders exactly as (d2, index)), the K smallest picked by a partial sort
+    and then sorted."""
+    G = grid_side
+    rows = np.asarray(rows, dtype=np.int64).reshape(-1)
+    cols = np.asarray(cols, dtype=np.int64).reshape(-1)
+    N = coords.shape[0]
+    if N >= 2 ** 25:
+        raise ValueError("token index must fit 25 bits")
+    out = np.full((rows.size, K), -1, dtype=np.int64)
+    if N == 0 or rows.size == 0:
+        return out
+    qx, qy = quantize(coords, G)
+    s = 2 ** (16 - grid_bits(G))
+    idx = np.arange(N, dtype=np.int64)
+    take = min(K, N)
+    for c0 in range(0, rows.size, chunk):
+        cy = ((2 * rows[c0:c0 + chunk] + 1) * s // 2)[:, None]
+        cx = ((2 * cols[c0:c0 + chunk] + 1) * s // 2)[:, None]
+        key = ((qx[None, :] - cx) ** 2 + (qy[None, :] - cy) ** 2) * (2 ** 25) + idx[None, :]
+        if take < N:
+            part = np.partition(key, take - 1, axis=1)[:, :take]
+        else:
+            part = key
+        part = np.sort(part, axis=1)[:, :take]
+        out[c0:c0 + chunk, :take] = part % (2 ** 25)
+    return out
 
 
 def query_cells(queries: np.ndarray, grid_side: int) -> tuple[np.ndarray, np.ndarray]:

@@ -223,14 +223,22 @@ def knn_fwd(lib, dt=1, B=2, N=100, M=50, C=128, G=16, K=8, p=1.0, ptrs=None):
 def test_knn_validation(lib):
     # table build limits
     t = lib.cluster_attn_knn_table
-    assert t(P, 2, 100, 65, 8, 2 * P, None) == CA_ERR_UNSUPPORTED     # G > 64
-    assert t(P, 2, 5000, 64, 8, 2 * P, None) == CA_ERR_UNSUPPORTED    # N > 4096
-    assert t(P, 2, 100, 64, 17, 2 * P, None) == CA_ERR_UNSUPPORTED    # K > 16
-    assert t(P, 2, 100, 0, 8, 2 * P, None) == CA_ERR_UNSUPPORTED
-    assert t(None, 2, 100, 64, 8, 2 * P, None) == CA_ERR_NULL
-    assert t(P, -1, 100, 64, 8, 2 * P, None) == CA_ERR_SHAPE
-    assert t(None, 0, 100, 64, 8, None, None) == CA_OK                # empty batch
-    assert t(P, 2, 100, 16, 8, P + 8, None) == CA_ERR_ALIAS           # table over coords
+    assert t(P, 2, 100, 2049, 8, 2 * P, None, 0, None) == CA_ERR_UNSUPPORTED   # G > 2048
+    assert t(P, 2, (1 << 24) + 1, 64, 8, 2 * P, None, 0, None) == CA_ERR_SHAPE
+    assert t(P, 2, 100, 64, 17, 2 * P, None, 0, None) == CA_ERR_UNSUPPORTED    # K > 16
+    assert t(P, 2, 100, 0, 8, 2 * P, None, 0, None) == CA_ERR_UNSUPPORTED
+    assert t(None, 2, 100, 64, 8, 2 * P, None, 0, None) == CA_ERR_NULL
+    assert t(P, -1, 100, 64, 8, 2 * P, None, 0, None) == CA_ERR_SHAPE
+    assert t(None, 0, 100, 64, 8, None, None, 0, None) == CA_OK                # empty batch
+    assert t(P, 2, 100, 16, 8, P + 8, None, 0, None) == CA_ERR_ALIAS           # table over coords
+    # images above 4096 tokens are bucketed in a workspace
+    assert lib.cluster_attn_knn_table_workspace(2, 4096, 64) == 0
+    need = lib.cluster_attn_knn_table_workspace(2, 32768, 256)
+    assert need >= 2 * 32768 * 12
+    assert lib.cluster_attn_knn_table_workspace(2, 32768, 4096) == 0         # invalid G
+    assert t(P, 2, 32768, 256, 8, 2 * P, None, need, None) == CA_ERR_NULL
+    assert t(P, 2, 32768, 256, 8, 2 * P, 8 * P, need - 1, None) == CA_ERR_WORKSPACE
+    assert t(P, 2, 32768, 256, 8, 2 * P, P + 64, need, None) == CA_ERR_ALIAS  # ws over coords
     # sampler
     assert knn_fwd(lib, dt=5) == CA_ERR_UNSUPPORTED
     assert knn_fwd(lib, C=12) == CA_ERR_UNSUPPORTED

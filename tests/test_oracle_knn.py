@@ -31,6 +31,31 @@ def test_table_hand_worked_ties():
     assert t3[0, 0].tolist() == [0, 1, 2, -1, -1]
 
 
+def test_table_cells_hand_worked_and_padding():
+    """The cell-restricted ranking on the hand-worked example above, in a
+    shuffled cell order, and with more slots than tokens."""
+    pts = np.asarray([[1, 0], [0, 1], [2, 2]], dtype=np.float32)
+    rows = np.array([2, 0, 3, 1, 2, 0])
+    cols = np.array([2, 0, 3, 1, 0, 2])
+    got = O.knn_table_cells(pts, 4, 2, rows, cols)
+    assert got.tolist() == [[2, 0], [0, 1], [2, 0], [0, 1], [1, 2], [0, 2]]
+    assert O.knn_table_cells(pts, 4, 5, [0], [0]).tolist() == [[0, 1, 2, -1, -1]]
+    assert O.knn_table_cells(np.zeros((0, 2), np.float32), 4, 3, [1], [2]).tolist() == [[-1] * 3]
+
+
+@pytest.mark.parametrize("G,N,K,chunk", [(16, 150, 6, 7), (32, 600, 8, 256), (8, 5, 8, 3)])
+def test_table_cells_match_full_table(G, N, K, chunk):
+    """Every cell, in chunks that do not divide the cell count, against the
+    per-cell lexicographic ranking (repeated coordinates give ties)."""
+    rng = np.random.default_rng(G + N)
+    pts = rng.uniform(-0.5, G - 0.5, size=(N, 2)).astype(np.float32)
+    pts[N // 2:N // 2 + N // 5] = pts[:N // 5]
+    full = O.knn_table(pts, G, K)
+    ii, jj = np.meshgrid(np.arange(G), np.arange(G), indexing="ij")
+    got = O.knn_table_cells(pts, G, K, ii.reshape(-1), jj.reshape(-1), chunk=chunk)
+    np.testing.assert_array_equal(got, full.reshape(G * G, K))
+
+
 def test_query_cells_closed_forms():
     q = np.array([[0.49, 0.5], [-3.0, 100.0], [2.5, 1.4999], [3.49, -0.5]], dtype=np.float32)
     i, j = O.query_cells(q, 4)
