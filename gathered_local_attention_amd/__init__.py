@@ -22,7 +22,7 @@ knn_table(coords, grid_side, K, workspace=None) -> table
 knn_sample_fwd(feats, coords, queries, table, p) -> out
 knn_sample_bwd(feats, coords, queries, table, p, dout) -> (dfeats, dq, dp)
 knn_sample(feats, coords, queries, table, p) -> out   (autograd: feats, queries)
-merge_plan(coords, scores, k, grid_side) -> (anchors, assign, members, offsets)
+merge_plan(coords, scores, k, grid_side, workspace=None) -> (anchors, assign, members, offsets)
 merge_fwd(feats, coords, scores, members, offsets, k) -> (out_feats, out_coords)
 merge_bwd(feats, coords, scores, members, offsets, dout_feats, dout_coords)
     -> (dfeats, dcoords, dscores)
@@ -59,6 +59,7 @@ __all__ = [
     "knn_sample",
     "knn_bwd_workspace_bytes",
     "merge_plan",
+    "merge_plan_workspace_bytes",
     "merge_fwd",
     "merge_bwd",
     "ClusterAttnError",
@@ -598,14 +599,26 @@ def knn_sample(feats, coords, queries, table, p: float):
 # Adaptive token merging
 # ---------------------------------------------------------------------------
 
-def merge_plan(coords: torch.Tensor, scores: torch.Tensor, k: int, grid_side: int):
+def merge_plan_workspace_bytes(B: int, N: int, k: int) -> int:
+    return int(_lib.load().cluster_attn_merge_plan_workspace(B, N, k))
+
+
+def merge_plan(coords: torch.Tensor, scores: torch.Tensor, k: int, grid_side: int,
+               workspace: torch.Tensor | None = None):
     """Anchors [B, k], assignment [B, N], member lists [B, N] and group
-    offsets [B, k + 1] (all int32)."""
+    offsets [B, k + 1] (all int32).  Images above 4096 tokens need a
+    workspace (allocated here when not given)."""
     lib = _lib.load()
-    B, N, two = coords.shape
-    if two != 2 or scores.shape != (B, N):
+    if coords.dim() != 3 or coords.shape[2] != 2 or scores.shape != coords.shape[:2]:
         raise ValueError("coords [B, N, 2] and scores [B, N] expected")
+    B, N, _ = coords.shape
     dev = coords.device
+    need = lib.cluster_attn_merge_plan_workspace(B, N, int(k))
+    ws_ptr, ws_n = 0, 0
+    if need:
+        if workspace is None:
+            workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+        ws_ptr, ws_n = workspace.data_ptr(), workspace.numel()
     anchors = torch.empty((B, k), dtype=torch.int32, device=dev)
     assign = torch.empty((B, N), dtype=torch.int32, device=dev)
     members = torch.empty((B, N), dtype=torch.int32, device=dev)
@@ -613,7 +626,7 @@ def merge_plan(coords: torch.Tensor, scores: torch.Tensor, k: int, grid_side: in
     _check(lib.cluster_attn_merge_plan(
         _dev(coords, "coords", torch.float32), _dev(scores, "scores", torch.float32), B, N, int(k),
         int(grid_side), anchors.data_ptr(), assign.data_ptr(), members.data_ptr(),
-        offsets.data_ptr(), _stream(coords)), "cluster_attn_merge_plan")
+        offsets.data_ptr(), ws_ptr, ws_n, _stream(coords)), "cluster_attn_merge_plan")
     return anchors, assign, members, offsets
 
 

@@ -67,8 +67,9 @@ SIGNATURES = {
     "cluster_attn_knn_sample_bwd": (
         _c_int, [_c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _f,
                  _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _c_size, _vp]),
+    "cluster_attn_merge_plan_workspace": (_c_size, [_c_int, _c_int, _c_int]),
     "cluster_attn_merge_plan": (
-        _c_int, [_vp, _vp, _c_int, _c_int, _c_int, _c_int, _vp, _vp, _vp, _vp, _vp]),
+        _c_int, [_vp, _vp, _c_int, _c_int, _c_int, _c_int, _vp, _vp, _vp, _vp, _vp, _c_size, _vp]),
     "cluster_attn_merge_fwd": (
         _c_int, [_c_int, _c_int, _c_int, _c_int, _c_int, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
     "cluster_attn_merge_bwd": (

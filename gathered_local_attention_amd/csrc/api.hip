@@ -97,7 +97,8 @@ ca_status check_merge_shape(int dt, int B, int N, int k, int C) {
   if (dt != CA_F32 && dt != CA_BF16 && dt != CA_F16)
     return fail(CA_ERR_UNSUPPORTED, "dtype %d is not one of CA_F32, CA_BF16, CA_F16", dt);
   if (B < 0 || N < 0 || k < 0) return fail(CA_ERR_SHAPE, "bad sizes B=%d N=%d k=%d", B, N, k);
-  if (N > 4096) return fail(CA_ERR_UNSUPPORTED, "N=%d: merging supports up to 4096 tokens", N);
+  if (N > (1 << 24)) return fail(CA_ERR_SHAPE, "N=%d above 2^24", N);
+  if ((int64_t)B * N > (int64_t(1) << 31) - 1) return fail(CA_ERR_SHAPE, "B*N above 2^31 - 1");
   if (k > N || (N > 0 && k < 1)) return fail(CA_ERR_SHAPE, "k=%d must be in [1, N=%d]", k, N);
   if (C < 8 || C > 1024 || C % 8 != 0)
     return fail(CA_ERR_UNSUPPORTED, "channels %d: must be a multiple of 8 in [8, 1024]", C);
@@ -616,23 +617,33 @@ ca_status cluster_attn_knn_sample_bwd(int dt, int B, int N, int M, int C, int gr
                     "knn bwd launch");
 }
 
+size_t cluster_attn_merge_plan_workspace(int B, int N, int k) {
+  if (B < 0 || N < 0 || N > (1 << 24) || k < 0 || k > N) return 0;
+  return ca::merge_layout(nullptr, B, N, k).bytes;
+}
+
 ca_status cluster_attn_merge_plan(const float* coords, const float* scores, int B, int N, int k,
-                            int grid_side, int32_t* anchors, int32_t* assign, int32_t* members,
-                            int32_t* offsets, void* hip_stream) {
+                                  int grid_side, int32_t* anchors, int32_t* assign,
+                                  int32_t* members, int32_t* offsets, void* ws, size_t ws_bytes,
+                                  void* hip_stream) {
   if (B < 0 || N < 0 || k < 0) return fail(CA_ERR_SHAPE, "bad sizes B=%d N=%d k=%d", B, N, k);
-  if (N > 4096) return fail(CA_ERR_UNSUPPORTED, "N=%d: merging supports up to 4096 tokens", N);
+  if (N > (1 << 24)) return fail(CA_ERR_SHAPE, "N=%d above 2^24", N);
+  if ((int64_t)B * N > (int64_t(1) << 31) - 1) return fail(CA_ERR_SHAPE, "B*N above 2^31 - 1");
   if (k > N || (N > 0 && k < 1)) return fail(CA_ERR_SHAPE, "k=%d must be in [1, N=%d]", k, N);
   if (grid_side < 1 || grid_side > 65536)
     return fail(CA_ERR_SHAPE, "grid_side=%d outside [1, 65536]", grid_side);
   if (B == 0 || N == 0) return ok();
   if (!coords || !scores || !anchors || !assign || !members || !offsets)
     return fail(CA_ERR_NULL, "NULL tensor pointer");
+  const size_t need = ca::merge_layout(nullptr, B, N, k).bytes;
+  if (need && !ws) return fail(CA_ERR_NULL, "NULL workspace (%zu bytes needed)", need);
+  if (ws_bytes < need) return fail(CA_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
   Range outs[] = {{anchors, (size_t)B * k * 4}, {assign, (size_t)B * N * 4},
-                  {members, (size_t)B * N * 4}, {offsets, (size_t)B * (k + 1) * 4}};
+                  {members, (size_t)B * N * 4}, {offsets, (size_t)B * (k + 1) * 4}, {ws, need}};
   Range ins[] = {{coords, (size_t)B * N * 8}, {scores, (size_t)B * N * 4}};
-  if (ca_status s = check_alias(outs, 4, ins, 2)) return s;
+  if (ca_status s = check_alias(outs, 5, ins, 2)) return s;
   return hip_status(ca::launch_merge_plan(coords, scores, B, N, k, grid_side, anchors, assign,
-                                          members, offsets, (hipStream_t)hip_stream),
+                                          members, offsets, ws, (hipStream_t)hip_stream),
                     "merge plan launch");
 }
 

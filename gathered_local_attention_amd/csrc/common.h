@@ -285,6 +285,61 @@ static inline KnnWorkspace knn_layout(void* base, int64_t B, int64_t N, int64_t 
   return w;
 }
 
+// ---- workspace layout of the merge plan (images above kMergeSmallTokens) ---
+constexpr int kMergeSmallTokens = 4096;   // images up to this many tokens are planned in LDS
+
+// anchor buckets of the large-image plan: squares of 2^bsh fixed-point
+// units, Pb = 2^pb to a side, about two anchors per bucket
+struct MergeBuckets {
+  int pb, bsh, Pb, nb;
+};
+__host__ __device__ inline MergeBuckets merge_buckets(int k) {
+  MergeBuckets g;
+  g.pb = 0;
+  const int half = (k > 1 ? k : 1) / 2;
+  while (g.pb < 15 && (int64_t(1) << (2 * g.pb + 2)) <= half) ++g.pb;
+  g.bsh = 16 - g.pb;
+  g.Pb = 1 << g.pb;
+  g.nb = g.Pb * g.Pb;
+  return g;
+}
+
+struct MergeWorkspace {
+  uint32_t* sk;     // [B, N]        order-preserving keys of the scores
+  int32_t* apos;    // [B, N]        anchor position of every token, -1 if none
+  int32_t* abcnt;   // [B, nb]       anchors per bucket
+  int32_t* abstart; // [B, nb + 1]   bucket starts
+  int32_t* abrank;  // [B, k]        rank of each anchor in its bucket
+  uint2* abk;       // [B, k]        (qx | qy << 16, position) in bucket order
+  int32_t* gcnt;    // [B, k]        group sizes, then placement cursors
+  int32_t* glst;    // [B, N]        members in placement order
+  size_t bytes;
+};
+
+static inline MergeWorkspace merge_layout(void* base, int64_t B, int64_t N, int64_t k) {
+  MergeWorkspace w;
+  size_t p = 0;
+  char* b = (char*)base;
+  auto take = [&](size_t n) {
+    size_t at = p;
+    p = align_up(p + n, 256);
+    return b ? (void*)(b + at) : (void*)nullptr;
+  };
+  const bool large = N > kMergeSmallTokens;
+  const int64_t nb = large ? merge_buckets((int)k).nb : 0;
+  const int64_t n = large ? N : 0, kk = large ? k : 0;
+  w.sk = (uint32_t*)take((size_t)(B * n) * 4);
+  w.apos = (int32_t*)take((size_t)(B * n) * 4);
+  w.abcnt = (int32_t*)take((size_t)(B * nb) * 4);
+  w.abstart = (int32_t*)take(large ? (size_t)(B * (nb + 1)) * 4 : 0);
+  w.abrank = (int32_t*)take((size_t)(B * kk) * 4);
+  w.abk = (uint2*)take((size_t)(B * kk) * 8);
+  w.gcnt = (int32_t*)take((size_t)(B * kk) * 4);
+  w.glst = (int32_t*)take((size_t)(B * n) * 4);
+  w.bytes = p;
+  return w;
+}
+
 // ---- wave helpers (64-lane wavefronts) ------------------------------------
 __device__ __forceinline__ float wave_max(float x) {
 #pragma unroll
@@ -389,6 +444,12 @@ hipError_t launch_bwd_mfma(int pass, int dt, int B, int N, int C, int H, int nk,
                            const int32_t* key_idx, void* dq, void* dk, void* dv,
                            const BwdWorkspace& w, hipStream_t st);
 
+// Integer helpers (scan.hip): x[0..n) = 0; per segment s of n counts,
+// off[s, 0..n] = exclusive prefix sums and the total (off has n + 1 entries
+// per segment)
+void launch_zero_i32(int64_t n, int32_t* x, hipStream_t st);
+void launch_segment_scan(int segments, int n, const int32_t* cnt, int32_t* off, hipStream_t st);
+
 // KNN-cache point sampler (knn_sampler.hip)
 hipError_t launch_knn_table(const float* coords, int B, int N, int G, int K, int32_t* table, void* ws,
                             hipStream_t st);
@@ -403,7 +464,7 @@ hipError_t launch_knn_bwd(int dt, int B, int N, int M, int Cf, int G, int K, flo
 // Adaptive token merging (token_merge.hip)
 hipError_t launch_merge_plan(const float* coords, const float* scores, int B, int N, int k, int G,
                              int32_t* anchors, int32_t* assign, int32_t* members,
-                             int32_t* offsets, hipStream_t st);
+                             int32_t* offsets, void* ws, hipStream_t st);
 hipError_t launch_merge_fwd(int dt, int B, int N, int k, int Cf, const void* feats,
                             const float* coords, const float* scores, const int32_t* members,
                             const int32_t* offsets, void* out_f, float* out_x, hipStream_t st);

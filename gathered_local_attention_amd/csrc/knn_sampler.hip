@@ -28,6 +28,9 @@
 //                         ring, every lane testing every token of the window,
 //                         and stops once each lane's K-th best is strictly
 //                         closer than any token outside the window can be.
+//   knn_bucket_count/place, knn_table_search_kernel  the same for images
+//                         above 4096 tokens, with the buckets in global
+//                         memory (bucketed once per image).
 //   knn_fwd_kernel        a group of lanes per query, 16 bytes of the
 //                         feature row per lane: cell, slots, distances and
 //                         weights (computed redundantly by the group's lanes),
@@ -40,7 +43,9 @@
 //                         query * K + slot) by a stable counting sort over
 //                         partitions of the entries: each token's segment is
 //                         in entry order, so the feature gradient is summed
-//                         in a fixed order.
+//                         in a fixed order.  Images above 4096 tokens:
+//                         knn_lplace/lrank (cursor placement, then each
+//                         entry's rank in its segment: the same lists).
 //   knn_dfeat_kernel      a lane group per token: dF = sum over its entries
 //                         of w * dO (gathered rows), written once (0 for
 //                         tokens no query reaches).
@@ -683,51 +688,6 @@ knn_pcount_kernel(int N, int64_t MK, int P, const int32_t* __restrict__ ent_slot
   for (int t = threadIdx.x; t < N; t += kKnnThreads) row[t] = c[t];
 }
 
-__global__ void __launch_bounds__(kKnnThreads)
-knn_zero_kernel(int64_t n, int32_t* __restrict__ x) {
-  const int64_t i = (int64_t)blockIdx.x * kKnnThreads + threadIdx.x;
-  if (i < n) x[i] = 0;
-}
-
-// per image: segment offsets of the token-major lists (counts staged through
-// LDS in chunks, one workgroup scan per chunk)
-constexpr int kScanThreads = 1024;
-constexpr int kScanChunk = 8192;
-__global__ void __launch_bounds__(kScanThreads)
-knn_scan_kernel(int N, const int32_t* __restrict__ cnt_all, int32_t* __restrict__ off_all) {
-  __shared__ int32_t v[kScanChunk];
-  __shared__ int tmp[17];
-  const int64_t b = blockIdx.x;
-  const int32_t* cnt = cnt_all + b * N;
-  int32_t* off = off_all + b * (N + 1);
-  constexpr int kPer = kScanChunk / kScanThreads;
-  int carry = 0;
-  for (int c0 = 0; c0 < N; c0 += kScanChunk) {
-    const int n = min(kScanChunk, N - c0);
-    for (int x = threadIdx.x; x < n; x += kScanThreads) v[x] = cnt[c0 + x];
-    __syncthreads();
-    const int r0 = threadIdx.x * kPer;
-    int run = 0;
-#pragma unroll
-    for (int r = 0; r < kPer; ++r) run += r0 + r < n ? v[r0 + r] : 0;
-    int tot;
-    int acc = carry + block_exclusive_scan(run, tmp, kScanThreads, &tot);
-#pragma unroll
-    for (int r = 0; r < kPer; ++r) {
-      if (r0 + r < n) {
-        const int c = v[r0 + r];
-        v[r0 + r] = acc;
-        acc += c;
-      }
-    }
-    __syncthreads();
-    for (int x = threadIdx.x; x < n; x += kScanThreads) off[c0 + x] = v[x];
-    carry += tot;
-    __syncthreads();
-  }
-  if (threadIdx.x == 0) off[N] = carry;
-}
-
 // Token-major entry lists, in entry order (entry = query * K + slot), by a
 // stable counting sort.  The entries of an image are cut into partitions of
 // kPart consecutive entries: (1) per partition and token, the count of its
@@ -735,7 +695,7 @@ knn_scan_kernel(int N, const int32_t* __restrict__ cnt_all, int32_t* __restrict_
 // depend on their order), or per partition in LDS (knn_pcount_kernel) when
 // the image fits; (2) per token, the counts turned into exclusive
 // prefixes over the partitions, and the token's total; (3) the totals
-// scanned into segment starts (knn_scan_kernel); (4) per partition, every
+// scanned into segment starts (launch_segment_scan); (4) per partition, every
 // entry placed at segment start + the partition's prefix + the number of
 // earlier entries of the same token in the partition.
 
@@ -790,7 +750,7 @@ knn_pplace_kernel(int N, int64_t MK, int P, const int32_t* __restrict__ ent_slot
 }
 
 // Large images: token-major entry lists by per-token cursors.  (1) The
-// query-major kernel counts the entries per token; (2) knn_scan_kernel
+// query-major kernel counts the entries per token; (2) launch_segment_scan
 // turns the counts into segment starts; (3) every entry takes a place in
 // its token's segment of lst from an integer atomic on the token's cursor
 // (in no fixed order); (4) every entry is moved to segment start + its rank
@@ -1070,7 +1030,7 @@ hipError_t bwd_t(int B, int N, int M, int Cf, int G, int K, float p, const float
   };
   // empty sizes launch nothing but what writes outputs (dF, dp)
   if (large && ntok > 0)
-    hipLaunchKernelGGL(knn_zero_kernel, grid1(ntok), dim3(kKnnThreads), 0, st, ntok, w.cnt);
+    launch_zero_i32(ntok, w.cnt, st);
   if (nq > 0) {
     if (K <= 4) go(knn_bwd_query_kernel<T, 4>);
     else if (K <= 8) go(knn_bwd_query_kernel<T, 8>);
@@ -1083,8 +1043,7 @@ hipError_t bwd_t(int B, int N, int M, int Cf, int G, int K, float p, const float
                            MK, P, (const int32_t*)w.slot, w.pcnt);
       hipLaunchKernelGGL(knn_pprefix_kernel, grid1(ntok), dim3(kKnnThreads), 0, st, N, P, ntok,
                          w.pcnt, w.cnt);
-      hipLaunchKernelGGL(knn_scan_kernel, dim3(B), dim3(kScanThreads), 0, st, N,
-                         (const int32_t*)w.cnt, w.off);
+      launch_segment_scan(B, N, w.cnt, w.off, st);
       if (nparts > 0)
         hipLaunchKernelGGL(knn_pplace_kernel, dim3((unsigned)nparts), dim3(kKnnThreads), 0, st, N,
                            MK, P, (const int32_t*)w.slot, (const int32_t*)w.off,
@@ -1092,9 +1051,8 @@ hipError_t bwd_t(int B, int N, int M, int Cf, int G, int K, float p, const float
       hipLaunchKernelGGL(knn_order_kernel, dim3(B), dim3(kTabThreads), 0, st, coords, N, G,
                          w.order);
     } else {
-      hipLaunchKernelGGL(knn_scan_kernel, dim3(B), dim3(kScanThreads), 0, st, N,
-                         (const int32_t*)w.cnt, w.off);
-      hipLaunchKernelGGL(knn_zero_kernel, grid1(ntok), dim3(kKnnThreads), 0, st, ntok, w.cnt);
+      launch_segment_scan(B, N, w.cnt, w.off, st);
+      launch_zero_i32(ntok, w.cnt, st);
       if (nent > 0) {
         hipLaunchKernelGGL(knn_lplace_kernel, grid1(nent), dim3(kKnnThreads), 0, st, N, MK, nent,
                            (const int32_t*)w.slot, (const int32_t*)w.off, w.cnt, w.lst);
@@ -1105,11 +1063,10 @@ hipError_t bwd_t(int B, int N, int M, int Cf, int G, int K, float p, const float
       // walk order: the tokens in bucket order
       const KnnBuckets bg = knn_buckets(N, G);
       const int64_t nbk = (int64_t)B * bg.nb;
-      hipLaunchKernelGGL(knn_zero_kernel, grid1(nbk), dim3(kKnnThreads), 0, st, nbk, w.bk.bcnt);
+      launch_zero_i32(nbk, w.bk.bcnt, st);
       hipLaunchKernelGGL(knn_bucket_count_kernel, grid1(ntok), dim3(kKnnThreads), 0, st, coords,
                          ntok, N, G, w.bk.bcnt, w.bk.brank);
-      hipLaunchKernelGGL(knn_scan_kernel, dim3(B), dim3(kScanThreads), 0, st, bg.nb,
-                         (const int32_t*)w.bk.bcnt, w.bk.bstart);
+      launch_segment_scan(B, bg.nb, w.bk.bcnt, w.bk.bstart, st);
       hipLaunchKernelGGL(knn_bucket_place_kernel, grid1(ntok), dim3(kKnnThreads), 0, st, coords,
                          ntok, N, G, (const int32_t*)w.bk.bstart, (const int32_t*)w.bk.brank,
                          (uint2*)nullptr, w.order);
@@ -1149,11 +1106,10 @@ hipError_t launch_knn_table(const float* coords, int B, int N, int G, int K, int
   const KnnBuckets bg = knn_buckets(N, G);
   const int64_t ntok = (int64_t)B * N, nbk = (int64_t)B * bg.nb;
   auto grid1 = [](int64_t n) { return dim3((unsigned)((n + kKnnThreads - 1) / kKnnThreads)); };
-  hipLaunchKernelGGL(knn_zero_kernel, grid1(nbk), dim3(kKnnThreads), 0, st, nbk, w.bcnt);
+  launch_zero_i32(nbk, w.bcnt, st);
   hipLaunchKernelGGL(knn_bucket_count_kernel, grid1(ntok), dim3(kKnnThreads), 0, st, coords, ntok,
                      N, G, w.bcnt, w.brank);
-  hipLaunchKernelGGL(knn_scan_kernel, dim3(B), dim3(kScanThreads), 0, st, bg.nb,
-                     (const int32_t*)w.bcnt, w.bstart);
+  launch_segment_scan(B, bg.nb, w.bcnt, w.bstart, st);
   hipLaunchKernelGGL(knn_bucket_place_kernel, grid1(ntok), dim3(kKnnThreads), 0, st, coords, ntok,
                      N, G, (const int32_t*)w.bstart, (const int32_t*)w.brank, w.tok,
                      (int32_t*)nullptr);

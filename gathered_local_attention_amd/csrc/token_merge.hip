@@ -27,6 +27,8 @@
 //   merge_members_kernel one workgroup per image: the groups' member lists
 //                      by a counting sort on the anchor, each group then
 //                      sorted by token index.
+//   merge_select/abucket/assign_wide/g* kernels  the same plan for images
+//                      above 4096 tokens, in global memory (a workspace).
 //   merge_fwd_kernel   a lane group per anchor (16 bytes of the row per
 //                      lane): the group's softmax, then the weighted sums.
 //   merge_bwd_kernel   the same groups: g_i = <dF'_a, F_i> + <dX'_a, X_i>
@@ -42,7 +44,7 @@ namespace ca {
 namespace {
 
 constexpr int kPlanT = 1024;
-constexpr int kMaxTok = 4096;
+constexpr int kMaxTok = kMergeSmallTokens;
 constexpr int kMergeThreads = 256;
 constexpr int kRingLanes = 4;   // lanes per token in the nearest-anchor search
 
@@ -99,33 +101,18 @@ __device__ __forceinline__ uint32_t score_key(float x) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-__global__ void __launch_bounds__(kPlanT)
-merge_assign_kernel(const float* __restrict__ coords, const float* __restrict__ scores, int N,
-                    int k, int G, int S, int32_t* __restrict__ anchors,
-                    int32_t* __restrict__ assign) {
-  __shared__ uint32_t sk[kMaxTok];                    // score keys
-  __shared__ uint32_t qc[kMaxTok];                    // token fixed-point (qx | qy << 16)
-  __shared__ int32_t apos[kMaxTok];                   // token -> anchor position, or -1
-  __shared__ uint2 abk[kMaxTok];                      // anchors in bucket order: (qc, position)
-  __shared__ int32_t bstart[kMaxTok];                 // bucket starts (<= 4096 buckets)
-  __shared__ int hist[256];
-  __shared__ uint32_t sel[2];                         // selected prefix, still wanted
-  __shared__ int tmp[17];
-  const int b = blockIdx.x / S, slice = blockIdx.x % S, tid = threadIdx.x;
-  const int bits = [&] { int v = 0; while ((1 << v) < G) ++v; return v; }();
-  const double step = (double)(1u << (16 - bits));
-  const float* s = scores + (int64_t)b * N;
-  const float2* xy = reinterpret_cast<const float2*>(coords) + (int64_t)b * N;
-  for (int i = tid; i < N; i += kPlanT) {
-    sk[i] = score_key(s[i]);
-    const float2 c = xy[i];
-    qc[i] = quantize_axis(c.x, step) | (quantize_axis(c.y, step) << 16);
-  }
+// Radix select of the k-th largest of the keys sk[0..N) by 8-bit digits
+// from the top, called by every thread of a kPlanT workgroup (sk in LDS or
+// in global memory, written before the call and visible to the workgroup).
+// On return sel[0] is the k-th largest key and sel[1] the number of keys
+// equal to it that belong to the k largest (the first ones in token order).
+__device__ __forceinline__ void radix_select(const uint32_t* sk, int N, int k, int* hist,
+                                             uint32_t* sel) {
+  const int tid = threadIdx.x;
   if (tid == 0) {
     sel[0] = 0u;
     sel[1] = (uint32_t)k;
   }
-  // 1. radix select of the k-th largest key
   for (int dg = 3; dg >= 0; --dg) {
     if (tid < 256) hist[tid] = 0;
     __syncthreads();
@@ -161,6 +148,32 @@ merge_assign_kernel(const float* __restrict__ coords, const float* __restrict__ 
     }
     __syncthreads();
   }
+}
+
+__global__ void __launch_bounds__(kPlanT)
+merge_assign_kernel(const float* __restrict__ coords, const float* __restrict__ scores, int N,
+                    int k, int G, int S, int32_t* __restrict__ anchors,
+                    int32_t* __restrict__ assign) {
+  __shared__ uint32_t sk[kMaxTok];                    // score keys
+  __shared__ uint32_t qc[kMaxTok];                    // token fixed-point (qx | qy << 16)
+  __shared__ int32_t apos[kMaxTok];                   // token -> anchor position, or -1
+  __shared__ uint2 abk[kMaxTok];                      // anchors in bucket order: (qc, position)
+  __shared__ int32_t bstart[kMaxTok];                 // bucket starts (<= 4096 buckets)
+  __shared__ int hist[256];
+  __shared__ uint32_t sel[2];                         // selected prefix, still wanted
+  __shared__ int tmp[17];
+  const int b = blockIdx.x / S, slice = blockIdx.x % S, tid = threadIdx.x;
+  const int bits = [&] { int v = 0; while ((1 << v) < G) ++v; return v; }();
+  const double step = (double)(1u << (16 - bits));
+  const float* s = scores + (int64_t)b * N;
+  const float2* xy = reinterpret_cast<const float2*>(coords) + (int64_t)b * N;
+  for (int i = tid; i < N; i += kPlanT) {
+    sk[i] = score_key(s[i]);
+    const float2 c = xy[i];
+    qc[i] = quantize_axis(c.x, step) | (quantize_axis(c.y, step) << 16);
+  }
+  // 1. radix select of the k-th largest key
+  radix_select(sk, N, k, hist, sel);
   const uint32_t kth = sel[0], n_eq = sel[1];   // take n_eq of the keys equal to kth
   // 2. flags in token order (thread t owns tokens 4t .. 4t+3), then positions
   //    (one scan of the packed counts of keys above and equal to the k-th:
@@ -397,6 +410,211 @@ merge_members_kernel(int N, int k, const int32_t* __restrict__ assign,
   }
 }
 
+// ---------------------------------------------------------------------------
+// Plan of images above kMaxTok tokens, in global memory (workspace):
+//  1. merge_select_kernel, one workgroup per image: the score keys, their
+//     radix select, then anchor flags and positions chunk by chunk in token
+//     order (a workgroup scan per chunk, carried across chunks);
+//  2. the anchors counting-sorted into square buckets (merge_buckets);
+//  3. merge_assign_wide_kernel: kRingLanes lanes per token, the ring search
+//     of the small-image kernel over the global bucket arrays;
+//  4. member lists: group sizes (integer atomics), offsets by a scan, every
+//     token placed by its group's cursor (in no fixed order), then moved to
+//     group start + its rank by token index inside the group.
+// Keys (d2 << 24 | anchor position) are exact for k < 2^24.
+// ---------------------------------------------------------------------------
+constexpr int kWideKeyBits = 24;
+
+__global__ void __launch_bounds__(kPlanT)
+merge_select_kernel(const float* __restrict__ scores, int N, int k, uint32_t* __restrict__ sk_all,
+                    int32_t* __restrict__ apos_all, int32_t* __restrict__ anchors) {
+  __shared__ int hist[256];
+  __shared__ uint32_t sel[2];
+  __shared__ int tmp[17];
+  const int64_t b = blockIdx.x;
+  const int tid = threadIdx.x;
+  const float* s = scores + b * N;
+  uint32_t* sk = sk_all + b * N;
+  int32_t* apos = apos_all + b * N;
+  for (int i = tid; i < N; i += kPlanT) sk[i] = score_key(s[i]);
+  radix_select(sk, N, k, hist, sel);
+  const uint32_t kth = sel[0], n_eq = sel[1];
+  // chunks of kPlanT * R tokens, thread t owning R consecutive ones; the
+  // anchors before a token are the larger keys before it and the first
+  // n_eq equal keys in token order
+  constexpr int R = 4;
+  int carry_gt = 0, carry_eq = 0;
+  for (int c0 = 0; c0 < N; c0 += kPlanT * R) {
+    uint32_t kv[R];
+    int gt_local = 0, eq_local = 0;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const int i = c0 + tid * R + r;
+      kv[r] = i < N ? sk[i] : 0u;
+      gt_local += (i < N && kv[r] > kth) ? 1 : 0;
+      eq_local += (i < N && kv[r] == kth) ? 1 : 0;
+    }
+    int tot;
+    const int ex = block_exclusive_scan((gt_local << 16) | eq_local, tmp, kPlanT, &tot);
+    int eq_before = carry_eq + (ex & 0xFFFF);
+    int pos = carry_gt + (ex >> 16) + min(eq_before, (int)n_eq);
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const int i = c0 + tid * R + r;
+      if (i < N) {
+        bool an = false;
+        if (kv[r] > kth) an = true;
+        else if (kv[r] == kth) an = (uint32_t)(eq_before++) < n_eq;
+        apos[i] = an ? pos : -1;
+        if (an) anchors[b * k + pos] = i;
+        pos += an ? 1 : 0;
+      }
+    }
+    carry_gt += tot >> 16;
+    carry_eq += tot & 0xFFFF;
+    __syncthreads();   // tmp is reused by the next chunk's scan
+  }
+}
+
+__device__ __forceinline__ uint32_t fixed_point(const float2 c, double step) {
+  return quantize_axis(c.x, step) | (quantize_axis(c.y, step) << 16);
+}
+
+__global__ void __launch_bounds__(kMergeThreads)
+merge_abucket_count_kernel(const float* __restrict__ coords, int N, int k, int G, int64_t n_anc,
+                           const int32_t* __restrict__ anchors, int32_t* __restrict__ abcnt,
+                           int32_t* __restrict__ abrank) {
+  const int64_t x = (int64_t)blockIdx.x * kMergeThreads + threadIdx.x;
+  if (x >= n_anc) return;
+  const int64_t b = x / k;
+  const MergeBuckets mb = merge_buckets(k);
+  const double step = (double)(1u << (16 - knn_ceil_log2(G)));
+  const uint32_t q = fixed_point(reinterpret_cast<const float2*>(coords)[b * N + anchors[x]], step);
+  const int bk = (int)(((q >> 16) >> mb.bsh) * (uint32_t)mb.Pb + ((q & 0xFFFFu) >> mb.bsh));
+  abrank[x] = atomicAdd(&abcnt[b * mb.nb + bk], 1);
+}
+
+__global__ void __launch_bounds__(kMergeThreads)
+merge_abucket_place_kernel(const float* __restrict__ coords, int N, int k, int G, int64_t n_anc,
+                           const int32_t* __restrict__ anchors, const int32_t* __restrict__ abstart,
+                           const int32_t* __restrict__ abrank, uint2* __restrict__ abk) {
+  const int64_t x = (int64_t)blockIdx.x * kMergeThreads + threadIdx.x;
+  if (x >= n_anc) return;
+  const int64_t b = x / k;
+  const int pos = (int)(x - b * k);
+  const MergeBuckets mb = merge_buckets(k);
+  const double step = (double)(1u << (16 - knn_ceil_log2(G)));
+  const uint32_t q = fixed_point(reinterpret_cast<const float2*>(coords)[b * N + anchors[x]], step);
+  const int bk = (int)(((q >> 16) >> mb.bsh) * (uint32_t)mb.Pb + ((q & 0xFFFFu) >> mb.bsh));
+  abk[b * k + abstart[b * (mb.nb + 1) + bk] + abrank[x]] = make_uint2(q, (uint32_t)pos);
+}
+
+// kRingLanes lanes per token (an aligned group: its lanes enter and leave
+// every loop together, so the group's shuffles see active lanes only)
+__global__ void __launch_bounds__(kMergeThreads)
+merge_assign_wide_kernel(const float* __restrict__ coords, int N, int k, int G, int64_t n_tok,
+                         const int32_t* __restrict__ apos_all, const int32_t* __restrict__ abstart_all,
+                         const uint2* __restrict__ abk_all, int32_t* __restrict__ assign) {
+  const int64_t t = ((int64_t)blockIdx.x * kMergeThreads + threadIdx.x) / kRingLanes;
+  const int u = threadIdx.x % kRingLanes;
+  if (t >= n_tok) return;
+  const int64_t b = t / N;
+  int a = apos_all[t];
+  if (a < 0) {
+    const MergeBuckets mb = merge_buckets(k);
+    const int bsh = mb.bsh, Pb = mb.Pb;
+    const int32_t* abstart = abstart_all + b * (mb.nb + 1);
+    const uint2* abk = abk_all + b * k;
+    const double step = (double)(1u << (16 - knn_ceil_log2(G)));
+    const uint32_t q = fixed_point(reinterpret_cast<const float2*>(coords)[t], step);
+    const int64_t x = q & 0xFFFFu, y = q >> 16;
+    const int bx0 = (int)(x >> bsh), by0 = (int)(y >> bsh);
+    uint64_t best = ~0ull;
+    for (int Rg = 0; Rg < Pb; ++Rg) {
+      const int y0 = by0 - Rg, y1 = by0 + Rg, x0 = bx0 - Rg, x1 = bx0 + Rg;
+      const int nring = Rg == 0 ? 1 : 8 * Rg, w = 2 * Rg + 1;
+      for (int j = u; j < nring; j += kRingLanes) {
+        int by, bx;
+        if (j < w) {
+          by = y0;
+          bx = x0 + j;
+        } else if (j < 2 * w) {
+          by = y1;
+          bx = x0 + j - w;
+        } else {
+          const int m = j - 2 * w;
+          by = y0 + 1 + (m >> 1);
+          bx = (m & 1) ? x1 : x0;
+        }
+        if (bx < 0 || bx >= Pb || by < 0 || by >= Pb) continue;
+        const int bb = by * Pb + bx;
+        const int t0 = abstart[bb], t1 = abstart[bb + 1];
+        for (int e = t0; e < t1; ++e) {
+          const uint2 v = abk[e];
+          const int64_t ix = (int64_t)(v.x & 0xFFFFu) - x, iy = (int64_t)(v.x >> 16) - y;
+          const uint64_t kk = ((uint64_t)(ix * ix + iy * iy) << kWideKeyBits) | v.y;
+          best = kk < best ? kk : best;
+        }
+      }
+#pragma unroll
+      for (int m = 1; m < kRingLanes; m <<= 1) {
+        const uint64_t o = ((uint64_t)(uint32_t)__shfl_xor((int)(best >> 32), m) << 32) |
+                           (uint32_t)__shfl_xor((int)(uint32_t)best, m);
+        best = o < best ? o : best;
+      }
+      int64_t lb = INT64_MAX;
+      if (y0 > 0) lb = min(lb, y - ((int64_t)y0 << bsh) + 1);
+      if (y1 < Pb - 1) lb = min(lb, ((int64_t)(y1 + 1) << bsh) - y);
+      if (x0 > 0) lb = min(lb, x - ((int64_t)x0 << bsh) + 1);
+      if (x1 < Pb - 1) lb = min(lb, ((int64_t)(x1 + 1) << bsh) - x);
+      if (best != ~0ull && (lb == INT64_MAX || (int64_t)(best >> kWideKeyBits) < lb * lb)) break;
+    }
+    a = (int)(best & ((1ull << kWideKeyBits) - 1));
+  }
+  if (u == 0) assign[t] = a;
+}
+
+__global__ void __launch_bounds__(kMergeThreads)
+merge_gcount_kernel(int N, int k, int64_t n_tok, const int32_t* __restrict__ assign,
+                    int32_t* __restrict__ gcnt) {
+  const int64_t t = (int64_t)blockIdx.x * kMergeThreads + threadIdx.x;
+  if (t >= n_tok) return;
+  const int64_t b = t / N;
+  atomicAdd(&gcnt[b * k + assign[t]], 1);
+}
+
+__global__ void __launch_bounds__(kMergeThreads)
+merge_gplace_kernel(int N, int k, int64_t n_tok, const int32_t* __restrict__ assign,
+                    const int32_t* __restrict__ offsets, int32_t* __restrict__ cur,
+                    int32_t* __restrict__ glst) {
+  const int64_t t = (int64_t)blockIdx.x * kMergeThreads + threadIdx.x;
+  if (t >= n_tok) return;
+  const int64_t b = t / N;
+  const int a = assign[t];
+  const int r = atomicAdd(&cur[b * k + a], 1);
+  glst[b * N + offsets[b * (k + 1) + a] + r] = (int32_t)(t - b * N);
+}
+
+__global__ void __launch_bounds__(kMergeThreads)
+merge_grank_kernel(int N, int k, int64_t n_tok, const int32_t* __restrict__ assign,
+                   const int32_t* __restrict__ offsets, const int32_t* __restrict__ glst,
+                   int32_t* __restrict__ members) {
+  const int64_t t = (int64_t)blockIdx.x * kMergeThreads + threadIdx.x;
+  if (t >= n_tok) return;
+  const int64_t b = t / N;
+  const int i = (int)(t - b * N);
+  const int a = assign[t];
+  const int lo = offsets[b * (k + 1) + a], hi = offsets[b * (k + 1) + a + 1];
+  const int32_t* seg = glst + b * N;
+  int rank = 0, y = lo;
+  for (; y + 4 <= hi; y += 4) {   // four loads in flight
+    const int v0 = seg[y], v1 = seg[y + 1], v2 = seg[y + 2], v3 = seg[y + 3];
+    rank += (v0 < i) + (v1 < i) + (v2 < i) + (v3 < i);
+  }
+  for (; y < hi; ++y) rank += seg[y] < i;
+  members[b * N + lo + rank] = i;
+}
+
 // Lane groups: L = 2^lg lanes per anchor, 64 / L anchors per wave.
 struct MGroup {
   int64_t id;
@@ -628,14 +846,43 @@ hipError_t bwd_t(int B, int N, int k, int Cf, const void* feats, const float* co
 
 hipError_t launch_merge_plan(const float* coords, const float* scores, int B, int N, int k, int G,
                              int32_t* anchors, int32_t* assign, int32_t* members,
-                             int32_t* offsets, hipStream_t st) {
-  // the ring search of an image is spread over S workgroups (each repeats the
-  // selection and the bucketing) so that a batch fills the chip
-  const int S = std::max(1, std::min({8, (N + 255) / 256, std::max(1, 256 / std::max(B, 1))}));
-  hipLaunchKernelGGL(merge_assign_kernel, dim3(B * S), dim3(kPlanT), 0, st, coords, scores, N, k,
-                     G, S, anchors, assign);
-  hipLaunchKernelGGL(merge_members_kernel, dim3(B), dim3(kPlanT), 0, st, N, k, assign, members,
-                     offsets);
+                             int32_t* offsets, void* ws, hipStream_t st) {
+  if (N <= kMaxTok) {
+    // the ring search of an image is spread over S workgroups (each repeats
+    // the selection and the bucketing) so that a batch fills the chip
+    const int S = std::max(1, std::min({8, (N + 255) / 256, std::max(1, 256 / std::max(B, 1))}));
+    hipLaunchKernelGGL(merge_assign_kernel, dim3(B * S), dim3(kPlanT), 0, st, coords, scores, N, k,
+                       G, S, anchors, assign);
+    hipLaunchKernelGGL(merge_members_kernel, dim3(B), dim3(kPlanT), 0, st, N, k, assign, members,
+                       offsets);
+    return hipGetLastError();
+  }
+  const MergeWorkspace w = merge_layout(ws, B, N, k);
+  const MergeBuckets mb = merge_buckets(k);
+  const int64_t n_tok = (int64_t)B * N, n_anc = (int64_t)B * k;
+  auto grid = [](int64_t n) { return dim3((unsigned)((n + kMergeThreads - 1) / kMergeThreads)); };
+  hipLaunchKernelGGL(merge_select_kernel, dim3(B), dim3(kPlanT), 0, st, scores, N, k, w.sk, w.apos,
+                     anchors);
+  launch_zero_i32((int64_t)B * mb.nb, w.abcnt, st);
+  hipLaunchKernelGGL(merge_abucket_count_kernel, grid(n_anc), dim3(kMergeThreads), 0, st, coords, N,
+                     k, G, n_anc, (const int32_t*)anchors, w.abcnt, w.abrank);
+  launch_segment_scan(B, mb.nb, w.abcnt, w.abstart, st);
+  hipLaunchKernelGGL(merge_abucket_place_kernel, grid(n_anc), dim3(kMergeThreads), 0, st, coords, N,
+                     k, G, n_anc, (const int32_t*)anchors, (const int32_t*)w.abstart,
+                     (const int32_t*)w.abrank, w.abk);
+  hipLaunchKernelGGL(merge_assign_wide_kernel, grid(n_tok * kRingLanes), dim3(kMergeThreads), 0, st,
+                     coords, N, k, G, n_tok, (const int32_t*)w.apos, (const int32_t*)w.abstart,
+                     (const uint2*)w.abk, assign);
+  launch_zero_i32(n_anc, w.gcnt, st);
+  hipLaunchKernelGGL(merge_gcount_kernel, grid(n_tok), dim3(kMergeThreads), 0, st, N, k, n_tok,
+                     (const int32_t*)assign, w.gcnt);
+  launch_segment_scan(B, k, w.gcnt, offsets, st);
+  launch_zero_i32(n_anc, w.gcnt, st);
+  hipLaunchKernelGGL(merge_gplace_kernel, grid(n_tok), dim3(kMergeThreads), 0, st, N, k, n_tok,
+                     (const int32_t*)assign, (const int32_t*)offsets, w.gcnt, w.glst);
+  hipLaunchKernelGGL(merge_grank_kernel, grid(n_tok), dim3(kMergeThreads), 0, st, N, k, n_tok,
+                     (const int32_t*)assign, (const int32_t*)offsets, (const int32_t*)w.glst,
+                     members);
   return hipGetLastError();
 }
 

@@ -7,8 +7,9 @@ Desktop Hardware": at retention 0.4 the stages keep 2048 -> 819 -> 328 ->
 batch 32 ("Key Designs" item 1 for the merge itself).  Readings where the
 pages are silent: the importance scores (the output of the scoring MLP) are
 standard normals; the first level's tokens are the Perlin-visible cells of
-the 64x64 grid, the later levels' tokens the nearest-anchor means of that
-set (as the stage-3 workload of the attention benchmarks).
+the 64x64 grid (every cell of the grid for the fine-tune workloads, which
+see whole images), the later levels' tokens the nearest-anchor means of
+that set (as the stage-3 workload of the attention benchmarks).
 
 Draw order from ``numpy.random.default_rng(seed)``: per image the Perlin
 set and, for the later levels, their anchors; then per level the scores
@@ -45,6 +46,14 @@ MERGE_CONFIGS = {
     "merge_tiny": MergeConfig("merge_tiny", 3001, 2, 16, ((60, 23, 16), (23, 9, 24)), "f32"),
     "merge_stages": MergeConfig("merge_stages", 3002, 32, 64,
                                 ((2048, 819, 128), (819, 328, 256), (328, 131, 512)), "bf16"),
+    # fine-tuning sees every token: the full 128 x 128 grid of a 1024-pixel
+    # image, and the 256 x 256 grid of a 2048-pixel one, at retention 0.4
+    "merge_finetune": MergeConfig("merge_finetune", 3003, 4, 128,
+                                  ((16384, 6554, 128), (6554, 2622, 256), (2622, 1049, 512)),
+                                  "bf16"),
+    "merge_highres": MergeConfig("merge_highres", 3004, 4, 256,
+                                 ((65536, 26214, 128), (26214, 10486, 256), (10486, 4194, 512)),
+                                 "bf16"),
 }
 
 
@@ -62,7 +71,10 @@ def make_merge_case(cfg: Union[str, MergeConfig], B: int | None = None, tensors:
     coords = [np.empty((cfg.B, n, 2), dtype=np.float32) for n, _, _ in cfg.levels]
     for b in range(cfg.B):
         n1 = cfg.levels[0][0]
-        if n1 <= G * G // 2:
+        if n1 == G * G:          # every cell of the grid, row-major
+            cells = np.arange(G * G)
+            pts = np.stack([cells % G, cells // G], 1).astype(np.float64)
+        elif n1 <= G * G // 2:
             vis = perlin_visible_cells(rng, G, n1)
             pts = np.stack([vis % G, vis // G], 1).astype(np.float64)
         else:

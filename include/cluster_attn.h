@@ -393,8 +393,13 @@ ca_status cluster_attn_knn_sample_bwd(int dt, int B, int N, int M, int C, int gr
  * every other token to the anchor nearest by squared distance of the 16-bit
  * fixed-point coordinates of the neighbour build (ties to the earlier
  * anchor); within a group the softmax of the members' scores weighs the
- * features and the coordinates.  N <= 4096 tokens per image; scores finite.
+ * features and the coordinates.  N <= 2^24 tokens per image (B*N < 2^31);
+ * scores finite.
  * ------------------------------------------------------------------------ */
+
+/* Workspace bytes needed by cluster_attn_merge_plan (0 for images of at most
+ * 4096 tokens, and for invalid sizes). */
+size_t cluster_attn_merge_plan_workspace(int B, int N, int k);
 
 /*
  * Plan (exact integers; the unique result of the rules above):
@@ -403,10 +408,14 @@ ca_status cluster_attn_knn_sample_bwd(int dt, int B, int N, int M, int C, int gr
  *   assign  [B, N] int32 out: anchor position of every token.
  *   members [B, N] int32 out, offsets [B, k + 1] int32 out: the tokens of
  *           group a are members[offsets[a] .. offsets[a+1]), in token order.
+ *   ws      device workspace of cluster_attn_merge_plan_workspace bytes
+ *           (images above 4096 tokens are planned there; NULL when 0); two
+ *           calls that overlap in time must not share it.
  */
 ca_status cluster_attn_merge_plan(const float* coords, const float* scores, int B, int N, int k,
-                            int grid_side, int32_t* anchors, int32_t* assign, int32_t* members,
-                            int32_t* offsets, void* hip_stream);
+                                  int grid_side, int32_t* anchors, int32_t* assign,
+                                  int32_t* members, int32_t* offsets, void* ws, size_t ws_bytes,
+                                  void* hip_stream);
 
 /*
  * Forward: w_i = exp(s_i) / sum over the group of exp(s_j) (max subtracted,

@@ -45,6 +45,7 @@ from .knn_sampler import (  # noqa: F401
 from .token_merge import (  # noqa: F401
     merge_anchors,
     merge_assign,
+    merge_assign_tree,
     merge_weights,
     merge_fwd,
     merge_bwd,

@@ -44,6 +44,7 @@ from .cluster_attention import quantize
 __all__ = [
     "merge_anchors",
     "merge_assign",
+    "merge_assign_tree",
     "merge_weights",
     "merge_fwd",
     "merge_bwd",
@@ -75,16 +76,41 @@ def merge_assign(coords: np.ndarray, anchors: np.ndarray, grid_side: int) -> np.
     return assign
 
 
+def merge_assign_tree(coords: np.ndarray, anchors: np.ndarray, grid_side: int) -> np.ndarray:
+    """Reading M3 for images too large for the per-token scan of
+    :func:`merge_assign`; the same result.
+
+    A k-d tree over the anchors' fixed-point coordinates (integers, exact in
+    fp64) gives every token's nearest distance and then every anchor within
+    a hair above it; among those, the exact integer squared distances pick
+    the nearest, ties to the earlier anchor."""
+    from scipy.spatial import cKDTree
+
+    qx, qy = quantize(np.asarray(coords, dtype=np.float32), grid_side)
+    P = np.stack([qx, qy], 1)
+    A = P[anchors]
+    tree = cKDTree(A.astype(np.float64))
+    dmin, _ = tree.query(P.astype(np.float64), k=1)
+    near = tree.query_ball_point(P.astype(np.float64), dmin * (1 + 1e-9) + 1e-6)
+    assign = np.empty(P.shape[0], dtype=np.int64)
+    for i, cand in enumerate(near):
+        c = np.asarray(cand, dtype=np.int64)
+        d2 = ((A[c] - P[i]) ** 2).sum(1)
+        assign[i] = c[d2 == d2.min()].min()
+    assign[anchors] = np.arange(anchors.shape[0], dtype=np.int64)
+    return assign
+
+
 def merge_weights(scores: np.ndarray, assign: np.ndarray, k: int) -> np.ndarray:
-    """Reading M4: softmax of the scores inside every group (fp64)."""
+    """Reading M4: softmax of the scores inside every group (fp64), with the
+    group maxima and sums gathered by group index."""
     s = np.asarray(scores, dtype=np.float64)
-    w = np.zeros_like(s)
-    for a in range(k):
-        g = assign == a
-        if g.any():
-            e = np.exp(s[g] - s[g].max())
-            w[g] = e / e.sum()
-    return w
+    a = np.asarray(assign, dtype=np.int64)
+    gmax = np.full(k, -np.inf)
+    np.maximum.at(gmax, a, s)
+    e = np.exp(s - gmax[a])
+    tot = np.bincount(a, weights=e, minlength=k)
+    return e / tot[a]
 
 
 def merge_fwd(feats, coords, scores, assign, k):

@@ -267,12 +267,20 @@ def test_knn_validation(lib):
 def test_merge_validation(lib):
     pl = lib.cluster_attn_merge_plan
     ptr = [P * (i + 1) for i in range(6)]
-    assert pl(*ptr[:2], 2, 5000, 100, 64, *ptr[2:], None) == CA_ERR_UNSUPPORTED   # N > 4096
-    assert pl(*ptr[:2], 2, 100, 0, 64, *ptr[2:], None) == CA_ERR_SHAPE            # k < 1
-    assert pl(*ptr[:2], 2, 100, 101, 64, *ptr[2:], None) == CA_ERR_SHAPE          # k > N
-    assert pl(*ptr[:2], 2, 100, 40, 0, *ptr[2:], None) == CA_ERR_SHAPE            # grid side
-    assert pl(None, P, 2, 100, 40, 64, *ptr[2:], None) == CA_ERR_NULL
-    assert pl(None, None, 0, 100, 40, 64, None, None, None, None, None) == CA_OK
+    assert pl(*ptr[:2], 2, (1 << 24) + 1, 100, 64, *ptr[2:], None, 0, None) == CA_ERR_SHAPE
+    assert pl(*ptr[:2], 2, 100, 0, 64, *ptr[2:], None, 0, None) == CA_ERR_SHAPE     # k < 1
+    assert pl(*ptr[:2], 2, 100, 101, 64, *ptr[2:], None, 0, None) == CA_ERR_SHAPE   # k > N
+    assert pl(*ptr[:2], 2, 100, 40, 0, *ptr[2:], None, 0, None) == CA_ERR_SHAPE     # grid side
+    assert pl(None, P, 2, 100, 40, 64, *ptr[2:], None, 0, None) == CA_ERR_NULL
+    assert pl(None, None, 0, 100, 40, 64, None, None, None, None, None, 0, None) == CA_OK
+    # images above 4096 tokens are planned in a workspace
+    assert lib.cluster_attn_merge_plan_workspace(2, 4096, 1000) == 0
+    need = lib.cluster_attn_merge_plan_workspace(2, 65536, 26214)
+    assert need >= 2 * (65536 * 12 + 26214 * 16)
+    assert lib.cluster_attn_merge_plan_workspace(2, 100, 101) == 0                # k > N
+    big = [P * 64 * (i + 1) for i in range(6)]
+    assert pl(*big[:2], 2, 65536, 26214, 256, *big[2:], None, need, None) == CA_ERR_NULL
+    assert pl(*big[:2], 2, 65536, 26214, 256, *big[2:], P * 2048, need - 1, None) == CA_ERR_WORKSPACE
     fw = lib.cluster_attn_merge_fwd
     t = [P * (i + 1) for i in range(7)]
     assert fw(9, 2, 100, 40, 64, *t, None) == CA_ERR_UNSUPPORTED

@@ -64,6 +64,35 @@ def test_assignment_matches_kdtree():
         assert assign[i] == np.nonzero(d2 == d2.min())[0][0]
 
 
+@pytest.mark.parametrize("geom,N,k,G", [("uniform", 500, 180, 32), ("dense", 256, 100, 16),
+                                         ("dense", 1024, 410, 32), ("uniform", 50, 50, 8)])
+def test_tree_assignment_matches_scan(geom, N, k, G):
+    """The k-d tree form against the per-token scan: uniform points with
+    repeated coordinates, and every cell of a dense grid (equidistant
+    anchors everywhere), up to k = N."""
+    rng = np.random.default_rng(N + k)
+    if geom == "dense":
+        cells = np.arange(G * G)[:N]
+        X = np.stack([cells % G, cells // G], 1).astype(np.float32)
+    else:
+        X = rng.uniform(-0.5, G - 0.5, size=(N, 2)).astype(np.float32)
+        X[N // 2:N // 2 + N // 5] = X[:N // 5]
+    anchors = O.merge_anchors(rng.standard_normal(N).astype(np.float32), k)
+    np.testing.assert_array_equal(O.merge_assign_tree(X, anchors, G), O.merge_assign(X, anchors, G))
+
+
+def test_weights_match_per_group_softmax():
+    """The gathered form of reading M4 against a softmax taken group by
+    group (scipy's, on each group's scores)."""
+    from scipy.special import softmax
+
+    X, s, F, anchors, assign = _case(seed=9, N=120, k=30)
+    w = O.merge_weights(s, assign, anchors.size)
+    for a in range(anchors.size):
+        g = assign == a
+        np.testing.assert_allclose(w[g], softmax(s[g]), rtol=1e-14, atol=0)
+
+
 def _case(seed=4, N=40, k=12, C=5):
     rng = np.random.default_rng(seed)
     X = rng.uniform(0, 10, size=(N, 2)).astype(np.float32)
