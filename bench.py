@@ -47,9 +47,9 @@ MERGE_ENTRY_KERNELS = {"plan": ["merge_assign_kernel", "merge_members_kernel"], 
 SAMPLER_ENTRY_KERNELS = {
     "table": ["knn_table_kernel"],
     "fwd": ["knn_fwd_kernel"],
-    "bwd": ["knn_zero_kernel", "knn_bwd_query_kernel", "knn_pprefix_kernel", "knn_scan_kernel",
-            "knn_pplace_kernel", "knn_order_kernel", "knn_dfeat_kernel", "knn_dp_kernel",
-            "knn_pcount_kernel"],
+    "bwd": ["knn_bwd_query_kernel", "knn_pcount_kernel (partition counts and walk order)",
+            "knn_pprefix_kernel", "segment_scan_kernel", "knn_pplace_kernel",
+            "knn_dfeat_kernel (feature gradient and dp)"],
 }
 BF16_MFMA_PEAK_TFLOPS = 2500.0  # dense
 

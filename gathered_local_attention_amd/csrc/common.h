@@ -251,7 +251,7 @@ struct KnnWorkspace {
   int32_t* lst;     // [B, M * K]    (large images, same place as pcnt) entries, unranked
   int32_t* slot;    // [B, M, K]     token of every (query, slot), -1 empty
   float* wgt;       // [B, M, K]     its weight
-  int32_t* ent;     // [B, M * K]    entries (query * K + slot) by token
+  int2* ent;        // [B, M * K]    (query, weight bits) of the entries, by token
   float* dpart;     // [B, M]        per-query share of dL/dp
   int32_t* order;   // [B, N]        walk order of the tokens (feature gradient)
   KnnTableWorkspace bk;   // large images: bucket arrays of the walk order
@@ -275,7 +275,7 @@ static inline KnnWorkspace knn_layout(void* base, int64_t B, int64_t N, int64_t 
   w.lst = w.pcnt;
   w.slot = (int32_t*)take((size_t)(B * M * K) * 4);
   w.wgt = (float*)take((size_t)(B * M * K) * 4);
-  w.ent = (int32_t*)take((size_t)(B * M * K) * 4);
+  w.ent = (int2*)take((size_t)(B * M * K) * 8);
   w.dpart = (float*)take((size_t)(B * M) * 4);
   w.order = (int32_t*)take((size_t)(B * N) * 4);
   const KnnTableWorkspace tb = knn_table_layout(nullptr, B, N);

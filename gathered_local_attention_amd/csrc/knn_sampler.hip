@@ -49,7 +49,8 @@
 //   knn_dfeat_kernel      a lane group per token: dF = sum over its entries
 //                         of w * dO (gathered rows), written once (0 for
 //                         tokens no query reaches).
-//   knn_dp_kernel         fixed-order reduction of the per-wave dp shares.
+//   dp                    fixed-order reduction of the per-wave dp shares,
+//                         by the feature-gradient kernel's last workgroup.
 // Nothing in the backward uses floating-point atomics: the results are
 // bitwise reproducible.
 #include "common.h"
@@ -358,8 +359,27 @@ struct Chunk<float> {
   __device__ static void store(float* p, const float* v) {
     *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
   }
+  // acc + <a, b> over the chunk, in order
+  __device__ static float dot(uint4 a, uint4 b, float acc) {
+    acc = fmaf(__uint_as_float(a.x), __uint_as_float(b.x), acc);
+    acc = fmaf(__uint_as_float(a.y), __uint_as_float(b.y), acc);
+    acc = fmaf(__uint_as_float(a.z), __uint_as_float(b.z), acc);
+    return fmaf(__uint_as_float(a.w), __uint_as_float(b.w), acc);
+  }
 };
 typedef float f32x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+// acc + a0 b0 + a1 b1 of two packed pairs, one instruction (v_dot2c_f32_*):
+// the half-precision products are exact in fp32
+__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float acc, bf16*) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b),
+                                         acc, false);
+}
+__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float acc, f16*) {
+  return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, a), __builtin_bit_cast(f16x2, b), acc,
+                                false);
+}
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 // eight bf16 / fp16 values: widening is exact, narrowing rounds to nearest even
@@ -381,6 +401,13 @@ struct HalfChunk {
   __device__ static void store(H* p, const float* v) {
     const f32x8 f = {v[0], v[1], v[2], v[3], v[4], v[5], v[6], v[7]};
     *reinterpret_cast<uint4*>(p) = __builtin_bit_cast(uint4, __builtin_convertvector(f, V));
+  }
+  // acc + <a, b> over the chunk: four pair products, each pair summed first
+  __device__ static float dot(uint4 a, uint4 b, float acc) {
+    acc = dot2(a.x, b.x, acc, (H*)nullptr);
+    acc = dot2(a.y, b.y, acc, (H*)nullptr);
+    acc = dot2(a.z, b.z, acc, (H*)nullptr);
+    return dot2(a.w, b.w, acc, (H*)nullptr);
   }
 };
 template <>
@@ -577,15 +604,10 @@ knn_bwd_query_kernel(int N, int M, int Cf, int G, int K, int lg, float p, int64_
 #pragma unroll
     for (int r = 0; r < Ck::NR; ++r) {
       if (r >= nr || !live) break;
-      float o[Ck::E];
-      Ck::cvt(oraw[r], o);
 #pragma unroll
       for (int k = 0; k < KM; ++k) {
         if (sl[k] < 0) raw[r][k] = make_uint4(0u, 0u, 0u, 0u);
-        float v[Ck::E];
-        Ck::cvt(raw[r][k], v);
-#pragma unroll
-        for (int e = 0; e < Ck::E; ++e) gk[k] = fmaf(o[e], v[e], gk[k]);
+        gk[k] = Ck::dot(oraw[r], raw[r][k], gk[k]);
       }
     }
     if (L >= KM) {
@@ -664,15 +686,79 @@ knn_bwd_query_kernel(int N, int M, int Cf, int G, int K, int lg, float p, int64_
   }
 }
 
+// Spatial walk order of the tokens for the feature gradient: the tokens of
+// an image bucketed on a coarse grid (about two per bucket) in LDS, so that
+// the waves resident at one time work on neighbouring tokens, which share
+// most of their queries (and so the dO rows they gather stay in L2).  Any
+// order gives the same result: each token's sum has its own fixed order.
+// One workgroup of kKnnThreads per image of at most kTabMaxTokens tokens;
+// start holds kTabMaxBuckets ints of LDS.
+__device__ __forceinline__ void order_image(const float* __restrict__ coords, int N, int G, int64_t b,
+                                            int* start, int* tmp, int32_t* __restrict__ order) {
+  const int tid = threadIdx.x;
+  const KnnBuckets bg = knn_buckets(N, G);
+  const double step = (double)(1 << bg.shift);
+  const int bs = bg.bs, Pb = bg.Pb, nb = bg.nb;
+  const float2* xy = reinterpret_cast<const float2*>(coords) + b * N;
+  for (int x = tid; x < nb; x += kKnnThreads) start[x] = 0;
+  __syncthreads();
+  constexpr int kPer = kTabMaxTokens / kKnnThreads;
+  int bk[kPer], rk[kPer];
+#pragma unroll
+  for (int r = 0; r < kPer; ++r) {
+    const int e = tid + r * kKnnThreads;
+    bk[r] = -1;
+    if (e < N) {
+      const float2 c = xy[e];
+      const uint32_t qx = quantize_axis(c.x, step), qy = quantize_axis(c.y, step);
+      // buckets in row-major order of the coarse grid
+      bk[r] = (int)((qy >> bs) * (uint32_t)Pb + (qx >> bs));
+      rk[r] = atomicAdd(&start[bk[r]], 1);
+    }
+  }
+  __syncthreads();
+  constexpr int kBPer = kTabMaxBuckets / kKnnThreads;
+  int cnt[kBPer];
+  int run = 0;
+#pragma unroll
+  for (int r = 0; r < kBPer; ++r) {
+    const int x = tid * kBPer + r;
+    cnt[r] = x < nb ? start[x] : 0;
+    run += cnt[r];
+  }
+  int total;
+  int acc = block_exclusive_scan(run, tmp, kKnnThreads, &total);
+#pragma unroll
+  for (int r = 0; r < kBPer; ++r) {
+    const int x = tid * kBPer + r;
+    if (x < nb) start[x] = acc;
+    acc += cnt[r];
+  }
+  __syncthreads();
+  int32_t* ord = order + b * N;
+#pragma unroll
+  for (int r = 0; r < kPer; ++r)
+    if (bk[r] >= 0) ord[start[bk[r]] + rk[r]] = tid + r * kKnnThreads;
+}
+
 // Per partition of kPart entries, the count of its entries per token,
 // accumulated in LDS (images of at most kTabMaxTokens tokens) and written
-// out whole (zeros included): one workgroup per partition.
+// out whole (zeros included): one workgroup per partition.  The launch
+// also carries the walk order: workgroups nparts .. nparts + B - 1 build
+// it for one image each (order_image).
 __global__ void __launch_bounds__(kKnnThreads)
-knn_pcount_kernel(int N, int64_t MK, int P, const int32_t* __restrict__ ent_slot,
-                  int32_t* __restrict__ pcnt) {
+knn_pcount_kernel(int N, int G, int64_t MK, int P, int64_t nparts, const int32_t* __restrict__ ent_slot,
+                  const float* __restrict__ coords, int32_t* __restrict__ pcnt,
+                  int32_t* __restrict__ order) {
   static_assert(kPart == kKnnThreads, "one entry per thread");
+  static_assert(kTabMaxBuckets == kTabMaxTokens, "one LDS array serves both");
   __shared__ int32_t c[kTabMaxTokens];
+  __shared__ int tmp[17];
   const int64_t part = blockIdx.x;
+  if (part >= nparts) {
+    order_image(coords, N, G, part - nparts, c, tmp, order);
+    return;
+  }
   const int64_t b = part / P;
   const int s = (int)(part - b * P);
   const int64_t e0 = (int64_t)s * kPart;
@@ -688,12 +774,11 @@ knn_pcount_kernel(int N, int64_t MK, int P, const int32_t* __restrict__ ent_slot
   for (int t = threadIdx.x; t < N; t += kKnnThreads) row[t] = c[t];
 }
 
-// Token-major entry lists, in entry order (entry = query * K + slot), by a
-// stable counting sort.  The entries of an image are cut into partitions of
-// kPart consecutive entries: (1) per partition and token, the count of its
-// entries (integer atomics in the query-major kernel: the counts do not
-// depend on their order), or per partition in LDS (knn_pcount_kernel) when
-// the image fits; (2) per token, the counts turned into exclusive
+// Token-major entry lists, in entry order (entry = query * K + slot), each
+// entry stored as its (query, weight) pair, by a stable counting sort.  The
+// entries of an image are cut into partitions of kPart consecutive entries:
+// (1) per partition and token, the count of its entries, in LDS
+// (knn_pcount_kernel); (2) per token, the counts turned into exclusive
 // prefixes over the partitions, and the token's total; (3) the totals
 // scanned into segment starts (launch_segment_scan); (4) per partition, every
 // entry placed at segment start + the partition's prefix + the number of
@@ -722,9 +807,9 @@ knn_pprefix_kernel(int N, int P, int64_t n_tok, int32_t* __restrict__ pcnt, int3
 // one workgroup per partition; wave w ranks the partition's entries
 // w*64 .. w*64+63 (one per lane) against the earlier entries of the partition
 __global__ void __launch_bounds__(kKnnThreads)
-knn_pplace_kernel(int N, int64_t MK, int P, const int32_t* __restrict__ ent_slot,
-                  const int32_t* __restrict__ off_all, const int32_t* __restrict__ pcnt,
-                  int32_t* __restrict__ ent_all) {
+knn_pplace_kernel(int N, int K, int64_t MK, int P, const int32_t* __restrict__ ent_slot,
+                  const float* __restrict__ ent_w, const int32_t* __restrict__ off_all,
+                  const int32_t* __restrict__ pcnt, int2* __restrict__ ent_all) {
   static_assert(kPart == kKnnThreads, "one entry per thread");
   __shared__ __align__(16) int32_t tok[kPart];
   const int64_t part = blockIdx.x;
@@ -746,7 +831,8 @@ knn_pplace_kernel(int N, int64_t MK, int P, const int32_t* __restrict__ ent_slot
             (v.w == t && y + 3 < u);
   }
   if (t >= 0)
-    ent_all[b * MK + off_all[b * (N + 1) + t] + pcnt[(b * P + s) * N + t] + rank] = (int32_t)(e0 + u);
+    ent_all[b * MK + off_all[b * (N + 1) + t] + pcnt[(b * P + s) * N + t] + rank] =
+        make_int2((int)((e0 + u) / K), __float_as_int(ent_w[b * MK + e0 + u]));
 }
 
 // Large images: token-major entry lists by per-token cursors.  (1) The
@@ -770,9 +856,9 @@ knn_lplace_kernel(int N, int64_t MK, int64_t n_ent, const int32_t* __restrict__ 
 }
 
 __global__ void __launch_bounds__(kKnnThreads)
-knn_lrank_kernel(int N, int64_t MK, int64_t n_ent, const int32_t* __restrict__ ent_slot,
-                 const int32_t* __restrict__ off_all, const int32_t* __restrict__ lst,
-                 int32_t* __restrict__ ent_all) {
+knn_lrank_kernel(int N, int K, int64_t MK, int64_t n_ent, const int32_t* __restrict__ ent_slot,
+                 const float* __restrict__ ent_w, const int32_t* __restrict__ off_all,
+                 const int32_t* __restrict__ lst, int2* __restrict__ ent_all) {
   const int64_t x = (int64_t)blockIdx.x * kKnnThreads + threadIdx.x;
   if (x >= n_ent) return;
   const int t = ent_slot[x];
@@ -787,90 +873,69 @@ knn_lrank_kernel(int N, int64_t MK, int64_t n_ent, const int32_t* __restrict__ e
     rank += (v0 < e) + (v1 < e) + (v2 < e) + (v3 < e);
   }
   for (; y < z; ++y) rank += seg[y] < e;
-  ent_all[b * MK + a + rank] = e;
+  ent_all[b * MK + a + rank] = make_int2(e / K, __float_as_int(ent_w[x]));
 }
 
-// Spatial walk order of the tokens for the feature gradient: the tokens of
-// an image bucketed on a coarse grid (about two per bucket) in LDS, so that
-// the waves resident at one time work on neighbouring tokens, which share
-// most of their queries (and so the dO rows they gather stay in L2).  Any
-// order gives the same result: each token's sum has its own fixed order.
-// grid = B, for images of at most kTabMaxTokens tokens.
-__global__ void __launch_bounds__(kTabThreads)
-knn_order_kernel(const float* __restrict__ coords, int N, int G, int32_t* __restrict__ order) {
-  __shared__ int start[kTabMaxBuckets];
-  const int b = blockIdx.x, tid = threadIdx.x;
-  const KnnBuckets bg = knn_buckets(N, G);
-  const double step = (double)(1 << bg.shift);
-  const int bs = bg.bs, Pb = bg.Pb, nb = bg.nb;
-  const float2* xy = reinterpret_cast<const float2*>(coords) + (int64_t)b * N;
-  for (int x = tid; x < nb; x += kTabThreads) start[x] = 0;
+
+// dp = sum of the per-wave shares, in a fixed order, by one workgroup of
+// NT threads
+template <int NT>
+__device__ __forceinline__ void dp_reduce(int64_t n, const float* __restrict__ dpart,
+                                          float* __restrict__ dp, float* red) {
+  float a[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};   // eight loads in flight
+  int64_t i = threadIdx.x;
+  for (; i + 7 * NT < n; i += 8 * NT)
+#pragma unroll
+    for (int u = 0; u < 8; ++u) a[u] += dpart[i + u * NT];
+  for (; i < n; i += NT) a[0] += dpart[i];
+  red[threadIdx.x] = ((a[0] + a[1]) + (a[2] + a[3])) + ((a[4] + a[5]) + (a[6] + a[7]));
   __syncthreads();
-  constexpr int kPer = kTabMaxTokens / kTabThreads;
-  int bk[kPer], rk[kPer];
-#pragma unroll
-  for (int r = 0; r < kPer; ++r) {
-    const int e = tid + r * kTabThreads;
-    bk[r] = -1;
-    if (e < N) {
-      const float2 c = xy[e];
-      const uint32_t qx = quantize_axis(c.x, step), qy = quantize_axis(c.y, step);
-      // buckets in row-major order of the coarse grid
-      bk[r] = (int)((qy >> bs) * (uint32_t)Pb + (qx >> bs));
-      rk[r] = atomicAdd(&start[bk[r]], 1);
-    }
+  for (int o = NT / 2; o >= 1; o >>= 1) {
+    if ((int)threadIdx.x < o) red[threadIdx.x] += red[threadIdx.x + o];
+    __syncthreads();
   }
-  __syncthreads();
-  __shared__ int tmp[17];
-  constexpr int kBPer = kTabMaxBuckets / kTabThreads;
-  int cnt[kBPer];
-  int run = 0;
-#pragma unroll
-  for (int r = 0; r < kBPer; ++r) {
-    const int x = tid * kBPer + r;
-    cnt[r] = x < nb ? start[x] : 0;
-    run += cnt[r];
-  }
-  int total;
-  int acc = block_exclusive_scan(run, tmp, kTabThreads, &total);
-#pragma unroll
-  for (int r = 0; r < kBPer; ++r) {
-    const int x = tid * kBPer + r;
-    if (x < nb) start[x] = acc;
-    acc += cnt[r];
-  }
-  __syncthreads();
-  int32_t* ord = order + (int64_t)b * N;
-#pragma unroll
-  for (int r = 0; r < kPer; ++r)
-    if (bk[r] >= 0) ord[start[bk[r]] + rk[r]] = tid + r * kTabThreads;
+  if (threadIdx.x == 0) dp[0] = red[0];
+}
+
+// images without tokens: dp alone (one workgroup)
+__global__ void __launch_bounds__(1024)
+knn_dp_kernel(int64_t n, const float* __restrict__ dpart, float* __restrict__ dp) {
+  __shared__ float red[1024];
+  dp_reduce<1024>(n, dpart, dp, red);
 }
 
 // ---------------------------------------------------------------------------
 // Backward, token-major part: dF[b, t] = sum over its entries of w dO[b, m].
 // ---------------------------------------------------------------------------
-// Workgroup = one group of 64 / L tokens (L lanes per token, 16 bytes of the
-// row per lane) and its four waves split each token's entries: wave w takes
-// the batches w, w + 4, ... of kB entries, and the four partial sums are
-// added in wave order through LDS, so every token's sum has one fixed order.
-// Workgroups are dealt XCD-aware: workgroup 8 i + x (dispatched to XCD x)
-// takes token group i of the images x, x + 8, x + 16, ... one after the
-// other, so that the workgroups of one XCD work on one image at a time and
-// its dO rows stay in that XCD's L2 (with fewer than 8 images, X = B
-// streams).
+// A group of L lanes per token (16 bytes of the row per lane); `split` waves
+// share a token group and take its batches of kB entries in turn (wave w:
+// batches w, w + split, ...); their partial sums are added in wave order
+// through LDS, so every token's sum has one fixed order.  The (query,
+// weight) pairs of the next batch load while the current batch's dO rows
+// are in flight.  Workgroups are dealt XCD-aware over S image streams:
+// workgroup i belongs to stream x = i mod S (dispatched to XCD i mod 8) and
+// takes its token group of the images x, x + S, ... in turn; with S a
+// multiple of 8 (or S = B) an image stays on one XCD, and S is picked so
+// that the dO rows of the images in flight on an XCD fit its L2.  The first
+// workgroup also sums the dp shares (complete: the query-major kernel has
+// finished).
 template <typename T>
 __global__ void __launch_bounds__(kKnnThreads)
-knn_dfeat_kernel(int B, int N, int M, int Cf, int K, int lg, int split, const T* __restrict__ dout,
-                 const int32_t* __restrict__ off_all, const int32_t* __restrict__ ent_all,
-                 const float* __restrict__ ent_w, const int32_t* __restrict__ order,
-                 T* __restrict__ dfeat) {
+knn_dfeat_kernel(int B, int N, int M, int Cf, int64_t MK, int lg, int split, int S,
+                 const T* __restrict__ dout, const int32_t* __restrict__ off_all,
+                 const int2* __restrict__ ent_all, const int32_t* __restrict__ order,
+                 T* __restrict__ dfeat, int64_t n_dp, const float* __restrict__ dpart,
+                 float* __restrict__ dp) {
   using Ck = Chunk<T>;
   constexpr int kB = 8;                          // entries (rows) per batch
   constexpr int kW = kKnnThreads / 64;           // waves per workgroup
   __shared__ float part[kW][Ck::NR * Ck::E][64];
+  if (blockIdx.x == 0) {
+    __shared__ float red[kKnnThreads];
+    dp_reduce<kKnnThreads>(n_dp, dpart, dp, red);
+  }
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  const int X = min(B, 8);                      // image streams (one per XCD when B >= 8)
-  const int x = (int)(blockIdx.x % X), gi = (int)(blockIdx.x / X);
+  const int x = (int)(blockIdx.x % S), gi = (int)(blockIdx.x / S);
   const int L = 1 << lg, sub = lane & (L - 1);
   // `split` waves share a token group; the workgroup covers kW / split groups
   const int grp = gi * (kW / split) + wv / split, sw = wv % split;
@@ -878,36 +943,38 @@ knn_dfeat_kernel(int B, int N, int M, int Cf, int K, int lg, int split, const T*
   const int nch = Cf / Ck::E;
   const int nr = (nch - sub + L - 1) / L;            // chunks of this lane
   const int cs = min(sub, nch - 1);   // idle lanes (sub >= nch, nr = 0) load inside the row
-  const int64_t per = (int64_t)M * K;
-  for (int img = x; img < B; img += X) {
+  for (int img = x; img < B; img += S) {
     const int64_t b = img;
     const bool live = pos < N;
-    const int t = live ? (order ? order[b * N + pos] : pos) : 0;
+    const int t = live ? order[b * N + pos] : 0;
     const int a = live ? off_all[b * (N + 1) + t] : 0;
     const int z = live ? off_all[b * (N + 1) + t + 1] : 0;
-    const int32_t* ent = ent_all + b * per;
-    const float* wimg = ent_w + b * per;
+    const int2* ent = ent_all + b * MK;
     const T* oimg = dout + b * M * Cf;
     float acc[Ck::NR][Ck::E];
 #pragma unroll
     for (int r = 0; r < Ck::NR; ++r)
 #pragma unroll
       for (int e = 0; e < Ck::E; ++e) acc[r][e] = 0.f;
-    for (int u = a + sw * kB; u < z; u += split * kB) {
-      int e[kB];
-      float wt[kB];
-      // unconditional loads (a batch past the segment end re-reads entry u),
-      // masked afterwards
+    int u = a + sw * kB;
+    int2 pr[kB];
+    if (u < z) {
 #pragma unroll
-      for (int h = 0; h < kB; ++h) e[h] = ent[u + h < z ? u + h : u];
-#pragma unroll
-      for (int h = 0; h < kB; ++h) wt[h] = wimg[e[h]];
+      for (int h = 0; h < kB; ++h) pr[h] = ent[min(u + h, z - 1)];
+    }
+    while (u < z) {
+      // this batch's rows (unconditional loads of clamped entries, masked
+      // afterwards), then the next batch's pairs (clamped inside the segment)
       uint4 raw[Ck::NR][kB];
 #pragma unroll
       for (int r = 0; r < Ck::NR; ++r)
 #pragma unroll
         for (int h = 0; h < kB; ++h)
-          raw[r][h] = Ck::raw(oimg + (int64_t)(e[h] / K) * Cf + (cs + (r < nr ? r * L : 0)) * Ck::E);
+          raw[r][h] = Ck::raw(oimg + (int64_t)pr[h].x * Cf + (cs + (r < nr ? r * L : 0)) * Ck::E);
+      const int un = u + split * kB;
+      int2 nx[kB];
+#pragma unroll
+      for (int h = 0; h < kB; ++h) nx[h] = ent[min(un + h, z - 1)];
 #pragma unroll
       for (int r = 0; r < Ck::NR; ++r) {
         if (r >= nr) break;
@@ -916,10 +983,14 @@ knn_dfeat_kernel(int B, int N, int M, int Cf, int K, int lg, int split, const T*
           if (u + h >= z) raw[r][h] = make_uint4(0u, 0u, 0u, 0u);
           float v[Ck::E];
           Ck::cvt(raw[r][h], v);
+          const float wt = __int_as_float(pr[h].y);
 #pragma unroll
-          for (int q = 0; q < Ck::E; ++q) acc[r][q] = fmaf(wt[h], v[q], acc[r][q]);
+          for (int q = 0; q < Ck::E; ++q) acc[r][q] = fmaf(wt, v[q], acc[r][q]);
         }
       }
+#pragma unroll
+      for (int h = 0; h < kB; ++h) pr[h] = nx[h];
+      u = un;
     }
     // partial sums of the group's other waves to its first, added in wave order
     if (split > 1) {
@@ -947,25 +1018,6 @@ knn_dfeat_kernel(int B, int N, int M, int Cf, int K, int lg, int split, const T*
       }
     }
   }
-}
-
-// dp = sum of the per-query shares, in a fixed order (one workgroup)
-__global__ void __launch_bounds__(1024)
-knn_dp_kernel(int64_t n, const float* __restrict__ dpart, float* __restrict__ dp) {
-  __shared__ float red[1024];
-  float a[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};   // eight loads in flight
-  int64_t i = threadIdx.x;
-  for (; i + 7 * 1024 < n; i += 8 * 1024)
-#pragma unroll
-    for (int u = 0; u < 8; ++u) a[u] += dpart[i + u * 1024];
-  for (; i < n; i += 1024) a[0] += dpart[i];
-  red[threadIdx.x] = ((a[0] + a[1]) + (a[2] + a[3])) + ((a[4] + a[5]) + (a[6] + a[7]));
-  __syncthreads();
-  for (int o = 512; o >= 1; o >>= 1) {
-    if ((int)threadIdx.x < o) red[threadIdx.x] += red[threadIdx.x + o];
-    __syncthreads();
-  }
-  if (threadIdx.x == 0) dp[0] = red[0];
 }
 
 int group_log2(int Cf, int E) {
@@ -1036,29 +1088,28 @@ hipError_t bwd_t(int B, int N, int M, int Cf, int G, int K, float p, const float
     else if (K <= 8) go(knn_bwd_query_kernel<T, 8>);
     else go(knn_bwd_query_kernel<T, 16>);
   }
+  const int64_t n_dp = nq > 0 ? (nq + qwv - 1) / qwv : 0;   // one dp share per wave of the query kernel
   if (ntok > 0) {
     if (!large) {
-      if (npc > 0)
-        hipLaunchKernelGGL(knn_pcount_kernel, dim3((unsigned)nparts), dim3(kKnnThreads), 0, st, N,
-                           MK, P, (const int32_t*)w.slot, w.pcnt);
+      // partition counts, and the walk order in B more workgroups
+      hipLaunchKernelGGL(knn_pcount_kernel, dim3((unsigned)(nparts + B)), dim3(kKnnThreads), 0, st,
+                         N, G, MK, P, nparts, (const int32_t*)w.slot, coords, w.pcnt, w.order);
       hipLaunchKernelGGL(knn_pprefix_kernel, grid1(ntok), dim3(kKnnThreads), 0, st, N, P, ntok,
                          w.pcnt, w.cnt);
       launch_segment_scan(B, N, w.cnt, w.off, st);
       if (nparts > 0)
         hipLaunchKernelGGL(knn_pplace_kernel, dim3((unsigned)nparts), dim3(kKnnThreads), 0, st, N,
-                           MK, P, (const int32_t*)w.slot, (const int32_t*)w.off,
-                           (const int32_t*)w.pcnt, w.ent);
-      hipLaunchKernelGGL(knn_order_kernel, dim3(B), dim3(kTabThreads), 0, st, coords, N, G,
-                         w.order);
+                           K, MK, P, (const int32_t*)w.slot, (const float*)w.wgt,
+                           (const int32_t*)w.off, (const int32_t*)w.pcnt, w.ent);
     } else {
       launch_segment_scan(B, N, w.cnt, w.off, st);
       launch_zero_i32(ntok, w.cnt, st);
       if (nent > 0) {
         hipLaunchKernelGGL(knn_lplace_kernel, grid1(nent), dim3(kKnnThreads), 0, st, N, MK, nent,
                            (const int32_t*)w.slot, (const int32_t*)w.off, w.cnt, w.lst);
-        hipLaunchKernelGGL(knn_lrank_kernel, grid1(nent), dim3(kKnnThreads), 0, st, N, MK, nent,
-                           (const int32_t*)w.slot, (const int32_t*)w.off, (const int32_t*)w.lst,
-                           w.ent);
+        hipLaunchKernelGGL(knn_lrank_kernel, grid1(nent), dim3(kKnnThreads), 0, st, N, K, MK, nent,
+                           (const int32_t*)w.slot, (const float*)w.wgt, (const int32_t*)w.off,
+                           (const int32_t*)w.lst, w.ent);
       }
       // walk order: the tokens in bucket order
       const KnnBuckets bg = knn_buckets(N, G);
@@ -1076,14 +1127,18 @@ hipError_t bwd_t(int B, int N, int M, int Cf, int G, int K, float p, const float
     const int split = ept < 16 ? 1 : (ept < 48 ? 2 : 4);
     const int groups = (N + (64 >> lg) - 1) / (64 >> lg);   // token groups per image
     const int wgs = (groups * split + kKnnThreads / 64 - 1) / (kKnnThreads / 64);
-    hipLaunchKernelGGL(knn_dfeat_kernel<T>, dim3((unsigned)(std::min(B, 8) * wgs)), dim3(kKnnThreads), 0, st,
-                       B, N, M, Cf, K, lg, split, (const T*)dout, (const int32_t*)w.off,
-                       (const int32_t*)w.ent, (const float*)w.wgt, (const int32_t*)w.order,
-                       (T*)dfeat);
+    // image streams: as many images in flight per XCD as keep their dO rows
+    // within about 3 MiB of its L2
+    const int64_t dimg = std::max<int64_t>(1, (int64_t)M * Cf * (int64_t)sizeof(T));
+    const int per_xcd = (int)std::max<int64_t>(1, std::min<int64_t>((3 << 20) / dimg, (B + 7) / 8));
+    const int S = std::min(B, 8 * per_xcd);
+    hipLaunchKernelGGL(knn_dfeat_kernel<T>, dim3((unsigned)(S * wgs)), dim3(kKnnThreads), 0, st,
+                       B, N, M, Cf, MK, lg, split, S, (const T*)dout, (const int32_t*)w.off,
+                       (const int2*)w.ent, (const int32_t*)w.order, (T*)dfeat, n_dp,
+                       (const float*)w.dpart, dp);
+  } else {
+    hipLaunchKernelGGL(knn_dp_kernel, dim3(1), dim3(1024), 0, st, n_dp, (const float*)w.dpart, dp);
   }
-  const int64_t nwaves = (nq + qwv - 1) / qwv;   // one dp share per wave of the query kernel
-  hipLaunchKernelGGL(knn_dp_kernel, dim3(1), dim3(1024), 0, st, nq > 0 ? nwaves : 0,
-                     (const float*)w.dpart, dp);
   return hipGetLastError();
 }
 
