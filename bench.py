@@ -42,14 +42,20 @@ ENTRY_KERNELS = {
     "fwd": ["fwd_lds_kernel"],
     "bwd": ["bwd_q_lds_kernel", "bwd_kv_lds_kernel"],
 }
-MERGE_ENTRY_KERNELS = {"plan": ["merge_assign_kernel", "merge_members_kernel"], "fwd": ["merge_fwd_kernel"],
-                       "bwd": ["merge_bwd_kernel"]}
+MERGE_ENTRY_KERNELS = {
+    "plan": ["merge_assign_kernel, merge_members_kernel (images <= 4096 tokens) | merge_select_kernel, "
+             "merge_abucket_count/place_kernel, merge_assign_wide_kernel, merge_gcount/gplace/grank_kernel, "
+             "zero_i32_kernel, segment_scan_kernel (larger)"],
+    "fwd": ["merge_fwd_kernel"],
+    "bwd": ["merge_bwd_kernel"]}
 SAMPLER_ENTRY_KERNELS = {
-    "table": ["knn_table_kernel"],
+    "table": ["knn_table_kernel (images <= 4096 tokens) | knn_bucket_count/place_kernel, "
+              "segment_scan_kernel, knn_table_search_kernel (larger)"],
     "fwd": ["knn_fwd_kernel"],
     "bwd": ["knn_bwd_query_kernel", "knn_pcount_kernel (partition counts and walk order)",
             "knn_pprefix_kernel", "segment_scan_kernel", "knn_pplace_kernel",
-            "knn_dfeat_kernel (feature gradient and dp)"],
+            "knn_dfeat_kernel (feature gradient and dp); larger images: zero_i32_kernel, "
+            "knn_lplace/lrank_kernel, knn_bucket_count/place_kernel in place of the partition kernels"],
 }
 BF16_MFMA_PEAK_TFLOPS = 2500.0  # dense
 
@@ -708,12 +714,23 @@ def sampler_algorithmic(cfg):
 
 def sampler_cpu_baseline(cfg, case, images: int):
     """The fp64 oracle's sampler forward + backward on `images` images, all
-    levels, single-threaded (tables built beforehand, outside the timing)."""
+    levels, single-threaded.  The table rows the queries use are ranked by
+    the oracle beforehand, outside the timing (only the queries' cells: the
+    other cells are never read)."""
+    import numpy as np
     from threadpoolctl import threadpool_limits
 
     import oracle as O
 
-    tabs = [[O.knn_table(case["coords"][li][b], cfg.G, cfg.K) for b in range(images)]
+    def rows_of(coords, q):
+        i, j = O.query_cells(q, cfg.G)
+        cells = np.unique(i * cfg.G + j)
+        t = np.full((cfg.G, cfg.G, cfg.K), -1, dtype=np.int64)
+        t[cells // cfg.G, cells % cfg.G] = O.knn_table_cells(coords, cfg.G, cfg.K, cells // cfg.G,
+                                                            cells % cfg.G)
+        return t
+
+    tabs = [[rows_of(case["coords"][li][b], case["queries"][b]) for b in range(images)]
             for li in range(len(cfg.levels))]
     with threadpool_limits(limits=1):
         t0 = time.perf_counter()
@@ -753,11 +770,13 @@ def bench_sampler(args, torch, ca):
         sets.append(s)
     wss = [torch.empty(max(1, ca.knn_bwd_workspace_bytes(cfg.B, N, cfg.M, cfg.K)),
                        dtype=torch.uint8, device=dev) for N, _ in cfg.levels]
+    tws = [torch.empty(max(1, ca.knn_table_workspace_bytes(cfg.B, N, cfg.G)),
+                       dtype=torch.uint8, device=dev) for N, _ in cfg.levels]
 
     def step(s):
         for li in range(L):
             lv = s["lv"][li]
-            table = ca.knn_table(lv["coords"], cfg.G, cfg.K)
+            table = ca.knn_table(lv["coords"], cfg.G, cfg.K, workspace=tws[li])
             ca.knn_sample_fwd(lv["feats"], lv["coords"], s["q"], table, cfg.p)
             ca.knn_sample_bwd(lv["feats"], lv["coords"], s["q"], table, cfg.p, lv["dout"],
                               workspace=wss[li])
@@ -774,9 +793,10 @@ def bench_sampler(args, torch, ca):
     # per-entry-point durations (all levels of one step), HIP events on the
     # launch stream around back-to-back calls
     n_ev = min(args.steps, 100)
-    tables = [[ca.knn_table(s["lv"][li]["coords"], cfg.G, cfg.K) for li in range(L)] for s in sets]
+    tables = [[ca.knn_table(s["lv"][li]["coords"], cfg.G, cfg.K, workspace=tws[li]) for li in range(L)]
+              for s in sets]
     calls = {
-        "table": lambda i: [ca.knn_table(sets[i]["lv"][li]["coords"], cfg.G, cfg.K)
+        "table": lambda i: [ca.knn_table(sets[i]["lv"][li]["coords"], cfg.G, cfg.K, workspace=tws[li])
                             for li in range(L)],
         "fwd": lambda i: [ca.knn_sample_fwd(sets[i]["lv"][li]["feats"], sets[i]["lv"][li]["coords"],
                                             sets[i]["q"], tables[i][li], cfg.p) for li in range(L)],
@@ -838,7 +858,8 @@ def bench_sampler(args, torch, ca):
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = sampler_cpu_baseline(cfg, case, min(12, cfg.B))
+        # about 24576 queries per level (12 images of the decoder workload)
+        line["cpu_baseline"] = sampler_cpu_baseline(cfg, case, max(1, min(cfg.B, 24576 // cfg.M)))
     print(json.dumps(line), flush=True)
 
 
@@ -875,7 +896,8 @@ def merge_cpu_baseline(cfg, case, images: int):
             for b in range(images):
                 c, s = case["coords"][li][b], case["scores"][li][b]
                 anchors = O.merge_anchors(s, k)
-                assign = O.merge_assign(c, anchors, cfg.G)
+                # the per-token scan, or its k-d tree form on large images
+                assign = (O.merge_assign if N <= 4096 else O.merge_assign_tree)(c, anchors, cfg.G)
                 O.merge_fwd(F[b], c, s, assign, k)
                 O.merge_bwd(F[b], c, s, assign, k, dF[b], case["dcoord"][li][b])
         dt = time.perf_counter() - t0
@@ -906,10 +928,13 @@ def bench_merge(args, torch, ca):
                       "feats": case["feats"][li].to(dev), "dfeat": case["dfeat"][li].to(dev),
                       "dcoord": torch.from_numpy(case["dcoord"][li]).to(dev)} for li in range(L)])
 
+    pws = [torch.empty(max(1, ca.merge_plan_workspace_bytes(cfg.B, N, k)), dtype=torch.uint8,
+                       device=dev) for N, k, _ in cfg.levels]
+
     def step(s):
         for li, (N, k, C) in enumerate(cfg.levels):
             lv = s[li]
-            _, _, mem, off = ca.merge_plan(lv["coords"], lv["scores"], k, cfg.G)
+            _, _, mem, off = ca.merge_plan(lv["coords"], lv["scores"], k, cfg.G, workspace=pws[li])
             ca.merge_fwd(lv["feats"], lv["coords"], lv["scores"], mem, off)
             ca.merge_bwd(lv["feats"], lv["coords"], lv["scores"], mem, off, lv["dfeat"], lv["dcoord"])
 
@@ -922,10 +947,11 @@ def bench_merge(args, torch, ca):
     torch.cuda.synchronize()
     ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
     n_ev = min(args.steps, 100)
-    plans = [[ca.merge_plan(s[li]["coords"], s[li]["scores"], k, cfg.G)
+    plans = [[ca.merge_plan(s[li]["coords"], s[li]["scores"], k, cfg.G, workspace=pws[li])
               for li, (N, k, C) in enumerate(cfg.levels)] for s in sets]
     calls = {
-        "plan": lambda i: [ca.merge_plan(sets[i][li]["coords"], sets[i][li]["scores"], k, cfg.G)
+        "plan": lambda i: [ca.merge_plan(sets[i][li]["coords"], sets[i][li]["scores"], k, cfg.G,
+                                         workspace=pws[li])
                            for li, (N, k, C) in enumerate(cfg.levels)],
         "fwd": lambda i: [ca.merge_fwd(sets[i][li]["feats"], sets[i][li]["coords"], sets[i][li]["scores"],
                                        plans[i][li][2], plans[i][li][3]) for li in range(L)],
@@ -983,7 +1009,7 @@ def bench_merge(args, torch, ca):
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = merge_cpu_baseline(cfg, case, cfg.B)
+        line["cpu_baseline"] = merge_cpu_baseline(cfg, case, max(1, min(cfg.B, 65536 // cfg.levels[0][0])))
     print(json.dumps(line), flush=True)
 
 

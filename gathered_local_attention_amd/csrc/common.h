@@ -304,14 +304,19 @@ __host__ __device__ inline MergeBuckets merge_buckets(int k) {
   return g;
 }
 
+constexpr int kMergeSelChunk = 4096;      // tokens per chunk of the anchor placement
+
 struct MergeWorkspace {
   uint32_t* sk;     // [B, N]        order-preserving keys of the scores
+  uint2* sel;       // [B]           (k-th largest key, how many keys equal to it are taken)
+  int2* chunk;      // [B, nch]      keys above / equal to the k-th before each chunk
   int32_t* apos;    // [B, N]        anchor position of every token, -1 if none
   int32_t* abcnt;   // [B, nb]       anchors per bucket
   int32_t* abstart; // [B, nb + 1]   bucket starts
   int32_t* abrank;  // [B, k]        rank of each anchor in its bucket
   uint2* abk;       // [B, k]        (qx | qy << 16, position) in bucket order
-  int32_t* gcnt;    // [B, k]        group sizes, then placement cursors
+  int32_t* gcnt;    // [B, k]        group sizes
+  int32_t* gcur;    // [B, k]        placement cursors
   int32_t* glst;    // [B, N]        members in placement order
   size_t bytes;
 };
@@ -328,13 +333,17 @@ static inline MergeWorkspace merge_layout(void* base, int64_t B, int64_t N, int6
   const bool large = N > kMergeSmallTokens;
   const int64_t nb = large ? merge_buckets((int)k).nb : 0;
   const int64_t n = large ? N : 0, kk = large ? k : 0;
+  const int64_t nch = large ? (N + kMergeSelChunk - 1) / kMergeSelChunk : 0;
   w.sk = (uint32_t*)take((size_t)(B * n) * 4);
+  w.sel = (uint2*)take(large ? (size_t)B * 8 : 0);
+  w.chunk = (int2*)take((size_t)(B * nch) * 8);
   w.apos = (int32_t*)take((size_t)(B * n) * 4);
   w.abcnt = (int32_t*)take((size_t)(B * nb) * 4);
   w.abstart = (int32_t*)take(large ? (size_t)(B * (nb + 1)) * 4 : 0);
   w.abrank = (int32_t*)take((size_t)(B * kk) * 4);
   w.abk = (uint2*)take((size_t)(B * kk) * 8);
   w.gcnt = (int32_t*)take((size_t)(B * kk) * 4);
+  w.gcur = (int32_t*)take((size_t)(B * kk) * 4);
   w.glst = (int32_t*)take((size_t)(B * n) * 4);
   w.bytes = p;
   return w;

@@ -118,8 +118,14 @@ __device__ __forceinline__ void radix_select(const uint32_t* sk, int N, int k, i
     __syncthreads();
     const uint32_t pre = sel[0];
     const uint32_t hmask = dg == 3 ? 0u : (0xFFFFFFFFu << (8 * (dg + 1)));
-    for (int i = tid; i < N; i += kPlanT)
-      if ((sk[i] & hmask) == pre) atomicAdd(&hist[(sk[i] >> (8 * dg)) & 255u], 1);
+    for (int i0 = tid; i0 < N; i0 += kPlanT * 8) {   // eight keys in flight
+      uint32_t kv[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) kv[u] = i0 + u * kPlanT < N ? sk[i0 + u * kPlanT] : 0u;
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (i0 + u * kPlanT < N && (kv[u] & hmask) == pre) atomicAdd(&hist[(kv[u] >> (8 * dg)) & 255u], 1);
+    }
     __syncthreads();
     if (tid < 64) {
       // the digit where the count from the top reaches `want`: lane l holds
@@ -413,66 +419,124 @@ merge_members_kernel(int N, int k, const int32_t* __restrict__ assign,
 // ---------------------------------------------------------------------------
 // Plan of images above kMaxTok tokens, in global memory (workspace):
 //  1. merge_select_kernel, one workgroup per image: the score keys, their
-//     radix select, then anchor flags and positions chunk by chunk in token
-//     order (a workgroup scan per chunk, carried across chunks);
+//     radix select and the counts of keys above / equal to the selected one
+//     before every chunk of tokens; merge_flag_kernel, a workgroup per
+//     chunk: anchor flags and positions in token order;
 //  2. the anchors counting-sorted into square buckets (merge_buckets);
 //  3. merge_assign_wide_kernel: kRingLanes lanes per token, the ring search
 //     of the small-image kernel over the global bucket arrays;
-//  4. member lists: group sizes (integer atomics), offsets by a scan, every
+//  4. member lists: group sizes (integer atomics, in the assignment kernel),
+//     offsets by a scan, every
 //     token placed by its group's cursor (in no fixed order), then moved to
 //     group start + its rank by token index inside the group.
 // Keys (d2 << 24 | anchor position) are exact for k < 2^24.
 // ---------------------------------------------------------------------------
 constexpr int kWideKeyBits = 24;
 
+// 1a. one workgroup per image: the score keys and their radix select, then
+// per chunk of kMergeSelChunk tokens the counts of keys above and equal to
+// the k-th one (a wave per chunk), turned into exclusive prefixes over the
+// chunks; the image's bucket and group counters are zeroed here too
 __global__ void __launch_bounds__(kPlanT)
-merge_select_kernel(const float* __restrict__ scores, int N, int k, uint32_t* __restrict__ sk_all,
-                    int32_t* __restrict__ apos_all, int32_t* __restrict__ anchors) {
+merge_select_kernel(const float* __restrict__ scores, int N, int k, int nb, int nch,
+                    uint32_t* __restrict__ sk_all, uint2* __restrict__ sel_all,
+                    int2* __restrict__ chunk_all, int32_t* __restrict__ abcnt,
+                    int32_t* __restrict__ gcnt, int32_t* __restrict__ gcur) {
   __shared__ int hist[256];
   __shared__ uint32_t sel[2];
   __shared__ int tmp[17];
+  __shared__ int2 ccnt[1024];
   const int64_t b = blockIdx.x;
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const float* s = scores + b * N;
   uint32_t* sk = sk_all + b * N;
-  int32_t* apos = apos_all + b * N;
   for (int i = tid; i < N; i += kPlanT) sk[i] = score_key(s[i]);
+  for (int i = tid; i < nb; i += kPlanT) abcnt[b * nb + i] = 0;
+  for (int i = tid; i < k; i += kPlanT) {
+    gcnt[b * k + i] = 0;
+    gcur[b * k + i] = 0;
+  }
   radix_select(sk, N, k, hist, sel);
   const uint32_t kth = sel[0], n_eq = sel[1];
-  // chunks of kPlanT * R tokens, thread t owning R consecutive ones; the
-  // anchors before a token are the larger keys before it and the first
-  // n_eq equal keys in token order
-  constexpr int R = 4;
+  if (tid == 0) sel_all[b] = make_uint2(kth, n_eq);
   int carry_gt = 0, carry_eq = 0;
-  for (int c0 = 0; c0 < N; c0 += kPlanT * R) {
-    uint32_t kv[R];
-    int gt_local = 0, eq_local = 0;
+  for (int c0 = 0; c0 < nch; c0 += 1024) {   // up to 1024 chunks per round
+    for (int c = c0 + wv; c < min(nch, c0 + 1024); c += kPlanT / 64) {
+      int gt = 0, eq = 0;
+      const int t0 = c * kMergeSelChunk, t1 = min(N, t0 + kMergeSelChunk);
+      for (int i0 = t0 + lane; i0 < t1; i0 += 64 * 8) {
+        uint32_t kv[8];
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
-      const int i = c0 + tid * R + r;
-      kv[r] = i < N ? sk[i] : 0u;
-      gt_local += (i < N && kv[r] > kth) ? 1 : 0;
-      eq_local += (i < N && kv[r] == kth) ? 1 : 0;
-    }
-    int tot;
-    const int ex = block_exclusive_scan((gt_local << 16) | eq_local, tmp, kPlanT, &tot);
-    int eq_before = carry_eq + (ex & 0xFFFF);
-    int pos = carry_gt + (ex >> 16) + min(eq_before, (int)n_eq);
+        for (int u = 0; u < 8; ++u) kv[u] = i0 + u * 64 < t1 ? sk[i0 + u * 64] : 0u;
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
-      const int i = c0 + tid * R + r;
-      if (i < N) {
-        bool an = false;
-        if (kv[r] > kth) an = true;
-        else if (kv[r] == kth) an = (uint32_t)(eq_before++) < n_eq;
-        apos[i] = an ? pos : -1;
-        if (an) anchors[b * k + pos] = i;
-        pos += an ? 1 : 0;
+        for (int u = 0; u < 8; ++u) {
+          const bool in = i0 + u * 64 < t1;
+          gt += (in && kv[u] > kth) ? 1 : 0;
+          eq += (in && kv[u] == kth) ? 1 : 0;
+        }
       }
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) {
+        gt += __shfl_xor(gt, o, 64);
+        eq += __shfl_xor(eq, o, 64);
+      }
+      if (lane == 0) ccnt[c - c0] = make_int2(gt, eq);
     }
-    carry_gt += tot >> 16;
-    carry_eq += tot & 0xFFFF;
-    __syncthreads();   // tmp is reused by the next chunk's scan
+    __syncthreads();
+    const bool have = c0 + tid < nch;
+    const int2 mine = have ? ccnt[tid] : make_int2(0, 0);
+    int tg, te;
+    const int pg = block_exclusive_scan(mine.x, tmp, kPlanT, &tg);
+    __syncthreads();
+    const int pe = block_exclusive_scan(mine.y, tmp, kPlanT, &te);
+    if (have) chunk_all[b * nch + c0 + tid] = make_int2(carry_gt + pg, carry_eq + pe);
+    carry_gt += tg;
+    carry_eq += te;
+    __syncthreads();
+  }
+}
+
+// 1b. grid B x nch: the anchors of one chunk, by a workgroup scan of its
+// keys in token order from the chunk's prefixes (thread t owns 4 tokens)
+__global__ void __launch_bounds__(kPlanT)
+merge_flag_kernel(int N, int k, int nch, const uint32_t* __restrict__ sk_all,
+                  const uint2* __restrict__ sel_all, const int2* __restrict__ chunk_all,
+                  int32_t* __restrict__ apos_all, int32_t* __restrict__ anchors) {
+  static_assert(kMergeSelChunk == kPlanT * 4, "four tokens per thread");
+  __shared__ int tmp[17];
+  const int64_t b = blockIdx.x / nch;
+  const int c = (int)(blockIdx.x - b * nch), tid = threadIdx.x;
+  const uint2 sl = sel_all[b];
+  const uint32_t kth = sl.x, n_eq = sl.y;
+  const int2 pre = chunk_all[b * nch + c];
+  const uint32_t* sk = sk_all + b * N;
+  int32_t* apos = apos_all + b * N;
+  constexpr int R = 4;
+  const int base = c * kMergeSelChunk + tid * R;
+  uint32_t kv[R];
+  int gt_local = 0, eq_local = 0;
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int i = base + r;
+    kv[r] = i < N ? sk[i] : 0u;
+    gt_local += (i < N && kv[r] > kth) ? 1 : 0;
+    eq_local += (i < N && kv[r] == kth) ? 1 : 0;
+  }
+  int tot;
+  const int ex = block_exclusive_scan((gt_local << 16) | eq_local, tmp, kPlanT, &tot);
+  int eq_before = pre.y + (ex & 0xFFFF);
+  int pos = pre.x + (ex >> 16) + min(eq_before, (int)n_eq);
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int i = base + r;
+    if (i < N) {
+      bool an = false;
+      if (kv[r] > kth) an = true;
+      else if (kv[r] == kth) an = (uint32_t)(eq_before++) < n_eq;
+      apos[i] = an ? pos : -1;
+      if (an) anchors[b * k + pos] = i;
+      pos += an ? 1 : 0;
+    }
   }
 }
 
@@ -514,7 +578,8 @@ merge_abucket_place_kernel(const float* __restrict__ coords, int N, int k, int G
 __global__ void __launch_bounds__(kMergeThreads)
 merge_assign_wide_kernel(const float* __restrict__ coords, int N, int k, int G, int64_t n_tok,
                          const int32_t* __restrict__ apos_all, const int32_t* __restrict__ abstart_all,
-                         const uint2* __restrict__ abk_all, int32_t* __restrict__ assign) {
+                         const uint2* __restrict__ abk_all, int32_t* __restrict__ assign,
+                         int32_t* __restrict__ gcnt) {
   const int64_t t = ((int64_t)blockIdx.x * kMergeThreads + threadIdx.x) / kRingLanes;
   const int u = threadIdx.x % kRingLanes;
   if (t >= n_tok) return;
@@ -571,16 +636,10 @@ merge_assign_wide_kernel(const float* __restrict__ coords, int N, int k, int G, 
     }
     a = (int)(best & ((1ull << kWideKeyBits) - 1));
   }
-  if (u == 0) assign[t] = a;
-}
-
-__global__ void __launch_bounds__(kMergeThreads)
-merge_gcount_kernel(int N, int k, int64_t n_tok, const int32_t* __restrict__ assign,
-                    int32_t* __restrict__ gcnt) {
-  const int64_t t = (int64_t)blockIdx.x * kMergeThreads + threadIdx.x;
-  if (t >= n_tok) return;
-  const int64_t b = t / N;
-  atomicAdd(&gcnt[b * k + assign[t]], 1);
+  if (u == 0) {
+    assign[t] = a;
+    atomicAdd(&gcnt[b * k + a], 1);   // group sizes (integer atomics: any order)
+  }
 }
 
 __global__ void __launch_bounds__(kMergeThreads)
@@ -859,11 +918,14 @@ hipError_t launch_merge_plan(const float* coords, const float* scores, int B, in
   }
   const MergeWorkspace w = merge_layout(ws, B, N, k);
   const MergeBuckets mb = merge_buckets(k);
+  const int nch = (N + kMergeSelChunk - 1) / kMergeSelChunk;
   const int64_t n_tok = (int64_t)B * N, n_anc = (int64_t)B * k;
   auto grid = [](int64_t n) { return dim3((unsigned)((n + kMergeThreads - 1) / kMergeThreads)); };
-  hipLaunchKernelGGL(merge_select_kernel, dim3(B), dim3(kPlanT), 0, st, scores, N, k, w.sk, w.apos,
+  hipLaunchKernelGGL(merge_select_kernel, dim3(B), dim3(kPlanT), 0, st, scores, N, k, mb.nb, nch,
+                     w.sk, w.sel, w.chunk, w.abcnt, w.gcnt, w.gcur);
+  hipLaunchKernelGGL(merge_flag_kernel, dim3((unsigned)(B * nch)), dim3(kPlanT), 0, st, N, k, nch,
+                     (const uint32_t*)w.sk, (const uint2*)w.sel, (const int2*)w.chunk, w.apos,
                      anchors);
-  launch_zero_i32((int64_t)B * mb.nb, w.abcnt, st);
   hipLaunchKernelGGL(merge_abucket_count_kernel, grid(n_anc), dim3(kMergeThreads), 0, st, coords, N,
                      k, G, n_anc, (const int32_t*)anchors, w.abcnt, w.abrank);
   launch_segment_scan(B, mb.nb, w.abcnt, w.abstart, st);
@@ -872,14 +934,10 @@ hipError_t launch_merge_plan(const float* coords, const float* scores, int B, in
                      (const int32_t*)w.abrank, w.abk);
   hipLaunchKernelGGL(merge_assign_wide_kernel, grid(n_tok * kRingLanes), dim3(kMergeThreads), 0, st,
                      coords, N, k, G, n_tok, (const int32_t*)w.apos, (const int32_t*)w.abstart,
-                     (const uint2*)w.abk, assign);
-  launch_zero_i32(n_anc, w.gcnt, st);
-  hipLaunchKernelGGL(merge_gcount_kernel, grid(n_tok), dim3(kMergeThreads), 0, st, N, k, n_tok,
-                     (const int32_t*)assign, w.gcnt);
+                     (const uint2*)w.abk, assign, w.gcnt);
   launch_segment_scan(B, k, w.gcnt, offsets, st);
-  launch_zero_i32(n_anc, w.gcnt, st);
   hipLaunchKernelGGL(merge_gplace_kernel, grid(n_tok), dim3(kMergeThreads), 0, st, N, k, n_tok,
-                     (const int32_t*)assign, (const int32_t*)offsets, w.gcnt, w.glst);
+                     (const int32_t*)assign, (const int32_t*)offsets, w.gcur, w.glst);
   hipLaunchKernelGGL(merge_grank_kernel, grid(n_tok), dim3(kMergeThreads), 0, st, N, k, n_tok,
                      (const int32_t*)assign, (const int32_t*)offsets, (const int32_t*)w.glst,
                      members);
