@@ -275,18 +275,21 @@ KERNEL_SOURCES = ("attn_mfma.hip", "attn_valu.hip", "mfma_util.h", "common.h", "
                   "neighbors.hip")
 
 
-def kernel_source_hash() -> str:
+SAMPLER_SOURCES = ("knn_sampler.hip", "scan.hip", "common.h")
+
+
+def kernel_source_hash(files=KERNEL_SOURCES) -> str:
     import hashlib
     h = hashlib.sha256()
     d = os.path.join(ROOT, "gathered_local_attention_amd", "csrc")
-    for name in KERNEL_SOURCES:
+    for name in files:
         h.update(name.encode())
         with open(os.path.join(d, name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()
 
 
-def counter_summary(config: str):
+def counter_summary(config: str, files=KERNEL_SOURCES):
     """The committed rocprofv3 summary of a configuration
     (profiles/<config>_hbm_traffic.json or _counters.json) if it was taken on
     the current kernel sources (same hash), else None."""
@@ -295,15 +298,15 @@ def counter_summary(config: str):
         if os.path.exists(path):
             with open(path) as f:
                 rec = json.load(f)
-            if rec.get("source_sha256") == kernel_source_hash():
+            if rec.get("source_sha256") == kernel_source_hash(files):
                 return rec
     return None
 
 
-def measured_traffic(config: str, entry: str):
+def measured_traffic(config: str, entry: str, files=KERNEL_SOURCES):
     """HBM bytes per launch of an entry point from FETCH_SIZE / WRITE_SIZE
     (calibrated against the copy kernel) in the committed summary, or None."""
-    rec = counter_summary(config)
+    rec = counter_summary(config, files)
     e = None if rec is None else rec.get("entries", {}).get(entry)
     return None if e is None else e["traffic_bytes"]
 
@@ -843,7 +846,7 @@ def bench_sampler(args, torch, ca):
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBPS,
-            "traffic": None,
+            "traffic": measured_traffic(cfg.name, dom, SAMPLER_SOURCES),
             "algorithmic_bytes": alg[dom],
             "avg_us": dur[dom],
         },
