@@ -244,6 +244,15 @@ static inline KnnTableWorkspace knn_table_layout(void* base, int64_t B, int64_t 
 // partition counts (pcnt); larger ones place them by per-token cursors into
 // lst, rank them inside each token's segment, and bucket the tokens for the
 // walk order (the table build's bucket arrays).
+// Images above kKnnSmallTokens tokens build the token lists by cursors and
+// ranks; smaller ones by the partitioned counting sort (its counts [B, P, N],
+// P = M K / kKnnPart, hold at most N / kKnnPart <= 16 ints per entry).
+__host__ __device__ inline bool knn_large_lists(int64_t N, int64_t M, int64_t K) {
+  (void)M;
+  (void)K;
+  return N > kKnnSmallTokens;
+}
+
 struct KnnWorkspace {
   int32_t* cnt;     // [B, N]        entries per token (then cursors, large images)
   int32_t* off;     // [B, N + 1]    segment starts (per image, relative)
@@ -267,7 +276,7 @@ static inline KnnWorkspace knn_layout(void* base, int64_t B, int64_t N, int64_t 
     p = align_up(p + n, 256);
     return b ? (void*)(b + at) : (void*)nullptr;
   };
-  const bool large = N > kKnnSmallTokens;
+  const bool large = knn_large_lists(N, M, K);
   w.cnt = (int32_t*)take((size_t)(B * N) * 4);
   w.off = (int32_t*)take((size_t)(B * (N + 1)) * 4);
   const int64_t P = (M * K + kKnnPart - 1) / kKnnPart;
@@ -278,9 +287,14 @@ static inline KnnWorkspace knn_layout(void* base, int64_t B, int64_t N, int64_t 
   w.ent = (int2*)take((size_t)(B * M * K) * 8);
   w.dpart = (float*)take((size_t)(B * M) * 4);
   w.order = (int32_t*)take((size_t)(B * N) * 4);
-  const KnnTableWorkspace tb = knn_table_layout(nullptr, B, N);
-  char* tb_base = (char*)take(tb.bytes);
-  w.bk = knn_table_layout(b ? tb_base : nullptr, B, N);
+  // large lists: bucket arrays for the walk order (sized as the table
+  // build's for an image above kKnnSmallTokens tokens)
+  const int64_t nbk = large ? knn_max_buckets(N) : 0;
+  w.bk.bcnt = (int32_t*)take((size_t)(B * nbk) * 4);
+  w.bk.bstart = (int32_t*)take(large ? (size_t)(B * (nbk + 1)) * 4 : 0);
+  w.bk.brank = (int32_t*)take(large ? (size_t)(B * N) * 4 : 0);
+  w.bk.tok = nullptr;
+  w.bk.bytes = 0;
   w.bytes = p;
   return w;
 }

@@ -784,24 +784,46 @@ knn_pcount_kernel(int N, int G, int64_t MK, int P, int64_t nparts, const int32_t
 // entry placed at segment start + the partition's prefix + the number of
 // earlier entries of the same token in the partition.
 
-__global__ void __launch_bounds__(kKnnThreads)
-knn_pprefix_kernel(int N, int P, int64_t n_tok, int32_t* __restrict__ pcnt, int32_t* __restrict__ cnt) {
-  const int64_t x = (int64_t)blockIdx.x * kKnnThreads + threadIdx.x;
-  if (x >= n_tok) return;
-  const int64_t b = x / N;
-  const int t = (int)(x - b * N);
+// Per token, the partition counts turned into exclusive prefixes over the
+// partitions, and the token's total.  Workgroup = 64 consecutive tokens of
+// one image (lane = token: coalesced rows of the counts); its kPrefWaves
+// waves split the partitions into contiguous ranges, sum them, exchange the
+// range sums through LDS, and rewrite their ranges as running prefixes.
+constexpr int kPrefWaves = 16;
+__global__ void __launch_bounds__(64 * kPrefWaves)
+knn_pprefix_kernel(int N, int P, int tgroups, int32_t* __restrict__ pcnt,
+                   int32_t* __restrict__ cnt) {
+  __shared__ int part[kPrefWaves][64];
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int64_t b = blockIdx.x / tgroups;
+  const int t = (int)(blockIdx.x - b * tgroups) * 64 + lane;
+  const bool live = t < N;
+  const int per = (P + kPrefWaves - 1) / kPrefWaves;
+  const int s0 = wv * per, s1 = min(P, s0 + per);
+  int32_t* col = pcnt + b * P * N + (live ? t : 0);
+  int sum = 0;
+  for (int s = s0; s < s1; s += 8) {   // eight loads in flight
+    int v[8];
+#pragma unroll
+    for (int h = 0; h < 8; ++h) v[h] = (live && s + h < s1) ? col[(int64_t)(s + h) * N] : 0;
+#pragma unroll
+    for (int h = 0; h < 8; ++h) sum += v[h];
+  }
+  part[wv][lane] = sum;
+  __syncthreads();
   int acc = 0;
-  for (int s0 = 0; s0 < P; s0 += 16) {   // sixteen loads in flight
-    int v[16];
+  for (int w = 0; w < wv; ++w) acc += part[w][lane];
+  if (wv == kPrefWaves - 1 && live) cnt[b * N + t] = acc + sum;
+  for (int s = s0; s < s1; s += 8) {
+    int v[8];
 #pragma unroll
-    for (int h = 0; h < 16; ++h) v[h] = s0 + h < P ? pcnt[(b * P + s0 + h) * N + t] : 0;
+    for (int h = 0; h < 8; ++h) v[h] = (live && s + h < s1) ? col[(int64_t)(s + h) * N] : 0;
 #pragma unroll
-    for (int h = 0; h < 16; ++h) {
-      if (s0 + h < P) pcnt[(b * P + s0 + h) * N + t] = acc;
+    for (int h = 0; h < 8; ++h) {
+      if (live && s + h < s1) col[(int64_t)(s + h) * N] = acc;
       acc += v[h];
     }
   }
-  cnt[x] = acc;
 }
 
 // one workgroup per partition; wave w ranks the partition's entries
@@ -1074,7 +1096,7 @@ hipError_t bwd_t(int B, int N, int M, int Cf, int G, int K, float p, const float
   // small images: counts per partition of kPart entries in LDS, stable
   // counting sort; large ones: per-token counts by integer atomics in the
   // query-major kernel, cursor placement and ranking
-  const bool large = N > kTabMaxTokens;
+  const bool large = knn_large_lists(N, M, K);
   auto go = [&](auto kern) {
     hipLaunchKernelGGL(kern, dim3(blocks_for(nq, qwv)), dim3(kKnnThreads), 0, st, N, M, Cf, G, K,
                        lg, p, nq, qwv, coords, (const T*)feats, queries, table, (const T*)dout, dq,
@@ -1094,8 +1116,9 @@ hipError_t bwd_t(int B, int N, int M, int Cf, int G, int K, float p, const float
       // partition counts, and the walk order in B more workgroups
       hipLaunchKernelGGL(knn_pcount_kernel, dim3((unsigned)(nparts + B)), dim3(kKnnThreads), 0, st,
                          N, G, MK, P, nparts, (const int32_t*)w.slot, coords, w.pcnt, w.order);
-      hipLaunchKernelGGL(knn_pprefix_kernel, grid1(ntok), dim3(kKnnThreads), 0, st, N, P, ntok,
-                         w.pcnt, w.cnt);
+      const int tgroups = (N + 63) / 64;
+      hipLaunchKernelGGL(knn_pprefix_kernel, dim3((unsigned)(B * tgroups)), dim3(64 * kPrefWaves), 0,
+                         st, N, P, tgroups, w.pcnt, w.cnt);
       launch_segment_scan(B, N, w.cnt, w.off, st);
       if (nparts > 0)
         hipLaunchKernelGGL(knn_pplace_kernel, dim3((unsigned)nparts), dim3(kKnnThreads), 0, st, N,
