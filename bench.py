@@ -276,6 +276,7 @@ KERNEL_SOURCES = ("attn_mfma.hip", "attn_valu.hip", "mfma_util.h", "common.h", "
 
 
 SAMPLER_SOURCES = ("knn_sampler.hip", "scan.hip", "common.h")
+MERGE_SOURCES = ("token_merge.hip", "scan.hip", "common.h")
 
 
 def kernel_source_hash(files=KERNEL_SOURCES) -> str:
@@ -998,7 +999,7 @@ def bench_merge(args, torch, ca):
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBPS,
-            "traffic": None,
+            "traffic": measured_traffic(cfg.name, dom, MERGE_SOURCES),
             "algorithmic_bytes": alg[dom],
             "avg_us": dur[dom],
         },
