@@ -117,6 +117,44 @@ def test_table_edge_shapes(ca, G, K, N):
         assert np.array_equal(table[b], ref), f"image {b}"
 
 
+@pytest.mark.parametrize("dtype,N,C,K,M", [(torch.float32, 100, 128, 16, 300),
+                                           (torch.float16, 300, 64, 4, 129),
+                                           (torch.bfloat16, 180, 128, 8, 1),
+                                           (torch.bfloat16, 7, 256, 8, 500)])
+def test_small_images_all_dtypes(ca, dtype, N, C, K, M):
+    """Small images in every element type: f32 / f16 / bf16, K = 4, 8, 16,
+    rows of 128 to 512 bytes, a query count that fills no whole wave, a
+    single query, fewer tokens than slots."""
+    G, p = 24, 0.9
+    rng = np.random.default_rng(N * 7 + C + K)
+    B = 2
+    pts = rng.uniform(-0.5, G - 0.5, size=(B, N, 2)).astype(np.float32)
+    q = rng.uniform(-2.0, G + 1.0, size=(B, M, 2)).astype(np.float32)
+    F = torch.from_numpy(rng.standard_normal((B, N, C)).astype(np.float32)).to(dtype)
+    dO = torch.from_numpy(rng.standard_normal((B, M, C)).astype(np.float32)).to(dtype)
+    print(f"case few-token images dtype={dtype} N={N} C={C} K={K} M={M}", flush=True)
+    dc = torch.from_numpy(pts).to(DEV)
+    dq_in = torch.from_numpy(q).to(DEV)
+    table = ca.knn_table(dc, G, K)
+    out = ca.knn_sample_fwd(F.to(DEV), dc, dq_in, table, p)
+    dF, dqg, dp = ca.knn_sample_bwd(F.to(DEV), dc, dq_in, table, p, dO.to(DEV))
+    torch.cuda.synchronize()
+    F64, dO64 = F.double().numpy(), dO.double().numpy()
+    dp_ref = 0.0
+    for b in range(B):
+        t_ref = O.knn_table(pts[b], G, K)
+        assert np.array_equal(table[b].cpu().numpy(), t_ref)
+        o_ref = O.knn_sample_fwd(pts[b], F64[b], q[b], t_ref, p)
+        _check(f"b{b} out", out[b].double().cpu().numpy(), o_ref, _bar(dtype, o_ref))
+        dF_ref, dq_ref, dp_b = O.knn_sample_bwd(pts[b], F64[b], q[b], t_ref, p, dO64[b])
+        dp_ref += dp_b
+        _check(f"b{b} dF", dF[b].double().cpu().numpy(), dF_ref, _bar(dtype, dF_ref))
+        sc = max(1.0, float(np.abs(dq_ref).max()))
+        _check(f"b{b} dq", dqg[b].double().cpu().numpy(), dq_ref, 2e-4 * sc + 1e-3 * np.abs(dq_ref))
+    _check("dp", np.array([float(dp.item())]), np.array([dp_ref]),
+           np.array([1e-4 * max(1.0, abs(dp_ref)) + 1e-4 * np.sqrt(B * M * K)]))
+
+
 def test_empty_token_set_and_far_queries(ca):
     """No tokens: zero output and zero gradients; queries far outside the
     grid use the clamped edge cells."""
