@@ -31,26 +31,30 @@
 //   knn_bucket_count/place, knn_table_search_kernel  the same for images
 //                         above 4096 tokens, with the buckets in global
 //                         memory (bucketed once per image).
-//   knn_fwd_kernel        a group of lanes per query, 16 bytes of the
-//                         feature row per lane: cell, slots, distances and
-//                         weights (computed redundantly by the group's lanes),
-//                         then the weighted sum of the K gathered rows.
-//   knn_bwd_query_kernel  the same groups: weights again, <dO, F_k> reduced
-//                         over the group, dq and the query's share of dp;
-//                         slots and weights kept for the feature gradient
-//                         and references counted per token.
-//   knn_pprefix/scan/pplace  token-major entry lists (entry =
-//                         query * K + slot) by a stable counting sort over
-//                         partitions of the entries: each token's segment is
-//                         in entry order, so the feature gradient is summed
-//                         in a fixed order.  Images above 4096 tokens:
-//                         knn_lplace/lrank (cursor placement, then each
-//                         entry's rank in its segment: the same lists).
+//   knn_fwd_kernel        a wave serves a run of queries: one lane per
+//                         query works out the cell, slots, distances and
+//                         weights into LDS, then lane groups (16 bytes of
+//                         the feature row per lane) sum the K gathered rows.
+//   knn_bwd_query_kernel  the same waves: weights again, <dO, F_k> by
+//                         bf16/fp16 dot-2 instructions reduced over the
+//                         group, dq and the wave's share of dp; slots and
+//                         weights kept for the feature gradient (and, for
+//                         images above 4096 tokens, references counted per
+//                         token).
+//   knn_pcount/pprefix/scan/pplace  token-major entry lists (entry =
+//                         query * K + slot, stored as its (query, weight)
+//                         pair) by a stable counting sort over partitions of
+//                         the entries: each token's segment is in entry
+//                         order, so the feature gradient is summed in a
+//                         fixed order; the count launch also builds the
+//                         tokens' spatial walk order.  Images above 4096
+//                         tokens: knn_lplace/lrank (cursor placement, then
+//                         each entry's rank in its segment: the same lists).
 //   knn_dfeat_kernel      a lane group per token: dF = sum over its entries
 //                         of w * dO (gathered rows), written once (0 for
 //                         tokens no query reaches).
 //   dp                    fixed-order reduction of the per-wave dp shares,
-//                         by the feature-gradient kernel's last workgroup.
+//                         by the feature-gradient kernel's first workgroup.
 // Nothing in the backward uses floating-point atomics: the results are
 // bitwise reproducible.
 #include "common.h"
