@@ -258,6 +258,7 @@ struct KnnWorkspace {
   int32_t* off;     // [B, N + 1]    segment starts (per image, relative)
   int32_t* pcnt;    // [B, P, N]     per partition of kKnnPart entries: counts, then prefixes
   int32_t* lst;     // [B, M * K]    (large images, same place as pcnt) entries, unranked
+  int32_t* srt;     // [B, M * K]    (large images) sort scratch of the longest segments
   int32_t* slot;    // [B, M, K]     token of every (query, slot), -1 empty
   float* wgt;       // [B, M, K]     its weight
   int2* ent;        // [B, M * K]    (query, weight bits) of the entries, by token
@@ -282,6 +283,7 @@ static inline KnnWorkspace knn_layout(void* base, int64_t B, int64_t N, int64_t 
   const int64_t P = (M * K + kKnnPart - 1) / kKnnPart;
   w.pcnt = (int32_t*)take(large ? (size_t)(B * M * K) * 4 : (size_t)(B * P * N) * 4);
   w.lst = w.pcnt;
+  w.srt = (int32_t*)take(large ? (size_t)(B * M * K) * 4 : 0);
   w.slot = (int32_t*)take((size_t)(B * M * K) * 4);
   w.wgt = (float*)take((size_t)(B * M * K) * 4);
   w.ent = (int2*)take((size_t)(B * M * K) * 8);
@@ -332,6 +334,7 @@ struct MergeWorkspace {
   int32_t* gcnt;    // [B, k]        group sizes
   int32_t* gcur;    // [B, k]        placement cursors
   int32_t* glst;    // [B, N]        members in placement order
+  int32_t* gtmp;    // [B, N]        sort scratch of the largest groups
   size_t bytes;
 };
 
@@ -359,6 +362,7 @@ static inline MergeWorkspace merge_layout(void* base, int64_t B, int64_t N, int6
   w.gcnt = (int32_t*)take((size_t)(B * kk) * 4);
   w.gcur = (int32_t*)take((size_t)(B * kk) * 4);
   w.glst = (int32_t*)take((size_t)(B * n) * 4);
+  w.gtmp = (int32_t*)take((size_t)(B * n) * 4);
   w.bytes = p;
   return w;
 }
@@ -472,6 +476,16 @@ hipError_t launch_bwd_mfma(int pass, int dt, int B, int N, int C, int H, int nk,
 // per segment)
 void launch_zero_i32(int64_t n, int32_t* x, hipStream_t st);
 void launch_segment_scan(int segments, int n, const int32_t* cnt, int32_t* off, hipStream_t st);
+// Segments longer than kLongSegment of a segmented list (B images of S
+// segments; segment s of image b is vals[b * stride + off[b * (S + 1) + s] ..
+// off[... + 1]), values in [0, max_value]) sorted stably by value into out
+// (or, with out2, as (value / K, bits of wgt[b * stride + value]) pairs);
+// tmp: scratch of vals' layout.  Shorter segments are left alone (their
+// rank kernels handle them).
+constexpr int kLongSegment = 1024;
+void launch_long_segment_sort(int B, int S, int64_t stride, int64_t max_value, const int32_t* off,
+                              int32_t* vals, int32_t* tmp, int32_t* out, int2* out2, int K,
+                              const float* wgt, hipStream_t st);
 
 // KNN-cache point sampler (knn_sampler.hip)
 hipError_t launch_knn_table(const float* coords, int B, int N, int G, int K, int32_t* table, void* ws,

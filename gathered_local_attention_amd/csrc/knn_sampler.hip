@@ -866,8 +866,10 @@ knn_pplace_kernel(int N, int K, int64_t MK, int P, const int32_t* __restrict__ e
 // turns the counts into segment starts; (3) every entry takes a place in
 // its token's segment of lst from an integer atomic on the token's cursor
 // (in no fixed order); (4) every entry is moved to segment start + its rank
-// among the segment's entries by entry number.  The lists come out in
-// entry order, as from the stable counting sort of small images.
+// among the segment's entries by entry number (segments longer than
+// kLongSegment are sorted by launch_long_segment_sort instead, bounding the
+// cost).  The lists come out in entry order, as from the stable counting
+// sort of small images.
 __global__ void __launch_bounds__(kKnnThreads)
 knn_lplace_kernel(int N, int64_t MK, int64_t n_ent, const int32_t* __restrict__ ent_slot,
                   const int32_t* __restrict__ off_all, int32_t* __restrict__ cur,
@@ -892,6 +894,7 @@ knn_lrank_kernel(int N, int K, int64_t MK, int64_t n_ent, const int32_t* __restr
   const int64_t b = x / MK;
   const int e = (int)(x - b * MK);
   const int a = off_all[b * (N + 1) + t], z = off_all[b * (N + 1) + t + 1];
+  if (z - a > kLongSegment) return;   // sorted by launch_long_segment_sort
   const int32_t* seg = lst + b * MK;
   int rank = 0, y = a;
   for (; y + 4 <= z; y += 4) {   // four loads in flight
@@ -1134,6 +1137,9 @@ hipError_t bwd_t(int B, int N, int M, int Cf, int G, int K, float p, const float
       if (nent > 0) {
         hipLaunchKernelGGL(knn_lplace_kernel, grid1(nent), dim3(kKnnThreads), 0, st, N, MK, nent,
                            (const int32_t*)w.slot, (const int32_t*)w.off, w.cnt, w.lst);
+        // tokens of more than kLongSegment entries: a stable sort; the rest ranked
+        launch_long_segment_sort(B, N, MK, MK - 1, (const int32_t*)w.off, w.lst, w.srt, nullptr,
+                                 w.ent, K, (const float*)w.wgt, st);
         hipLaunchKernelGGL(knn_lrank_kernel, grid1(nent), dim3(kKnnThreads), 0, st, N, K, MK, nent,
                            (const int32_t*)w.slot, (const float*)w.wgt, (const int32_t*)w.off,
                            (const int32_t*)w.lst, w.ent);

@@ -428,7 +428,8 @@ merge_members_kernel(int N, int k, const int32_t* __restrict__ assign,
 //  4. member lists: group sizes (integer atomics, in the assignment kernel),
 //     offsets by a scan, every
 //     token placed by its group's cursor (in no fixed order), then moved to
-//     group start + its rank by token index inside the group.
+//     group start + its rank by token index inside the group (groups of
+//     more than kLongSegment members sorted by launch_long_segment_sort).
 // Keys (d2 << 24 | anchor position) are exact for k < 2^24.
 // ---------------------------------------------------------------------------
 constexpr int kWideKeyBits = 24;
@@ -664,6 +665,7 @@ merge_grank_kernel(int N, int k, int64_t n_tok, const int32_t* __restrict__ assi
   const int i = (int)(t - b * N);
   const int a = assign[t];
   const int lo = offsets[b * (k + 1) + a], hi = offsets[b * (k + 1) + a + 1];
+  if (hi - lo > kLongSegment) return;   // sorted by launch_long_segment_sort
   const int32_t* seg = glst + b * N;
   int rank = 0, y = lo;
   for (; y + 4 <= hi; y += 4) {   // four loads in flight
@@ -938,6 +940,9 @@ hipError_t launch_merge_plan(const float* coords, const float* scores, int B, in
   launch_segment_scan(B, k, w.gcnt, offsets, st);
   hipLaunchKernelGGL(merge_gplace_kernel, grid(n_tok), dim3(kMergeThreads), 0, st, N, k, n_tok,
                      (const int32_t*)assign, (const int32_t*)offsets, w.gcur, w.glst);
+  // groups of more than kLongSegment members: a stable sort; the rest ranked
+  launch_long_segment_sort(B, k, N, N - 1, offsets, w.glst, w.gtmp, members, nullptr, 0, nullptr,
+                           st);
   hipLaunchKernelGGL(merge_grank_kernel, grid(n_tok), dim3(kMergeThreads), 0, st, N, k, n_tok,
                      (const int32_t*)assign, (const int32_t*)offsets, (const int32_t*)w.glst,
                      members);

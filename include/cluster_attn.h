@@ -374,10 +374,10 @@ size_t cluster_attn_knn_sample_bwd_workspace(int B, int N, int M, int K);
  *           get 0).   dq [B, M, 2] f32 out.   dp: one f32 out (device).
  *   ws      device workspace of cluster_attn_knn_sample_bwd_workspace bytes;
  *           two calls that overlap in time must not share it.
- * Cost: for images above 4096 tokens each (query, slot) entry is ranked
- * against all entries of its token, so the time grows with the square of
- * the most-referenced token's entry count (queries spread over the image
- * give tens to hundreds; all queries on one token would not).
+ * Cost: for images above 4096 tokens the entries of tokens referenced up
+ * to 1024 times are ranked against their token's entries, those of more
+ * referenced tokens radix-sorted (a workgroup per token), so the time stays
+ * near linear in the entry count however the queries concentrate.
  */
 ca_status cluster_attn_knn_sample_bwd(int dt, int B, int N, int M, int C, int grid_side, int K, float p,
                                 const float* coords, const void* feats, const float* queries,
@@ -415,10 +415,9 @@ size_t cluster_attn_merge_plan_workspace(int B, int N, int k);
  *   ws      device workspace of cluster_attn_merge_plan_workspace bytes
  *           (images above 4096 tokens are planned there; NULL when 0); two
  *           calls that overlap in time must not share it.
- * Cost: above 4096 tokens each member is ranked against its whole group,
- * so the time grows with the square of the largest group (a few ms for a
- * single group of 65,536 tokens; degenerate calls such as k = 1 on millions
- * of tokens take far longer).
+ * Cost: above 4096 tokens the members of groups of up to 1024 tokens are
+ * ranked against their group, larger groups are radix-sorted (a workgroup
+ * per group), so the time stays near linear in N for any grouping.
  */
 ca_status cluster_attn_merge_plan(const float* coords, const float* scores, int B, int N, int k,
                                   int grid_side, int32_t* anchors, int32_t* assign,

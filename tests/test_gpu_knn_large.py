@@ -200,3 +200,34 @@ def test_large_backward_uncovered_tokens_get_zero(ca):
     _check("dp", np.array([float(dp.item())]), np.array([dp_ref]),
            np.array([1e-4 * max(1.0, abs(dp_ref)) + 1e-4 * np.sqrt(M * K)]))
     assert int((dF_ref == 0).all(axis=1).sum()) > N - 200
+
+
+def test_large_backward_token_with_thousands_of_entries(ca):
+    """Every query in one corner and K = 16: the corner tokens hold thousands
+    of entries each (their lists go through the stable long-segment sort,
+    the others through the ranking); everything against the oracle."""
+    G, K, C, N, M = 80, 16, 32, 5000, 4000
+    rng = np.random.default_rng(21)
+    pts = rng.uniform(-0.5, G - 0.5, size=(1, N, 2)).astype(np.float32)
+    q = rng.uniform(0, 2.5, size=(1, M, 2)).astype(np.float32)
+    F = rng.standard_normal((1, N, C)).astype(np.float32)
+    dO = rng.standard_normal((1, M, C)).astype(np.float32)
+    dc = torch.from_numpy(pts).to(DEV)
+    table = ca.knn_table(dc, G, K)
+    dF, dq, dp = ca.knn_sample_bwd(torch.from_numpy(F).to(DEV), dc, torch.from_numpy(q).to(DEV),
+                                   table, 1.1, torch.from_numpy(dO).to(DEV))
+    dF2, _, _ = ca.knn_sample_bwd(torch.from_numpy(F).to(DEV), dc, torch.from_numpy(q).to(DEV),
+                                  table, 1.1, torch.from_numpy(dO).to(DEV))
+    torch.cuda.synchronize()
+    assert torch.equal(dF, dF2), "not bitwise repeatable"
+    qi, qj = O.query_cells(q[0], G)
+    t_sp = _sparse_table(pts[0], G, K, qi, qj)
+    counts = np.bincount(t_sp[qi, qj].reshape(-1), minlength=N)
+    print(f"  most entries of one token: {counts.max()}", flush=True)
+    assert counts.max() > 1024
+    dF_ref, dq_ref, dp_ref = O.knn_sample_bwd(pts[0], F[0].astype(np.float64), q[0], t_sp, 1.1,
+                                              dO[0].astype(np.float64))
+    _check("dF", dF[0].double().cpu().numpy(), dF_ref, _bar(torch.float32, dF_ref))
+    _check("dq", dq[0].double().cpu().numpy(), dq_ref, _dq_bar(dq_ref))
+    _check("dp", np.array([float(dp.item())]), np.array([dp_ref]),
+           np.array([1e-4 * max(1.0, abs(dp_ref)) + 1e-4 * np.sqrt(M * K)]))

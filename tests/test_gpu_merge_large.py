@@ -126,12 +126,14 @@ def test_whole_grid_levels(ca, name, li):
 
 @pytest.mark.parametrize("N,k,G,scores", [(20000, 7777, 64, "ties"), (4097, 1, 64, "normal"),
                                          (5000, 5000, 64, "normal"), (9000, 2, 300, "ties"),
-                                         (12000, 4000, 1, "normal")])
+                                         (12000, 4000, 1, "normal"), (70000, 3, 256, "ties")])
 def test_large_plan_edge_cases(ca, N, k, G, scores):
     """Scores with many ties across the select kernel's chunks (part of the
     tied value taken), one anchor (a single group of every token), every
     token an anchor, a grid side that is not a power of two, a one-cell
-    grid (all coordinates quantised onto few points: distance ties)."""
+    grid (all coordinates quantised onto few points: distance ties), and
+    three groups of ~23,000 members (their lists sorted by three radix
+    passes)."""
     rng = np.random.default_rng(N + k + G)
     B, C = 2, 16
     X = rng.uniform(-1.0, G, size=(B, N, 2)).astype(np.float32)
