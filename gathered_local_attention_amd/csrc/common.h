@@ -482,7 +482,7 @@ void launch_segment_scan(int segments, int n, const int32_t* cnt, int32_t* off, 
 // (or, with out2, as (value / K, bits of wgt[b * stride + value]) pairs);
 // tmp: scratch of vals' layout.  Shorter segments are left alone (their
 // rank kernels handle them).
-constexpr int kLongSegment = 1024;
+constexpr int kLongSegment = 256;
 void launch_long_segment_sort(int B, int S, int64_t stride, int64_t max_value, const int32_t* off,
                               int32_t* vals, int32_t* tmp, int32_t* out, int2* out2, int K,
                               const float* wgt, hipStream_t st);

@@ -375,7 +375,7 @@ size_t cluster_attn_knn_sample_bwd_workspace(int B, int N, int M, int K);
  *   ws      device workspace of cluster_attn_knn_sample_bwd_workspace bytes;
  *           two calls that overlap in time must not share it.
  * Cost: for images above 4096 tokens the entries of tokens referenced up
- * to 1024 times are ranked against their token's entries, those of more
+ * to 256 times are ranked against their token's entries, those of more
  * referenced tokens radix-sorted (a workgroup per token), so the time stays
  * near linear in the entry count however the queries concentrate.
  */
@@ -415,7 +415,7 @@ size_t cluster_attn_merge_plan_workspace(int B, int N, int k);
  *   ws      device workspace of cluster_attn_merge_plan_workspace bytes
  *           (images above 4096 tokens are planned there; NULL when 0); two
  *           calls that overlap in time must not share it.
- * Cost: above 4096 tokens the members of groups of up to 1024 tokens are
+ * Cost: above 4096 tokens the members of groups of up to 256 tokens are
  * ranked against their group, larger groups are radix-sorted (a workgroup
  * per group), so the time stays near linear in N for any grouping.
  */
