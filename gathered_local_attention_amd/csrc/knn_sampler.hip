@@ -59,6 +59,8 @@
 // bitwise reproducible.
 #include "common.h"
 
+#include <type_traits>
+
 namespace ca {
 
 namespace {
@@ -480,7 +482,7 @@ __device__ __forceinline__ void wave_slots(int64_t base, int64_t total, int qwv,
   __builtin_amdgcn_wave_barrier();   // one wave: its LDS writes precede its reads
 }
 
-template <typename T, int KM>
+template <typename T, int KM, int NRM>
 __global__ void __launch_bounds__(kKnnThreads)
 knn_fwd_kernel(int N, int M, int Cf, int G, int K, int lg, float p, int64_t total, int qwv,
                const float* __restrict__ coords, const T* __restrict__ feats,
@@ -512,19 +514,21 @@ knn_fwd_kernel(int N, int M, int Cf, int G, int K, int lg, float p, int64_t tota
       sl[k] = sw[wv].slot[u][k];
       wt[k] = sw[wv].w[u][k];
     }
-    // every chunk's rows in flight before the sums: the loads are
-    // unconditional (an empty slot or a chunk past the row reads a valid
-    // place, the data is then masked), so that no branch splits them
-    uint4 raw[Ck::NR][KM];
+    // every chunk's rows in flight before the sums: an empty slot reads a
+    // valid row (masked afterwards); a lane with fewer chunks than NRM skips
+    // the last round's loads
+    uint4 raw[NRM][KM];
     if (N > 0) {
 #pragma unroll
-      for (int r = 0; r < Ck::NR; ++r)
+      for (int r = 0; r < NRM; ++r)
+        if (r < nr) {
 #pragma unroll
-        for (int k = 0; k < KM; ++k)
-          raw[r][k] = Ck::raw(fimg + (int64_t)max(sl[k], 0) * Cf + (cs + (r < nr ? r * L : 0)) * Ck::E);
+          for (int k = 0; k < KM; ++k)
+            raw[r][k] = Ck::raw(fimg + (int64_t)max(sl[k], 0) * Cf + (cs + r * L) * Ck::E);
+        }
     }
 #pragma unroll
-    for (int r = 0; r < Ck::NR; ++r) {
+    for (int r = 0; r < NRM; ++r) {
       if (r >= nr) break;
       float acc[Ck::E];
 #pragma unroll
@@ -549,8 +553,8 @@ knn_fwd_kernel(int N, int M, int Cf, int G, int K, int lg, float p, int64_t tota
 // reduced over the group, into LDS; (3) lane = query again: dq and the
 // query's share of dp.
 // ---------------------------------------------------------------------------
-template <typename T, int KM>
-__global__ void __launch_bounds__(kKnnThreads) __attribute__((amdgpu_waves_per_eu(sizeof(T) == 2 && KM <= 8 ? 4 : 1)))
+template <typename T, int KM, int NRM>
+__global__ void __launch_bounds__(kKnnThreads) __attribute__((amdgpu_waves_per_eu(sizeof(T) == 2 && KM <= 8 ? (NRM == 1 ? 4 : 3) : 1)))
 knn_bwd_query_kernel(int N, int M, int Cf, int G, int K, int lg, float p, int64_t total, int qwv,
                      const float* __restrict__ coords, const T* __restrict__ feats,
                      const float* __restrict__ queries, const int32_t* __restrict__ table,
@@ -593,20 +597,21 @@ knn_bwd_query_kernel(int N, int M, int Cf, int G, int K, int lg, float p, int64_
     float gk[KM];
 #pragma unroll
     for (int k = 0; k < KM; ++k) gk[k] = 0.f;
-    // unconditional loads (see the forward), masked afterwards
-    uint4 raw[Ck::NR][KM], oraw[Ck::NR];
+    // all loads issued before the sums (see the forward), masked afterwards
+    uint4 raw[NRM][KM], oraw[NRM];
     const int64_t oid = live ? id : base;
 #pragma unroll
-    for (int r = 0; r < Ck::NR; ++r) {
-      const int c = cs + (r < nr ? r * L : 0);
-      oraw[r] = Ck::raw(dout + oid * Cf + c * Ck::E);
-      if (N > 0) {
+    for (int r = 0; r < NRM; ++r)
+      if (r < nr) {
+        const int c = cs + r * L;
+        oraw[r] = Ck::raw(dout + oid * Cf + c * Ck::E);
+        if (N > 0) {
 #pragma unroll
-        for (int k = 0; k < KM; ++k) raw[r][k] = Ck::raw(fimg + (int64_t)max(sl[k], 0) * Cf + c * Ck::E);
+          for (int k = 0; k < KM; ++k) raw[r][k] = Ck::raw(fimg + (int64_t)max(sl[k], 0) * Cf + c * Ck::E);
+        }
       }
-    }
 #pragma unroll
-    for (int r = 0; r < Ck::NR; ++r) {
+    for (int r = 0; r < NRM; ++r) {
       if (r >= nr || !live) break;
 #pragma unroll
       for (int k = 0; k < KM; ++k) {
@@ -948,7 +953,7 @@ knn_dp_kernel(int64_t n, const float* __restrict__ dpart, float* __restrict__ dp
 // that the dO rows of the images in flight on an XCD fit its L2.  The first
 // workgroup also sums the dp shares (complete: the query-major kernel has
 // finished).
-template <typename T>
+template <typename T, int NRM>
 __global__ void __launch_bounds__(kKnnThreads)
 knn_dfeat_kernel(int B, int N, int M, int Cf, int64_t MK, int lg, int split, int S,
                  const T* __restrict__ dout, const int32_t* __restrict__ off_all,
@@ -958,7 +963,7 @@ knn_dfeat_kernel(int B, int N, int M, int Cf, int64_t MK, int lg, int split, int
   using Ck = Chunk<T>;
   constexpr int kB = 8;                          // entries (rows) per batch
   constexpr int kW = kKnnThreads / 64;           // waves per workgroup
-  __shared__ float part[kW][Ck::NR * Ck::E][64];
+  __shared__ float part[kW][NRM * Ck::E][64];
   if (blockIdx.x == 0) {
     __shared__ float red[kKnnThreads];
     dp_reduce<kKnnThreads>(n_dp, dpart, dp, red);
@@ -980,9 +985,9 @@ knn_dfeat_kernel(int B, int N, int M, int Cf, int64_t MK, int lg, int split, int
     const int z = live ? off_all[b * (N + 1) + t + 1] : 0;
     const int2* ent = ent_all + b * MK;
     const T* oimg = dout + b * M * Cf;
-    float acc[Ck::NR][Ck::E];
+    float acc[NRM][Ck::E];
 #pragma unroll
-    for (int r = 0; r < Ck::NR; ++r)
+    for (int r = 0; r < NRM; ++r)
 #pragma unroll
       for (int e = 0; e < Ck::E; ++e) acc[r][e] = 0.f;
     int u = a + sw * kB;
@@ -992,20 +997,23 @@ knn_dfeat_kernel(int B, int N, int M, int Cf, int64_t MK, int lg, int split, int
       for (int h = 0; h < kB; ++h) pr[h] = ent[min(u + h, z - 1)];
     }
     while (u < z) {
-      // this batch's rows (unconditional loads of clamped entries, masked
-      // afterwards), then the next batch's pairs (clamped inside the segment)
-      uint4 raw[Ck::NR][kB];
+      // this batch's rows (clamped entries, masked afterwards; a lane with
+      // fewer chunks than NRM skips the last round), then the next batch's
+      // pairs (clamped inside the segment)
+      uint4 raw[NRM][kB];
 #pragma unroll
-      for (int r = 0; r < Ck::NR; ++r)
+      for (int r = 0; r < NRM; ++r)
+        if (r < nr) {
 #pragma unroll
-        for (int h = 0; h < kB; ++h)
-          raw[r][h] = Ck::raw(oimg + (int64_t)pr[h].x * Cf + (cs + (r < nr ? r * L : 0)) * Ck::E);
+          for (int h = 0; h < kB; ++h)
+            raw[r][h] = Ck::raw(oimg + (int64_t)pr[h].x * Cf + (cs + r * L) * Ck::E);
+        }
       const int un = u + split * kB;
       int2 nx[kB];
 #pragma unroll
       for (int h = 0; h < kB; ++h) nx[h] = ent[min(un + h, z - 1)];
 #pragma unroll
-      for (int r = 0; r < Ck::NR; ++r) {
+      for (int r = 0; r < NRM; ++r) {
         if (r >= nr) break;
 #pragma unroll
         for (int h = 0; h < kB; ++h) {
@@ -1025,7 +1033,7 @@ knn_dfeat_kernel(int B, int N, int M, int Cf, int64_t MK, int lg, int split, int
     if (split > 1) {
       if (sw > 0) {
 #pragma unroll
-        for (int r = 0; r < Ck::NR; ++r)
+        for (int r = 0; r < NRM; ++r)
 #pragma unroll
           for (int q = 0; q < Ck::E; ++q) part[wv][r * Ck::E + q][lane] = acc[r][q];
       }
@@ -1033,7 +1041,7 @@ knn_dfeat_kernel(int B, int N, int M, int Cf, int64_t MK, int lg, int split, int
       if (sw == 0) {
         for (int v2 = 1; v2 < split; ++v2)
 #pragma unroll
-          for (int r = 0; r < Ck::NR; ++r)
+          for (int r = 0; r < NRM; ++r)
 #pragma unroll
             for (int q = 0; q < Ck::E; ++q) acc[r][q] += part[wv + v2][r * Ck::E + q][lane];
       }
@@ -1041,7 +1049,7 @@ knn_dfeat_kernel(int B, int N, int M, int Cf, int64_t MK, int lg, int split, int
     }
     if (sw == 0 && live) {
 #pragma unroll
-      for (int r = 0; r < Ck::NR; ++r) {
+      for (int r = 0; r < NRM; ++r) {
         if (r >= nr) break;
         Ck::store(dfeat + (b * N + t) * Cf + (cs + r * L) * Ck::E, acc[r]);
       }
@@ -1054,6 +1062,18 @@ int group_log2(int Cf, int E) {
   int lg = 0;
   while ((1 << lg) < nch && lg < 6) ++lg;
   return lg;
+}
+
+// Chunks of 16 bytes per lane at most (lane groups of 2^lg lanes)
+int chunks_per_lane(int Cf, int E, int lg) { return (Cf / E + (1 << lg) - 1) >> lg; }
+
+// Kernel instance by the chunks a lane holds at most: 1, 2, or Chunk<T>::NR
+// (4 for fp32 rows) for anything longer.
+template <typename T, typename F>
+void with_chunks(int nrm, F&& f) {
+  if (nrm <= 1) f(std::integral_constant<int, 1>{});
+  else if (nrm <= 2) f(std::integral_constant<int, 2>{});
+  else f(std::integral_constant<int, Chunk<T>::NR>{});
 }
 
 // Queries per wave of the forward and the query-major backward: eight
@@ -1083,9 +1103,12 @@ hipError_t fwd_t(int B, int N, int M, int Cf, int G, int K, float p, const float
     hipLaunchKernelGGL(kern, grid, dim3(kKnnThreads), 0, st, N, M, Cf, G, K, lg, p, total, qwv,
                        coords, (const T*)feats, queries, table, (T*)out);
   };
-  if (K <= 4) go(knn_fwd_kernel<T, 4>);
-  else if (K <= 8) go(knn_fwd_kernel<T, 8>);
-  else go(knn_fwd_kernel<T, 16>);
+  with_chunks<T>(chunks_per_lane(Cf, Chunk<T>::E, lg), [&](auto nrm) {
+    constexpr int R = decltype(nrm)::value;
+    if (K <= 4) go(knn_fwd_kernel<T, 4, R>);
+    else if (K <= 8) go(knn_fwd_kernel<T, 8, R>);
+    else go(knn_fwd_kernel<T, 16, R>);
+  });
   return hipGetLastError();
 }
 
@@ -1112,10 +1135,14 @@ hipError_t bwd_t(int B, int N, int M, int Cf, int G, int K, float p, const float
   // empty sizes launch nothing but what writes outputs (dF, dp)
   if (large && ntok > 0)
     launch_zero_i32(ntok, w.cnt, st);
+  const int nrm = chunks_per_lane(Cf, Chunk<T>::E, lg);
   if (nq > 0) {
-    if (K <= 4) go(knn_bwd_query_kernel<T, 4>);
-    else if (K <= 8) go(knn_bwd_query_kernel<T, 8>);
-    else go(knn_bwd_query_kernel<T, 16>);
+    with_chunks<T>(nrm, [&](auto nr) {
+      constexpr int R = decltype(nr)::value;
+      if (K <= 4) go(knn_bwd_query_kernel<T, 4, R>);
+      else if (K <= 8) go(knn_bwd_query_kernel<T, 8, R>);
+      else go(knn_bwd_query_kernel<T, 16, R>);
+    });
   }
   const int64_t n_dp = nq > 0 ? (nq + qwv - 1) / qwv : 0;   // one dp share per wave of the query kernel
   if (ntok > 0) {
@@ -1165,10 +1192,12 @@ hipError_t bwd_t(int B, int N, int M, int Cf, int G, int K, float p, const float
     const int64_t dimg = std::max<int64_t>(1, (int64_t)M * Cf * (int64_t)sizeof(T));
     const int per_xcd = (int)std::max<int64_t>(1, std::min<int64_t>((3 << 20) / dimg, (B + 7) / 8));
     const int S = std::min(B, 8 * per_xcd);
-    hipLaunchKernelGGL(knn_dfeat_kernel<T>, dim3((unsigned)(S * wgs)), dim3(kKnnThreads), 0, st,
-                       B, N, M, Cf, MK, lg, split, S, (const T*)dout, (const int32_t*)w.off,
-                       (const int2*)w.ent, (const int32_t*)w.order, (T*)dfeat, n_dp,
-                       (const float*)w.dpart, dp);
+    with_chunks<T>(nrm, [&](auto nr) {
+      hipLaunchKernelGGL((knn_dfeat_kernel<T, decltype(nr)::value>), dim3((unsigned)(S * wgs)),
+                         dim3(kKnnThreads), 0, st, B, N, M, Cf, MK, lg, split, S, (const T*)dout,
+                         (const int32_t*)w.off, (const int2*)w.ent, (const int32_t*)w.order,
+                         (T*)dfeat, n_dp, (const float*)w.dpart, dp);
+    });
   } else {
     hipLaunchKernelGGL(knn_dp_kernel, dim3(1), dim3(1024), 0, st, n_dp, (const float*)w.dpart, dp);
   }
