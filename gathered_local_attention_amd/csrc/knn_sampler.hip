@@ -352,7 +352,7 @@ struct Chunk;
 template <>
 struct Chunk<float> {
   static constexpr int E = 4;
-  static constexpr int NR = 4;   // chunks per lane at most (1024 channels)
+  static constexpr int NR = 4;   // chunks per lane at most
   __device__ static uint4 raw(const float* p) { return *reinterpret_cast<const uint4*>(p); }
   __device__ static void cvt(uint4 a, float* v) {
     v[0] = __uint_as_float(a.x); v[1] = __uint_as_float(a.y);
@@ -392,7 +392,7 @@ typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 template <typename H, typename V>
 struct HalfChunk {
   static constexpr int E = 8;
-  static constexpr int NR = 2;   // chunks per lane at most (1024 channels)
+  static constexpr int NR = 3;   // chunks per lane at most
   __device__ static uint4 raw(const H* p) { return *reinterpret_cast<const uint4*>(p); }
   __device__ static void cvt(uint4 a, float* v) {
     const f32x8 f = __builtin_convertvector(__builtin_bit_cast(V, a), f32x8);
@@ -554,7 +554,7 @@ knn_fwd_kernel(int N, int M, int Cf, int G, int K, int lg, float p, int64_t tota
 // query's share of dp.
 // ---------------------------------------------------------------------------
 template <typename T, int KM, int NRM>
-__global__ void __launch_bounds__(kKnnThreads) __attribute__((amdgpu_waves_per_eu(sizeof(T) == 2 && KM <= 8 ? (NRM == 1 ? 4 : 3) : 1)))
+__global__ void __launch_bounds__(kKnnThreads) __attribute__((amdgpu_waves_per_eu(sizeof(T) == 2 && KM <= 8 ? (NRM == 1 ? 4 : NRM == 2 ? 3 : 2) : 1)))
 knn_bwd_query_kernel(int N, int M, int Cf, int G, int K, int lg, float p, int64_t total, int qwv,
                      const float* __restrict__ coords, const T* __restrict__ feats,
                      const float* __restrict__ queries, const int32_t* __restrict__ table,
@@ -1057,23 +1057,41 @@ knn_dfeat_kernel(int B, int N, int M, int Cf, int64_t MK, int lg, int split, int
   }
 }
 
-int group_log2(int Cf, int E) {
+// Lane-group width 2^lg for rows of Cf / E chunks: the width whose
+// rounds (chunks per lane, at most maxr) leave the fewest lanes idle, the
+// wider one on ties (e.g. 96 chunks: 32 lanes x 3, not 64 lanes x 2 with
+// half the lanes idle in the second round).
+int group_log2(int Cf, int E, int maxr) {
   const int nch = Cf / E;
-  int lg = 0;
-  while ((1 << lg) < nch && lg < 6) ++lg;
-  return lg;
+  int best = 6;
+  int64_t bn = 0, bd = 1;   // best utilisation nch / (L r), as a fraction
+  for (int lg = 6; lg >= 0; --lg) {
+    const int L = 1 << lg, r = (nch + L - 1) / L;
+    if (r > maxr) break;
+    if ((int64_t)nch * bd > bn * (int64_t)(L * r)) {
+      bn = nch;
+      bd = (int64_t)L * r;
+      best = lg;
+    }
+  }
+  return best;
 }
 
 // Chunks of 16 bytes per lane at most (lane groups of 2^lg lanes)
 int chunks_per_lane(int Cf, int E, int lg) { return (Cf / E + (1 << lg) - 1) >> lg; }
 
-// Kernel instance by the chunks a lane holds at most: 1, 2, or Chunk<T>::NR
-// (4 for fp32 rows) for anything longer.
+// Lane-group width of a row type: at most Chunk<T>::NR chunks per lane
+template <typename T>
+int row_group_log2(int Cf) { return group_log2(Cf, Chunk<T>::E, Chunk<T>::NR); }
+
+// Kernel instance by the chunks a lane holds at most (1 .. Chunk<T>::NR)
 template <typename T, typename F>
 void with_chunks(int nrm, F&& f) {
   if (nrm <= 1) f(std::integral_constant<int, 1>{});
   else if (nrm <= 2) f(std::integral_constant<int, 2>{});
-  else f(std::integral_constant<int, Chunk<T>::NR>{});
+  else if constexpr (Chunk<T>::NR == 3) f(std::integral_constant<int, 3>{});
+  else if (nrm <= 3) f(std::integral_constant<int, 3>{});
+  else f(std::integral_constant<int, 4>{});
 }
 
 // Queries per wave of the forward and the query-major backward: eight
@@ -1095,7 +1113,7 @@ template <typename T>
 hipError_t fwd_t(int B, int N, int M, int Cf, int G, int K, float p, const float* coords,
                  const void* feats, const float* queries, const int32_t* table, void* out,
                  hipStream_t st) {
-  const int lg = group_log2(Cf, Chunk<T>::E);
+  const int lg = row_group_log2<T>(Cf);
   const int64_t total = (int64_t)B * M;
   const int qwv = queries_per_wave(lg);
   const dim3 grid = dim3(blocks_for(total, qwv));
@@ -1116,7 +1134,7 @@ template <typename T>
 hipError_t bwd_t(int B, int N, int M, int Cf, int G, int K, float p, const float* coords,
                  const void* feats, const float* queries, const int32_t* table, const void* dout,
                  void* dfeat, float* dq, float* dp, const KnnWorkspace& w, hipStream_t st) {
-  const int lg = group_log2(Cf, Chunk<T>::E);
+  const int lg = row_group_log2<T>(Cf);
   const int64_t nq = (int64_t)B * M, ntok = (int64_t)B * N, nent = nq * K;
   auto grid1 = [](int64_t n) { return dim3((unsigned)((n + kKnnThreads - 1) / kKnnThreads)); };
   const int64_t MK = (int64_t)M * K;
