@@ -954,14 +954,17 @@ knn_dp_kernel(int64_t n, const float* __restrict__ dpart, float* __restrict__ dp
 // workgroup also sums the dp shares (complete: the query-major kernel has
 // finished).
 template <typename T, int NRM>
-__global__ void __launch_bounds__(kKnnThreads)
+__global__ void __launch_bounds__(kKnnThreads) __attribute__((amdgpu_waves_per_eu(NRM == 1 ? 8 : 1)))
 knn_dfeat_kernel(int B, int N, int M, int Cf, int64_t MK, int lg, int split, int S,
                  const T* __restrict__ dout, const int32_t* __restrict__ off_all,
                  const int2* __restrict__ ent_all, const int32_t* __restrict__ order,
                  T* __restrict__ dfeat, int64_t n_dp, const float* __restrict__ dpart,
                  float* __restrict__ dp) {
   using Ck = Chunk<T>;
-  constexpr int kB = 8;                          // entries (rows) per batch
+  // entries (rows) per batch: four for one-chunk rows, which keeps the
+  // kernel within 64 registers (eight waves per SIMD hide the dependent
+  // order -> offsets -> pairs -> rows chain of the short token lists)
+  constexpr int kB = NRM == 1 ? 4 : 8;
   constexpr int kW = kKnnThreads / 64;           // waves per workgroup
   __shared__ float part[kW][NRM * Ck::E][64];
   if (blockIdx.x == 0) {
