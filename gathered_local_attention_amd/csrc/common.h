@@ -178,7 +178,7 @@ static inline BuildWorkspace build_layout(void* base, int64_t B, int64_t T, int6
 }
 
 // ---- spatial buckets of the KNN sampler -----------------------------------
-constexpr int kKnnPart = 256;          // entries per partition of the stable counting sort
+constexpr int kKnnPart = 2048;         // entries per partition of the stable counting sort
 constexpr int kKnnSmallTokens = 4096;  // images up to this many tokens are bucketed in LDS
 
 __host__ __device__ inline int knn_ceil_log2(int v) {
@@ -246,7 +246,7 @@ static inline KnnTableWorkspace knn_table_layout(void* base, int64_t B, int64_t 
 // walk order (the table build's bucket arrays).
 // Images above kKnnSmallTokens tokens build the token lists by cursors and
 // ranks; smaller ones by the partitioned counting sort (its counts [B, P, N],
-// P = M K / kKnnPart, hold at most N / kKnnPart <= 16 ints per entry).
+// P = M K / kKnnPart, hold at most N / kKnnPart <= 2 ints per entry).
 __host__ __device__ inline bool knn_large_lists(int64_t N, int64_t M, int64_t K) {
   (void)M;
   (void)K;

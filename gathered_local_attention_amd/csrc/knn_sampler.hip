@@ -33,8 +33,10 @@
 //                         memory (bucketed once per image).
 //   knn_fwd_kernel        a wave serves a run of queries: one lane per
 //                         query works out the cell, slots, distances and
-//                         weights into LDS, then lane groups (16 bytes of
-//                         the feature row per lane) sum the K gathered rows.
+//                         weights into LDS, then lane groups sum the K
+//                         gathered rows, each lane the 16-byte chunks it
+//                         owns (group width: the one leaving the fewest
+//                         lanes idle, up to 3 chunks per lane for bf16/f16).
 //   knn_bwd_query_kernel  the same waves: weights again, <dO, F_k> by
 //                         bf16/fp16 dot-2 instructions reduced over the
 //                         group, dq and the wave's share of dp; slots and
@@ -44,9 +46,11 @@
 //   knn_pcount/pprefix/scan/pplace  token-major entry lists (entry =
 //                         query * K + slot, stored as its (query, weight)
 //                         pair) by a stable counting sort over partitions of
-//                         the entries: each token's segment is in entry
-//                         order, so the feature gradient is summed in a
-//                         fixed order; the count launch also builds the
+//                         2048 entries (ranks inside a partition: per-wave
+//                         counts, then ballot matching of equal tokens in
+//                         each 64-entry batch): each token's segment is in
+//                         entry order, so the feature gradient is summed in
+//                         a fixed order; the count launch also builds the
 //                         tokens' spatial walk order.  Images above 4096
 //                         tokens: knn_lplace/lrank (cursor placement, then
 //                         each entry's rank in its segment: the same lists).
@@ -700,8 +704,9 @@ knn_bwd_query_kernel(int N, int M, int Cf, int G, int K, int lg, float p, int64_
 // the waves resident at one time work on neighbouring tokens, which share
 // most of their queries (and so the dO rows they gather stay in L2).  Any
 // order gives the same result: each token's sum has its own fixed order.
-// One workgroup of kKnnThreads per image of at most kTabMaxTokens tokens;
-// start holds kTabMaxBuckets ints of LDS.
+// One workgroup of NT threads per image of at most kTabMaxTokens tokens;
+// start holds kTabMaxBuckets ints of LDS, tmp 17.
+template <int NT>
 __device__ __forceinline__ void order_image(const float* __restrict__ coords, int N, int G, int64_t b,
                                             int* start, int* tmp, int32_t* __restrict__ order) {
   const int tid = threadIdx.x;
@@ -709,13 +714,13 @@ __device__ __forceinline__ void order_image(const float* __restrict__ coords, in
   const double step = (double)(1 << bg.shift);
   const int bs = bg.bs, Pb = bg.Pb, nb = bg.nb;
   const float2* xy = reinterpret_cast<const float2*>(coords) + b * N;
-  for (int x = tid; x < nb; x += kKnnThreads) start[x] = 0;
+  for (int x = tid; x < nb; x += NT) start[x] = 0;
   __syncthreads();
-  constexpr int kPer = kTabMaxTokens / kKnnThreads;
+  constexpr int kPer = kTabMaxTokens / NT;
   int bk[kPer], rk[kPer];
 #pragma unroll
   for (int r = 0; r < kPer; ++r) {
-    const int e = tid + r * kKnnThreads;
+    const int e = tid + r * NT;
     bk[r] = -1;
     if (e < N) {
       const float2 c = xy[e];
@@ -726,7 +731,7 @@ __device__ __forceinline__ void order_image(const float* __restrict__ coords, in
     }
   }
   __syncthreads();
-  constexpr int kBPer = kTabMaxBuckets / kKnnThreads;
+  constexpr int kBPer = kTabMaxBuckets / NT;
   int cnt[kBPer];
   int run = 0;
 #pragma unroll
@@ -736,7 +741,7 @@ __device__ __forceinline__ void order_image(const float* __restrict__ coords, in
     run += cnt[r];
   }
   int total;
-  int acc = block_exclusive_scan(run, tmp, kKnnThreads, &total);
+  int acc = block_exclusive_scan(run, tmp, NT, &total);
 #pragma unroll
   for (int r = 0; r < kBPer; ++r) {
     const int x = tid * kBPer + r;
@@ -747,40 +752,48 @@ __device__ __forceinline__ void order_image(const float* __restrict__ coords, in
   int32_t* ord = order + b * N;
 #pragma unroll
   for (int r = 0; r < kPer; ++r)
-    if (bk[r] >= 0) ord[start[bk[r]] + rk[r]] = tid + r * kKnnThreads;
+    if (bk[r] >= 0) ord[start[bk[r]] + rk[r]] = tid + r * NT;
 }
 
 // Per partition of kPart entries, the count of its entries per token,
-// accumulated in LDS (images of at most kTabMaxTokens tokens) and written
-// out whole (zeros included): one workgroup per partition.  The launch
-// also carries the walk order: workgroups nparts .. nparts + B - 1 build
-// it for one image each (order_image).
-__global__ void __launch_bounds__(kKnnThreads)
+// accumulated in LDS (images of at most kTabMaxTokens tokens; integer
+// atomics, order independent) and written out whole (zeros included): one
+// workgroup of kChunkThreads per partition, each thread kChunkPer entries.
+// The launch also carries the walk order: workgroups nparts .. nparts + B - 1
+// build it for one image each (order_image).
+constexpr int kChunkWaves = 8;
+constexpr int kChunkThreads = 64 * kChunkWaves;
+constexpr int kChunkPer = kPart / kChunkThreads;   // entries per thread
+__global__ void __launch_bounds__(kChunkThreads)
 knn_pcount_kernel(int N, int G, int64_t MK, int P, int64_t nparts, const int32_t* __restrict__ ent_slot,
                   const float* __restrict__ coords, int32_t* __restrict__ pcnt,
                   int32_t* __restrict__ order) {
-  static_assert(kPart == kKnnThreads, "one entry per thread");
+  static_assert(kPart % kChunkThreads == 0, "whole entries per thread");
   static_assert(kTabMaxBuckets == kTabMaxTokens, "one LDS array serves both");
   __shared__ int32_t c[kTabMaxTokens];
   __shared__ int tmp[17];
   const int64_t part = blockIdx.x;
   if (part >= nparts) {
-    order_image(coords, N, G, part - nparts, c, tmp, order);
+    order_image<kChunkThreads>(coords, N, G, part - nparts, c, tmp, order);
     return;
   }
   const int64_t b = part / P;
   const int s = (int)(part - b * P);
   const int64_t e0 = (int64_t)s * kPart;
-  const int n = (int)min((int64_t)kPart, MK - e0);
-  for (int t = threadIdx.x; t < N; t += kKnnThreads) c[t] = 0;
-  __syncthreads();
-  if ((int)threadIdx.x < n) {
-    const int t = ent_slot[b * MK + e0 + threadIdx.x];
-    if (t >= 0) atomicAdd(&c[t], 1);
+  int tv[kChunkPer];
+#pragma unroll
+  for (int r = 0; r < kChunkPer; ++r) {
+    const int64_t x = e0 + r * kChunkThreads + threadIdx.x;
+    tv[r] = x < MK ? ent_slot[b * MK + x] : -1;
   }
+  for (int t = threadIdx.x; t < N; t += kChunkThreads) c[t] = 0;
+  __syncthreads();
+#pragma unroll
+  for (int r = 0; r < kChunkPer; ++r)
+    if (tv[r] >= 0) atomicAdd(&c[tv[r]], 1);
   __syncthreads();
   int32_t* row = pcnt + (b * P + s) * N;
-  for (int t = threadIdx.x; t < N; t += kKnnThreads) row[t] = c[t];
+  for (int t = threadIdx.x; t < N; t += kChunkThreads) row[t] = c[t];
 }
 
 // Token-major entry lists, in entry order (entry = query * K + slot), each
@@ -835,35 +848,79 @@ knn_pprefix_kernel(int N, int P, int tgroups, int32_t* __restrict__ pcnt,
   }
 }
 
-// one workgroup per partition; wave w ranks the partition's entries
-// w*64 .. w*64+63 (one per lane) against the earlier entries of the partition
-__global__ void __launch_bounds__(kKnnThreads)
+// One workgroup of kChunkWaves waves per partition.  Wave w takes the
+// partition's entries [w kChunkRun, (w + 1) kChunkRun) (wave order is entry
+// order) in batches of 64: (1) each wave counts its entries per token in
+// its own LDS row (integer atomics); (2) per token, the rows become the
+// waves' first places: segment start + the partition's prefix + the counts
+// of the earlier waves; (3) each wave walks its batches in order: lanes
+// holding the same token find each other by matching the token's bits with
+// ballots, an entry goes to its wave's place + the number of equal tokens
+// in lower lanes, and the last such lane advances the place.  Dynamic LDS:
+// kChunkWaves x N ints.
+constexpr int kChunkRun = kPart / kChunkWaves;    // entries per wave
+constexpr int kChunkBatches = kChunkRun / 64;
+__global__ void __launch_bounds__(kChunkThreads)
 knn_pplace_kernel(int N, int K, int64_t MK, int P, const int32_t* __restrict__ ent_slot,
                   const float* __restrict__ ent_w, const int32_t* __restrict__ off_all,
                   const int32_t* __restrict__ pcnt, int2* __restrict__ ent_all) {
-  static_assert(kPart == kKnnThreads, "one entry per thread");
-  __shared__ __align__(16) int32_t tok[kPart];
+  static_assert(kChunkRun % 64 == 0, "whole batches per wave");
+  extern __shared__ int32_t cw[];   // [kChunkWaves][N]
   const int64_t part = blockIdx.x;
   const int64_t b = part / P;
   const int s = (int)(part - b * P);
-  const int64_t e0 = (int64_t)s * kPart;
-  const int n = (int)min((int64_t)kPart, MK - e0);
-  const int u = threadIdx.x;
-  const int t = u < n ? ent_slot[b * MK + e0 + u] : -1;
-  tok[u] = t;
-  __syncthreads();
-  const int ymax = (threadIdx.x & ~63) + 64;   // the wave's entries are below this
-  int rank = 0;
-  const int4* t4 = reinterpret_cast<const int4*>(tok);
-  for (int y4 = 0; y4 < ymax / 4; ++y4) {
-    const int4 v = t4[y4];
-    const int y = 4 * y4;
-    rank += (v.x == t && y < u) + (v.y == t && y + 1 < u) + (v.z == t && y + 2 < u) +
-            (v.w == t && y + 3 < u);
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int64_t ew0 = (int64_t)s * kPart + wv * kChunkRun;
+  int tk[kChunkBatches];
+  float wk[kChunkBatches];
+#pragma unroll
+  for (int h = 0; h < kChunkBatches; ++h) {
+    const int64_t x = ew0 + h * 64 + lane;
+    tk[h] = x < MK ? ent_slot[b * MK + x] : -1;
+    wk[h] = x < MK ? ent_w[b * MK + x] : 0.f;
   }
-  if (t >= 0)
-    ent_all[b * MK + off_all[b * (N + 1) + t] + pcnt[(b * P + s) * N + t] + rank] =
-        make_int2((int)((e0 + u) / K), __float_as_int(ent_w[b * MK + e0 + u]));
+  for (int t = threadIdx.x; t < N; t += kChunkThreads)
+#pragma unroll
+    for (int w = 0; w < kChunkWaves; ++w) cw[w * N + t] = 0;
+  __syncthreads();
+  int32_t* mine = cw + wv * N;
+#pragma unroll
+  for (int h = 0; h < kChunkBatches; ++h)
+    if (tk[h] >= 0) atomicAdd(&mine[tk[h]], 1);
+  __syncthreads();
+  const int32_t* off = off_all + b * (N + 1);
+  const int32_t* pre = pcnt + (b * P + s) * N;
+  for (int t = threadIdx.x; t < N; t += kChunkThreads) {
+    int base = off[t] + pre[t];
+#pragma unroll
+    for (int w = 0; w < kChunkWaves; ++w) {
+      const int c = cw[w * N + t];
+      cw[w * N + t] = base;
+      base += c;
+    }
+  }
+  __syncthreads();
+  const int nbits = N > 1 ? 32 - __clz(N - 1) : 0;   // token bits
+  const uint64_t below = (uint64_t(1) << lane) - 1;
+  const uint64_t upto = lane == 63 ? ~uint64_t(0) : (uint64_t(2) << lane) - 1;
+  int2* ent = ent_all + b * MK;
+#pragma unroll
+  for (int h = 0; h < kChunkBatches; ++h) {
+    const int t = tk[h];
+    // lanes holding the same valid token (0 for an empty slot)
+    const bool ok = t >= 0;
+    uint64_t same = __ballot(ok);
+    for (int i = 0; i < nbits; ++i) {
+      const bool bit = (t >> i) & 1;
+      const uint64_t on = __ballot(ok && bit);
+      same &= bit ? on : ~on;
+    }
+    if (ok) {
+      const int pos = mine[t] + __popcll(same & below);
+      ent[pos] = make_int2((int)((ew0 + h * 64 + lane) / K), __float_as_int(wk[h]));
+      if ((same & ~upto) == 0) mine[t] = pos + 1;
+    }
+  }
 }
 
 // Large images: token-major entry lists by per-token cursors.  (1) The
@@ -1169,16 +1226,17 @@ hipError_t bwd_t(int B, int N, int M, int Cf, int G, int K, float p, const float
   if (ntok > 0) {
     if (!large) {
       // partition counts, and the walk order in B more workgroups
-      hipLaunchKernelGGL(knn_pcount_kernel, dim3((unsigned)(nparts + B)), dim3(kKnnThreads), 0, st,
+      hipLaunchKernelGGL(knn_pcount_kernel, dim3((unsigned)(nparts + B)), dim3(kChunkThreads), 0, st,
                          N, G, MK, P, nparts, (const int32_t*)w.slot, coords, w.pcnt, w.order);
       const int tgroups = (N + 63) / 64;
       hipLaunchKernelGGL(knn_pprefix_kernel, dim3((unsigned)(B * tgroups)), dim3(64 * kPrefWaves), 0,
                          st, N, P, tgroups, w.pcnt, w.cnt);
       launch_segment_scan(B, N, w.cnt, w.off, st);
       if (nparts > 0)
-        hipLaunchKernelGGL(knn_pplace_kernel, dim3((unsigned)nparts), dim3(kKnnThreads), 0, st, N,
-                           K, MK, P, (const int32_t*)w.slot, (const float*)w.wgt,
-                           (const int32_t*)w.off, (const int32_t*)w.pcnt, w.ent);
+        hipLaunchKernelGGL(knn_pplace_kernel, dim3((unsigned)nparts), dim3(kChunkThreads),
+                           (unsigned)(kChunkWaves * N * sizeof(int32_t)), st, N, K, MK, P,
+                           (const int32_t*)w.slot, (const float*)w.wgt, (const int32_t*)w.off,
+                           (const int32_t*)w.pcnt, w.ent);
     } else {
       launch_segment_scan(B, N, w.cnt, w.off, st);
       launch_zero_i32(ntok, w.cnt, st);
