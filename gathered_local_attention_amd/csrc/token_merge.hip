@@ -56,6 +56,12 @@ typedef _Float16 mf16x8 __attribute__((ext_vector_type(8)));
 template <typename T> struct Row16;
 template <> struct Row16<float> {
   static constexpr int E = 4;
+  static constexpr int NR = 4;   // chunks per lane at most (1024 channels, 64 lanes)
+  __device__ static uint4 raw(const float* p) { return *reinterpret_cast<const uint4*>(p); }
+  __device__ static void cvt(uint4 a, float* v) {
+    v[0] = __uint_as_float(a.x); v[1] = __uint_as_float(a.y);
+    v[2] = __uint_as_float(a.z); v[3] = __uint_as_float(a.w);
+  }
   __device__ static void load(const float* p, float* v) {
     const float4 a = *reinterpret_cast<const float4*>(p);
     v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
@@ -66,6 +72,13 @@ template <> struct Row16<float> {
 };
 template <typename H, typename V> struct Row16Half {
   static constexpr int E = 8;
+  static constexpr int NR = 2;   // chunks per lane at most (1024 channels, 64 lanes)
+  __device__ static uint4 raw(const H* p) { return *reinterpret_cast<const uint4*>(p); }
+  __device__ static void cvt(uint4 a, float* v) {
+    const mf32x8 f = __builtin_convertvector(__builtin_bit_cast(V, a), mf32x8);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = f[e];
+  }
   __device__ static void load(const H* p, float* v) {
     const mf32x8 f = __builtin_convertvector(__builtin_bit_cast(V, *reinterpret_cast<const uint4*>(p)), mf32x8);
 #pragma unroll
@@ -696,25 +709,63 @@ __device__ __forceinline__ MGroup mgroup(int lg, int64_t total) {
 // are read four at a time with clamped indices (every load of a batch
 // issues together), the extra ones masked.
 constexpr int kMB = 4;
+// one batch of scores (members u .. u + kMB - 1 of a group ending at z)
+// into the running max and sum
+__device__ __forceinline__ void softmax_batch(const float* v, int u, int z, float& mx, float& sum) {
+  float m2 = mx;
+#pragma unroll
+  for (int h = 0; h < kMB; ++h) m2 = u + h < z ? fmaxf(m2, v[h]) : m2;
+  sum *= __builtin_amdgcn_exp2f((mx - m2) * 1.4426950408889634f);   // rescale to the new max
+  mx = m2;
+#pragma unroll
+  for (int h = 0; h < kMB; ++h)
+    sum += u + h < z ? __builtin_amdgcn_exp2f((v[h] - mx) * 1.4426950408889634f) : 0.f;
+}
+// the statistics of a group whose first batch of scores v0 is at hand:
+// max and 1 / sum of exp
 __device__ __forceinline__ void group_softmax(const int32_t* __restrict__ mem, int a, int z,
-                                              const float* __restrict__ s, float& mx, float& inv) {
+                                              const float* __restrict__ s, const float* v0,
+                                              float& mx, float& inv) {
   mx = -INFINITY;
   float sum = 0.f;
-  for (int u = a; u < z; u += kMB) {
+  softmax_batch(v0, a, z, mx, sum);
+  for (int u = a + kMB; u < z; u += kMB) {
     float v[kMB];
 #pragma unroll
     for (int h = 0; h < kMB; ++h) v[h] = s[mem[min(u + h, z - 1)]];
-    float m2 = mx;
-#pragma unroll
-    for (int h = 0; h < kMB; ++h) m2 = u + h < z ? fmaxf(m2, v[h]) : m2;
-    sum *= __builtin_amdgcn_exp2f((mx - m2) * 1.4426950408889634f);   // rescale to the new max
-    mx = m2;
-#pragma unroll
-    for (int h = 0; h < kMB; ++h)
-      sum += u + h < z ? __builtin_amdgcn_exp2f((v[h] - mx) * 1.4426950408889634f) : 0.f;
+    softmax_batch(v, u, z, mx, sum);
   }
   inv = sum > 0.f ? 1.f / sum : 0.f;
 }
+
+// A group's first batch of members, with their scores, coordinates and the
+// lane's chunks of their rows, all loads issued together (clamped indices:
+// an empty group reads member 0 of the image, masked by the callers)
+template <typename T>
+struct FirstBatch {
+  int mi[kMB];
+  float sv[kMB];
+  float2 x[kMB];
+  uint4 row[Row16<T>::NR][kMB];
+  __device__ void load(const int32_t* __restrict__ mem, int a, int z, const float* __restrict__ s,
+                       const float2* __restrict__ xy, const T* __restrict__ fimg, int Cf, int sub,
+                       int L, int nr) {
+#pragma unroll
+    for (int h = 0; h < kMB; ++h) mi[h] = mem[z > a ? min(a + h, z - 1) : 0];
+#pragma unroll
+    for (int h = 0; h < kMB; ++h) {
+      sv[h] = s[mi[h]];
+      x[h] = xy[mi[h]];
+    }
+#pragma unroll
+    for (int r = 0; r < Row16<T>::NR; ++r)
+      if (r < nr) {
+#pragma unroll
+        for (int h = 0; h < kMB; ++h)
+          row[r][h] = Row16<T>::raw(fimg + (int64_t)mi[h] * Cf + (sub + r * L) * Row16<T>::E);
+      }
+  }
+};
 
 template <typename T>
 __global__ void __launch_bounds__(kMergeThreads)
@@ -731,49 +782,51 @@ merge_fwd_kernel(int N, int k, int Cf, int lg, int64_t total, const T* __restric
   const int32_t* mem = members + b * N;
   const int a = offsets[b * (k + 1) + an], z = offsets[b * (k + 1) + an + 1];
   const float* s = scores + b * N;
-  float mx, inv;
-  group_softmax(mem, a, z, s, mx, inv);
   const int nch = Cf / Rw::E;
   const T* fimg = feats + b * N * Cf;
   const float2* xy = reinterpret_cast<const float2*>(coords) + b * N;
-  float acc[kMaxChunks][Rw::E];
+  const int nr = (nch - g.sub + L - 1) / L;   // chunks of this lane
+  FirstBatch<T> fb;
+  fb.load(mem, a, z, s, xy, fimg, Cf, g.sub, L, nr);
+  float mx, inv;
+  group_softmax(mem, a, z, s, fb.sv, mx, inv);
+  float acc[Rw::NR][Rw::E];
 #pragma unroll
-  for (int r = 0; r < kMaxChunks; ++r)
+  for (int r = 0; r < Rw::NR; ++r)
 #pragma unroll
     for (int e = 0; e < Rw::E; ++e) acc[r][e] = 0.f;
   float ax = 0.f, ay = 0.f;
-  const int nr = (nch - g.sub + L - 1) / L;   // chunks of this lane
-  for (int u = a; u < z; u += kMB) {   // four members at a time, loads first
-    int mi[kMB];
+  // one batch of kMB members: weights, rows (loaded), coordinates
+  auto batch = [&](int u, const float* sv, const float2* x, const uint4 (*row)[kMB]) {
     float w[kMB];
 #pragma unroll
-    for (int h = 0; h < kMB; ++h) mi[h] = mem[min(u + h, z - 1)];
-#pragma unroll
     for (int h = 0; h < kMB; ++h)
-      w[h] = u + h < z ? __builtin_amdgcn_exp2f((s[mi[h]] - mx) * 1.4426950408889634f) * inv : 0.f;
-    float2 x[kMB];
+      w[h] = u + h < z ? __builtin_amdgcn_exp2f((sv[h] - mx) * 1.4426950408889634f) * inv : 0.f;
 #pragma unroll
-    for (int h = 0; h < kMB; ++h) x[h] = xy[mi[h]];
-#pragma unroll
-    for (int r = 0; r < kMaxChunks; ++r) {
+    for (int r = 0; r < Rw::NR; ++r) {
       if (r >= nr) break;
-      const int c = g.sub + r * L;
-      float v[kMB][Rw::E];
 #pragma unroll
-      for (int h = 0; h < kMB; ++h) Rw::load(fimg + (int64_t)mi[h] * Cf + c * Rw::E, v[h]);
+      for (int h = 0; h < kMB; ++h) {
+        float v[Rw::E];
+        Rw::cvt(row[r][h], v);
 #pragma unroll
-      for (int h = 0; h < kMB; ++h)
-#pragma unroll
-        for (int e = 0; e < Rw::E; ++e) acc[r][e] = fmaf(w[h], v[h][e], acc[r][e]);
+        for (int e = 0; e < Rw::E; ++e) acc[r][e] = fmaf(w[h], v[e], acc[r][e]);
+      }
     }
 #pragma unroll
     for (int h = 0; h < kMB; ++h) {
       ax = fmaf(w[h], x[h].x, ax);
       ay = fmaf(w[h], x[h].y, ay);
     }
+  };
+  batch(a, fb.sv, fb.x, fb.row);
+  for (int u = a + kMB; u < z; u += kMB) {   // larger groups: four members at a time, loads first
+    FirstBatch<T> nb;
+    nb.load(mem, u, z, s, xy, fimg, Cf, g.sub, L, nr);
+    batch(u, nb.sv, nb.x, nb.row);
   }
 #pragma unroll
-  for (int r = 0; r < kMaxChunks; ++r) {
+  for (int r = 0; r < Rw::NR; ++r) {
     const int c = g.sub + r * L;
     if (c >= nch) break;
     Rw::store(out_f + g.id * Cf + c * Rw::E, acc[r]);
@@ -794,51 +847,50 @@ merge_bwd_kernel(int N, int k, int Cf, int lg, int64_t total, const T* __restric
   const int64_t id = g.valid ? g.id : 0;   // idle lanes mirror anchor 0 (group shuffles)
   const int64_t b = id / k;
   const int an = (int)(id - b * k);
-  const int32_t* mem = members + b * N;
-  const int a = offsets[b * (k + 1) + an], z = offsets[b * (k + 1) + an + 1];
-  const float* s = scores + b * N;
-  float mx, inv;
-  group_softmax(mem, a, z, s, mx, inv);
   const int nch = Cf / Rw::E;
-  const T* fimg = feats + b * N * Cf;
-  const float2* xy = reinterpret_cast<const float2*>(coords) + b * N;
-  float dof[kMaxChunks][Rw::E];
+  // the anchor's output gradient first (independent of the member lists)
+  float dof[Rw::NR][Rw::E];
 #pragma unroll
-  for (int r = 0; r < kMaxChunks; ++r) {
+  for (int r = 0; r < Rw::NR; ++r) {
     const int c = g.sub + r * L;
 #pragma unroll
     for (int e = 0; e < Rw::E; ++e) dof[r][e] = 0.f;
     if (c < nch) Rw::load(dout_f + id * Cf + c * Rw::E, dof[r]);
   }
   const float2 dox = reinterpret_cast<const float2*>(dout_x)[id];
-  float gbar = 0.f;
+  const int32_t* mem = members + b * N;
+  const int a = offsets[b * (k + 1) + an], z = offsets[b * (k + 1) + an + 1];
+  const float* s = scores + b * N;
+  const T* fimg = feats + b * N * Cf;
+  const float2* xy = reinterpret_cast<const float2*>(coords) + b * N;
   const int nr = (nch - g.sub + L - 1) / L;   // chunks of this lane
-  for (int u = a; u < z; u += kMB) {   // same trip count for the whole group
-    int mi[kMB];
-    float w[kMB], dot[kMB];
-#pragma unroll
-    for (int h = 0; h < kMB; ++h) mi[h] = mem[min(u + h, z - 1)];
+  FirstBatch<T> fb;
+  fb.load(mem, a, z, s, xy, fimg, Cf, g.sub, L, nr);
+  float mx, inv;
+  group_softmax(mem, a, z, s, fb.sv, mx, inv);
+  float gbar = 0.f;
+  // one batch of kMB members (same trip count for the whole group: the
+  // group shuffles): dF rows, <dO, F_i> + <dO_x, x_i> = g_i into gi, the
+  // weights into w, the coordinate gradients
+  auto batch = [&](int u, const int* mi, const float* sv, const float2* x, const uint4 (*row)[kMB],
+                   float* w, float* gi) {
+    float dot[kMB];
 #pragma unroll
     for (int h = 0; h < kMB; ++h) {
-      w[h] = u + h < z ? __builtin_amdgcn_exp2f((s[mi[h]] - mx) * 1.4426950408889634f) * inv : 0.f;
+      w[h] = u + h < z ? __builtin_amdgcn_exp2f((sv[h] - mx) * 1.4426950408889634f) * inv : 0.f;
       dot[h] = 0.f;
     }
-    float2 x[kMB];
 #pragma unroll
-    for (int h = 0; h < kMB; ++h) x[h] = xy[mi[h]];
-#pragma unroll
-    for (int r = 0; r < kMaxChunks; ++r) {
+    for (int r = 0; r < Rw::NR; ++r) {
       if (r >= nr) break;
       const int c = g.sub + r * L;
-      float v[kMB][Rw::E];
-#pragma unroll
-      for (int h = 0; h < kMB; ++h) Rw::load(fimg + (int64_t)mi[h] * Cf + c * Rw::E, v[h]);
 #pragma unroll
       for (int h = 0; h < kMB; ++h) {
-        float d[Rw::E];
+        float v[Rw::E], d[Rw::E];
+        Rw::cvt(row[r][h], v);
 #pragma unroll
         for (int e = 0; e < Rw::E; ++e) {
-          dot[h] = fmaf(dof[r][e], v[h][e], dot[h]);
+          dot[h] = fmaf(dof[r][e], v[e], dot[h]);
           d[e] = w[h] * dof[r][e];
         }
         if (g.valid && u + h < z) Rw::store(dfeats + (b * N + mi[h]) * Cf + c * Rw::E, d);
@@ -849,16 +901,30 @@ merge_bwd_kernel(int N, int k, int Cf, int lg, int64_t total, const T* __restric
       for (int h = 0; h < kMB; ++h) dot[h] += __shfl_xor(dot[h], o, 64);
 #pragma unroll
     for (int h = 0; h < kMB; ++h) {
-      const float gi = dot[h] + dox.x * x[h].x + dox.y * x[h].y;
-      gbar = fmaf(w[h], gi, gbar);
-      if (g.valid && g.sub == 0 && u + h < z) {
-        dscores[b * N + mi[h]] = gi;   // g_i for now; finished below by the same lane
+      gi[h] = dot[h] + dox.x * x[h].x + dox.y * x[h].y;
+      gbar = fmaf(w[h], gi[h], gbar);
+      if (g.valid && g.sub == 0 && u + h < z)
         reinterpret_cast<float2*>(dcoords)[b * N + mi[h]] = make_float2(w[h] * dox.x, w[h] * dox.y);
-      }
     }
+  };
+  float w0[kMB], g0[kMB];
+  batch(a, fb.mi, fb.sv, fb.x, fb.row, w0, g0);
+  for (int u = a + kMB; u < z; u += kMB) {   // larger groups: later batches, loads first
+    FirstBatch<T> nb;
+    nb.load(mem, u, z, s, xy, fimg, Cf, g.sub, L, nr);
+    float w[kMB], gi[kMB];
+    batch(u, nb.mi, nb.sv, nb.x, nb.row, w, gi);
+    if (g.valid && g.sub == 0)
+#pragma unroll
+      for (int h = 0; h < kMB; ++h)
+        if (u + h < z) dscores[b * N + nb.mi[h]] = gi[h];   // g_i for now; finished below
   }
   if (!g.valid || g.sub != 0) return;
-  for (int u = a; u < z; ++u) {
+  // dL/ds_i = w_i (g_i - sum_j w_j g_j): the first batch from registers
+#pragma unroll
+  for (int h = 0; h < kMB; ++h)
+    if (a + h < z) dscores[b * N + fb.mi[h]] = w0[h] * (g0[h] - gbar);
+  for (int u = a + kMB; u < z; ++u) {
     const int i = mem[u];
     const float w = __builtin_amdgcn_exp2f((s[i] - mx) * 1.4426950408889634f) * inv;
     dscores[b * N + i] = w * (dscores[b * N + i] - gbar);
