@@ -932,17 +932,40 @@ knn_pplace_kernel(int N, int K, int64_t MK, int P, const int32_t* __restrict__ e
 // kLongSegment are sorted by launch_long_segment_sort instead, bounding the
 // cost).  The lists come out in entry order, as from the stable counting
 // sort of small images.
+// The lanes of a wave that hold the same token (consecutive entries: a
+// few neighbouring queries, which share most of their tokens) take their
+// places with one atomic: they find each other by ballots over the bits in
+// which the wave's token ids differ, the lowest of them adds the group's
+// count, and each lane takes the returned base + its rank in the group.
 __global__ void __launch_bounds__(kKnnThreads)
 knn_lplace_kernel(int N, int64_t MK, int64_t n_ent, const int32_t* __restrict__ ent_slot,
                   const int32_t* __restrict__ off_all, int32_t* __restrict__ cur,
                   int32_t* __restrict__ lst) {
   const int64_t x = (int64_t)blockIdx.x * kKnnThreads + threadIdx.x;
-  if (x >= n_ent) return;
-  const int t = ent_slot[x];
-  if (t < 0) return;
-  const int64_t b = x / MK;
-  const int r = atomicAdd(&cur[b * N + t], 1);
-  lst[b * MK + off_all[b * (N + 1) + t] + r] = (int32_t)(x - b * MK);
+  const int lane = threadIdx.x & 63;
+  const int t = x < n_ent ? ent_slot[x] : -1;
+  const bool ok = t >= 0;
+  const int64_t b = ok ? x / MK : 0;
+  const uint32_t key = ok ? (uint32_t)(b * N + t) : 0u;   // B N < 2^31
+  const uint32_t key0 = (uint32_t)__builtin_amdgcn_readfirstlane((int)key);
+  uint32_t diff = ok ? key ^ key0 : 0u;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) diff |= (uint32_t)__shfl_xor((int)diff, o, 64);
+  uint64_t same = __ballot(ok);
+  for (uint32_t d = diff; d != 0u; d &= d - 1u) {   // wave-uniform
+    const int i = __builtin_ctz(d);
+    const bool bit = (key >> i) & 1u;
+    const uint64_t on = __ballot(ok && bit);
+    same &= bit ? on : ~on;
+  }
+  if (!ok) same = 0;
+  const uint64_t below = (uint64_t(1) << lane) - 1;
+  const int rank = __popcll(same & below);
+  const int leader = same ? __builtin_ctzll(same) : lane;
+  int base = 0;
+  if (ok && rank == 0) base = atomicAdd(&cur[key], __popcll(same));
+  base = __shfl(base, leader, 64);
+  if (ok) lst[b * MK + off_all[b * (N + 1) + t] + base + rank] = (int32_t)(x - b * MK);
 }
 
 __global__ void __launch_bounds__(kKnnThreads)
