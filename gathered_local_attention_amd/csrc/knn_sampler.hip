@@ -932,11 +932,28 @@ knn_pplace_kernel(int N, int K, int64_t MK, int P, const int32_t* __restrict__ e
 // kLongSegment are sorted by launch_long_segment_sort instead, bounding the
 // cost).  The lists come out in entry order, as from the stable counting
 // sort of small images.
-// The lanes of a wave that hold the same token (consecutive entries: a
-// few neighbouring queries, which share most of their tokens) take their
-// places with one atomic: they find each other by ballots over the bits in
-// which the wave's token ids differ, the lowest of them adds the group's
-// count, and each lane takes the returned base + its rank in the group.
+// The lanes of a wave holding the same token (consecutive entries: a few
+// neighbouring queries, which share most of their tokens) find each other
+// by ballots over the bits in which the wave's token ids differ: the mask
+// of the lanes whose key equals this lane's (0 where !ok).  Wave-uniform.
+__device__ __forceinline__ uint64_t wave_same_key(uint32_t key, bool ok) {
+  const uint32_t key0 = (uint32_t)__builtin_amdgcn_readfirstlane((int)key);
+  uint32_t diff = ok ? key ^ key0 : 0u;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) diff |= (uint32_t)__shfl_xor((int)diff, o, 64);
+  uint64_t same = __ballot(ok);
+  for (uint32_t d = diff; d != 0u; d &= d - 1u) {
+    const int i = __builtin_ctz(d);
+    const bool bit = (key >> i) & 1u;
+    const uint64_t on = __ballot(ok && bit);
+    same &= bit ? on : ~on;
+  }
+  return ok ? same : uint64_t(0);
+}
+
+// Such a group takes its places with one atomic: the lowest lane adds the
+// group's count, and each lane takes the returned base + its rank in the
+// group (its entries stay in entry order, side by side).
 __global__ void __launch_bounds__(kKnnThreads)
 knn_lplace_kernel(int N, int64_t MK, int64_t n_ent, const int32_t* __restrict__ ent_slot,
                   const int32_t* __restrict__ off_all, int32_t* __restrict__ cur,
@@ -947,20 +964,8 @@ knn_lplace_kernel(int N, int64_t MK, int64_t n_ent, const int32_t* __restrict__ 
   const bool ok = t >= 0;
   const int64_t b = ok ? x / MK : 0;
   const uint32_t key = ok ? (uint32_t)(b * N + t) : 0u;   // B N < 2^31
-  const uint32_t key0 = (uint32_t)__builtin_amdgcn_readfirstlane((int)key);
-  uint32_t diff = ok ? key ^ key0 : 0u;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) diff |= (uint32_t)__shfl_xor((int)diff, o, 64);
-  uint64_t same = __ballot(ok);
-  for (uint32_t d = diff; d != 0u; d &= d - 1u) {   // wave-uniform
-    const int i = __builtin_ctz(d);
-    const bool bit = (key >> i) & 1u;
-    const uint64_t on = __ballot(ok && bit);
-    same &= bit ? on : ~on;
-  }
-  if (!ok) same = 0;
-  const uint64_t below = (uint64_t(1) << lane) - 1;
-  const int rank = __popcll(same & below);
+  const uint64_t same = wave_same_key(key, ok);
+  const int rank = __popcll(same & ((uint64_t(1) << lane) - 1));
   const int leader = same ? __builtin_ctzll(same) : lane;
   int base = 0;
   if (ok && rank == 0) base = atomicAdd(&cur[key], __popcll(same));
@@ -972,22 +977,35 @@ __global__ void __launch_bounds__(kKnnThreads)
 knn_lrank_kernel(int N, int K, int64_t MK, int64_t n_ent, const int32_t* __restrict__ ent_slot,
                  const float* __restrict__ ent_w, const int32_t* __restrict__ off_all,
                  const int32_t* __restrict__ lst, int2* __restrict__ ent_all) {
+  // the lanes of a wave with the same token hold consecutive entries of
+  // its segment: the lowest counts the segment's entries below its own, the
+  // others add their rank in the group
   const int64_t x = (int64_t)blockIdx.x * kKnnThreads + threadIdx.x;
-  if (x >= n_ent) return;
-  const int t = ent_slot[x];
-  if (t < 0) return;
-  const int64_t b = x / MK;
+  const int lane = threadIdx.x & 63;
+  const int t = x < n_ent ? ent_slot[x] : -1;
+  const bool ok = t >= 0;
+  const int64_t b = ok ? x / MK : 0;
+  const uint64_t same = wave_same_key(ok ? (uint32_t)(b * N + t) : 0u, ok);
+  const int rank = __popcll(same & ((uint64_t(1) << lane) - 1));
+  const int leader = same ? __builtin_ctzll(same) : lane;
   const int e = (int)(x - b * MK);
-  const int a = off_all[b * (N + 1) + t], z = off_all[b * (N + 1) + t + 1];
-  if (z - a > kLongSegment) return;   // sorted by launch_long_segment_sort
-  const int32_t* seg = lst + b * MK;
-  int rank = 0, y = a;
-  for (; y + 4 <= z; y += 4) {   // four loads in flight
-    const int v0 = seg[y], v1 = seg[y + 1], v2 = seg[y + 2], v3 = seg[y + 3];
-    rank += (v0 < e) + (v1 < e) + (v2 < e) + (v3 < e);
+  const int a = ok ? off_all[b * (N + 1) + t] : 0, z = ok ? off_all[b * (N + 1) + t + 1] : 0;
+  const bool mine = ok && z - a <= kLongSegment;   // longer: launch_long_segment_sort
+  int below = 0;
+  if (mine && rank == 0) {
+    const int32_t* seg = lst + b * MK;
+    int y = a;
+    for (; y + 8 <= z; y += 8) {   // eight loads in flight
+      int v[8];
+#pragma unroll
+      for (int h = 0; h < 8; ++h) v[h] = seg[y + h];
+#pragma unroll
+      for (int h = 0; h < 8; ++h) below += v[h] < e;
+    }
+    for (; y < z; ++y) below += seg[y] < e;
   }
-  for (; y < z; ++y) rank += seg[y] < e;
-  ent_all[b * MK + a + rank] = make_int2(e / K, __float_as_int(ent_w[x]));
+  below = __shfl(below, leader, 64);
+  if (mine) ent_all[b * MK + a + below + rank] = make_int2(e / K, __float_as_int(ent_w[x]));
 }
 
 
