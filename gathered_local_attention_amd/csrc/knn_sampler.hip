@@ -116,23 +116,26 @@ __device__ __forceinline__ void table_tile(const int* start, const uint2* tok, i
   const int ilast = min(G, i0 + 8) - 1, jlast = min(G, j0 + 8) - 1;
   const int tr0 = (i0 << shift) >> bs, tr1 = (((ilast + 1) << shift) - 1) >> bs;
   const int tc0 = (j0 << shift) >> bs, tc1 = (((jlast + 1) << shift) - 1) >> bs;
+  // the K smallest keys seen, unordered (slots past K stay 0, so they are
+  // never the largest), the largest of them and its slot; sorted at the end
   uint64_t best[KM];
 #pragma unroll
-  for (int r = 0; r < KM; ++r) best[r] = ~0ull;
-  uint64_t worst = ~0ull;   // best[K - 1]
+  for (int r = 0; r < KM; ++r) best[r] = r < K ? ~0ull : 0ull;
+  uint64_t worst = ~0ull;
+  int wslot = 0;
   auto insert = [&](uint2 e) {
     const int64_t dx = (int64_t)(e.x & 0xFFFFu) - cx, dy = (int64_t)(e.x >> 16) - cy;
-    uint64_t x = ((uint64_t)(dx * dx + dy * dy) << kTokBits) | e.y;
+    const uint64_t x = ((uint64_t)(dx * dx + dy * dy) << kTokBits) | e.y;
     if (x >= worst) return;
 #pragma unroll
-    for (int r = 0; r < KM; ++r) {
-      if (r < K) {
-        const uint64_t lo = x < best[r] ? x : best[r];
-        const uint64_t hi = x < best[r] ? best[r] : x;
-        best[r] = lo;
-        x = hi;
-      }
-      if (r == K - 1) worst = best[r];
+    for (int r = 0; r < KM; ++r) best[r] = r == wslot ? x : best[r];
+    worst = best[0];
+    wslot = 0;
+#pragma unroll
+    for (int r = 1; r < KM; ++r) {
+      const bool w = best[r] > worst;
+      worst = w ? best[r] : worst;
+      wslot = w ? r : wslot;
     }
   };
   // tokens of the buckets (by, bx0 .. bx1): one contiguous range
@@ -152,8 +155,18 @@ __device__ __forceinline__ void table_tile(const int* start, const uint2* tok, i
         }
       }
     } else {
-      const int t0 = start[bb0], t1 = bb1 + 1 < nb ? start[bb1 + 1] : total;
-      for (int t = t0; t < t1; ++t) insert(tok[t]);
+      // wave-uniform bounds; four tokens read per step, so that one LDS
+      // wait covers them
+      const int t0 = __builtin_amdgcn_readfirstlane(start[bb0]);
+      const int t1 = __builtin_amdgcn_readfirstlane(bb1 + 1 < nb ? start[bb1 + 1] : total);
+      for (int t = t0; t < t1; t += 4) {
+        uint2 e[4];
+#pragma unroll
+        for (int h = 0; h < 4; ++h) e[h] = tok[min(t + h, t1 - 1)];
+#pragma unroll
+        for (int h = 0; h < 4; ++h)
+          if (t + h < t1) insert(e[h]);
+      }
     }
   };
   for (int m = 0;; ++m) {
@@ -179,6 +192,18 @@ __device__ __forceinline__ void table_tile(const int* start, const uint2* tok, i
     if (__all(done)) break;
   }
   if (!valid) return;
+  // ascending order (odd-even transposition over the K slots; the zero
+  // slots past K are left out)
+#pragma unroll
+  for (int p = 0; p < KM; ++p)
+#pragma unroll
+    for (int r = p & 1; r + 1 < KM; r += 2)
+      if (r + 1 < K) {
+        const uint64_t lo = best[r] < best[r + 1] ? best[r] : best[r + 1];
+        const uint64_t hi = best[r] < best[r + 1] ? best[r + 1] : best[r];
+        best[r] = lo;
+        best[r + 1] = hi;
+      }
   int32_t* row = table_img + ((int64_t)i * G + j) * K;
 #pragma unroll
   for (int r = 0; r < KM; ++r)
