@@ -121,6 +121,27 @@ def test_edge_sizes_and_ties(ca, N, k):
     _run(ca, coords, scores, feats, dfeat, dcoord, k, G)
 
 
+@pytest.mark.parametrize("dtype,N,k,C", [(torch.float16, 400, 100, 192),
+                                         (torch.bfloat16, 300, 60, 768),
+                                         (torch.float32, 200, 50, 1024),
+                                         (torch.bfloat16, 150, 7, 1024),
+                                         (torch.float32, 100, 100, 8)])
+def test_row_widths_all_dtypes(ca, dtype, N, k, C):
+    """Every element type and row width: one to four 16-byte chunks per lane,
+    groups where some lanes hold one chunk fewer (768 bf16 channels), idle
+    lanes (192 f16 channels over 32 lanes), groups of one member and groups
+    of tens of members (several batches of four)."""
+    rng = np.random.default_rng(N * 31 + C)
+    G = 32
+    coords = rng.uniform(-0.5, G - 0.5, size=(2, N, 2)).astype(np.float32)
+    scores = rng.standard_normal((2, N)).astype(np.float32)
+    feats = torch.from_numpy(rng.standard_normal((2, N, C)).astype(np.float32)).to(dtype)
+    dfeat = torch.from_numpy(rng.standard_normal((2, k, C)).astype(np.float32)).to(dtype)
+    dcoord = rng.standard_normal((2, k, 2)).astype(np.float32)
+    print(f"case merge widths dtype={dtype} N={N} k={k} C={C}", flush=True)
+    _run(ca, coords, scores, feats, dfeat, dcoord, k, G)
+
+
 def test_backward_is_deterministic(ca):
     case = make_merge_case("merge_stages", B=4)
     cfg = case["cfg"]
