@@ -124,14 +124,15 @@ def test_table_edge_shapes(ca, G, K, N):
                                            (torch.float16, 150, 192, 8, 200),
                                            (torch.bfloat16, 120, 640, 4, 150),
                                            (torch.float32, 90, 768, 8, 100),
-                                           (torch.float32, 60, 1024, 16, 64)])
+                                           (torch.float32, 60, 1024, 16, 64),
+                                           (torch.bfloat16, 4096, 128, 8, 700)])
 def test_small_images_all_dtypes(ca, dtype, N, C, K, M):
     """Small images in every element type: f32 / f16 / bf16, K = 4, 8, 16,
     rows of 128 to 4096 bytes, a query count that fills no whole wave, a
     single query, fewer tokens than slots.  The row widths also give every
     lane-group shape: one to four 16-byte chunks per lane, and groups where
     some lanes hold one chunk fewer than the others (C = 640 bf16: 80 chunks
-    over 32 lanes)."""
+    over 32 lanes).  4096 tokens: the largest image of the in-LDS lists."""
     G, p = 24, 0.9
     rng = np.random.default_rng(N * 7 + C + K)
     B = 2
