@@ -69,7 +69,6 @@ namespace ca {
 
 namespace {
 
-constexpr int kKnnMaxK = 16;
 constexpr int kTabThreads = 256;
 constexpr int kTabMaxBuckets = 64 * 64;   // LDS buckets of the small-image build (at most 2048 used)
 constexpr int kTabMaxTokens = kKnnSmallTokens;
@@ -450,7 +449,6 @@ struct Chunk<bf16> : HalfChunk<bf16, bf16x8> {};
 template <>
 struct Chunk<f16> : HalfChunk<f16, f16x8> {};
 
-constexpr int kMaxChunksPerLane = 4;   // rows up to 256 chunks of 16 bytes (1024 f32 channels)
 
 // Lane-group geometry: a group of L = 2^lg lanes serves one query (or one
 // token); lane `sub` of the group covers chunks sub, sub + L.
@@ -1265,7 +1263,7 @@ hipError_t bwd_t(int B, int N, int M, int Cf, int G, int K, float p, const float
   auto grid1 = [](int64_t n) { return dim3((unsigned)((n + kKnnThreads - 1) / kKnnThreads)); };
   const int64_t MK = (int64_t)M * K;
   const int P = (int)((MK + kPart - 1) / kPart);
-  const int64_t npc = (int64_t)B * P * N, nparts = (int64_t)B * P;
+  const int64_t nparts = (int64_t)B * P;
   const int qwv = queries_per_wave(lg);
   // small images: counts per partition of kPart entries in LDS, stable
   // counting sort; large ones: per-token counts by integer atomics in the

@@ -92,7 +92,6 @@ template <typename H, typename V> struct Row16Half {
 template <> struct Row16<bf16> : Row16Half<bf16, mbf16x8> {};
 template <> struct Row16<f16> : Row16Half<f16, mf16x8> {};
 
-constexpr int kMaxChunks = 4;   // chunks of 16 bytes per lane (1024 channels of f32)
 
 // ---------------------------------------------------------------------------
 // Plan: anchors, assignment, member lists.  Assignment grid = B x S
