@@ -52,6 +52,27 @@ constexpr int NK = 48;
 constexpr int kWaves = 4;
 __device__ __forceinline__ uint32_t swz(int s) { return (uint32_t)((s & 15) >> 1); }
 
+// An output row of one head (32 dims) leaves the MFMA with lane group g
+// holding dims 4g .. 4g+3 (lo) and 16+4g .. 16+4g+3 (hi).  Trading one half
+// with the lane of group g ^ 1 (the same row) gives every lane 8
+// consecutive dims, written with one 16-byte store at byte offset col.
+// Every lane must take part (the exchange is a shuffle).
+struct Row8 {
+  uint4 v;
+  uint32_t col;
+};
+__device__ __forceinline__ Row8 row8(uint2 lo, uint2 hi, int g) {
+  const bool odd = (g & 1) != 0;
+  const uint2 give = odd ? lo : hi;
+  const uint2 got = make_uint2((uint32_t)__shfl_xor((int)give.x, 16, 64),
+                               (uint32_t)__shfl_xor((int)give.y, 16, 64));
+  Row8 r;
+  // even g: dims 4g .. 4g+7; odd g: dims 12+4g .. 16+4g+3
+  r.v = odd ? make_uint4(got.x, got.y, hi.x, hi.y) : make_uint4(lo.x, lo.y, got.x, got.y);
+  r.col = odd ? 24u + 8u * (uint32_t)g : 8u * (uint32_t)g;
+  return r;
+}
+
 // ---------------------------------------------------------------------------
 // forward, LDS-staged gathers
 // ---------------------------------------------------------------------------
@@ -181,10 +202,10 @@ __device__ __forceinline__ void gather_tile(const T* __restrict__ src, const Fwd
 // LDS and every tile is refilled as soon as it has been consumed.  Memory
 // operations are issued in this order in iteration t (vmcnt retires them in
 // issue order):
-//   idx(t+2) [2], K(t+1) [6], Q(t+1) [1], V(t+1) [6], O/LSE(t) stores [3]
+//   idx(t+2) [2], K(t+1) [6], Q(t+1) [1], V(t+1) [6], O/LSE(t) stores [2]
 // so at the top of iteration t, K(t), Q(t) and idx(t+1) are complete once
-// at most V(t) + stores(t-1) = 9 newer operations remain, and V(t) is
-// complete once at most stores(t-1) + idx(t+2) + K(t+1) = 11 remain.
+// at most V(t) + stores(t-1) = 8 newer operations remain, and V(t) is
+// complete once at most stores(t-1) + idx(t+2) + K(t+1) = 10 remain.
 template <typename T>
 __global__ void __launch_bounds__(64 * kFwdWaves)
 fwd_lds_kernel(int N, int C, int H, int HP, int n_items, int ipw, float scale_log2,
@@ -272,7 +293,7 @@ fwd_lds_kernel(int N, int C, int H, int HP, int n_items, int ipw, float scale_lo
     const int hq = left ? h0 : h0 + 1;
 
     // K(t), Q(t) and idx(t+1) have landed
-    if (prev) wait_vm<9>();
+    if (prev) wait_vm<8>();
     else wait_vm<6>();
     if (more) {
       read_idx(ti, lane, xn);
@@ -355,8 +376,8 @@ fwd_lds_kernel(int N, int C, int H, int HP, int n_items, int ipw, float scale_lo
     const uint4 bp0 = cat(ph[0], ph[1]), bp1 = pad(ph[2]);
 
     // V(t) has landed
-    if (prev && more2) wait_vm<11>();
-    else wait_vm_n((prev ? 3 : 0) + (more2 ? 2 : 0) + (more ? 6 : 0));
+    if (prev && more2) wait_vm<10>();
+    else wait_vm_n((prev ? 2 : 0) + (more2 ? 2 : 0) + (more ? 6 : 0));
 
     // O^T = V^T P^T per head.  Transposed read: lane c16 = 4e + qq of group g
     // addresses dims 16hf + 4qq.. of slot 16blk + 4g + e and receives dim
@@ -384,17 +405,14 @@ fwd_lds_kernel(int N, int C, int H, int HP, int n_items, int ipw, float scale_lo
       gather_tile<T>(v, oxn, av);
     }
 
-    // exactly three store instructions per item (the pipeline counts them);
+    // exactly two store instructions per item (the pipeline counts them);
     // 1/l through the hardware reciprocal (1 ulp)
     const float inv = l > 0.f ? __builtin_amdgcn_rcpf(l) : 0.f;
     const bool st = hq < H && x.qc >= 0;
     const uint32_t qrow = (uint32_t)__umul24((uint32_t)x.qc, (uint32_t)H) + (uint32_t)(img * H);
-    const uint32_t orow = (qrow + (uint32_t)(st ? hq : h0)) * kRow + 8u * g;
-#pragma unroll
-    for (int hf = 0; hf < 2; ++hf) {
-      const uint2 ov = pack4<T>((left ? oacc[0][hf] : oacc[1][hf]) * inv);
-      if (st) stv<uint2>(o, orow + 32u * hf, ov);
-    }
+    const Row8 ov = row8(pack4<T>((left ? oacc[0][0] : oacc[1][0]) * inv),
+                         pack4<T>((left ? oacc[0][1] : oacc[1][1]) * inv), g);
+    if (st) stv<uint4>(o, (qrow + (uint32_t)hq) * kRow + ov.col, ov.v);
     if (st && g == 0)
       lse[qrow + hq] = l > 0.f ? (mref + __log2f(l)) * kLn2 : -INFINITY;
     x = xn;
@@ -455,7 +473,7 @@ __device__ __forceinline__ KvPos kv_next(KvPos p, const KvStep& st, int HP, int 
 // issued and land while item t is computed from registers.  The index rows
 // (key_idx and q_idx rows, as in the forward) run one item further ahead and
 // the LSE values one item ahead, both through small LDS tiles, so that no
-// register load crosses an iteration.  The three stores of an item are the
+// register load crosses an iteration.  The two stores of an item are the
 // last memory operations of its step: the wait at the top leaves exactly
 // them in flight.
 constexpr int kQWaves = 2;
@@ -550,8 +568,8 @@ bwd_q_lds_kernel(int N, int C, int H, int HP, int n_items, int ipw, float scale,
     const KvPos pnn = kv_next(pn, st, HP, C);
 
     // this item's gathers and LSE and the next item's index rows have
-    // landed; the three stores of the previous item may still be in flight
-    if (pos.item > first) wait_vm<3>();
+    // landed; the two stores of the previous item may still be in flight
+    if (pos.item > first) wait_vm<2>();
     else wait_vm<0>();
 
     // every LDS operand of the item into registers
@@ -651,17 +669,14 @@ bwd_q_lds_kernel(int N, int C, int H, int HP, int n_items, int ipw, float scale,
         acc[hh][hf] = Mfma<T>::mma(pad(kt[hh][hf][2]), b1h, acc[hh][hf]);
       }
     }
-    // exactly three store instructions per item (lane 0, member 0 of the
+    // exactly two store instructions per item (lane 0, member 0 of the
     // cluster, always stores)
     const uint32_t qrow = (uint32_t)__umul24((uint32_t)x.qc, (uint32_t)H) + (uint32_t)(img * H);
     const bool live = hq < H && x.qc >= 0;
+    const Row8 dv8 = row8(pack4<T>((left ? acc[0][0] : acc[1][0]) * scale),
+                          pack4<T>((left ? acc[0][1] : acc[1][1]) * scale), g);
     if (live && g == 0) ld[qrow + hq] = make_float2(lse2, dl);
-    if (live) {
-      const uint32_t drow = (qrow + (uint32_t)hq) * kRow + 8u * g;
-#pragma unroll
-      for (int hf = 0; hf < 2; ++hf)
-        stv<uint2>(dq, drow + 32u * hf, pack4<T>((left ? acc[0][hf] : acc[1][hf]) * scale));
-    }
+    if (live) stv<uint4>(dq, (qrow + (uint32_t)hq) * kRow + dv8.col, dv8.v);
     if (!more) break;
     pos = pn;
     pn = pnn;
@@ -921,12 +936,15 @@ bwd_kv_lds_kernel(int N, int C, int H, int HP, int n_items, float scale, const T
       }
     }
 
-    if (hk < H && ktok >= 0) {   // -1: absent member of a partial key cluster
-      const uint32_t orow = (uint32_t)((img + ktok) * H + hk) * kRow + 8u * g;
-#pragma unroll
-      for (int hf = 0; hf < 2; ++hf) {
-        stv<uint2>(dk, orow + 32u * hf, pack4<T>((left ? dka[0][hf] : dka[1][hf]) * scale));
-        stv<uint2>(dv, orow + 32u * hf, pack4<T>(left ? dva[0][hf] : dva[1][hf]));
+    {
+      const Row8 k8 = row8(pack4<T>((left ? dka[0][0] : dka[1][0]) * scale),
+                           pack4<T>((left ? dka[0][1] : dka[1][1]) * scale), g);
+      const Row8 v8 = row8(pack4<T>(left ? dva[0][0] : dva[1][0]),
+                           pack4<T>(left ? dva[0][1] : dva[1][1]), g);
+      if (hk < H && ktok >= 0) {   // -1: absent member of a partial key cluster
+        const uint32_t orow = (uint32_t)((img + ktok) * H + hk) * kRow;
+        stv<uint4>(dk, orow + k8.col, k8.v);
+        stv<uint4>(dv, orow + v8.col, v8.v);
       }
     }
     if (nx.item >= n_items) break;

@@ -134,12 +134,10 @@ __device__ __forceinline__ void dma4(const void* base, uint32_t voff, uint32_t l
 // s_waitcnt vmcnt(n) for a run-time n from the few values the pipelines use
 // (a larger count is never required: any n' <= n is safe, only slower)
 __device__ __forceinline__ void wait_vm_n(int n) {
-  if (n >= 11) wait_vm<11>();
-  else if (n >= 9) wait_vm<9>();
+  if (n >= 10) wait_vm<10>();
   else if (n >= 8) wait_vm<8>();
   else if (n >= 6) wait_vm<6>();
-  else if (n >= 5) wait_vm<5>();
-  else if (n >= 3) wait_vm<3>();
+  else if (n >= 4) wait_vm<4>();
   else if (n >= 2) wait_vm<2>();
   else wait_vm<0>();
 }
