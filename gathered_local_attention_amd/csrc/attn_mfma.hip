@@ -132,15 +132,15 @@ constexpr int kFwdWaves = 2;
 constexpr int kFwdWavesPerCU = 8;
 constexpr int kFwdWaveLds = 2 * kTileBytes + 1024 + kIdxBytes;
 
-// Two exec-masked 16-byte loads: lanes 0..11 fetch the key_idx row of the
-// cluster (ints 0..47 of the tile), lanes 12..13 its q_idx row (ints
-// 48..55).  Few active lanes keep the address work small.  Counts as two
-// vector-memory operations.
+// One exec-masked 16-byte load with per-lane addresses: lanes 0..11 fetch
+// the key_idx row of the cluster (ints 0..47 of the tile), lanes 12..13 its
+// q_idx row (ints 48..55).  Counts as one vector-memory operation.
 __device__ __forceinline__ void gather_idx(int bc, const int32_t* __restrict__ q_idx,
                                            const int32_t* __restrict__ key_idx, int lane,
                                            uint32_t lds) {
-  if (lane < 12) dma16(key_idx, (uint32_t)(bc * NK) * 4u + 16u * (uint32_t)lane, lds);
-  else if (lane < 14) dma16(q_idx, (uint32_t)(bc * CS) * 4u + 16u * (uint32_t)(lane - 12), lds);
+  if (lane < 14)
+    dma16v(lane < 12 ? key_idx + (int64_t)bc * NK + 4 * lane : q_idx + (int64_t)bc * CS + 4 * (lane - 12),
+           lds);
 }
 
 // Per-lane indices of one item, read from its LDS index tile.
@@ -202,10 +202,10 @@ __device__ __forceinline__ void gather_tile(const T* __restrict__ src, const Fwd
 // LDS and every tile is refilled as soon as it has been consumed.  Memory
 // operations are issued in this order in iteration t (vmcnt retires them in
 // issue order):
-//   idx(t+2) [2], K(t+1) [6], Q(t+1) [1], V(t+1) [6], O/LSE(t) stores [2]
+//   idx(t+2) [1], K(t+1) [6], Q(t+1) [1], V(t+1) [6], O/LSE(t) stores [2]
 // so at the top of iteration t, K(t), Q(t) and idx(t+1) are complete once
 // at most V(t) + stores(t-1) = 8 newer operations remain, and V(t) is
-// complete once at most stores(t-1) + idx(t+2) + K(t+1) = 10 remain.
+// complete once at most stores(t-1) + idx(t+2) + K(t+1) = 9 remain.
 template <typename T>
 __global__ void __launch_bounds__(64 * kFwdWaves)
 fwd_lds_kernel(int N, int C, int H, int HP, int n_items, int ipw, float scale_log2,
@@ -376,8 +376,8 @@ fwd_lds_kernel(int N, int C, int H, int HP, int n_items, int ipw, float scale_lo
     const uint4 bp0 = cat(ph[0], ph[1]), bp1 = pad(ph[2]);
 
     // V(t) has landed
-    if (prev && more2) wait_vm<10>();
-    else wait_vm_n((prev ? 2 : 0) + (more2 ? 2 : 0) + (more ? 6 : 0));
+    if (prev && more2) wait_vm<9>();
+    else wait_vm_n((prev ? 2 : 0) + (more2 ? 1 : 0) + (more ? 6 : 0));
 
     // O^T = V^T P^T per head.  Transposed read: lane c16 = 4e + qq of group g
     // addresses dims 16hf + 4qq.. of slot 16blk + 4g + e and receives dim

@@ -115,6 +115,15 @@ __device__ __forceinline__ void dma16(const void* base, uint32_t voff, uint32_t 
                : "memory", "m0");
 }
 
+// The same with a per-lane 64-bit global address (lanes may read from
+// different arrays in one instruction).
+__device__ __forceinline__ void dma16v(const void* addr, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(addr), "s"(lds)
+               : "memory", "m0");
+}
+
 // s_waitcnt with vmcnt = N (0..63) and no wait on the other counters
 template <int N>
 __device__ __forceinline__ void wait_vm() {
@@ -134,12 +143,20 @@ __device__ __forceinline__ void dma4(const void* base, uint32_t voff, uint32_t l
 // s_waitcnt vmcnt(n) for a run-time n from the few values the pipelines use
 // (a larger count is never required: any n' <= n is safe, only slower)
 __device__ __forceinline__ void wait_vm_n(int n) {
-  if (n >= 10) wait_vm<10>();
-  else if (n >= 8) wait_vm<8>();
-  else if (n >= 6) wait_vm<6>();
-  else if (n >= 4) wait_vm<4>();
-  else if (n >= 2) wait_vm<2>();
-  else wait_vm<0>();
+  switch (n) {   // n wave-uniform; above 11 waits as for 11
+    case 0: wait_vm<0>(); break;
+    case 1: wait_vm<1>(); break;
+    case 2: wait_vm<2>(); break;
+    case 3: wait_vm<3>(); break;
+    case 4: wait_vm<4>(); break;
+    case 5: wait_vm<5>(); break;
+    case 6: wait_vm<6>(); break;
+    case 7: wait_vm<7>(); break;
+    case 8: wait_vm<8>(); break;
+    case 9: wait_vm<9>(); break;
+    case 10: wait_vm<10>(); break;
+    default: wait_vm<11>(); break;
+  }
 }
 
 // wait for this wave's outstanding LDS reads (before a DMA overwrites them)
