@@ -462,11 +462,13 @@ __device__ __forceinline__ KvPos kv_next(KvPos p, const KvStep& st, int HP, int 
 // backward pass A (query-major), LDS-staged gathers: Delta and dQ
 // ---------------------------------------------------------------------------
 // Per item (cluster, head pair), the 48 slot rows of K and V and the 8 query
-// rows of Q, dO and O go to a wavefront-private LDS tile (direct-to-LDS
-// loads, whole 128-byte rows).  Delta = <dO, O> per (query, head);
-// S^T = K Q^T and dP^T = V dO^T read K and V in the A layout; dQ^T = K^T dS^T
-// reads K through the transposing LDS read.  dS is rounded once to the
-// operand type for that product.
+// rows of Q and dO go to a wavefront-private LDS tile (direct-to-LDS loads,
+// whole 128-byte rows).  S^T = K Q^T and dP^T = V dO^T read K and V in the A
+// layout; dQ^T = K^T dS^T reads K through the transposing LDS read.  dS is
+// rounded once to the operand type for that product.  Delta, the row sum of
+// dO * O, equals the row sum of P * dP (O is the P-weighted sum of the V
+// rows), so it is taken from the P and dP this pass computes anyway, in fp32
+// before any rounding, and O is not read: a sixth of the pass's input bytes.
 //
 // Pipeline: at the top of item t every LDS operand of t is read into
 // registers at once, which frees the tiles; the gathers of item t+1 are then
@@ -477,14 +479,14 @@ __device__ __forceinline__ KvPos kv_next(KvPos p, const KvStep& st, int HP, int 
 // last memory operations of its step: the wait at the top leaves exactly
 // them in flight.
 constexpr int kQWaves = 2;
-constexpr int kQWaveLds = 2 * kTileBytes + 3 * 1024 + kIdxBytes + 64;   // K, V, Q, dO, O, idx, LSE
+constexpr int kQWaveLds = 2 * kTileBytes + 2 * 1024 + kIdxBytes + 64;   // K, V, Q, dO, idx, LSE
 constexpr int kQWavesPerCU = 8;
 
 template <typename T>
 __global__ void __launch_bounds__(64 * kQWaves)
 bwd_q_lds_kernel(int N, int C, int H, int HP, int n_items, int ipw, float scale,
                  const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
-                 const T* __restrict__ o, const T* __restrict__ dout,
+                 const T* __restrict__ dout,
                  const float* __restrict__ lse, const int32_t* __restrict__ q_idx,
                  const int32_t* __restrict__ key_idx, T* __restrict__ dq,
                  float2* __restrict__ ld, float4* __restrict__ ld_none) {
@@ -505,14 +507,13 @@ bwd_q_lds_kernel(int N, int C, int H, int HP, int n_items, int ipw, float scale,
   char* tv = tk + kTileBytes;
   char* tq = tv + kTileBytes;
   char* tdo = tq + 1024;
-  char* to = tdo + 1024;
-  char* ti = to + 1024;
+  char* ti = tdo + 1024;
   const float* tls = reinterpret_cast<const float*>(ti + kIdxBytes);
   auto lds_addr = [](const char* ptr) {
     return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const char*)ptr;
   };
   const uint32_t ak = lds_addr(tk), av = lds_addr(tv), aq = lds_addr(tq), ado = lds_addr(tdo),
-                 ao = lds_addr(to), ai = lds_addr(ti), als = lds_addr(ti + kIdxBytes);
+                 ai = lds_addr(ti), als = lds_addr(ti + kIdxBytes);
   const f32x4 z = {0.f, 0.f, 0.f, 0.f};
   const int e = c16 >> 2, qq = c16 & 3;
   const float scale_log2 = scale * kLog2e;
@@ -526,7 +527,7 @@ bwd_q_lds_kernel(int N, int C, int H, int HP, int n_items, int ipw, float scale,
   st.s_hp = stride - st.s_bj * HP;
   st.s_b = st.s_bj / C;
   st.s_j = st.s_bj - st.s_b * C;
-  // all gathers of an item (15 vector-memory operations)
+  // all gathers of an item (14 vector-memory operations)
   auto gather = [&](const KvPos& p, const FwdIdx2& x) {
     const bool two = 2 * p.hp + 1 < H;
     FwdOffs of;
@@ -535,7 +536,6 @@ bwd_q_lds_kernel(int N, int C, int H, int HP, int n_items, int ipw, float scale,
     gather_tile<T>(v, of, av);
     dma16(q, of.qr, aq);
     dma16(dout, of.qr, ado);
-    dma16(o, of.qr, ao);
   };
   // LSE of (query lane & 7, head h0 + (lane >> 3 & 1)) into the LSE tile
   // (lanes 0..15; one vector-memory operation)
@@ -577,7 +577,7 @@ bwd_q_lds_kernel(int N, int C, int H, int HP, int n_items, int ipw, float scale,
     const int qm = c16 & 7;
     const uint32_t qoff = (uint32_t)qm * kSlotBytes +
                           16u * ((uint32_t)((c16 >> 3) * 4 + g) ^ swz(qm));
-    const uint4 qv = lds16(tq, qoff), dov = lds16(tdo, qoff), ov = lds16(to, qoff);
+    const uint4 qv = lds16(tq, qoff), dov = lds16(tdo, qoff);
     uint4 k0[3], k1[3], v0[3], v1[3];
 #pragma unroll
     for (int b = 0; b < 3; ++b) {
@@ -610,19 +610,6 @@ bwd_q_lds_kernel(int N, int C, int H, int HP, int n_items, int ipw, float scale,
       if (pnn.item < n_items) gather_idx(pnn.bj, q_idx, key_idx, lane, ai);
     }
 
-    // Delta of (query c16 & 7, head hq)
-    float dl = 0.f;
-    {
-      const uint32_t a[4] = {dov.x, dov.y, dov.z, dov.w};
-      const uint32_t c[4] = {ov.x, ov.y, ov.z, ov.w};
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const f32x2 xa = Mfma<T>::unpack(a[i]), ya = Mfma<T>::unpack(c[i]);
-        dl = fmaf(xa[0], ya[0], fmaf(xa[1], ya[1], dl));
-      }
-    }
-    dl = shfl_sum16_32(dl);
-
     const uint4 qL = sel(left, qv), qR = sel(!left, qv);
     const uint4 dL = sel(left, dov), dR = sel(!left, dov);
     float p[3][4], dpv[3][4];
@@ -648,6 +635,13 @@ bwd_q_lds_kernel(int N, int C, int H, int HP, int n_items, int ipw, float scale,
           if (!((vb >> (4 * g + i)) & 1u)) p[b][i] = 0.f;
       }
     }
+    // Delta of (query c16 & 7, head hq) = sum over the slots of P * dP
+    float dl = 0.f;
+#pragma unroll
+    for (int b = 0; b < 3; ++b)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) dl = fmaf(p[b][i], dpv[b][i], dl);
+    dl = shfl_sum16_32(dl);
     float ds[3][4];
 #pragma unroll
     for (int b = 0; b < 3; ++b)
@@ -990,6 +984,7 @@ hipError_t bwd_t(int pass, int B, int N, int C, int H, int nk, float scale, cons
                  const void* k, const void* v, const void* o, const void* dout, const float* lse,
                  const int32_t* q_idx, const int32_t* key_idx, void* dq, void* dk, void* dv,
                  const BwdWorkspace& w, hipStream_t st) {
+  (void)o;   // pass A takes Delta from P and dP; O is not read
   const int HP = (H + 1) / 2;
   const int items = B * C * HP;
   const int kv_waves = std::min(items, 256 * kKvWavesPerCU);
@@ -999,7 +994,7 @@ hipError_t bwd_t(int pass, int B, int N, int C, int H, int nk, float scale, cons
     const int waves = (items + ipw - 1) / ipw;
     hipLaunchKernelGGL((bwd_q_lds_kernel<T>), dim3((waves + kQWaves - 1) / kQWaves),
                        dim3(64 * kQWaves), 0, st, N, C, H, HP, items, ipw, scale, (const T*)q,
-                       (const T*)k, (const T*)v, (const T*)o, (const T*)dout, lse, q_idx, key_idx,
+                       (const T*)k, (const T*)v, (const T*)dout, lse, q_idx, key_idx,
                        (T*)dq, w.ld, w.ld_none);
   }
   if (pass & 2) {
