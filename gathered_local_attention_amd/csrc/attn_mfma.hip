@@ -88,9 +88,9 @@ constexpr int kSlotBytes = 2 * kRow;            // one slot: both heads of the p
 constexpr int kTileBytes = NK * kSlotBytes;     // 6 KiB per tensor
 constexpr int kWaveLds = 2 * kTileBytes;        // K and V
 
-// Position of an item (cluster bc of the batch, head pair hp) walked
-// incrementally: a wavefront's items are consecutive, so one division at
-// the start replaces the per-item ones.
+// Position of an item (cluster bc of the batch, head pair hp), numbered
+// item = bc * HP + hp; the forward steps it by a fixed stride without
+// divisions after one initial division.
 struct ItemPos {
   int bc, hp, cin, img;   // cluster (batch-wide), head pair, cluster in image, image base token
   __device__ void init(int item, int HP, int C, int N) {
@@ -99,25 +99,6 @@ struct ItemPos {
     const int b = bc / C;
     cin = bc - b * C;
     img = b * N;
-  }
-  // head-pair-major numbering: item = hp * BC + bc (BC clusters in the batch),
-  // so consecutive items are consecutive clusters of one head pair
-  __device__ void init_hp_major(int item, int BC, int C, int N) {
-    hp = item / BC;
-    bc = item - hp * BC;
-    const int b = bc / C;
-    cin = bc - b * C;
-    img = b * N;
-  }
-  __device__ void next(int HP, int C, int N) {
-    if (++hp == HP) {
-      hp = 0;
-      ++bc;
-      if (++cin == C) {
-        cin = 0;
-        img += N;
-      }
-    }
   }
 };
 
@@ -238,24 +219,27 @@ fwd_lds_kernel(int N, int C, int H, int HP, int n_items, int ipw, float scale_lo
   const bool neg = scale_log2 < 0.f;        // wave-uniform
   const float csl = fabsf(scale_log2);
 
-  // Item positions (head-pair-major numbering item = hp * BC + bc) advance
-  // by the fixed stride without divisions.
-  const int BC = n_items / HP;
-  const int st_hp = stride / BC, st_bc = stride - st_hp * BC;
+  // Items are numbered item = bc * HP + hp: the head pairs of a cluster are
+  // neighbouring items, so the wavefronts on one window read whole token
+  // rows (all heads) at once rather than one head pair's half of each row
+  // per pass over the batch (stage-3, 16 heads: 19.1 -> 17.4 us).
+  // Positions advance by the fixed stride without divisions.
+  const int st_bc = stride / HP, st_hp = stride - st_bc * HP;
   const int st_b = st_bc / CperImg, st_c = st_bc - st_b * CperImg;
   auto step = [&](ItemPos p) {
     p.hp += st_hp;
-    p.bc += st_bc;
-    p.cin += st_c;
+    int dbc = st_bc, dc = st_c;
+    if (p.hp >= HP) {
+      p.hp -= HP;
+      ++dbc;
+      ++dc;
+    }
+    p.bc += dbc;
+    p.cin += dc;
     p.img += st_b * N;
     if (p.cin >= CperImg) {
       p.cin -= CperImg;
       p.img += N;
-    }
-    if (p.bc >= BC) {
-      p.bc -= BC;
-      p.img -= BC / CperImg * N;
-      ++p.hp;
     }
     return p;
   };
@@ -270,7 +254,7 @@ fwd_lds_kernel(int N, int C, int H, int HP, int n_items, int ipw, float scale_lo
 
   // prologue: indices of `first`, then of `first + 1`, then the tiles of `first`
   ItemPos pc, pn, pnn;   // items it, it + stride, it + 2 * stride
-  pc.init_hp_major(first, BC, CperImg, N);
+  pc.init(first, HP, CperImg, N);
   pn = step(pc);
   pnn = step(pn);
   FwdIdx2 x, xn;
