@@ -137,6 +137,53 @@ def entry_times(torch, calls, n_ev, n_sets):
     return out
 
 
+def entry_times_stream(torch, calls, n_sets, blocks=20):
+    """Back-to-back eager calls in blocks of one rotation (n_sets calls, one
+    per input copy) with HIP events only between blocks: nothing waits
+    between the calls of a block, so while the host issues calls faster than
+    the GPU runs them this is the GPU's time per call in a full queue (the
+    kernels and the gaps between them).  Returns name -> {mean, median, p10,
+    p90} (per call, microseconds, statistics over the blocks)."""
+    out = {}
+    for name, call in calls.items():
+        for i in range(n_sets):
+            call(i)
+        torch.cuda.synchronize()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(blocks + 1)]
+        ev[0].record()
+        for b in range(blocks):
+            for i in range(n_sets):
+                call(i)
+            ev[b + 1].record()
+        torch.cuda.synchronize()
+        d = sorted(ev[b].elapsed_time(ev[b + 1]) * 1e3 / n_sets for b in range(blocks))
+        q = lambda f: d[min(blocks - 1, int(round(f * (blocks - 1))))]
+        out[name] = {"mean": ev[0].elapsed_time(ev[blocks]) * 1e3 / (blocks * n_sets),
+                     "median": q(0.5), "p10": q(0.1), "p90": q(0.9)}
+    return out
+
+
+def pick_timing(names, graph, stream):
+    """Per-launch figure of each entry point: the lower mean of the graph
+    replay (when its outputs matched an eager call's) and the eager stream;
+    both are real launch modes of the same work.  Returns (stats, how)."""
+    stats, how = {}, {}
+    for name in names:
+        g, s = (graph or {}).get(name), stream[name]
+        if g is not None and g["mean"] <= s["mean"]:
+            stats[name], how[name] = g, ("graph: one call per rotating copy captured, 10 "
+                                         "replays, every captured call bitwise equal to an "
+                                         "eager call (faster than the eager stream)")
+        else:
+            stats[name], how[name] = s, ("stream: blocks of back-to-back eager calls over the "
+                                         "rotating copies, events between blocks only"
+                                         + (" (faster than the graph replay)" if g is not None
+                                            else " (no bitwise-matching graph replay: the plan "
+                                            "buffer also holds scratch whose contents vary)"
+                                            if graph is not None else ""))
+    return stats, how
+
+
 def entry_times_graph(torch, calls, n_sets, replays=10):
     """The same entry points launched from a HIP graph: one call per
     rotating copy captured once, the graph replayed `replays` times with HIP
@@ -436,9 +483,11 @@ def main():
     }
     eager = entry_times(torch, calls, n_ev, len(sets))
     graph = entry_times_graph(torch, calls, len(sets))
-    # per-launch figures: the graph replay where it matched the eager results
-    # (GPU time; the eager back-to-back calls also wait for the Python launch)
-    stats = {name: graph[name] if graph.get(name) else eager[name] for name in calls}
+    stream = entry_times_stream(torch, calls, len(sets))
+    # per-launch figures: the faster of the graph replay (where it matched
+    # the eager results) and the eager stream; the per-call-event figures
+    # (an event between every two calls) are kept beside them
+    stats, how = pick_timing(calls, graph, stream)
     dur = {name: st["mean"] for name, st in stats.items()}   # microseconds per launch
 
     # warm-cache variant: every step on the same copy
@@ -516,12 +565,9 @@ def main():
         },
         "entry_us": dur,
         "entry_us_stats": stats,
-        "entry_timing": {name: ("graph: one call per rotating copy captured, 10 replays, "
-                                "every captured call bitwise equal to an eager call")
-                         if graph.get(name) else "eager back-to-back calls (the captured "
-                         "outputs were not bitwise equal to an eager call's: the plan buffer "
-                         "also holds scratch whose contents vary)"
-                         for name in calls},
+        "entry_timing": how,
+        "entry_us_graph": {name: (st["mean"] if st else None) for name, st in graph.items()},
+        "entry_us_stream": {name: st["mean"] for name, st in stream.items()},
         "entry_us_eager": {name: st["mean"] for name, st in eager.items()},
         "entry_us_stats_eager": eager,
         "mfma_counters": measured_mfma(cfg.name, dur),
@@ -636,7 +682,8 @@ def bench_varlen(args, torch, ca):
                                                  outs[i][2], sets[i]["do"], outs[i][3], outs[i][0],
                                                  outs[i][1], scale, workspace=gws),
     }
-    stats = entry_times(torch, calls, n_ev, len(sets))
+    eager = entry_times(torch, calls, n_ev, len(sets))
+    stats, how = pick_timing(calls, None, entry_times_stream(torch, calls, len(sets)))
     dur = {name: st["mean"] for name, st in stats.items()}
 
     alg = algorithmic_tc(T, Ct, cfg.H, cfg.D, cfg.nk, cfg.k, cfg.cs, cfg.dtype)
@@ -690,6 +737,8 @@ def bench_varlen(args, torch, ca):
         },
         "entry_us": dur,
         "entry_us_stats": stats,
+        "entry_timing": how,
+        "entry_us_eager": {name: st["mean"] for name, st in eager.items()},
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
@@ -809,7 +858,8 @@ def bench_sampler(args, torch, ca):
                                             sets[i]["lv"][li]["dout"], workspace=wss[li])
                           for li in range(L)],
     }
-    stats = entry_times(torch, calls, n_ev, len(sets))
+    eager = entry_times(torch, calls, n_ev, len(sets))
+    stats, how = pick_timing(calls, None, entry_times_stream(torch, calls, len(sets)))
     dur = {name: st["mean"] for name, st in stats.items()}
     alg = sampler_algorithmic(cfg)
     dom = max(("table", "fwd", "bwd"), key=lambda k: dur[k])
@@ -859,6 +909,8 @@ def bench_sampler(args, torch, ca):
         },
         "entry_us": dur,
         "entry_us_stats": stats,
+        "entry_timing": how,
+        "entry_us_eager": {name: st["mean"] for name, st in eager.items()},
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
@@ -963,7 +1015,8 @@ def bench_merge(args, torch, ca):
                                        plans[i][li][2], plans[i][li][3], sets[i][li]["dfeat"],
                                        sets[i][li]["dcoord"]) for li in range(L)],
     }
-    stats = entry_times(torch, calls, n_ev, len(sets))
+    eager = entry_times(torch, calls, n_ev, len(sets))
+    stats, how = pick_timing(calls, None, entry_times_stream(torch, calls, len(sets)))
     dur = {name: st["mean"] for name, st in stats.items()}
     alg = merge_algorithmic(cfg)
     dom = max(("plan", "fwd", "bwd"), key=lambda k: dur[k])
@@ -1010,6 +1063,8 @@ def bench_merge(args, torch, ca):
         },
         "entry_us": dur,
         "entry_us_stats": stats,
+        "entry_timing": how,
+        "entry_us_eager": {name: st["mean"] for name, st in eager.items()},
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:

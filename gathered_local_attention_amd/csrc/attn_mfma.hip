@@ -654,7 +654,7 @@ bwd_q_lds_kernel(int N, int C, int H, int HP, int n_items, int ipw, float scale,
     const Row8 dv8 = row8(pack4<T>((left ? acc[0][0] : acc[1][0]) * scale),
                           pack4<T>((left ? acc[0][1] : acc[1][1]) * scale), g);
     if (live && g == 0) ld[qrow + hq] = make_float2(lse2, dl);
-    if (live) stv<uint4>(dq, (qrow + (uint32_t)hq) * kRow + dv8.col, dv8.v);
+    if (live) st16_nt(dq, (qrow + (uint32_t)hq) * kRow + dv8.col, dv8.v);
     if (!more) break;
     pos = pn;
     pn = pnn;
@@ -921,8 +921,8 @@ bwd_kv_lds_kernel(int N, int C, int H, int HP, int n_items, float scale, const T
                            pack4<T>(left ? dva[0][1] : dva[1][1]), g);
       if (hk < H && ktok >= 0) {   // -1: absent member of a partial key cluster
         const uint32_t orow = (uint32_t)((img + ktok) * H + hk) * kRow;
-        stv<uint4>(dk, orow + k8.col, k8.v);
-        stv<uint4>(dv, orow + v8.col, v8.v);
+        st16_nt(dk, orow + k8.col, k8.v);
+        st16_nt(dv, orow + v8.col, v8.v);
       }
     }
     if (nx.item >= n_items) break;
