@@ -222,7 +222,7 @@ fwd_lds_kernel(int N, int C, int H, int HP, int n_items, int ipw, float scale_lo
   // Items are numbered item = bc * HP + hp: the head pairs of a cluster are
   // neighbouring items, so the wavefronts on one window read whole token
   // rows (all heads) at once rather than one head pair's half of each row
-  // per pass over the batch (stage-3, 16 heads: 19.1 -> 17.4 us).
+  // per pass over the batch (stage-3, 16 heads: 19.1 -> 18.1 us).
   // Positions advance by the fixed stride without divisions.
   const int st_bc = stride / HP, st_hp = stride - st_bc * HP;
   const int st_b = st_bc / CperImg, st_c = st_bc - st_b * CperImg;
