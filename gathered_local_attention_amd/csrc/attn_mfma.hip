@@ -266,7 +266,7 @@ fwd_lds_kernel(int N, int C, int H, int HP, int n_items, int ipw, float scale_lo
   if (first + stride < n_items) gather_idx(pn.bc, q_idx, key_idx, lane, ai);
   offs_of(x, pc, ox);
   gather_tile<T>(k, ox, ak);
-  dma16(q, ox.qr, aq);
+  dma16_nt(q, ox.qr, aq);
   gather_tile<T>(v, ox, av);
 
   for (int it = first; it < n_items; it += stride) {
@@ -385,7 +385,7 @@ fwd_lds_kernel(int N, int C, int H, int HP, int n_items, int ipw, float scale_lo
     }
     if (more) {   // Q and V tiles consumed: next item's
       wait_lgkm0();
-      dma16(q, oxn.qr, aq);
+      dma16_nt(q, oxn.qr, aq);
       gather_tile<T>(v, oxn, av);
     }
 

@@ -127,6 +127,16 @@ __device__ __forceinline__ void dma16(const void* base, uint32_t voff, uint32_t 
                : "memory", "m0");
 }
 
+// The same for rows that no other item reads again (a cluster's own query
+// rows): a streaming (non-temporal) load, so they do not push gathered rows
+// that other items still need out of the L2.
+__device__ __forceinline__ void dma16_nt(const void* base, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1 nt"
+               :
+               : "v"(voff), "s"(base), "s"(lds)
+               : "memory", "m0");
+}
+
 // The same with a per-lane 64-bit global address (lanes may read from
 // different arrays in one instruction).
 __device__ __forceinline__ void dma16v(const void* addr, uint32_t lds) {
