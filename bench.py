@@ -84,6 +84,18 @@ def algorithmic_tc(T, C, H, D, nk, k, cs, dtype):
     }
 
 
+def formulation_bytes(cfg, dom, alg, dur):
+    """The bf16/f16 backward takes Delta from P and dP and reads no O, so it
+    must move one [tokens, H, D] tensor fewer than the algorithmic bytes
+    above (which count O as a backward input); reported beside the roofline
+    so that its fraction can be read on either count."""
+    if dom != "bwd" or cfg.dtype == "f32":
+        return {}
+    b = alg["bwd"]["bytes"] - cfg.tokens * cfg.H * cfg.D * 2
+    gbps = b / (dur["bwd"] * 1e-6) / 1e9
+    return {"bytes_this_formulation_moves": b, "frac_on_those_bytes": gbps / HBM_PEAK_GBPS}
+
+
 def copy_bandwidth(torch, ca, nbytes=1 << 30, reps=10):
     """Achievable HBM bandwidth: the library's plain copy kernel
     (cluster_attn_device_copy) moving `nbytes` (1 GiB read + 1 GiB written),
@@ -549,6 +561,7 @@ def main():
             "traffic": measured_traffic(cfg.name, dom),
             "algorithmic_bytes": alg[dom]["bytes"],
             "avg_us": dur[dom],
+            **formulation_bytes(cfg, dom, alg, dur),
         },
         "fwd_bwd": {
             "note": "forward + backward on built lists and plan (both depend on the coordinates "

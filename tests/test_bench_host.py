@@ -37,3 +37,11 @@ def test_pick_timing_takes_the_faster_launch_mode():
     assert stats["c"]["mean"] == 7.0 and how["c"].startswith("stream")
     stats, how = bench.pick_timing(["a"], None, stream)
     assert stats["a"]["mean"] == 9.0 and how["a"].startswith("stream")
+
+
+def test_formulation_bytes_drop_the_unread_output():
+    cfg = CONFIGS["stage1"]
+    alg = bench.algorithmic(cfg)
+    f = bench.formulation_bytes(cfg, "bwd", alg, {"bwd": 50.0})
+    assert f["bytes_this_formulation_moves"] == 137_101_312 - 65536 * 4 * 32 * 2
+    assert bench.formulation_bytes(cfg, "fwd", alg, {"fwd": 20.0}) == {}
