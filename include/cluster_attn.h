@@ -201,8 +201,9 @@ size_t cluster_attn_bwd_workspace(int dt, int B, int N, int H, int D, int cs, in
  * forward's probabilities recomputed as exp(S - LSE):
  *   Delta_m = <dO_m, O_m>;  dP_ms = <dO_m, V_s>;  dS = P * (dP - Delta)
  * Since O_m = sum_s P_ms V_s, Delta_m also equals sum_s P_ms dP_ms; the
- * bf16/f16 kernels take it in that form from the fp32 P and dP they compute
- * anyway, so they do not read o (the fp32 kernels read it).
+ * matrix-core kernels (bf16/f16 with nk = 48) take it in that form from the
+ * fp32 P and dP they compute anyway, so they do not read o (the vector-ALU
+ * kernels for f32 and other list lengths read it).
  *   dQ_m = scale sum_s dS_ms K_s
  *   dK_j = scale sum over every (cluster, slot) whose key is j of dS Q
  *   dV_j = sum over the same slots of P dO
@@ -211,8 +212,8 @@ size_t cluster_attn_bwd_workspace(int dt, int B, int N, int H, int D, int cs, in
  * directly, so no atomics touch the gradients and the result is bitwise
  * reproducible.  fp32 accumulation throughout; P and dS are rounded once to
  * dt as operands of the dV, dK and dQ products (bf16/f16); outputs RNE to dt.
- *   q, k, v, o, dout [B, N, H, D] dt (o as returned by the forward; read
- *             only when dt is f32, but always a valid pointer).
+ *   q, k, v, o, dout [B, N, H, D] dt (o as returned by the forward; not
+ *             read by the matrix-core kernels, but always a valid pointer).
  *   lse       [B, N, H] f32 from the forward.
  *   dq, dk, dv [B, N, H, D] dt out.
  *   ws        device workspace of at least cluster_attn_bwd_workspace(...)
