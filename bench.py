@@ -85,11 +85,12 @@ def algorithmic_tc(T, C, H, D, nk, k, cs, dtype):
 
 
 def formulation_bytes(cfg, dom, alg, dur):
-    """The bf16/f16 backward takes Delta from P and dP and reads no O, so it
-    must move one [tokens, H, D] tensor fewer than the algorithmic bytes
-    above (which count O as a backward input); reported beside the roofline
-    so that its fraction can be read on either count."""
-    if dom != "bwd" or cfg.dtype == "f32":
+    """The matrix-core backward (bf16/f16, 48 slots) takes Delta from P and
+    dP and reads no O, so it must move one [tokens, H, D] tensor fewer than
+    the algorithmic bytes above (which count O as a backward input);
+    reported beside the roofline so that its fraction can be read on either
+    count."""
+    if dom != "bwd" or cfg.dtype == "f32" or cfg.nk != 48:
         return {}
     b = alg["bwd"]["bytes"] - cfg.tokens * cfg.H * cfg.D * 2
     gbps = b / (dur["bwd"] * 1e-6) / 1e9
