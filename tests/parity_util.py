@@ -25,7 +25,7 @@ TOL = {
 
 
 def tol_for(cfg):
-    return TOL["stress"] if cfg.qkv_scale != 1.0 else TOL[cfg.dtype]
+    return TOL["stress"] if getattr(cfg, "qkv_scale", 1.0) != 1.0 else TOL[cfg.dtype]
 
 
 def to_np(t: torch.Tensor) -> np.ndarray:

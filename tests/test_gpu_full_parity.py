@@ -1,7 +1,8 @@
 """Every output element at the launch configuration the benchmark times.
 
-The benchmark runs whole batches (stage-1, stage-3 and the stress workload
-at B = 32, high-res at B = 4) through the forward and the planned backward,
+The benchmark runs whole batches (stage-1, stage-2, stage-3, stage-4, the
+stress workload and the 3D volumes at B = 32, high-res at B = 4) through
+the forward and the planned backward,
 where every wavefront walks several items.  These tests run exactly those
 launches and compare every element of O, LSE, dQ, dK and dV with the fp64
 oracle (gathered form, cluster blocks); high-res compares one whole image.
@@ -32,7 +33,7 @@ import pytest
 import torch
 
 import oracle as O
-from gen import make_case, stress_duplicate_slots
+from gen import make_case, make_volume_case, stress_duplicate_slots
 from gen.synth import stress_rng
 from parity_util import assert_finite, check_close, term_magnitudes, to_np, tol_for
 
@@ -123,7 +124,8 @@ def _sum_rules(cfg, r):
     assert rk <= 1.0 and rv <= 1.0
 
 
-@pytest.mark.parametrize("name,B", [("stage1", 32), ("stage3", 32), ("stress", 32), ("stage1", 19)])
+@pytest.mark.parametrize("name,B", [("stage1", 32), ("stage3", 32), ("stress", 32), ("stage1", 19),
+                                    ("stage2", 32), ("stage4", 32)])
 def test_whole_batch_every_element(ca, name, B):
     case = make_case(name, B=B)
     cfg = case["cfg"]
@@ -137,6 +139,26 @@ def test_whole_batch_every_element(ca, name, B):
     if cfg.qkv_scale != 1.0:
         mag = term_magnitudes(case["q"], case["k"], case["v"], case["do"], qi, key_np, r["scale"])
     _compare(cfg, r, ref_o, ref_lse, ref_g, mag=mag)
+    _sum_rules(cfg, r)
+
+
+def test_volume_whole_batch_every_element(ca):
+    """The 32-volume 3D batch as the benchmark runs it (lists from the 3D
+    build, bit-exact), every element against the oracle."""
+    case = make_volume_case("volume")
+    cfg = case["cfg"]
+    print(f"case volume B={cfg.B} N={cfg.N} (3D, every element)", flush=True)
+    perm, _, key = ca.build_neighbors(torch.from_numpy(case["coords"]).to(DEV), cfg.G)
+    torch.cuda.synchronize()
+    perm_r, _, key_r = O.build_neighbors_3d(case["coords"], cfg.G)
+    assert np.array_equal(perm.cpu().numpy(), perm_r), "perm differs from the oracle"
+    assert np.array_equal(key.cpu().numpy(), key_r), "key_idx differs from the oracle"
+    r = _run(ca, case, perm, key)
+    qi = perm_r.reshape(cfg.B, -1, cfg.cs)
+    ref_o, ref_lse = O.attn_fwd_gathered(case["q"], case["k"], case["v"], qi, key_r, r["scale"])
+    ref_g = O.attn_bwd_gathered(case["q"], case["k"], case["v"], case["do"], qi, key_r,
+                                r["scale"])
+    _compare(cfg, r, ref_o, ref_lse, ref_g)
     _sum_rules(cfg, r)
 
 
