@@ -162,6 +162,28 @@ def test_volume_whole_batch_every_element(ca):
     _sum_rules(cfg, r)
 
 
+def test_volume_hr_whole_volume_every_element(ca):
+    """The two 64,000-token volumes as the benchmark runs them; volume 0 is
+    compared element by element (lists of both bit-exact)."""
+    case = make_volume_case("volume_hr")
+    cfg = case["cfg"]
+    print(f"case volume_hr B={cfg.B} N={cfg.N} (3D, volume 0, every element)", flush=True)
+    perm, _, key = ca.build_neighbors(torch.from_numpy(case["coords"]).to(DEV), cfg.G)
+    torch.cuda.synchronize()
+    perm_r, _, key_r = O.build_neighbors_3d(case["coords"], cfg.G)
+    assert np.array_equal(perm.cpu().numpy(), perm_r), "perm differs from the oracle"
+    assert np.array_equal(key.cpu().numpy(), key_r), "key_idx differs from the oracle"
+    r = _run(ca, case, perm, key)
+    qi = perm_r.reshape(cfg.B, -1, cfg.cs)
+    one = lambda t: t[0:1]
+    ref_o, ref_lse = O.attn_fwd_gathered(one(case["q"]), one(case["k"]), one(case["v"]),
+                                         qi[0:1], key_r[0:1], r["scale"])
+    ref_g = O.attn_bwd_gathered(one(case["q"]), one(case["k"]), one(case["v"]), one(case["do"]),
+                                qi[0:1], key_r[0:1], r["scale"])
+    _compare(cfg, r, ref_o, ref_lse, ref_g, sel=slice(0, 1))
+    _sum_rules(cfg, r)
+
+
 def test_highres_whole_image_every_element(ca):
     """B = 4 images of 65,536 tokens run as the benchmark runs them; image 0
     is compared element by element (the oracle works through it in blocks
