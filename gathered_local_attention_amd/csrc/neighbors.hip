@@ -520,6 +520,27 @@ select_box_kernel(Geom g, const typename Space<DIM>::FCent* __restrict__ cent_al
 // ---------------------------------------------------------------------------
 constexpr int kSmallThreads = 1024;
 
+// 64-bit lane move with a DPP pattern (both halves moved the same way)
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp64(uint64_t v) {
+  const int lo = __builtin_amdgcn_mov_dpp((int)(uint32_t)v, CTRL, 0xF, 0xF, false);
+  const int hi = __builtin_amdgcn_mov_dpp((int)(uint32_t)(v >> 32), CTRL, 0xF, 0xF, false);
+  return ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo;
+}
+
+// Minimum over each aligned group of `lanes` lanes (a power of two <= 16,
+// wave-uniform), every lane active: quad swaps, then the half-row and row
+// mirrors, which pair each quad (eight) with the other one of its eight
+// (sixteen).  Register moves instead of LDS-crossbar shuffles.
+__device__ __forceinline__ uint64_t group_min64(uint64_t m, int lanes) {
+  uint64_t x;
+  if (lanes > 1) { x = dpp64<0xB1>(m); m = x < m ? x : m; }    // quad_perm [1,0,3,2]
+  if (lanes > 2) { x = dpp64<0x4E>(m); m = x < m ? x : m; }    // quad_perm [2,3,0,1]
+  if (lanes > 4) { x = dpp64<0x141>(m); m = x < m ? x : m; }   // row_half_mirror
+  if (lanes > 8) { x = dpp64<0x140>(m); m = x < m ? x : m; }   // row_mirror
+  return m;
+}
+
 constexpr int kBuckets = 2 * kSmallThreads;       // counting-sort buckets (11 key bits)
 constexpr int kMaxBucket = 32;                    // larger buckets -> bitonic fallback
 
@@ -784,11 +805,7 @@ build_small_kernel(const float* __restrict__ coords, Geom g, double step, int pa
     uint64_t merged[KB];
 #pragma unroll
     for (int r = 0; r < KM1; ++r) {
-      uint64_t m = best[0];
-      for (int o = 1; o < lanes; o <<= 1) {
-        const uint64_t x = __shfl_xor(m, o, 64);
-        m = x < m ? x : m;
-      }
+      const uint64_t m = group_min64(best[0], lanes);
       merged[r] = m;
       if (best[0] == m && m != ~0ull) {
 #pragma unroll
