@@ -332,7 +332,7 @@ def cpu_baseline(cfg, case, images: int, single_images: int = 8, runs: int = 3):
 
 # the kernel sources whose rocprofv3 counter summaries bench.py reports
 KERNEL_SOURCES = ("attn_mfma.hip", "attn_valu.hip", "mfma_util.h", "common.h", "bwd_plan.hip",
-                  "neighbors.hip")
+                  "neighbors.hip", "dpp_scan.h")
 
 
 SAMPLER_SOURCES = ("knn_sampler.hip", "scan.hip", "common.h")

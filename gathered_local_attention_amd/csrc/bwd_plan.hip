@@ -29,6 +29,7 @@
 //      every entry gets the q_idx row of its i, so that the key-major pass
 //      gathers without a further lookup.
 #include "common.h"
+#include "dpp_scan.h"
 
 #include <algorithm>
 
@@ -187,7 +188,7 @@ plan_scan_kernel(int C, int nk, const int32_t* __restrict__ cnt_all, int2* __res
 #pragma unroll
     for (int r = 0; r < kPer; ++r) run += r0 + r < n ? v[r0 + r] : 0;
     int tot;
-    int acc = carry + block_exclusive_scan(run, tmp, kPlanThreads, &tot);
+    int acc = carry + block_exclusive_scan_dpp(run, tmp, kPlanThreads, &tot);
 #pragma unroll
     for (int r = 0; r < kPer; ++r) {
       if (r0 + r < n) {
@@ -451,7 +452,7 @@ plan_small_kernel(Geom g, int nk, const int32_t* __restrict__ q_idx,
     for (int w = 0; w < kWords; ++w) vsum += __popc(bits[tid][w]);
   }
   int total;
-  const int ex = block_exclusive_scan(vsum, tmp, kPlanThreads, &total);
+  const int ex = block_exclusive_scan_dpp(vsum, tmp, kPlanThreads, &total);
   if (tid < C) {
     int a = ex;
 #pragma unroll
