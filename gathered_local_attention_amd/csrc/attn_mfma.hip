@@ -106,10 +106,13 @@ struct ItemPos {
 // LDS tile of one item's indices: ints 0..47 key tokens of the 48 slots,
 // 48..55 the query tokens of the cluster, 56..63 unused (never written).
 constexpr int kIdxBytes = 256;
-constexpr int kFwdWaves = 2;
+// Wavefronts per workgroup: eight, i.e. four clusters with both head pairs
+// (H=4) in one workgroup on one CU (LDS: one such workgroup per
+// CU).  Against two per workgroup: high-res forward 84.0 -> 76.6 us,
+// stage-1 23.8 -> 22.5 us, stage-3 unchanged.
+constexpr int kFwdWaves = 8;
 // Waves per CU the launch is sized for (one round over all 256 CUs); the
-// measured optimum at the stage-1 shape is below the LDS/VGPR residency
-// limit of 12.
+// measured optimum at the stage-1 shape.
 constexpr int kFwdWavesPerCU = 8;
 constexpr int kFwdWaveLds = 2 * kTileBytes + 1024 + kIdxBytes;
 
@@ -462,7 +465,9 @@ __device__ __forceinline__ KvPos kv_next(KvPos p, const KvStep& st, int HP, int 
 // register load crosses an iteration.  The two stores of an item are the
 // last memory operations of its step: the wait at the top leaves exactly
 // them in flight.
-constexpr int kQWaves = 2;
+// four wavefronts per workgroup (two per workgroup: high-res backward
+// 193.9 -> 183.3 us with four, stage-1 and stage-3 0.5-0.7 us faster)
+constexpr int kQWaves = 4;
 constexpr int kQWaveLds = 2 * kTileBytes + 2 * 1024 + kIdxBytes + 64;   // K, V, Q, dO, idx, LSE
 constexpr int kQWavesPerCU = 8;
 
